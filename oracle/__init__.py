@@ -1,0 +1,23 @@
+"""FP64 CPU oracle of the routed MoE layer (test infrastructure only).
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package.  The product path never does.
+"""
+from .moe_oracle import (  # noqa: F401
+    backward,
+    bf16_to_f64,
+    brute_force_forward,
+    combine,
+    expert_weight_grads,
+    f64_to_bf16_bits,
+    forward,
+    permute_routes,
+    route_gates,
+    routed_rows,
+    router_logits,
+    select_routes,
+    shared_expert,
+    sigmoid,
+    silu,
+    swiglu_expert,
+)

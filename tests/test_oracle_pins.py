@@ -1,0 +1,295 @@
+"""Pins of the FP64 oracle against facts that do not come from the oracle.
+
+Each test ties one part of the oracle to something independent of it:
+brute-force per-token loops, special cases that reduce to a dense MLP or a
+closed form, the tie rule of the pages' routing step, invariants of a
+permutation, central finite differences and an independent torch float64
+autograd of the same layer definition.  A plausible slip anywhere in the
+oracle (a dropped shared term, a transposed weight, a wrong slot order, a
+sign in the softmax backward) fails at least one of them.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def small_cfg(**kw):
+    base = dict(name="small", tokens=24, hidden=64, experts=32, top_k=4, inter=32, shared_inter=32)
+    base.update(kw)
+    return W.MoEConfig(**base)
+
+
+def layer_and_x(cfg):
+    layer = W.make_layer(cfg)
+    return layer, W.tokens(cfg)
+
+
+# ---------------------------------------------------------------- P1 brute force
+@pytest.mark.parametrize("cfgname", ["small", "tiny"])
+def test_brute_force_matches_vectorised(cfgname):
+    cfg = small_cfg() if cfgname == "small" else W.CONFIGS["tiny"]
+    layer, x = layer_and_x(cfg)
+    x = x[:48]
+    fwd = O.forward(layer, x, cfg.top_k)
+    routes, out = O.brute_force_forward(layer, x, cfg.top_k)
+    assert np.array_equal(routes, fwd["idx"])
+    assert np.max(np.abs(out - fwd["out"])) <= 1e-12
+
+
+def test_brute_force_at_production_shape():
+    """Eight tokens of the 2048-hidden, 512-intermediate layer; only the
+    experts those tokens touch are generated (the rest stay zero and are
+    never read)."""
+    cfg = W.CONFIGS["moe1k"]
+    layer = W.make_layer(cfg, with_experts=False)
+    x = W.tokens(cfg)[:8]
+    idx = O.select_routes(O.router_logits(x, layer["w_router"]), cfg.top_k)
+    E, H, I = cfg.experts, cfg.hidden, cfg.inter
+    w13 = np.zeros((E, 2 * I, H), np.uint16)
+    w2 = np.zeros((E, H, I), np.uint16)
+    for e in np.unique(idx):
+        a, b = W.expert_weights(cfg, int(e), 1)
+        w13[e], w2[e] = a[0], b[0]
+    layer["w13"], layer["w2"] = w13, w2
+    fwd = O.forward(layer, x, cfg.top_k)
+    routes, out = O.brute_force_forward(layer, x, cfg.top_k)
+    assert np.array_equal(routes, fwd["idx"])
+    assert np.max(np.abs(out - fwd["out"])) <= 1e-12
+
+
+# ---------------------------------------------------------------- P2 identical experts
+def test_identical_experts_reduce_to_dense_mlp():
+    """All experts equal and no shared expert: the gates sum to one, so the
+    layer is one dense SwiGLU MLP whatever the routing."""
+    cfg = small_cfg(shared_inter=0)
+    layer, x = layer_and_x(cfg)
+    layer["w13"] = np.broadcast_to(layer["w13"][3], layer["w13"].shape)
+    layer["w2"] = np.broadcast_to(layer["w2"][3], layer["w2"].shape)
+    fwd = O.forward(layer, x, cfg.top_k)
+    xf = O.bf16_to_f64(x)
+    w13 = O.bf16_to_f64(layer["w13"][0])
+    w2 = O.bf16_to_f64(layer["w2"][0])
+    h = xf @ w13.T
+    g, u = h[:, : cfg.inter], h[:, cfg.inter:]
+    dense = (g / (1 + np.exp(-g)) * u) @ w2.T
+    assert np.max(np.abs(fwd["out"] - dense)) <= 1e-12
+
+
+# ---------------------------------------------------------------- P3 zero router
+def test_zero_router_picks_lowest_ids_with_equal_gates():
+    """All logits equal: the tie rule keeps experts 0..K-1 in order, and the
+    renormalised gates are exactly 1/K."""
+    cfg = small_cfg()
+    layer, x = layer_and_x(cfg)
+    layer["w_router"] = np.zeros_like(layer["w_router"])
+    fwd = O.forward(layer, x, cfg.top_k)
+    assert np.array_equal(fwd["idx"], np.tile(np.arange(cfg.top_k, dtype=np.int32), (cfg.tokens, 1)))
+    assert np.all(fwd["gates"] == 1.0 / cfg.top_k)
+
+
+# ---------------------------------------------------------------- P4 forced bias
+def test_forced_bias_orders_slots_descending():
+    """A bias of -100*e dominates the O(1) logits: slot k holds expert k,
+    and the gates equal scipy's softmax of those ten logits."""
+    from scipy.special import softmax
+    cfg = small_cfg()
+    layer, x = layer_and_x(cfg)
+    layer["router_bias"] = (-100.0 * np.arange(cfg.experts)).astype(np.float32)
+    fwd = O.forward(layer, x, cfg.top_k)
+    assert np.array_equal(fwd["idx"], np.tile(np.arange(cfg.top_k, dtype=np.int32), (cfg.tokens, 1)))
+    ref = softmax(fwd["logits"][:, : cfg.top_k], axis=1)
+    assert np.max(np.abs(fwd["gates"] - ref)) <= 1e-15
+    assert np.all(np.diff(fwd["logits"][:, : cfg.top_k], axis=1) < 0)
+
+
+def test_tie_goes_to_lower_id_inside_the_top_k():
+    """Two experts with bit-equal logits: the lower id takes the earlier slot."""
+    cfg = small_cfg()
+    layer, x = layer_and_x(cfg)
+    wr = layer["w_router"].copy()
+    wr[7] = wr[19]
+    bias = np.zeros(cfg.experts, np.float32)
+    bias[[7, 19]] = 50.0
+    layer["w_router"], layer["router_bias"] = wr, bias
+    fwd = O.forward(layer, x, cfg.top_k)
+    assert np.all(fwd["idx"][:, 0] == 7) and np.all(fwd["idx"][:, 1] == 19)
+    assert np.allclose(fwd["gates"][:, 0], fwd["gates"][:, 1], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- P5 expert-id probe
+def test_expert_id_probe_maps_routes_to_their_experts():
+    """Experts built so that expert e outputs the constant c_e on every
+    hidden unit: x[:,0] = 1, every gate row = (a,0,...), every up row =
+    (b_e,0,...), W2[:,0] = 1.  Then out[t] = sum_k g[t,k] silu(a) b_{e_k}
+    exactly, which checks that each route reaches its own expert and its own
+    slot's gate."""
+    cfg = small_cfg(shared_inter=0)
+    layer, x = layer_and_x(cfg)
+    x = x.copy()
+    x[:, 0] = W.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    E, H, I = cfg.experts, cfg.hidden, cfg.inter
+    a = 1.5
+    b = np.array([2.0 ** (e // 8 - 2) * (1 + (e % 8) / 8) for e in range(E)])
+    w13 = np.zeros((E, 2 * I, H))
+    w13[:, :I, 0] = a
+    w13[:, I:, 0] = b[:, None]
+    w2 = np.zeros((E, H, I))
+    w2[:, :, 0] = 1.0
+    layer["w13"] = W.f32_to_bf16_bits(w13.astype(np.float32))
+    layer["w2"] = W.f32_to_bf16_bits(w2.astype(np.float32))
+    assert np.array_equal(O.bf16_to_f64(layer["w13"]), w13)
+    fwd = O.forward(layer, x, cfg.top_k)
+    c = a / (1 + np.exp(-a)) * b
+    expect = (fwd["gates"] * c[fwd["idx"]]).sum(axis=1)
+    assert np.max(np.abs(fwd["out"] - expect[:, None])) <= 1e-12
+
+
+# ---------------------------------------------------------------- P6 invariants
+def test_routing_and_permutation_invariants():
+    cfg = W.CONFIGS["tiny"]
+    layer, x = layer_and_x(cfg)
+    fwd = O.forward(layer, x, cfg.top_k)
+    idx, g = fwd["idx"], fwd["gates"]
+    T, K, E = cfg.tokens, cfg.top_k, cfg.experts
+    assert all(len(set(row)) == K for row in idx.tolist())
+    assert np.max(np.abs(g.sum(axis=1) - 1.0)) <= 1e-12
+    assert np.all(np.diff(g, axis=1) <= 0)       # slot 0 is the largest
+    off, srt, pos = fwd["expert_offsets"], fwd["sorted_route"], fwd["route_pos"]
+    assert off[0] == 0 and off[-1] == T * K and np.all(np.diff(off) >= 0)
+    assert np.array_equal(np.sort(srt), np.arange(T * K))
+    assert np.array_equal(pos[srt], np.arange(T * K))
+    flat = idx.reshape(-1)
+    for e in range(E):
+        seg = srt[off[e]: off[e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg) > 0)          # ascending route id inside a segment
+
+
+def test_selection_matches_brute_force_ranking_on_random_logits():
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((64, 512))
+    logits[3, 10] = logits[3, 400]               # exact tie
+    idx = O.select_routes(logits, 10)
+    for t in range(64):
+        ranked = sorted(range(512), key=lambda e: (-np.float32(logits[t, e]), e))[:10]
+        assert list(idx[t]) == ranked
+
+
+# ---------------------------------------------------------------- P7 backward
+def _loss(layer, x, d_out, idx, top_k):
+    fwd = O.forward(layer, x, top_k, forced_idx=idx)
+    return float(np.sum(O.bf16_to_f64(d_out) * fwd["out"]))
+
+
+def _tiny_float_layer():
+    cfg = small_cfg(tokens=6, hidden=16, experts=8, top_k=3, inter=8, shared_inter=8)
+    layer, x = layer_and_x(cfg)
+    f = {k: (O.bf16_to_f64(v) if v is not None and v.dtype == np.uint16 else v) for k, v in layer.items()}
+    f["w_router"] = layer["w_router"].astype(np.float64) * 20.0   # spread the gates
+    return cfg, f, O.bf16_to_f64(x), W.grad_out(cfg)
+
+
+@pytest.mark.parametrize("name", ["w_router", "w13", "w2", "ws13", "ws2", "w_sgate", "x"])
+def test_backward_matches_central_differences(name):
+    cfg, layer, x, d_out = _tiny_float_layer()
+    fwd = O.forward(layer, x, cfg.top_k)
+    idx = fwd["idx"]
+    grads = O.backward(layer, x, fwd, d_out)
+    key = {"x": "dx", "w_router": "d_w_router"}.get(name, "d_" + name)
+    g = grads[key]
+    base = x if name == "x" else layer[name]
+    rng = np.random.default_rng(1)
+    flat_ids = rng.choice(base.size, size=min(24, base.size), replace=False)
+    h = 1e-6
+    for fi in flat_ids:
+        pert = base.copy().reshape(-1)
+        orig = pert[fi]
+        vals = []
+        for s in (+1, -1):
+            pert[fi] = orig + s * h
+            arr = pert.reshape(base.shape)
+            if name == "x":
+                vals.append(_loss(layer, arr, d_out, idx, cfg.top_k))
+            else:
+                lay = dict(layer)
+                lay[name] = arr
+                vals.append(_loss(lay, x, d_out, idx, cfg.top_k))
+        fd = (vals[0] - vals[1]) / (2 * h)
+        an = g.reshape(-1)[fi]
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fi, fd, an)
+
+
+def test_backward_matches_torch_float64_autograd():
+    torch = pytest.importorskip("torch")
+    cfg, layer, x, d_out = _tiny_float_layer()
+    fwd = O.forward(layer, x, cfg.top_k)
+    idx = fwd["idx"]
+    grads = O.backward(layer, x, fwd, d_out)
+    T = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    tx, twr, tw13, tw2 = T(x), T(layer["w_router"]), T(layer["w13"]), T(layer["w2"])
+    tws13, tws2, twsg = T(layer["ws13"]), T(layer["ws2"]), T(layer["w_sgate"])
+    I = cfg.inter
+    logits = tx @ twr.T
+    sel = torch.gather(logits, 1, torch.tensor(idx, dtype=torch.int64))
+    gates = torch.softmax(sel, dim=1)
+    out = torch.zeros(cfg.tokens, cfg.hidden, dtype=torch.float64)
+    for t in range(cfg.tokens):
+        for k in range(cfg.top_k):
+            e = int(idx[t, k])
+            h = tw13[e] @ tx[t]
+            act = torch.nn.functional.silu(h[:I]) * h[I:]
+            out[t] = out[t] + gates[t, k] * (tw2[e] @ act)
+    hs = tx @ tws13.T
+    s = (torch.nn.functional.silu(hs[:, :I]) * hs[:, I:]) @ tws2.T
+    out = out + torch.sigmoid(tx @ twsg)[:, None] * s
+    (out * torch.tensor(O.bf16_to_f64(d_out))).sum().backward()
+    pairs = [("dx", tx), ("d_w_router", twr), ("d_w13", tw13), ("d_w2", tw2),
+             ("d_ws13", tws13), ("d_ws2", tws2), ("d_w_sgate", twsg)]
+    assert np.max(np.abs(fwd["out"] - out.detach().numpy())) <= 1e-12
+    for key, tt in pairs:
+        assert np.max(np.abs(grads[key] - tt.grad.numpy())) <= 1e-12, key
+
+
+def test_expert_weight_grads_match_full_backward():
+    cfg, layer, x, d_out = _tiny_float_layer()
+    fwd = O.forward(layer, x, cfg.top_k)
+    grads = O.backward(layer, x, fwd, d_out)
+    flat = fwd["idx"].reshape(-1)
+    for e in np.unique(flat):
+        rows = np.nonzero(flat == e)[0]
+        dw13, dw2 = O.expert_weight_grads(layer, x, d_out, fwd["idx"], fwd["gates"], fwd["gu"][rows], int(e))
+        assert np.max(np.abs(dw13 - grads["d_w13"][e])) <= 1e-13
+        assert np.max(np.abs(dw2 - grads["d_w2"][e])) <= 1e-13
+
+
+# ---------------------------------------------------------------- subsets and bf16 report
+def test_token_subset_equals_full_rows():
+    cfg = small_cfg()
+    layer, x = layer_and_x(cfg)
+    full = O.forward(layer, x, cfg.top_k)
+    sub = [0, 5, 23, 11]
+    part = O.forward(layer, x, cfg.top_k, tokens=sub)
+    assert np.array_equal(part["idx"], full["idx"][sub])
+    # BLAS may block a float64 product differently for a different row count
+    assert np.max(np.abs(part["out"] - full["out"][sub])) <= 1e-15
+    K = cfg.top_k
+    rows = np.concatenate([np.arange(t * K, t * K + K) for t in sub])
+    assert np.max(np.abs(part["y"] - full["y"][rows])) <= 1e-15
+
+
+def test_bf16_round_trip_and_rounding():
+    vals = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -9, -2.5, 3.0e-3])
+    bits = O.f64_to_bf16_bits(vals)
+    back = O.bf16_to_f64(bits)
+    assert back[0] == 1.0
+    assert back[1] == 1.0                # tie -> even
+    assert back[2] == 1.0 + 2.0 ** -7    # above the half-way point -> up
+    assert back[3] == -2.5
+    # half an ulp of the binade [2^-9, 2^-8): 2^-9 * 2^-8
+    assert abs(back[4] - 3.0e-3) <= 2.0 ** -17
