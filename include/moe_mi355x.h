@@ -1,0 +1,220 @@
+/*
+ * moe_mi355x.h -- C ABI of a deterministic, batch-invariant routed
+ * mixture-of-experts layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one described on the RL-Kernel pull request 557 page
+ * (Qwen3-Next EP4 distributed logprob parity), in the commit message of its
+ * stack entry "MoE route/combine contract with a batch-invariant grouped
+ * expert GEMM", with the model shape of the SkyRL pull request 2513 page
+ * (section "What": 512 routed experts, top-10, a shared expert):
+ *
+ *   route    FP32 router projection, softmax, stable descending top-k with
+ *            ties to the lower expert id, FP32 renormalisation of the
+ *            selected gates                       (contract, Routing bullet)
+ *   permute  counting sort of the token-routes by expert    (page "What":
+ *            dispatch is a local selection of each expert's routes)
+ *   ffn      per-route gate_up and down projections with one fixed tile
+ *            configuration, no gate multiply and no sum inside, exactly one
+ *            writer per (token, route) row              (Experts bullet)
+ *   combine  the route terms summed in FP32 in route order, one cast to
+ *            BF16, no atomics                          (Combine bullet)
+ *   backward per-expert weight gradients into dense buffers, each token's
+ *            input gradient summed over its routes in ascending expert id
+ *                                                        (Backward bullet)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Dimensions: T tokens, H hidden, E experts, K routes per token, I expert
+ *    intermediate size, Is shared-expert intermediate size (0 = no shared
+ *    expert).  R = T*K route rows.  Route id r = t*K + k (slot k of token t).
+ *  - bf16 tensors are passed as uint16_t bit patterns.  All tensors are
+ *    dense, row-major, in device memory, 16-byte aligned.
+ *  - Ownership: the caller owns every buffer.  The library never allocates,
+ *    frees or keeps a pointer past the call, and never synchronises the
+ *    stream.  All work is enqueued on `stream` in call order.
+ *  - Outputs are fully overwritten; nothing accumulates into caller memory.
+ *  - Errors: every call validates its arguments on the host before it
+ *    enqueues anything; on failure it returns a non-zero status and has
+ *    enqueued nothing (fail closed).  Bad data found on the device (a
+ *    caller-supplied expert id out of range or repeated within a token) sets
+ *    a sticky error word in the workspace, read by moe_last_device_error().
+ *  - Supported sizes: E % 64 == 0 and 64 <= E <= 1024; 1 <= K <= 16 and
+ *    K <= E; H % 256 == 0, 256 <= H <= 16384; I % 128 == 0, 128 <= I <= 4096;
+ *    Is == 0 or the same rule as I; 0 <= T and T*K < 2^31.  T == 0 returns
+ *    MOE_OK and enqueues nothing.
+ *  - Determinism: every output is a pure function of the inputs, identical
+ *    bit for bit across runs, streams and batch compositions: a token's
+ *    routes, gates, route rows, output and input gradient do not depend on
+ *    the other tokens in the batch or on its position.  Weight gradients are
+ *    sums over the batch: deterministic, but naturally batch-dependent.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_E_NULL = 1,        /* a required pointer is NULL                         */
+  MOE_E_SHAPE = 2,       /* a dimension is out of the supported range          */
+  MOE_E_UNSUPPORTED = 3, /* a valid but unsupported combination                */
+  MOE_E_ALIGN = 4,       /* a pointer is not 16-byte aligned                   */
+  MOE_E_WORKSPACE = 5,   /* workspace NULL or smaller than moe_workspace_bytes */
+  MOE_E_DEVICE = 6,      /* current device is not gfx950, or device data error */
+  MOE_E_LAUNCH = 7,      /* a kernel launch failed                             */
+  MOE_E_ALIAS = 8        /* an output overlaps an input or another output      */
+};
+
+/* operation ids for moe_workspace_bytes */
+enum moe_op {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_FFN = 2,
+  MOE_OP_FORWARD = 3,
+  MOE_OP_BACKWARD = 4
+};
+
+typedef struct moe_dims {
+  int64_t tokens;       /* T */
+  int32_t hidden;       /* H */
+  int32_t experts;      /* E */
+  int32_t top_k;        /* K */
+  int32_t inter;        /* I  */
+  int32_t shared_inter; /* Is (0: no shared expert) */
+} moe_dims;
+
+typedef struct moe_weights {
+  const float* w_router;    /* [E][H] fp32                                   */
+  const float* router_bias; /* [E] fp32 added to the logits, or NULL          */
+  const uint16_t* w13;      /* [E][2I][H] bf16: rows 0..I-1 gate, I..2I-1 up  */
+  const uint16_t* w2;       /* [E][H][I] bf16                                 */
+  const uint16_t* ws13;     /* [2Is][H] bf16 shared gate/up (NULL iff Is==0)  */
+  const uint16_t* ws2;      /* [H][Is] bf16 shared down (NULL iff Is==0)      */
+  const uint16_t* w_sgate;  /* [H] bf16 shared-expert gate (NULL iff Is==0)   */
+} moe_weights;
+
+typedef struct moe_routes {
+  int32_t* topk_idx;       /* [T][K] expert id of slot k, slot 0 the largest */
+  float* topk_gate;        /* [T][K] renormalised gate of slot k             */
+  float* logits;           /* [T][E] fp32 router logits, or NULL             */
+  int32_t* expert_offsets; /* [E+1] start of expert e's segment; [E] = R     */
+  int32_t* sorted_route;   /* [R] route ids sorted by (expert, route id)     */
+  int32_t* route_pos;      /* [R] inverse: sorted_route[route_pos[r]] == r   */
+} moe_routes;
+
+typedef struct moe_saved {
+  float* y;           /* [R][H] fp32 expert output of route r (row r=t*K+k)   */
+  float* gu;          /* [R][2I] fp32 gate|up pre-activations, row = sorted
+                         position p (NULL: not saved, forward-only)          */
+  float* shared_y;    /* [T][H] fp32 shared-expert output (Is>0)             */
+  float* shared_gate; /* [T] fp32 sigmoid(w_sgate . x) (Is>0)                */
+  float* shared_gu;   /* [T][2Is] fp32 shared gate|up (NULL: not saved)      */
+} moe_saved;
+
+typedef struct moe_grads {
+  float* d_w_router; /* [E][H]      */
+  float* d_w13;      /* [E][2I][H]  */
+  float* d_w2;       /* [E][H][I]   */
+  float* d_ws13;     /* [2Is][H]    (Is>0) */
+  float* d_ws2;      /* [H][Is]     (Is>0) */
+  float* d_w_sgate;  /* [H]         (Is>0) */
+} moe_grads;
+
+/* MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* moe_status_str(int status);
+
+/* Bytes of device workspace the operation `op` (enum moe_op) needs for these
+ * dims; 0 if the dims are invalid.  The workspace is scratch owned by the
+ * caller; its contents between calls carry only the sticky device-error
+ * word.  Size it once per shape; a workspace sized for MOE_OP_BACKWARD also
+ * serves every other operation at the same dims. */
+size_t moe_workspace_bytes(const moe_dims* dims, int op);
+
+/* Route (contract, Routing bullet).
+ * x [T][H] bf16.  Writes logits (if routes->logits != NULL), topk_idx and
+ * topk_gate.  The router logit l[t][e] = sum_h x[t][h] * w_router[e][h]
+ * (+ router_bias[e]) is formed with exact bf16 x fp32 products (the fp32
+ * weight split into three bf16 parts on the matrix cores), summed in
+ * fixed 64-wide chunks in fp32 and across chunks in fp64, then rounded to
+ * fp32.  Selection compares those fp32 logits (greater first, equal values
+ * to the lower id); the gates are exp(l_k - l_0) / sum_j exp(l_j - l_0) over
+ * the selected slots, in fp32. */
+int moe_route(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
+              moe_routes* routes, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Permute (page "What": local selection of each expert's routes).
+ * Reads routes->topk_idx (from moe_route, or supplied by the caller, e.g.
+ * replayed routing) and writes expert_offsets, sorted_route and route_pos:
+ * a stable counting sort of route ids by expert (ascending route id inside
+ * each expert's segment).  Out-of-range or repeated ids within a token set
+ * the sticky device error and leave the permutation unspecified. */
+int moe_permute(const moe_dims* dims, moe_routes* routes, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* Grouped expert FFN (contract, Experts bullet).
+ * For each route r of expert e: gu = W13_e x[t] (fp32 accumulation of exact
+ * bf16 products, fixed K order), act = silu(gate) * up in fp32, passed to
+ * the down projection as a bf16 hi/lo pair, y = W2_e act accumulated in fp32
+ * and written to saved->y row r; one writer per row, no gate multiply.  The
+ * shared expert (Is > 0) runs through the same kernels on all T tokens and
+ * writes saved->shared_y, and saved->shared_gate = sigmoid(w_sgate . x).
+ * Needs the permutation of moe_permute.  saved->gu / shared_gu are written
+ * when non-NULL (needed by moe_backward). */
+int moe_grouped_ffn(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
+                    const moe_routes* routes, moe_saved* saved, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Combine (contract, Combine bullet).
+ * out[t] = fma chain over k = 0..K-1 of topk_gate[t][k] * y[t*K+k] starting
+ * from +0, then one more fma with shared_gate[t] * shared_y[t] (Is > 0),
+ * all in fp32; out_f32 gets that value, out_bf16 its round-to-nearest-even
+ * bf16.  Either output may be NULL, not both.  No atomics. */
+int moe_combine(const moe_dims* dims, const moe_routes* routes, const moe_saved* saved,
+                float* out_f32, uint16_t* out_bf16, hipStream_t stream);
+
+/* Whole forward: route, permute, grouped FFN, combine, in that order on
+ * `stream`.  routes->logits may be NULL (the workspace holds them). */
+int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                moe_routes* routes, moe_saved* saved, float* out_f32, uint16_t* out_bf16,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward (contract, Backward bullet).
+ * Inputs: the forward's x, routes and saved tensors (saved->gu, and
+ * saved->shared_gu when Is > 0, must have been written), d_out [T][H] bf16.
+ * Outputs: d_x_f32 [T][H] (and its bf16 rounding in d_x_bf16 if non-NULL)
+ * and every weight gradient in `grads` (fp32, overwritten).
+ *   dg[t][k] = <d_out[t], y[t*K+k]>   (fixed per-token reduction order)
+ *   dl = g * (dg - sum_j g_j dg_j)     (softmax backward over selected slots)
+ *   route r: dy = g * d_out[t]; dact = dy W2_e; SwiGLU backward -> dgu;
+ *            dx_r = dgu W13_e; dW2_e = sum_r dy^T act; dW13_e = sum_r dgu^T x
+ *   shared:  dz = <d_out, shared_y> sg (1 - sg); dw_sgate = sum_t dz x;
+ *            same expert backward with dy = sg * d_out
+ *   router:  d_w_router[e] = sum_t dl[t][e] x[t];  dx_router = sum_k dl W_r
+ *   d_x[t] = ((sum of dx_r over its routes in ascending expert id) +
+ *            dx_shared) + dz * w_sgate + dx_router, in that order, fp32.
+ * Weight-gradient sums run over routes (tokens) in ascending order; no
+ * atomics anywhere. */
+int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                 const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
+                 float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws,
+                 size_t ws_bytes, hipStream_t stream);
+
+/* Synchronises `stream`, then returns and clears the sticky device error
+ * word of workspace `ws` (MOE_OK or MOE_E_DEVICE).  Debug/validation use. */
+int moe_last_device_error(void* ws, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,441 @@
+// Host side of the C ABI declared in include/moe_mi355x.h: argument
+// validation (everything is checked before anything is enqueued), workspace
+// layout and the launch sequence of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/moe_mi355x.h"
+#include "moe_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// ---------------------------------------------------------------------------
+// workspace layout (byte offsets from the workspace base)
+// ---------------------------------------------------------------------------
+struct Layout {
+  size_t err = 0;         // int error word (first 256 bytes)
+  size_t logits = 0;      // [T][E] f32 when the caller passes no logits buffer
+  size_t hist = 0;        // [NB][E+1] i32
+  size_t block_base = 0;  // [NB][E] i32
+  size_t tiles = 0;       // [2*max_tiles] i32
+  size_t meta = 0;        // [64] i32
+  size_t act_hi = 0, act_lo = 0;    // [R][I] bf16
+  size_t sact_hi = 0, sact_lo = 0;  // [T][Is] bf16
+  size_t fwd_end = 0;
+  size_t bwd_end = 0;
+  int nblocks = 0;
+  int max_tiles = 0;
+};
+
+Layout make_layout(const moe_dims& d) {
+  Layout L;
+  const int64_t T = d.tokens, R = T * d.top_k;
+  const int E = d.experts, I = d.inter, Is = d.shared_inter;
+  L.nblocks = static_cast<int>((T + moe::kSortBlock - 1) / moe::kSortBlock);
+  L.max_tiles = static_cast<int>(moe::max_row_tiles(T, d.top_k, E, Is > 0));
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.err = take(kAlign);
+  L.logits = take(static_cast<size_t>(T) * E * 4);
+  L.hist = take(static_cast<size_t>(L.nblocks) * (E + 1) * 4);
+  L.block_base = take(static_cast<size_t>(L.nblocks) * E * 4);
+  L.tiles = take(static_cast<size_t>(L.max_tiles) * 2 * 4);
+  L.meta = take(64 * 4);
+  L.act_hi = take(static_cast<size_t>(R) * I * 2);
+  L.act_lo = take(static_cast<size_t>(R) * I * 2);
+  L.sact_hi = take(static_cast<size_t>(T) * Is * 2);
+  L.sact_lo = take(static_cast<size_t>(T) * Is * 2);
+  L.fwd_end = o;
+  L.bwd_end = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+int check_dims(const moe_dims* d) {
+  if (!d) return MOE_E_NULL;
+  if (d->tokens < 0) return MOE_E_SHAPE;
+  if (d->experts < 64 || d->experts > 1024 || d->experts % 64) return MOE_E_SHAPE;
+  if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->experts) return MOE_E_SHAPE;
+  if (d->hidden < 256 || d->hidden > 16384 || d->hidden % 256) return MOE_E_SHAPE;
+  if (d->inter < 128 || d->inter > 4096 || d->inter % 128) return MOE_E_SHAPE;
+  if (d->shared_inter != 0 &&
+      (d->shared_inter < 128 || d->shared_inter > 4096 || d->shared_inter % 128))
+    return MOE_E_SHAPE;
+  if (d->tokens * static_cast<int64_t>(d->top_k) >= (int64_t{1} << 31)) return MOE_E_SHAPE;
+  return MOE_OK;
+}
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+  bool out;
+};
+
+// Collects the buffers of one call, then checks presence, alignment and
+// overlap (an output may overlap nothing else).
+class Args {
+ public:
+  void in(const void* p, size_t bytes, bool required = true) { add(p, bytes, false, required); }
+  void out(const void* p, size_t bytes, bool required = true) { add(p, bytes, true, required); }
+  int status() const {
+    if (null_) return MOE_E_NULL;
+    if (misaligned_) return MOE_E_ALIGN;
+    for (size_t a = 0; a < bufs_.size(); ++a) {
+      for (size_t b = a + 1; b < bufs_.size(); ++b) {
+        if (!bufs_[a].out && !bufs_[b].out) continue;
+        const auto pa = reinterpret_cast<uintptr_t>(bufs_[a].p);
+        const auto pb = reinterpret_cast<uintptr_t>(bufs_[b].p);
+        if (pa < pb + bufs_[b].bytes && pb < pa + bufs_[a].bytes) return MOE_E_ALIAS;
+      }
+    }
+    return MOE_OK;
+  }
+
+ private:
+  void add(const void* p, size_t bytes, bool out, bool required) {
+    if (!p) {
+      if (required && bytes) null_ = true;
+      return;
+    }
+    if (reinterpret_cast<uintptr_t>(p) % 16) misaligned_ = true;
+    if (bytes) bufs_.push_back({p, bytes, out});
+  }
+  std::vector<Buf> bufs_;
+  bool null_ = false;
+  bool misaligned_ = false;
+};
+
+int check_ws(const moe_dims& d, const void* ws, size_t ws_bytes, int op) {
+  if (!ws) return MOE_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_E_ALIGN;
+  if (ws_bytes < moe_workspace_bytes(&d, op)) return MOE_E_WORKSPACE;
+  return MOE_OK;
+}
+
+// gfx950 check of the current device, cached per device id.
+int check_device() {
+  static std::mutex mu;
+  static std::vector<int> verdict;  // 0 unknown, 1 ok, 2 bad
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return MOE_E_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<size_t>(dev) >= verdict.size()) verdict.resize(dev + 1, 0);
+  if (verdict[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_E_DEVICE;
+    }
+    verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return verdict[dev] == 1 ? MOE_OK : MOE_E_DEVICE;
+}
+
+#define MOE_TRY(expr)                       \
+  do {                                      \
+    const int _st = (expr);                 \
+    if (_st != MOE_OK) return _st;          \
+  } while (0)
+
+#define MOE_LAUNCH(expr)                            \
+  do {                                              \
+    if ((expr) != hipSuccess) return MOE_E_LAUNCH;  \
+  } while (0)
+
+size_t bytes_x(const moe_dims& d) { return static_cast<size_t>(d.tokens) * d.hidden * 2; }
+
+void add_weights(Args& a, const moe_dims& d, const moe_weights* w, bool router, bool experts) {
+  const size_t E = d.experts, H = d.hidden, I = d.inter, Is = d.shared_inter;
+  if (router) {
+    a.in(w->w_router, E * H * 4);
+    a.in(w->router_bias, E * 4, false);
+  }
+  if (experts) {
+    a.in(w->w13, E * 2 * I * H * 2);
+    a.in(w->w2, E * H * I * 2);
+    if (Is) {
+      a.in(w->ws13, 2 * Is * H * 2);
+      a.in(w->ws2, H * Is * 2);
+      a.in(w->w_sgate, H * 2);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch sequences (arguments already validated)
+// ---------------------------------------------------------------------------
+int run_route(const moe_dims& d, const uint16_t* x, const moe_weights* w, moe_routes* r, void* ws,
+              const Layout& L, hipStream_t s) {
+  float* logits = r->logits ? r->logits : at<float>(ws, L.logits);
+  MOE_LAUNCH(moe::launch_router_logits(x, w->w_router, w->router_bias, logits, d.tokens, d.hidden,
+                                       d.experts, s));
+  MOE_LAUNCH(moe::launch_topk_gate(logits, r->topk_idx, r->topk_gate, d.tokens, d.experts, d.top_k, s));
+  return MOE_OK;
+}
+
+int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hipStream_t s) {
+  MOE_LAUNCH(moe::launch_route_hist(r->topk_idx, at<int32_t>(ws, L.hist), r->route_pos, d.tokens,
+                                    d.experts, d.top_k, s));
+  MOE_LAUNCH(moe::launch_route_scan(at<int32_t>(ws, L.hist), at<int32_t>(ws, L.block_base),
+                                    r->expert_offsets, at<int32_t>(ws, L.tiles),
+                                    at<int32_t>(ws, L.meta), L.nblocks, d.experts, d.tokens,
+                                    d.shared_inter > 0, at<int>(ws, L.err), s));
+  MOE_LAUNCH(moe::launch_route_scatter(r->topk_idx, at<int32_t>(ws, L.block_base),
+                                       r->expert_offsets, r->route_pos, r->sorted_route, d.tokens,
+                                       d.experts, d.top_k, s));
+  return MOE_OK;
+}
+
+// tiles_ready: the work list in the workspace was built by run_permute.
+int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const moe_routes* r,
+            moe_saved* sv, void* ws, const Layout& L, bool tiles_ready, hipStream_t s) {
+  const int has_shared = d.shared_inter > 0;
+  if (!tiles_ready)
+    MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles),
+                                     at<int32_t>(ws, L.meta), d.experts, d.tokens, has_shared, s));
+  if (has_shared)
+    MOE_LAUNCH(moe::launch_shared_gate(x, w->w_sgate, sv->shared_gate, d.tokens, d.hidden, s));
+  MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, r->expert_offsets, r->sorted_route,
+                                at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta),
+                                at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
+                                at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), sv->gu,
+                                has_shared ? sv->shared_gu : nullptr, d.tokens, d.hidden,
+                                d.experts, d.top_k, d.inter, d.shared_inter, L.max_tiles, s));
+  MOE_LAUNCH(moe::launch_ffn_down(at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
+                                  at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), w->w2,
+                                  w->ws2, r->expert_offsets, r->sorted_route,
+                                  at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta), sv->y,
+                                  has_shared ? sv->shared_y : nullptr, d.tokens, d.hidden,
+                                  d.experts, d.top_k, d.inter, d.shared_inter, L.max_tiles, s));
+  return MOE_OK;
+}
+
+int run_combine(const moe_dims& d, const moe_routes* r, const moe_saved* sv, float* o32,
+                uint16_t* o16, hipStream_t s) {
+  const bool sh = d.shared_inter > 0;
+  MOE_LAUNCH(moe::launch_combine(sv->y, r->topk_gate, sh ? sv->shared_y : nullptr,
+                                 sh ? sv->shared_gate : nullptr, o32, o16, d.tokens, d.hidden,
+                                 d.top_k, s));
+  return MOE_OK;
+}
+
+// buffer registration per stage
+void add_routes_out(Args& a, const moe_dims& d, const moe_routes* r) {
+  const size_t T = d.tokens, K = d.top_k, E = d.experts;
+  a.out(r->topk_idx, T * K * 4);
+  a.out(r->topk_gate, T * K * 4);
+  a.out(r->logits, T * E * 4, false);
+}
+
+void add_perm_out(Args& a, const moe_dims& d, const moe_routes* r) {
+  const size_t T = d.tokens, K = d.top_k, E = d.experts;
+  a.out(r->expert_offsets, (E + 1) * 4);
+  a.out(r->sorted_route, T * K * 4);
+  a.out(r->route_pos, T * K * 4);
+}
+
+void add_saved(Args& a, const moe_dims& d, const moe_saved* sv, bool out) {
+  const size_t T = d.tokens, K = d.top_k, H = d.hidden, I = d.inter, Is = d.shared_inter;
+  auto add = [&](const void* p, size_t b, bool req) { out ? a.out(p, b, req) : a.in(p, b, req); };
+  add(sv->y, T * K * H * 4, true);
+  add(sv->gu, T * K * 2 * I * 4, false);
+  if (Is) {
+    add(sv->shared_y, T * H * 4, true);
+    add(sv->shared_gate, T * 4, true);
+    add(sv->shared_gu, T * 2 * Is * 4, false);
+  }
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_E_NULL: return "required pointer is NULL";
+    case MOE_E_SHAPE: return "dimension out of the supported range";
+    case MOE_E_UNSUPPORTED: return "unsupported combination";
+    case MOE_E_ALIGN: return "pointer not 16-byte aligned (workspace: 256-byte)";
+    case MOE_E_WORKSPACE: return "workspace missing or too small";
+    case MOE_E_DEVICE: return "device is not gfx950, or device data error";
+    case MOE_E_LAUNCH: return "kernel launch failed";
+    case MOE_E_ALIAS: return "an output overlaps another buffer";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_dims* dims, int op) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  const Layout L = make_layout(*dims);
+  switch (op) {
+    case MOE_OP_ROUTE:
+    case MOE_OP_PERMUTE:
+    case MOE_OP_FFN:
+    case MOE_OP_FORWARD: return L.fwd_end;
+    case MOE_OP_BACKWARD: return L.bwd_end;
+    default: return 0;
+  }
+}
+
+int moe_route(const moe_dims* dims, const uint16_t* x, const moe_weights* w, moe_routes* routes,
+              void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!w || !routes) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  Args a;
+  a.in(x, bytes_x(d));
+  add_weights(a, d, w, true, false);
+  add_routes_out(a, d, routes);
+  a.in(ws, moe_workspace_bytes(dims, MOE_OP_ROUTE), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_ROUTE));
+  MOE_TRY(check_device());
+  return run_route(d, x, w, routes, ws, make_layout(d), stream);
+}
+
+int moe_permute(const moe_dims* dims, moe_routes* routes, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!routes) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  Args a;
+  a.in(routes->topk_idx, static_cast<size_t>(d.tokens) * d.top_k * 4);
+  add_perm_out(a, d, routes);
+  a.in(ws, moe_workspace_bytes(dims, MOE_OP_PERMUTE), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_PERMUTE));
+  MOE_TRY(check_device());
+  return run_permute(d, routes, ws, make_layout(d), stream);
+}
+
+int moe_grouped_ffn(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
+                    const moe_routes* routes, moe_saved* saved, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!w || !routes || !saved) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, K = d.top_k, E = d.experts;
+  Args a;
+  a.in(x, bytes_x(d));
+  add_weights(a, d, w, false, true);
+  a.in(routes->expert_offsets, (E + 1) * 4);
+  a.in(routes->sorted_route, T * K * 4);
+  add_saved(a, d, saved, true);
+  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FFN), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FFN));
+  MOE_TRY(check_device());
+  return run_ffn(d, x, w, routes, saved, ws, make_layout(d), false, stream);
+}
+
+int moe_combine(const moe_dims* dims, const moe_routes* routes, const moe_saved* saved,
+                float* out_f32, uint16_t* out_bf16, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!routes || !saved) return MOE_E_NULL;
+  if (!out_f32 && !out_bf16) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, K = d.top_k, H = d.hidden;
+  Args a;
+  a.in(routes->topk_gate, T * K * 4);
+  a.in(saved->y, T * K * H * 4);
+  if (d.shared_inter) {
+    a.in(saved->shared_y, T * H * 4);
+    a.in(saved->shared_gate, T * 4);
+  }
+  a.out(out_f32, T * H * 4, false);
+  a.out(out_bf16, T * H * 2, false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_device());
+  return run_combine(d, routes, saved, out_f32, out_bf16, stream);
+}
+
+int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, moe_routes* routes,
+                moe_saved* saved, float* out_f32, uint16_t* out_bf16, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!w || !routes || !saved) return MOE_E_NULL;
+  if (!out_f32 && !out_bf16) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, H = d.hidden;
+  Args a;
+  a.in(x, bytes_x(d));
+  add_weights(a, d, w, true, true);
+  add_routes_out(a, d, routes);
+  add_perm_out(a, d, routes);
+  add_saved(a, d, saved, true);
+  a.out(out_f32, T * H * 4, false);
+  a.out(out_bf16, T * H * 2, false);
+  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FORWARD), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD));
+  MOE_TRY(check_device());
+  const Layout L = make_layout(d);
+  MOE_TRY(run_route(d, x, w, routes, ws, L, stream));
+  MOE_TRY(run_permute(d, routes, ws, L, stream));
+  MOE_TRY(run_ffn(d, x, w, routes, saved, ws, L, true, stream));
+  return run_combine(d, routes, saved, out_f32, out_bf16, stream);
+}
+
+int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                 const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
+                 float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  (void)w;
+  (void)x;
+  (void)routes;
+  (void)saved;
+  (void)d_out;
+  (void)d_x_f32;
+  (void)d_x_bf16;
+  (void)grads;
+  (void)ws;
+  (void)ws_bytes;
+  (void)stream;
+  return MOE_E_UNSUPPORTED;
+}
+
+int moe_last_device_error(void* ws, hipStream_t stream) {
+  if (!ws) return MOE_E_WORKSPACE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOE_E_LAUNCH;
+  int v = 0;
+  if (hipMemcpy(&v, ws, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return MOE_E_LAUNCH;
+  return v ? MOE_E_DEVICE : MOE_OK;
+}
+
+}  // extern "C"

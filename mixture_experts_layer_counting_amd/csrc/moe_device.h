@@ -1,0 +1,79 @@
+// Device helpers shared by the gfx950 kernels of the routed MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+// Routed rows per grouped-GEMM work item (four 32-row MFMA blocks).
+constexpr int kRowsPerTile = 128;
+// Activation columns per up-projection work item (four waves x 32).
+constexpr int kUpCols = 128;
+// Hidden columns per down-projection work item (four waves x 64).
+constexpr int kDownCols = 256;
+// Tokens per block of the permutation's counting sort.
+constexpr int kSortBlock = 256;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+__device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+// D = A(32x16) * B(16x32) + C on the matrix cores, bf16 inputs, fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32) .. +8] and B[8*(l/32) .. +8][l%32]; it holds
+// D[8*(v/4) + 4*(l/32) + v%4][l%32] in element v.
+__device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator that element v of lane `half` (= lane/32) holds.
+__device__ __forceinline__ int acc_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) z[v] = 0.f;
+  return z;
+}
+
+// Split a float into the bf16 pair (hi, lo) with hi = bf16(a), lo = bf16(a - hi).
+__device__ __forceinline__ void split_hi_lo(float a, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(a);
+  lo = f32_to_bf16(a - bf16_to_f32(hi));
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// XCD-aware mapping of a 1-D grid onto `items` work items.  The hardware
+// deals workgroups round-robin over the 8 XCDs (workgroup g runs on XCD g%8);
+// this gives each XCD one contiguous range of items, so items that share
+// operands (the N-tiles of one row tile, the row tiles of one expert) meet in
+// the same L2.  Returns -1 for workgroups with no item.
+__device__ __forceinline__ int xcd_item(int g, int items) {
+  const int per = (items + 7) >> 3;
+  const int xcd = g & 7, slot = g >> 3;
+  if (slot >= per) return -1;
+  const int it = xcd * per + slot;
+  return it < items ? it : -1;
+}
+
+}  // namespace moe

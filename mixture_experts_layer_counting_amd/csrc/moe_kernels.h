@@ -1,0 +1,51 @@
+// Kernel launchers of the routed MoE layer.  Each launcher enqueues one
+// kernel on `stream` and returns hipGetLastError(); callers have validated
+// every size and pointer before.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_device.h"
+
+namespace moe {
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias,
+                                float* logits, int64_t T, int H, int E, hipStream_t stream);
+hipError_t launch_topk_gate(const float* logits, int32_t* topk_idx, float* topk_gate, int64_t T,
+                            int E, int K, hipStream_t stream);
+hipError_t launch_route_hist(const int32_t* topk_idx, int32_t* hist, int32_t* route_rank,
+                             int64_t T, int E, int K, hipStream_t stream);
+hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* offsets,
+                             int32_t* tiles, int32_t* meta, int nblocks, int E, int64_t T,
+                             int has_shared, int* err_word, hipStream_t stream);
+hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* meta, int E, int64_t T,
+                            int has_shared, hipStream_t stream);
+hipError_t launch_route_scatter(const int32_t* topk_idx, const int32_t* block_base,
+                                const int32_t* offsets, int32_t* route_pos, int32_t* sorted_route,
+                                int64_t T, int E, int K, hipStream_t stream);
+hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* w_sgate, float* sg, int64_t T,
+                              int H, hipStream_t stream);
+hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t* ws13,
+                         const int32_t* offsets, const int32_t* sorted_route, const int32_t* tiles,
+                         const int32_t* meta, uint16_t* act_hi, uint16_t* act_lo,
+                         uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu, int64_t T,
+                         int H, int E, int K, int I, int Is, int max_tiles, hipStream_t stream);
+hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
+                           const uint16_t* sact_hi, const uint16_t* sact_lo, const uint16_t* w2,
+                           const uint16_t* ws2, const int32_t* offsets,
+                           const int32_t* sorted_route, const int32_t* tiles,
+                           const int32_t* meta, float* y, float* sy, int64_t T, int H, int E,
+                           int K, int I, int Is, int max_tiles, hipStream_t stream);
+hipError_t launch_combine(const float* y, const float* gate, const float* sy, const float* sg,
+                          float* out32, uint16_t* out16, int64_t T, int H, int K,
+                          hipStream_t stream);
+
+// Upper bound on grouped-GEMM row tiles for T tokens: every non-empty
+// expert's last tile may be partial, plus the shared expert's tiles.
+inline int64_t max_row_tiles(int64_t T, int K, int E, int has_shared) {
+  const int64_t R = T * K;
+  return E + (R + kRowsPerTile - 1) / kRowsPerTile +
+         (has_shared ? (T + kRowsPerTile - 1) / kRowsPerTile : 0);
+}
+
+}  // namespace moe

@@ -1,0 +1,424 @@
+// Routing and permutation kernels of the routed MoE layer (gfx950).
+//
+// Routing follows the Routing bullet of the "MoE route/combine contract"
+// commit on the RL-Kernel pull request 557 page: an FP32 router, softmax,
+// stable descending selection with ties to the lower expert id, FP32
+// renormalisation of the selected gates.  The permutation is the local
+// selection of each expert's routes described in that page's "What" section,
+// done as a stable counting sort so that an expert's rows keep ascending
+// route id.
+#include "moe_kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Router logits: l[t][e] = sum_h x[t][h] * wr[e][h] (+ bias[e]).
+//
+// The fp32 weight is split exactly into three bf16 parts (hi + mid + lo), so
+// each product with the bf16 activation is exact on the matrix cores.  Each
+// 64-wide K chunk is accumulated in fp32 by 12 MFMAs (4 K-steps x 3 parts,
+// hi then mid then lo) from zero; the chunk sums are added in fp64 in
+// ascending chunk order and rounded once to fp32.  A logit's arithmetic
+// depends only on its own token row and expert row, never on the batch.
+//
+// Grid: (ceil(T/64), E/64), 256 threads.  Wave w computes tokens
+// t0 + 32*(w&1) .. +32 against experts e0 + 32*(w>>1) .. +32.
+// Inside a 64-wide chunk, lane half h and K-step s use k = 32h + 8s .. +8, so
+// every lane reads contiguous 64-byte runs of x and 128-byte runs of wr.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ wr,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ logits, int64_t T,
+                                                            int H, int E) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 31, half = lane >> 5;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 64 + 32 * (wave & 1);
+  const int e0 = blockIdx.y * 64 + 32 * (wave >> 1);
+  int64_t trow = t0 + i;
+  if (trow > T - 1) trow = T - 1;
+  const uint16_t* xr = x + trow * H + 32 * half;
+  const float* wrow = wr + static_cast<int64_t>(e0 + i) * H + 32 * half;
+
+  double acc[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0;
+
+  for (int c = 0; c < H; c += 64) {
+    u32x4_t a[4];
+    f32x4v_t w[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = ld16(xr + c + 8 * s);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = *reinterpret_cast<const f32x4v_t*>(wrow + c + 4 * q);
+    f32x16_t part = zero16();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint16_t hi[8], mid[8], lo[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float wv = w[2 * s + (r >> 2)][r & 3];
+        hi[r] = f32_to_bf16(wv);
+        const float r1 = wv - bf16_to_f32(hi[r]);
+        mid[r] = f32_to_bf16(r1);
+        lo[r] = f32_to_bf16(r1 - bf16_to_f32(mid[r]));
+      }
+      u32x4_t bh, bm, bl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bh[q] = static_cast<uint32_t>(hi[2 * q]) | (static_cast<uint32_t>(hi[2 * q + 1]) << 16);
+        bm[q] = static_cast<uint32_t>(mid[2 * q]) | (static_cast<uint32_t>(mid[2 * q + 1]) << 16);
+        bl[q] = static_cast<uint32_t>(lo[2 * q]) | (static_cast<uint32_t>(lo[2 * q + 1]) << 16);
+      }
+      part = mfma32x32x16(a[s], bh, part);
+      part = mfma32x32x16(a[s], bm, part);
+      part = mfma32x32x16(a[s], bl, part);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] += static_cast<double>(part[v]);
+  }
+
+  const int e = e0 + i;
+  const double b = bias ? static_cast<double>(bias[e]) : 0.0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t t = t0 + acc_row(v, half);
+    if (t < T) logits[t * E + e] = static_cast<float>(acc[v] + b);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k selection and gates, one wave per token.
+// Lane l holds logits l, l+64, ...; each of the K rounds takes the wave-wide
+// maximum under the order (greater logit first, then lower expert id), so
+// the result is the stable descending order with ties to the lower id.
+// Gates: w_k = exp(l_k - l_0), summed in slot order, g_k = w_k / sum.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ logits,
+                                                        int32_t* __restrict__ topk_idx,
+                                                        float* __restrict__ topk_gate, int64_t T,
+                                                        int E, int K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  const int nq = E >> 6;
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = q < nq ? row[q * 64 + lane] : -INFINITY;
+  uint32_t taken = 0;
+  float my_val = 0.f;
+  int my_id = 0;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (q < nq && !((taken >> q) & 1u)) {
+        const int e = q * 64 + lane;
+        if (v[q] > bv || (v[q] == bv && e < be)) {
+          bv = v[q];
+          be = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == k) {
+      my_val = bv;
+      my_id = be;
+    }
+  }
+  const float top = __shfl(my_val, 0, 64);
+  const float w = lane < K ? expf(my_val - top) : 0.f;
+  float sum = 0.f;
+  for (int k = 0; k < K; ++k) sum += __shfl(w, k, 64);
+  if (lane < K) {
+    topk_idx[t * K + lane] = my_id;
+    topk_gate[t * K + lane] = w / sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Counting sort, pass 1: per block of 256 tokens, a 256-bit token mask per
+// expert (LDS), giving each route its rank among the block's routes of the
+// same expert (ranks follow token order, i.e. route id order since a token
+// holds an expert at most once) and the block's count per expert.
+// hist row layout: [E] counts, then one word of error bits
+// (1: expert id out of range, 2: expert repeated within a token).
+// route_rank receives the in-block rank (-1 for an invalid id).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* __restrict__ topk_idx,
+                                                         int32_t* __restrict__ hist,
+                                                         int32_t* __restrict__ route_rank,
+                                                         int64_t T, int E, int K) {
+  __shared__ unsigned long long mask[1024 * 4];
+  __shared__ int err;
+  const int tid = threadIdx.x;
+  for (int q = tid; q < E * 4; q += 256) mask[q] = 0ull;
+  if (tid == 0) err = 0;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kSortBlock + tid;
+  const int word = tid >> 6;
+  const unsigned long long bit = 1ull << (tid & 63);
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = topk_idx[t * K + k];
+      if (e < 0 || e >= E) {
+        atomicOr(&err, 1);
+        continue;
+      }
+      const unsigned long long old = atomicOr(&mask[e * 4 + word], bit);
+      if (old & bit) atomicOr(&err, 2);
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = topk_idx[t * K + k];
+      int rank = -1;
+      if (e >= 0 && e < E) {
+        rank = __popcll(mask[e * 4 + word] & (bit - 1ull));
+        for (int w = 0; w < word; ++w) rank += __popcll(mask[e * 4 + w]);
+      }
+      route_rank[t * K + k] = rank;
+    }
+  }
+  int32_t* hrow = hist + static_cast<int64_t>(blockIdx.x) * (E + 1);
+  for (int e = tid; e < E; e += 256)
+    hrow[e] = __popcll(mask[e * 4]) + __popcll(mask[e * 4 + 1]) + __popcll(mask[e * 4 + 2]) +
+              __popcll(mask[e * 4 + 3]);
+  if (tid == 0) hrow[E] = err;
+}
+
+// Inclusive scan of one int per thread over a 1024-thread block.
+__device__ __forceinline__ int block_scan_incl(int v, int* buf) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += add;
+    __syncthreads();
+  }
+  const int r = buf[tid];
+  __syncthreads();
+  return r;
+}
+
+// Grouped-GEMM work list from per-group row counts (1024-thread block; thread
+// e < E holds expert e's count).  Expert e's rows are split into row tiles of
+// kRowsPerTile, in expert order, followed by the shared expert's T rows as
+// group E when has_shared.  tiles[2j] = group, tiles[2j+1] = first row;
+// meta[0] = number of tiles.
+__device__ void emit_tiles(int count, int E, int64_t T, int has_shared, int32_t* tiles,
+                           int32_t* meta, int* buf) {
+  const int e = threadIdx.x;
+  const int ntile = (count + kRowsPerTile - 1) / kRowsPerTile;
+  const int tincl = block_scan_incl(ntile, buf);
+  const int tfirst = tincl - ntile;
+  for (int c = 0; c < ntile; ++c) {
+    tiles[2 * (tfirst + c)] = e;
+    tiles[2 * (tfirst + c) + 1] = c * kRowsPerTile;
+  }
+  if (e == 1023) buf[0] = tincl;
+  __syncthreads();
+  const int routed_tiles = buf[0];
+  __syncthreads();
+  const int shared_tiles = has_shared ? static_cast<int>((T + kRowsPerTile - 1) / kRowsPerTile) : 0;
+  for (int c = e; c < shared_tiles; c += 1024) {
+    tiles[2 * (routed_tiles + c)] = E;
+    tiles[2 * (routed_tiles + c) + 1] = c * kRowsPerTile;
+  }
+  if (e == 0) meta[0] = routed_tiles + shared_tiles;
+}
+
+// ---------------------------------------------------------------------------
+// Counting sort, pass 2 (one 1024-thread workgroup): per expert, the
+// exclusive running count over blocks (block_base) and the expert segment
+// offsets; the error bits of all blocks (meta[1] and the workspace error
+// word, overwritten); and the grouped-GEMM work list (emit_tiles).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ block_base,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ meta, int nblocks,
+                                                          int E, int64_t T, int has_shared,
+                                                          int* __restrict__ err_word) {
+  __shared__ int buf[1024];
+  __shared__ int errs;
+  const int e = threadIdx.x;
+  if (e == 0) errs = 0;
+  int run = 0;
+  int errbits = 0;
+  for (int b = e; b < nblocks; b += 1024) errbits |= hist[static_cast<int64_t>(b) * (E + 1) + E];
+  if (e < E) {
+    int b = 0;
+    for (; b + 8 <= nblocks; b += 8) {
+      int h[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) h[q] = hist[static_cast<int64_t>(b + q) * (E + 1) + e];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        block_base[static_cast<int64_t>(b + q) * E + e] = run;
+        run += h[q];
+      }
+    }
+    for (; b < nblocks; ++b) {
+      const int h = hist[static_cast<int64_t>(b) * (E + 1) + e];
+      block_base[static_cast<int64_t>(b) * E + e] = run;
+      run += h;
+    }
+  }
+  const int incl = block_scan_incl(run, buf);
+  if (e < E) offsets[e] = incl - run;
+  if (e == E - 1) offsets[E] = incl;
+  if (errbits) atomicOr(&errs, errbits);
+  emit_tiles(run, E, T, has_shared, tiles, meta, buf);
+  __syncthreads();
+  if (e == 0) {
+    meta[1] = errs;
+    *err_word = errs ? 1 : 0;
+  }
+}
+
+// Work list alone, from caller-supplied expert offsets (grouped FFN run on
+// its own).
+__global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ meta, int E,
+                                                         int64_t T, int has_shared) {
+  __shared__ int buf[1024];
+  const int e = threadIdx.x;
+  int count = 0;
+  if (e < E) {
+    count = offsets[e + 1] - offsets[e];
+    if (count < 0) count = 0;
+  }
+  emit_tiles(count, E, T, has_shared, tiles, meta, buf);
+}
+
+// ---------------------------------------------------------------------------
+// Counting sort, pass 3: scatter.  pos = offsets[e] + block_base[b][e] +
+// in-block rank; sorted_route[pos] = r and route_pos[r] = pos.  route_pos
+// holds the in-block rank on entry (written by pass 1).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                            const int32_t* __restrict__ block_base,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ route_pos,
+                                                            int32_t* __restrict__ sorted_route,
+                                                            int64_t T, int E, int K) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kSortBlock + threadIdx.x;
+  if (t >= T) return;
+  for (int k = 0; k < K; ++k) {
+    const int64_t r = t * K + k;
+    const int e = topk_idx[r];
+    const int rank = route_pos[r];
+    if (e < 0 || e >= E || rank < 0) {
+      route_pos[r] = -1;
+      continue;
+    }
+    const int pos = offsets[e] + block_base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+    route_pos[r] = pos;
+    sorted_route[pos] = static_cast<int32_t>(r);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared-expert gate sg[t] = sigmoid(sum_h w_sgate[h] x[t][h]), one wave per
+// token: each lane sums its H/64 products in fp64 in ascending h, then a
+// fixed butterfly adds the lanes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void shared_gate_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w_sgate,
+                                                          float* __restrict__ sg, int64_t T,
+                                                          int H) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint16_t* xr = x + t * H;
+  double acc = 0.0;
+  for (int c = lane * 8; c < H; c += 512) {
+    const u32x4_t xv = ld16(xr + c), wv = ld16(w_sgate + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc += static_cast<double>(bf16_to_f32(static_cast<uint16_t>(xv[q] & 0xffffu))) *
+             static_cast<double>(bf16_to_f32(static_cast<uint16_t>(wv[q] & 0xffffu)));
+      acc += static_cast<double>(bf16_to_f32(static_cast<uint16_t>(xv[q] >> 16))) *
+             static_cast<double>(bf16_to_f32(static_cast<uint16_t>(wv[q] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) sg[t] = static_cast<float>(1.0 / (1.0 + exp(-acc)));
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+namespace moe {
+
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias,
+                                float* logits, int64_t T, int H, int E, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>(E / 64));
+  router_logits_kernel<<<grid, 256, 0, stream>>>(x, wr, bias, logits, T, H, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_gate(const float* logits, int32_t* topk_idx, float* topk_gate, int64_t T,
+                            int E, int K, hipStream_t stream) {
+  topk_gate_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, stream>>>(logits, topk_idx,
+                                                                          topk_gate, T, E, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_hist(const int32_t* topk_idx, int32_t* hist, int32_t* route_rank,
+                             int64_t T, int E, int K, hipStream_t stream) {
+  const unsigned nb = static_cast<unsigned>((T + kSortBlock - 1) / kSortBlock);
+  route_hist_kernel<<<nb, 256, 0, stream>>>(topk_idx, hist, route_rank, T, E, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* offsets,
+                             int32_t* tiles, int32_t* meta, int nblocks, int E, int64_t T,
+                             int has_shared, int* err_word, hipStream_t stream) {
+  route_scan_kernel<<<1, 1024, 0, stream>>>(hist, block_base, offsets, tiles, meta, nblocks, E, T,
+                                            has_shared, err_word);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* meta, int E, int64_t T,
+                            int has_shared, hipStream_t stream) {
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, meta, E, T, has_shared);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scatter(const int32_t* topk_idx, const int32_t* block_base,
+                                const int32_t* offsets, int32_t* route_pos, int32_t* sorted_route,
+                                int64_t T, int E, int K, hipStream_t stream) {
+  const unsigned nb = static_cast<unsigned>((T + kSortBlock - 1) / kSortBlock);
+  route_scatter_kernel<<<nb, 256, 0, stream>>>(topk_idx, block_base, offsets, route_pos,
+                                               sorted_route, T, E, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* w_sgate, float* sg, int64_t T,
+                              int H, hipStream_t stream) {
+  shared_gate_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, stream>>>(x, w_sgate, sg, T, H);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every entry point include/moe_mi355x.h
+declares, size its workspace, and reject bad arguments with the documented
+status before anything is enqueued (fail closed).  Validation runs before
+the device check, so these calls return without touching a GPU; fake but
+aligned addresses are fine because nothing dereferences them.
+"""
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_counting_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m.LIB_PATH):
+        from mixture_experts_layer_counting_amd._build import build
+        build()
+    return m.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z][\w ]*?\**\s*\**(moe_\w+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward",
+              "moe_workspace_bytes", "moe_status_str", "moe_abi_version", "moe_last_device_error"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert set(declared_functions()) <= set(m.EXPORTS) | set(declared_functions())
+    assert m.moe_abi_version() == m.ABI_VERSION
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert m.moe_status_str(s) and m.moe_status_str(s) != "unknown status"
+    assert m.moe_status_str(99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    d = m.Dims(1024, 2048)
+    fwd = m.moe_workspace_bytes(d, m.MOE_OP_FORWARD)
+    assert fwd > 0
+    assert m.moe_workspace_bytes(d, m.MOE_OP_BACKWARD) >= fwd
+    # grows with tokens; zero for invalid dims or op
+    assert m.moe_workspace_bytes(m.Dims(8192, 2048), m.MOE_OP_FORWARD) > fwd
+    assert m.moe_workspace_bytes(m.Dims(1024, 2000), m.MOE_OP_FORWARD) == 0
+    assert m.moe_workspace_bytes(d, 17) == 0
+
+
+# fake, 256-byte aligned, non-overlapping device addresses
+class Fake:
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes):
+        a = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 4096
+        return a
+
+
+def full_args(d: m.Dims):
+    f = Fake()
+    T, H, E, K, I, Is = d.tokens, d.hidden, d.experts, d.top_k, d.inter, d.shared_inter
+    w = m.Weights(w_router=f(E * H * 4), w13=f(E * 2 * I * H * 2), w2=f(E * H * I * 2), router_bias=None,
+                  ws13=f(2 * Is * H * 2), ws2=f(H * Is * 2), w_sgate=f(H * 2))
+    r = m.Routes(topk_idx=f(T * K * 4), topk_gate=f(T * K * 4), logits=f(T * E * 4), expert_offsets=f((E + 1) * 4),
+                 sorted_route=f(T * K * 4), route_pos=f(T * K * 4))
+    s = m.Saved(y=f(T * K * H * 4), gu=None, shared_y=f(T * H * 4), shared_gate=f(T * 4), shared_gu=None)
+    x = f(T * H * 2)
+    o32, o16 = f(T * H * 4), f(T * H * 2)
+    nws = m.moe_workspace_bytes(d, m.MOE_OP_FORWARD)
+    ws = (f(nws), nws)
+    return w, r, s, x, o32, o16, ws, f
+
+
+def fwd(d, w, r, s, x, o32, o16, ws):
+    return m.moe_forward(d, w, x, r, s, o32, o16, ws, stream=0)
+
+
+def test_forward_validation_fails_closed(lib):
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    assert fwd(m.Dims(64, 500, 512, 10, 128, 128), w, r, s, x, o32, o16, ws) == m.MOE_E_SHAPE
+    assert fwd(m.Dims(64, 512, 500, 10, 128, 128), w, r, s, x, o32, o16, ws) == m.MOE_E_SHAPE
+    assert fwd(m.Dims(64, 512, 512, 17, 128, 128), w, r, s, x, o32, o16, ws) == m.MOE_E_SHAPE
+    assert fwd(m.Dims(64, 512, 512, 10, 96, 128), w, r, s, x, o32, o16, ws) == m.MOE_E_SHAPE
+    assert fwd(m.Dims(-1, 512, 512, 10, 128, 128), w, r, s, x, o32, o16, ws) == m.MOE_E_SHAPE
+    assert fwd(m.Dims(1 << 28, 512, 512, 10, 128, 128), w, r, s, x, o32, o16, ws) == m.MOE_E_SHAPE
+    assert fwd(d, w, r, s, None, o32, o16, ws) == m.MOE_E_NULL
+    assert fwd(d, w, r, s, x, None, None, ws) == m.MOE_E_NULL
+    w2 = m.Weights(**{**w.__dict__, "w13": None})
+    assert fwd(d, w2, r, s, x, o32, o16, ws) == m.MOE_E_NULL
+    w3 = m.Weights(**{**w.__dict__, "w2": w.w2 + 2})
+    assert fwd(d, w3, r, s, x, o32, o16, ws) == m.MOE_E_ALIGN
+    # an output aliasing an input
+    r2 = m.Routes(**{**r.__dict__, "topk_gate": x})
+    assert fwd(d, w, r2, s, x, o32, o16, ws) == m.MOE_E_ALIAS
+    s2 = m.Saved(**{**s.__dict__, "y": o32})
+    assert fwd(d, w, r, s2, x, o32, o16, ws) == m.MOE_E_ALIAS
+    # workspace missing / too small / misaligned
+    assert fwd(d, w, r, s, x, o32, o16, (ws[0], ws[1] - 1)) == m.MOE_E_WORKSPACE
+    assert fwd(d, w, r, s, x, o32, o16, None) == m.MOE_E_WORKSPACE
+    assert fwd(d, w, r, s, x, o32, o16, (ws[0] + 16, ws[1])) == m.MOE_E_ALIGN
+    # T == 0 is a no-op, whatever the pointers
+    assert fwd(m.Dims(0, 512, 512, 10, 128, 128), w, r, s, None, None, None, None) == m.MOE_OK
+
+
+def test_stage_validation_fails_closed(lib):
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    assert m.moe_route(d, None, w, r, ws, stream=0) == m.MOE_E_NULL
+    assert m.moe_permute(d, m.Routes(topk_idx=r.topk_idx), ws, stream=0) == m.MOE_E_NULL
+    assert m.moe_grouped_ffn(d, x, w, r, m.Saved(), ws, stream=0) == m.MOE_E_NULL
+    assert m.moe_combine(d, r, s, None, None, stream=0) == m.MOE_E_NULL
+    assert m.moe_combine(d, r, m.Saved(**{**s.__dict__, "shared_y": None}), o32, None, stream=0) == m.MOE_E_NULL
+    assert m.moe_combine(d, r, s, s.y, None, stream=0) == m.MOE_E_ALIAS
+    assert m.moe_last_device_error(None, stream=0) == m.MOE_E_WORKSPACE
+
+
+def test_valid_arguments_reach_the_device_check(lib):
+    """With every argument valid the only remaining check is the gfx950
+    device; without a GPU it fails there, so still nothing is launched."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid fake pointers would be launched")
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    assert fwd(d, w, r, s, x, o32, o16, ws) == m.MOE_E_DEVICE

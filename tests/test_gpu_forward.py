@@ -1,0 +1,154 @@
+"""GPU parity of the forward path against the FP64 oracle, through the C ABI.
+
+Routes bit-exact (fp32 router ties counted), permutation bit-exact, gates,
+route rows Y, shared expert and output within 5e-5 + 1e-3 |ref|; the bf16
+output is the round-to-nearest-even of the fp32 output.  Large workloads are
+compared on sampled tokens (first, last, tile boundaries and a seeded
+sample) plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_counting_amd as m
+import oracle as O
+import workloads as W
+from tests.gpu_util import (DEV, assert_close, check_forward, dev_bits, dev_weights, dims_of, gpu_forward,
+                            load_cfg, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_tokens(T, n=48, seed=7):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, T // 2, T - 2, T - 1]
+    pick = set(t for t in fixed if 0 <= t < T) | set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    return np.array(sorted(pick))
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg, layer, x = load_cfg("tiny")
+    return cfg, layer, x, dev_weights(layer)
+
+
+def test_tiny_forward_all_tokens(tiny):
+    cfg, layer, x, w = tiny
+    say("case: tiny forward, all 256 tokens")
+    g = gpu_forward(cfg, w, dev_bits(x)).host()
+    check_forward(cfg, layer, x, g)
+
+
+def test_tiny_ragged_token_counts(tiny):
+    """Token counts that are not multiples of any tile (1, 33, 100, 255)."""
+    cfg, layer, x, w = tiny
+    for T in (1, 33, 100, 255):
+        say(f"case: tiny forward, T={T}")
+        xs = x[:T]
+        g = gpu_forward(cfg, w, dev_bits(xs)).host()
+        check_forward(cfg, layer, xs, g)
+
+
+def test_stages_equal_whole_forward(tiny):
+    """route + permute + grouped_ffn + combine called one by one give the same
+    bits as moe_forward."""
+    cfg, layer, x, w = tiny
+    say("case: tiny, staged entry points vs moe_forward")
+    xd = dev_bits(x)
+    whole = gpu_forward(cfg, w, xd).host()
+    d = dims_of(cfg)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, DEV)
+    routes = m.alloc_routes(d, DEV)
+    saved = m.alloc_saved(d, DEV)
+    out32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV)
+    m.check(m.moe_route(d, xd, w, routes, ws), "moe_route")
+    m.check(m.moe_permute(d, routes, ws), "moe_permute")
+    m.check(m.moe_grouped_ffn(d, xd, w, routes, saved, ws), "moe_grouped_ffn")
+    m.check(m.moe_combine(d, routes, saved, out32, out16), "moe_combine")
+    torch.cuda.synchronize()
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+    assert np.array_equal(routes.topk_idx.cpu().numpy(), whole["idx"])
+    assert np.array_equal(routes.sorted_route.cpu().numpy(), whole["sorted_route"])
+    assert np.array_equal(saved.y.cpu().numpy().view(np.uint32), whole["y"].view(np.uint32))
+    assert np.array_equal(out32.cpu().numpy().view(np.uint32), whole["out32"].view(np.uint32))
+
+
+def test_replayed_routes_through_permute(tiny):
+    """Caller-supplied routes (routing replay): the oracle's ids, reversed
+    slot order per token, go through moe_permute / grouped_ffn / combine and
+    match the oracle run on the same forced routes."""
+    cfg, layer, x, w = tiny
+    say("case: tiny, replayed routes")
+    ref_idx = O.forward(layer, x, cfg.top_k)["idx"][:, ::-1].copy()
+    d = dims_of(cfg)
+    xd = dev_bits(x)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, DEV)
+    routes = m.alloc_routes(d, DEV)
+    saved = m.alloc_saved(d, DEV)
+    routes.topk_idx.copy_(torch.from_numpy(ref_idx.astype(np.int32)))
+    # gates of the replayed routes come from the oracle definition on its own logits
+    ref = O.forward(layer, x, cfg.top_k, forced_idx=ref_idx)
+    routes.topk_gate.copy_(torch.from_numpy(ref["gates"].astype(np.float32)))
+    out32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    m.check(m.moe_permute(d, routes, ws), "moe_permute")
+    m.check(m.moe_grouped_ffn(d, xd, w, routes, saved, ws), "moe_grouped_ffn")
+    m.check(m.moe_combine(d, routes, saved, out32, None), "moe_combine")
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+    off, srt, pos = O.permute_routes(ref_idx, cfg.experts)
+    assert np.array_equal(routes.sorted_route.cpu().numpy(), srt)
+    assert np.array_equal(routes.route_pos.cpu().numpy(), pos)
+    assert_close(saved.y.cpu().numpy(), ref["y"], "replayed Y")
+    assert_close(out32.cpu().numpy(), ref["out"], "replayed out")
+
+
+def test_bad_route_ids_set_device_error(tiny):
+    """An out-of-range expert id and a repeated id are reported through the
+    device error word; every kernel bounds-checks them, so nothing faults."""
+    cfg, layer, x, w = tiny
+    say("case: tiny, invalid caller routes -> device error")
+    d = dims_of(cfg, 64)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, DEV)
+    idx = np.tile(np.arange(cfg.top_k, dtype=np.int32), (64, 1))
+    for bad in ("range", "repeat"):
+        j = idx.copy()
+        if bad == "range":
+            j[5, 3] = cfg.experts + 7
+        else:
+            j[9, 4] = j[9, 2]
+        routes = m.alloc_routes(d, DEV)
+        routes.topk_idx.copy_(torch.from_numpy(j))
+        m.check(m.moe_permute(d, routes, ws), "moe_permute")
+        assert m.moe_last_device_error(ws) == m.MOE_E_DEVICE, bad
+    routes = m.alloc_routes(d, DEV)
+    routes.topk_idx.copy_(torch.from_numpy(idx))
+    m.check(m.moe_permute(d, routes, ws), "moe_permute")
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+
+
+def test_zero_tokens_is_a_noop(tiny):
+    cfg, layer, x, w = tiny
+    d = dims_of(cfg, 0)
+    r = m.Routes()
+    s = m.Saved()
+    assert m.moe_forward(d, w, None, r, s, None, None, None) == m.MOE_OK
+
+
+@pytest.mark.parametrize("name", ["moe1k", "moe8k", "skew16k"])
+def test_full_size_forward_sampled(name):
+    cfg, layer, x = load_cfg(name)
+    w = dev_weights(layer)
+    say(f"case: {name} forward on GPU (T={cfg.tokens})")
+    g = gpu_forward(cfg, w, dev_bits(x)).host()
+    # properties at full size
+    idx = g["idx"]
+    assert ((idx >= 0) & (idx < cfg.experts)).all()
+    assert all(len(set(r)) == cfg.top_k for r in idx[:: max(1, cfg.tokens // 512)].tolist())
+    assert np.max(np.abs(g["gates"].astype(np.float64).sum(1) - 1.0)) <= 2e-6
+    load = np.diff(g["offsets"])
+    say(f"  expert load: min {load.min()} max {load.max()} empty {(load == 0).sum()}")
+    if name == "skew16k":
+        assert load.max() > 2000 and (load == 0).sum() >= 100
+    tok = sample_tokens(cfg.tokens)
+    say(f"  oracle on {len(tok)} sampled tokens")
+    check_forward(cfg, layer, x, g, tokens=tok)
