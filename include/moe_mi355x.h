@@ -145,9 +145,9 @@ size_t moe_workspace_bytes(const moe_dims* dims, int op);
  * x [T][H] bf16.  Writes logits (if routes->logits != NULL), topk_idx and
  * topk_gate.  The router logit l[t][e] = sum_h x[t][h] * w_router[e][h]
  * (+ router_bias[e]) is formed with exact bf16 x fp32 products (the fp32
- * weight split into three bf16 parts on the matrix cores), summed in
- * fixed 64-wide chunks in fp32 and across chunks in fp64, then rounded to
- * fp32.  Selection compares those fp32 logits (greater first, equal values
+ * weight split exactly into three bf16 parts, multiplied on the matrix
+ * cores), summed in fixed 256-wide chunks in fp32 and across chunks in fp64,
+ * then rounded to fp32.  Selection compares those fp32 logits (greater first, equal values
  * to the lower id); the gates are exp(l_k - l_0) / sum_j exp(l_j - l_0) over
  * the selected slots, in fp32. */
 int moe_route(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
@@ -210,8 +210,25 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                  float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws,
                  size_t ws_bytes, hipStream_t stream);
 
-/* Synchronises `stream`, then returns and clears the sticky device error
- * word of workspace `ws` (MOE_OK or MOE_E_DEVICE).  Debug/validation use. */
+/* Profiling variant of moe_forward: the same kernels in the same order on
+ * `stream`, with events[i] recorded just before kernel i and events[n] after
+ * the last one, n = moe_forward_kernel_count(dims).  `events` are created by
+ * the caller (hipEventCreate); n_events must be >= n + 1.  Results are
+ * identical to moe_forward.  Kernel order: router_split, router_logits, topk_gate,
+ * route_hist, route_scan, route_scatter, [shared_gate if Is > 0], ffn_up,
+ * ffn_down, combine. */
+int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                         moe_routes* routes, moe_saved* saved, float* out_f32,
+                         uint16_t* out_bf16, void* ws, size_t ws_bytes, hipEvent_t* events,
+                         int n_events, hipStream_t stream);
+
+/* Number of kernels moe_forward launches for these dims (0 if invalid). */
+int moe_forward_kernel_count(const moe_dims* dims);
+
+/* Synchronises `stream`, then returns the device error word of workspace
+ * `ws` (MOE_OK or MOE_E_DEVICE) as left by the last moe_permute or
+ * moe_forward on that workspace (each such call overwrites it).
+ * Debug/validation use. */
 int moe_last_device_error(void* ws, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -56,7 +56,10 @@ class MoeGrads(ctypes.Structure):
 
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
-           "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error")
+           "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
+           "moe_forward_profiled", "moe_forward_kernel_count")
+FORWARD_KERNELS = ("router_split", "router_logits", "topk_gate", "route_hist", "route_scan", "route_scatter", "shared_gate",
+                   "ffn_up", "ffn_down", "combine")
 
 _lib = None
 
@@ -90,6 +93,11 @@ def load_library():
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                  P(MoeGrads), *ws]
+    lib.moe_forward_profiled.restype = ctypes.c_int
+    lib.moe_forward_profiled.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP,
+                                         _VP, ctypes.c_size_t, _VP, ctypes.c_int, _VP]
+    lib.moe_forward_kernel_count.restype = ctypes.c_int
+    lib.moe_forward_kernel_count.argtypes = [P(MoeDims)]
     lib.moe_last_device_error.restype = ctypes.c_int
     lib.moe_last_device_error.argtypes = [_VP, _VP]
     if lib.moe_abi_version() != ABI_VERSION:
@@ -246,6 +254,23 @@ def moe_backward(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grad
                                        _stream(stream))
 
 
+def moe_forward_profiled(dims, weights, x, routes, saved, out_f32, out_bf16, ws, events, stream=None) -> int:
+    """events: a ctypes array of hipEvent_t handles (see forward_kernel_names)."""
+    p, n = _ws(ws)
+    return load_library().moe_forward_profiled(ctypes.byref(dims.c()), ctypes.byref(weights.c()), _ptr(x),
+                                               ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(out_f32),
+                                               _ptr(out_bf16), p, n, events, len(events), _stream(stream))
+
+
+def moe_forward_kernel_count(dims) -> int:
+    return load_library().moe_forward_kernel_count(ctypes.byref(dims.c()))
+
+
+def forward_kernel_names(dims):
+    """Kernel names of moe_forward in launch order."""
+    return [k for k in FORWARD_KERNELS if k != "shared_gate" or dims.shared_inter > 0]
+
+
 def moe_last_device_error(ws, stream=None) -> int:
     p, _ = _ws(ws)
     return load_library().moe_last_device_error(p, _stream(stream))
@@ -277,6 +302,15 @@ def alloc_saved(dims: Dims, device, training: bool = False) -> Saved:
                  shared_gu=f(T, 2 * Is) if (Is and training) else None)
 
 
+def alloc_grads(dims: Dims, device) -> Grads:
+    import torch
+    E, H, I, Is = dims.experts, dims.hidden, dims.inter, dims.shared_inter
+    f = lambda *s: torch.empty(*s, dtype=torch.float32, device=device)
+    return Grads(d_w_router=f(E, H), d_w13=f(E, 2 * I, H), d_w2=f(E, H, I),
+                 d_ws13=f(2 * Is, H) if Is else None, d_ws2=f(H, Is) if Is else None,
+                 d_w_sgate=f(H) if Is else None)
+
+
 def alloc_workspace(dims: Dims, op: int, device):
     import torch
     n = moe_workspace_bytes(dims, op)
@@ -305,3 +339,18 @@ class Layer:
             ws = alloc_workspace(d, MOE_OP_BACKWARD if training else MOE_OP_FORWARD, dev)
         check(moe_forward(d, self.weights, x, routes, saved, out32, out16, ws, stream), "moe_forward")
         return routes, saved, out32, out16
+
+    def backward(self, x, routes, saved, d_out, ws=None, want_bf16: bool = False, stream=None):
+        """Gradients for upstream gradient d_out (bf16 bits); needs the
+        routes and saved tensors of a training-mode forward."""
+        import torch
+        d = dataclasses.replace(self.dims, tokens=int(x.shape[0]))
+        dev = x.device
+        grads = alloc_grads(d, dev)
+        dx32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=dev)
+        dx16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev) if want_bf16 else None
+        if ws is None:
+            ws = alloc_workspace(d, MOE_OP_BACKWARD, dev)
+        check(moe_backward(d, self.weights, x, routes, saved, d_out, dx32, dx16, grads, ws, stream),
+              "moe_backward")
+        return dx32, dx16, grads

@@ -24,6 +24,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t err = 0;         // int error word (first 256 bytes)
   size_t logits = 0;      // [T][E] f32 when the caller passes no logits buffer
+  size_t wsplit = 0;      // [3][E][H] bf16: exact hi/mid/lo split of the router weight
   size_t hist = 0;        // [NB][E+1] i32
   size_t block_base = 0;  // [NB][E] i32
   size_t tiles = 0;       // [2*max_tiles] i32
@@ -31,9 +32,20 @@ struct Layout {
   size_t act_hi = 0, act_lo = 0;    // [R][I] bf16
   size_t sact_hi = 0, sact_lo = 0;  // [T][Is] bf16
   size_t fwd_end = 0;
+  // backward regions (after fwd_end)
+  size_t tiles64 = 0, meta64 = 0;    // 64-row work list
+  size_t dl = 0, dz = 0;             // [T][K], [T] f32
+  size_t dgu[3] = {0, 0, 0};         // [R][2I] bf16 planes (hi, mid, lo)
+  size_t sdgu[3] = {0, 0, 0};        // [T][2Is]
+  size_t gact[3] = {0, 0, 0};        // [R][I]
+  size_t sgact[3] = {0, 0, 0};       // [T][Is]
+  size_t dx_route = 0;               // [R][H] f32
+  size_t dx_shared = 0;              // [T][H] f32
+  size_t wsg_partial = 0;            // [ceil(T/64)][H] f64
   size_t bwd_end = 0;
   int nblocks = 0;
   int max_tiles = 0;
+  int max_tiles64 = 0;
 };
 
 Layout make_layout(const moe_dims& d) {
@@ -50,6 +62,7 @@ Layout make_layout(const moe_dims& d) {
   };
   L.err = take(kAlign);
   L.logits = take(static_cast<size_t>(T) * E * 4);
+  L.wsplit = take(static_cast<size_t>(3) * E * d.hidden * 2);
   L.hist = take(static_cast<size_t>(L.nblocks) * (E + 1) * 4);
   L.block_base = take(static_cast<size_t>(L.nblocks) * E * 4);
   L.tiles = take(static_cast<size_t>(L.max_tiles) * 2 * 4);
@@ -59,6 +72,21 @@ Layout make_layout(const moe_dims& d) {
   L.sact_hi = take(static_cast<size_t>(T) * Is * 2);
   L.sact_lo = take(static_cast<size_t>(T) * Is * 2);
   L.fwd_end = o;
+  const int64_t H = d.hidden;
+  L.max_tiles64 = static_cast<int>(moe::max_row_tiles(T, d.top_k, E, Is > 0, 64));
+  L.tiles64 = take(static_cast<size_t>(L.max_tiles64) * 2 * 4);
+  L.meta64 = take(64 * 4);
+  L.dl = take(static_cast<size_t>(R) * 4);
+  L.dz = take(static_cast<size_t>(T) * 4);
+  for (int q = 0; q < 3; ++q) {
+    L.dgu[q] = take(static_cast<size_t>(R) * 2 * I * 2);
+    L.sdgu[q] = take(static_cast<size_t>(T) * 2 * Is * 2);
+    L.gact[q] = take(static_cast<size_t>(R) * I * 2);
+    L.sgact[q] = take(static_cast<size_t>(T) * Is * 2);
+  }
+  L.dx_route = take(static_cast<size_t>(R) * H * 4);
+  L.dx_shared = take(static_cast<size_t>(T) * H * 4);
+  L.wsg_partial = take(static_cast<size_t>((T + 63) / 64) * H * 8);
   L.bwd_end = o;
   return L;
 }
@@ -160,9 +188,24 @@ int check_device() {
     if (_st != MOE_OK) return _st;          \
   } while (0)
 
-#define MOE_LAUNCH(expr)                            \
-  do {                                              \
-    if ((expr) != hipSuccess) return MOE_E_LAUNCH;  \
+// Optional per-kernel events of moe_forward_profiled: when set, an event is
+// recorded before every launch.
+struct Marks {
+  hipEvent_t* ev = nullptr;
+  int n = 0;
+  int next = 0;
+  hipStream_t s = nullptr;
+  hipError_t mark() {
+    if (!ev || next >= n) return hipSuccess;
+    return hipEventRecord(ev[next++], s);
+  }
+};
+thread_local Marks* g_marks = nullptr;
+
+#define MOE_LAUNCH(expr)                                                  \
+  do {                                                                    \
+    if (g_marks && g_marks->mark() != hipSuccess) return MOE_E_LAUNCH;    \
+    if ((expr) != hipSuccess) return MOE_E_LAUNCH;                        \
   } while (0)
 
 size_t bytes_x(const moe_dims& d) { return static_cast<size_t>(d.tokens) * d.hidden * 2; }
@@ -190,7 +233,9 @@ void add_weights(Args& a, const moe_dims& d, const moe_weights* w, bool router, 
 int run_route(const moe_dims& d, const uint16_t* x, const moe_weights* w, moe_routes* r, void* ws,
               const Layout& L, hipStream_t s) {
   float* logits = r->logits ? r->logits : at<float>(ws, L.logits);
-  MOE_LAUNCH(moe::launch_router_logits(x, w->w_router, w->router_bias, logits, d.tokens, d.hidden,
+  uint16_t* planes = at<uint16_t>(ws, L.wsplit);
+  MOE_LAUNCH(moe::launch_router_split(w->w_router, planes, d.hidden, d.experts, s));
+  MOE_LAUNCH(moe::launch_router_logits(x, planes, w->router_bias, logits, d.tokens, d.hidden,
                                        d.experts, s));
   MOE_LAUNCH(moe::launch_topk_gate(logits, r->topk_idx, r->topk_gate, d.tokens, d.experts, d.top_k, s));
   return MOE_OK;
@@ -215,7 +260,8 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
   const int has_shared = d.shared_inter > 0;
   if (!tiles_ready)
     MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles),
-                                     at<int32_t>(ws, L.meta), d.experts, d.tokens, has_shared, s));
+                                     at<int32_t>(ws, L.meta), d.experts, d.tokens, has_shared,
+                                     moe::kRowsPerTile, s));
   if (has_shared)
     MOE_LAUNCH(moe::launch_shared_gate(x, w->w_sgate, sv->shared_gate, d.tokens, d.hidden, s));
   MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, r->expert_offsets, r->sorted_route,
@@ -410,24 +456,123 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, m
   return run_combine(d, routes, saved, out_f32, out_bf16, stream);
 }
 
+int moe_forward_kernel_count(const moe_dims* dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return dims->shared_inter > 0 ? 10 : 9;
+}
+
+int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                         moe_routes* routes, moe_saved* saved, float* out_f32,
+                         uint16_t* out_bf16, void* ws, size_t ws_bytes, hipEvent_t* events,
+                         int n_events, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (!events) return MOE_E_NULL;
+  if (n_events < moe_forward_kernel_count(dims) + 1) return MOE_E_SHAPE;
+  Marks marks;
+  marks.ev = events;
+  marks.n = n_events;
+  marks.s = stream;
+  g_marks = &marks;
+  const int st = moe_forward(dims, w, x, routes, saved, out_f32, out_bf16, ws, ws_bytes, stream);
+  g_marks = nullptr;
+  if (st != MOE_OK) return st;
+  if (dims->tokens > 0 && marks.mark() != hipSuccess) return MOE_E_LAUNCH;
+  return MOE_OK;
+}
+
 int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                  const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
                  float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws, size_t ws_bytes,
                  hipStream_t stream) {
   MOE_TRY(check_dims(dims));
   if (dims->tokens == 0) return MOE_OK;
-  (void)w;
-  (void)x;
-  (void)routes;
-  (void)saved;
-  (void)d_out;
-  (void)d_x_f32;
-  (void)d_x_bf16;
-  (void)grads;
-  (void)ws;
-  (void)ws_bytes;
-  (void)stream;
-  return MOE_E_UNSUPPORTED;
+  if (!w || !routes || !saved || !grads) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, K = d.top_k, E = d.experts, H = d.hidden, I = d.inter,
+               Is = d.shared_inter;
+  Args a;
+  a.in(x, bytes_x(d));
+  a.in(d_out, bytes_x(d));
+  add_weights(a, d, w, true, true);
+  a.in(routes->topk_idx, T * K * 4);
+  a.in(routes->topk_gate, T * K * 4);
+  a.in(routes->expert_offsets, (E + 1) * 4);
+  a.in(routes->sorted_route, T * K * 4);
+  a.in(saved->y, T * K * H * 4);
+  a.in(saved->gu, T * K * 2 * I * 4);
+  if (Is) {
+    a.in(saved->shared_y, T * H * 4);
+    a.in(saved->shared_gate, T * 4);
+    a.in(saved->shared_gu, T * 2 * Is * 4);
+  }
+  a.out(d_x_f32, T * H * 4);
+  a.out(d_x_bf16, T * H * 2, false);
+  a.out(grads->d_w_router, E * H * 4);
+  a.out(grads->d_w13, E * 2 * I * H * 4);
+  a.out(grads->d_w2, E * H * I * 4);
+  if (Is) {
+    a.out(grads->d_ws13, 2 * Is * H * 4);
+    a.out(grads->d_ws2, H * Is * 4);
+    a.out(grads->d_w_sgate, H * 4);
+  }
+  a.in(ws, moe_workspace_bytes(dims, MOE_OP_BACKWARD), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_BACKWARD));
+  MOE_TRY(check_device());
+  const Layout L = make_layout(d);
+  const bool sh = Is > 0;
+  hipStream_t s = stream;
+  MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles64),
+                                   at<int32_t>(ws, L.meta64), d.experts, d.tokens, sh, 64, s));
+  MOE_LAUNCH(moe::launch_bwd_gate(d_out, saved->y, sh ? saved->shared_y : nullptr, routes->topk_gate,
+                                  sh ? saved->shared_gate : nullptr, at<float>(ws, L.dl),
+                                  at<float>(ws, L.dz), d.tokens, d.hidden, d.top_k, s));
+  moe::BwdLaunch b;
+  b.T = d.tokens;
+  b.H = d.hidden;
+  b.E = d.experts;
+  b.K = d.top_k;
+  b.I = d.inter;
+  b.Is = d.shared_inter;
+  b.max_tiles64 = L.max_tiles64;
+  b.offsets = routes->expert_offsets;
+  b.sorted_route = routes->sorted_route;
+  b.gate = routes->topk_gate;
+  b.sg = sh ? saved->shared_gate : nullptr;
+  b.tiles = at<int32_t>(ws, L.tiles64);
+  b.meta = at<int32_t>(ws, L.meta64);
+  b.x = x;
+  b.dout = d_out;
+  b.w13 = w->w13;
+  b.w2 = w->w2;
+  b.ws13 = sh ? w->ws13 : nullptr;
+  b.ws2 = sh ? w->ws2 : nullptr;
+  b.gu = saved->gu;
+  b.sgu = sh ? saved->shared_gu : nullptr;
+  for (int q = 0; q < 3; ++q) {
+    b.dgu[q] = at<uint16_t>(ws, L.dgu[q]);
+    b.sdgu[q] = at<uint16_t>(ws, L.sdgu[q]);
+    b.gact[q] = at<uint16_t>(ws, L.gact[q]);
+    b.sgact[q] = at<uint16_t>(ws, L.sgact[q]);
+  }
+  b.dx_route = at<float>(ws, L.dx_route);
+  b.dx_shared = sh ? at<float>(ws, L.dx_shared) : nullptr;
+  b.dw13 = grads->d_w13;
+  b.dw2 = grads->d_w2;
+  b.dws13 = sh ? grads->d_ws13 : nullptr;
+  b.dws2 = sh ? grads->d_ws2 : nullptr;
+  MOE_LAUNCH(moe::launch_bwd_gemms(b, s));
+  MOE_LAUNCH(moe::launch_bwd_router(x, at<float>(ws, L.dl), routes->expert_offsets,
+                                    routes->sorted_route, grads->d_w_router, d.tokens, d.hidden,
+                                    d.experts, d.top_k, s));
+  if (sh)
+    MOE_LAUNCH(moe::launch_bwd_wsg(x, at<float>(ws, L.dz), at<double>(ws, L.wsg_partial),
+                                   grads->d_w_sgate, d.tokens, d.hidden, s));
+  MOE_LAUNCH(moe::launch_bwd_dx_sum(routes->topk_idx, at<float>(ws, L.dl), at<float>(ws, L.dx_route),
+                                    sh ? at<float>(ws, L.dx_shared) : nullptr, at<float>(ws, L.dz),
+                                    sh ? w->w_sgate : nullptr, w->w_router, d_x_f32, d_x_bf16,
+                                    d.tokens, d.hidden, d.experts, d.top_k, s));
+  return MOE_OK;
 }
 
 int moe_last_device_error(void* ws, hipStream_t stream) {

@@ -61,6 +61,16 @@ __device__ __forceinline__ void split_hi_lo(float a, uint16_t& hi, uint16_t& lo)
   lo = f32_to_bf16(a - bf16_to_f32(hi));
 }
 
+// Split a float exactly into three bf16 parts p[0] + p[1] + p[2] (hi, mid,
+// lo): each step rounds the remainder to bf16, and an fp32 significand has
+// 24 bits, so the third remainder fits in bf16 exactly.
+__device__ __forceinline__ void split3(float a, uint16_t (&p)[3]) {
+  p[0] = f32_to_bf16(a);
+  const float r1 = a - bf16_to_f32(p[0]);
+  p[1] = f32_to_bf16(r1);
+  p[2] = f32_to_bf16(r1 - bf16_to_f32(p[1]));
+}
+
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 // XCD-aware mapping of a 1-D grid onto `items` work items.  The hardware

@@ -9,7 +9,8 @@
 
 namespace moe {
 
-hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias,
+hipError_t launch_router_split(const float* wr, uint16_t* planes, int H, int E, hipStream_t stream);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* planes, const float* bias,
                                 float* logits, int64_t T, int H, int E, hipStream_t stream);
 hipError_t launch_topk_gate(const float* logits, int32_t* topk_idx, float* topk_gate, int64_t T,
                             int E, int K, hipStream_t stream);
@@ -19,7 +20,7 @@ hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* 
                              int32_t* tiles, int32_t* meta, int nblocks, int E, int64_t T,
                              int has_shared, int* err_word, hipStream_t stream);
 hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* meta, int E, int64_t T,
-                            int has_shared, hipStream_t stream);
+                            int has_shared, int rows_per_tile, hipStream_t stream);
 hipError_t launch_route_scatter(const int32_t* topk_idx, const int32_t* block_base,
                                 const int32_t* offsets, int32_t* route_pos, int32_t* sorted_route,
                                 int64_t T, int E, int K, hipStream_t stream);
@@ -40,12 +41,52 @@ hipError_t launch_combine(const float* y, const float* gate, const float* sy, co
                           float* out32, uint16_t* out16, int64_t T, int H, int K,
                           hipStream_t stream);
 
+// Arguments of the backward's grouped GEMMs (see bwd_kernels.hip).
+struct BwdLaunch {
+  int64_t T;
+  int H, E, K, I, Is;
+  int max_tiles64;
+  const int32_t* offsets;
+  const int32_t* sorted_route;
+  const float* gate;
+  const float* sg;
+  const int32_t* tiles;  // 64-row tiles
+  const int32_t* meta;
+  const uint16_t* x;
+  const uint16_t* dout;
+  const uint16_t* w13;
+  const uint16_t* w2;
+  const uint16_t* ws13;
+  const uint16_t* ws2;
+  const float* gu;
+  const float* sgu;
+  uint16_t* dgu[3];    // hi/mid/lo planes
+  uint16_t* sdgu[3];
+  uint16_t* gact[3];
+  uint16_t* sgact[3];
+  float *dx_route, *dx_shared;
+  float *dw13, *dw2, *dws13, *dws2;
+};
+
+hipError_t launch_bwd_gate(const uint16_t* dout, const float* y, const float* sy, const float* gate,
+                           const float* sg, float* dl, float* dz, int64_t T, int H, int K,
+                           hipStream_t stream);
+hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream);
+hipError_t launch_bwd_router(const uint16_t* x, const float* dl, const int32_t* offsets,
+                             const int32_t* sorted_route, float* dwr, int64_t T, int H, int E,
+                             int K, hipStream_t stream);
+hipError_t launch_bwd_wsg(const uint16_t* x, const float* dz, double* partial, float* dwsg, int64_t T,
+                          int H, hipStream_t stream);
+hipError_t launch_bwd_dx_sum(const int32_t* topk_idx, const float* dl, const float* dx_route,
+                             const float* dx_shared, const float* dz, const uint16_t* w_sgate,
+                             const float* w_router, float* dx32, uint16_t* dx16, int64_t T, int H,
+                             int E, int K, hipStream_t stream);
+
 // Upper bound on grouped-GEMM row tiles for T tokens: every non-empty
 // expert's last tile may be partial, plus the shared expert's tiles.
-inline int64_t max_row_tiles(int64_t T, int K, int E, int has_shared) {
+inline int64_t max_row_tiles(int64_t T, int K, int E, int has_shared, int rows = kRowsPerTile) {
   const int64_t R = T * K;
-  return E + (R + kRowsPerTile - 1) / kRowsPerTile +
-         (has_shared ? (T + kRowsPerTile - 1) / kRowsPerTile : 0);
+  return E + (R + rows - 1) / rows + (has_shared ? (T + rows - 1) / rows : 0);
 }
 
 }  // namespace moe

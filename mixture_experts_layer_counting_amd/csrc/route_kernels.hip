@@ -12,78 +12,110 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
+// Router weight split: wr[e][h] (fp32) = hi + mid + lo exactly, each part a
+// bf16, stored as three planes [3][E][H].  hi = bf16(w), mid = bf16(w - hi),
+// lo = w - hi - mid (at most 8 significant bits, so exact in bf16).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
+                                                           uint16_t* __restrict__ planes,
+                                                           int64_t n) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const f32x4v_t w0 = *reinterpret_cast<const f32x4v_t*>(wr + i);
+  const f32x4v_t w1 = *reinterpret_cast<const f32x4v_t*>(wr + i + 4);
+  u32x4_t ph, pm, pl;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t h2 = 0, m2 = 0, l2 = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 2 * q + u;
+      const float w = r < 4 ? w0[r] : w1[r - 4];
+      const uint16_t hi = f32_to_bf16(w);
+      const float r1 = w - bf16_to_f32(hi);
+      const uint16_t mid = f32_to_bf16(r1);
+      const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+      h2 |= static_cast<uint32_t>(hi) << (16 * u);
+      m2 |= static_cast<uint32_t>(mid) << (16 * u);
+      l2 |= static_cast<uint32_t>(lo) << (16 * u);
+    }
+    ph[q] = h2;
+    pm[q] = m2;
+    pl[q] = l2;
+  }
+  st16(planes + i, ph);
+  st16(planes + n + i, pm);
+  st16(planes + 2 * n + i, pl);
+}
+
+// ---------------------------------------------------------------------------
 // Router logits: l[t][e] = sum_h x[t][h] * wr[e][h] (+ bias[e]).
 //
-// The fp32 weight is split exactly into three bf16 parts (hi + mid + lo), so
-// each product with the bf16 activation is exact on the matrix cores.  Each
-// 64-wide K chunk is accumulated in fp32 by 12 MFMAs (4 K-steps x 3 parts,
-// hi then mid then lo) from zero; the chunk sums are added in fp64 in
-// ascending chunk order and rounded once to fp32.  A logit's arithmetic
-// depends only on its own token row and expert row, never on the batch.
+// With wr = hi + mid + lo (router_split_kernel) every product with the bf16
+// activation is exact on the matrix cores.  Each 256-wide K chunk is
+// accumulated in fp32 by 48 MFMAs (16 K-steps, each hi then mid then lo)
+// from zero; the chunk sums are added in fp64 in ascending chunk order and
+// rounded once to fp32.  A logit's arithmetic depends only on its own token
+// row and expert row, never on the batch.
 //
-// Grid: (ceil(T/64), E/64), 256 threads.  Wave w computes tokens
-// t0 + 32*(w&1) .. +32 against experts e0 + 32*(w>>1) .. +32.
-// Inside a 64-wide chunk, lane half h and K-step s use k = 32h + 8s .. +8, so
-// every lane reads contiguous 64-byte runs of x and 128-byte runs of wr.
+// Grid: (ceil(T/128), ceil(E/128)), 512 threads.  Wave w computes tokens
+// t0 + 32*(w&3) .. +32 against experts e0 + 64*(w>>2) .. +64 (two 32-wide
+// blocks).  Inside a chunk, lane half h and K-step s use k = 128h + 8s .. +8,
+// so each lane reads one contiguous 256-byte run per operand row.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const float* __restrict__ wr,
+__global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ planes,
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ logits, int64_t T,
                                                             int H, int E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 31, half = lane >> 5;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 64 + 32 * (wave & 1);
-  const int e0 = blockIdx.y * 64 + 32 * (wave >> 1);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 128 + 32 * (wave & 3);
+  const int e0 = blockIdx.y * 128 + 64 * (wave >> 2);
+  if (t0 >= T || e0 >= E) return;  // E is a multiple of 64: a wave's experts are all in or all out
   int64_t trow = t0 + i;
   if (trow > T - 1) trow = T - 1;
-  const uint16_t* xr = x + trow * H + 32 * half;
-  const float* wrow = wr + static_cast<int64_t>(e0 + i) * H + 32 * half;
+  const int64_t n = static_cast<int64_t>(E) * H;
+  const uint16_t* xr = x + trow * H + 128 * half;
+  const uint16_t* w0 = planes + static_cast<int64_t>(e0 + i) * H + 128 * half;
+  const uint16_t* w1 = w0 + static_cast<int64_t>(32) * H;
 
-  double acc[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0;
-
-  for (int c = 0; c < H; c += 64) {
-    u32x4_t a[4];
-    f32x4v_t w[8];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = ld16(xr + c + 8 * s);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) w[q] = *reinterpret_cast<const f32x4v_t*>(wrow + c + 4 * q);
-    f32x16_t part = zero16();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint16_t hi[8], mid[8], lo[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float wv = w[2 * s + (r >> 2)][r & 3];
-        hi[r] = f32_to_bf16(wv);
-        const float r1 = wv - bf16_to_f32(hi[r]);
-        mid[r] = f32_to_bf16(r1);
-        lo[r] = f32_to_bf16(r1 - bf16_to_f32(mid[r]));
-      }
-      u32x4_t bh, bm, bl;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bh[q] = static_cast<uint32_t>(hi[2 * q]) | (static_cast<uint32_t>(hi[2 * q + 1]) << 16);
-        bm[q] = static_cast<uint32_t>(mid[2 * q]) | (static_cast<uint32_t>(mid[2 * q + 1]) << 16);
-        bl[q] = static_cast<uint32_t>(lo[2 * q]) | (static_cast<uint32_t>(lo[2 * q + 1]) << 16);
-      }
-      part = mfma32x32x16(a[s], bh, part);
-      part = mfma32x32x16(a[s], bm, part);
-      part = mfma32x32x16(a[s], bl, part);
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] += static_cast<double>(part[v]);
-  }
-
-  const int e = e0 + i;
-  const double b = bias ? static_cast<double>(bias[e]) : 0.0;
+  double acc[2][16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int64_t t = t0 + acc_row(v, half);
-    if (t < T) logits[t * E + e] = static_cast<float>(acc[v] + b);
+    acc[0][v] = 0.0;
+    acc[1][v] = 0.0;
+  }
+  for (int c = 0; c < H; c += 256) {
+    f32x16_t p0 = zero16(), p1 = zero16();
+#pragma unroll 4
+    for (int s = 0; s < 16; ++s) {
+      const int k = c + 8 * s;
+      const u32x4_t a = ld16(xr + k);
+      const u32x4_t h0 = ld16(w0 + k), m0 = ld16(w0 + n + k), l0 = ld16(w0 + 2 * n + k);
+      const u32x4_t h1 = ld16(w1 + k), m1 = ld16(w1 + n + k), l1 = ld16(w1 + 2 * n + k);
+      p0 = mfma32x32x16(a, h0, p0);
+      p1 = mfma32x32x16(a, h1, p1);
+      p0 = mfma32x32x16(a, m0, p0);
+      p1 = mfma32x32x16(a, m1, p1);
+      p0 = mfma32x32x16(a, l0, p0);
+      p1 = mfma32x32x16(a, l1, p1);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      acc[0][v] += static_cast<double>(p0[v]);
+      acc[1][v] += static_cast<double>(p1[v]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int e = e0 + 32 * nb + i;
+    const double b = bias ? static_cast<double>(bias[e]) : 0.0;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t t = t0 + acc_row(v, half);
+      if (t < T) logits[t * E + e] = static_cast<float>(acc[nb][v] + b);
+    }
   }
 }
 
@@ -217,27 +249,27 @@ __device__ __forceinline__ int block_scan_incl(int v, int* buf) {
 
 // Grouped-GEMM work list from per-group row counts (1024-thread block; thread
 // e < E holds expert e's count).  Expert e's rows are split into row tiles of
-// kRowsPerTile, in expert order, followed by the shared expert's T rows as
+// rows_per_tile, in expert order, followed by the shared expert's T rows as
 // group E when has_shared.  tiles[2j] = group, tiles[2j+1] = first row;
 // meta[0] = number of tiles.
 __device__ void emit_tiles(int count, int E, int64_t T, int has_shared, int32_t* tiles,
-                           int32_t* meta, int* buf) {
+                           int32_t* meta, int* buf, int rows_per_tile) {
   const int e = threadIdx.x;
-  const int ntile = (count + kRowsPerTile - 1) / kRowsPerTile;
+  const int ntile = (count + rows_per_tile - 1) / rows_per_tile;
   const int tincl = block_scan_incl(ntile, buf);
   const int tfirst = tincl - ntile;
   for (int c = 0; c < ntile; ++c) {
     tiles[2 * (tfirst + c)] = e;
-    tiles[2 * (tfirst + c) + 1] = c * kRowsPerTile;
+    tiles[2 * (tfirst + c) + 1] = c * rows_per_tile;
   }
   if (e == 1023) buf[0] = tincl;
   __syncthreads();
   const int routed_tiles = buf[0];
   __syncthreads();
-  const int shared_tiles = has_shared ? static_cast<int>((T + kRowsPerTile - 1) / kRowsPerTile) : 0;
+  const int shared_tiles = has_shared ? static_cast<int>((T + rows_per_tile - 1) / rows_per_tile) : 0;
   for (int c = e; c < shared_tiles; c += 1024) {
     tiles[2 * (routed_tiles + c)] = E;
-    tiles[2 * (routed_tiles + c) + 1] = c * kRowsPerTile;
+    tiles[2 * (routed_tiles + c) + 1] = c * rows_per_tile;
   }
   if (e == 0) meta[0] = routed_tiles + shared_tiles;
 }
@@ -284,7 +316,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   if (e < E) offsets[e] = incl - run;
   if (e == E - 1) offsets[E] = incl;
   if (errbits) atomicOr(&errs, errbits);
-  emit_tiles(run, E, T, has_shared, tiles, meta, buf);
+  emit_tiles(run, E, T, has_shared, tiles, meta, buf, kRowsPerTile);
   __syncthreads();
   if (e == 0) {
     meta[1] = errs;
@@ -297,7 +329,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ meta, int E,
-                                                         int64_t T, int has_shared) {
+                                                         int64_t T, int has_shared,
+                                                         int rows_per_tile) {
   __shared__ int buf[1024];
   const int e = threadIdx.x;
   int count = 0;
@@ -305,7 +338,7 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
     count = offsets[e + 1] - offsets[e];
     if (count < 0) count = 0;
   }
-  emit_tiles(count, E, T, has_shared, tiles, meta, buf);
+  emit_tiles(count, E, T, has_shared, tiles, meta, buf, rows_per_tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -371,10 +404,16 @@ __global__ __launch_bounds__(256) void shared_gate_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------
 namespace moe {
 
-hipError_t launch_router_logits(const uint16_t* x, const float* wr, const float* bias,
+hipError_t launch_router_split(const float* wr, uint16_t* planes, int H, int E, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(E) * H;
+  router_split_kernel<<<static_cast<unsigned>((n / 8 + 255) / 256), 256, 0, stream>>>(wr, planes, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* planes, const float* bias,
                                 float* logits, int64_t T, int H, int E, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>(E / 64));
-  router_logits_kernel<<<grid, 256, 0, stream>>>(x, wr, bias, logits, T, H, E);
+  dim3 grid(static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>((E + 127) / 128));
+  router_logits_kernel<<<grid, 512, 0, stream>>>(x, planes, bias, logits, T, H, E);
   return hipGetLastError();
 }
 
@@ -401,8 +440,8 @@ hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* 
 }
 
 hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* meta, int E, int64_t T,
-                            int has_shared, hipStream_t stream) {
-  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, meta, E, T, has_shared);
+                            int has_shared, int rows_per_tile, hipStream_t stream) {
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, meta, E, T, has_shared, rows_per_tile);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ from .moe_oracle import (  # noqa: F401
     router_logits,
     select_routes,
     shared_expert,
+    shared_expert_grads,
     sigmoid,
     silu,
     swiglu_expert,

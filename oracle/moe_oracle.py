@@ -293,6 +293,18 @@ def backward(layer: dict, x_bits, fwd: dict, d_out_bits) -> dict:
     return res
 
 
+def shared_expert_grads(layer: dict, x_bits, d_out_bits) -> dict:
+    """Gradients of the shared expert and its gate alone (they sum over all
+    tokens): dz = <dOut, S> sg (1 - sg), d_w_sgate = sum_t dz x, and the
+    SwiGLU backward with dy = sg * dOut.  Same formulas as backward()."""
+    x64 = bf16_to_f64(x_bits)
+    dO = bf16_to_f64(d_out_bits)
+    s, sg, sgu = shared_expert(x_bits, layer["ws13"], layer["ws2"], layer["w_sgate"])
+    dz = (dO * s).sum(axis=1) * sg * (1.0 - sg)
+    dxs, dws2, dws13, _ = _swiglu_backward(sg[:, None] * dO, sgu, x64, layer["ws13"], layer["ws2"])
+    return {"dz": dz, "d_w_sgate": dz @ x64, "d_ws13": dws13, "d_ws2": dws2, "dx_shared": dxs}
+
+
 def expert_weight_grads(layer: dict, x_bits, d_out_bits, idx, gates, gu_rows, expert: int):
     """dW13_e and dW2_e of one expert from its own routes only (for spot
     checks at sizes where the full backward is too large).  gu_rows are the

@@ -152,3 +152,19 @@ def test_full_size_forward_sampled(name):
     tok = sample_tokens(cfg.tokens)
     say(f"  oracle on {len(tok)} sampled tokens")
     check_forward(cfg, layer, x, g, tokens=tok)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(tokens=100, hidden=256, experts=192, top_k=6, inter=128, shared_inter=0),
+    dict(tokens=77, hidden=256, experts=64, top_k=16, inter=256, shared_inter=128),
+    dict(tokens=300, hidden=768, experts=1024, top_k=1, inter=384, shared_inter=256),
+])
+def test_shape_edge_cases(shape):
+    """Expert counts that are not multiples of 128, K = 1 and K = 16, no
+    shared expert, intermediate sizes that are not powers of two."""
+    cfg = W.MoEConfig(name="edge", **shape)
+    layer = W.make_layer(cfg)
+    x = W.tokens(cfg)
+    say(f"case: edge shape {shape}")
+    g = gpu_forward(cfg, dev_weights(layer), dev_bits(x)).host()
+    check_forward(cfg, layer, x, g)

@@ -268,6 +268,28 @@ def test_expert_weight_grads_match_full_backward():
         assert np.max(np.abs(dw2 - grads["d_w2"][e])) <= 1e-13
 
 
+def test_shared_expert_grads_match_full_backward():
+    cfg, layer, x, d_out = _tiny_float_layer()
+    fwd = O.forward(layer, x, cfg.top_k)
+    full = O.backward(layer, x, fwd, d_out)
+    sh = O.shared_expert_grads(layer, x, d_out)
+    for k in ("dz", "d_w_sgate", "d_ws13", "d_ws2"):
+        assert np.max(np.abs(sh[k] - full[k])) <= 1e-13, k
+
+
+def test_token_subset_backward_gives_the_same_input_gradient_rows():
+    """dX of a token depends only on that token: the backward of a token
+    subset reproduces the full batch's dX rows (used for sampled GPU checks)."""
+    cfg, layer, x, d_out = _tiny_float_layer()
+    fwd = O.forward(layer, x, cfg.top_k)
+    full = O.backward(layer, x, fwd, d_out)
+    sub = np.array([1, 4, 5])
+    fs = O.forward(layer, x[sub], cfg.top_k)
+    part = O.backward(layer, x[sub], fs, d_out[sub])
+    assert np.max(np.abs(part["dx"] - full["dx"][sub])) <= 1e-13
+    assert np.max(np.abs(part["dl"] - full["dl"][sub])) <= 1e-13
+
+
 # ---------------------------------------------------------------- subsets and bf16 report
 def test_token_subset_equals_full_rows():
     cfg = small_cfg()
