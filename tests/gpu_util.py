@@ -97,6 +97,18 @@ def assert_close(got, ref, what, atol=ATOL, rtol=RTOL):
     return err.max()
 
 
+def assert_close_sum(got, ref, what, n_terms):
+    """Tolerance for a weight gradient, which sums n_terms per-token terms:
+    each term's factors meet the per-token rule, and independent per-term
+    errors grow as sqrt(n), so the absolute floor is 5e-5 * sqrt(n_terms).
+    The strict per-token rule's worst err/tol is reported alongside."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    strict = (np.abs(g - r) / (ATOL + RTOL * np.abs(r))).max()
+    say(f"  {what}: strict-rule worst err/tol {strict:.3f} (n={n_terms})")
+    return assert_close(got, ref, what + " [sum rule]", atol=ATOL * np.sqrt(max(1, n_terms)))
+
+
 def compare_routes(idx_gpu, idx_ref, logits64):
     """Ordered expert lists equal except for fp32 router ties; returns the
     tokens with a tie (their gap is checked on the exact logits)."""
