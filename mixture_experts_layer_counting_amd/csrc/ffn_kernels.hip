@@ -5,8 +5,8 @@
 // projections with ONE fixed tile configuration, no gate multiply and no sum
 // inside, exactly one writer per (token, route) row.  Here the fixed part is
 // the per-element arithmetic: the 32x32x16 bf16 MFMA, the K order (64-wide
-// blocks in ascending order, inside a block the lane-half/K-step order
-// below) and fp32 accumulation from zero.  How rows are grouped into tiles
+// blocks in an order fixed by (expert, column tile), inside a block the
+// lane-half/K-step order below) and fp32 accumulation from zero.  How rows are grouped into tiles
 // (which depends on the batch) never changes a row's arithmetic, because an
 // MFMA output row depends only on its own A row.
 //
@@ -16,10 +16,31 @@
 
 namespace moe {
 
-// LDS row stride (bf16 elements) of a 64-wide K block: 64 + 8 of padding
-// keeps the 16-byte MFMA operand reads of 16 consecutive rows on distinct
-// banks.
-constexpr int kLdsStride = 72;
+// ---------------------------------------------------------------------------
+// Operand staging shared by both projections.
+//
+// Every operand row segment of one 64-wide K block is 128 contiguous bytes.
+// Loads are issued so that each wave instruction reads 8 rows x 128 bytes
+// (lane l: row l/8, 16-byte chunk l%8) -- whole cache lines of a few rows --
+// and the K blocks of a work item are visited starting at a rotation fixed
+// by (group, column tile), so concurrently streamed rows sit at different
+// offsets inside their rows.  Measured on MI355X, that pattern streams HBM at
+// ~6 TB/s, where MFMA-fragment-shaped loads (32 rows x 32 bytes per
+// instruction, all items starting at K = 0) stay at ~4.6 TB/s.
+//
+// In LDS a row of a K block takes 64 bf16 (128 bytes); its 16-byte chunk c
+// is stored at position c ^ ((row >> 1) & 7), which makes both the 8x128-byte
+// stores and the 32-row fragment reads of ds_*_b128 conflict-free.
+// Inside a K block, MFMA K step s and lane half h use chunk 4h + s, i.e.
+// k = 32h + 8s .. +8.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+}
+
+// K rotation of a work item: fixed per (group, column tile), so a given
+// output element always sums its K blocks in the same order.
+__device__ __forceinline__ int k_rotation(int grp, int nt, int nkb) { return (grp * 7 + nt * 3) % nkb; }
 
 // ---------------------------------------------------------------------------
 // Up projection + SwiGLU.
@@ -28,10 +49,12 @@ constexpr int kLdsStride = 72;
 // group E is the shared expert, rows are tokens row0 ...
 // Wave w owns activation columns c = nt*128 + 32w .. +32 and computes both
 // gate (W13 row c) and up (W13 row I + c) for every row of the tile, so the
-// SwiGLU is elementwise on the two accumulators.  The weight rows stream from
-// HBM straight into registers (each lane 64 contiguous bytes per block, the
-// two lane halves one 128-byte line per row); the gathered activation rows
-// are staged in LDS and shared by the four waves.
+// SwiGLU is elementwise on the two accumulators.  Its 64 weight rows go
+// through a private LDS area; the gathered activation rows through a
+// double-buffered area shared by the four waves.  One K block of loads is in
+// flight while the previous one is multiplied; 64-row tiles keep registers
+// and LDS small enough for several workgroups per CU, which is what keeps
+// enough bytes in flight.
 // Outputs: act as a bf16 hi/lo pair (row = sorted position, or token for the
 // shared expert) and, if requested, the fp32 gate/up values.
 // ---------------------------------------------------------------------------
@@ -57,7 +80,8 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   const int nmb = (rows + 31) >> 5;
   const uint16_t* W = shared ? ws13 : w13 + static_cast<int64_t>(grp) * 2 * I * H;
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kRowsPerTile][kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kRowsPerTile * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[4][64 * 64];
   __shared__ int s_tok[kRowsPerTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -77,83 +101,81 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   }
   __syncthreads();
 
-  const int arow = tid >> 1, acol = (tid & 1) * 32;
-  const bool aload = arow < nmb * 32;
-  const uint16_t* xa = x + static_cast<int64_t>(s_tok[arow]) * H + acol;
-
-  const int col = nt * kUpCols + wave * 32 + j;
-  const uint16_t* wg = W + static_cast<int64_t>(col) * H + 32 * half;
-  const uint16_t* wu = W + static_cast<int64_t>(Ie + col) * H + 32 * half;
-
-  f32x16_t accg[4], accu[4];
+  const int nkb = H >> 6;
+  const int rot = k_rotation(grp, nt, nkb);
+  // A loader: rows ar0 + 32q (q < nmb), chunk ac
+  const int ac = tid & 7, ar0 = tid >> 3;
+  const uint16_t* xa[2];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int q = 0; q < 2; ++q) xa[q] = x + static_cast<int64_t>(s_tok[ar0 + 32 * q]) * H + ac * 8;
+  // B loader: this wave's gate rows (Bs rows 0..31) and up rows (32..63),
+  // eight rows x 128 bytes per instruction
+  const int bc = lane & 7, br8 = lane >> 3;
+  const int col = nt * kUpCols + wave * 32 + j;
+  const uint16_t* wgp = W + static_cast<int64_t>(nt * kUpCols + wave * 32 + br8) * H + bc * 8;
+  const uint16_t* wup = wgp + static_cast<int64_t>(Ie) * H;
+
+  f32x16_t accg[2], accu[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
     accg[mb] = zero16();
     accu[mb] = zero16();
   }
-  u32x4_t ra[4], bg[4], bu[4], nbg[4], nbu[4];
+  u32x4_t ra[2], rb[8];
 
-  if (aload) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ra[q] = ld16(xa + 8 * q);
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bg[s] = ld16(wg + 8 * s);
-    bu[s] = ld16(wu + 8 * s);
-  }
-  if (aload) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) st16(&As[0][arow][acol + 8 * q], ra[q]);
-  }
+#define MOE_UP_ISSUE(KB)                                                   \
+  do {                                                                     \
+    int kk_ = (KB) + rot;                                                  \
+    if (kk_ >= nkb) kk_ -= nkb;                                            \
+    const int kp_ = kk_ << 6;                                              \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) if (q < nmb) ra[q] = ld16(xa[q] + kp_); \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                        \
+      rb[q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp_);            \
+      rb[4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp_);        \
+    }                                                                      \
+  } while (0)
+#define MOE_UP_STASH(BUF)                                                  \
+  do {                                                                     \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q)                          \
+      if (q < nmb) st16(&As[BUF][lds_off(ar0 + 32 * q, ac)], ra[q]);        \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q)                          \
+      st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[q]);                    \
+  } while (0)
 
-  const int nkb = H >> 6;
+  MOE_UP_ISSUE(0);
+  MOE_UP_STASH(0);
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
     const int cur = kb & 1;
     const bool more = kb + 1 < nkb;
-    if (more) {
-      const int k1 = (kb + 1) << 6;
-      if (aload) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ra[q] = ld16(xa + k1 + 8 * q);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        nbg[s] = ld16(wg + k1 + 8 * s);
-        nbu[s] = ld16(wu + k1 + 8 * s);
-      }
-    }
+    if (more) MOE_UP_ISSUE(kb + 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const int c = 4 * half + s;
+      const u32x4_t bg = ld16(&Bs[wave][lds_off(j, c)]);
+      const u32x4_t bu = ld16(&Bs[wave][lds_off(32 + j, c)]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 2; ++mb) {
         if (mb < nmb) {
-          const u32x4_t a = ld16(&As[cur][mb * 32 + j][32 * half + 8 * s]);
-          accg[mb] = mfma32x32x16(a, bg[s], accg[mb]);
-          accu[mb] = mfma32x32x16(a, bu[s], accu[mb]);
+          const u32x4_t a = ld16(&As[cur][lds_off(mb * 32 + j, c)]);
+          accg[mb] = mfma32x32x16(a, bg, accg[mb]);
+          accu[mb] = mfma32x32x16(a, bu, accu[mb]);
         }
       }
     }
-    if (more) {
-      if (aload) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st16(&As[cur ^ 1][arow][acol + 8 * q], ra[q]);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bg[s] = nbg[s];
-        bu[s] = nbu[s];
-      }
-    }
+    // the B area is private to the wave: overwriting it after this block's
+    // reads is ordered by the wave's own LDS instruction order
+    if (more) MOE_UP_STASH(cur ^ 1);
   }
+#undef MOE_UP_ISSUE
+#undef MOE_UP_STASH
 
   uint16_t* ohi = shared ? sact_hi : act_hi;
   uint16_t* olo = shared ? sact_lo : act_lo;
   float* ogu = shared ? sgu : gu;
   const int64_t p0 = shared ? row0 : static_cast<int64_t>(seg0) + row0;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < 2; ++mb) {
     if (mb < nmb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -179,8 +201,10 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 // ---------------------------------------------------------------------------
 // Down projection: y = act W2^T with act = hi + lo (two MFMA passes into the
 // same fp32 accumulator, hi first), written to route row sorted_route[p] of y
-// (or token row of shared_y).  Work item = (row tile, 256 hidden columns);
-// wave w owns columns nt*256 + 64w .. +64 as two 32-column blocks.
+// (or token row of shared_y).  Work item = (row tile, 128 hidden columns);
+// wave w owns columns nt*128 + 32w .. +32.  Same staging as the up
+// projection: the wave's 32 W2 rows through a private LDS area, the act
+// planes through a double-buffered shared one.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     const uint16_t* __restrict__ act_hi, const uint16_t* __restrict__ act_lo,
@@ -203,12 +227,10 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   const int nmb = (rows + 31) >> 5;
   const uint16_t* W = shared ? ws2 : w2 + static_cast<int64_t>(grp) * H * I;
   const int64_t p0 = shared ? row0 : static_cast<int64_t>(seg0) + row0;
-  const uint16_t* Ahi = (shared ? sact_hi : act_hi) + p0 * Ie;
-  const uint16_t* Alo = (shared ? sact_lo : act_lo) + p0 * Ie;
   float* out = shared ? sy : y;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][kRowsPerTile][kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Al[2][kRowsPerTile][kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][2][kRowsPerTile * 64];  // [buf][hi/lo]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[4][32 * 64];
   __shared__ int s_dst[kRowsPerTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -228,105 +250,84 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     s_dst[tid] = dst;
   }
 
-  const int arow = tid >> 1, acol = (tid & 1) * 32;
-  const bool aload = arow < nmb * 32;
-  const int64_t aoff = static_cast<int64_t>(min(arow, rows - 1)) * Ie + acol;
-
-  const int n0 = nt * kDownCols + wave * 64;
-  const uint16_t* wb0 = W + static_cast<int64_t>(n0 + j) * Ie + 32 * half;
-  const uint16_t* wb1 = W + static_cast<int64_t>(n0 + 32 + j) * Ie + 32 * half;
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    acc[mb][0] = zero16();
-    acc[mb][1] = zero16();
-  }
-  u32x4_t rh[4], rl[4], b0[4], b1[4], nb0[4], nb1[4];
-
-  if (aload) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      rh[q] = ld16(Ahi + aoff + 8 * q);
-      rl[q] = ld16(Alo + aoff + 8 * q);
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    b0[s] = ld16(wb0 + 8 * s);
-    b1[s] = ld16(wb1 + 8 * s);
-  }
-  if (aload) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      st16(&Ah[0][arow][acol + 8 * q], rh[q]);
-      st16(&Al[0][arow][acol + 8 * q], rl[q]);
-    }
-  }
-
   const int nkb = Ie >> 6;
+  const int rot = k_rotation(grp, nt, nkb);
+  const int ac = tid & 7, ar0 = tid >> 3;
+  const uint16_t* ahi = (shared ? sact_hi : act_hi) + p0 * Ie + ac * 8;
+  const uint16_t* alo = (shared ? sact_lo : act_lo) + p0 * Ie + ac * 8;
+  int64_t aoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) aoff[q] = static_cast<int64_t>(min(ar0 + 32 * q, rows - 1)) * Ie;
+  const int bc = lane & 7, br8 = lane >> 3;
+  const int n0 = nt * kDownCols + wave * 32;
+  const uint16_t* wb = W + static_cast<int64_t>(n0 + br8) * Ie + bc * 8;
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) acc[mb] = zero16();
+  u32x4_t rh[2], rl[2], rb[4];
+
+#define MOE_DN_ISSUE(KB)                                                   \
+  do {                                                                     \
+    int kk_ = (KB) + rot;                                                  \
+    if (kk_ >= nkb) kk_ -= nkb;                                            \
+    const int kp_ = kk_ << 6;                                              \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                        \
+      if (q < nmb) {                                                       \
+        rh[q] = ld16(ahi + aoff[q] + kp_);                                 \
+        rl[q] = ld16(alo + aoff[q] + kp_);                                 \
+      }                                                                    \
+    }                                                                      \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                          \
+      rb[q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp_);            \
+  } while (0)
+#define MOE_DN_STASH(BUF)                                                  \
+  do {                                                                     \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                        \
+      if (q < nmb) {                                                       \
+        st16(&As[BUF][0][lds_off(ar0 + 32 * q, ac)], rh[q]);                \
+        st16(&As[BUF][1][lds_off(ar0 + 32 * q, ac)], rl[q]);                \
+      }                                                                    \
+    }                                                                      \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                          \
+      st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[q]);                    \
+  } while (0)
+
+  MOE_DN_ISSUE(0);
+  MOE_DN_STASH(0);
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
     const int cur = kb & 1;
     const bool more = kb + 1 < nkb;
-    if (more) {
-      const int k1 = (kb + 1) << 6;
-      if (aload) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          rh[q] = ld16(Ahi + aoff + k1 + 8 * q);
-          rl[q] = ld16(Alo + aoff + k1 + 8 * q);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        nb0[s] = ld16(wb0 + k1 + 8 * s);
-        nb1[s] = ld16(wb1 + k1 + 8 * s);
-      }
-    }
+    if (more) MOE_DN_ISSUE(kb + 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const int c = 4 * half + s;
+      const u32x4_t b = ld16(&Bs[wave][lds_off(j, c)]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 2; ++mb) {
         if (mb < nmb) {
-          const u32x4_t ah = ld16(&Ah[cur][mb * 32 + j][32 * half + 8 * s]);
-          const u32x4_t al = ld16(&Al[cur][mb * 32 + j][32 * half + 8 * s]);
-          acc[mb][0] = mfma32x32x16(ah, b0[s], acc[mb][0]);
-          acc[mb][0] = mfma32x32x16(al, b0[s], acc[mb][0]);
-          acc[mb][1] = mfma32x32x16(ah, b1[s], acc[mb][1]);
-          acc[mb][1] = mfma32x32x16(al, b1[s], acc[mb][1]);
+          const u32x4_t ah = ld16(&As[cur][0][lds_off(mb * 32 + j, c)]);
+          const u32x4_t al = ld16(&As[cur][1][lds_off(mb * 32 + j, c)]);
+          acc[mb] = mfma32x32x16(ah, b, acc[mb]);
+          acc[mb] = mfma32x32x16(al, b, acc[mb]);
         }
       }
     }
-    if (more) {
-      if (aload) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          st16(&Ah[cur ^ 1][arow][acol + 8 * q], rh[q]);
-          st16(&Al[cur ^ 1][arow][acol + 8 * q], rl[q]);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        b0[s] = nb0[s];
-        b1[s] = nb1[s];
-      }
-    }
+    if (more) MOE_DN_STASH(cur ^ 1);
   }
+#undef MOE_DN_ISSUE
+#undef MOE_DN_STASH
 
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < 2; ++mb) {
     if (mb < nmb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = mb * 32 + acc_row(v, half);
         if (row < rows) {
           const int dst = s_dst[row];
-          if (dst >= 0) {
-            float* o = out + static_cast<int64_t>(dst) * H + n0 + j;
-            o[0] = acc[mb][0][v];
-            o[32] = acc[mb][1][v];
-          }
+          if (dst >= 0) out[static_cast<int64_t>(dst) * H + n0 + j] = acc[mb][v];
         }
       }
     }

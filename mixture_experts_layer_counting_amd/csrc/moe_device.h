@@ -11,12 +11,12 @@ typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
 namespace moe {
 
-// Routed rows per grouped-GEMM work item (four 32-row MFMA blocks).
-constexpr int kRowsPerTile = 128;
+// Routed rows per grouped-GEMM work item (two 32-row MFMA blocks).
+constexpr int kRowsPerTile = 64;
 // Activation columns per up-projection work item (four waves x 32).
 constexpr int kUpCols = 128;
-// Hidden columns per down-projection work item (four waves x 64).
-constexpr int kDownCols = 256;
+// Hidden columns per down-projection work item (four waves x 32).
+constexpr int kDownCols = 128;
 // Tokens per block of the permutation's counting sort.
 constexpr int kSortBlock = 256;
 

@@ -52,69 +52,140 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // Router logits: l[t][e] = sum_h x[t][h] * wr[e][h] (+ bias[e]).
 //
 // With wr = hi + mid + lo (router_split_kernel) every product with the bf16
-// activation is exact on the matrix cores.  Each 256-wide K chunk is
-// accumulated in fp32 by 48 MFMAs (16 K-steps, each hi then mid then lo)
-// from zero; the chunk sums are added in fp64 in ascending chunk order and
-// rounded once to fp32.  A logit's arithmetic depends only on its own token
-// row and expert row, never on the batch.
+// activation is exact on the matrix cores.  K runs in 32-wide blocks staged
+// through double-buffered LDS; inside a block, K step s and lane half h
+// cover k = 16s + 8h .. +8, and each step adds hi, then mid, then lo.  The
+// MFMA partial of eight blocks (256 of K) starts from zero and is then added
+// to an fp64 sum, in ascending order; the logit is that sum (+ bias) rounded
+// once to fp32.  A logit's arithmetic depends only on its own token row and
+// expert row, never on the batch or the tile it falls in.
 //
-// Grid: (ceil(T/128), ceil(E/128)), 512 threads.  Wave w computes tokens
-// t0 + 32*(w&3) .. +32 against experts e0 + 64*(w>>2) .. +64 (two 32-wide
-// blocks).  Inside a chunk, lane half h and K-step s use k = 128h + 8s .. +8,
-// so each lane reads one contiguous 256-byte run per operand row.
+// Workgroup tile: WM*64 tokens x 128 experts, four waves in a 2x2 grid, wave
+// (wt, we) owning tokens wt*WM*32 .. +WM*32 and experts we*64 .. +64.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ planes,
-                                                            const float* __restrict__ bias,
-                                                            float* __restrict__ logits, int64_t T,
-                                                            int H, int E) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = lane & 31, half = lane >> 5;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 128 + 32 * (wave & 3);
-  const int e0 = blockIdx.y * 128 + 64 * (wave >> 2);
-  if (t0 >= T || e0 >= E) return;  // E is a multiple of 64: a wave's experts are all in or all out
-  int64_t trow = t0 + i;
-  if (trow > T - 1) trow = T - 1;
-  const int64_t n = static_cast<int64_t>(E) * H;
-  const uint16_t* xr = x + trow * H + 128 * half;
-  const uint16_t* w0 = planes + static_cast<int64_t>(e0 + i) * H + 128 * half;
-  const uint16_t* w1 = w0 + static_cast<int64_t>(32) * H;
+constexpr int kRtBK = 32;      // K block
+constexpr int kRtStride = 40;  // LDS row stride (bf16): 32 + 8 padding, conflict-free fragment reads
 
-  double acc[2][16];
+template <int WM>
+__global__ __launch_bounds__(256, 3 - WM) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ planes,
+                                                               const float* __restrict__ bias,
+                                                               float* __restrict__ logits,
+                                                               int64_t T, int H, int E) {
+  constexpr int BM = WM * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM][kRtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][3][128][kRtStride];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 31, half = lane >> 5;
+  const int wt = wave & 1, we = wave >> 1;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int e0 = blockIdx.y * 128;
+  const int64_t n = static_cast<int64_t>(E) * H;
+  const int ecount = min(128, E - e0);  // 64 or 128 (E is a multiple of 64)
+
+  // loader roles: row r = tid >> 2 (0..63), 16-byte chunk c = tid & 3
+  const int lr = tid >> 2, lc = (tid & 3) * 8;
+  const uint16_t* xsrc[WM];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    acc[0][v] = 0.0;
-    acc[1][v] = 0.0;
+  for (int q = 0; q < WM; ++q) {
+    int64_t t = t0 + q * 64 + lr;
+    if (t > T - 1) t = T - 1;
+    xsrc[q] = x + t * H + lc;
   }
-  for (int c = 0; c < H; c += 256) {
-    f32x16_t p0 = zero16(), p1 = zero16();
-#pragma unroll 4
-    for (int s = 0; s < 16; ++s) {
-      const int k = c + 8 * s;
-      const u32x4_t a = ld16(xr + k);
-      const u32x4_t h0 = ld16(w0 + k), m0 = ld16(w0 + n + k), l0 = ld16(w0 + 2 * n + k);
-      const u32x4_t h1 = ld16(w1 + k), m1 = ld16(w1 + n + k), l1 = ld16(w1 + 2 * n + k);
-      p0 = mfma32x32x16(a, h0, p0);
-      p1 = mfma32x32x16(a, h1, p1);
-      p0 = mfma32x32x16(a, m0, p0);
-      p1 = mfma32x32x16(a, m1, p1);
-      p0 = mfma32x32x16(a, l0, p0);
-      p1 = mfma32x32x16(a, l1, p1);
-    }
+  const uint16_t* wsrc[2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      acc[0][v] += static_cast<double>(p0[v]);
-      acc[1][v] += static_cast<double>(p1[v]);
+  for (int q = 0; q < 2; ++q) {
+    const int e = min(e0 + q * 64 + lr, E - 1);
+    wsrc[q] = planes + static_cast<int64_t>(e) * H + lc;
+  }
+
+  u32x4_t rx[WM], rw[3][2];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < WM; ++q) rx[q] = ld16(xsrc[q] + k0);
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) rw[pl][q] = ld16(wsrc[q] + pl * n + k0);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < WM; ++q) st16(&Xs[buf][q * 64 + lr][lc], rx[q]);
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) st16(&Ws[buf][pl][q * 64 + lr][lc], rw[pl][q]);
+    }
+  };
+
+  f32x16_t part[WM][2];
+  double acc[WM][2][16];
+#pragma unroll
+  for (int mb = 0; mb < WM; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      part[mb][nb] = zero16();
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.0;
     }
   }
+
+  const int nkb = H / kRtBK;
+  fetch(0);
+  stash(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();
+    const int cur = kb & 1;
+    const bool more = kb + 1 < nkb;
+    if (more) fetch((kb + 1) * kRtBK);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4_t a[WM], b[2][3];
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
+        a[mb] = ld16(&Xs[cur][wt * WM * 32 + mb * 32 + i][16 * s + 8 * half]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) b[nb][pl] = ld16(&Ws[cur][pl][we * 64 + nb * 32 + i][16 * s + 8 * half]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int pl = 0; pl < 3; ++pl) part[mb][nb] = mfma32x32x16(a[mb], b[nb][pl], part[mb][nb]);
+        }
+      }
+    }
+    if ((kb & 7) == 7 || kb == nkb - 1) {
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[mb][nb][v] += static_cast<double>(part[mb][nb][v]);
+          part[mb][nb] = zero16();
+        }
+      }
+    }
+    if (more) stash(cur ^ 1);
+  }
+
+  if (we * 64 >= ecount) return;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int e = e0 + 32 * nb + i;
+    const int e = e0 + we * 64 + nb * 32 + i;
     const double b = bias ? static_cast<double>(bias[e]) : 0.0;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t t = t0 + acc_row(v, half);
-      if (t < T) logits[t * E + e] = static_cast<float>(acc[nb][v] + b);
+    for (int mb = 0; mb < WM; ++mb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t t = t0 + wt * WM * 32 + mb * 32 + acc_row(v, half);
+        if (t < T) logits[t * E + e] = static_cast<float>(acc[mb][nb][v] + b);
+      }
     }
   }
 }
@@ -412,8 +483,15 @@ hipError_t launch_router_split(const float* wr, uint16_t* planes, int H, int E, 
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* planes, const float* bias,
                                 float* logits, int64_t T, int H, int E, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>((E + 127) / 128));
-  router_logits_kernel<<<grid, 512, 0, stream>>>(x, planes, bias, logits, T, H, E);
+  // the token tile only changes which tokens share a workgroup, never a
+  // logit's arithmetic; small batches use the smaller tile to fill the GPU
+  if (T >= 4096) {
+    dim3 grid(static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>((E + 127) / 128));
+    router_logits_kernel<2><<<grid, 256, 0, stream>>>(x, planes, bias, logits, T, H, E);
+  } else {
+    dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>((E + 127) / 128));
+    router_logits_kernel<1><<<grid, 256, 0, stream>>>(x, planes, bias, logits, T, H, E);
+  }
   return hipGetLastError();
 }
 
