@@ -196,6 +196,54 @@ def summarize(cfg, r, steps):
     )
 
 
+def run_backward(cfg, steps, warmup):
+    """Forward (training mode) once, then `steps` timed backward passes of
+    the same batch (HIP-event timed on the kernels' stream)."""
+    import torch
+    import mixture_experts_layer_counting_amd as m
+    import workloads as W
+    dev = torch.device("cuda:0")
+    w = device_layer(W.make_layer(cfg))
+    x = torch.from_numpy(W.tokens(cfg).view(np.int16)).to(dev)
+    dout = torch.from_numpy(W.grad_out(cfg).view(np.int16)).to(dev)
+    d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD, dev)
+    routes = m.alloc_routes(d, dev, logits=False)
+    saved = m.alloc_saved(d, dev, training=True)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev)
+    m.check(m.moe_forward(d, w, x, routes, saved, None, out16, ws), "moe_forward")
+    grads = m.alloc_grads(d, dev)
+    dx32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def bwd():
+        m.check(m.moe_backward(d, w, x, routes, saved, dout, dx32, None, grads, ws, stream), "moe_backward")
+
+    for _ in range(warmup):
+        bwd()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    touched = int((np.diff(routes.expert_offsets.cpu().numpy()) > 0).sum())
+    H, I, Is, T, R, E = cfg.hidden, cfg.inter, cfg.shared_inter, cfg.tokens, cfg.routes, cfg.experts
+    # algorithmic bytes: weights read, fp32 weight gradients written, per-route
+    # and per-token activations read once (Y, gate/up, x, dOut), dx route rows
+    # written and read once, dX written
+    byts = (touched * 3 * I * H * 2 + 3 * Is * H * 2 + E * H * 4 + touched * 3 * I * H * 4 + 3 * Is * H * 4
+            + E * H * 4 + R * H * 4 + R * 2 * I * 4 + T * 2 * Is * 4 + T * H * 4 + 2 * T * H * 2
+            + R * H * 4 * 2 + T * H * 4)
+    flop = 2 * 2 * (R * 3 * I * H + T * 3 * Is * H)
+    t_roof = max(flop / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
+    return {"workload": f"{cfg.name}: {T} tokens backward", "ms": ms, "tokens_per_s": T / (ms / 1e3),
+            "bytes": byts, "flop": flop, "t_roof_ms": t_roof * 1e3, "roofline_frac": t_roof / (ms / 1e3),
+            "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9)}
+
+
 def cpu_baseline(cfg, layer, budget_s=12.0):
     """The FP64 oracle as it stands, on the first tokens of the same workload,
     64 at a time until `budget_s` seconds have passed."""
@@ -226,6 +274,7 @@ def main():
     ap.add_argument("--config", default="moe1k")
     ap.add_argument("--secondary", default="moe8k", help="second workload to report, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", default="bwd4k", help="workload of the backward timing, or 'none'")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -269,6 +318,12 @@ def main():
         secondary[c2.name] = summarize(c2, r2, args.steps)
         log(f"bench: {c2.name} {secondary[c2.name]['ms_per_step']:.3f} ms/step")
 
+    backward = None
+    if args.backward != "none":
+        log(f"bench: backward {args.backward}")
+        backward = run_backward(W.CONFIGS[args.backward], max(3, args.steps // 4), 1)
+        log(f"bench: backward {backward['ms']:.3f} ms")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
@@ -304,6 +359,7 @@ def main():
         "ffn_down_gbs": main_s["ffn_down_gbs"],
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 
