@@ -11,11 +11,10 @@
 //
 // Precision: products of bf16 values are exact on the matrix cores; an fp32
 // operand (activation gradients, gate-scaled activations) enters split
-// exactly into three bf16 parts (hi + mid + lo), i.e. three MFMA passes.
-// Each 32-wide K block is summed in fp32 on the matrix cores and the block
-// sums are accumulated in fp64, so long contractions (weight gradients sum
-// over every route of an expert, or every token for the shared expert) do
-// not lose precision as the sum grows.
+// exactly into three bf16 parts (hi + mid + lo), i.e. three MFMAs per K step.
+// The grouped GEMMs accumulate in fp32 on the matrix cores in a fixed K
+// order; the small reductions (route weights, shared gate, router weights)
+// accumulate in fp64.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -88,38 +87,75 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Generic grouped GEMM for the expert backward: D[m][n] = sum_k A[m][k] B[n][k]
-// over 64x64 output tiles, 32-wide K blocks staged in LDS (one block of
-// register prefetch), four waves each owning one 32x32 MFMA block.
+// Grouped GEMMs of the expert backward: D[m][n] = sum_k A[m][k] B[k][n] over
+// 128x128 output tiles and 32-wide K blocks; four waves in a 2x2 grid, each
+// owning a 64x64 block (2x2 MFMA 32x32x16 blocks) accumulated in fp32 on the
+// matrix cores.
 //
-// Operands are staged in LDS as [row][k] (row = m for A, n for B), loaded
-// either from k-contiguous rows (one 16-byte store per thread) or from
-// sources whose rows are indexed by k (transposed on the way into LDS).  An
-// operand given as three bf16 planes (hi, mid, lo) takes three MFMA passes
-// in that order.  Per K block the passes accumulate in fp32 from zero; the
-// block sums are added in fp64 in ascending block order.
+// Operands are staged in LDS, two stages: the next K block's global loads are
+// issued before the current block's MFMAs and stored to the other stage after
+// them, so one barrier per block separates the stages.  Two LDS layouts:
+//   * [row][k] (80-byte rows) for sources stored k-contiguous (the routed or
+//     token rows of a dgrad); fragments are 16-byte LDS loads;
+//   * [k][col] (288-byte rows) for sources whose rows are indexed by k (the
+//     expert weights read along their output dimension, and both operands
+//     of a weight gradient, whose contraction runs over the routes of an
+//     expert).  Rows are stored as the 16-byte pieces they are loaded in and
+//     fragments are read with the gfx950 LDS transpose read
+//     (ds_read_b64_tr_b16), two per fragment.  Consecutive 288-byte rows
+//     start 32 bytes apart in the bank space, so those reads are free of
+//     bank conflicts.
+// An operand given as three bf16 planes (hi, mid, lo) takes three MFMAs per
+// K step, in that order.
 //
 // Modes (group g: routed expert g < E, shared expert g == E; p = row of the
-// group's segment, t(p) its token):
-//   kDact: rows p, n = i < Ie, k = h < H.  A = dOut[t(p)][h]; B = W2_g[h][i]
-//          (transposed).  Epilogue: dact = acc * g_p; SwiGLU backward with the
-//          saved gate/up -> dGU planes [p][2Ie], and g_p*act planes [p][Ie].
-//   kDx:   rows p, n = h < H, k = j < 2Ie.  A = dGU (3 planes); B = W13_g[j][h]
-//          (transposed).  Epilogue: row p of dx_route (route-major, row
+// group's segment in sorted order, t(p) its token):
+//   kDact: m = p (128-row tile), n = i < Ie, k = h < H.  A = dOut[t(p)][h]
+//          ([row][k]); B = W2_g[h][i] ([k][col]).  Epilogue: dact = D * g_p,
+//          SwiGLU backward with the saved gate/up pre-activations -> dGU
+//          planes [p][2Ie] and g_p*act planes [p][Ie].
+//   kDx:   m = p, n = h < H, k = j < 2Ie.  A = dGU planes ([row][k]);
+//          B = W13_g[j][h] ([k][col]).  Epilogue: row of dx_route (route row
 //          sorted_route[p]) or of dx_shared (token row).
 //   kDw2:  m = h < H, n = i < Ie, k = p over the segment.  A = dOut[t(p)][h]
-//          (transposed, gathered); B = g*act [p][i] (transposed, 3 planes).
+//          ([k][col], gathered rows); B = g*act planes [p][i] ([k][col]).
 //          Epilogue: dW2_g[h][i].
-//   kDw13: m = j < 2Ie, n = h < H, k = p.  A = dGU[p][j] (transposed, 3 planes);
-//          B = x[t(p)][h] (transposed, gathered).  Epilogue: dW13_g[j][h].
-// The K order of every output element is fixed: ascending 32-wide blocks, in
-// each block K-step 0 then 1, lane half 0 then 1 inside the MFMA.
+//   kDw13: m = j < 2Ie, n = h < H, k = p.  A = dGU planes [p][j] ([k][col]);
+//          B = x[t(p)][h] ([k][col], gathered rows).  Epilogue: dW13_g[j][h].
+// The K order of every output element is fixed: K blocks in ascending order
+// (for the two dgrad modes starting at a rotation fixed by the group and the
+// column tile, as in the forward), in each block K step 0 then 1, and in
+// each step the planes hi, mid, lo.  A dgrad row's result therefore depends
+// only on its own row, its expert and its column tile, never on the batch.
 // ---------------------------------------------------------------------------
 enum BwdMode { kDact = 0, kDx = 1, kDw2 = 2, kDw13 = 3 };
 
-constexpr int kBwdRows = 64;  // rows per dgrad row tile (and GEMM tile edge)
+constexpr int kBT = kBwdRowsPerTile;  // edge of every output tile (128)
 constexpr int kBK = 32;
-constexpr int kBStride = 40;  // LDS row stride in bf16 (32 + 8 padding)
+constexpr int kKStride = 40;   // [row][k] layout: 32 k + 8 padding (bf16)
+constexpr int kRStride = 144;  // [k][col] layout: 128 columns + 16 padding
+constexpr int kKPlane = kBT * kKStride;
+constexpr int kRPlane = kBK * kRStride;
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// MFMA operand for lane `lane` from a [k][col] LDS plane: column
+// col0 + lane%32, k = k0 + 8*(lane/32) .. +8.  Each transpose read gathers,
+// in a group of 16 lanes, a 4x4 block of 16-bit elements (4 k rows x 4
+// columns per lane address) and hands lane i the column i of it; the lane
+// addresses below make the 16 columns of a group consecutive.
+__device__ __forceinline__ u32x4_t frag_tr(const uint16_t* plane, int k0, int col0, int lane) {
+  const int L = lane & 15;
+  const int row = k0 + 8 * (lane >> 5) + (L >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+  const uint16_t* p = plane + row * kRStride + col;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p + 4 * kRStride));
+  const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(u32x4_t, v);
+}
 
 struct BwdArgs {
   int64_t T;
@@ -152,9 +188,9 @@ struct BwdArgs {
 
 // Work item of a grouped-GEMM launch.
 struct BwdTile {
-  int grp, m0, n0;
-  int rows;     // valid rows (dgrad) / contraction length (wgrad)
-  int seg0;     // first sorted position of the group (0 for the shared group)
+  int grp, m0, n0, nt;
+  int rows;  // valid rows (dgrad) / contraction length (wgrad)
+  int seg0;  // first sorted position of the group (0 for the shared group)
   bool shared;
   int Ie;
 };
@@ -163,30 +199,32 @@ template <int MODE>
 __device__ __forceinline__ bool bwd_decode(const BwdArgs& a, int g, BwdTile& w) {
   const int Imax = a.I > a.Is ? a.I : a.Is;
   if (MODE == kDact || MODE == kDx) {
-    const int ncol = MODE == kDact ? Imax / kBwdRows : a.H / kBwdRows;
+    const int ncol = MODE == kDact ? Imax / kBT : a.H / kBT;
     const int item = xcd_item(g, a.meta[0] * ncol);
     if (item < 0) return false;
-    const int tile = item / ncol, nt = item - tile * ncol;
+    const int tile = item / ncol;
+    w.nt = item - tile * ncol;
     w.grp = a.tiles[2 * tile];
     w.m0 = a.tiles[2 * tile + 1];
-    w.n0 = nt * kBwdRows;
+    w.n0 = w.nt * kBT;
     w.shared = w.grp == a.E;
     w.Ie = w.shared ? a.Is : a.I;
     if (MODE == kDact && w.n0 >= w.Ie) return false;
     w.seg0 = w.shared ? 0 : a.offsets[w.grp];
     const int cnt = w.shared ? static_cast<int>(a.T) : a.offsets[w.grp + 1] - w.seg0;
-    w.rows = min(kBwdRows, cnt - w.m0);
+    w.rows = min(kBT, cnt - w.m0);
     return w.rows > 0;
   }
   const int groups = a.E + (a.Is > 0 ? 1 : 0);
-  const int mt = MODE == kDw2 ? a.H / kBwdRows : 2 * Imax / kBwdRows;
-  const int nt = MODE == kDw2 ? Imax / kBwdRows : a.H / kBwdRows;
+  const int mt = MODE == kDw2 ? a.H / kBT : 2 * Imax / kBT;
+  const int nt = MODE == kDw2 ? Imax / kBT : a.H / kBT;
   const int item = xcd_item(g, groups * mt * nt);
   if (item < 0) return false;
   w.grp = item / (mt * nt);
   const int rem = item - w.grp * (mt * nt);
-  w.m0 = (rem / nt) * kBwdRows;
-  w.n0 = (rem % nt) * kBwdRows;
+  w.nt = rem % nt;
+  w.m0 = (rem / nt) * kBT;
+  w.n0 = w.nt * kBT;
   w.shared = w.grp == a.E;
   w.Ie = w.shared ? a.Is : a.I;
   if (MODE == kDw2 && w.n0 >= w.Ie) return false;
@@ -196,7 +234,7 @@ __device__ __forceinline__ bool bwd_decode(const BwdArgs& a, int g, BwdTile& w) 
   return true;
 }
 
-// token of sorted row p of a group (bounds-checked)
+// token of sorted row p of a group (route ids outside [0, T*K) map to token 0)
 __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w, int64_t p) {
   if (w.shared) return p;
   const int64_t r = a.sorted_route[p];
@@ -204,203 +242,293 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256) void bwd_gemm_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
+  constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
   constexpr int NPA = (MODE == kDx || MODE == kDw13) ? 3 : 1;
   constexpr int NPB = MODE == kDw2 ? 3 : 1;
-  constexpr bool A_TRANS = MODE == kDw2 || MODE == kDw13;
-  constexpr bool B_TRANS = true;
+  constexpr int APLANE = WGRAD ? kRPlane : kKPlane;
+  constexpr int STAGE = NPA * APLANE + NPB * kRPlane;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
   BwdTile w;
   if (!bwd_decode<MODE>(a, blockIdx.x, w)) return;
-
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][NPA][kBwdRows][kBStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][NPB][kBwdRows][kBStride];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 31, half = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
   const int Ie = w.Ie;
 
-  // contraction length and number of K blocks
   int kdim;
   if (MODE == kDact) kdim = a.H;
   else if (MODE == kDx) kdim = 2 * Ie;
   else kdim = w.rows;
   const int nkb = (kdim + kBK - 1) / kBK;
+  const int rot = WGRAD ? 0 : k_rotation(w.grp, w.nt, nkb);
 
-  // ---- per-thread load roles
-  // k-contiguous role: row lr = tid>>2 (0..63), k offset lc = (tid&3)*8
-  // transposed role: k row kr = tid>>3 (0..31), m/n offset tc = (tid&7)*8
+  // ---- load roles.  [row][k] operand: rows lr + 64c, 8 k at lc.
+  // [k][col] operands: k rows kr + 16c, 8 columns at tc.
   const int lr = tid >> 2, lc = (tid & 3) * 8;
-  const int kr = tid >> 3, tc = (tid & 7) * 8;
+  const int kr = tid >> 4, tc = (tid & 15) * 8;
 
-  // A source row pointers (k-contiguous modes)
-  const uint16_t* a_row[NPA];
-  if (!A_TRANS) {
-    const int rr = min(lr, w.rows - 1);
-    const int64_t p = static_cast<int64_t>(w.seg0) + w.m0 + rr;
-    if (MODE == kDact) {
-      a_row[0] = a.dout + bwd_token(a, w, p) * a.H;
-    } else {  // kDx: dGU row p
-      const int64_t rowp = w.shared ? (w.m0 + rr) : p;
+  // dgrad A: element offsets of this thread's two rows in the source
+  int64_t a_off[2] = {0, 0};
+  const uint16_t* a_base[NPA];
+  if (!WGRAD) {
 #pragma unroll
-      for (int q = 0; q < NPA; ++q) a_row[q] = (w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie;
-    }
-  }
-  // B source base (all modes load B transposed: B[n][k] = src[k][n])
-  const uint16_t* wbase = nullptr;
-  if (MODE == kDact) wbase = w.shared ? a.ws2 : a.w2 + static_cast<int64_t>(w.grp) * a.H * a.I;
-  if (MODE == kDx) wbase = w.shared ? a.ws13 : a.w13 + static_cast<int64_t>(w.grp) * 2 * a.I * a.H;
-
-  auto fetch = [&](int kb, u32x4_t (&ra)[NPA], u32x4_t (&rb)[NPB]) {
-    const int k0 = kb * kBK;
-    // ---- A
-    if (!A_TRANS) {
-#pragma unroll
-      for (int q = 0; q < NPA; ++q) ra[q] = ld16(a_row[q] + k0 + lc);
-    } else {
-      const int kk = k0 + kr;  // segment row
-      if (kk < w.rows) {
-        const int64_t p = static_cast<int64_t>(w.seg0) + kk;
-        if (MODE == kDw2) {
-          ra[0] = ld16(a.dout + bwd_token(a, w, p) * a.H + w.m0 + tc);
-        } else {  // kDw13: dGU[p][m]
-          const int64_t rowp = w.shared ? kk : p;
-#pragma unroll
-          for (int q = 0; q < NPA; ++q)
-            ra[q] = ld16((w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie + w.m0 + tc);
-        }
+    for (int c = 0; c < 2; ++c) {
+      const int rr = min(lr + 64 * c, w.rows - 1);
+      if (MODE == kDact) {
+        a_off[c] = bwd_token(a, w, static_cast<int64_t>(w.seg0) + w.m0 + rr) * a.H;
       } else {
-#pragma unroll
-        for (int q = 0; q < NPA; ++q) ra[q] = u32x4_t{0u, 0u, 0u, 0u};
+        const int64_t rowp = w.shared ? (w.m0 + rr) : (static_cast<int64_t>(w.seg0) + w.m0 + rr);
+        a_off[c] = rowp * 2 * Ie;
       }
     }
-    // ---- B (transposed)
-    const int kk = k0 + kr;
-    if (MODE == kDact || MODE == kDx) {
-      const int ncols = MODE == kDact ? Ie : a.H;
-      rb[0] = ld16(wbase + static_cast<int64_t>(kk) * ncols + w.n0 + tc);
-    } else if (kk < w.rows) {
-      const int64_t p = static_cast<int64_t>(w.seg0) + kk;
+    if (MODE == kDact) {
+      a_base[0] = a.dout;
+    } else {
+#pragma unroll
+      for (int q = 0; q < NPA; ++q) a_base[q] = w.shared ? a.sdgu[q] : a.dgu[q];
+    }
+  }
+  // dgrad B: the expert's weight, rows indexed by k
+  const uint16_t* wbase = nullptr;
+  int wcols = 0;
+  if (MODE == kDact) {
+    wbase = w.shared ? a.ws2 : a.w2 + static_cast<int64_t>(w.grp) * a.H * a.I;
+    wcols = Ie;
+  }
+  if (MODE == kDx) {
+    wbase = w.shared ? a.ws13 : a.w13 + static_cast<int64_t>(w.grp) * 2 * a.I * a.H;
+    wcols = a.H;
+  }
+
+  // wgrad: token of each of this thread's two k rows in the block being
+  // fetched next (-1: beyond the segment); the gathered operand's rows.
+  int64_t tok[2] = {-1, -1};
+  auto wg_tokens = [&](int kb, int64_t (&t)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int kk = kb * kBK + kr + 16 * c;
+      t[c] = kk < w.rows ? bwd_token(a, w, static_cast<int64_t>(w.seg0) + kk) : -1;
+    }
+  };
+
+  u32x4_t ra[NPA][2], rb[NPB][2];
+  auto fetch = [&](int kb) {
+    const int k0 = kb * kBK;
+    if (!WGRAD) {
+#pragma unroll
+      for (int q = 0; q < NPA; ++q)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) ra[q][c] = ld16(a_base[q] + a_off[c] + k0 + lc);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        rb[0][c] = ld16(wbase + static_cast<int64_t>(k0 + kr + 16 * c) * wcols + w.n0 + tc);
+      return;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int kk = k0 + kr + 16 * c;
+      const bool in = kk < w.rows;
+      const int64_t rowp = w.shared ? kk : static_cast<int64_t>(w.seg0) + kk;
       if (MODE == kDw2) {
-        const int64_t rowp = w.shared ? kk : p;
+        // A = dOut[t(p)][m0 + tc], B = g*act planes [p][n0 + tc]
+        ra[0][c] = in ? ld16(a.dout + tok[c] * a.H + w.m0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int q = 0; q < NPB; ++q)
-          rb[q] = ld16((w.shared ? a.sgact[q] : a.gact[q]) + rowp * Ie + w.n0 + tc);
-      } else {  // kDw13: x[t(p)][n]
-        rb[0] = ld16(a.x + bwd_token(a, w, p) * a.H + w.n0 + tc);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < NPB; ++q) rb[q] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-
-  auto stash = [&](int buf, const u32x4_t (&ra)[NPA], const u32x4_t (&rb)[NPB]) {
-#pragma unroll
-    for (int q = 0; q < NPA; ++q) {
-      if (!A_TRANS) {
-        st16(&As[buf][q][lr][lc], ra[q]);
+          rb[q][c] = in ? ld16((w.shared ? a.sgact[q] : a.gact[q]) + rowp * Ie + w.n0 + tc)
+                        : u32x4_t{0u, 0u, 0u, 0u};
       } else {
+        // A = dGU planes [p][m0 + tc], B = x[t(p)][n0 + tc]
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          As[buf][q][tc + e][kr] = static_cast<uint16_t>(ra[q][e >> 1] >> (16 * (e & 1)));
+        for (int q = 0; q < NPA; ++q)
+          ra[q][c] = in ? ld16((w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie + w.m0 + tc)
+                        : u32x4_t{0u, 0u, 0u, 0u};
+        rb[0][c] = in ? ld16(a.x + tok[c] * a.H + w.n0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
+  };
+  auto stash = [&](int stage) {
+    uint16_t* s = smem + stage * STAGE;
 #pragma unroll
-    for (int q = 0; q < NPB; ++q) {
+    for (int q = 0; q < NPA; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Bs[buf][q][tc + e][kr] = static_cast<uint16_t>(rb[q][e >> 1] >> (16 * (e & 1)));
-    }
+      for (int c = 0; c < 2; ++c) {
+        if (!WGRAD) st16(s + q * APLANE + (lr + 64 * c) * kKStride + lc, ra[q][c]);
+        else st16(s + q * APLANE + (kr + 16 * c) * kRStride + tc, ra[q][c]);
+      }
+#pragma unroll
+    for (int q = 0; q < NPB; ++q)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) st16(s + NPA * APLANE + q * kRPlane + (kr + 16 * c) * kRStride + tc, rb[q][c]);
   };
 
-  double acc[16];
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0;
-  u32x4_t ra[NPA], rb[NPB];
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
+
   if (nkb > 0) {
-    fetch(0, ra, rb);
-    stash(0, ra, rb);
+    if (WGRAD) wg_tokens(0, tok);
+    fetch(rot);
+    stash(0);
+    if (WGRAD && nkb > 1) wg_tokens(1, tok);
   }
-  for (int kb = 0; kb < nkb; ++kb) {
+  for (int it = 0; it < nkb; ++it) {
     __syncthreads();
-    const int cur = kb & 1;
-    const bool more = kb + 1 < nkb;
-    if (more) fetch(kb + 1, ra, rb);
-    f32x16_t part = zero16();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4_t fa[NPA], fb[NPB];
-#pragma unroll
-      for (int q = 0; q < NPA; ++q) fa[q] = ld16(&As[cur][q][wm * 32 + i][16 * s + 8 * half]);
-#pragma unroll
-      for (int q = 0; q < NPB; ++q) fb[q] = ld16(&Bs[cur][q][wn * 32 + i][16 * s + 8 * half]);
-      // at most one operand has several planes
-#pragma unroll
-      for (int q = 0; q < NPA; ++q) part = mfma32x32x16(fa[q], fb[0], part);
-#pragma unroll
-      for (int q = 1; q < NPB; ++q) part = mfma32x32x16(fa[0], fb[q], part);
+    const int cur = it & 1;
+    const bool more = it + 1 < nkb;
+    if (more) {
+      int kn = rot + it + 1;
+      if (kn >= nkb) kn -= nkb;
+      fetch(kn);
+      if (WGRAD && it + 2 < nkb) wg_tokens(it + 2, tok);
     }
+    const uint16_t* s = smem + cur * STAGE;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] += static_cast<double>(part[v]);
-    if (more) stash(cur ^ 1, ra, rb);
+    for (int st = 0; st < 2; ++st) {
+      u32x4_t fa[2][NPA], fb[2][NPB];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int q = 0; q < NPA; ++q) {
+          if (!WGRAD)
+            fa[mb][q] = ld16(s + q * APLANE + (wm * 64 + mb * 32 + i) * kKStride + 16 * st + 8 * half);
+          else
+            fa[mb][q] = frag_tr(s + q * APLANE, 16 * st, wm * 64 + mb * 32, lane);
+        }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < NPB; ++q) fb[nb][q] = frag_tr(s + NPA * APLANE + q * kRPlane, 16 * st, wn * 64 + nb * 32, lane);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          // at most one operand has several planes
+#pragma unroll
+          for (int q = 0; q < NPA; ++q) acc[mb][nb] = mfma32x32x16(fa[mb][q], fb[nb][0], acc[mb][nb]);
+#pragma unroll
+          for (int q = 1; q < NPB; ++q) acc[mb][nb] = mfma32x32x16(fa[mb][0], fb[nb][q], acc[mb][nb]);
+        }
+    }
+    if (more) stash(cur ^ 1);
   }
 
-  // ---- epilogue: lane holds D[m0 + wm*32 + acc_row(v)][n0 + wn*32 + i]
-  const int col = w.n0 + wn * 32 + i;
+  if (MODE == kDact) {
+    // D goes through LDS one 64-row half at a time; then each thread takes
+    // 8 consecutive columns of a row for the SwiGLU backward, so the saved
+    // pre-activations are read and the gradient planes written 16 bytes at a
+    // time.
+    constexpr int ES = kBT + 4;  // fp32 row stride of a staged half
+    static_assert(64 * ES * 4 <= 2 * STAGE * 2, "a staged half fits in the operand stages");
+    float* ep = reinterpret_cast<float*>(smem);
+    const int er = tid >> 4, ec = (tid & 15) * 8;
+    for (int hh = 0; hh < 2; ++hh) {
+      __syncthreads();
+      if (wm == hh) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int lrow = wm * 32 + acc_row(v, half);
-    const float val = static_cast<float>(acc[v]);
-    if (MODE == kDact) {
-      if (lrow >= w.rows) continue;
-      const int64_t p = static_cast<int64_t>(w.seg0) + w.m0 + lrow;  // sorted row / token
-      float g;
-      int64_t rowp;
-      if (w.shared) {
-        rowp = w.m0 + lrow;
-        g = a.sg[rowp];
-      } else {
-        rowp = p;
-        const int64_t r = a.sorted_route[p];
-        g = (r >= 0 && r < a.T * a.K) ? a.gate[r] : 0.f;
-      }
-      const float* gur = (w.shared ? a.sgu : a.gu) + rowp * 2 * Ie;
-      const float gv = gur[col], uv = gur[Ie + col];
-      const float dact = val * g;
-      const float sgm = 1.0f / (1.0f + expf(-gv));
-      const float dgate = dact * uv * sgm * (1.0f + gv * (1.0f - sgm));
-      const float silu = silu_f32(gv);
-      const float dup = dact * silu;
-      const float gact = g * (silu * uv);
-      uint16_t pg[3], pu[3], pa[3];
-      split3(dgate, pg);
-      split3(dup, pu);
-      split3(gact, pa);
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        uint16_t* dq = (w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie;
-        dq[col] = pg[q];
-        dq[Ie + col] = pu[q];
-        (w.shared ? a.sgact[q] : a.gact[q])[rowp * Ie + col] = pa[q];
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              ep[(mb * 32 + acc_row(v, half)) * ES + wn * 64 + nb * 32 + i] = acc[mb][nb][v];
       }
-    } else if (MODE == kDx) {
-      if (lrow >= w.rows) continue;
-      if (w.shared) {
-        a.dx_shared[static_cast<int64_t>(w.m0 + lrow) * a.H + col] = val;
-      } else {
-        const int64_t r = a.sorted_route[static_cast<int64_t>(w.seg0) + w.m0 + lrow];
-        if (r >= 0 && r < a.T * a.K) a.dx_route[r * a.H + col] = val;
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int lrow = hh * 64 + er + 16 * c;
+        if (lrow >= w.rows) continue;
+        float g;
+        int64_t rowp;
+        if (w.shared) {
+          rowp = w.m0 + lrow;
+          g = a.sg[rowp];
+        } else {
+          rowp = static_cast<int64_t>(w.seg0) + w.m0 + lrow;
+          const int64_t r = a.sorted_route[rowp];
+          g = (r >= 0 && r < a.T * a.K) ? a.gate[r] : 0.f;
+        }
+        const int col = w.n0 + ec;
+        const float* gur = (w.shared ? a.sgu : a.gu) + rowp * 2 * Ie;
+        const f32x4v_t* dsrc = reinterpret_cast<const f32x4v_t*>(ep + (er + 16 * c) * ES + ec);
+        const f32x4v_t d0 = dsrc[0], d1 = dsrc[1];
+        const f32x4v_t g0 = *reinterpret_cast<const f32x4v_t*>(gur + col);
+        const f32x4v_t g1 = *reinterpret_cast<const f32x4v_t*>(gur + col + 4);
+        const f32x4v_t u0 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col);
+        const f32x4v_t u1 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col + 4);
+        uint32_t pg[3][4], pu[3][4], pa[3][4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float dv = e < 4 ? d0[e] : d1[e - 4];
+          const float gv = e < 4 ? g0[e] : g1[e - 4];
+          const float uv = e < 4 ? u0[e] : u1[e - 4];
+          const float dact = dv * g;
+          const float sgm = 1.0f / (1.0f + expf(-gv));
+          const float dgate = dact * uv * sgm * (1.0f + gv * (1.0f - sgm));
+          const float silu = silu_f32(gv);
+          const float dup = dact * silu;
+          const float gact = g * (silu * uv);
+          uint16_t sg3[3], su3[3], sa3[3];
+          split3(dgate, sg3);
+          split3(dup, su3);
+          split3(gact, sa3);
+          const int sh = 16 * (e & 1);
+#pragma unroll
+          for (int q = 0; q < 3; ++q) {
+            if ((e & 1) == 0) {
+              pg[q][e >> 1] = sg3[q];
+              pu[q][e >> 1] = su3[q];
+              pa[q][e >> 1] = sa3[q];
+            } else {
+              pg[q][e >> 1] |= static_cast<uint32_t>(sg3[q]) << sh;
+              pu[q][e >> 1] |= static_cast<uint32_t>(su3[q]) << sh;
+              pa[q][e >> 1] |= static_cast<uint32_t>(sa3[q]) << sh;
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          uint16_t* dq = (w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie;
+          st16(dq + col, u32x4_t{pg[q][0], pg[q][1], pg[q][2], pg[q][3]});
+          st16(dq + Ie + col, u32x4_t{pu[q][0], pu[q][1], pu[q][2], pu[q][3]});
+          st16((w.shared ? a.sgact[q] : a.gact[q]) + rowp * Ie + col,
+               u32x4_t{pa[q][0], pa[q][1], pa[q][2], pa[q][3]});
+        }
       }
-    } else if (MODE == kDw2) {
-      const int64_t hrow = w.m0 + lrow;
-      float* o = w.shared ? a.dws2 : a.dw2 + static_cast<int64_t>(w.grp) * a.H * a.I;
-      o[hrow * Ie + col] = val;
-    } else {
-      const int64_t jrow = w.m0 + lrow;
-      float* o = w.shared ? a.dws13 : a.dw13 + static_cast<int64_t>(w.grp) * 2 * a.I * a.H;
-      o[jrow * a.H + col] = val;
+    }
+    return;
+  }
+
+  // ---- epilogue: lane holds D[wm*64 + 32mb + acc_row(v)][wn*64 + 32nb + i]
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = w.n0 + wn * 64 + nb * 32 + i;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lrow = wm * 64 + mb * 32 + acc_row(v, half);
+        const float val = acc[mb][nb][v];
+        if (MODE == kDx) {
+          if (lrow >= w.rows) continue;
+          if (w.shared) {
+            a.dx_shared[static_cast<int64_t>(w.m0 + lrow) * a.H + col] = val;
+          } else {
+            const int64_t r = a.sorted_route[static_cast<int64_t>(w.seg0) + w.m0 + lrow];
+            if (r >= 0 && r < a.T * a.K) a.dx_route[r * a.H + col] = val;
+          }
+        } else if (MODE == kDw2) {
+          float* o = w.shared ? a.dws2 : a.dw2 + static_cast<int64_t>(w.grp) * a.H * a.I;
+          o[static_cast<int64_t>(w.m0 + lrow) * Ie + col] = val;
+        } else {
+          float* o = w.shared ? a.dws13 : a.dw13 + static_cast<int64_t>(w.grp) * 2 * a.I * a.H;
+          o[static_cast<int64_t>(w.m0 + lrow) * a.H + col] = val;
+        }
+      }
     }
   }
 }
@@ -603,15 +731,15 @@ hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
   a.dws2 = L.dws2;
   const int Imax = L.I > L.Is ? L.I : L.Is;
   auto rounds = [](int64_t items) { return static_cast<unsigned>(((items + 7) / 8) * 8); };
-  const int64_t dgrad_tiles = L.max_tiles64;
-  bwd_gemm_kernel<kDact><<<rounds(dgrad_tiles * (Imax / kBwdRows)), 256, 0, stream>>>(a);
+  const int64_t dgrad_tiles = L.max_tiles_bwd;
+  bwd_gemm_kernel<kDact><<<rounds(dgrad_tiles * (Imax / kBT)), 256, 0, stream>>>(a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  bwd_gemm_kernel<kDx><<<rounds(dgrad_tiles * (L.H / kBwdRows)), 256, 0, stream>>>(a);
+  bwd_gemm_kernel<kDx><<<rounds(dgrad_tiles * (L.H / kBT)), 256, 0, stream>>>(a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
-  bwd_gemm_kernel<kDw2><<<rounds(groups * (L.H / kBwdRows) * (Imax / kBwdRows)), 256, 0, stream>>>(a);
+  bwd_gemm_kernel<kDw2><<<rounds(groups * (L.H / kBT) * (Imax / kBT)), 256, 0, stream>>>(a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  bwd_gemm_kernel<kDw13><<<rounds(groups * (2 * Imax / kBwdRows) * (L.H / kBwdRows)), 256, 0, stream>>>(a);
+  bwd_gemm_kernel<kDw13><<<rounds(groups * (2 * Imax / kBT) * (L.H / kBT)), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

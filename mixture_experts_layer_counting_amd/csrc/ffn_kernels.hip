@@ -38,10 +38,6 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
-// K rotation of a work item: fixed per (group, column tile), so a given
-// output element always sums its K blocks in the same order.
-__device__ __forceinline__ int k_rotation(int grp, int nt, int nkb) { return (grp * 7 + nt * 3) % nkb; }
-
 // ---------------------------------------------------------------------------
 // Up projection + SwiGLU.
 // Work item = (row tile of one group, 128 activation columns).  Group g < E

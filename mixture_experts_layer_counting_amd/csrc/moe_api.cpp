@@ -33,7 +33,7 @@ struct Layout {
   size_t sact_hi = 0, sact_lo = 0;  // [T][Is] bf16
   size_t fwd_end = 0;
   // backward regions (after fwd_end)
-  size_t tiles64 = 0, meta64 = 0;    // 64-row work list
+  size_t tiles_bwd = 0, meta_bwd = 0;  // work list of the backward's row tiles
   size_t dl = 0, dz = 0;             // [T][K], [T] f32
   size_t dgu[3] = {0, 0, 0};         // [R][2I] bf16 planes (hi, mid, lo)
   size_t sdgu[3] = {0, 0, 0};        // [T][2Is]
@@ -45,7 +45,7 @@ struct Layout {
   size_t bwd_end = 0;
   int nblocks = 0;
   int max_tiles = 0;
-  int max_tiles64 = 0;
+  int max_tiles_bwd = 0;
 };
 
 Layout make_layout(const moe_dims& d) {
@@ -73,9 +73,9 @@ Layout make_layout(const moe_dims& d) {
   L.sact_lo = take(static_cast<size_t>(T) * Is * 2);
   L.fwd_end = o;
   const int64_t H = d.hidden;
-  L.max_tiles64 = static_cast<int>(moe::max_row_tiles(T, d.top_k, E, Is > 0, 64));
-  L.tiles64 = take(static_cast<size_t>(L.max_tiles64) * 2 * 4);
-  L.meta64 = take(64 * 4);
+  L.max_tiles_bwd = static_cast<int>(moe::max_row_tiles(T, d.top_k, E, Is > 0, moe::kBwdRowsPerTile));
+  L.tiles_bwd = take(static_cast<size_t>(L.max_tiles_bwd) * 2 * 4);
+  L.meta_bwd = take(64 * 4);
   L.dl = take(static_cast<size_t>(R) * 4);
   L.dz = take(static_cast<size_t>(T) * 4);
   for (int q = 0; q < 3; ++q) {
@@ -522,8 +522,9 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
   const Layout L = make_layout(d);
   const bool sh = Is > 0;
   hipStream_t s = stream;
-  MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles64),
-                                   at<int32_t>(ws, L.meta64), d.experts, d.tokens, sh, 64, s));
+  MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles_bwd),
+                                   at<int32_t>(ws, L.meta_bwd), d.experts, d.tokens, sh,
+                                   moe::kBwdRowsPerTile, s));
   MOE_LAUNCH(moe::launch_bwd_gate(d_out, saved->y, sh ? saved->shared_y : nullptr, routes->topk_gate,
                                   sh ? saved->shared_gate : nullptr, at<float>(ws, L.dl),
                                   at<float>(ws, L.dz), d.tokens, d.hidden, d.top_k, s));
@@ -534,13 +535,13 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
   b.K = d.top_k;
   b.I = d.inter;
   b.Is = d.shared_inter;
-  b.max_tiles64 = L.max_tiles64;
+  b.max_tiles_bwd = L.max_tiles_bwd;
   b.offsets = routes->expert_offsets;
   b.sorted_route = routes->sorted_route;
   b.gate = routes->topk_gate;
   b.sg = sh ? saved->shared_gate : nullptr;
-  b.tiles = at<int32_t>(ws, L.tiles64);
-  b.meta = at<int32_t>(ws, L.meta64);
+  b.tiles = at<int32_t>(ws, L.tiles_bwd);
+  b.meta = at<int32_t>(ws, L.meta_bwd);
   b.x = x;
   b.dout = d_out;
   b.w13 = w->w13;

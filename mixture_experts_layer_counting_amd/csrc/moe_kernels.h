@@ -45,12 +45,12 @@ hipError_t launch_combine(const float* y, const float* gate, const float* sy, co
 struct BwdLaunch {
   int64_t T;
   int H, E, K, I, Is;
-  int max_tiles64;
+  int max_tiles_bwd;
   const int32_t* offsets;
   const int32_t* sorted_route;
   const float* gate;
   const float* sg;
-  const int32_t* tiles;  // 64-row tiles
+  const int32_t* tiles;  // kBwdRowsPerTile-row tiles
   const int32_t* meta;
   const uint16_t* x;
   const uint16_t* dout;
