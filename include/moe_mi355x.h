@@ -184,7 +184,7 @@ int moe_combine(const moe_dims* dims, const moe_routes* routes, const moe_saved*
                 float* out_f32, uint16_t* out_bf16, hipStream_t stream);
 
 /* Whole forward: route, permute, grouped FFN, combine, in that order on
- * `stream`.  routes->logits may be NULL (the workspace holds them). */
+ * `stream`.  routes->logits may be NULL (the logits are then not stored). */
 int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                 moe_routes* routes, moe_saved* saved, float* out_f32, uint16_t* out_bf16,
                 void* ws, size_t ws_bytes, hipStream_t stream);

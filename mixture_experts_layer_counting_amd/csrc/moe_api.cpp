@@ -23,7 +23,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // ---------------------------------------------------------------------------
 struct Layout {
   size_t err = 0;         // int error word (first 256 bytes)
-  size_t logits = 0;      // [T][E] f32 when the caller passes no logits buffer
+  size_t rpart = 0;       // [T][H/256][E] f32: router MFMA sums per 256-wide K chunk
   size_t wsplit = 0;      // [3][E][H] bf16: exact hi/mid/lo split of the router weight
   size_t hist = 0;        // [NB][E+1] i32
   size_t block_base = 0;  // [NB][E] i32
@@ -61,7 +61,7 @@ Layout make_layout(const moe_dims& d) {
     return at;
   };
   L.err = take(kAlign);
-  L.logits = take(static_cast<size_t>(T) * E * 4);
+  L.rpart = take(static_cast<size_t>(d.hidden / 256) * T * E * 4);
   L.wsplit = take(static_cast<size_t>(3) * E * d.hidden * 2);
   L.hist = take(static_cast<size_t>(L.nblocks) * (E + 1) * 4);
   L.block_base = take(static_cast<size_t>(L.nblocks) * E * 4);
@@ -232,12 +232,12 @@ void add_weights(Args& a, const moe_dims& d, const moe_weights* w, bool router, 
 // ---------------------------------------------------------------------------
 int run_route(const moe_dims& d, const uint16_t* x, const moe_weights* w, moe_routes* r, void* ws,
               const Layout& L, hipStream_t s) {
-  float* logits = r->logits ? r->logits : at<float>(ws, L.logits);
+  float* part = at<float>(ws, L.rpart);
   uint16_t* planes = at<uint16_t>(ws, L.wsplit);
   MOE_LAUNCH(moe::launch_router_split(w->w_router, planes, d.hidden, d.experts, s));
-  MOE_LAUNCH(moe::launch_router_logits(x, planes, w->router_bias, logits, d.tokens, d.hidden,
-                                       d.experts, s));
-  MOE_LAUNCH(moe::launch_topk_gate(logits, r->topk_idx, r->topk_gate, d.tokens, d.experts, d.top_k, s));
+  MOE_LAUNCH(moe::launch_router_logits(x, planes, part, d.tokens, d.hidden, d.experts, s));
+  MOE_LAUNCH(moe::launch_topk_gate(part, w->router_bias, r->logits, r->topk_idx, r->topk_gate,
+                                   d.tokens, d.hidden, d.experts, d.top_k, s));
   return MOE_OK;
 }
 

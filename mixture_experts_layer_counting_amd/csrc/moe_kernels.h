@@ -9,11 +9,13 @@
 
 namespace moe {
 
+// Router: exact three-way bf16 split of the fp32 weight, per-chunk MFMA sums
+// part[t][c][e] (c < H/256), then top-k, which reduces them to the logits.
 hipError_t launch_router_split(const float* wr, uint16_t* planes, int H, int E, hipStream_t stream);
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* planes, const float* bias,
-                                float* logits, int64_t T, int H, int E, hipStream_t stream);
-hipError_t launch_topk_gate(const float* logits, int32_t* topk_idx, float* topk_gate, int64_t T,
-                            int E, int K, hipStream_t stream);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* planes, float* part, int64_t T,
+                                int H, int E, hipStream_t stream);
+hipError_t launch_topk_gate(const float* part, const float* bias, float* logits, int32_t* topk_idx,
+                            float* topk_gate, int64_t T, int H, int E, int K, hipStream_t stream);
 hipError_t launch_route_hist(const int32_t* topk_idx, int32_t* hist, int32_t* route_rank,
                              int64_t T, int E, int K, hipStream_t stream);
 hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* offsets,

@@ -52,94 +52,101 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // Router logits: l[t][e] = sum_h x[t][h] * wr[e][h] (+ bias[e]).
 //
 // With wr = hi + mid + lo (router_split_kernel) every product with the bf16
-// activation is exact on the matrix cores.  K runs in 32-wide blocks staged
-// through double-buffered LDS; inside a block, K step s and lane half h
-// cover k = 16s + 8h .. +8, and each step adds hi, then mid, then lo.  The
-// MFMA partial of eight blocks (256 of K) starts from zero and is then added
-// to an fp64 sum, in ascending order; the logit is that sum (+ bias) rounded
-// once to fp32.  A logit's arithmetic depends only on its own token row and
-// expert row, never on the batch or the tile it falls in.
+// activation is exact on the matrix cores.  K runs in 32-wide blocks staged through
+// double-buffered LDS; inside a block, K step s and lane half h cover
+// k = 16s + 8h .. +8, and each step adds hi, then mid, then lo.  K is cut
+// into chunks of 256 (eight blocks): one workgroup computes one chunk's MFMA
+// sum, from zero, in fp32, and writes it to part[t][c][e].  The top-k kernel
+// then adds the chunk sums in ascending chunk order in fp64, adds the bias,
+// and rounds once to fp32.  A logit's arithmetic depends only on its own
+// token row and expert row, never on the batch or the tile it falls in.
 //
-// Workgroup tile: WM*64 tokens x 128 experts, four waves in a 2x2 grid, wave
-// (wt, we) owning tokens wt*WM*32 .. +WM*32 and experts we*64 .. +64.
+// Workgroup tile: WM*64 tokens x 128 experts x one K chunk; four waves in a
+// 2x2 grid, wave (wt, we) owning tokens wt*WM*32 .. +WM*32 and experts
+// we*64 .. +64.
 // ---------------------------------------------------------------------------
 constexpr int kRtBK = 32;      // K block
+constexpr int kRtChunk = 256;  // K chunk of one workgroup
 constexpr int kRtStride = 40;  // LDS row stride (bf16): 32 + 8 padding, conflict-free fragment reads
 
 template <int WM>
-__global__ __launch_bounds__(256, 3 - WM) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                               const uint16_t* __restrict__ planes,
-                                                               const float* __restrict__ bias,
-                                                               float* __restrict__ logits,
-                                                               int64_t T, int H, int E) {
+__global__ __launch_bounds__(256) void router_part_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ planes,
+                                                          float* __restrict__ part, int64_t T,
+                                                          int H, int E) {
   constexpr int BM = WM * 64;
+  // work item (token tile, expert tile, chunk), chunk slowest: with the
+  // XCD-aware mapping each XCD's L2 holds the weight planes of about one chunk
+  const int ntt = static_cast<int>((T + BM - 1) / BM), net = (E + 127) / 128;
+  const int item = xcd_item(blockIdx.x, ntt * net * (H / kRtChunk));
+  if (item < 0) return;
+  const int tt = item % ntt, et = (item / ntt) % net, chunk = item / (ntt * net);
   __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM][kRtStride];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][3][128][kRtStride];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 31, half = lane >> 5;
   const int wt = wave & 1, we = wave >> 1;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BM;
-  const int e0 = blockIdx.y * 128;
-  const int64_t n = static_cast<int64_t>(E) * H;
+  const int64_t t0 = static_cast<int64_t>(tt) * BM;
+  const int e0 = et * 128;
+  const int kc = chunk * kRtChunk;
   const int ecount = min(128, E - e0);  // 64 or 128 (E is a multiple of 64)
 
-  // loader roles: row r = tid >> 2 (0..63), 16-byte chunk c = tid & 3
+  // loader roles: row r = tid >> 2 (0..63), 8 elements of K at lc
   const int lr = tid >> 2, lc = (tid & 3) * 8;
   const uint16_t* xsrc[WM];
 #pragma unroll
   for (int q = 0; q < WM; ++q) {
     int64_t t = t0 + q * 64 + lr;
     if (t > T - 1) t = T - 1;
-    xsrc[q] = x + t * H + lc;
+    xsrc[q] = x + t * H + kc + lc;
   }
+  const int64_t n = static_cast<int64_t>(E) * H;
   const uint16_t* wsrc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = min(e0 + q * 64 + lr, E - 1);
-    wsrc[q] = planes + static_cast<int64_t>(e) * H + lc;
+    wsrc[q] = planes + static_cast<int64_t>(e) * H + kc + lc;
   }
 
-  u32x4_t rx[WM], rw[3][2];
-  auto fetch = [&](int k0) {
+  // two register sets: block kb + 2 is loaded while block kb is multiplied
+  // and block kb + 1 waits in registers (the loop is fully unrolled, so the
+  // set index is a constant)
+  u32x4_t rx[2][WM], rw[2][3][2];
+  auto fetch = [&](int set, int k0) {
 #pragma unroll
-    for (int q = 0; q < WM; ++q) rx[q] = ld16(xsrc[q] + k0);
+    for (int q = 0; q < WM; ++q) rx[set][q] = ld16(xsrc[q] + k0);
 #pragma unroll
     for (int pl = 0; pl < 3; ++pl) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) rw[pl][q] = ld16(wsrc[q] + pl * n + k0);
+      for (int q = 0; q < 2; ++q) rw[set][pl][q] = ld16(wsrc[q] + pl * n + k0);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int set, int buf) {
 #pragma unroll
-    for (int q = 0; q < WM; ++q) st16(&Xs[buf][q * 64 + lr][lc], rx[q]);
+    for (int q = 0; q < WM; ++q) st16(&Xs[buf][q * 64 + lr][lc], rx[set][q]);
 #pragma unroll
     for (int pl = 0; pl < 3; ++pl) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) st16(&Ws[buf][pl][q * 64 + lr][lc], rw[pl][q]);
+      for (int q = 0; q < 2; ++q) st16(&Ws[buf][pl][q * 64 + lr][lc], rw[set][pl][q]);
     }
   };
 
-  f32x16_t part[WM][2];
-  double acc[WM][2][16];
+  f32x16_t acc[WM][2];
 #pragma unroll
-  for (int mb = 0; mb < WM; ++mb) {
+  for (int mb = 0; mb < WM; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      part[mb][nb] = zero16();
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.0;
-    }
-  }
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
 
-  const int nkb = H / kRtBK;
-  fetch(0);
-  stash(0);
+  constexpr int nkb = kRtChunk / kRtBK;
+  fetch(0, 0);
+  fetch(1, kRtBK);
+  stash(0, 0);
+#pragma unroll
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
     const int cur = kb & 1;
-    const bool more = kb + 1 < nkb;
-    if (more) fetch((kb + 1) * kRtBK);
+    if (kb + 2 < nkb) fetch(cur, (kb + 2) * kRtBK);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4_t a[WM], b[2][3];
@@ -156,35 +163,26 @@ __global__ __launch_bounds__(256, 3 - WM) void router_logits_kernel(const uint16
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-          for (int pl = 0; pl < 3; ++pl) part[mb][nb] = mfma32x32x16(a[mb], b[nb][pl], part[mb][nb]);
+          for (int pl = 0; pl < 3; ++pl) acc[mb][nb] = mfma32x32x16(a[mb], b[nb][pl], acc[mb][nb]);
         }
       }
     }
-    if ((kb & 7) == 7 || kb == nkb - 1) {
-#pragma unroll
-      for (int mb = 0; mb < WM; ++mb) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[mb][nb][v] += static_cast<double>(part[mb][nb][v]);
-          part[mb][nb] = zero16();
-        }
-      }
-    }
-    if (more) stash(cur ^ 1);
+    if (kb + 1 < nkb) stash(cur ^ 1, cur ^ 1);
   }
 
   if (we * 64 >= ecount) return;
+  // part[t][chunk][e]: a token's chunk sums are contiguous for the top-k pass
+  const int nchunk = H / kRtChunk;
+  float* out = part + static_cast<int64_t>(chunk) * E;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int e = e0 + we * 64 + nb * 32 + i;
-    const double b = bias ? static_cast<double>(bias[e]) : 0.0;
 #pragma unroll
     for (int mb = 0; mb < WM; ++mb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t t = t0 + wt * WM * 32 + mb * 32 + acc_row(v, half);
-        if (t < T) logits[t * E + e] = static_cast<float>(acc[mb][nb][v] + b);
+        if (t < T) out[t * nchunk * E + e] = acc[mb][nb][v];
       }
     }
   }
@@ -192,23 +190,58 @@ __global__ __launch_bounds__(256, 3 - WM) void router_logits_kernel(const uint16
 
 // ---------------------------------------------------------------------------
 // Top-k selection and gates, one wave per token.
-// Lane l holds logits l, l+64, ...; each of the K rounds takes the wave-wide
-// maximum under the order (greater logit first, then lower expert id), so
-// the result is the stable descending order with ties to the lower id.
+// Lane l first forms logits l, l+64, ... from the router's chunk sums (fp64,
+// ascending chunk order, + bias, one rounding to fp32), writing them out if
+// asked.  Each of the K rounds then takes the wave-wide maximum under the
+// order (greater logit first, then lower expert id), so the result is the
+// stable descending order with ties to the lower id.
 // Gates: w_k = exp(l_k - l_0), summed in slot order, g_k = w_k / sum.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ logits,
+template <int NQ>
+__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ part, int nchunk,
+                                                        const float* __restrict__ bias,
+                                                        float* __restrict__ logits,
                                                         int32_t* __restrict__ topk_idx,
                                                         float* __restrict__ topk_gate, int64_t T,
                                                         int E, int K) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + t * E;
-  const int nq = E >> 6;
-  float v[16];
+  const int nq = E >> 6;  // logits per lane, <= NQ
+  const int64_t cstride = E;
+  // chunk sums in ascending chunk order; the loads of four chunks are issued
+  // together, unconditionally (indices clamped into range, surplus values
+  // unused), so that their latencies overlap
+  double acc[NQ];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) v[q] = q < nq ? row[q * 64 + lane] : -INFINITY;
+  for (int q = 0; q < NQ; ++q) acc[q] = 0.0;
+  const float* pp = part + t * nchunk * E + lane;
+  for (int c0 = 0; c0 < nchunk; c0 += 4) {
+    float pv[4][NQ];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        pv[c][q] = pp[min(c0 + c, nchunk - 1) * cstride + min(q, nq - 1) * 64];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c0 + c < nchunk) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) acc[q] += static_cast<double>(pv[c][q]);
+      }
+    }
+  }
+  float v[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if (q < nq) {
+      const int e = q * 64 + lane;
+      v[q] = static_cast<float>(acc[q] + (bias ? static_cast<double>(bias[e]) : 0.0));
+      if (logits) logits[t * E + e] = v[q];
+    } else {
+      v[q] = -INFINITY;
+    }
+  }
   uint32_t taken = 0;
   float my_val = 0.f;
   int my_id = 0;
@@ -216,7 +249,7 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       if (q < nq && !((taken >> q) & 1u)) {
         const int e = q * 64 + lane;
         if (v[q] > bv || (v[q] == bv && e < be)) {
@@ -396,7 +429,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 }
 
 // Work list alone, from caller-supplied expert offsets (grouped FFN run on
-// its own).
+// its own, or the backward's list).
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ meta, int E,
@@ -481,24 +514,34 @@ hipError_t launch_router_split(const float* wr, uint16_t* planes, int H, int E, 
   return hipGetLastError();
 }
 
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* planes, const float* bias,
-                                float* logits, int64_t T, int H, int E, hipStream_t stream) {
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* planes, float* part, int64_t T,
+                                int H, int E, hipStream_t stream) {
+  const int64_t per_chunk = static_cast<int64_t>((E + 127) / 128) * (H / kRtChunk);
+  auto grid = [&](int64_t bm) {
+    const int64_t items = ((T + bm - 1) / bm) * per_chunk;
+    return static_cast<unsigned>(((items + 7) / 8) * 8);
+  };
   // the token tile only changes which tokens share a workgroup, never a
   // logit's arithmetic; small batches use the smaller tile to fill the GPU
-  if (T >= 4096) {
-    dim3 grid(static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>((E + 127) / 128));
-    router_logits_kernel<2><<<grid, 256, 0, stream>>>(x, planes, bias, logits, T, H, E);
-  } else {
-    dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>((E + 127) / 128));
-    router_logits_kernel<1><<<grid, 256, 0, stream>>>(x, planes, bias, logits, T, H, E);
-  }
+  if (T >= 4096)
+    router_part_kernel<2><<<grid(128), 256, 0, stream>>>(x, planes, part, T, H, E);
+  else
+    router_part_kernel<1><<<grid(64), 256, 0, stream>>>(x, planes, part, T, H, E);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_gate(const float* logits, int32_t* topk_idx, float* topk_gate, int64_t T,
-                            int E, int K, hipStream_t stream) {
-  topk_gate_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, stream>>>(logits, topk_idx,
-                                                                          topk_gate, T, E, K);
+hipError_t launch_topk_gate(const float* part, const float* bias, float* logits, int32_t* topk_idx,
+                            float* topk_gate, int64_t T, int H, int E, int K, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+  const int nq = E / 64, nchunk = H / kRtChunk;
+  if (nq <= 2)
+    topk_gate_kernel<2><<<grid, 256, 0, stream>>>(part, nchunk, bias, logits, topk_idx, topk_gate, T, E, K);
+  else if (nq <= 4)
+    topk_gate_kernel<4><<<grid, 256, 0, stream>>>(part, nchunk, bias, logits, topk_idx, topk_gate, T, E, K);
+  else if (nq <= 8)
+    topk_gate_kernel<8><<<grid, 256, 0, stream>>>(part, nchunk, bias, logits, topk_idx, topk_gate, T, E, K);
+  else
+    topk_gate_kernel<16><<<grid, 256, 0, stream>>>(part, nchunk, bias, logits, topk_idx, topk_gate, T, E, K);
   return hipGetLastError();
 }
 
