@@ -119,32 +119,34 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   }
   u32x4_t ra[2], rb[8];
 
-#define MOE_UP_ISSUE(KB)                                                   \
-  do {                                                                     \
-    int kk_ = (KB) + rot;                                                  \
-    if (kk_ >= nkb) kk_ -= nkb;                                            \
-    const int kp_ = kk_ << 6;                                              \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) if (q < nmb) ra[q] = ld16(xa[q] + kp_); \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                        \
-      rb[q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp_);            \
-      rb[4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp_);        \
-    }                                                                      \
-  } while (0)
-#define MOE_UP_STASH(BUF)                                                  \
-  do {                                                                     \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q)                          \
-      if (q < nmb) st16(&As[BUF][lds_off(ar0 + 32 * q, ac)], ra[q]);        \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q)                          \
-      st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[q]);                    \
-  } while (0)
+  auto issue = [&](int kb) {
+    int kk = kb + rot;
+    if (kk >= nkb) kk -= nkb;
+    const int kp = kk << 6;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (q < nmb) ra[q] = ld16(xa[q] + kp);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      rb[q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp);
+      rb[4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (q < nmb) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[q]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[q]);
+  };
 
-  MOE_UP_ISSUE(0);
-  MOE_UP_STASH(0);
+  issue(0);
+  stash(0);
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
     const int cur = kb & 1;
     const bool more = kb + 1 < nkb;
-    if (more) MOE_UP_ISSUE(kb + 1);
+    if (more) issue(kb + 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = 4 * half + s;
@@ -161,10 +163,8 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     }
     // the B area is private to the wave: overwriting it after this block's
     // reads is ordered by the wave's own LDS instruction order
-    if (more) MOE_UP_STASH(cur ^ 1);
+    if (more) stash(cur ^ 1);
   }
-#undef MOE_UP_ISSUE
-#undef MOE_UP_STASH
 
   uint16_t* ohi = shared ? sact_hi : act_hi;
   uint16_t* olo = shared ? sact_lo : act_lo;
@@ -201,7 +201,12 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 // wave w owns columns nt*128 + 32w .. +32.  Same staging as the up
 // projection: the wave's 32 W2 rows through a private LDS area, the act
 // planes through a double-buffered shared one.
+// NKB > 0 instantiates the K loop fully unrolled for Ie = 64 * NKB with two
+// register sets of loads in flight (block kb + 2 loads while kb is
+// multiplied); NKB = 0 is the general loop with one block in flight.  Both
+// run the same MFMA sequence on every output element.
 // ---------------------------------------------------------------------------
+template <int NKB>
 __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     const uint16_t* __restrict__ act_hi, const uint16_t* __restrict__ act_lo,
     const uint16_t* __restrict__ sact_hi, const uint16_t* __restrict__ sact_lo,
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     s_dst[tid] = dst;
   }
 
-  const int nkb = Ie >> 6;
+  const int nkb = NKB > 0 ? NKB : Ie >> 6;
   const int rot = k_rotation(grp, nt, nkb);
   const int ac = tid & 7, ar0 = tid >> 3;
   const uint16_t* ahi = (shared ? sact_hi : act_hi) + p0 * Ie + ac * 8;
@@ -261,41 +266,32 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   f32x16_t acc[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) acc[mb] = zero16();
-  u32x4_t rh[2], rl[2], rb[4];
+  constexpr int NSET = NKB > 0 ? 2 : 1;
+  u32x4_t rh[NSET][2], rl[NSET][2], rb[NSET][4];
 
-#define MOE_DN_ISSUE(KB)                                                   \
-  do {                                                                     \
-    int kk_ = (KB) + rot;                                                  \
-    if (kk_ >= nkb) kk_ -= nkb;                                            \
-    const int kp_ = kk_ << 6;                                              \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                        \
-      if (q < nmb) {                                                       \
-        rh[q] = ld16(ahi + aoff[q] + kp_);                                 \
-        rl[q] = ld16(alo + aoff[q] + kp_);                                 \
-      }                                                                    \
-    }                                                                      \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q)                          \
-      rb[q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp_);            \
-  } while (0)
-#define MOE_DN_STASH(BUF)                                                  \
-  do {                                                                     \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                        \
-      if (q < nmb) {                                                       \
-        st16(&As[BUF][0][lds_off(ar0 + 32 * q, ac)], rh[q]);                \
-        st16(&As[BUF][1][lds_off(ar0 + 32 * q, ac)], rl[q]);                \
-      }                                                                    \
-    }                                                                      \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q)                          \
-      st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[q]);                    \
-  } while (0)
-
-  MOE_DN_ISSUE(0);
-  MOE_DN_STASH(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    const int cur = kb & 1;
-    const bool more = kb + 1 < nkb;
-    if (more) MOE_DN_ISSUE(kb + 1);
+  // activation rows past the tile's end repeat its last row (unused)
+  auto issue = [&](int set, int kb) {
+    int kk = kb + rot;
+    if (kk >= nkb) kk -= nkb;
+    const int kp = kk << 6;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      rh[set][q] = ld16(ahi + aoff[q] + kp);
+      rl[set][q] = ld16(alo + aoff[q] + kp);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rb[set][q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp);
+  };
+  auto stash = [&](int set, int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      st16(&As[buf][0][lds_off(ar0 + 32 * q, ac)], rh[set][q]);
+      st16(&As[buf][1][lds_off(ar0 + 32 * q, ac)], rl[set][q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[set][q]);
+  };
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = 4 * half + s;
@@ -303,17 +299,40 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         if (mb < nmb) {
-          const u32x4_t ah = ld16(&As[cur][0][lds_off(mb * 32 + j, c)]);
-          const u32x4_t al = ld16(&As[cur][1][lds_off(mb * 32 + j, c)]);
+          const u32x4_t ah = ld16(&As[buf][0][lds_off(mb * 32 + j, c)]);
+          const u32x4_t al = ld16(&As[buf][1][lds_off(mb * 32 + j, c)]);
           acc[mb] = mfma32x32x16(ah, b, acc[mb]);
           acc[mb] = mfma32x32x16(al, b, acc[mb]);
         }
       }
     }
-    if (more) MOE_DN_STASH(cur ^ 1);
+  };
+
+  // The B area is private to the wave: overwriting it after the reads of
+  // the previous block is ordered by the wave's own LDS instruction order.
+  if constexpr (NKB > 0) {
+    issue(0, 0);
+    if (NKB > 1) issue(1, 1);
+    stash(0, 0);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      __syncthreads();
+      if (kb + 2 < NKB) issue(kb & 1, kb + 2);
+      compute(kb & 1);
+      if (kb + 1 < NKB) stash((kb + 1) & 1, (kb + 1) & 1);
+    }
+  } else {
+    issue(0, 0);
+    stash(0, 0);
+    for (int kb = 0; kb < nkb; ++kb) {
+      __syncthreads();
+      const int cur = kb & 1;
+      const bool more = kb + 1 < nkb;
+      if (more) issue(0, kb + 1);
+      compute(cur);
+      if (more) stash(0, cur ^ 1);
+    }
   }
-#undef MOE_DN_ISSUE
-#undef MOE_DN_STASH
 
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -417,8 +436,13 @@ hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
                            int K, int I, int Is, int max_tiles, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(max_tiles) * (H / kDownCols);
   const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
-  ffn_down_kernel<<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
-                                            sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
+  // the unrolled instantiation covers expert and shared sizes of 512
+  if (I == 512 && (Is == 0 || Is == 512))
+    ffn_down_kernel<8><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
+                                                 sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
+  else
+    ffn_down_kernel<0><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
+                                                 sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
   return hipGetLastError();
 }
 
