@@ -97,14 +97,14 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
 // them, so one barrier per block separates the stages.  Two LDS layouts:
 //   * [row][k] (80-byte rows) for sources stored k-contiguous (the routed or
 //     token rows of a dgrad); fragments are 16-byte LDS loads;
-//   * [k][col] (288-byte rows) for sources whose rows are indexed by k (the
+//   * [k][col] (320-byte rows) for sources whose rows are indexed by k (the
 //     expert weights read along their output dimension, and both operands
 //     of a weight gradient, whose contraction runs over the routes of an
 //     expert).  Rows are stored as the 16-byte pieces they are loaded in and
 //     fragments are read with the gfx950 LDS transpose read
-//     (ds_read_b64_tr_b16), two per fragment.  Consecutive 288-byte rows
-//     start 32 bytes apart in the bank space, so those reads are free of
-//     bank conflicts.
+//     (ds_read_b64_tr_b16), two per fragment.  The 64 bytes of padding per
+//     row make those reads free of bank conflicts on MI355X (measured with
+//     the LDS bank-conflict counter: 256- and 288-byte rows conflict).
 // An operand given as three bf16 planes (hi, mid, lo) takes three MFMAs per
 // K step, in that order.
 //
@@ -133,7 +133,7 @@ enum BwdMode { kDact = 0, kDx = 1, kDw2 = 2, kDw13 = 3 };
 constexpr int kBT = kBwdRowsPerTile;  // edge of every output tile (128)
 constexpr int kBK = 32;
 constexpr int kKStride = 40;   // [row][k] layout: 32 k + 8 padding (bf16)
-constexpr int kRStride = 144;  // [k][col] layout: 128 columns + 16 padding
+constexpr int kRStride = 160;  // [k][col] layout: 128 columns + 32 padding
 constexpr int kKPlane = kBT * kKStride;
 constexpr int kRPlane = kBK * kRStride;
 
