@@ -37,7 +37,8 @@
  *    enqueues anything; on failure it returns a non-zero status and has
  *    enqueued nothing (fail closed).  Bad data found on the device (a
  *    caller-supplied expert id out of range or repeated within a token) sets
- *    a sticky error word in the workspace, read by moe_last_device_error().
+ *    an error word in the workspace, which each moe_permute / moe_forward
+ *    overwrites; moe_last_device_error() reads it.
  *  - Supported sizes: E % 64 == 0 and 64 <= E <= 1024; 1 <= K <= 16 and
  *    K <= E; H % 256 == 0, 256 <= H <= 16384; I % 128 == 0, 128 <= I <= 4096;
  *    Is == 0 or the same rule as I; 0 <= T and T*K < 2^31.  T == 0 returns
@@ -136,8 +137,8 @@ const char* moe_status_str(int status);
 
 /* Bytes of device workspace the operation `op` (enum moe_op) needs for these
  * dims; 0 if the dims are invalid.  The workspace is scratch owned by the
- * caller; its contents between calls carry only the sticky device-error
- * word.  Size it once per shape; a workspace sized for MOE_OP_BACKWARD also
+ * caller; its contents between calls carry only the device-error word of
+ * the last permutation.  Size it once per shape; a workspace sized for MOE_OP_BACKWARD also
  * serves every other operation at the same dims. */
 size_t moe_workspace_bytes(const moe_dims* dims, int op);
 
@@ -158,7 +159,8 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
  * replayed routing) and writes expert_offsets, sorted_route and route_pos:
  * a stable counting sort of route ids by expert (ascending route id inside
  * each expert's segment).  Out-of-range or repeated ids within a token set
- * the sticky device error and leave the permutation unspecified. */
+ * the workspace's device-error word (cleared otherwise) and leave the
+ * permutation unspecified. */
 int moe_permute(const moe_dims* dims, moe_routes* routes, void* ws, size_t ws_bytes,
                 hipStream_t stream);
 
