@@ -242,13 +242,16 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void bwd_gemm_kernel(const BwdArgs a) {
   constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
   constexpr int NPA = (MODE == kDx || MODE == kDw13) ? 3 : 1;
   constexpr int NPB = MODE == kDw2 ? 3 : 1;
   constexpr int APLANE = WGRAD ? kRPlane : kKPlane;
   constexpr int STAGE = NPA * APLANE + NPB * kRPlane;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  // weight gradients (short contractions): one LDS stage and two barriers
+  // per K block, which leaves room for three workgroups per CU
+  constexpr int NSTAGE = WGRAD ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
 
   BwdTile w;
   if (!bwd_decode<MODE>(a, blockIdx.x, w)) return;
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
   }
   for (int it = 0; it < nkb; ++it) {
     __syncthreads();
-    const int cur = it & 1;
+    const int cur = NSTAGE == 2 ? (it & 1) : 0;
     const bool more = it + 1 < nkb;
     if (more) {
       int kn = rot + it + 1;
@@ -414,7 +417,10 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
           for (int q = 1; q < NPB; ++q) acc[mb][nb] = mfma32x32x16(fa[mb][0], fb[nb][q], acc[mb][nb]);
         }
     }
-    if (more) stash(cur ^ 1);
+    if (more) {
+      if (NSTAGE == 1) __syncthreads();  // every wave is done reading the stage
+      stash(NSTAGE == 2 ? cur ^ 1 : 0);
+    }
   }
 
   if (MODE == kDact) {
