@@ -27,6 +27,7 @@ namespace moe {
 // dl[k] = g_k (dg_k - sum_j g_j dg_j) (softmax backward over the selected
 // slots); dz = ds * sg * (1 - sg).
 // ---------------------------------------------------------------------------
+template <int KT>
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ y,
                                                        const float* __restrict__ sy,
@@ -34,45 +35,51 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
                                                        const float* __restrict__ sg,
                                                        float* __restrict__ dl,
                                                        float* __restrict__ dz, int H, int K) {
-  __shared__ double red[4][17];
+  // rows k < K are the route rows y[t*K + k], row K the shared row; all KT+1
+  // row loads of a column chunk are issued before any is used (surplus
+  // slots re-read the last route row and are not used)
+  __shared__ double red[4][KT + 1];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* d = dout + t * H;
   const int nsum = K + (sy ? 1 : 0);
-  double part[17];
+  const float* rowp[KT + 1];
 #pragma unroll
-  for (int k = 0; k < 17; ++k) part[k] = 0.0;
+  for (int k = 0; k < KT; ++k) rowp[k] = y + (t * K + min(k, K - 1)) * H;
+  rowp[KT] = sy ? sy + t * H : rowp[KT - 1];
+  double part[KT + 1];
+#pragma unroll
+  for (int k = 0; k <= KT; ++k) part[k] = 0.0;
   for (int c = tid * 4; c < H; c += 1024) {
     const uint2 dv = *reinterpret_cast<const uint2*>(d + c);
+    f32x4v_t v[KT + 1];
+#pragma unroll
+    for (int k = 0; k <= KT; ++k) v[k] = *reinterpret_cast<const f32x4v_t*>(rowp[k] + c);
     const double d0 = bf16_to_f32(static_cast<uint16_t>(dv.x & 0xffffu));
     const double d1 = bf16_to_f32(static_cast<uint16_t>(dv.x >> 16));
     const double d2 = bf16_to_f32(static_cast<uint16_t>(dv.y & 0xffffu));
     const double d3 = bf16_to_f32(static_cast<uint16_t>(dv.y >> 16));
 #pragma unroll
-    for (int k = 0; k < 17; ++k) {
-      if (k < nsum) {
-        const float* row = k < K ? y + (t * K + k) * H : sy + t * H;
-        const f32x4v_t v = *reinterpret_cast<const f32x4v_t*>(row + c);
-        part[k] += d0 * v[0];
-        part[k] += d1 * v[1];
-        part[k] += d2 * v[2];
-        part[k] += d3 * v[3];
-      }
+    for (int k = 0; k <= KT; ++k) {
+      part[k] += d0 * v[k][0];
+      part[k] += d1 * v[k][1];
+      part[k] += d2 * v[k][2];
+      part[k] += d3 * v[k][3];
     }
   }
+  // slot s of the reduction: route k = s for s < K, the shared row at s = K
 #pragma unroll
-  for (int k = 0; k < 17; ++k) {
-    if (k < nsum) {
-      double v = part[k];
+  for (int k = 0; k <= KT; ++k) {
+    double v = part[k];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      if (lane == 0) red[wave][k] = v;
-    }
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) red[wave][k] = v;
   }
   __syncthreads();
   if (tid == 0) {
-    double dg[17];
-    for (int k = 0; k < nsum; ++k) dg[k] = (red[0][k] + red[1][k]) + (red[2][k] + red[3][k]);
+    double dg[KT + 1];
+#pragma unroll
+    for (int k = 0; k <= KT; ++k) dg[k] = (red[0][k] + red[1][k]) + (red[2][k] + red[3][k]);
     double mean = 0.0;
     for (int k = 0; k < K; ++k) mean += static_cast<double>(gate[t * K + k]) * dg[k];
     for (int k = 0; k < K; ++k) {
@@ -81,9 +88,10 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
     }
     if (sy) {
       const double s = sg[t];
-      dz[t] = static_cast<float>(dg[K] * s * (1.0 - s));
+      dz[t] = static_cast<float>(dg[KT] * s * (1.0 - s));
     }
   }
+  (void)nsum;
 }
 
 // ---------------------------------------------------------------------------
@@ -619,6 +627,7 @@ __global__ __launch_bounds__(256) void bwd_wsg_final_kernel(const double* __rest
 //   dx_router = sum over the same routes, same order, of dl * w_router[e]
 // (fp32; the route order is fixed by sorting the token's expert ids).
 // ---------------------------------------------------------------------------
+template <int KT>
 __global__ __launch_bounds__(256) void bwd_dx_sum_kernel(
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
     const float* __restrict__ dx_route, const float* __restrict__ dx_shared,
@@ -626,51 +635,76 @@ __global__ __launch_bounds__(256) void bwd_dx_sum_kernel(
     const float* __restrict__ w_router, float* __restrict__ dx32, uint16_t* __restrict__ dx16,
     int H, int E, int K) {
   const int64_t t = blockIdx.x;
-  // slots of this token in ascending expert id (insertion sort, K <= 16)
-  int ord[16];
-  int eid[16];
+  // the token's valid slots in ascending expert id: rank[k] = number of
+  // valid ids below slot k's (ids are distinct within a token, invalid ones
+  // take no rank); slot_j / eid_j = the slot and id of rank j
+  int e[KT], rank[KT];
   int n = 0;
-  for (int k = 0; k < K; ++k) {
-    int e = topk_idx[t * K + k];
-    if (e < 0 || e >= E) continue;
-    int j = n++;
-    while (j > 0 && eid[j - 1] > e) {
-      eid[j] = eid[j - 1];
-      ord[j] = ord[j - 1];
-      --j;
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    e[k] = k < K ? topk_idx[t * K + k] : -1;
+    if (e[k] >= E) e[k] = -1;
+    n += e[k] >= 0 ? 1 : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    int r = 0;
+#pragma unroll
+    for (int q = 0; q < KT; ++q) r += (e[q] >= 0 && e[q] < e[k]) ? 1 : 0;
+    rank[k] = e[k] >= 0 ? r : -1;
+  }
+  const float* xrow[KT];
+  const float* wrow[KT];
+  float s[KT];
+#pragma unroll
+  for (int j = 0; j < KT; ++j) {
+    int slot = 0, id = 0;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      if (rank[k] == j) {
+        slot = k;
+        id = e[k];
+      }
     }
-    eid[j] = e;
-    ord[j] = k;
+    // ranks past the valid count keep slot 0 / expert 0: loaded, unused
+    xrow[j] = dx_route + (t * K + slot) * H;
+    wrow[j] = w_router + static_cast<int64_t>(id) * H;
+    s[j] = dl[t * K + slot];
   }
   const float dzt = dx_shared ? dz[t] : 0.f;
   for (int c = threadIdx.x * 4; c < H; c += 1024) {
+    f32x4v_t v[KT], wv[KT];
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      v[j] = *reinterpret_cast<const f32x4v_t*>(xrow[j] + c);
+      wv[j] = *reinterpret_cast<const f32x4v_t*>(wrow[j] + c);
+    }
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-    for (int j = 0; j < n; ++j) {
-      const int k = ord[j];
-      const f32x4v_t v = *reinterpret_cast<const f32x4v_t*>(dx_route + (t * K + k) * H + c);
-      a0 += v[0];
-      a1 += v[1];
-      a2 += v[2];
-      a3 += v[3];
-      const float s = dl[t * K + k];
-      const f32x4v_t wv = *reinterpret_cast<const f32x4v_t*>(w_router + static_cast<int64_t>(eid[j]) * H + c);
-      r0 = fmaf(s, wv[0], r0);
-      r1 = fmaf(s, wv[1], r1);
-      r2 = fmaf(s, wv[2], r2);
-      r3 = fmaf(s, wv[3], r3);
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      if (j < n) {
+        a0 += v[j][0];
+        a1 += v[j][1];
+        a2 += v[j][2];
+        a3 += v[j][3];
+        r0 = fmaf(s[j], wv[j][0], r0);
+        r1 = fmaf(s[j], wv[j][1], r1);
+        r2 = fmaf(s[j], wv[j][2], r2);
+        r3 = fmaf(s[j], wv[j][3], r3);
+      }
     }
     if (dx_shared) {
-      const f32x4v_t v = *reinterpret_cast<const f32x4v_t*>(dx_shared + t * H + c);
-      a0 += v[0];
-      a1 += v[1];
-      a2 += v[2];
-      a3 += v[3];
-      const uint2 wv = *reinterpret_cast<const uint2*>(w_sgate + c);
-      a0 = fmaf(dzt, bf16_to_f32(static_cast<uint16_t>(wv.x & 0xffffu)), a0);
-      a1 = fmaf(dzt, bf16_to_f32(static_cast<uint16_t>(wv.x >> 16)), a1);
-      a2 = fmaf(dzt, bf16_to_f32(static_cast<uint16_t>(wv.y & 0xffffu)), a2);
-      a3 = fmaf(dzt, bf16_to_f32(static_cast<uint16_t>(wv.y >> 16)), a3);
+      const f32x4v_t v2 = *reinterpret_cast<const f32x4v_t*>(dx_shared + t * H + c);
+      a0 += v2[0];
+      a1 += v2[1];
+      a2 += v2[2];
+      a3 += v2[3];
+      const uint2 w2v = *reinterpret_cast<const uint2*>(w_sgate + c);
+      a0 = fmaf(dzt, bf16_to_f32(static_cast<uint16_t>(w2v.x & 0xffffu)), a0);
+      a1 = fmaf(dzt, bf16_to_f32(static_cast<uint16_t>(w2v.x >> 16)), a1);
+      a2 = fmaf(dzt, bf16_to_f32(static_cast<uint16_t>(w2v.y & 0xffffu)), a2);
+      a3 = fmaf(dzt, bf16_to_f32(static_cast<uint16_t>(w2v.y >> 16)), a3);
     }
     a0 += r0;
     a1 += r1;
@@ -697,7 +731,10 @@ __global__ __launch_bounds__(256) void bwd_dx_sum_kernel(
 hipError_t launch_bwd_gate(const uint16_t* dout, const float* y, const float* sy, const float* gate,
                            const float* sg, float* dl, float* dz, int64_t T, int H, int K,
                            hipStream_t stream) {
-  bwd_gate_kernel<<<static_cast<unsigned>(T), 256, 0, stream>>>(dout, y, sy, gate, sg, dl, dz, H, K);
+  if (K <= 10)
+    bwd_gate_kernel<10><<<static_cast<unsigned>(T), 256, 0, stream>>>(dout, y, sy, gate, sg, dl, dz, H, K);
+  else
+    bwd_gate_kernel<16><<<static_cast<unsigned>(T), 256, 0, stream>>>(dout, y, sy, gate, sg, dl, dz, H, K);
   return hipGetLastError();
 }
 
@@ -771,8 +808,12 @@ hipError_t launch_bwd_dx_sum(const int32_t* topk_idx, const float* dl, const flo
                              const float* dx_shared, const float* dz, const uint16_t* w_sgate,
                              const float* w_router, float* dx32, uint16_t* dx16, int64_t T, int H,
                              int E, int K, hipStream_t stream) {
-  bwd_dx_sum_kernel<<<static_cast<unsigned>(T), 256, 0, stream>>>(topk_idx, dl, dx_route, dx_shared, dz,
-                                                                 w_sgate, w_router, dx32, dx16, H, E, K);
+  if (K <= 10)
+    bwd_dx_sum_kernel<10><<<static_cast<unsigned>(T), 256, 0, stream>>>(
+        topk_idx, dl, dx_route, dx_shared, dz, w_sgate, w_router, dx32, dx16, H, E, K);
+  else
+    bwd_dx_sum_kernel<16><<<static_cast<unsigned>(T), 256, 0, stream>>>(
+        topk_idx, dl, dx_route, dx_shared, dz, w_sgate, w_router, dx32, dx16, H, E, K);
   return hipGetLastError();
 }
 

@@ -353,7 +353,10 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 // Combine: out[t] = fma chain over slots k = 0..K-1 of g[t][k] * y[t*K+k],
 // from +0, then fma(sg[t], shared_y[t], .); fp32, one bf16 rounding.
 // One workgroup per token; each thread owns 4 consecutive hidden columns.
+// The K route rows (KT >= K slots, surplus slots re-read the last row and
+// are not used) are all loaded before the chain, so their latencies overlap.
 // ---------------------------------------------------------------------------
+template <int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ gate,
                                                       const float* __restrict__ sy,
@@ -362,29 +365,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       uint16_t* __restrict__ out16, int64_t T,
                                                       int H, int K) {
   const int64_t t = blockIdx.x;
-  float g[16];
+  float g[KT];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) g[k] = k < K ? gate[t * K + k] : 0.f;
+  for (int k = 0; k < KT; ++k) g[k] = gate[t * K + min(k, K - 1)];
   const float sgt = sy ? sg[t] : 0.f;
   const float* yt = y + t * K * H;
   for (int c = threadIdx.x * 4; c < H; c += 1024) {
+    f32x4v_t v[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+      v[k] = *reinterpret_cast<const f32x4v_t*>(yt + static_cast<int64_t>(min(k, K - 1)) * H + c);
+    f32x4v_t vs;
+    if (sy) vs = *reinterpret_cast<const f32x4v_t*>(sy + t * H + c);
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < KT; ++k) {
       if (k < K) {
-        const f32x4v_t v = *reinterpret_cast<const f32x4v_t*>(yt + static_cast<int64_t>(k) * H + c);
-        a0 = fmaf(g[k], v[0], a0);
-        a1 = fmaf(g[k], v[1], a1);
-        a2 = fmaf(g[k], v[2], a2);
-        a3 = fmaf(g[k], v[3], a3);
+        a0 = fmaf(g[k], v[k][0], a0);
+        a1 = fmaf(g[k], v[k][1], a1);
+        a2 = fmaf(g[k], v[k][2], a2);
+        a3 = fmaf(g[k], v[k][3], a3);
       }
     }
     if (sy) {
-      const f32x4v_t v = *reinterpret_cast<const f32x4v_t*>(sy + t * H + c);
-      a0 = fmaf(sgt, v[0], a0);
-      a1 = fmaf(sgt, v[1], a1);
-      a2 = fmaf(sgt, v[2], a2);
-      a3 = fmaf(sgt, v[3], a3);
+      a0 = fmaf(sgt, vs[0], a0);
+      a1 = fmaf(sgt, vs[1], a1);
+      a2 = fmaf(sgt, vs[2], a2);
+      a3 = fmaf(sgt, vs[3], a3);
     }
     if (out32) {
       f32x4v_t o;
@@ -449,8 +456,12 @@ hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
 hipError_t launch_combine(const float* y, const float* gate, const float* sy, const float* sg,
                           float* out32, uint16_t* out16, int64_t T, int H, int K,
                           hipStream_t stream) {
-  combine_kernel<<<static_cast<unsigned>(T), 256, 0, stream>>>(y, gate, sy, sg, out32, out16, T, H,
-                                                              K);
+  if (K <= 10)
+    combine_kernel<10><<<static_cast<unsigned>(T), 256, 0, stream>>>(y, gate, sy, sg, out32, out16,
+                                                                    T, H, K);
+  else
+    combine_kernel<16><<<static_cast<unsigned>(T), 256, 0, stream>>>(y, gate, sy, sg, out32, out16,
+                                                                    T, H, K);
   return hipGetLastError();
 }
 
