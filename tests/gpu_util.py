@@ -97,16 +97,42 @@ def assert_close(got, ref, what, atol=ATOL, rtol=RTOL):
     return err.max()
 
 
-def assert_close_sum(got, ref, what, n_terms):
+def assert_close_sum(got, ref, what, n_terms, term_scale=None):
     """Tolerance for a weight gradient, which sums n_terms per-token terms:
     each term's factors meet the per-token rule, and independent per-term
     errors grow as sqrt(n), so the absolute floor is 5e-5 * sqrt(n_terms).
-    The strict per-token rule's worst err/tol is reported alongside."""
+    The relative part is taken against term_scale, the sum of the terms'
+    absolute values, where given (the per-token rule applied to each term and
+    summed: terms of both signs may cancel in the sum, their errors do not),
+    else against |ref|.  The strict per-token rule's worst err/tol is
+    reported alongside."""
     g = np.asarray(got, np.float64)
     r = np.asarray(ref, np.float64)
     strict = (np.abs(g - r) / (ATOL + RTOL * np.abs(r))).max()
     say(f"  {what}: strict-rule worst err/tol {strict:.3f} (n={n_terms})")
-    return assert_close(got, ref, what + " [sum rule]", atol=ATOL * np.sqrt(max(1, n_terms)))
+    scale = np.abs(r) if term_scale is None else np.maximum(np.abs(r), np.asarray(term_scale, np.float64))
+    err = np.abs(g - r)
+    tol = ATOL * np.sqrt(max(1, n_terms)) + RTOL * scale
+    bad = err > tol
+    say(f"  {what} [sum rule]: max-abs {err.max():.3e}, worst err/tol {(err / tol).max():.3f}")
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} elements outside tolerance, max-abs {err.max():.3e}"
+    return err.max()
+
+
+def router_term_scale(x_bits, idx, dl, experts):
+    """Sum over the routes of each expert of |dl| * |x|: the absolute values of
+    the per-route terms that the router weight gradient adds up."""
+    ax = np.abs(O.bf16_to_f64(x_bits))
+    s = np.zeros((experts, ax.shape[1]))
+    for k in range(idx.shape[1]):
+        np.add.at(s, idx[:, k], np.abs(dl[:, k])[:, None] * ax)
+    return s
+
+
+def gate_term_scale(x_bits, dz):
+    """Sum over tokens of |dz| * |x|: the absolute values of the per-token
+    terms that the shared-gate weight gradient adds up."""
+    return np.abs(np.asarray(dz, np.float64)) @ np.abs(O.bf16_to_f64(x_bits))
 
 
 def compare_routes(idx_gpu, idx_ref, logits64):

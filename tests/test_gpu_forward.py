@@ -158,10 +158,15 @@ def test_full_size_forward_sampled(name):
     dict(tokens=100, hidden=256, experts=192, top_k=6, inter=128, shared_inter=0),
     dict(tokens=77, hidden=256, experts=64, top_k=16, inter=256, shared_inter=128),
     dict(tokens=300, hidden=768, experts=1024, top_k=1, inter=384, shared_inter=256),
+    dict(tokens=130, hidden=256, experts=1024, top_k=16, inter=128, shared_inter=128),
+    dict(tokens=64, hidden=16384, experts=64, top_k=2, inter=128, shared_inter=128),
+    dict(tokens=48, hidden=256, experts=64, top_k=4, inter=4096, shared_inter=4096),
+    dict(tokens=1, hidden=512, experts=512, top_k=10, inter=512, shared_inter=512),
 ])
 def test_shape_edge_cases(shape):
     """Expert counts that are not multiples of 128, K = 1 and K = 16, no
-    shared expert, intermediate sizes that are not powers of two."""
+    shared expert, intermediate sizes that are not powers of two, the largest
+    supported E (with the largest K), H and I, and a single token."""
     cfg = W.MoEConfig(name="edge", **shape)
     layer = W.make_layer(cfg)
     x = W.tokens(cfg)
