@@ -215,10 +215,14 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
 /* Profiling variant of moe_forward: the same kernels in the same order on
  * `stream`, with events[i] recorded just before kernel i and events[n] after
  * the last one, n = moe_forward_kernel_count(dims).  `events` are created by
- * the caller (hipEventCreate); n_events must be >= n + 1.  Results are
- * identical to moe_forward.  Kernel order: router_split, router_logits, topk_gate,
- * route_hist, route_scan, route_scatter, [shared_gate if Is > 0], ffn_up,
- * ffn_down, combine. */
+ * the caller (hipEventCreate); a NULL entry records nothing at its position
+ * (so a caller can time one kernel with two events and leave the others
+ * unmarked); n_events must be >= n + 1.  Results are
+ * identical to moe_forward.  Kernel order (moe_forward_kernel_name gives
+ * the names): router_split, router_logits, topk_gate (which also forms the
+ * shared-expert gate when Is > 0), the permutation (route_sort, one kernel,
+ * when experts * ceil(tokens / 32) <= 16384, else route_hist, route_scan,
+ * route_scatter), ffn_up, ffn_down, combine. */
 int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                          moe_routes* routes, moe_saved* saved, float* out_f32,
                          uint16_t* out_bf16, void* ws, size_t ws_bytes, hipEvent_t* events,
@@ -226,6 +230,10 @@ int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint1
 
 /* Number of kernels moe_forward launches for these dims (0 if invalid). */
 int moe_forward_kernel_count(const moe_dims* dims);
+
+/* Name of kernel i (0-based, launch order) of moe_forward for these dims, a
+ * static string; NULL if the dims are invalid or i is out of range. */
+const char* moe_forward_kernel_name(const moe_dims* dims, int i);
 
 /* Synchronises `stream`, then returns the device error word of workspace
  * `ws` (MOE_OK or MOE_E_DEVICE) as left by the last moe_permute or

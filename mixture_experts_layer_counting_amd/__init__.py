@@ -57,9 +57,7 @@ class MoeGrads(ctypes.Structure):
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
-           "moe_forward_profiled", "moe_forward_kernel_count")
-FORWARD_KERNELS = ("router_split", "router_logits", "topk_gate", "route_hist", "route_scan", "route_scatter", "shared_gate",
-                   "ffn_up", "ffn_down", "combine")
+           "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name")
 
 _lib = None
 
@@ -98,6 +96,8 @@ def load_library():
                                          _VP, ctypes.c_size_t, _VP, ctypes.c_int, _VP]
     lib.moe_forward_kernel_count.restype = ctypes.c_int
     lib.moe_forward_kernel_count.argtypes = [P(MoeDims)]
+    lib.moe_forward_kernel_name.restype = ctypes.c_char_p
+    lib.moe_forward_kernel_name.argtypes = [P(MoeDims), ctypes.c_int]
     lib.moe_last_device_error.restype = ctypes.c_int
     lib.moe_last_device_error.argtypes = [_VP, _VP]
     if lib.moe_abi_version() != ABI_VERSION:
@@ -267,8 +267,10 @@ def moe_forward_kernel_count(dims) -> int:
 
 
 def forward_kernel_names(dims):
-    """Kernel names of moe_forward in launch order."""
-    return [k for k in FORWARD_KERNELS if k != "shared_gate" or dims.shared_inter > 0]
+    """Kernel names of moe_forward in launch order (from the library)."""
+    lib = load_library()
+    n = lib.moe_forward_kernel_count(ctypes.byref(dims.c()))
+    return [lib.moe_forward_kernel_name(ctypes.byref(dims.c()), i).decode() for i in range(n)]
 
 
 def moe_last_device_error(ws, stream=None) -> int:

@@ -47,13 +47,17 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // gate (W13 row c) and up (W13 row I + c) for every row of the tile, so the
 // SwiGLU is elementwise on the two accumulators.  Its 64 weight rows go
 // through a private LDS area; the gathered activation rows through a
-// double-buffered area shared by the four waves.  One K block of loads is in
-// flight while the previous one is multiplied; 64-row tiles keep registers
-// and LDS small enough for several workgroups per CU, which is what keeps
-// enough bytes in flight.
+// double-buffered area shared by the four waves.  64-row tiles keep
+// registers and LDS small enough for two workgroups per CU, which with the
+// loads of the next K blocks in flight keeps enough bytes moving.
 // Outputs: act as a bf16 hi/lo pair (row = sorted position, or token for the
 // shared expert) and, if requested, the fp32 gate/up values.
+// NKB > 0 instantiates the K loop fully unrolled for H = 64 * NKB with two
+// register sets of loads (block kb + 2 is loaded while kb is multiplied and
+// kb + 1 waits in registers); NKB = 0 is the general loop with one block in
+// flight.  Both run the same MFMA sequence on every output element.
 // ---------------------------------------------------------------------------
+template <int NKB>
 __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
     const uint16_t* __restrict__ ws13, const int32_t* __restrict__ offsets,
@@ -64,13 +68,13 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     int H, int E, int K, int I, int Is, int ncol_tiles) {
   const int item = xcd_item(blockIdx.x, meta[0] * ncol_tiles);
   if (item < 0) return;
-  const int tile = item / ncol_tiles, nt = item - tile * ncol_tiles;
-  const int grp = tiles[2 * tile], row0 = tiles[2 * tile + 1];
+  const GroupItem gi = group_item(item, ncol_tiles, tiles, offsets, E, T, kRowsPerTile);
+  const int nt = gi.nt, grp = gi.grp, row0 = gi.row0;
   const bool shared = grp == E;
   const int Ie = shared ? Is : I;
   if (nt * kUpCols >= Ie) return;
-  const int seg0 = shared ? 0 : offsets[grp];
-  const int cnt = shared ? static_cast<int>(T) : offsets[grp + 1] - seg0;
+  const int seg0 = gi.seg0;
+  const int cnt = gi.cnt;
   const int rows = min(kRowsPerTile, cnt - row0);
   if (rows <= 0) return;
   const int nmb = (rows + 31) >> 5;
@@ -84,6 +88,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   const int j = lane & 31, half = lane >> 5;
   const int64_t R = T * K;
 
+  // rows past the tile's end repeat its last row (loaded, never used)
   if (tid < kRowsPerTile) {
     const int rr = min(tid, rows - 1);
     int64_t tok;
@@ -97,9 +102,9 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   }
   __syncthreads();
 
-  const int nkb = H >> 6;
+  const int nkb = NKB > 0 ? NKB : H >> 6;
   const int rot = k_rotation(grp, nt, nkb);
-  // A loader: rows ar0 + 32q (q < nmb), chunk ac
+  // A loader: rows ar0 + 32q, chunk ac
   const int ac = tid & 7, ar0 = tid >> 3;
   const uint16_t* xa[2];
 #pragma unroll
@@ -117,36 +122,28 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     accg[mb] = zero16();
     accu[mb] = zero16();
   }
-  u32x4_t ra[2], rb[8];
+  constexpr int NSET = NKB > 0 ? 2 : 1;
+  u32x4_t ra[NSET][2], rb[NSET][8];
 
-  auto issue = [&](int kb) {
+  auto issue = [&](int set, int kb) {
     int kk = kb + rot;
     if (kk >= nkb) kk -= nkb;
     const int kp = kk << 6;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (q < nmb) ra[q] = ld16(xa[q] + kp);
+    for (int q = 0; q < 2; ++q) ra[set][q] = ld16(xa[q] + kp);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      rb[q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp);
-      rb[4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp);
+      rb[set][q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp);
+      rb[set][4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int set, int buf) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (q < nmb) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[q]);
+    for (int q = 0; q < 2; ++q) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[set][q]);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[q]);
+    for (int q = 0; q < 8; ++q) st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[set][q]);
   };
-
-  issue(0);
-  stash(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    const int cur = kb & 1;
-    const bool more = kb + 1 < nkb;
-    if (more) issue(kb + 1);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = 4 * half + s;
@@ -155,15 +152,38 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         if (mb < nmb) {
-          const u32x4_t a = ld16(&As[cur][lds_off(mb * 32 + j, c)]);
+          const u32x4_t a = ld16(&As[buf][lds_off(mb * 32 + j, c)]);
           accg[mb] = mfma32x32x16(a, bg, accg[mb]);
           accu[mb] = mfma32x32x16(a, bu, accu[mb]);
         }
       }
     }
-    // the B area is private to the wave: overwriting it after this block's
-    // reads is ordered by the wave's own LDS instruction order
-    if (more) stash(cur ^ 1);
+  };
+
+  // The B area is private to the wave: overwriting it after the reads of
+  // the previous block is ordered by the wave's own LDS instruction order.
+  if constexpr (NKB > 0) {
+    issue(0, 0);
+    if (NKB > 1) issue(1, 1);
+    stash(0, 0);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      __syncthreads();
+      if (kb + 2 < NKB) issue(kb & 1, kb + 2);
+      compute(kb & 1);
+      if (kb + 1 < NKB) stash((kb + 1) & 1, (kb + 1) & 1);
+    }
+  } else {
+    issue(0, 0);
+    stash(0, 0);
+    for (int kb = 0; kb < nkb; ++kb) {
+      __syncthreads();
+      const int cur = kb & 1;
+      const bool more = kb + 1 < nkb;
+      if (more) issue(0, kb + 1);
+      compute(cur);
+      if (more) stash(0, cur ^ 1);
+    }
   }
 
   uint16_t* ohi = shared ? sact_hi : act_hi;
@@ -217,12 +237,12 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   const int ncol_tiles = H / kDownCols;
   const int item = xcd_item(blockIdx.x, meta[0] * ncol_tiles);
   if (item < 0) return;
-  const int tile = item / ncol_tiles, nt = item - tile * ncol_tiles;
-  const int grp = tiles[2 * tile], row0 = tiles[2 * tile + 1];
+  const GroupItem gi = group_item(item, ncol_tiles, tiles, offsets, E, T, kRowsPerTile);
+  const int nt = gi.nt, grp = gi.grp, row0 = gi.row0;
   const bool shared = grp == E;
   const int Ie = shared ? Is : I;
-  const int seg0 = shared ? 0 : offsets[grp];
-  const int cnt = shared ? static_cast<int>(T) : offsets[grp + 1] - seg0;
+  const int seg0 = gi.seg0;
+  const int cnt = gi.cnt;
   const int rows = min(kRowsPerTile, cnt - row0);
   if (rows <= 0) return;
   const int nmb = (rows + 31) >> 5;
@@ -429,9 +449,15 @@ hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t*
   const int ncol = (I > Is ? I : Is) / kUpCols;
   const int64_t items = static_cast<int64_t>(max_tiles) * ncol;
   const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
-  ffn_up_kernel<<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta, act_hi,
-                                          act_lo, sact_hi, sact_lo, gu, sgu, T, H, E, K, I, Is,
-                                          ncol);
+  // the unrolled instantiation covers hidden size 2048
+  if (H == 2048)
+    ffn_up_kernel<32><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta,
+                                                act_hi, act_lo, sact_hi, sact_lo, gu, sgu, T, H, E,
+                                                K, I, Is, ncol);
+  else
+    ffn_up_kernel<0><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta,
+                                               act_hi, act_lo, sact_hi, sact_lo, gu, sgu, T, H, E,
+                                               K, I, Is, ncol);
   return hipGetLastError();
 }
 

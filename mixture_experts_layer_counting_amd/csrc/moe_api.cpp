@@ -23,7 +23,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // ---------------------------------------------------------------------------
 struct Layout {
   size_t err = 0;         // int error word (first 256 bytes)
-  size_t rpart = 0;       // [T][H/256][E] f32: router MFMA sums per 256-wide K chunk
+  size_t rlogits = 0;     // router chunk sums [T][H/256][E] f32, or logits [T][E] f32 for large T
   size_t wsplit = 0;      // [3][E][H] bf16: exact hi/mid/lo split of the router weight
   size_t hist = 0;        // [NB][E+1] i32
   size_t block_base = 0;  // [NB][E] i32
@@ -61,7 +61,7 @@ Layout make_layout(const moe_dims& d) {
     return at;
   };
   L.err = take(kAlign);
-  L.rpart = take(static_cast<size_t>(d.hidden / 256) * T * E * 4);
+  L.rlogits = take(static_cast<size_t>(moe::router_full(T) ? 1 : d.hidden / 256) * T * E * 4);
   L.wsplit = take(static_cast<size_t>(3) * E * d.hidden * 2);
   L.hist = take(static_cast<size_t>(L.nblocks) * (E + 1) * 4);
   L.block_base = take(static_cast<size_t>(L.nblocks) * E * 4);
@@ -188,8 +188,8 @@ int check_device() {
     if (_st != MOE_OK) return _st;          \
   } while (0)
 
-// Optional per-kernel events of moe_forward_profiled: when set, an event is
-// recorded before every launch.
+// Optional per-kernel events of moe_forward_profiled: when set, event i is
+// recorded before launch i (NULL entries are skipped).
 struct Marks {
   hipEvent_t* ev = nullptr;
   int n = 0;
@@ -197,7 +197,8 @@ struct Marks {
   hipStream_t s = nullptr;
   hipError_t mark() {
     if (!ev || next >= n) return hipSuccess;
-    return hipEventRecord(ev[next++], s);
+    hipEvent_t e = ev[next++];
+    return e ? hipEventRecord(e, s) : hipSuccess;
   }
 };
 thread_local Marks* g_marks = nullptr;
@@ -230,18 +231,37 @@ void add_weights(Args& a, const moe_dims& d, const moe_weights* w, bool router, 
 // ---------------------------------------------------------------------------
 // launch sequences (arguments already validated)
 // ---------------------------------------------------------------------------
+// sg: when non-null, the top-k kernel also writes the shared-expert gate.
 int run_route(const moe_dims& d, const uint16_t* x, const moe_weights* w, moe_routes* r, void* ws,
-              const Layout& L, hipStream_t s) {
-  float* part = at<float>(ws, L.rpart);
+              const Layout& L, float* sg, hipStream_t s) {
   uint16_t* planes = at<uint16_t>(ws, L.wsplit);
+  float* rbuf = at<float>(ws, L.rlogits);
+  const uint16_t* xs = sg ? x : nullptr;
+  const uint16_t* wsg = sg ? w->w_sgate : nullptr;
   MOE_LAUNCH(moe::launch_router_split(w->w_router, planes, d.hidden, d.experts, s));
-  MOE_LAUNCH(moe::launch_router_logits(x, planes, part, d.tokens, d.hidden, d.experts, s));
-  MOE_LAUNCH(moe::launch_topk_gate(part, w->router_bias, r->logits, r->topk_idx, r->topk_gate,
-                                   d.tokens, d.hidden, d.experts, d.top_k, s));
+  if (moe::router_full(d.tokens)) {
+    float* logits = r->logits ? r->logits : rbuf;
+    MOE_LAUNCH(moe::launch_router_full(x, planes, w->router_bias, logits, d.tokens, d.hidden,
+                                       d.experts, s));
+    MOE_LAUNCH(moe::launch_topk_gate(logits, 1, nullptr, nullptr, r->topk_idx, r->topk_gate, xs,
+                                     wsg, sg, d.tokens, d.hidden, d.experts, d.top_k, s));
+  } else {
+    MOE_LAUNCH(moe::launch_router_part(x, planes, rbuf, d.tokens, d.hidden, d.experts, s));
+    MOE_LAUNCH(moe::launch_topk_gate(rbuf, d.hidden / 256, w->router_bias, r->logits,
+                                     r->topk_idx, r->topk_gate, xs, wsg, sg, d.tokens, d.hidden,
+                                     d.experts, d.top_k, s));
+  }
   return MOE_OK;
 }
 
 int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hipStream_t s) {
+  if (moe::sort_small_fits(d.tokens, d.experts)) {
+    MOE_LAUNCH(moe::launch_route_sort_small(r->topk_idx, r->expert_offsets, r->route_pos,
+                                            r->sorted_route, at<int32_t>(ws, L.tiles),
+                                            at<int32_t>(ws, L.meta), at<int>(ws, L.err), d.tokens,
+                                            d.experts, d.top_k, d.shared_inter > 0, s));
+    return MOE_OK;
+  }
   MOE_LAUNCH(moe::launch_route_hist(r->topk_idx, at<int32_t>(ws, L.hist), r->route_pos, d.tokens,
                                     d.experts, d.top_k, s));
   MOE_LAUNCH(moe::launch_route_scan(at<int32_t>(ws, L.hist), at<int32_t>(ws, L.block_base),
@@ -254,15 +274,16 @@ int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hip
   return MOE_OK;
 }
 
-// tiles_ready: the work list in the workspace was built by run_permute.
+// whole_forward: the work list in the workspace was built by run_permute and
+// the shared-expert gate by run_route.
 int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const moe_routes* r,
-            moe_saved* sv, void* ws, const Layout& L, bool tiles_ready, hipStream_t s) {
+            moe_saved* sv, void* ws, const Layout& L, bool whole_forward, hipStream_t s) {
   const int has_shared = d.shared_inter > 0;
-  if (!tiles_ready)
+  if (!whole_forward)
     MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles),
                                      at<int32_t>(ws, L.meta), d.experts, d.tokens, has_shared,
                                      moe::kRowsPerTile, s));
-  if (has_shared)
+  if (has_shared && !whole_forward)
     MOE_LAUNCH(moe::launch_shared_gate(x, w->w_sgate, sv->shared_gate, d.tokens, d.hidden, s));
   MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, r->expert_offsets, r->sorted_route,
                                 at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta),
@@ -366,7 +387,7 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const moe_weights* w, moe
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_ROUTE));
   MOE_TRY(check_device());
-  return run_route(d, x, w, routes, ws, make_layout(d), stream);
+  return run_route(d, x, w, routes, ws, make_layout(d), nullptr, stream);
 }
 
 int moe_permute(const moe_dims* dims, moe_routes* routes, void* ws, size_t ws_bytes,
@@ -450,15 +471,29 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, m
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD));
   MOE_TRY(check_device());
   const Layout L = make_layout(d);
-  MOE_TRY(run_route(d, x, w, routes, ws, L, stream));
+  MOE_TRY(run_route(d, x, w, routes, ws, L, d.shared_inter > 0 ? saved->shared_gate : nullptr,
+                    stream));
   MOE_TRY(run_permute(d, routes, ws, L, stream));
   MOE_TRY(run_ffn(d, x, w, routes, saved, ws, L, true, stream));
   return run_combine(d, routes, saved, out_f32, out_bf16, stream);
 }
 
+namespace {
+const char* const kFwdSmall[] = {"router_split", "router_logits", "topk_gate", "route_sort",
+                                 "ffn_up", "ffn_down", "combine"};
+const char* const kFwdLarge[] = {"router_split", "router_logits", "topk_gate", "route_hist",
+                                 "route_scan", "route_scatter", "ffn_up", "ffn_down", "combine"};
+}  // namespace
+
 int moe_forward_kernel_count(const moe_dims* dims) {
   if (check_dims(dims) != MOE_OK) return 0;
-  return dims->shared_inter > 0 ? 10 : 9;
+  return moe::sort_small_fits(dims->tokens, dims->experts) ? 7 : 9;
+}
+
+const char* moe_forward_kernel_name(const moe_dims* dims, int i) {
+  const int n = moe_forward_kernel_count(dims);
+  if (i < 0 || i >= n) return nullptr;
+  return n == 7 ? kFwdSmall[i] : kFwdLarge[i];
 }
 
 int moe_forward_profiled(const moe_dims* dims, const moe_weights* w, const uint16_t* x,

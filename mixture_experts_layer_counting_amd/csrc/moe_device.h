@@ -19,6 +19,9 @@ constexpr int kUpCols = 128;
 constexpr int kDownCols = 128;
 // Tokens per block of the permutation's counting sort.
 constexpr int kSortBlock = 256;
+// 32-bit token-mask words (experts x ceil(tokens / 32)) of the one-workgroup
+// counting sort; larger batches take the three-kernel sort.
+constexpr int kSortSmallWords = 16384;
 // Rows per row tile of the backward's grouped GEMMs (and the edge of their
 // 128x128 output tiles).
 constexpr int kBwdRowsPerTile = 128;
@@ -94,6 +97,35 @@ __device__ __forceinline__ int xcd_item(int g, int items) {
   if (slot >= per) return -1;
   const int it = xcd * per + slot;
   return it < items ? it : -1;
+}
+
+// Work item -> (row tile, column tile) of a grouped GEMM whose work list
+// `tiles` holds (group, first row) pairs, each group's row tiles contiguous
+// and in row order.  Items [first*ncol, (first+nrt)*ncol) belong to the group
+// whose row tiles are first .. first+nrt-1 (so a group's items stay one
+// contiguous range: one XCD under xcd_item); inside that range the column
+// tile is the slow index, so the row tiles that stream the same weight slice
+// are dispatched next to each other and share its reads in L2.
+struct GroupItem {
+  int tile, nt, grp, row0, seg0, cnt;
+};
+__device__ __forceinline__ GroupItem group_item(int item, int ncol, const int32_t* tiles,
+                                                const int32_t* offsets, int E, int64_t T,
+                                                int rows_per_tile) {
+  GroupItem g;
+  const int tg = item / ncol;
+  g.grp = tiles[2 * tg];
+  const int first = tg - tiles[2 * tg + 1] / rows_per_tile;
+  const bool shared = g.grp == E;
+  g.seg0 = shared ? 0 : offsets[g.grp];
+  g.cnt = shared ? static_cast<int>(T) : offsets[g.grp + 1] - g.seg0;
+  const int nrt = max(1, (g.cnt + rows_per_tile - 1) / rows_per_tile);
+  const int local = item - first * ncol;
+  g.nt = local / nrt;
+  const int rt = local - g.nt * nrt;
+  g.tile = first + rt;
+  g.row0 = rt * rows_per_tile;
+  return g;
 }
 
 }  // namespace moe

@@ -9,13 +9,28 @@
 
 namespace moe {
 
-// Router: exact three-way bf16 split of the fp32 weight, per-chunk MFMA sums
-// part[t][c][e] (c < H/256), then top-k, which reduces them to the logits.
+// Router: exact three-way bf16 split of the fp32 weight, the logits (or their
+// per-chunk sums), then top-k and gates (optionally with the shared-expert
+// gate).
+// Permutation: one-workgroup counting sort when sort_small_fits, else the
+// three passes hist / scan / scatter.
 hipError_t launch_router_split(const float* wr, uint16_t* planes, int H, int E, hipStream_t stream);
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* planes, float* part, int64_t T,
-                                int H, int E, hipStream_t stream);
-hipError_t launch_topk_gate(const float* part, const float* bias, float* logits, int32_t* topk_idx,
-                            float* topk_gate, int64_t T, int H, int E, int K, hipStream_t stream);
+// router_full(T): large batches take router_full (logits written directly),
+// smaller ones router_part (per-chunk sums) with top-k forming the logits.
+bool router_full(int64_t T);
+hipError_t launch_router_part(const uint16_t* x, const uint16_t* planes, float* part, int64_t T,
+                              int H, int E, hipStream_t stream);
+hipError_t launch_router_full(const uint16_t* x, const uint16_t* planes, const float* bias,
+                              float* logits, int64_t T, int H, int E, hipStream_t stream);
+hipError_t launch_topk_gate(const float* src, int nchunk, const float* bias, float* logits_out,
+                            int32_t* topk_idx, float* topk_gate, const uint16_t* x,
+                            const uint16_t* w_sgate, float* sg, int64_t T, int H, int E, int K,
+                            hipStream_t stream);
+bool sort_small_fits(int64_t T, int E);
+hipError_t launch_route_sort_small(const int32_t* topk_idx, int32_t* offsets, int32_t* route_pos,
+                                   int32_t* sorted_route, int32_t* tiles, int32_t* meta,
+                                   int* err_word, int64_t T, int E, int K, int has_shared,
+                                   hipStream_t stream);
 hipError_t launch_route_hist(const int32_t* topk_idx, int32_t* hist, int32_t* route_rank,
                              int64_t T, int E, int K, hipStream_t stream);
 hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* offsets,
