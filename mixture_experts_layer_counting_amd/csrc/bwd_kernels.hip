@@ -113,8 +113,9 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
 //     (ds_read_b64_tr_b16), two per fragment.  The 64 bytes of padding per
 //     row make those reads free of bank conflicts on MI355X (measured with
 //     the LDS bank-conflict counter: 256- and 288-byte rows conflict).
-// An operand given as three bf16 planes (hi, mid, lo) takes three MFMAs per
-// K step, in that order.
+// An fp32 operand (dGU, g*act) is given as kGradPlanes bf16 planes, a hi/lo
+// pair (hi = bf16(v), lo = bf16(v - hi)), and takes one MFMA per plane per K
+// step, hi first.
 //
 // Modes (group g: routed expert g < E, shared expert g == E; p = row of the
 // group's segment in sorted order, t(p) its token):
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
 // The K order of every output element is fixed: K blocks in ascending order
 // (for the two dgrad modes starting at a rotation fixed by the group and the
 // column tile, as in the forward), in each block K step 0 then 1, and in
-// each step the planes hi, mid, lo.  A dgrad row's result therefore depends
+// each step the planes hi, lo.  A dgrad row's result therefore depends
 // only on its own row, its expert and its column tile, never on the batch.
 // ---------------------------------------------------------------------------
 enum BwdMode { kDact = 0, kDx = 1, kDw2 = 2, kDw13 = 3 };
@@ -182,10 +183,10 @@ struct BwdArgs {
   const uint16_t* ws2;
   const float* gu;
   const float* sgu;
-  uint16_t* dgu[3];    // planes of dGU [R][2I]
-  uint16_t* sdgu[3];   // [T][2Is]
-  uint16_t* gact[3];   // planes of g*act [R][I]
-  uint16_t* sgact[3];  // [T][Is]
+  uint16_t* dgu[kGradPlanes];    // planes of dGU [R][2I]
+  uint16_t* sdgu[kGradPlanes];   // [T][2Is]
+  uint16_t* gact[kGradPlanes];   // planes of g*act [R][I]
+  uint16_t* sgact[kGradPlanes];  // [T][Is]
   float* dx_route;
   float* dx_shared;
   float* dw13;
@@ -252,14 +253,17 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
 template <int MODE>
 __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void bwd_gemm_kernel(const BwdArgs a) {
   constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
-  constexpr int NPA = (MODE == kDx || MODE == kDw13) ? 3 : 1;
-  constexpr int NPB = MODE == kDw2 ? 3 : 1;
+  constexpr int NPA = (MODE == kDx || MODE == kDw13) ? kGradPlanes : 1;
+  constexpr int NPB = MODE == kDw2 ? kGradPlanes : 1;
   constexpr int APLANE = WGRAD ? kRPlane : kKPlane;
   constexpr int STAGE = NPA * APLANE + NPB * kRPlane;
   // weight gradients (short contractions): one LDS stage and two barriers
   // per K block, which leaves room for three workgroups per CU
   constexpr int NSTAGE = WGRAD ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE];
+  // the epilogue stages a 64-row half of the fp32 tile (stride kBT + 4) in
+  // the same area
+  constexpr int EPI = 64 * (kBT + 4) * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI];
 
   BwdTile w;
   if (!bwd_decode<MODE>(a, blockIdx.x, w)) return;
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
     // pre-activations are read and the gradient planes written 16 bytes at a
     // time.
     constexpr int ES = kBT + 4;  // fp32 row stride of a staged half
-    static_assert(64 * ES * 4 <= 2 * STAGE * 2, "a staged half fits in the operand stages");
+    static_assert(64 * ES * 2 <= EPI, "a staged half fits in the shared area");
     float* ep = reinterpret_cast<float*>(smem);
     const int er = tid >> 4, ec = (tid & 15) * 8;
     for (int hh = 0; hh < 2; ++hh) {
@@ -474,7 +478,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
         const f32x4v_t g1 = *reinterpret_cast<const f32x4v_t*>(gur + col + 4);
         const f32x4v_t u0 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col);
         const f32x4v_t u1 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col + 4);
-        uint32_t pg[3][4], pu[3][4], pa[3][4];
+        uint32_t pg[kGradPlanes][4], pu[kGradPlanes][4], pa[kGradPlanes][4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float dv = e < 4 ? d0[e] : d1[e - 4];
@@ -486,13 +490,13 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
           const float silu = silu_f32(gv);
           const float dup = dact * silu;
           const float gact = g * (silu * uv);
-          uint16_t sg3[3], su3[3], sa3[3];
-          split3(dgate, sg3);
-          split3(dup, su3);
-          split3(gact, sa3);
+          uint16_t sg3[kGradPlanes], su3[kGradPlanes], sa3[kGradPlanes];
+          split_hi_lo(dgate, sg3[0], sg3[1]);
+          split_hi_lo(dup, su3[0], su3[1]);
+          split_hi_lo(gact, sa3[0], sa3[1]);
           const int sh = 16 * (e & 1);
 #pragma unroll
-          for (int q = 0; q < 3; ++q) {
+          for (int q = 0; q < kGradPlanes; ++q) {
             if ((e & 1) == 0) {
               pg[q][e >> 1] = sg3[q];
               pu[q][e >> 1] = su3[q];
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
           }
         }
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
+        for (int q = 0; q < kGradPlanes; ++q) {
           uint16_t* dq = (w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie;
           st16(dq + col, u32x4_t{pg[q][0], pg[q][1], pg[q][2], pg[q][3]});
           st16(dq + Ie + col, u32x4_t{pu[q][0], pu[q][1], pu[q][2], pu[q][3]});
@@ -517,31 +521,45 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
     return;
   }
 
-  // ---- epilogue: lane holds D[wm*64 + 32mb + acc_row(v)][wn*64 + 32nb + i]
+  // ---- epilogue: the 128x128 fp32 tile goes through LDS one 64-row half at
+  // a time (waves with wm == half write their accumulators), then each row
+  // leaves as 16-byte pieces, 512 contiguous bytes per row per 32 lanes.
+  constexpr int ES = kBT + 4;  // fp32 row stride of a staged half
+  static_assert(64 * ES * 2 <= EPI, "a staged half fits in the shared area");
+  float* ep = reinterpret_cast<float*>(smem);
+  const int piece = tid & 31;
+  for (int hh = 0; hh < 2; ++hh) {
+    __syncthreads();
+    if (wm == hh) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int col = w.n0 + wn * 64 + nb * 32 + i;
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int lrow = wm * 64 + mb * 32 + acc_row(v, half);
-        const float val = acc[mb][nb][v];
-        if (MODE == kDx) {
-          if (lrow >= w.rows) continue;
-          if (w.shared) {
-            a.dx_shared[static_cast<int64_t>(w.m0 + lrow) * a.H + col] = val;
-          } else {
-            const int64_t r = a.sorted_route[static_cast<int64_t>(w.seg0) + w.m0 + lrow];
-            if (r >= 0 && r < a.T * a.K) a.dx_route[r * a.H + col] = val;
-          }
-        } else if (MODE == kDw2) {
-          float* o = w.shared ? a.dws2 : a.dw2 + static_cast<int64_t>(w.grp) * a.H * a.I;
-          o[static_cast<int64_t>(w.m0 + lrow) * Ie + col] = val;
+          for (int v = 0; v < 16; ++v)
+            ep[(mb * 32 + acc_row(v, half)) * ES + wn * 64 + nb * 32 + i] = acc[mb][nb][v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (tid >> 5) + 8 * j;
+      const int lrow = hh * 64 + r;
+      const u32x4_t val = ld16(ep + r * ES + piece * 4);
+      const int col = w.n0 + piece * 4;
+      if (MODE == kDx) {
+        if (lrow >= w.rows) continue;
+        if (w.shared) {
+          st16(a.dx_shared + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
         } else {
-          float* o = w.shared ? a.dws13 : a.dw13 + static_cast<int64_t>(w.grp) * 2 * a.I * a.H;
-          o[static_cast<int64_t>(w.m0 + lrow) * a.H + col] = val;
+          const int64_t rt = a.sorted_route[static_cast<int64_t>(w.seg0) + w.m0 + lrow];
+          if (rt >= 0 && rt < a.T * a.K) st16(a.dx_route + rt * a.H + col, val);
         }
+      } else if (MODE == kDw2) {
+        float* o = w.shared ? a.dws2 : a.dw2 + static_cast<int64_t>(w.grp) * a.H * a.I;
+        st16(o + static_cast<int64_t>(w.m0 + lrow) * Ie + col, val);
+      } else {
+        float* o = w.shared ? a.dws13 : a.dw13 + static_cast<int64_t>(w.grp) * 2 * a.I * a.H;
+        st16(o + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
       }
     }
   }
@@ -760,7 +778,7 @@ hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
   a.ws2 = L.ws2;
   a.gu = L.gu;
   a.sgu = L.sgu;
-  for (int q = 0; q < 3; ++q) {
+  for (int q = 0; q < kGradPlanes; ++q) {
     a.dgu[q] = L.dgu[q];
     a.sdgu[q] = L.sdgu[q];
     a.gact[q] = L.gact[q];

@@ -52,12 +52,12 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // loads of the next K blocks in flight keeps enough bytes moving.
 // Outputs: act as a bf16 hi/lo pair (row = sorted position, or token for the
 // shared expert) and, if requested, the fp32 gate/up values.
-// NKB > 0 instantiates the K loop fully unrolled for H = 64 * NKB with two
-// register sets of loads (block kb + 2 is loaded while kb is multiplied and
-// kb + 1 waits in registers); NKB = 0 is the general loop with one block in
-// flight.  Both run the same MFMA sequence on every output element.
+// NKB > 0 instantiates the K loop fully unrolled for H = 64 * NKB with a
+// ring of NSET register sets of loads (blocks kb + 1 .. kb + NSET - 1 are in
+// flight while kb is multiplied); NKB = 0 is the general loop with one block
+// in flight (NSET = 1).  All run the same MFMA sequence on every element.
 // ---------------------------------------------------------------------------
-template <int NKB>
+template <int NKB, int NSET>
 __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
     const uint16_t* __restrict__ ws13, const int32_t* __restrict__ offsets,
@@ -122,7 +122,6 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     accg[mb] = zero16();
     accu[mb] = zero16();
   }
-  constexpr int NSET = NKB > 0 ? 2 : 1;
   u32x4_t ra[NSET][2], rb[NSET][8];
 
   auto issue = [&](int set, int kb) {
@@ -163,15 +162,15 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   // The B area is private to the wave: overwriting it after the reads of
   // the previous block is ordered by the wave's own LDS instruction order.
   if constexpr (NKB > 0) {
-    issue(0, 0);
-    if (NKB > 1) issue(1, 1);
+#pragma unroll
+    for (int q = 0; q < NSET && q < NKB; ++q) issue(q, q);
     stash(0, 0);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       __syncthreads();
-      if (kb + 2 < NKB) issue(kb & 1, kb + 2);
+      if (kb + NSET < NKB) issue(kb % NSET, kb + NSET);
       compute(kb & 1);
-      if (kb + 1 < NKB) stash((kb + 1) & 1, (kb + 1) & 1);
+      if (kb + 1 < NKB) stash((kb + 1) % NSET, (kb + 1) & 1);
     }
   } else {
     issue(0, 0);
@@ -221,12 +220,12 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 // wave w owns columns nt*128 + 32w .. +32.  Same staging as the up
 // projection: the wave's 32 W2 rows through a private LDS area, the act
 // planes through a double-buffered shared one.
-// NKB > 0 instantiates the K loop fully unrolled for Ie = 64 * NKB with two
-// register sets of loads in flight (block kb + 2 loads while kb is
-// multiplied); NKB = 0 is the general loop with one block in flight.  Both
-// run the same MFMA sequence on every output element.
+// NKB > 0 instantiates the K loop fully unrolled for Ie = 64 * NKB with a
+// ring of NSET register sets of loads (blocks kb + 1 .. kb + NSET - 1 in
+// flight while kb is multiplied); NKB = 0 is the general loop with one block
+// in flight (NSET = 1).  All run the same MFMA sequence on every element.
 // ---------------------------------------------------------------------------
-template <int NKB>
+template <int NKB, int NSET>
 __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     const uint16_t* __restrict__ act_hi, const uint16_t* __restrict__ act_lo,
     const uint16_t* __restrict__ sact_hi, const uint16_t* __restrict__ sact_lo,
@@ -286,7 +285,6 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   f32x16_t acc[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) acc[mb] = zero16();
-  constexpr int NSET = NKB > 0 ? 2 : 1;
   u32x4_t rh[NSET][2], rl[NSET][2], rb[NSET][4];
 
   // activation rows past the tile's end repeat its last row (unused)
@@ -331,15 +329,15 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   // The B area is private to the wave: overwriting it after the reads of
   // the previous block is ordered by the wave's own LDS instruction order.
   if constexpr (NKB > 0) {
-    issue(0, 0);
-    if (NKB > 1) issue(1, 1);
+#pragma unroll
+    for (int q = 0; q < NSET && q < NKB; ++q) issue(q, q);
     stash(0, 0);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       __syncthreads();
-      if (kb + 2 < NKB) issue(kb & 1, kb + 2);
+      if (kb + NSET < NKB) issue(kb % NSET, kb + NSET);
       compute(kb & 1);
-      if (kb + 1 < NKB) stash((kb + 1) & 1, (kb + 1) & 1);
+      if (kb + 1 < NKB) stash((kb + 1) % NSET, (kb + 1) & 1);
     }
   } else {
     issue(0, 0);
@@ -354,17 +352,26 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     }
   }
 
+  // Epilogue: the 64 x 128 fp32 tile is staged in LDS (the A area) and each
+  // route row goes out as 16-byte pieces, 512 contiguous bytes per row.
+  __syncthreads();  // every wave is done with the A area
+  static_assert(sizeof(As) >= kRowsPerTile * kDownCols * sizeof(float), "staging fits the A area");
+  float* Cs = reinterpret_cast<float*>(&As[0][0][0]);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (mb < nmb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = mb * 32 + acc_row(v, half);
-        if (row < rows) {
-          const int dst = s_dst[row];
-          if (dst >= 0) out[static_cast<int64_t>(dst) * H + n0 + j] = acc[mb][v];
-        }
-      }
+      for (int v = 0; v < 16; ++v) Cs[(mb * 32 + acc_row(v, half)) * kDownCols + wave * 32 + j] = acc[mb][v];
+    }
+  }
+  __syncthreads();
+  const int piece = tid & 31;  // 32 pieces of 4 floats per row
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 5) + 8 * i;
+    if (r < rows) {
+      const int dst = s_dst[r];
+      if (dst >= 0) st16(out + static_cast<int64_t>(dst) * H + nt * kDownCols + piece * 4, ld16(Cs + r * kDownCols + piece * 4));
     }
   }
 }
@@ -451,11 +458,11 @@ hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t*
   const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
   // the unrolled instantiation covers hidden size 2048
   if (H == 2048)
-    ffn_up_kernel<32><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta,
+    ffn_up_kernel<32, 2><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta,
                                                 act_hi, act_lo, sact_hi, sact_lo, gu, sgu, T, H, E,
                                                 K, I, Is, ncol);
   else
-    ffn_up_kernel<0><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta,
+    ffn_up_kernel<0, 1><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta,
                                                act_hi, act_lo, sact_hi, sact_lo, gu, sgu, T, H, E,
                                                K, I, Is, ncol);
   return hipGetLastError();
@@ -471,10 +478,10 @@ hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
   const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
   // the unrolled instantiation covers expert and shared sizes of 512
   if (I == 512 && (Is == 0 || Is == 512))
-    ffn_down_kernel<8><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
+    ffn_down_kernel<8, 2><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
                                                  sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
   else
-    ffn_down_kernel<0><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
+    ffn_down_kernel<0, 1><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
                                                  sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
   return hipGetLastError();
 }

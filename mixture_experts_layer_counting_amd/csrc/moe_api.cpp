@@ -35,10 +35,10 @@ struct Layout {
   // backward regions (after fwd_end)
   size_t tiles_bwd = 0, meta_bwd = 0;  // work list of the backward's row tiles
   size_t dl = 0, dz = 0;             // [T][K], [T] f32
-  size_t dgu[3] = {0, 0, 0};         // [R][2I] bf16 planes (hi, mid, lo)
-  size_t sdgu[3] = {0, 0, 0};        // [T][2Is]
-  size_t gact[3] = {0, 0, 0};        // [R][I]
-  size_t sgact[3] = {0, 0, 0};       // [T][Is]
+  size_t dgu[moe::kGradPlanes] = {};    // [R][2I] bf16 planes (hi, lo)
+  size_t sdgu[moe::kGradPlanes] = {};   // [T][2Is]
+  size_t gact[moe::kGradPlanes] = {};   // [R][I]
+  size_t sgact[moe::kGradPlanes] = {};  // [T][Is]
   size_t dx_route = 0;               // [R][H] f32
   size_t dx_shared = 0;              // [T][H] f32
   size_t wsg_partial = 0;            // [ceil(T/64)][H] f64
@@ -78,7 +78,7 @@ Layout make_layout(const moe_dims& d) {
   L.meta_bwd = take(64 * 4);
   L.dl = take(static_cast<size_t>(R) * 4);
   L.dz = take(static_cast<size_t>(T) * 4);
-  for (int q = 0; q < 3; ++q) {
+  for (int q = 0; q < moe::kGradPlanes; ++q) {
     L.dgu[q] = take(static_cast<size_t>(R) * 2 * I * 2);
     L.sdgu[q] = take(static_cast<size_t>(T) * 2 * Is * 2);
     L.gact[q] = take(static_cast<size_t>(R) * I * 2);
@@ -585,7 +585,7 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
   b.ws2 = sh ? w->ws2 : nullptr;
   b.gu = saved->gu;
   b.sgu = sh ? saved->shared_gu : nullptr;
-  for (int q = 0; q < 3; ++q) {
+  for (int q = 0; q < moe::kGradPlanes; ++q) {
     b.dgu[q] = at<uint16_t>(ws, L.dgu[q]);
     b.sdgu[q] = at<uint16_t>(ws, L.sdgu[q]);
     b.gact[q] = at<uint16_t>(ws, L.gact[q]);

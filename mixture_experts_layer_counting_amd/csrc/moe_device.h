@@ -25,6 +25,9 @@ constexpr int kSortSmallWords = 16384;
 // Rows per row tile of the backward's grouped GEMMs (and the edge of their
 // 128x128 output tiles).
 constexpr int kBwdRowsPerTile = 128;
+// bf16 planes carrying each fp32 backward GEMM operand (dGU, g*act): a hi/lo
+// pair, hi = bf16(v), lo = bf16(v - hi).
+constexpr int kGradPlanes = 2;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);

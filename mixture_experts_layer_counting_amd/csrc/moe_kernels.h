@@ -77,10 +77,10 @@ struct BwdLaunch {
   const uint16_t* ws2;
   const float* gu;
   const float* sgu;
-  uint16_t* dgu[3];    // hi/mid/lo planes
-  uint16_t* sdgu[3];
-  uint16_t* gact[3];
-  uint16_t* sgact[3];
+  uint16_t* dgu[kGradPlanes];    // hi/lo planes
+  uint16_t* sdgu[kGradPlanes];
+  uint16_t* gact[kGradPlanes];
+  uint16_t* sgact[kGradPlanes];
   float *dx_route, *dx_shared;
   float *dw13, *dw2, *dws13, *dws2;
 };

@@ -22,3 +22,4 @@ from .moe_oracle import (  # noqa: F401
     silu,
     swiglu_expert,
 )
+from .moe_oracle import _swiglu_backward as swiglu_backward  # noqa: F401

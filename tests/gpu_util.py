@@ -129,6 +129,33 @@ def router_term_scale(x_bits, idx, dl, experts):
     return s
 
 
+def swiglu_term_scales(dy, gu_rows, x_rows, w13_bits, w2_bits):
+    """Sums of the absolute per-row terms of one expert's weight gradients:
+    sum_r |dGU_r| x |x_r| (shape of dW13) and sum_r |dy_r| x |act_r| (shape
+    of dW2), with dGU from the oracle's SwiGLU backward of these rows."""
+    dgu = O.swiglu_backward(dy, gu_rows, x_rows, w13_bits, w2_bits)[3]
+    inter = gu_rows.shape[1] // 2
+    gate, up = gu_rows[:, :inter], gu_rows[:, inter:]
+    act = gate / (1.0 + np.exp(-gate)) * up
+    return np.abs(dgu).T @ np.abs(x_rows), np.abs(dy).T @ np.abs(act)
+
+
+def expert_term_scales(layer, x_bits, dout_bits, idx, gates, gu, expert):
+    """swiglu_term_scales for routed expert `expert` (idx, gates, gu route-major
+    as the oracle's forward returns them)."""
+    K = idx.shape[1]
+    rows = np.nonzero(idx.reshape(-1) == expert)[0]
+    t = rows // K
+    dy = gates.reshape(-1)[rows, None] * O.bf16_to_f64(dout_bits)[t]
+    return swiglu_term_scales(dy, gu[rows], O.bf16_to_f64(x_bits)[t], layer["w13"][expert], layer["w2"][expert])
+
+
+def shared_term_scales(layer, x_bits, dout_bits, sg, sgu):
+    """swiglu_term_scales for the shared expert over all tokens."""
+    dy = sg[:, None] * O.bf16_to_f64(dout_bits)
+    return swiglu_term_scales(dy, sgu, O.bf16_to_f64(x_bits), layer["ws13"], layer["ws2"])
+
+
 def gate_term_scale(x_bits, dz):
     """Sum over tokens of |dz| * |x|: the absolute values of the per-token
     terms that the shared-gate weight gradient adds up."""

@@ -5,12 +5,12 @@ The input gradient dX, a per-token quantity, is compared with the per-token
 rule |gpu - ref| <= 5e-5 + 1e-3 |ref|.  A weight gradient sums n per-token
 terms over the batch; its absolute floor grows as sqrt(n)
 (tests/gpu_util.assert_close_sum), n = the routes summed into it (an
-expert's route count, or T for the shared expert and its gate).  The router
-and shared-gate weight gradients take the relative part against the sum of
-their terms' absolute values (sum over routes of |dl| |x|, over tokens of
-|dz| |x|): their terms carry the relative error of dl or dz, which come from
-H-long dot products of fp32 forward outputs, and terms of both signs cancel in
-the sum while their errors do not.  The small
+expert's route count, or T for the shared expert and its gate).  The
+relative part is taken against the sum of the terms' absolute values (sum
+over routes of |dGU| |x| for dW13, |dy| |act| for dW2, |dl| |x| for the
+router, |dz| |x| for the shared gate): each term carries a small relative
+error (the bf16 hi/lo operands, fp32 forward outputs), and terms of both
+signs cancel in the sum while their errors do not.  The small
 layer is compared in full; the 4096-token layer on sampled tokens (dX rows),
 sampled experts (their dW13, dW2 and router rows, from those experts' own
 routes) and the shared expert's weight gradients in full.
@@ -23,8 +23,8 @@ import mixture_experts_layer_counting_amd as m
 import oracle as O
 import workloads as W
 from tests.gpu_util import (DEV, assert_close, assert_close_sum, bf16_rne_bits, compare_routes, dev_bits,
-                            dev_weights, dims_of, gate_term_scale, gpu_forward, load_cfg,
-                            router_term_scale, say)
+                            dev_weights, dims_of, expert_term_scales, gate_term_scale, gpu_forward, load_cfg,
+                            router_term_scale, say, shared_term_scales)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,20 +56,25 @@ def full_backward_check(cfg, layer, x, dout):
     assert_close(dx32.cpu().numpy(), ref["dx"], "dX")
     assert np.array_equal(dx16.cpu().numpy().view(np.uint16), bf16_rne_bits(dx32.cpu().numpy()))
     load = np.bincount(idx.reshape(-1), minlength=cfg.experts)
-    router_scale = router_term_scale(x, ref_f["idx"], ref["dl"], cfg.experts)
+    scales = {"d_w_router": router_term_scale(x, ref_f["idx"], ref["dl"], cfg.experts),
+              "d_w13": np.zeros(layer["w13"].shape), "d_w2": np.zeros(layer["w2"].shape)}
+    for e in np.nonzero(load)[0]:
+        scales["d_w13"][e], scales["d_w2"][e] = expert_term_scales(layer, x, dout, ref_f["idx"], ref_f["gates"],
+                                                                  ref_f["gu"], int(e))
     for name, key in (("dW_router", "d_w_router"), ("dW13", "d_w13"), ("dW2", "d_w2")):
         got = getattr(gr, key).cpu().numpy().astype(np.float64)
         err = np.abs(got - ref[key])
         floor = 5e-5 * np.sqrt(np.maximum(1, load)).reshape(-1, *([1] * (got.ndim - 1)))
-        scale = np.maximum(np.abs(ref[key]), router_scale) if key == "d_w_router" else np.abs(ref[key])
+        scale = np.maximum(np.abs(ref[key]), scales[key])
         ratio = err / (floor + 1e-3 * scale)
         strict = err / (5e-5 + 1e-3 * np.abs(ref[key]))
         say(f"  {name}: max-abs {err.max():.3e}, worst err/tol {ratio.max():.3f} (sum rule), "
             f"{strict.max():.3f} (per-token rule)")
         assert ratio.max() <= 1.0, f"{name}: {(ratio > 1).sum()} elements outside tolerance"
     if cfg.shared_inter:
-        assert_close_sum(gr.d_ws13.cpu().numpy(), ref["d_ws13"], "dWs13", cfg.tokens)
-        assert_close_sum(gr.d_ws2.cpu().numpy(), ref["d_ws2"], "dWs2", cfg.tokens)
+        s13, s2 = shared_term_scales(layer, x, dout, ref_f["sg"], ref_f["sgu"])
+        assert_close_sum(gr.d_ws13.cpu().numpy(), ref["d_ws13"], "dWs13", cfg.tokens, s13)
+        assert_close_sum(gr.d_ws2.cpu().numpy(), ref["d_ws2"], "dWs2", cfg.tokens, s2)
         assert_close_sum(gr.d_w_sgate.cpu().numpy(), ref["d_w_sgate"], "dw_sgate", cfg.tokens,
                          gate_term_scale(x, ref["dz"]))
 
@@ -122,15 +127,18 @@ def test_bwd4k_sampled():
         fe = O.forward(layer, x[te], cfg.top_k, forced_idx=idx[te])
         rows = np.nonzero(fe["idx"].reshape(-1) == e)[0]
         r13, r2 = O.expert_weight_grads(layer, x[te], dout[te], fe["idx"], fe["gates"], fe["gu"][rows], int(e))
-        assert_close_sum(dw13[e], r13, f"dW13[{e}]", len(te))
-        assert_close_sum(dw2[e], r2, f"dW2[{e}]", len(te))
+        s13, s2 = expert_term_scales(layer, x[te], dout[te], fe["idx"], fe["gates"], fe["gu"], int(e))
+        assert_close_sum(dw13[e], r13, f"dW13[{e}]", len(te), s13)
+        assert_close_sum(dw2[e], r2, f"dW2[{e}]", len(te), s2)
         be = O.backward(layer, x[te], fe, dout[te])
         assert_close_sum(dwr[e], be["d_w_router"][e], f"dW_router[{e}]", len(te),
                          router_term_scale(x[te], fe["idx"], be["dl"], cfg.experts)[e])
     say("  oracle shared-expert gradients over all tokens")
     sh = O.shared_expert_grads(layer, x, dout)
-    assert_close_sum(gr.d_ws13.cpu().numpy(), sh["d_ws13"], "dWs13", cfg.tokens)
-    assert_close_sum(gr.d_ws2.cpu().numpy(), sh["d_ws2"], "dWs2", cfg.tokens)
+    _, s_sg, s_sgu = O.shared_expert(x, layer["ws13"], layer["ws2"], layer["w_sgate"])
+    s13, s2 = shared_term_scales(layer, x, dout, s_sg, s_sgu)
+    assert_close_sum(gr.d_ws13.cpu().numpy(), sh["d_ws13"], "dWs13", cfg.tokens, s13)
+    assert_close_sum(gr.d_ws2.cpu().numpy(), sh["d_ws2"], "dWs2", cfg.tokens, s2)
     assert_close_sum(gr.d_w_sgate.cpu().numpy(), sh["d_w_sgate"], "dw_sgate", cfg.tokens,
                      gate_term_scale(x, sh["dz"]))
 
