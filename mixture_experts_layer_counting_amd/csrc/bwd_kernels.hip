@@ -140,6 +140,7 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
 enum BwdMode { kDact = 0, kDx = 1, kDw2 = 2, kDw13 = 3 };
 
 constexpr int kBT = kBwdRowsPerTile;  // edge of every output tile (128)
+constexpr int kBwdTokLds = 256;       // weight-gradient segments up to this length keep their tokens in LDS
 constexpr int kBK = 32;
 constexpr int kKStride = 40;   // [row][k] layout: 32 k + 8 padding (bf16)
 constexpr int kRStride = 160;  // [k][col] layout: 128 columns + 32 padding
@@ -319,13 +320,24 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   }
 
   // wgrad: token of each of this thread's two k rows in the block being
-  // fetched next (-1: beyond the segment); the gathered operand's rows.
+  // fetched next (-1: beyond the segment); the gathered operand's rows.  A
+  // segment of at most kBwdTokLds rows has all its tokens read into LDS
+  // once, so later blocks' gathers wait on one LDS read instead of a global
+  // load.
+  __shared__ int s_tok[WGRAD ? kBwdTokLds : 1];
+  const bool tok_lds = WGRAD && w.rows <= kBwdTokLds;
+  if (tok_lds) {
+    if (tid < w.rows) s_tok[tid] = static_cast<int>(bwd_token(a, w, static_cast<int64_t>(w.seg0) + tid));
+    __syncthreads();
+  }
   int64_t tok[2] = {-1, -1};
   auto wg_tokens = [&](int kb, int64_t (&t)[2]) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int kk = kb * kBK + kr + 16 * c;
-      t[c] = kk < w.rows ? bwd_token(a, w, static_cast<int64_t>(w.seg0) + kk) : -1;
+      t[c] = kk < w.rows ? (tok_lds ? static_cast<int64_t>(s_tok[kk])
+                                    : bwd_token(a, w, static_cast<int64_t>(w.seg0) + kk))
+                         : -1;
     }
   };
 
