@@ -379,11 +379,13 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 // ---------------------------------------------------------------------------
 // Combine: out[t] = fma chain over slots k = 0..K-1 of g[t][k] * y[t*K+k],
 // from +0, then fma(sg[t], shared_y[t], .); fp32, one bf16 rounding.
-// One workgroup per token; each thread owns 4 consecutive hidden columns.
-// The K route rows (KT >= K slots, surplus slots re-read the last row and
-// are not used) are all loaded before the chain, so their latencies overlap.
+// One workgroup per token; each thread owns 4 consecutive hidden columns of
+// every 1024-column chunk.  The K route rows (KT >= K slots, surplus slots
+// re-read the last row and are not used) and the shared row of NC chunks
+// (NC = H / 1024 when instantiated, else one chunk at a time) are all loaded
+// before the chains, so their latencies overlap.
 // ---------------------------------------------------------------------------
-template <int KT>
+template <int KT, int NC>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ gate,
                                                       const float* __restrict__ sy,
@@ -391,50 +393,62 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       float* __restrict__ out32,
                                                       uint16_t* __restrict__ out16, int64_t T,
                                                       int H, int K) {
+  // NC > 0: H = 1024 * NC, every column chunk's route rows loaded in one
+  // batch; NC = 0: general H, one chunk at a time
+  constexpr int NB = NC > 0 ? NC : 1;
   const int64_t t = blockIdx.x;
   float g[KT];
 #pragma unroll
   for (int k = 0; k < KT; ++k) g[k] = gate[t * K + min(k, K - 1)];
   const float sgt = sy ? sg[t] : 0.f;
   const float* yt = y + t * K * H;
-  for (int c = threadIdx.x * 4; c < H; c += 1024) {
-    f32x4v_t v[KT];
+  const float* st = sy ? sy + t * H : yt;  // read (unused) when there is no shared expert
+  for (int c0 = threadIdx.x * 4; c0 < H; c0 += 1024 * NB) {
+    f32x4v_t v[NB][KT], vs[NB];
 #pragma unroll
-    for (int k = 0; k < KT; ++k)
-      v[k] = *reinterpret_cast<const f32x4v_t*>(yt + static_cast<int64_t>(min(k, K - 1)) * H + c);
-    f32x4v_t vs;
-    if (sy) vs = *reinterpret_cast<const f32x4v_t*>(sy + t * H + c);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int b = 0; b < NB; ++b) {
+      const int c = min(c0 + 1024 * b, H - 4);
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
-      if (k < K) {
-        a0 = fmaf(g[k], v[k][0], a0);
-        a1 = fmaf(g[k], v[k][1], a1);
-        a2 = fmaf(g[k], v[k][2], a2);
-        a3 = fmaf(g[k], v[k][3], a3);
+      for (int k = 0; k < KT; ++k)
+        v[b][k] = *reinterpret_cast<const f32x4v_t*>(yt + static_cast<int64_t>(min(k, K - 1)) * H + c);
+      vs[b] = *reinterpret_cast<const f32x4v_t*>(st + c);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c = c0 + 1024 * b;
+      if (c >= H) break;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        if (k < K) {
+          a0 = fmaf(g[k], v[b][k][0], a0);
+          a1 = fmaf(g[k], v[b][k][1], a1);
+          a2 = fmaf(g[k], v[b][k][2], a2);
+          a3 = fmaf(g[k], v[b][k][3], a3);
+        }
       }
-    }
-    if (sy) {
-      a0 = fmaf(sgt, vs[0], a0);
-      a1 = fmaf(sgt, vs[1], a1);
-      a2 = fmaf(sgt, vs[2], a2);
-      a3 = fmaf(sgt, vs[3], a3);
-    }
-    if (out32) {
-      f32x4v_t o;
-      o[0] = a0;
-      o[1] = a1;
-      o[2] = a2;
-      o[3] = a3;
-      *reinterpret_cast<f32x4v_t*>(out32 + t * H + c) = o;
-    }
-    if (out16) {
-      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(a0)) | (static_cast<uint32_t>(f32_to_bf16(a1)) << 16);
-      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(a2)) | (static_cast<uint32_t>(f32_to_bf16(a3)) << 16);
-      uint2 pk;
-      pk.x = lo;
-      pk.y = hi;
-      *reinterpret_cast<uint2*>(out16 + t * H + c) = pk;
+      if (sy) {
+        a0 = fmaf(sgt, vs[b][0], a0);
+        a1 = fmaf(sgt, vs[b][1], a1);
+        a2 = fmaf(sgt, vs[b][2], a2);
+        a3 = fmaf(sgt, vs[b][3], a3);
+      }
+      if (out32) {
+        f32x4v_t o;
+        o[0] = a0;
+        o[1] = a1;
+        o[2] = a2;
+        o[3] = a3;
+        *reinterpret_cast<f32x4v_t*>(out32 + t * H + c) = o;
+      }
+      if (out16) {
+        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(a0)) | (static_cast<uint32_t>(f32_to_bf16(a1)) << 16);
+        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(a2)) | (static_cast<uint32_t>(f32_to_bf16(a3)) << 16);
+        uint2 pk;
+        pk.x = lo;
+        pk.y = hi;
+        *reinterpret_cast<uint2*>(out16 + t * H + c) = pk;
+      }
     }
   }
 }
@@ -489,12 +503,13 @@ hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
 hipError_t launch_combine(const float* y, const float* gate, const float* sy, const float* sg,
                           float* out32, uint16_t* out16, int64_t T, int H, int K,
                           hipStream_t stream) {
-  if (K <= 10)
-    combine_kernel<10><<<static_cast<unsigned>(T), 256, 0, stream>>>(y, gate, sy, sg, out32, out16,
-                                                                    T, H, K);
+  const unsigned grid = static_cast<unsigned>(T);
+  if (K <= 10 && H == 2048)
+    combine_kernel<10, 2><<<grid, 256, 0, stream>>>(y, gate, sy, sg, out32, out16, T, H, K);
+  else if (K <= 10)
+    combine_kernel<10, 0><<<grid, 256, 0, stream>>>(y, gate, sy, sg, out32, out16, T, H, K);
   else
-    combine_kernel<16><<<static_cast<unsigned>(T), 256, 0, stream>>>(y, gate, sy, sg, out32, out16,
-                                                                    T, H, K);
+    combine_kernel<16, 0><<<grid, 256, 0, stream>>>(y, gate, sy, sg, out32, out16, T, H, K);
   return hipGetLastError();
 }
 
