@@ -10,8 +10,9 @@
 // runs in a fixed order.
 //
 // Precision: products of bf16 values are exact on the matrix cores; an fp32
-// operand (activation gradients, gate-scaled activations) enters split
-// exactly into three bf16 parts (hi + mid + lo), i.e. three MFMAs per K step.
+// operand (activation gradients, gate-scaled activations) enters as a bf16
+// hi/lo pair (hi = bf16(v), lo = bf16(v - hi), 16 significant bits of v),
+// i.e. two MFMAs per K step.
 // The grouped GEMMs accumulate in fp32 on the matrix cores in a fixed K
 // order; the small reductions (route weights, shared gate, router weights)
 // accumulate in fp64.
@@ -502,21 +503,21 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
           const float silu = silu_f32(gv);
           const float dup = dact * silu;
           const float gact = g * (silu * uv);
-          uint16_t sg3[kGradPlanes], su3[kGradPlanes], sa3[kGradPlanes];
-          split_hi_lo(dgate, sg3[0], sg3[1]);
-          split_hi_lo(dup, su3[0], su3[1]);
-          split_hi_lo(gact, sa3[0], sa3[1]);
+          uint16_t sgp[kGradPlanes], sup[kGradPlanes], sap[kGradPlanes];
+          split_hi_lo(dgate, sgp[0], sgp[1]);
+          split_hi_lo(dup, sup[0], sup[1]);
+          split_hi_lo(gact, sap[0], sap[1]);
           const int sh = 16 * (e & 1);
 #pragma unroll
           for (int q = 0; q < kGradPlanes; ++q) {
             if ((e & 1) == 0) {
-              pg[q][e >> 1] = sg3[q];
-              pu[q][e >> 1] = su3[q];
-              pa[q][e >> 1] = sa3[q];
+              pg[q][e >> 1] = sgp[q];
+              pu[q][e >> 1] = sup[q];
+              pa[q][e >> 1] = sap[q];
             } else {
-              pg[q][e >> 1] |= static_cast<uint32_t>(sg3[q]) << sh;
-              pu[q][e >> 1] |= static_cast<uint32_t>(su3[q]) << sh;
-              pa[q][e >> 1] |= static_cast<uint32_t>(sa3[q]) << sh;
+              pg[q][e >> 1] |= static_cast<uint32_t>(sgp[q]) << sh;
+              pu[q][e >> 1] |= static_cast<uint32_t>(sup[q]) << sh;
+              pa[q][e >> 1] |= static_cast<uint32_t>(sap[q]) << sh;
             }
           }
         }

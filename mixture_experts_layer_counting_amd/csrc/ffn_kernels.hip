@@ -216,16 +216,18 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 // ---------------------------------------------------------------------------
 // Down projection: y = act W2^T with act = hi + lo (two MFMA passes into the
 // same fp32 accumulator, hi first), written to route row sorted_route[p] of y
-// (or token row of shared_y).  Work item = (row tile, 128 hidden columns);
-// wave w owns columns nt*128 + 32w .. +32.  Same staging as the up
-// projection: the wave's 32 W2 rows through a private LDS area, the act
-// planes through a double-buffered shared one.
+// (or token row of shared_y).  Work item = (row tile, 128 * NBW hidden
+// columns); wave w owns columns nt*128*NBW + 32*NBW*w .. + 32*NBW, as NBW
+// MFMA column blocks.  Same staging as the up projection: the wave's W2 rows
+// through a private LDS area, the act planes through a double-buffered
+// shared one.  Wider items (NBW = 2) read each act block once per 256
+// columns and keep twice the weight bytes in flight per workgroup.
 // NKB > 0 instantiates the K loop fully unrolled for Ie = 64 * NKB with a
 // ring of NSET register sets of loads (blocks kb + 1 .. kb + NSET - 1 in
 // flight while kb is multiplied); NKB = 0 is the general loop with one block
 // in flight (NSET = 1).  All run the same MFMA sequence on every element.
 // ---------------------------------------------------------------------------
-template <int NKB, int NSET>
+template <int NKB, int NSET, int NBW>
 __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     const uint16_t* __restrict__ act_hi, const uint16_t* __restrict__ act_lo,
     const uint16_t* __restrict__ sact_hi, const uint16_t* __restrict__ sact_lo,
@@ -233,7 +235,9 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_route,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ meta, float* __restrict__ y,
     float* __restrict__ sy, int64_t T, int H, int E, int K, int I, int Is) {
-  const int ncol_tiles = H / kDownCols;
+  constexpr int COLS = kDownCols * NBW;  // hidden columns of a work item
+  constexpr int WROWS = 32 * NBW;        // W2 rows (hidden columns) of a wave
+  const int ncol_tiles = H / COLS;
   const int item = xcd_item(blockIdx.x, meta[0] * ncol_tiles);
   if (item < 0) return;
   const GroupItem gi = group_item(item, ncol_tiles, tiles, offsets, E, T, kRowsPerTile);
@@ -249,9 +253,15 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   const int64_t p0 = shared ? row0 : static_cast<int64_t>(seg0) + row0;
   float* out = shared ? sy : y;
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][2][kRowsPerTile * 64];  // [buf][hi/lo]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[4][32 * 64];
+  // LDS: act planes [buf][hi/lo][64 rows x 64 k], then the waves' W2 rows;
+  // the epilogue stages the fp32 tile over both
+  constexpr int kAsElems = 2 * 2 * kRowsPerTile * 64;
+  constexpr int kBsElems = 4 * WROWS * 64;
+  static_assert((kAsElems + kBsElems) * 2 >= kRowsPerTile * COLS * 4, "the epilogue tile fits");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kAsElems + kBsElems];
   __shared__ int s_dst[kRowsPerTile];
+  auto As = [&](int buf, int plane) { return smem + (buf * 2 + plane) * kRowsPerTile * 64; };
+  uint16_t* const Bw = smem + kAsElems + (threadIdx.x >> 6) * WROWS * 64;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, half = lane >> 5;
@@ -279,13 +289,15 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 #pragma unroll
   for (int q = 0; q < 2; ++q) aoff[q] = static_cast<int64_t>(min(ar0 + 32 * q, rows - 1)) * Ie;
   const int bc = lane & 7, br8 = lane >> 3;
-  const int n0 = nt * kDownCols + wave * 32;
+  const int n0 = nt * COLS + wave * WROWS;
   const uint16_t* wb = W + static_cast<int64_t>(n0 + br8) * Ie + bc * 8;
 
-  f32x16_t acc[2];
+  f32x16_t acc[2][NBW];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) acc[mb] = zero16();
-  u32x4_t rh[NSET][2], rl[NSET][2], rb[NSET][4];
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = zero16();
+  u32x4_t rh[NSET][2], rl[NSET][2], rb[NSET][4 * NBW];
 
   // activation rows past the tile's end repeat its last row (unused)
   auto issue = [&](int set, int kb) {
@@ -298,29 +310,34 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
       rl[set][q] = ld16(alo + aoff[q] + kp);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rb[set][q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp);
+    for (int q = 0; q < 4 * NBW; ++q) rb[set][q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp);
   };
   auto stash = [&](int set, int buf) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      st16(&As[buf][0][lds_off(ar0 + 32 * q, ac)], rh[set][q]);
-      st16(&As[buf][1][lds_off(ar0 + 32 * q, ac)], rl[set][q]);
+      st16(As(buf, 0) + lds_off(ar0 + 32 * q, ac), rh[set][q]);
+      st16(As(buf, 1) + lds_off(ar0 + 32 * q, ac), rl[set][q]);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[set][q]);
+    for (int q = 0; q < 4 * NBW; ++q) st16(Bw + lds_off(8 * q + br8, bc), rb[set][q]);
   };
   auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = 4 * half + s;
-      const u32x4_t b = ld16(&Bs[wave][lds_off(j, c)]);
+      u32x4_t b[NBW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) b[nb] = ld16(Bw + lds_off(32 * nb + j, c));
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         if (mb < nmb) {
-          const u32x4_t ah = ld16(&As[buf][0][lds_off(mb * 32 + j, c)]);
-          const u32x4_t al = ld16(&As[buf][1][lds_off(mb * 32 + j, c)]);
-          acc[mb] = mfma32x32x16(ah, b, acc[mb]);
-          acc[mb] = mfma32x32x16(al, b, acc[mb]);
+          const u32x4_t ah = ld16(As(buf, 0) + lds_off(mb * 32 + j, c));
+          const u32x4_t al = ld16(As(buf, 1) + lds_off(mb * 32 + j, c));
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) {
+            acc[mb][nb] = mfma32x32x16(ah, b[nb], acc[mb][nb]);
+            acc[mb][nb] = mfma32x32x16(al, b[nb], acc[mb][nb]);
+          }
         }
       }
     }
@@ -352,26 +369,30 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     }
   }
 
-  // Epilogue: the 64 x 128 fp32 tile is staged in LDS (the A area) and each
-  // route row goes out as 16-byte pieces, 512 contiguous bytes per row.
-  __syncthreads();  // every wave is done with the A area
-  static_assert(sizeof(As) >= kRowsPerTile * kDownCols * sizeof(float), "staging fits the A area");
-  float* Cs = reinterpret_cast<float*>(&As[0][0][0]);
+  // Epilogue: the 64 x COLS fp32 tile is staged in LDS and each route row
+  // goes out as 16-byte pieces, COLS * 4 contiguous bytes per row.
+  __syncthreads();  // every wave is done with the operand areas
+  float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (mb < nmb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) Cs[(mb * 32 + acc_row(v, half)) * kDownCols + wave * 32 + j] = acc[mb][v];
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          Cs[(mb * 32 + acc_row(v, half)) * COLS + wave * WROWS + nb * 32 + j] = acc[mb][nb][v];
     }
   }
   __syncthreads();
-  const int piece = tid & 31;  // 32 pieces of 4 floats per row
+  constexpr int kPieces = COLS / 4;           // 16-byte pieces per row
+  constexpr int kRowsPerPass = 256 / kPieces;  // rows stored per pass of the workgroup
+  const int piece = tid % kPieces;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (tid >> 5) + 8 * i;
+  for (int i = 0; i < kRowsPerTile / kRowsPerPass; ++i) {
+    const int r = tid / kPieces + kRowsPerPass * i;
     if (r < rows) {
       const int dst = s_dst[r];
-      if (dst >= 0) st16(out + static_cast<int64_t>(dst) * H + nt * kDownCols + piece * 4, ld16(Cs + r * kDownCols + piece * 4));
+      if (dst >= 0) st16(out + static_cast<int64_t>(dst) * H + nt * COLS + piece * 4, ld16(Cs + r * COLS + piece * 4));
     }
   }
 }
@@ -488,15 +509,19 @@ hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
                            const int32_t* sorted_route, const int32_t* tiles,
                            const int32_t* meta, float* y, float* sy, int64_t T, int H, int E,
                            int K, int I, int Is, int max_tiles, hipStream_t stream) {
-  const int64_t items = static_cast<int64_t>(max_tiles) * (H / kDownCols);
-  const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
-  // the unrolled instantiation covers expert and shared sizes of 512
-  if (I == 512 && (Is == 0 || Is == 512))
-    ffn_down_kernel<8, 2><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
-                                                 sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
-  else
-    ffn_down_kernel<0, 1><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
-                                                 sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
+  // the unrolled instantiation covers expert and shared sizes of 512 (and
+  // takes 256-column items when H allows); the general one 128 columns
+  if (I == 512 && (Is == 0 || Is == 512) && H % (2 * kDownCols) == 0) {
+    const int64_t items = static_cast<int64_t>(max_tiles) * (H / (2 * kDownCols));
+    const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
+    ffn_down_kernel<8, 2, 2><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
+                                                    sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
+  } else {
+    const int64_t items = static_cast<int64_t>(max_tiles) * (H / kDownCols);
+    const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
+    ffn_down_kernel<0, 1, 1><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
+                                                    sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
+  }
   return hipGetLastError();
 }
 
