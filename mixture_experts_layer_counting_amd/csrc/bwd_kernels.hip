@@ -252,9 +252,16 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
   return (r >= 0 && r < a.T * a.K) ? r / a.K : 0;
 }
 
-template <int MODE>
+// NKB > 0 (dgrad modes only) instantiates the K loop fully unrolled for a
+// contraction of NKB blocks with a ring of four register sets, so three K
+// blocks' loads are in flight while one is multiplied; NKB = 0 is the
+// general loop with one block in flight.  Both run the same MFMA sequence on
+// every element.
+template <int MODE, int NKB = 0>
 __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void bwd_gemm_kernel(const BwdArgs a) {
   constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
+  static_assert(NKB == 0 || !WGRAD, "the unrolled loop is for the dgrad modes");
+  constexpr int NSET = NKB > 0 ? 4 : 1;
   constexpr int NPA = (MODE == kDx || MODE == kDw13) ? kGradPlanes : 1;
   constexpr int NPB = MODE == kDw2 ? kGradPlanes : 1;
   constexpr int APLANE = WGRAD ? kRPlane : kKPlane;
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   if (MODE == kDact) kdim = a.H;
   else if (MODE == kDx) kdim = 2 * Ie;
   else kdim = w.rows;
-  const int nkb = (kdim + kBK - 1) / kBK;
+  const int nkb = NKB > 0 ? NKB : (kdim + kBK - 1) / kBK;
   const int rot = WGRAD ? 0 : k_rotation(w.grp, w.nt, nkb);
 
   // ---- load roles.  [row][k] operand: rows lr + 64c, 8 k at lc.
@@ -342,19 +349,21 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
     }
   };
 
-  u32x4_t ra[NPA][2], rb[NPB][2];
-  auto fetch = [&](int kb) {
+  u32x4_t ra_set[NSET][NPA][2], rb_set[NSET][NPB][2];
+  auto fetch_set = [&](int set, int kb) {
     const int k0 = kb * kBK;
     if (!WGRAD) {
 #pragma unroll
       for (int q = 0; q < NPA; ++q)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) ra[q][c] = ld16(a_base[q] + a_off[c] + k0 + lc);
+        for (int c = 0; c < 2; ++c) ra_set[set][q][c] = ld16(a_base[q] + a_off[c] + k0 + lc);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        rb[0][c] = ld16(wbase + static_cast<int64_t>(k0 + kr + 16 * c) * wcols + w.n0 + tc);
+        rb_set[set][0][c] = ld16(wbase + static_cast<int64_t>(k0 + kr + 16 * c) * wcols + w.n0 + tc);
       return;
     }
+    auto& ra = ra_set[set];
+    auto& rb = rb_set[set];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int kk = k0 + kr + 16 * c;
@@ -377,7 +386,9 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
       }
     }
   };
-  auto stash = [&](int stage) {
+  auto stash_set = [&](int set, int stage) {
+    const auto& ra = ra_set[set];
+    const auto& rb = rb_set[set];
     uint16_t* s = smem + stage * STAGE;
 #pragma unroll
     for (int q = 0; q < NPA; ++q)
@@ -398,23 +409,8 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
 
-  if (nkb > 0) {
-    if (WGRAD) wg_tokens(0, tok);
-    fetch(rot);
-    stash(0);
-    if (WGRAD && nkb > 1) wg_tokens(1, tok);
-  }
-  for (int it = 0; it < nkb; ++it) {
-    __syncthreads();
-    const int cur = NSTAGE == 2 ? (it & 1) : 0;
-    const bool more = it + 1 < nkb;
-    if (more) {
-      int kn = rot + it + 1;
-      if (kn >= nkb) kn -= nkb;
-      fetch(kn);
-      if (WGRAD && it + 2 < nkb) wg_tokens(it + 2, tok);
-    }
-    const uint16_t* s = smem + cur * STAGE;
+  auto compute = [&](int stage) {
+    const uint16_t* s = smem + stage * STAGE;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       u32x4_t fa[2][NPA], fb[2][NPB];
@@ -442,9 +438,42 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
           for (int q = 1; q < NPB; ++q) acc[mb][nb] = mfma32x32x16(fa[mb][0], fb[nb][q], acc[mb][nb]);
         }
     }
-    if (more) {
-      if (NSTAGE == 1) __syncthreads();  // every wave is done reading the stage
-      stash(NSTAGE == 2 ? cur ^ 1 : 0);
+  };
+  // K block at position `it` of this item's order (rotation)
+  auto block_at = [&](int it) { return rot + it < nkb ? rot + it : rot + it - nkb; };
+
+  if constexpr (NKB > 0) {
+    // dgrad, unrolled: blocks it + 1 .. it + 3 in flight while it is multiplied
+#pragma unroll
+    for (int q = 0; q < NSET && q < NKB; ++q) fetch_set(q, block_at(q));
+    stash_set(0, 0);
+#pragma unroll
+    for (int it = 0; it < NKB; ++it) {
+      __syncthreads();
+      if (it + NSET < NKB) fetch_set(it % NSET, block_at(it + NSET));
+      compute(it & 1);
+      if (it + 1 < NKB) stash_set((it + 1) % NSET, (it + 1) & 1);
+    }
+  } else {
+    if (nkb > 0) {
+      if (WGRAD) wg_tokens(0, tok);
+      fetch_set(0, block_at(0));
+      stash_set(0, 0);
+      if (WGRAD && nkb > 1) wg_tokens(1, tok);
+    }
+    for (int it = 0; it < nkb; ++it) {
+      __syncthreads();
+      const int cur = NSTAGE == 2 ? (it & 1) : 0;
+      const bool more = it + 1 < nkb;
+      if (more) {
+        fetch_set(0, block_at(it + 1));
+        if (WGRAD && it + 2 < nkb) wg_tokens(it + 2, tok);
+      }
+      compute(cur);
+      if (more) {
+        if (NSTAGE == 1) __syncthreads();  // every wave is done reading the stage
+        stash_set(0, NSTAGE == 2 ? cur ^ 1 : 0);
+      }
     }
   }
 
@@ -806,9 +835,17 @@ hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
   const int Imax = L.I > L.Is ? L.I : L.Is;
   auto rounds = [](int64_t items) { return static_cast<unsigned>(((items + 7) / 8) * 8); };
   const int64_t dgrad_tiles = L.max_tiles_bwd;
-  bwd_gemm_kernel<kDact><<<rounds(dgrad_tiles * (Imax / kBT)), 256, 0, stream>>>(a);
+  // the unrolled dgrad instantiations cover H = 2048 (dact) and expert and
+  // shared sizes of 512 (dx)
+  if (L.H == 2048)
+    bwd_gemm_kernel<kDact, 2048 / kBK><<<rounds(dgrad_tiles * (Imax / kBT)), 256, 0, stream>>>(a);
+  else
+    bwd_gemm_kernel<kDact><<<rounds(dgrad_tiles * (Imax / kBT)), 256, 0, stream>>>(a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  bwd_gemm_kernel<kDx><<<rounds(dgrad_tiles * (L.H / kBT)), 256, 0, stream>>>(a);
+  if (L.I == 512 && (L.Is == 0 || L.Is == 512))
+    bwd_gemm_kernel<kDx, 2 * 512 / kBK><<<rounds(dgrad_tiles * (L.H / kBT)), 256, 0, stream>>>(a);
+  else
+    bwd_gemm_kernel<kDx><<<rounds(dgrad_tiles * (L.H / kBT)), 256, 0, stream>>>(a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
   bwd_gemm_kernel<kDw2><<<rounds(groups * (L.H / kBT) * (Imax / kBT)), 256, 0, stream>>>(a);
