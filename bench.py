@@ -202,6 +202,68 @@ def summarize(cfg, r, steps):
     )
 
 
+def expert_share(m, cfg, w, x, share):
+    """One GPU's share of an expert-parallel layout over `share` GPUs: the
+    dims, weights and permutation of experts [0, E/share) with their routes
+    of this batch (from the full layer's routing on the GPU), in ascending
+    route id per expert -- what that GPU's grouped FFN receives after the
+    exchange.  No shared expert (it is not expert-sharded)."""
+    import torch
+    dev = x.device
+    d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
+    routes = m.alloc_routes(d, dev, logits=False)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, dev)
+    m.check(m.moe_route(d, x, w, routes, ws), "moe_route")
+    m.check(m.moe_permute(d, routes, ws), "moe_permute")
+    torch.cuda.synchronize()
+    el = cfg.experts // share
+    dl = m.Dims(cfg.tokens, cfg.hidden, el, cfg.top_k, cfg.inter, 0)
+    rl = m.alloc_routes(dl, dev, logits=False)
+    rl.expert_offsets.copy_(routes.expert_offsets[:el + 1])
+    n_local = int(routes.expert_offsets[el].item())
+    rl.sorted_route.fill_(-1)
+    rl.sorted_route[:n_local].copy_(routes.sorted_route[:n_local])
+    wl = m.Weights(w_router=w.w_router, w13=w.w13, w2=w.w2, router_bias=w.router_bias)
+    return dl, wl, rl, routes, n_local
+
+
+def run_ep_share(cfg, w, steps, warmup, share):
+    """Grouped FFN (up + down) of one GPU's expert share, HIP-event timed on
+    the kernels' stream."""
+    import torch
+    import mixture_experts_layer_counting_amd as m
+    import workloads as W
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(W.tokens(cfg).view(np.int16)).to(dev)
+    dl, wl, rl, _, n_local = expert_share(m, cfg, w, x, share)
+    saved = m.alloc_saved(dl, dev)
+    ws = m.alloc_workspace(dl, m.MOE_OP_FFN, dev)
+    stream = torch.cuda.current_stream()
+
+    def ffn():
+        m.check(m.moe_grouped_ffn(dl, x, wl, rl, saved, ws, stream), "moe_grouped_ffn")
+
+    for _ in range(warmup):
+        ffn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        ffn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    touched = int((np.diff(rl.expert_offsets.cpu().numpy()) > 0).sum())
+    H, I = cfg.hidden, cfg.inter
+    # touched local experts' weights once, their x rows gathered once per
+    # route, act hi/lo written and read once, fp32 route rows written once
+    byts = touched * 3 * I * H * 2 + n_local * H * 2 + n_local * I * 4 * 2 + n_local * H * 4
+    return {"workload": f"{cfg.name}: experts [0, {dl.experts}) of {cfg.experts} (one GPU of {share}) "
+                        f"with their {n_local} routes, grouped FFN only",
+            "ms": ms, "routes": n_local, "bytes": byts,
+            "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9)}
+
+
 def run_backward(cfg, steps, warmup):
     """Forward (training mode) once, then `steps` timed backward passes of
     the same batch (HIP-event timed on the kernels' stream)."""
@@ -281,6 +343,8 @@ def main():
     ap.add_argument("--secondary", default="moe8k", help="second workload to report, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", default="bwd4k", help="workload of the backward timing, or 'none'")
+    ap.add_argument("--ep-share", type=int, default=8,
+                    help="also time the grouped FFN on one GPU's share of this many expert-parallel GPUs (0: off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -324,6 +388,12 @@ def main():
         secondary[c2.name] = summarize(c2, r2, args.steps)
         log(f"bench: {c2.name} {secondary[c2.name]['ms_per_step']:.3f} ms/step")
 
+    ep_share = None
+    if args.ep_share > 1:
+        log(f"bench: grouped FFN on one of {args.ep_share} expert shares")
+        ep_share = run_ep_share(cfg, w, args.steps, args.warmup, args.ep_share)
+        log(f"bench: expert share {ep_share['ms']:.3f} ms")
+
     backward = None
     if args.backward != "none":
         log(f"bench: backward {args.backward}")
@@ -364,6 +434,7 @@ def main():
         "ffn_down_gbs": main_s["ffn_down_gbs"],
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "ep_share": ep_share,
         "backward": backward,
     }
     print(json.dumps(line), flush=True)
