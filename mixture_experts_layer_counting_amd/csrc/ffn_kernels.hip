@@ -40,15 +40,17 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 
 // ---------------------------------------------------------------------------
 // Up projection + SwiGLU.
-// Work item = (row tile of one group, 128 activation columns).  Group g < E
+// Work item = (row tile of 32 * MBT rows of one group, 128 activation
+// columns).  Group g < E
 // is routed expert g, its rows are the sorted positions offsets[g] + row0 ..;
 // group E is the shared expert, rows are tokens row0 ...
 // Wave w owns activation columns c = nt*128 + 32w .. +32 and computes both
 // gate (W13 row c) and up (W13 row I + c) for every row of the tile, so the
 // SwiGLU is elementwise on the two accumulators.  Its 64 weight rows go
 // through a private LDS area; the gathered activation rows through a
-// double-buffered area shared by the four waves.  64-row tiles keep
-// registers and LDS small enough for two workgroups per CU, which with the
+// double-buffered area shared by the four waves.  64-row tiles (96 rows
+// at large batches) keep registers and LDS small enough for two workgroups
+// per CU, which with the
 // loads of the next K blocks in flight keeps enough bytes moving.
 // Outputs: act as a bf16 hi/lo pair (row = sorted position, or token for the
 // shared expert) and, if requested, the fp32 gate/up values.
@@ -57,39 +59,40 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // flight while kb is multiplied); NKB = 0 is the general loop with one block
 // in flight (NSET = 1).  All run the same MFMA sequence on every element.
 // ---------------------------------------------------------------------------
-template <int NKB, int NSET>
+template <int NKB, int NSET, int MBT>
 __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
     const uint16_t* __restrict__ ws13, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_route, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ meta, uint16_t* __restrict__ act_hi,
+    const int32_t* __restrict__ ntiles, uint16_t* __restrict__ act_hi,
     uint16_t* __restrict__ act_lo, uint16_t* __restrict__ sact_hi,
     uint16_t* __restrict__ sact_lo, float* __restrict__ gu, float* __restrict__ sgu, int64_t T,
     int H, int E, int K, int I, int Is, int ncol_tiles) {
-  const int item = xcd_item(blockIdx.x, meta[0] * ncol_tiles);
+  constexpr int ROWS = 32 * MBT;  // rows of a work item
+  const int item = xcd_item(blockIdx.x, ntiles[0] * ncol_tiles);
   if (item < 0) return;
-  const GroupItem gi = group_item(item, ncol_tiles, tiles, offsets, E, T, kRowsPerTile);
+  const GroupItem gi = group_item(item, ncol_tiles, tiles, offsets, E, T, ROWS);
   const int nt = gi.nt, grp = gi.grp, row0 = gi.row0;
   const bool shared = grp == E;
   const int Ie = shared ? Is : I;
   if (nt * kUpCols >= Ie) return;
   const int seg0 = gi.seg0;
   const int cnt = gi.cnt;
-  const int rows = min(kRowsPerTile, cnt - row0);
+  const int rows = min(ROWS, cnt - row0);
   if (rows <= 0) return;
   const int nmb = (rows + 31) >> 5;
   const uint16_t* W = shared ? ws13 : w13 + static_cast<int64_t>(grp) * 2 * I * H;
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kRowsPerTile * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[4][64 * 64];
-  __shared__ int s_tok[kRowsPerTile];
+  __shared__ int s_tok[ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, half = lane >> 5;
   const int64_t R = T * K;
 
   // rows past the tile's end repeat its last row (loaded, never used)
-  if (tid < kRowsPerTile) {
+  if (tid < ROWS) {
     const int rr = min(tid, rows - 1);
     int64_t tok;
     if (shared) {
@@ -106,9 +109,9 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   const int rot = k_rotation(grp, nt, nkb);
   // A loader: rows ar0 + 32q, chunk ac
   const int ac = tid & 7, ar0 = tid >> 3;
-  const uint16_t* xa[2];
+  const uint16_t* xa[MBT];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) xa[q] = x + static_cast<int64_t>(s_tok[ar0 + 32 * q]) * H + ac * 8;
+  for (int q = 0; q < MBT; ++q) xa[q] = x + static_cast<int64_t>(s_tok[ar0 + 32 * q]) * H + ac * 8;
   // B loader: this wave's gate rows (Bs rows 0..31) and up rows (32..63),
   // eight rows x 128 bytes per instruction
   const int bc = lane & 7, br8 = lane >> 3;
@@ -116,20 +119,20 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   const uint16_t* wgp = W + static_cast<int64_t>(nt * kUpCols + wave * 32 + br8) * H + bc * 8;
   const uint16_t* wup = wgp + static_cast<int64_t>(Ie) * H;
 
-  f32x16_t accg[2], accu[2];
+  f32x16_t accg[MBT], accu[MBT];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MBT; ++mb) {
     accg[mb] = zero16();
     accu[mb] = zero16();
   }
-  u32x4_t ra[NSET][2], rb[NSET][8];
+  u32x4_t ra[NSET][MBT], rb[NSET][8];
 
   auto issue = [&](int set, int kb) {
     int kk = kb + rot;
     if (kk >= nkb) kk -= nkb;
     const int kp = kk << 6;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) ra[set][q] = ld16(xa[q] + kp);
+    for (int q = 0; q < MBT; ++q) ra[set][q] = ld16(xa[q] + kp);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       rb[set][q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp);
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   };
   auto stash = [&](int set, int buf) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[set][q]);
+    for (int q = 0; q < MBT; ++q) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[set][q]);
 #pragma unroll
     for (int q = 0; q < 8; ++q) st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[set][q]);
   };
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
       const u32x4_t bg = ld16(&Bs[wave][lds_off(j, c)]);
       const u32x4_t bu = ld16(&Bs[wave][lds_off(32 + j, c)]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MBT; ++mb) {
         if (mb < nmb) {
           const u32x4_t a = ld16(&As[buf][lds_off(mb * 32 + j, c)]);
           accg[mb] = mfma32x32x16(a, bg, accg[mb]);
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   float* ogu = shared ? sgu : gu;
   const int64_t p0 = shared ? row0 : static_cast<int64_t>(seg0) + row0;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MBT; ++mb) {
     if (mb < nmb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -485,21 +488,25 @@ namespace moe {
 
 hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t* ws13,
                          const int32_t* offsets, const int32_t* sorted_route, const int32_t* tiles,
-                         const int32_t* meta, uint16_t* act_hi, uint16_t* act_lo,
+                         const int32_t* ntiles, int up_rows, uint16_t* act_hi, uint16_t* act_lo,
                          uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu, int64_t T,
                          int H, int E, int K, int I, int Is, int max_tiles, hipStream_t stream) {
   const int ncol = (I > Is ? I : Is) / kUpCols;
   const int64_t items = static_cast<int64_t>(max_tiles) * ncol;
   const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
-  // the unrolled instantiation covers hidden size 2048
-  if (H == 2048)
-    ffn_up_kernel<32, 2><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta,
-                                                act_hi, act_lo, sact_hi, sact_lo, gu, sgu, T, H, E,
-                                                K, I, Is, ncol);
+  // the unrolled instantiations cover hidden size 2048 (64- and 96-row items)
+  if (H == 2048 && up_rows == kUpTallRows)
+    ffn_up_kernel<32, 2, kUpTallRows / 32><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles,
+                                                                  ntiles, act_hi, act_lo, sact_hi, sact_lo,
+                                                                  gu, sgu, T, H, E, K, I, Is, ncol);
+  else if (H == 2048)
+    ffn_up_kernel<32, 2, kRowsPerTile / 32><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles,
+                                                                   ntiles, act_hi, act_lo, sact_hi, sact_lo,
+                                                                   gu, sgu, T, H, E, K, I, Is, ncol);
   else
-    ffn_up_kernel<0, 1><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles, meta,
-                                               act_hi, act_lo, sact_hi, sact_lo, gu, sgu, T, H, E,
-                                               K, I, Is, ncol);
+    ffn_up_kernel<0, 1, kRowsPerTile / 32><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles,
+                                                                  ntiles, act_hi, act_lo, sact_hi, sact_lo,
+                                                                  gu, sgu, T, H, E, K, I, Is, ncol);
   return hipGetLastError();
 }
 

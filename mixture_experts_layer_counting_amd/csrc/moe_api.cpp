@@ -28,6 +28,7 @@ struct Layout {
   size_t hist = 0;        // [NB][E+1] i32
   size_t block_base = 0;  // [NB][E] i32
   size_t tiles = 0;       // [2*max_tiles] i32
+  size_t tiles_up = 0;    // [2*max_tiles_up] i32: the up projection's list when its rows differ
   size_t meta = 0;        // [64] i32
   size_t act_hi = 0, act_lo = 0;    // [R][I] bf16
   size_t sact_hi = 0, sact_lo = 0;  // [T][Is] bf16
@@ -45,6 +46,8 @@ struct Layout {
   size_t bwd_end = 0;
   int nblocks = 0;
   int max_tiles = 0;
+  int up_rows = 0;       // rows per up-projection item (moe::up_rows_per_tile)
+  int max_tiles_up = 0;
   int max_tiles_bwd = 0;
 };
 
@@ -54,6 +57,8 @@ Layout make_layout(const moe_dims& d) {
   const int E = d.experts, I = d.inter, Is = d.shared_inter;
   L.nblocks = static_cast<int>((T + moe::kSortBlock - 1) / moe::kSortBlock);
   L.max_tiles = static_cast<int>(moe::max_row_tiles(T, d.top_k, E, Is > 0));
+  L.up_rows = moe::up_rows_per_tile(T, d.hidden);
+  L.max_tiles_up = static_cast<int>(moe::max_row_tiles(T, d.top_k, E, Is > 0, L.up_rows));
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -66,6 +71,7 @@ Layout make_layout(const moe_dims& d) {
   L.hist = take(static_cast<size_t>(L.nblocks) * (E + 1) * 4);
   L.block_base = take(static_cast<size_t>(L.nblocks) * E * 4);
   L.tiles = take(static_cast<size_t>(L.max_tiles) * 2 * 4);
+  L.tiles_up = take(L.up_rows != moe::kRowsPerTile ? static_cast<size_t>(L.max_tiles_up) * 2 * 4 : 0);
   L.meta = take(64 * 4);
   L.act_hi = take(static_cast<size_t>(R) * I * 2);
   L.act_lo = take(static_cast<size_t>(R) * I * 2);
@@ -254,20 +260,26 @@ int run_route(const moe_dims& d, const uint16_t* x, const moe_weights* w, moe_ro
   return MOE_OK;
 }
 
+// The up projection's own work list (null when it uses the common one).
+int32_t* tiles_up_of(void* ws, const Layout& L) {
+  return L.up_rows != moe::kRowsPerTile ? at<int32_t>(ws, L.tiles_up) : nullptr;
+}
+
 int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hipStream_t s) {
   if (moe::sort_small_fits(d.tokens, d.experts)) {
     MOE_LAUNCH(moe::launch_route_sort_small(r->topk_idx, r->expert_offsets, r->route_pos,
                                             r->sorted_route, at<int32_t>(ws, L.tiles),
-                                            at<int32_t>(ws, L.meta), at<int>(ws, L.err), d.tokens,
-                                            d.experts, d.top_k, d.shared_inter > 0, s));
+                                            tiles_up_of(ws, L), L.up_rows, at<int32_t>(ws, L.meta),
+                                            at<int>(ws, L.err), d.tokens, d.experts, d.top_k,
+                                            d.shared_inter > 0, s));
     return MOE_OK;
   }
   MOE_LAUNCH(moe::launch_route_hist(r->topk_idx, at<int32_t>(ws, L.hist), r->route_pos, d.tokens,
                                     d.experts, d.top_k, s));
   MOE_LAUNCH(moe::launch_route_scan(at<int32_t>(ws, L.hist), at<int32_t>(ws, L.block_base),
-                                    r->expert_offsets, at<int32_t>(ws, L.tiles),
-                                    at<int32_t>(ws, L.meta), L.nblocks, d.experts, d.tokens,
-                                    d.shared_inter > 0, at<int>(ws, L.err), s));
+                                    r->expert_offsets, at<int32_t>(ws, L.tiles), tiles_up_of(ws, L),
+                                    L.up_rows, at<int32_t>(ws, L.meta), L.nblocks, d.experts,
+                                    d.tokens, d.shared_inter > 0, at<int>(ws, L.err), s));
   MOE_LAUNCH(moe::launch_route_scatter(r->topk_idx, at<int32_t>(ws, L.block_base),
                                        r->expert_offsets, r->route_pos, r->sorted_route, d.tokens,
                                        d.experts, d.top_k, s));
@@ -280,17 +292,20 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
             moe_saved* sv, void* ws, const Layout& L, bool whole_forward, hipStream_t s) {
   const int has_shared = d.shared_inter > 0;
   if (!whole_forward)
-    MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles),
-                                     at<int32_t>(ws, L.meta), d.experts, d.tokens, has_shared,
-                                     moe::kRowsPerTile, s));
+    MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles), tiles_up_of(ws, L),
+                                     L.up_rows, at<int32_t>(ws, L.meta), d.experts, d.tokens,
+                                     has_shared, moe::kRowsPerTile, s));
   if (has_shared && !whole_forward)
     MOE_LAUNCH(moe::launch_shared_gate(x, w->w_sgate, sv->shared_gate, d.tokens, d.hidden, s));
+  const bool own_up = tiles_up_of(ws, L) != nullptr;
   MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, r->expert_offsets, r->sorted_route,
-                                at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta),
+                                own_up ? tiles_up_of(ws, L) : at<int32_t>(ws, L.tiles),
+                                at<int32_t>(ws, L.meta) + (own_up ? 2 : 0), L.up_rows,
                                 at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
                                 at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), sv->gu,
                                 has_shared ? sv->shared_gu : nullptr, d.tokens, d.hidden,
-                                d.experts, d.top_k, d.inter, d.shared_inter, L.max_tiles, s));
+                                d.experts, d.top_k, d.inter, d.shared_inter,
+                                own_up ? L.max_tiles_up : L.max_tiles, s));
   MOE_LAUNCH(moe::launch_ffn_down(at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
                                   at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), w->w2,
                                   w->ws2, r->expert_offsets, r->sorted_route,
@@ -557,7 +572,7 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
   const Layout L = make_layout(d);
   const bool sh = Is > 0;
   hipStream_t s = stream;
-  MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles_bwd),
+  MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles_bwd), nullptr, 0,
                                    at<int32_t>(ws, L.meta_bwd), d.experts, d.tokens, sh,
                                    moe::kBwdRowsPerTile, s));
   MOE_LAUNCH(moe::launch_bwd_gate(d_out, saved->y, sh ? saved->shared_y : nullptr, routes->topk_gate,

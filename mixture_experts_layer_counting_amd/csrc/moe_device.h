@@ -13,6 +13,12 @@ namespace moe {
 
 // Routed rows per grouped-GEMM work item (two 32-row MFMA blocks).
 constexpr int kRowsPerTile = 64;
+// Rows per up-projection work item from this many tokens on (hidden size
+// 2048): three 32-row MFMA blocks, so an expert's ~160 routes at 8K tokens
+// stream its gate/up weights twice instead of three times.  The down
+// projection keeps kRowsPerTile.
+constexpr int kUpTallRows = 96;
+constexpr int64_t kUpTallMin = 4096;
 // Activation columns per up-projection work item (four waves x 32).
 constexpr int kUpCols = 128;
 // Hidden columns per down-projection work item (four waves x 32).

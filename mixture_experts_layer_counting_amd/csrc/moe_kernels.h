@@ -27,25 +27,37 @@ hipError_t launch_topk_gate(const float* src, int nchunk, const float* bias, flo
                             const uint16_t* w_sgate, float* sg, int64_t T, int H, int E, int K,
                             hipStream_t stream);
 bool sort_small_fits(int64_t T, int E);
+// Work lists: the permutation kernels (and launch_ffn_tiles) also write the
+// up projection's list of up_rows-row tiles to tiles_up when it is not null
+// (up_rows_per_tile(...) != kRowsPerTile); its count goes to meta[2].
 hipError_t launch_route_sort_small(const int32_t* topk_idx, int32_t* offsets, int32_t* route_pos,
-                                   int32_t* sorted_route, int32_t* tiles, int32_t* meta,
-                                   int* err_word, int64_t T, int E, int K, int has_shared,
-                                   hipStream_t stream);
+                                   int32_t* sorted_route, int32_t* tiles, int32_t* tiles_up,
+                                   int up_rows, int32_t* meta, int* err_word, int64_t T, int E,
+                                   int K, int has_shared, hipStream_t stream);
 hipError_t launch_route_hist(const int32_t* topk_idx, int32_t* hist, int32_t* route_rank,
                              int64_t T, int E, int K, hipStream_t stream);
 hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* offsets,
-                             int32_t* tiles, int32_t* meta, int nblocks, int E, int64_t T,
-                             int has_shared, int* err_word, hipStream_t stream);
-hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* meta, int E, int64_t T,
-                            int has_shared, int rows_per_tile, hipStream_t stream);
+                             int32_t* tiles, int32_t* tiles_up, int up_rows, int32_t* meta,
+                             int nblocks, int E, int64_t T, int has_shared, int* err_word,
+                             hipStream_t stream);
+hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* tiles_up, int up_rows,
+                            int32_t* meta, int E, int64_t T, int has_shared, int rows_per_tile,
+                            hipStream_t stream);
 hipError_t launch_route_scatter(const int32_t* topk_idx, const int32_t* block_base,
                                 const int32_t* offsets, int32_t* route_pos, int32_t* sorted_route,
                                 int64_t T, int E, int K, hipStream_t stream);
 hipError_t launch_shared_gate(const uint16_t* x, const uint16_t* w_sgate, float* sg, int64_t T,
                               int H, hipStream_t stream);
+// Rows per up-projection work item at this batch: kUpTallRows from
+// kUpTallMin tokens at hidden size 2048, else kRowsPerTile.  Only the work
+// split changes; every element's arithmetic is the same.
+inline int up_rows_per_tile(int64_t T, int H) {
+  return (T >= kUpTallMin && H == 2048) ? kUpTallRows : kRowsPerTile;
+}
+// tiles / ntiles: the up_rows-row work list and the int holding its length.
 hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t* ws13,
                          const int32_t* offsets, const int32_t* sorted_route, const int32_t* tiles,
-                         const int32_t* meta, uint16_t* act_hi, uint16_t* act_lo,
+                         const int32_t* ntiles, int up_rows, uint16_t* act_hi, uint16_t* act_lo,
                          uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu, int64_t T,
                          int H, int E, int K, int I, int Is, int max_tiles, hipStream_t stream);
 hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,

@@ -545,9 +545,9 @@ __device__ __forceinline__ int block_scan_incl(int v, int* buf) {
 // e < E holds expert e's count).  Expert e's rows are split into row tiles of
 // rows_per_tile, in expert order, followed by the shared expert's T rows as
 // group E when has_shared.  tiles[2j] = group, tiles[2j+1] = first row;
-// meta[0] = number of tiles.
+// *ntiles = number of tiles.
 __device__ void emit_tiles(int count, int E, int64_t T, int has_shared, int32_t* tiles,
-                           int32_t* meta, int* buf, int rows_per_tile) {
+                           int32_t* ntiles, int* buf, int rows_per_tile) {
   const int e = threadIdx.x;
   const int ntile = (count + rows_per_tile - 1) / rows_per_tile;
   const int tincl = block_scan_incl(ntile, buf);
@@ -565,7 +565,15 @@ __device__ void emit_tiles(int count, int E, int64_t T, int has_shared, int32_t*
     tiles[2 * (routed_tiles + c)] = E;
     tiles[2 * (routed_tiles + c) + 1] = c * rows_per_tile;
   }
-  if (e == 0) meta[0] = routed_tiles + shared_tiles;
+  if (e == 0) *ntiles = routed_tiles + shared_tiles;
+}
+
+// The forward's work lists: kRowsPerTile-row tiles (meta[0] of them) and,
+// when tiles_up is given, the up projection's up_rows-row tiles (meta[2]).
+__device__ void emit_work_lists(int count, int E, int64_t T, int has_shared, int32_t* tiles,
+                                int32_t* tiles_up, int up_rows, int32_t* meta, int* buf) {
+  emit_tiles(count, E, T, has_shared, tiles, &meta[0], buf, kRowsPerTile);
+  if (tiles_up) emit_tiles(count, E, T, has_shared, tiles_up, &meta[2], buf, up_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -578,6 +586,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ block_base,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ tiles_up, int up_rows,
                                                           int32_t* __restrict__ meta, int nblocks,
                                                           int E, int64_t T, int has_shared,
                                                           int* __restrict__ err_word) {
@@ -610,7 +619,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   if (e < E) offsets[e] = incl - run;
   if (e == E - 1) offsets[E] = incl;
   if (errbits) atomicOr(&errs, errbits);
-  emit_tiles(run, E, T, has_shared, tiles, meta, buf, kRowsPerTile);
+  emit_work_lists(run, E, T, has_shared, tiles, tiles_up, up_rows, meta, buf);
   __syncthreads();
   if (e == 0) {
     meta[1] = errs;
@@ -619,9 +628,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 }
 
 // Work list alone, from caller-supplied expert offsets (grouped FFN run on
-// its own, or the backward's list).
+// its own, with the up projection's list when tiles_up is given, or the
+// backward's list).
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ tiles_up, int up_rows,
                                                          int32_t* __restrict__ meta, int E,
                                                          int64_t T, int has_shared,
                                                          int rows_per_tile) {
@@ -632,7 +643,8 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
     count = offsets[e + 1] - offsets[e];
     if (count < 0) count = 0;
   }
-  emit_tiles(count, E, T, has_shared, tiles, meta, buf, rows_per_tile);
+  emit_tiles(count, E, T, has_shared, tiles, &meta[0], buf, rows_per_tile);
+  if (tiles_up) emit_tiles(count, E, T, has_shared, tiles_up, &meta[2], buf, up_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -678,8 +690,9 @@ template <int KT>
 __global__ __launch_bounds__(1024) void route_sort_small_kernel(
     const int32_t* __restrict__ topk_idx, int32_t* __restrict__ offsets,
     int32_t* __restrict__ route_pos, int32_t* __restrict__ sorted_route,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ meta, int* __restrict__ err_word,
-    int64_t T, int E, int K, int has_shared) {
+    int32_t* __restrict__ tiles, int32_t* __restrict__ tiles_up, int up_rows,
+    int32_t* __restrict__ meta, int* __restrict__ err_word, int64_t T, int E, int K,
+    int has_shared) {
   // mask[w * E + e]; the extra last word absorbs invalid routes' updates
   __shared__ uint32_t mask[kSortSmallWords + 1];
   __shared__ uint16_t below[kSortSmallWords];  // tokens of e in the words before w
@@ -743,7 +756,7 @@ __global__ __launch_bounds__(1024) void route_sort_small_kernel(
     offsets[E] = incl;
     total = incl;
   }
-  emit_tiles(count, E, T, has_shared, tiles, meta, buf, kRowsPerTile);
+  emit_work_lists(count, E, T, has_shared, tiles, tiles_up, up_rows, meta, buf);
   __syncthreads();
 
   // positions of token t's routes (-1 for an invalid id)
@@ -866,15 +879,17 @@ bool sort_small_fits(int64_t T, int E) {
 }
 
 hipError_t launch_route_sort_small(const int32_t* topk_idx, int32_t* offsets, int32_t* route_pos,
-                                   int32_t* sorted_route, int32_t* tiles, int32_t* meta,
-                                   int* err_word, int64_t T, int E, int K, int has_shared,
-                                   hipStream_t stream) {
+                                   int32_t* sorted_route, int32_t* tiles, int32_t* tiles_up,
+                                   int up_rows, int32_t* meta, int* err_word, int64_t T, int E,
+                                   int K, int has_shared, hipStream_t stream) {
   if (K <= 10)
     route_sort_small_kernel<10><<<1, 1024, 0, stream>>>(topk_idx, offsets, route_pos, sorted_route,
-                                                        tiles, meta, err_word, T, E, K, has_shared);
+                                                        tiles, tiles_up, up_rows, meta, err_word, T,
+                                                        E, K, has_shared);
   else
     route_sort_small_kernel<16><<<1, 1024, 0, stream>>>(topk_idx, offsets, route_pos, sorted_route,
-                                                        tiles, meta, err_word, T, E, K, has_shared);
+                                                        tiles, tiles_up, up_rows, meta, err_word, T,
+                                                        E, K, has_shared);
   return hipGetLastError();
 }
 
@@ -886,16 +901,19 @@ hipError_t launch_route_hist(const int32_t* topk_idx, int32_t* hist, int32_t* ro
 }
 
 hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* offsets,
-                             int32_t* tiles, int32_t* meta, int nblocks, int E, int64_t T,
-                             int has_shared, int* err_word, hipStream_t stream) {
-  route_scan_kernel<<<1, 1024, 0, stream>>>(hist, block_base, offsets, tiles, meta, nblocks, E, T,
-                                            has_shared, err_word);
+                             int32_t* tiles, int32_t* tiles_up, int up_rows, int32_t* meta,
+                             int nblocks, int E, int64_t T, int has_shared, int* err_word,
+                             hipStream_t stream) {
+  route_scan_kernel<<<1, 1024, 0, stream>>>(hist, block_base, offsets, tiles, tiles_up, up_rows, meta,
+                                            nblocks, E, T, has_shared, err_word);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* meta, int E, int64_t T,
-                            int has_shared, int rows_per_tile, hipStream_t stream) {
-  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, meta, E, T, has_shared, rows_per_tile);
+hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* tiles_up, int up_rows,
+                            int32_t* meta, int E, int64_t T, int has_shared, int rows_per_tile,
+                            hipStream_t stream) {
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, tiles_up, up_rows, meta, E, T, has_shared,
+                                           rows_per_tile);
   return hipGetLastError();
 }
 
