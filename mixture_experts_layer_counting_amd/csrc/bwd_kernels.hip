@@ -104,8 +104,9 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
 // Operands are staged in LDS, two stages: the next K block's global loads are
 // issued before the current block's MFMAs and stored to the other stage after
 // them, so one barrier per block separates the stages.  Two LDS layouts:
-//   * [row][k] (80-byte rows) for sources stored k-contiguous (the routed or
-//     token rows of a dgrad); fragments are 16-byte LDS loads;
+//   * [row][k] (64-byte rows, XOR-swizzled 16-byte pieces: rk_off) for
+//     sources stored k-contiguous (the routed or token rows of a dgrad);
+//     fragments are 16-byte LDS loads;
 //   * [k][col] (320-byte rows) for sources whose rows are indexed by k (the
 //     expert weights read along their output dimension, and both operands
 //     of a weight gradient, whose contraction runs over the routes of an
@@ -143,9 +144,12 @@ enum BwdMode { kDact = 0, kDx = 1, kDw2 = 2, kDw13 = 3 };
 constexpr int kBT = kBwdRowsPerTile;  // edge of every output tile (128)
 constexpr int kBwdTokLds = 256;       // weight-gradient segments up to this length keep their tokens in LDS
 constexpr int kBK = 32;
-constexpr int kKStride = 40;   // [row][k] layout: 32 k + 8 padding (bf16)
+// [row][k] layout: 64-byte rows (32 k), 16-byte piece c of a row stored at
+// c ^ ((row >> 2) & 3), which keeps both the loaders' stores (4 rows x 4
+// pieces per 16 lanes) and the 32-row fragment reads free of bank conflicts.
+__device__ __forceinline__ int rk_off(int row, int c) { return row * kBK + ((c ^ ((row >> 2) & 3)) << 3); }
 constexpr int kRStride = 160;  // [k][col] layout: 128 columns + 32 padding
-constexpr int kKPlane = kBT * kKStride;
+constexpr int kKPlane = kBT * kBK;
 constexpr int kRPlane = kBK * kRStride;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
     for (int q = 0; q < NPA; ++q)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        if (!WGRAD) st16(s + q * APLANE + (lr + 64 * c) * kKStride + lc, ra[q][c]);
+        if (!WGRAD) st16(s + q * APLANE + rk_off(lr + 64 * c, lc >> 3), ra[q][c]);
         else st16(s + q * APLANE + (kr + 16 * c) * kRStride + tc, ra[q][c]);
       }
 #pragma unroll
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
 #pragma unroll
         for (int q = 0; q < NPA; ++q) {
           if (!WGRAD)
-            fa[mb][q] = ld16(s + q * APLANE + (wm * 64 + mb * 32 + i) * kKStride + 16 * st + 8 * half);
+            fa[mb][q] = ld16(s + q * APLANE + rk_off(wm * 64 + mb * 32 + i, 2 * st + half));
           else
             fa[mb][q] = frag_tr(s + q * APLANE, 16 * st, wm * 64 + mb * 32, lane);
         }
