@@ -43,7 +43,6 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* d = dout + t * H;
-  const int nsum = K + (sy ? 1 : 0);
   const float* rowp[KT + 1];
 #pragma unroll
   for (int k = 0; k < KT; ++k) rowp[k] = y + (t * K + min(k, K - 1)) * H;
@@ -92,7 +91,6 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
       dz[t] = static_cast<float>(dg[KT] * s * (1.0 - s));
     }
   }
-  (void)nsum;
 }
 
 // ---------------------------------------------------------------------------
