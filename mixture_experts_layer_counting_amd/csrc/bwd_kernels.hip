@@ -131,11 +131,10 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
 //          Epilogue: dW2_g[h][i].
 //   kDw13: m = j < 2Ie, n = h < H, k = p.  A = dGU planes [p][j] ([k][col]);
 //          B = x[t(p)][h] ([k][col], gathered rows).  Epilogue: dW13_g[j][h].
-// The K order of every output element is fixed: K blocks in ascending order
-// (for the two dgrad modes starting at a rotation fixed by the group and the
-// column tile, as in the forward), in each block K step 0 then 1, and in
-// each step the planes hi, lo.  A dgrad row's result therefore depends
-// only on its own row, its expert and its column tile, never on the batch.
+// The K order of every output element is fixed: K blocks in ascending order,
+// in each block K step 0 then 1, and in each step the planes hi, lo.  A
+// dgrad row's result therefore depends only on its own row and its expert,
+// never on the batch.
 // ---------------------------------------------------------------------------
 enum BwdMode { kDact = 0, kDx = 1, kDw2 = 2, kDw13 = 3 };
 
@@ -289,7 +288,6 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   else if (MODE == kDx) kdim = 2 * Ie;
   else kdim = w.rows;
   const int nkb = NKB > 0 ? NKB : (kdim + kBK - 1) / kBK;
-  const int rot = WGRAD ? 0 : k_rotation(w.grp, w.nt, nkb);
 
   // ---- load roles.  [row][k] operand: rows lr + 64c, 8 k at lc.
   // [k][col] operands: k rows kr + 16c, 8 columns at tc.
@@ -441,25 +439,23 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
         }
     }
   };
-  // K block at position `it` of this item's order (rotation)
-  auto block_at = [&](int it) { return rot + it < nkb ? rot + it : rot + it - nkb; };
 
   if constexpr (NKB > 0) {
     // dgrad, unrolled: blocks it + 1 .. it + 3 in flight while it is multiplied
 #pragma unroll
-    for (int q = 0; q < NSET && q < NKB; ++q) fetch_set(q, block_at(q));
+    for (int q = 0; q < NSET && q < NKB; ++q) fetch_set(q, q);
     stash_set(0, 0);
 #pragma unroll
     for (int it = 0; it < NKB; ++it) {
       __syncthreads();
-      if (it + NSET < NKB) fetch_set(it % NSET, block_at(it + NSET));
+      if (it + NSET < NKB) fetch_set(it % NSET, it + NSET);
       compute(it & 1);
       if (it + 1 < NKB) stash_set((it + 1) % NSET, (it + 1) & 1);
     }
   } else {
     if (nkb > 0) {
       if (WGRAD) wg_tokens(0, tok);
-      fetch_set(0, block_at(0));
+      fetch_set(0, 0);
       stash_set(0, 0);
       if (WGRAD && nkb > 1) wg_tokens(1, tok);
     }
@@ -468,7 +464,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
       const int cur = NSTAGE == 2 ? (it & 1) : 0;
       const bool more = it + 1 < nkb;
       if (more) {
-        fetch_set(0, block_at(it + 1));
+        fetch_set(0, it + 1);
         if (WGRAD && it + 2 < nkb) wg_tokens(it + 2, tok);
       }
       compute(cur);

@@ -5,8 +5,8 @@
 // projections with ONE fixed tile configuration, no gate multiply and no sum
 // inside, exactly one writer per (token, route) row.  Here the fixed part is
 // the per-element arithmetic: the 32x32x16 bf16 MFMA, the K order (64-wide
-// blocks in an order fixed by (expert, column tile), inside a block the
-// lane-half/K-step order below) and fp32 accumulation from zero.  How rows are grouped into tiles
+// blocks in ascending order, inside a block the lane-half/K-step order
+// below) and fp32 accumulation from zero.  How rows are grouped into tiles
 // (which depends on the batch) never changes a row's arithmetic, because an
 // MFMA output row depends only on its own A row.
 //
@@ -21,12 +21,13 @@ namespace moe {
 //
 // Every operand row segment of one 64-wide K block is 128 contiguous bytes.
 // Loads are issued so that each wave instruction reads 8 rows x 128 bytes
-// (lane l: row l/8, 16-byte chunk l%8) -- whole cache lines of a few rows --
-// and the K blocks of a work item are visited starting at a rotation fixed
-// by (group, column tile), so concurrently streamed rows sit at different
-// offsets inside their rows.  Measured on MI355X, that pattern streams HBM at
-// ~6 TB/s, where MFMA-fragment-shaped loads (32 rows x 32 bytes per
-// instruction, all items starting at K = 0) stay at ~4.6 TB/s.
+// (lane l: row l/8, 16-byte chunk l%8) -- whole cache lines of a few rows.
+// Measured on MI355X, MFMA-fragment-shaped loads (32 rows x 32 bytes per
+// instruction) stay at ~4.6 TB/s where this pattern streams ~5.1 TB/s.
+// Every work item walks its K blocks in ascending order: a synthetic
+// weight-only stream is faster when concurrent items start at different K
+// offsets, but in these kernels starting together keeps the gathered
+// activation blocks of concurrent items in L2, which measured faster.
 //
 // In LDS a row of a K block takes 64 bf16 (128 bytes); its 16-byte chunk c
 // is stored at position c ^ ((row >> 1) & 7), which makes both the 8x128-byte
@@ -106,7 +107,6 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   __syncthreads();
 
   const int nkb = NKB > 0 ? NKB : H >> 6;
-  const int rot = k_rotation(grp, nt, nkb);
   // A loader: rows ar0 + 32q, chunk ac
   const int ac = tid & 7, ar0 = tid >> 3;
   const uint16_t* xa[MBT];
@@ -128,9 +128,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   u32x4_t ra[NSET][MBT], rb[NSET][8];
 
   auto issue = [&](int set, int kb) {
-    int kk = kb + rot;
-    if (kk >= nkb) kk -= nkb;
-    const int kp = kk << 6;
+    const int kp = kb << 6;
 #pragma unroll
     for (int q = 0; q < MBT; ++q) ra[set][q] = ld16(xa[q] + kp);
 #pragma unroll
@@ -284,7 +282,6 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   }
 
   const int nkb = NKB > 0 ? NKB : Ie >> 6;
-  const int rot = k_rotation(grp, nt, nkb);
   const int ac = tid & 7, ar0 = tid >> 3;
   const uint16_t* ahi = (shared ? sact_hi : act_hi) + p0 * Ie + ac * 8;
   const uint16_t* alo = (shared ? sact_lo : act_lo) + p0 * Ie + ac * 8;
@@ -304,9 +301,7 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 
   // activation rows past the tile's end repeat its last row (unused)
   auto issue = [&](int set, int kb) {
-    int kk = kb + rot;
-    if (kk >= nkb) kk -= nkb;
-    const int kp = kk << 6;
+    const int kp = kb << 6;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       rh[set][q] = ld16(ahi + aoff[q] + kp);

@@ -88,13 +88,6 @@ __device__ __forceinline__ void split3(float a, uint16_t (&p)[3]) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
-// K rotation of a grouped-GEMM work item that streams an expert's weights:
-// consecutive work items start their K loop at different blocks, which
-// spreads concurrent weight reads over HBM channels.  It is fixed per
-// (group, column tile), so the per-element K order of a row never depends on
-// the batch.
-__device__ __forceinline__ int k_rotation(int grp, int nt, int nkb) { return (grp * 7 + nt * 3) % nkb; }
-
 // XCD-aware mapping of a 1-D grid onto `items` work items.  The hardware
 // deals workgroups round-robin over the 8 XCDs (workgroup g runs on XCD g%8);
 // this gives each XCD one contiguous range of items, so items that share

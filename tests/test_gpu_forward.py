@@ -154,32 +154,35 @@ def test_full_size_forward_sampled(name):
     check_forward(cfg, layer, x, g, tokens=tok)
 
 
-@pytest.mark.parametrize("name", ["tiny", "moe1k"])
-def test_expert_share_matches_full_layer(name):
-    """One GPU's share of an 8-way expert-parallel layout -- experts [0, E/8)
-    with their routes of the batch, in ascending route id, no shared expert --
-    through moe_grouped_ffn gives route rows bit-identical to the full
-    layer's (a route row's arithmetic depends on its token, its expert and
-    the column tile only), and within tolerance of the oracle."""
+@pytest.mark.parametrize("name,shard", [("tiny", 0), ("tiny", 5), ("moe1k", 0), ("moe1k", 3)])
+def test_expert_share_matches_full_layer(name, shard):
+    """One GPU's share of an 8-way expert-parallel layout -- experts
+    [shard*E/8, (shard+1)*E/8) with their routes of the batch, in ascending
+    route id, no shared expert -- through moe_grouped_ffn gives route rows
+    bit-identical to the full layer's (a route row's arithmetic depends on
+    its token and its expert's weights only), and within tolerance of the
+    oracle."""
     cfg, layer, x = load_cfg(name)
     w = dev_weights(layer)
     xd = dev_bits(x)
     g = gpu_forward(cfg, w, xd).host()
     el = cfg.experts // 8
-    n_local = int(g["offsets"][el])
-    say(f"case: {name}, experts [0, {el}) with {n_local} routes through moe_grouped_ffn")
+    e0 = shard * el
+    p0, p1 = int(g["offsets"][e0]), int(g["offsets"][e0 + el])
+    n_local = p1 - p0
+    say(f"case: {name}, experts [{e0}, {e0 + el}) with {n_local} routes through moe_grouped_ffn")
     dl = m.Dims(cfg.tokens, cfg.hidden, el, cfg.top_k, cfg.inter, 0)
     rl = m.alloc_routes(dl, DEV, logits=False)
-    rl.expert_offsets.copy_(torch.from_numpy(np.ascontiguousarray(g["offsets"][:el + 1])))
+    rl.expert_offsets.copy_(torch.from_numpy(np.ascontiguousarray(g["offsets"][e0:e0 + el + 1] - p0)))
     srt = np.full(cfg.tokens * cfg.top_k, -1, np.int32)
-    srt[:n_local] = g["sorted_route"][:n_local]
+    srt[:n_local] = g["sorted_route"][p0:p1]
     rl.sorted_route.copy_(torch.from_numpy(srt))
-    wl = m.Weights(w_router=w.w_router, w13=w.w13, w2=w.w2, router_bias=w.router_bias)
+    wl = m.Weights(w_router=w.w_router, w13=w.w13[e0:], w2=w.w2[e0:], router_bias=w.router_bias)
     saved = m.alloc_saved(dl, DEV)
     ws = m.alloc_workspace(dl, m.MOE_OP_FFN, DEV)
     m.check(m.moe_grouped_ffn(dl, xd, wl, rl, saved, ws), "moe_grouped_ffn")
     torch.cuda.synchronize()
-    local = g["sorted_route"][:n_local]
+    local = g["sorted_route"][p0:p1]
     y = saved.y.cpu().numpy()
     assert np.array_equal(y[local].view(np.uint32), g["y"][local].view(np.uint32))
     tok = np.unique(local // cfg.top_k)[:64]
