@@ -42,17 +42,16 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // ---------------------------------------------------------------------------
 // Up projection + SwiGLU.
 // Work item = (row tile of 32 * MBT rows of one group, 128 activation
-// columns).  Group g < E
-// is routed expert g, its rows are the sorted positions offsets[g] + row0 ..;
-// group E is the shared expert, rows are tokens row0 ...
-// Wave w owns activation columns c = nt*128 + 32w .. +32 and computes both
-// gate (W13 row c) and up (W13 row I + c) for every row of the tile, so the
-// SwiGLU is elementwise on the two accumulators.  Its 64 weight rows go
-// through a private LDS area; the gathered activation rows through a
-// double-buffered area shared by the four waves.  64-row tiles (96 rows
-// at large batches) keep registers and LDS small enough for two workgroups
-// per CU, which with the
-// loads of the next K blocks in flight keeps enough bytes moving.
+// columns).  Group g < E is routed expert g, its rows are the sorted
+// positions offsets[g] + row0 ..; group E is the shared expert, rows are
+// tokens row0 ...  Wave w owns activation columns c = nt*128 + 32w .. +32
+// and computes both gate (W13 row c) and up (W13 row I + c) for every row of
+// the tile, so the SwiGLU is elementwise on the two accumulators.  Its 64
+// weight rows go through a private LDS area; the gathered activation rows
+// through a double-buffered area shared by the four waves.  64-row tiles
+// (96 rows at large batches) keep registers and LDS small enough for two
+// workgroups per CU, which with the loads of the next K blocks in flight
+// keeps enough bytes moving.
 // Outputs: act as a bf16 hi/lo pair (row = sorted position, or token for the
 // shared expert) and, if requested, the fp32 gate/up values.
 // NKB > 0 instantiates the K loop fully unrolled for H = 64 * NKB with a
