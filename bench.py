@@ -264,6 +264,60 @@ def run_ep_share(cfg, w, steps, warmup, share):
             "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9)}
 
 
+def run_mx(cfg, layer, steps, warmup):
+    """The forward with block-scaled FP8 expert weights (the layer's bf16
+    expert weights encoded to OCP MX E4M3 + E8M0 scales per 32 elements),
+    HIP-event timed on the kernels' stream over `steps` forwards."""
+    import torch
+    import mixture_experts_layer_counting_amd as m
+    import workloads as W
+    import workloads.mx as MX
+    dev = torch.device("cuda:0")
+    mxl = MX.mx_layer(layer)
+    u8 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(dev)
+    f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    bits = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    g = lambda k, i: None if mxl[k] is None else u8(mxl[k][i])
+    wm = m.WeightsMx(w_router=f32(layer["w_router"]), router_bias=f32(layer["router_bias"]),
+                     w13_q=g("w13", 0), w13_s=g("w13", 1), w2_q=g("w2", 0), w2_s=g("w2", 1),
+                     ws13_q=g("ws13", 0), ws13_s=g("ws13", 1), ws2_q=g("ws2", 0), ws2_s=g("ws2", 1),
+                     w_sgate=bits(layer["w_sgate"]))
+    del mxl
+    x = torch.from_numpy(W.tokens(cfg).view(np.int16)).to(dev)
+    d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
+    routes = m.alloc_routes(d, dev, logits=False)
+    saved = m.alloc_saved(d, dev)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        m.check(m.moe_forward_mx(d, wm, x, routes, saved, None, out16, ws, stream), "moe_forward_mx")
+
+    for _ in range(warmup):
+        fwd()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+    touched = int((np.diff(routes.expert_offsets.cpu().numpy()) > 0).sum())
+    H, I, Is, T, R, E = cfg.hidden, cfg.inter, cfg.shared_inter, cfg.tokens, cfg.routes, cfg.experts
+    # as the bf16 layer's bytes with one byte per expert weight plus one
+    # scale byte per 32
+    wb = 1 + 1 / 32
+    byts = (touched * 3 * I * H * wb + 3 * Is * H * wb + E * H * 4 + H * 2 + T * H * 2
+            + R * H * 4 * 2 + T * H * 2)
+    return {"workload": f"{cfg.name}: {T} tokens, expert weights block-scaled FP8 (OCP MX E4M3, "
+                        f"32-element E8M0 scales)", "dtype": "bf16 activations, fp8-e4m3 expert weights",
+            "ms": ms, "tokens_per_s": T / (ms / 1e3), "bytes": byts,
+            "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9)}
+
+
 def run_backward(cfg, steps, warmup):
     """Forward (training mode) once, then `steps` timed backward passes of
     the same batch (HIP-event timed on the kernels' stream)."""
@@ -345,6 +399,8 @@ def main():
     ap.add_argument("--backward", default="bwd4k", help="workload of the backward timing, or 'none'")
     ap.add_argument("--ep-share", type=int, default=8,
                     help="also time the grouped FFN on one GPU's share of this many expert-parallel GPUs (0: off)")
+    ap.add_argument("--mx", type=int, default=1,
+                    help="also time the forward with block-scaled FP8 expert weights (0: off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -394,6 +450,12 @@ def main():
         ep_share = run_ep_share(cfg, w, args.steps, args.warmup, args.ep_share)
         log(f"bench: expert share {ep_share['ms']:.3f} ms")
 
+    mx = None
+    if args.mx:
+        log(f"bench: {cfg.name} with block-scaled FP8 expert weights")
+        mx = run_mx(cfg, layer, args.steps, args.warmup)
+        log(f"bench: {cfg.name} mx {mx['ms']:.3f} ms/step")
+
     backward = None
     if args.backward != "none":
         log(f"bench: backward {args.backward}")
@@ -435,6 +497,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "ep_share": ep_share,
+        "mx_weights": mx,
         "backward": backward,
     }
     print(json.dumps(line), flush=True)

@@ -212,6 +212,42 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                  float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws,
                  size_t ws_bytes, hipStream_t stream);
 
+/* Block-scaled FP8 expert weights (OCP MX format, the E4M3 element type).
+ * Every 32 consecutive elements of a weight row along its contraction axis
+ * (H for W13 / Ws13, I for W2 / Ws2) share one E8M0 scale code s, value
+ * 2^(s - 127); an element is an E4M3 code (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; code 0x7F / 0xFF is NaN).  The weight this represents
+ * is code value x 2^(s - 127), exactly: an E4M3 value has at most 4
+ * significant bits, so every represented weight in bf16 range is a bf16.
+ * Layouts are those of moe_weights with one byte per element; the scale
+ * arrays have one byte per 32 elements.  Scale code 255 (NaN) is not
+ * allowed.  Router, bias and shared gate are as in moe_weights. */
+typedef struct {
+  const float* w_router;    /* [E][H] fp32 */
+  const float* router_bias; /* [E] fp32 or NULL */
+  const uint8_t* w13_q;     /* [E][2I][H] E4M3 */
+  const uint8_t* w13_s;     /* [E][2I][H/32] E8M0 */
+  const uint8_t* w2_q;      /* [E][H][I] E4M3 */
+  const uint8_t* w2_s;      /* [E][H][I/32] E8M0 */
+  const uint8_t* ws13_q;    /* [2Is][H] (NULL iff Is == 0) */
+  const uint8_t* ws13_s;    /* [2Is][H/32] */
+  const uint8_t* ws2_q;     /* [H][Is] */
+  const uint8_t* ws2_s;     /* [H][Is/32] */
+  const uint16_t* w_sgate;  /* [H] bf16 (NULL iff Is == 0) */
+} moe_weights_mx;
+
+/* Forward with block-scaled FP8 expert weights (the low-precision expert
+ * weights named as follow-up work on the RL-Kernel 557 page's Stage 3).
+ * Same contract, kernels and per-element arithmetic as moe_forward with
+ * each expert weight replaced by its represented value: the expert GEMMs
+ * expand every 16 codes to bf16 with the gfx950 scaled conversion as they
+ * stage them, so for equal represented weights the results are bit for bit
+ * those of moe_forward.  Reads about half of moe_forward's weight bytes.
+ * Same errors as moe_forward. */
+int moe_forward_mx(const moe_dims* dims, const moe_weights_mx* w, const uint16_t* x,
+                   moe_routes* routes, moe_saved* saved, float* out_f32, uint16_t* out_bf16,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Profiling variant of moe_forward: the same kernels in the same order on
  * `stream`, with events[i] recorded just before kernel i and events[n] after
  * the last one, n = moe_forward_kernel_count(dims).  `events` are created by

@@ -42,6 +42,11 @@ class MoeWeights(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("w_router", "router_bias", "w13", "w2", "ws13", "ws2", "w_sgate")]
 
 
+class MoeWeightsMx(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in ("w_router", "router_bias", "w13_q", "w13_s", "w2_q", "w2_s", "ws13_q",
+                                   "ws13_s", "ws2_q", "ws2_s", "w_sgate")]
+
+
 class MoeRoutes(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("topk_idx", "topk_gate", "logits", "expert_offsets", "sorted_route",
                                    "route_pos")]
@@ -57,7 +62,7 @@ class MoeGrads(ctypes.Structure):
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
-           "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name")
+           "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx")
 
 _lib = None
 
@@ -88,6 +93,9 @@ def load_library():
     lib.moe_combine.argtypes = [P(MoeDims), P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP]
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, *ws]
+    lib.moe_forward_mx.restype = ctypes.c_int
+    lib.moe_forward_mx.argtypes = [P(MoeDims), P(MoeWeightsMx), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP,
+                                   *ws]
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                  P(MoeGrads), *ws]
@@ -153,6 +161,26 @@ class Weights:
 
     def c(self) -> MoeWeights:
         return MoeWeights(*(_ptr(getattr(self, n)) for n, _ in MoeWeights._fields_))
+
+
+@dataclasses.dataclass
+class WeightsMx:
+    """Block-scaled FP8 expert weights: E4M3 codes and E8M0 scale codes (one
+    per 32 elements along each row) as uint8 tensors."""
+    w_router: object
+    w13_q: object
+    w13_s: object
+    w2_q: object
+    w2_s: object
+    router_bias: object = None
+    ws13_q: object = None
+    ws13_s: object = None
+    ws2_q: object = None
+    ws2_s: object = None
+    w_sgate: object = None
+
+    def c(self) -> MoeWeightsMx:
+        return MoeWeightsMx(*(_ptr(getattr(self, n)) for n, _ in MoeWeightsMx._fields_))
 
 
 @dataclasses.dataclass
@@ -244,6 +272,13 @@ def moe_forward(dims, weights, x, routes, saved, out_f32, out_bf16, ws, stream=N
     return load_library().moe_forward(ctypes.byref(dims.c()), ctypes.byref(weights.c()), _ptr(x),
                                       ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(out_f32),
                                       _ptr(out_bf16), p, n, _stream(stream))
+
+
+def moe_forward_mx(dims, weights_mx, x, routes, saved, out_f32, out_bf16, ws, stream=None) -> int:
+    p, n = _ws(ws)
+    return load_library().moe_forward_mx(ctypes.byref(dims.c()), ctypes.byref(weights_mx.c()), _ptr(x),
+                                         ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(out_f32),
+                                         _ptr(out_bf16), p, n, _stream(stream))
 
 
 def moe_backward(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, ws, stream=None) -> int:

@@ -59,15 +59,15 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // flight while kb is multiplied); NKB = 0 is the general loop with one block
 // in flight (NSET = 1).  All run the same MFMA sequence on every element.
 // ---------------------------------------------------------------------------
-template <int NKB, int NSET, int MBT>
+template <int NKB, int NSET, int MBT, bool MX>
 __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
     const uint16_t* __restrict__ ws13, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_route, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, uint16_t* __restrict__ act_hi,
     uint16_t* __restrict__ act_lo, uint16_t* __restrict__ sact_hi,
-    uint16_t* __restrict__ sact_lo, float* __restrict__ gu, float* __restrict__ sgu, int64_t T,
-    int H, int E, int K, int I, int Is, int ncol_tiles) {
+    uint16_t* __restrict__ sact_lo, float* __restrict__ gu, float* __restrict__ sgu, const MxWeights mx,
+    int64_t T, int H, int E, int K, int I, int Is, int ncol_tiles) {
   constexpr int ROWS = 32 * MBT;  // rows of a work item
   const int item = xcd_item(blockIdx.x, ntiles[0] * ncol_tiles);
   if (item < 0) return;
@@ -117,6 +117,22 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   const int col = nt * kUpCols + wave * 32 + j;
   const uint16_t* wgp = W + static_cast<int64_t>(nt * kUpCols + wave * 32 + br8) * H + bc * 8;
   const uint16_t* wup = wgp + static_cast<int64_t>(Ie) * H;
+  // MX B loader: the same 64 rows as 16 rows x 64 code bytes per
+  // instruction (lane: row 16q + bq, 16-byte piece cq), with each row's
+  // scale code for the piece's 32-element half
+  const int cq = lane & 3, bq = lane >> 2;
+  const uint8_t* mq[4];
+  const uint8_t* ms[4];
+  if constexpr (MX) {
+    const uint8_t* Wq = shared ? mx.sq : mx.q + static_cast<int64_t>(grp) * 2 * I * H;
+    const uint8_t* Wsc = shared ? mx.ss : mx.s + static_cast<int64_t>(grp) * 2 * I * (H / 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t r = (q < 2 ? 0 : Ie) + nt * kUpCols + wave * 32 + 16 * (q & 1) + bq;
+      mq[q] = Wq + r * H + cq * 16;
+      ms[q] = Wsc + r * (H / 32) + (cq >> 1);
+    }
+  }
 
   f32x16_t accg[MBT], accu[MBT];
 #pragma unroll
@@ -125,22 +141,42 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     accu[mb] = zero16();
   }
   u32x4_t ra[NSET][MBT], rb[NSET][8];
+  u32x4_t rq[NSET][4];
+  uint32_t rs[NSET][4];
 
   auto issue = [&](int set, int kb) {
     const int kp = kb << 6;
 #pragma unroll
     for (int q = 0; q < MBT; ++q) ra[set][q] = ld16(xa[q] + kp);
+    if constexpr (MX) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      rb[set][q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp);
-      rb[set][4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp);
+      for (int q = 0; q < 4; ++q) {
+        rq[set][q] = ld16(mq[q] + kp);
+        rs[set][q] = ms[q][2 * kb];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rb[set][q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp);
+        rb[set][4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp);
+      }
     }
   };
   auto stash = [&](int set, int buf) {
 #pragma unroll
     for (int q = 0; q < MBT; ++q) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[set][q]);
+    if constexpr (MX) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[set][q]);
+      for (int q = 0; q < 4; ++q) {
+        u32x4_t lo, hi;
+        mx_dequant16(rq[set][q], e8m0_scale(rs[set][q]), lo, hi);
+        st16(&Bs[wave][lds_off(16 * q + bq, 2 * cq)], lo);
+        st16(&Bs[wave][lds_off(16 * q + bq, 2 * cq + 1)], hi);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) st16(&Bs[wave][lds_off(8 * q + br8, bc)], rb[set][q]);
+    }
   };
   auto compute = [&](int buf) {
 #pragma unroll
@@ -227,14 +263,14 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 // flight while kb is multiplied); NKB = 0 is the general loop with one block
 // in flight (NSET = 1).  All run the same MFMA sequence on every element.
 // ---------------------------------------------------------------------------
-template <int NKB, int NSET, int NBW>
+template <int NKB, int NSET, int NBW, bool MX>
 __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     const uint16_t* __restrict__ act_hi, const uint16_t* __restrict__ act_lo,
     const uint16_t* __restrict__ sact_hi, const uint16_t* __restrict__ sact_lo,
     const uint16_t* __restrict__ w2, const uint16_t* __restrict__ ws2,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_route,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ meta, float* __restrict__ y,
-    float* __restrict__ sy, int64_t T, int H, int E, int K, int I, int Is) {
+    float* __restrict__ sy, const MxWeights mx, int64_t T, int H, int E, int K, int I, int Is) {
   constexpr int COLS = kDownCols * NBW;  // hidden columns of a work item
   constexpr int WROWS = 32 * NBW;        // W2 rows (hidden columns) of a wave
   const int ncol_tiles = H / COLS;
@@ -290,6 +326,22 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   const int bc = lane & 7, br8 = lane >> 3;
   const int n0 = nt * COLS + wave * WROWS;
   const uint16_t* wb = W + static_cast<int64_t>(n0 + br8) * Ie + bc * 8;
+  // MX B loader: the wave's rows as 16 rows x 64 code bytes per instruction
+  // (lane: row 16q + bq, 16-byte piece cq) with the piece's scale code
+  constexpr int NQ = WROWS / 16;
+  const int cq = lane & 3, bq = lane >> 2;
+  const uint8_t* mq[NQ];
+  const uint8_t* ms[NQ];
+  if constexpr (MX) {
+    const uint8_t* Wq = shared ? mx.sq : mx.q + static_cast<int64_t>(grp) * H * I;
+    const uint8_t* Wsc = shared ? mx.ss : mx.s + static_cast<int64_t>(grp) * H * (I / 32);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int64_t r = n0 + 16 * q + bq;
+      mq[q] = Wq + r * Ie + cq * 16;
+      ms[q] = Wsc + r * (Ie / 32) + (cq >> 1);
+    }
+  }
 
   f32x16_t acc[2][NBW];
 #pragma unroll
@@ -297,6 +349,8 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = zero16();
   u32x4_t rh[NSET][2], rl[NSET][2], rb[NSET][4 * NBW];
+  u32x4_t rq[NSET][NQ];
+  uint32_t rs[NSET][NQ];
 
   // activation rows past the tile's end repeat its last row (unused)
   auto issue = [&](int set, int kb) {
@@ -306,8 +360,16 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
       rh[set][q] = ld16(ahi + aoff[q] + kp);
       rl[set][q] = ld16(alo + aoff[q] + kp);
     }
+    if constexpr (MX) {
 #pragma unroll
-    for (int q = 0; q < 4 * NBW; ++q) rb[set][q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp);
+      for (int q = 0; q < NQ; ++q) {
+        rq[set][q] = ld16(mq[q] + kp);
+        rs[set][q] = ms[q][2 * kb];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4 * NBW; ++q) rb[set][q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp);
+    }
   };
   auto stash = [&](int set, int buf) {
 #pragma unroll
@@ -315,8 +377,18 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
       st16(As(buf, 0) + lds_off(ar0 + 32 * q, ac), rh[set][q]);
       st16(As(buf, 1) + lds_off(ar0 + 32 * q, ac), rl[set][q]);
     }
+    if constexpr (MX) {
 #pragma unroll
-    for (int q = 0; q < 4 * NBW; ++q) st16(Bw + lds_off(8 * q + br8, bc), rb[set][q]);
+      for (int q = 0; q < NQ; ++q) {
+        u32x4_t lo, hi;
+        mx_dequant16(rq[set][q], e8m0_scale(rs[set][q]), lo, hi);
+        st16(Bw + lds_off(16 * q + bq, 2 * cq), lo);
+        st16(Bw + lds_off(16 * q + bq, 2 * cq + 1), hi);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4 * NBW; ++q) st16(Bw + lds_off(8 * q + br8, bc), rb[set][q]);
+    }
   };
   auto compute = [&](int buf) {
 #pragma unroll
@@ -481,48 +553,64 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 namespace moe {
 
 hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t* ws13,
-                         const int32_t* offsets, const int32_t* sorted_route, const int32_t* tiles,
-                         const int32_t* ntiles, int up_rows, uint16_t* act_hi, uint16_t* act_lo,
-                         uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu, int64_t T,
-                         int H, int E, int K, int I, int Is, int max_tiles, hipStream_t stream) {
+                         const MxWeights* mx, const int32_t* offsets, const int32_t* sorted_route,
+                         const int32_t* tiles, const int32_t* ntiles, int up_rows, uint16_t* act_hi,
+                         uint16_t* act_lo, uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu,
+                         int64_t T, int H, int E, int K, int I, int Is, int max_tiles,
+                         hipStream_t stream) {
   const int ncol = (I > Is ? I : Is) / kUpCols;
   const int64_t items = static_cast<int64_t>(max_tiles) * ncol;
   const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
+  const MxWeights m = mx ? *mx : MxWeights{nullptr, nullptr, nullptr, nullptr};
+#define MOE_UP(NKB, NSET, MBT)                                                                        \
+  do {                                                                                              \
+    if (mx)                                                                                         \
+      ffn_up_kernel<NKB, NSET, MBT, true><<<grid, 256, 0, stream>>>(                                \
+          x, w13, ws13, offsets, sorted_route, tiles, ntiles, act_hi, act_lo, sact_hi, sact_lo, gu, \
+          sgu, m, T, H, E, K, I, Is, ncol);                                                         \
+    else                                                                                            \
+      ffn_up_kernel<NKB, NSET, MBT, false><<<grid, 256, 0, stream>>>(                               \
+          x, w13, ws13, offsets, sorted_route, tiles, ntiles, act_hi, act_lo, sact_hi, sact_lo, gu, \
+          sgu, m, T, H, E, K, I, Is, ncol);                                                         \
+  } while (0)
   // the unrolled instantiations cover hidden size 2048 (64- and 96-row items)
   if (H == 2048 && up_rows == kUpTallRows)
-    ffn_up_kernel<32, 2, kUpTallRows / 32><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles,
-                                                                  ntiles, act_hi, act_lo, sact_hi, sact_lo,
-                                                                  gu, sgu, T, H, E, K, I, Is, ncol);
+    MOE_UP(32, 2, kUpTallRows / 32);
   else if (H == 2048)
-    ffn_up_kernel<32, 2, kRowsPerTile / 32><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles,
-                                                                   ntiles, act_hi, act_lo, sact_hi, sact_lo,
-                                                                   gu, sgu, T, H, E, K, I, Is, ncol);
+    MOE_UP(32, 2, kRowsPerTile / 32);
   else
-    ffn_up_kernel<0, 1, kRowsPerTile / 32><<<grid, 256, 0, stream>>>(x, w13, ws13, offsets, sorted_route, tiles,
-                                                                  ntiles, act_hi, act_lo, sact_hi, sact_lo,
-                                                                  gu, sgu, T, H, E, K, I, Is, ncol);
+    MOE_UP(0, 1, kRowsPerTile / 32);
+#undef MOE_UP
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
                            const uint16_t* sact_hi, const uint16_t* sact_lo, const uint16_t* w2,
-                           const uint16_t* ws2, const int32_t* offsets,
+                           const uint16_t* ws2, const MxWeights* mx, const int32_t* offsets,
                            const int32_t* sorted_route, const int32_t* tiles,
                            const int32_t* meta, float* y, float* sy, int64_t T, int H, int E,
                            int K, int I, int Is, int max_tiles, hipStream_t stream) {
+  const MxWeights m = mx ? *mx : MxWeights{nullptr, nullptr, nullptr, nullptr};
+#define MOE_DOWN(NKB, NSET, NBW, COLS)                                                                \
+  do {                                                                                              \
+    const int64_t items = static_cast<int64_t>(max_tiles) * (H / (COLS));                           \
+    const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);                             \
+    if (mx)                                                                                         \
+      ffn_down_kernel<NKB, NSET, NBW, true><<<grid, 256, 0, stream>>>(                              \
+          act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets, sorted_route, tiles, meta, y, sy, m,  \
+          T, H, E, K, I, Is);                                                                       \
+    else                                                                                            \
+      ffn_down_kernel<NKB, NSET, NBW, false><<<grid, 256, 0, stream>>>(                             \
+          act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets, sorted_route, tiles, meta, y, sy, m,  \
+          T, H, E, K, I, Is);                                                                       \
+  } while (0)
   // the unrolled instantiation covers expert and shared sizes of 512 (and
   // takes 256-column items when H allows); the general one 128 columns
-  if (I == 512 && (Is == 0 || Is == 512) && H % (2 * kDownCols) == 0) {
-    const int64_t items = static_cast<int64_t>(max_tiles) * (H / (2 * kDownCols));
-    const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
-    ffn_down_kernel<8, 2, 2><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
-                                                    sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
-  } else {
-    const int64_t items = static_cast<int64_t>(max_tiles) * (H / kDownCols);
-    const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
-    ffn_down_kernel<0, 1, 1><<<grid, 256, 0, stream>>>(act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets,
-                                                    sorted_route, tiles, meta, y, sy, T, H, E, K, I, Is);
-  }
+  if (I == 512 && (Is == 0 || Is == 512) && H % (2 * kDownCols) == 0)
+    MOE_DOWN(8, 2, 2, 2 * kDownCols);
+  else
+    MOE_DOWN(0, 1, 1, kDownCols);
+#undef MOE_DOWN
   return hipGetLastError();
 }
 

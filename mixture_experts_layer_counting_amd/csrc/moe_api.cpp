@@ -288,8 +288,11 @@ int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hip
 
 // whole_forward: the work list in the workspace was built by run_permute and
 // the shared-expert gate by run_route.
+// mx13 / mx2: block-scaled FP8 expert weights of the two projections (then
+// w's expert matrices are not read), or null.
 int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const moe_routes* r,
-            moe_saved* sv, void* ws, const Layout& L, bool whole_forward, hipStream_t s) {
+            moe_saved* sv, void* ws, const Layout& L, bool whole_forward, hipStream_t s,
+            const moe::MxWeights* mx13 = nullptr, const moe::MxWeights* mx2 = nullptr) {
   const int has_shared = d.shared_inter > 0;
   if (!whole_forward)
     MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles), tiles_up_of(ws, L),
@@ -298,7 +301,7 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
   if (has_shared && !whole_forward)
     MOE_LAUNCH(moe::launch_shared_gate(x, w->w_sgate, sv->shared_gate, d.tokens, d.hidden, s));
   const bool own_up = tiles_up_of(ws, L) != nullptr;
-  MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, r->expert_offsets, r->sorted_route,
+  MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, mx13, r->expert_offsets, r->sorted_route,
                                 own_up ? tiles_up_of(ws, L) : at<int32_t>(ws, L.tiles),
                                 at<int32_t>(ws, L.meta) + (own_up ? 2 : 0), L.up_rows,
                                 at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
@@ -308,7 +311,7 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
                                 own_up ? L.max_tiles_up : L.max_tiles, s));
   MOE_LAUNCH(moe::launch_ffn_down(at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
                                   at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), w->w2,
-                                  w->ws2, r->expert_offsets, r->sorted_route,
+                                  w->ws2, mx2, r->expert_offsets, r->sorted_route,
                                   at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta), sv->y,
                                   has_shared ? sv->shared_y : nullptr, d.tokens, d.hidden,
                                   d.experts, d.top_k, d.inter, d.shared_inter, L.max_tiles, s));
@@ -490,6 +493,53 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, m
                     stream));
   MOE_TRY(run_permute(d, routes, ws, L, stream));
   MOE_TRY(run_ffn(d, x, w, routes, saved, ws, L, true, stream));
+  return run_combine(d, routes, saved, out_f32, out_bf16, stream);
+}
+
+int moe_forward_mx(const moe_dims* dims, const moe_weights_mx* w, const uint16_t* x,
+                   moe_routes* routes, moe_saved* saved, float* out_f32, uint16_t* out_bf16,
+                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!w || !routes || !saved) return MOE_E_NULL;
+  if (!out_f32 && !out_bf16) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, H = d.hidden, E = d.experts, I = d.inter, Is = d.shared_inter;
+  Args a;
+  a.in(x, bytes_x(d));
+  a.in(w->w_router, E * H * 4);
+  a.in(w->router_bias, E * 4, false);
+  a.in(w->w13_q, E * 2 * I * H);
+  a.in(w->w13_s, E * 2 * I * (H / 32));
+  a.in(w->w2_q, E * H * I);
+  a.in(w->w2_s, E * H * (I / 32));
+  if (Is) {
+    a.in(w->ws13_q, 2 * Is * H);
+    a.in(w->ws13_s, 2 * Is * (H / 32));
+    a.in(w->ws2_q, H * Is);
+    a.in(w->ws2_s, H * (Is / 32));
+    a.in(w->w_sgate, H * 2);
+  }
+  add_routes_out(a, d, routes);
+  add_perm_out(a, d, routes);
+  add_saved(a, d, saved, true);
+  a.out(out_f32, T * H * 4, false);
+  a.out(out_bf16, T * H * 2, false);
+  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FORWARD), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD));
+  MOE_TRY(check_device());
+  moe_weights wr = {};
+  wr.w_router = w->w_router;
+  wr.router_bias = w->router_bias;
+  wr.w_sgate = w->w_sgate;
+  const moe::MxWeights mx13{w->w13_q, w->w13_s, w->ws13_q, w->ws13_s};
+  const moe::MxWeights mx2{w->w2_q, w->w2_s, w->ws2_q, w->ws2_s};
+  const Layout L = make_layout(d);
+  MOE_TRY(run_route(d, x, &wr, routes, ws, L, d.shared_inter > 0 ? saved->shared_gate : nullptr,
+                    stream));
+  MOE_TRY(run_permute(d, routes, ws, L, stream));
+  MOE_TRY(run_ffn(d, x, &wr, routes, saved, ws, L, true, stream, &mx13, &mx2));
   return run_combine(d, routes, saved, out_f32, out_bf16, stream);
 }
 

@@ -88,6 +88,40 @@ __device__ __forceinline__ void split3(float a, uint16_t (&p)[3]) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
+// Block-scaled FP8 expert weights (OCP MX: E4M3 element codes, one E8M0 scale
+// code per 32 consecutive elements along the contraction axis): routed
+// experts' codes and scales, then the shared expert's.
+struct MxWeights {
+  const uint8_t* q;
+  const uint8_t* s;
+  const uint8_t* sq;
+  const uint8_t* ss;
+};
+
+// E8M0 scale code -> 2^(code - 127) as a float (code 0 is the denormal 2^-127).
+__device__ __forceinline__ float e8m0_scale(uint32_t code) {
+  return __uint_as_float(code ? (code << 23) : 0x00400000u);
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// Sixteen E4M3 codes (one 16-byte load, element i in byte i) times `scale`
+// -> sixteen bf16 (elements 0..7 in lo, 8..15 in hi), with the gfx950
+// scaled conversion.  For a power-of-two scale the result is exact: an E4M3
+// value has at most 4 significant bits.
+__device__ __forceinline__ void mx_dequant16(u32x4_t codes, float scale, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[q], scale, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[q], scale, true);
+    o[2 * q] = __builtin_bit_cast(uint32_t, a);
+    o[2 * q + 1] = __builtin_bit_cast(uint32_t, b);
+  }
+  lo = u32x4_t{o[0], o[1], o[2], o[3]};
+  hi = u32x4_t{o[4], o[5], o[6], o[7]};
+}
+
 // XCD-aware mapping of a 1-D grid onto `items` work items.  The hardware
 // deals workgroups round-robin over the 8 XCDs (workgroup g runs on XCD g%8);
 // this gives each XCD one contiguous range of items, so items that share

@@ -55,14 +55,17 @@ inline int up_rows_per_tile(int64_t T, int H) {
   return (T >= kUpTallMin && H == 2048) ? kUpTallRows : kRowsPerTile;
 }
 // tiles / ntiles: the up_rows-row work list and the int holding its length.
+// mx: block-scaled FP8 expert weights (then w13 / ws13 resp. w2 / ws2 are
+// not read), or null for bf16 weights.
 hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t* ws13,
-                         const int32_t* offsets, const int32_t* sorted_route, const int32_t* tiles,
-                         const int32_t* ntiles, int up_rows, uint16_t* act_hi, uint16_t* act_lo,
-                         uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu, int64_t T,
-                         int H, int E, int K, int I, int Is, int max_tiles, hipStream_t stream);
+                         const MxWeights* mx, const int32_t* offsets, const int32_t* sorted_route,
+                         const int32_t* tiles, const int32_t* ntiles, int up_rows, uint16_t* act_hi,
+                         uint16_t* act_lo, uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu,
+                         int64_t T, int H, int E, int K, int I, int Is, int max_tiles,
+                         hipStream_t stream);
 hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
                            const uint16_t* sact_hi, const uint16_t* sact_lo, const uint16_t* w2,
-                           const uint16_t* ws2, const int32_t* offsets,
+                           const uint16_t* ws2, const MxWeights* mx, const int32_t* offsets,
                            const int32_t* sorted_route, const int32_t* tiles,
                            const int32_t* meta, float* y, float* sy, int64_t T, int H, int E,
                            int K, int I, int Is, int max_tiles, hipStream_t stream);

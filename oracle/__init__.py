@@ -8,9 +8,12 @@ from .moe_oracle import (  # noqa: F401
     bf16_to_f64,
     brute_force_forward,
     combine,
+    e4m3_to_f64,
+    e8m0_to_f64,
     expert_weight_grads,
     f64_to_bf16_bits,
     forward,
+    mx_to_f64,
     permute_routes,
     route_gates,
     routed_rows,

@@ -69,6 +69,34 @@ def f64_to_bf16_bits(a) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP FP8 E4M3 element codes -> float64, exactly (OCP Microscaling
+    Formats v1.0, element type E4M3: 1 sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent field 0 is subnormal, m x 2^-9; the codes with
+    all exponent and mantissa bits set are NaN; no infinities)."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(F64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    """OCP E8M0 scale codes -> 2^(code - 127); code 255 is NaN."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+def mx_to_f64(codes, scale_codes, block: int = 32) -> np.ndarray:
+    """Block-scaled FP8 weights -> float64: element i of a row times the scale
+    of its block of `block` consecutive elements along the last axis."""
+    v = e4m3_to_f64(codes)
+    sc = e8m0_to_f64(scale_codes)
+    return v * np.repeat(sc, block, axis=-1)
+
+
 def silu(z):
     return z / (1.0 + np.exp(-z))
 

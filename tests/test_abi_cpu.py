@@ -140,3 +140,25 @@ def test_valid_arguments_reach_the_device_check(lib):
     d = m.Dims(64, 512, 512, 10, 128, 128)
     w, r, s, x, o32, o16, ws, f = full_args(d)
     assert fwd(d, w, r, s, x, o32, o16, ws) == m.MOE_E_DEVICE
+
+
+def test_mx_forward_validation_fails_closed(lib):
+    """moe_forward_mx checks dims, every code and scale buffer and the
+    workspace on the host before anything is launched."""
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    E, H, I, Is = d.experts, d.hidden, d.inter, d.shared_inter
+    wm = m.WeightsMx(w_router=w.w_router, w13_q=f(E * 2 * I * H), w13_s=f(E * 2 * I * H // 32),
+                     w2_q=f(E * H * I), w2_s=f(E * H * I // 32), ws13_q=f(2 * Is * H), ws13_s=f(2 * Is * H // 32),
+                     ws2_q=f(H * Is), ws2_s=f(H * Is // 32), w_sgate=w.w_sgate)
+    mx = lambda dd, ww, xx=x, wss=ws: m.moe_forward_mx(dd, ww, xx, r, s, o32, o16, wss, stream=0)
+    assert mx(m.Dims(64, 500, 512, 10, 128, 128), wm) == m.MOE_E_SHAPE
+    assert mx(d, wm, xx=None) == m.MOE_E_NULL
+    assert mx(d, m.WeightsMx(**{**wm.__dict__, "w13_s": None})) == m.MOE_E_NULL
+    assert mx(d, m.WeightsMx(**{**wm.__dict__, "w2_q": wm.w2_q + 4})) == m.MOE_E_ALIGN
+    assert mx(d, m.WeightsMx(**{**wm.__dict__, "ws2_s": None})) == m.MOE_E_NULL
+    assert mx(d, wm, wss=(ws[0], ws[1] - 1)) == m.MOE_E_WORKSPACE
+    assert mx(m.Dims(0, 512, 512, 10, 128, 128), wm, xx=None, wss=None) == m.MOE_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert mx(d, wm) == m.MOE_E_DEVICE

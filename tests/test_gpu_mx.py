@@ -1,0 +1,91 @@
+"""GPU parity of the forward with block-scaled FP8 expert weights.
+
+The weights are the seeded bf16 layer encoded to OCP MX (E4M3 elements, one
+E8M0 scale per 32 elements along the contraction; workloads/mx.py).  The
+weight each code pair represents is exact in bf16, so
+  * moe_forward_mx must give, bit for bit, what moe_forward gives on the
+    represented weights (decoded by the oracle), and
+  * both must match the FP64 oracle on the represented weights within the
+    forward's tolerance (all tokens of the 256-token layer).
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_counting_amd as m
+import oracle as O
+import workloads.mx as MX
+from tests.gpu_util import (DEV, check_forward, dev_bits, dev_f32, dev_weights, dims_of, gpu_forward,
+                            load_cfg, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def represented_bits(q, s):
+    """bf16 bits of the weights the codes represent (the oracle's decoding;
+    exact, asserted), one leading index at a time."""
+    out = np.empty(q.shape, np.uint16)
+
+    def one(i):
+        v = O.mx_to_f64(q[i], s[i])
+        b = O.f64_to_bf16_bits(v)
+        assert np.array_equal(O.bf16_to_f64(b), v)
+        out[i] = b
+
+    with ThreadPoolExecutor(8) as ex:
+        list(ex.map(one, range(q.shape[0])))
+    return out
+
+
+def dev_u8(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(DEV)
+
+
+def mx_weights(layer, mxl):
+    g = lambda k, i: None if mxl[k] is None else dev_u8(mxl[k][i])
+    return m.WeightsMx(w_router=dev_f32(layer["w_router"]), router_bias=dev_f32(layer["router_bias"]),
+                       w13_q=g("w13", 0), w13_s=g("w13", 1), w2_q=g("w2", 0), w2_s=g("w2", 1),
+                       ws13_q=g("ws13", 0), ws13_s=g("ws13", 1), ws2_q=g("ws2", 0), ws2_s=g("ws2", 1),
+                       w_sgate=dev_bits(layer["w_sgate"]))
+
+
+def gpu_forward_mx(cfg, wm, x_dev):
+    d = dims_of(cfg, int(x_dev.shape[0]))
+    routes = m.alloc_routes(d, DEV)
+    saved = m.alloc_saved(d, DEV)
+    out32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, DEV)
+    m.check(m.moe_forward_mx(d, wm, x_dev, routes, saved, out32, out16, ws), "moe_forward_mx")
+    torch.cuda.synchronize()
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+    h = lambda t: None if t is None else t.cpu().numpy()
+    return dict(idx=h(routes.topk_idx), gates=h(routes.topk_gate), logits=h(routes.logits),
+                offsets=h(routes.expert_offsets), sorted_route=h(routes.sorted_route),
+                route_pos=h(routes.route_pos), y=h(saved.y), s=h(saved.shared_y), sg=h(saved.shared_gate),
+                out32=h(out32), out16=h(out16).view(np.uint16))
+
+
+@pytest.mark.parametrize("name", ["tiny", "moe1k"])
+def test_mx_forward_equals_bf16_forward_on_represented_weights(name):
+    cfg, layer, x = load_cfg(name)
+    say(f"case: {name}, encoding the expert weights to MX")
+    mxl = MX.mx_layer(layer)
+    rep = dict(layer)
+    for k in ("w13", "w2", "ws13", "ws2"):
+        if mxl[k] is not None:
+            rep[k] = represented_bits(*mxl[k])
+    xd = dev_bits(x)
+    say(f"case: {name}, moe_forward_mx vs moe_forward on the represented weights")
+    g_mx = gpu_forward_mx(cfg, mx_weights(layer, mxl), xd)
+    g_bf = gpu_forward(cfg, dev_weights(rep), xd).host()
+    for k in ("idx", "sorted_route", "offsets"):
+        assert np.array_equal(g_mx[k], g_bf[k]), k
+    for k in ("gates", "y", "out32", "s"):
+        assert np.array_equal(g_mx[k].view(np.uint32), g_bf[k].view(np.uint32)), k
+    assert np.array_equal(g_mx["out16"], g_bf["out16"])
+    if name == "tiny":
+        say("  oracle on the represented weights, all tokens")
+        check_forward(cfg, rep, x, g_mx)

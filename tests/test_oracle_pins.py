@@ -315,3 +315,70 @@ def test_bf16_round_trip_and_rounding():
     assert back[3] == -2.5
     # half an ulp of the binade [2^-9, 2^-8): 2^-9 * 2^-8
     assert abs(back[4] - 3.0e-3) <= 2.0 ** -17
+
+
+# ------------------------------------------------- block-scaled FP8 weights
+def test_e4m3_decode_matches_the_format_definition():
+    """OCP MX v1.0, E4M3 element type: bias 7, 3 mantissa bits, exponent
+    field 0 subnormal (m x 2^-9), S.1111.111 NaN, largest normal 448."""
+    d = O.e4m3_to_f64
+    assert d(0x00) == 0.0 and np.signbit(d(0x80))
+    assert d(0x01) == 2.0 ** -9                      # smallest subnormal
+    assert d(0x07) == 0.875 * 2.0 ** -6              # largest subnormal
+    assert d(0x08) == 2.0 ** -6                      # smallest normal
+    assert d(0x38) == 1.0 and d(0xB8) == -1.0
+    assert d(0x39) == 1.125 and d(0x3F) == 1.875
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0    # largest normal
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    # every finite code: exponent/mantissa composition, brute force
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        e, m, s = (c >> 3) & 15, c & 7, -1.0 if c & 0x80 else 1.0
+        want = s * (m / 8.0 * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+        assert d(c) == want
+
+
+def test_e8m0_and_block_scaling():
+    assert O.e8m0_to_f64(127) == 1.0
+    assert O.e8m0_to_f64(0) == 2.0 ** -127 and O.e8m0_to_f64(254) == 2.0 ** 127
+    assert np.isnan(O.e8m0_to_f64(255))
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 0x7F, size=(3, 96)).astype(np.uint8)
+    scales = rng.integers(100, 140, size=(3, 3)).astype(np.uint8)
+    got = O.mx_to_f64(codes, scales)
+    for r in range(3):
+        for i in range(96):
+            assert got[r, i] == O.e4m3_to_f64(codes[r, i]) * 2.0 ** (int(scales[r, i // 32]) - 127)
+
+
+def test_mx_encoder_picks_the_nearest_representable_weight():
+    """The input encoder (workloads.mx) against brute force over the oracle's
+    decoding of all finite codes: each element is the nearest E4M3 value of
+    the scaled weight (ties to the even code), clamped at 448, and the block
+    scale is 2^(floor(log2 amax) - 8)."""
+    import workloads.mx as MX
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    fvals = O.e4m3_to_f64(finite)
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((4, 64)).astype(np.float32) * np.float32(0.02)
+    w[0, :32] = 0.0                                    # an all-zero block
+    w[1, 3] = np.float32(5.0)                          # a block dominated by one value
+    bits = W.f32_to_bf16_bits(w)
+    codes, sc = MX.encode_mx(bits)
+    v = O.bf16_to_f64(bits)
+    for r in range(4):
+        for b in range(2):
+            blk = v[r, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            want_s = 127 if amax == 0 else int(np.floor(np.log2(amax))) - 8 + 127
+            assert sc[r, b] == want_s
+            X = 2.0 ** (int(sc[r, b]) - 127)
+            for i in range(32):
+                y = min(max(blk[i] / X, -448.0), 448.0)
+                dist = np.abs(fvals - y)
+                best = finite[dist == dist.min()]
+                if len(best) > 1:                       # a tie: the even mantissa
+                    best = best[(best & 1) == 0]
+                    best = best[np.signbit(O.e4m3_to_f64(best)) == np.signbit(y)] if len(best) > 1 else best
+                assert O.e4m3_to_f64(codes[r, 32 * b + i]) == O.e4m3_to_f64(best[0])
