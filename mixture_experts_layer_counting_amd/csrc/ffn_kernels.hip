@@ -119,10 +119,13 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   const uint16_t* wup = wgp + static_cast<int64_t>(Ie) * H;
   // MX B loader: the same 64 rows as 16 rows x 64 code bytes per
   // instruction (lane: row 16q + bq, 16-byte piece cq), with each row's
-  // scale code for the piece's 32-element half
+  // scale code for the piece's 32-element half.  The unrolled loop reads a
+  // row's scale codes 16 at a time (8 K blocks) into a pair of register
+  // groups; the general loop one byte per block.
   const int cq = lane & 3, bq = lane >> 2;
   const uint8_t* mq[4];
   const uint8_t* ms[4];
+  const uint8_t* msr[4];
   if constexpr (MX) {
     const uint8_t* Wq = shared ? mx.sq : mx.q + static_cast<int64_t>(grp) * 2 * I * H;
     const uint8_t* Wsc = shared ? mx.ss : mx.s + static_cast<int64_t>(grp) * 2 * I * (H / 32);
@@ -131,8 +134,20 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
       const int64_t r = (q < 2 ? 0 : Ie) + nt * kUpCols + wave * 32 + 16 * (q & 1) + bq;
       mq[q] = Wq + r * H + cq * 16;
       ms[q] = Wsc + r * (H / 32) + (cq >> 1);
+      msr[q] = Wsc + r * (H / 32);
     }
   }
+  u32x4_t sg[2][4];
+  // scale codes of K blocks 8g .. 8g + 7 of the wave's rows
+  auto load_scales = [&](int g) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sg[g & 1][q] = ld16(msr[q] + 16 * g);
+  };
+  // scale code of block kb for row group q (compile-time kb)
+  auto group_scale = [&](int kb, int q) {
+    const uint32_t w = sg[(kb >> 3) & 1][q][(kb & 7) >> 1];
+    return (w >> (8 * (2 * (kb & 1) + (cq >> 1)))) & 0xffu;
+  };
 
   f32x16_t accg[MBT], accu[MBT];
 #pragma unroll
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         rq[set][q] = ld16(mq[q] + kp);
-        rs[set][q] = ms[q][2 * kb];
+        if constexpr (NKB == 0) rs[set][q] = ms[q][2 * kb];
       }
     } else {
 #pragma unroll
@@ -162,14 +177,16 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
       }
     }
   };
-  auto stash = [&](int set, int buf) {
+  // blk: the K block being staged (compile-time in the unrolled loop)
+  auto stash = [&](int set, int buf, int blk) {
 #pragma unroll
     for (int q = 0; q < MBT; ++q) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[set][q]);
     if constexpr (MX) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x4_t lo, hi;
-        mx_dequant16(rq[set][q], e8m0_scale(rs[set][q]), lo, hi);
+        const uint32_t sc = NKB > 0 ? group_scale(blk, q) : rs[set][q];
+        mx_dequant16(rq[set][q], e8m0_scale(sc), lo, hi);
         st16(&Bs[wave][lds_off(16 * q + bq, 2 * cq)], lo);
         st16(&Bs[wave][lds_off(16 * q + bq, 2 * cq + 1)], hi);
       }
@@ -198,26 +215,33 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   // The B area is private to the wave: overwriting it after the reads of
   // the previous block is ordered by the wave's own LDS instruction order.
   if constexpr (NKB > 0) {
+    static_assert(!MX || NKB % 8 == 0, "scale codes are read 8 K blocks at a time");
+    if constexpr (MX) {
+      load_scales(0);
+      if (NKB > 8) load_scales(1);
+    }
 #pragma unroll
     for (int q = 0; q < NSET && q < NKB; ++q) issue(q, q);
-    stash(0, 0);
+    stash(0, 0, 0);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       __syncthreads();
       if (kb + NSET < NKB) issue(kb % NSET, kb + NSET);
+      // group g's registers are free once block 8g + 7 is staged
+      if (MX && (kb & 7) == 7 && kb + 9 < NKB) load_scales((kb >> 3) + 2);
       compute(kb & 1);
-      if (kb + 1 < NKB) stash((kb + 1) % NSET, (kb + 1) & 1);
+      if (kb + 1 < NKB) stash((kb + 1) % NSET, (kb + 1) & 1, kb + 1);
     }
   } else {
     issue(0, 0);
-    stash(0, 0);
+    stash(0, 0, 0);
     for (int kb = 0; kb < nkb; ++kb) {
       __syncthreads();
       const int cur = kb & 1;
       const bool more = kb + 1 < nkb;
       if (more) issue(0, kb + 1);
       compute(cur);
-      if (more) stash(0, cur ^ 1);
+      if (more) stash(0, cur ^ 1, kb + 1);
     }
   }
 
@@ -327,11 +351,14 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   const int n0 = nt * COLS + wave * WROWS;
   const uint16_t* wb = W + static_cast<int64_t>(n0 + br8) * Ie + bc * 8;
   // MX B loader: the wave's rows as 16 rows x 64 code bytes per instruction
-  // (lane: row 16q + bq, 16-byte piece cq) with the piece's scale code
+  // (lane: row 16q + bq, 16-byte piece cq) with the piece's scale code.  The
+  // unrolled loop (Ie = 512: 16 scale codes per row) reads all of a row's
+  // scale codes once; the general loop one byte per block.
   constexpr int NQ = WROWS / 16;
   const int cq = lane & 3, bq = lane >> 2;
   const uint8_t* mq[NQ];
   const uint8_t* ms[NQ];
+  u32x4_t sall[NQ];
   if constexpr (MX) {
     const uint8_t* Wq = shared ? mx.sq : mx.q + static_cast<int64_t>(grp) * H * I;
     const uint8_t* Wsc = shared ? mx.ss : mx.s + static_cast<int64_t>(grp) * H * (I / 32);
@@ -340,8 +367,15 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
       const int64_t r = n0 + 16 * q + bq;
       mq[q] = Wq + r * Ie + cq * 16;
       ms[q] = Wsc + r * (Ie / 32) + (cq >> 1);
+      if constexpr (NKB > 0) {
+        static_assert(NKB == 8, "a row's scale codes are one 16-byte load");
+        sall[q] = ld16(Wsc + r * (Ie / 32));
+      }
     }
   }
+  auto row_scale = [&](int kb, int q) {
+    return (sall[q][kb >> 1] >> (8 * (2 * (kb & 1) + (cq >> 1)))) & 0xffu;
+  };
 
   f32x16_t acc[2][NBW];
 #pragma unroll
@@ -364,14 +398,15 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         rq[set][q] = ld16(mq[q] + kp);
-        rs[set][q] = ms[q][2 * kb];
+        if constexpr (NKB == 0) rs[set][q] = ms[q][2 * kb];
       }
     } else {
 #pragma unroll
       for (int q = 0; q < 4 * NBW; ++q) rb[set][q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp);
     }
   };
-  auto stash = [&](int set, int buf) {
+  // blk: the K block being staged (compile-time in the unrolled loop)
+  auto stash = [&](int set, int buf, int blk) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       st16(As(buf, 0) + lds_off(ar0 + 32 * q, ac), rh[set][q]);
@@ -381,7 +416,8 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         u32x4_t lo, hi;
-        mx_dequant16(rq[set][q], e8m0_scale(rs[set][q]), lo, hi);
+        const uint32_t sc = NKB > 0 ? row_scale(blk, q) : rs[set][q];
+        mx_dequant16(rq[set][q], e8m0_scale(sc), lo, hi);
         st16(Bw + lds_off(16 * q + bq, 2 * cq), lo);
         st16(Bw + lds_off(16 * q + bq, 2 * cq + 1), hi);
       }
@@ -417,24 +453,24 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   if constexpr (NKB > 0) {
 #pragma unroll
     for (int q = 0; q < NSET && q < NKB; ++q) issue(q, q);
-    stash(0, 0);
+    stash(0, 0, 0);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       __syncthreads();
       if (kb + NSET < NKB) issue(kb % NSET, kb + NSET);
       compute(kb & 1);
-      if (kb + 1 < NKB) stash((kb + 1) % NSET, (kb + 1) & 1);
+      if (kb + 1 < NKB) stash((kb + 1) % NSET, (kb + 1) & 1, kb + 1);
     }
   } else {
     issue(0, 0);
-    stash(0, 0);
+    stash(0, 0, 0);
     for (int kb = 0; kb < nkb; ++kb) {
       __syncthreads();
       const int cur = kb & 1;
       const bool more = kb + 1 < nkb;
       if (more) issue(0, kb + 1);
       compute(cur);
-      if (more) stash(0, cur ^ 1);
+      if (more) stash(0, cur ^ 1, kb + 1);
     }
   }
 
