@@ -236,8 +236,9 @@ typedef struct {
   const uint16_t* w_sgate;  /* [H] bf16 (NULL iff Is == 0) */
 } moe_weights_mx;
 
-/* Forward with block-scaled FP8 expert weights (the low-precision expert
- * weights named as follow-up work on the RL-Kernel 557 page's Stage 3).
+/* Forward with block-scaled FP8 expert weights (the MXFP8 item of the
+ * SkyRL pull request 2513 page's progress list, Stage 3: performance and
+ * quantization, follow-up).
  * Same contract, kernels and per-element arithmetic as moe_forward with
  * each expert weight replaced by its represented value: the expert GEMMs
  * expand every 16 codes to bf16 with the gfx950 scaled conversion as they
