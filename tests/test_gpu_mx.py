@@ -16,6 +16,7 @@ import torch
 
 import mixture_experts_layer_counting_amd as m
 import oracle as O
+import workloads as W
 import workloads.mx as MX
 from tests.gpu_util import (DEV, check_forward, dev_bits, dev_f32, dev_weights, dims_of, gpu_forward,
                             load_cfg, say)
@@ -68,9 +69,25 @@ def gpu_forward_mx(cfg, wm, x_dev):
                 out32=h(out32), out16=h(out16).view(np.uint16))
 
 
-@pytest.mark.parametrize("name", ["tiny", "moe1k"])
+EDGE = {
+    # no shared expert, expert count not a multiple of 128, ragged tokens
+    "edge_noshared": dict(tokens=100, hidden=256, experts=192, top_k=6, inter=128, shared_inter=0),
+    # the unrolled kernels (H = 2048, I = 512) with a single token
+    "edge_t1": dict(tokens=1, hidden=2048, experts=64, top_k=10, inter=512, shared_inter=512),
+}
+
+
+def load_any(name):
+    if name in EDGE:
+        cfg = W.MoEConfig(name=name, **EDGE[name])
+        return cfg, W.make_layer(cfg), W.tokens(cfg)
+    return load_cfg(name)
+
+
+# moe8k also runs the 96-row up-projection items
+@pytest.mark.parametrize("name", ["tiny", "moe1k", "moe8k", "edge_noshared", "edge_t1"])
 def test_mx_forward_equals_bf16_forward_on_represented_weights(name):
-    cfg, layer, x = load_cfg(name)
+    cfg, layer, x = load_any(name)
     say(f"case: {name}, encoding the expert weights to MX")
     mxl = MX.mx_layer(layer)
     rep = dict(layer)
@@ -84,8 +101,11 @@ def test_mx_forward_equals_bf16_forward_on_represented_weights(name):
     for k in ("idx", "sorted_route", "offsets"):
         assert np.array_equal(g_mx[k], g_bf[k]), k
     for k in ("gates", "y", "out32", "s"):
+        if g_bf[k] is None:          # no shared expert
+            assert g_mx[k] is None
+            continue
         assert np.array_equal(g_mx[k].view(np.uint32), g_bf[k].view(np.uint32)), k
     assert np.array_equal(g_mx["out16"], g_bf["out16"])
-    if name == "tiny":
+    if name in ("tiny", "edge_noshared", "edge_t1"):
         say("  oracle on the represented weights, all tokens")
         check_forward(cfg, rep, x, g_mx)
