@@ -10,9 +10,11 @@ from .moe_oracle import (  # noqa: F401
     combine,
     e4m3_to_f64,
     e8m0_to_f64,
+    expert_lora_rank,
     expert_weight_grads,
     f64_to_bf16_bits,
     forward,
+    lora_delta,
     mx_to_f64,
     permute_routes,
     route_gates,

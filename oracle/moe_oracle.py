@@ -28,7 +28,12 @@ design notes):
     router precision), stable descending, ties to the lower expert id; the
     gates themselves are computed from the exact logits;
   * inside an expert's segment routes keep ascending route id
-    (r = token * top_k + slot).
+    (r = token * top_k + slot);
+  * LoRA adapters (ROLL pull request 502 page: grouped expert LoRA of rank
+    r // top_k, deterministic shrink) attach to the routed experts' two
+    projections only, with the textbook update scale * B (A v); the scale
+    is an input (the pages do not say whether alpha is divided by r or by
+    the expert rank).
 
 Parity pins: every public function here is pinned by tests/test_oracle_pins.py
 against brute force, closed forms, special cases, finite differences or an
@@ -159,26 +164,52 @@ def permute_routes(idx, experts: int):
     return offsets, sorted_route, route_pos
 
 
-def swiglu_expert(xrows, w13_bits, w2_bits):
+def expert_lora_rank(r: int, top_k: int) -> int:
+    """Rank of each routed expert's adapter for a LoRA of rank r (ROLL pull
+    request 502 page, "What this changes", grouped expert LoRA rank bullet:
+    the adapter rank is divided by the router's top-k, integer division)."""
+    return r // top_k
+
+
+def lora_delta(rows, a_bits, b_bits, scale: float):
+    """LoRA update of one linear map y = rows W^T on a block of rows:
+    scale * (rows A^T) B^T with A [rank, in] (the shrink) and B [out, rank]
+    (the expand), both bf16 bits (Hu et al., LoRA, section 4.1: h = W0 x +
+    B A x, scaled by alpha / r; the scale is the caller's)."""
+    a = bf16_to_f64(a_bits)
+    b = bf16_to_f64(b_bits)
+    return scale * ((rows @ a.T) @ b.T)
+
+
+def swiglu_expert(xrows, w13_bits, w2_bits, lora=None):
     """One SwiGLU expert on a block of rows (float64).
 
     gu = x W13^T (first I columns gate, last I up), act = silu(gate)*up,
-    y = act W2^T.  Returns (y, gu)."""
+    y = act W2^T.  `lora` = (a13, b13, a2, b2, scale) adds a LoRA update to
+    both projections: gu += scale (x A13^T) B13^T, y += scale (act A2^T)
+    B2^T.  Returns (y, gu)."""
     w13 = bf16_to_f64(w13_bits)
     w2 = bf16_to_f64(w2_bits)
     inter = w13.shape[0] // 2
     gu = xrows @ w13.T
+    if lora is not None:
+        gu = gu + lora_delta(xrows, lora[0], lora[1], lora[4])
     act = silu(gu[:, :inter]) * gu[:, inter:]
-    return act @ w2.T, gu
+    y = act @ w2.T
+    if lora is not None:
+        y = y + lora_delta(act, lora[2], lora[3], lora[4])
+    return y, gu
 
 
-def routed_rows(x_bits, idx, w13_bits, w2_bits, tokens=None):
+def routed_rows(x_bits, idx, w13_bits, w2_bits, tokens=None, lora=None):
     """Per-route expert outputs Y (route-major) and their gate/up values.
 
     Contract "Experts" bullet: each (token, route) row gets its own expert
     output, with no gate multiply and no sum inside the expert step.
     `tokens` restricts the work to a subset of tokens (rows are returned in
-    the order of that subset, K per token)."""
+    the order of that subset, K per token).  `lora` (dict: a13 [E,r,H],
+    b13 [E,2I,r], a2 [E,r,I], b2 [E,H,r] bf16 bits, scale) gives every
+    routed expert its own adapter."""
     T, K = idx.shape
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     x64 = bf16_to_f64(x_bits)
@@ -190,7 +221,9 @@ def routed_rows(x_bits, idx, w13_bits, w2_bits, tokens=None):
     gu = np.zeros((flat.size, n2I), F64)
     for e in np.unique(flat):
         rows = np.nonzero(flat == e)[0]
-        ye, gue = swiglu_expert(x64[tok[rows // K]], w13_bits[e], w2_bits[e])
+        ad = None if lora is None else (lora["a13"][e], lora["b13"][e], lora["a2"][e],
+                                        lora["b2"][e], float(lora["scale"]))
+        ye, gue = swiglu_expert(x64[tok[rows // K]], w13_bits[e], w2_bits[e], ad)
         y[rows] = ye
         gu[rows] = gue
     return y, gu
@@ -219,14 +252,16 @@ def combine(y, gates, s=None, sg=None) -> np.ndarray:
     return out
 
 
-def forward(layer: dict, x_bits, top_k: int = 10, tokens=None, forced_idx=None) -> dict:
+def forward(layer: dict, x_bits, top_k: int = 10, tokens=None, forced_idx=None,
+            lora=None) -> dict:
     """Whole forward pass in float64.
 
     layer: w_router [E,H] f32, router_bias [E] f32|None, w13 [E,2I,H] bf16,
     w2 [E,H,I] bf16, ws13/ws2/w_sgate bf16 or None.  `tokens` restricts the
     token-wise outputs to a subset; the permutation is returned only for the
     full batch.  `forced_idx` (full [T,K]) replaces the selection, as when
-    routes are replayed."""
+    routes are replayed.  `lora` adds per-expert LoRA adapters to the routed
+    experts (see routed_rows); the router and the shared expert have none."""
     T = x_bits.shape[0]
     E = layer["w_router"].shape[0]
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
@@ -236,7 +271,7 @@ def forward(layer: dict, x_bits, top_k: int = 10, tokens=None, forced_idx=None) 
     else:
         idx_sub = select_routes(logits, top_k)
     g = route_gates(logits, idx_sub)
-    y, gu = routed_rows(x_bits[tok], idx_sub, layer["w13"], layer["w2"])
+    y, gu = routed_rows(x_bits[tok], idx_sub, layer["w13"], layer["w2"], lora=lora)
     res = {"tokens": tok, "logits": logits, "idx": idx_sub, "gates": g, "y": y, "gu": gu}
     if layer.get("ws13") is not None:
         s, sg, sgu = shared_expert(x_bits[tok], layer["ws13"], layer["ws2"], layer["w_sgate"])

@@ -382,3 +382,103 @@ def test_mx_encoder_picks_the_nearest_representable_weight():
                     best = best[(best & 1) == 0]
                     best = best[np.signbit(O.e4m3_to_f64(best)) == np.signbit(y)] if len(best) > 1 else best
                 assert O.e4m3_to_f64(codes[r, 32 * b + i]) == O.e4m3_to_f64(best[0])
+
+
+# ---------------------------------------------------------------- LoRA adapters
+BF16_ONE = 0x3F80
+
+
+def lora_for(cfg, rank, scale=0.75):
+    import workloads.lora as WL
+    return WL.lora_adapters(cfg, rank, scale)
+
+
+def test_expert_lora_rank_matches_the_pages():
+    """ROLL pull request 502 page, "What this changes": an adapter of rank
+    64 over a top-10 router gives rank-6 expert adapters."""
+    assert O.expert_lora_rank(64, 10) == 6
+
+
+def test_lora_with_zero_expand_is_the_base_layer():
+    cfg = small_cfg()
+    layer, x = layer_and_x(cfg)
+    ad = lora_for(cfg, 3)
+    ad["b13"][:] = 0
+    ad["b2"][:] = 0
+    base = O.forward(layer, x, cfg.top_k)
+    lo = O.forward(layer, x, cfg.top_k, lora=ad)
+    for key in ("y", "gu", "out"):
+        assert np.array_equal(base[key], lo[key])
+
+
+def test_lora_equals_the_merged_weight_layer():
+    """LoRA's defining identity W x + s B (A x) = (W + s B A) x, route by
+    route: the merged weights (float64, no longer bf16) go through a plain
+    per-route SwiGLU written here."""
+    cfg = small_cfg()
+    layer, x = layer_and_x(cfg)
+    ad = lora_for(cfg, 3)
+    s = ad["scale"]
+    fwd = O.forward(layer, x, cfg.top_k, lora=ad)
+    bf = O.bf16_to_f64
+    x64 = bf(x)
+    I, K = cfg.inter, cfg.top_k
+    merged = {}
+    for t in range(cfg.tokens):
+        for k in range(K):
+            e = int(fwd["idx"][t, k])
+            if e not in merged:
+                merged[e] = (bf(layer["w13"][e]) + s * bf(ad["b13"][e]) @ bf(ad["a13"][e]),
+                             bf(layer["w2"][e]) + s * bf(ad["b2"][e]) @ bf(ad["a2"][e]))
+            w13, w2 = merged[e]
+            gu = w13 @ x64[t]
+            act = gu[:I] / (1.0 + np.exp(-gu[:I])) * gu[I:]
+            y = w2 @ act
+            r = t * K + k
+            assert np.max(np.abs(gu - fwd["gu"][r])) <= 1e-12
+            assert np.max(np.abs(y - fwd["y"][r])) <= 1e-12
+    # the update is not negligible at these magnitudes
+    base = O.forward(layer, x, cfg.top_k)
+    assert np.max(np.abs(base["y"] - fwd["y"])) > 1e-4
+
+
+def test_lora_one_hot_up_adapter_moves_one_gate_up_column():
+    """Rank 1, A13 one-hot at input feature h0, B13 one-hot at gate/up
+    column c0: only gu[:, c0] changes, by scale * x[token, h0].  A
+    transposed factor, a wrong axis or a misplaced scale fails this."""
+    cfg = small_cfg()
+    layer, x = layer_and_x(cfg)
+    E, H, I, K = cfg.experts, cfg.hidden, cfg.inter, cfg.top_k
+    h0, c0, s = 5, I + 7, 0.75
+    ad = {"a13": np.zeros((E, 1, H), np.uint16), "b13": np.zeros((E, 2 * I, 1), np.uint16),
+          "a2": np.zeros((E, 1, I), np.uint16), "b2": np.zeros((E, H, 1), np.uint16), "scale": s}
+    ad["a13"][:, 0, h0] = BF16_ONE
+    ad["b13"][:, c0, 0] = BF16_ONE
+    base = O.forward(layer, x, K)
+    lo = O.forward(layer, x, K, lora=ad)
+    d = lo["gu"] - base["gu"]
+    want = s * O.bf16_to_f64(x)[np.repeat(np.arange(cfg.tokens), K), h0]
+    assert np.max(np.abs(d[:, c0] - want)) <= 1e-15
+    assert not np.any(np.delete(d, c0, axis=1))
+
+
+def test_lora_one_hot_down_adapter_moves_one_hidden_column():
+    """Rank 1, A2 one-hot at activation column i0, B2 one-hot at hidden
+    column h1: only y[:, h1] changes, by scale * act[:, i0] (act from the
+    unchanged gate/up values)."""
+    cfg = small_cfg()
+    layer, x = layer_and_x(cfg)
+    E, H, I, K = cfg.experts, cfg.hidden, cfg.inter, cfg.top_k
+    i0, h1, s = 3, 11, 0.75
+    ad = {"a13": np.zeros((E, 1, H), np.uint16), "b13": np.zeros((E, 2 * I, 1), np.uint16),
+          "a2": np.zeros((E, 1, I), np.uint16), "b2": np.zeros((E, H, 1), np.uint16), "scale": s}
+    ad["a2"][:, 0, i0] = BF16_ONE
+    ad["b2"][:, h1, 0] = BF16_ONE
+    base = O.forward(layer, x, K)
+    lo = O.forward(layer, x, K, lora=ad)
+    assert np.array_equal(lo["gu"], base["gu"])
+    gu = base["gu"]
+    act = gu[:, :I] / (1.0 + np.exp(-gu[:, :I])) * gu[:, I:]
+    d = lo["y"] - base["y"]
+    assert np.max(np.abs(d[:, h1] - s * act[:, i0])) <= 1e-15
+    assert not np.any(np.delete(d, h1, axis=1))
