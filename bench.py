@@ -318,6 +318,49 @@ def run_mx(cfg, layer, steps, warmup):
             "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9)}
 
 
+def run_lora(cfg, w, steps, warmup):
+    """The forward with LoRA adapters on every routed expert (seeded, rank
+    64 // 10 = 6), HIP-event timed on the kernels' stream over `steps`
+    forwards, with the plain forward timed the same way beside it."""
+    import torch
+    import mixture_experts_layer_counting_amd as m
+    import workloads as W
+    import workloads.lora as WL
+    dev = torch.device("cuda:0")
+    ad = WL.lora_adapters(cfg)
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    lo = m.Lora(rank=ad["rank"], scale=ad["scale"], a13=bits(ad["a13"]), b13=bits(ad["b13"]),
+                a2=bits(ad["a2"]), b2=bits(ad["b2"]))
+    x = torch.from_numpy(W.tokens(cfg).view(np.int16)).to(dev)
+    d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
+    routes = m.alloc_routes(d, dev, logits=False)
+    saved = m.alloc_saved(d, dev)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD_LORA, dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(lambda: m.check(m.moe_forward_lora(d, w, lo, x, routes, saved, None, out16, ws, stream),
+                               "moe_forward_lora"))
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+    ms_plain = timed(lambda: m.check(m.moe_forward(d, w, x, routes, saved, None, out16, ws, stream),
+                                     "moe_forward"))
+    return {"workload": f"{cfg.name}: {cfg.tokens} tokens, LoRA adapters of rank {ad['rank']} on all "
+                        f"{cfg.experts} routed experts", "ms": ms, "tokens_per_s": cfg.tokens / (ms / 1e3),
+            "plain_forward_ms": ms_plain, "adapter_bytes": sum(int(ad[k].nbytes) for k in ("a13", "b13", "a2", "b2"))}
+
+
 def run_backward(cfg, steps, warmup):
     """Forward (training mode) once, then `steps` timed backward passes of
     the same batch (HIP-event timed on the kernels' stream)."""
@@ -401,6 +444,8 @@ def main():
                     help="also time the grouped FFN on one GPU's share of this many expert-parallel GPUs (0: off)")
     ap.add_argument("--mx", type=int, default=1,
                     help="also time the forward with block-scaled FP8 expert weights (0: off)")
+    ap.add_argument("--lora", type=int, default=1,
+                    help="also time the forward with LoRA adapters on the routed experts (0: off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -456,6 +501,12 @@ def main():
         mx = run_mx(cfg, layer, args.steps, args.warmup)
         log(f"bench: {cfg.name} mx {mx['ms']:.3f} ms/step")
 
+    lora = None
+    if args.lora:
+        log(f"bench: {cfg.name} with LoRA adapters")
+        lora = run_lora(cfg, w, args.steps, args.warmup)
+        log(f"bench: {cfg.name} lora {lora['ms']:.3f} ms/step (plain {lora['plain_forward_ms']:.3f})")
+
     backward = None
     if args.backward != "none":
         log(f"bench: backward {args.backward}")
@@ -498,6 +549,7 @@ def main():
         "secondary": secondary,
         "ep_share": ep_share,
         "mx_weights": mx,
+        "lora": lora,
         "backward": backward,
     }
     print(json.dumps(line), flush=True)

@@ -80,7 +80,8 @@ enum moe_op {
   MOE_OP_PERMUTE = 1,
   MOE_OP_FFN = 2,
   MOE_OP_FORWARD = 3,
-  MOE_OP_BACKWARD = 4
+  MOE_OP_BACKWARD = 4,
+  MOE_OP_FORWARD_LORA = 5
 };
 
 typedef struct moe_dims {
@@ -248,6 +249,45 @@ typedef struct {
 int moe_forward_mx(const moe_dims* dims, const moe_weights_mx* w, const uint16_t* x,
                    moe_routes* routes, moe_saved* saved, float* out_f32, uint16_t* out_bf16,
                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* LoRA adapters of the routed experts (ROLL pull request 502 page,
+ * Qwen3.8-Flash-Next adapter: grouped expert adapters of rank r // top_k,
+ * "What this changes"; the adapters' shrink with a single K partition, no
+ * fp32 atomics, opening summary).  Expert e's two projections get the
+ * update scale * B (A v) (LoRA, Hu et al., section 4.1, with the caller's
+ * scale, e.g. alpha / r):
+ *   gate/up:  gu_r += scale * B13_e (A13_e x_t)
+ *   down:     y_r  += scale * B2_e (A2_e act_r)
+ * All matrices bf16, row-major, caller-owned, 16-byte aligned:
+ *   a13 [E][rank][H], b13 [E][2I][rank], a2 [E][rank][I], b2 [E][H][rank].
+ * 1 <= rank <= 16.  The shared expert and the router have no adapter. */
+typedef struct {
+  int32_t rank;
+  float scale;
+  const uint16_t* a13;
+  const uint16_t* b13;
+  const uint16_t* a2;
+  const uint16_t* b2;
+} moe_lora;
+
+/* Forward of the layer whose routed experts carry LoRA adapters.  Kernels
+ * and per-element arithmetic of moe_forward, plus two shrink kernels and
+ * the expand inside the grouped GEMMs' epilogues:
+ *   z[p][j] = sum_k A_e[j][k] v_p[k] (fp32, one wave per row p, lane-strided
+ *            ascending pieces, then a fixed 64-lane butterfly), v_p = x_t for
+ *            the gate/up adapter, act_r (its exact bf16 hi + lo) for down;
+ *   gate/up (and y) += scale * (fp32 fma chain over ascending j of z[p][j] *
+ *            B[col][j]), one fma into the GEMM accumulator, before the
+ *            SwiGLU (and before y is stored).
+ * So every route row is a function of its own data only (batch invariant,
+ * deterministic, no atomics).  saved->gu, if given, receives the gate/up
+ * values with the update; moe_backward does not take adapters.  Workspace:
+ * moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA).  Errors as moe_forward,
+ * plus MOE_E_NULL for a missing adapter matrix and MOE_E_SHAPE for a rank
+ * outside 1..16. */
+int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,
+                     const uint16_t* x, moe_routes* routes, moe_saved* saved, float* out_f32,
+                     uint16_t* out_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Profiling variant of moe_forward: the same kernels in the same order on
  * `stream`, with events[i] recorded just before kernel i and events[n] after

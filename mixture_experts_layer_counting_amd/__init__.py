@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 
 MOE_OK, MOE_E_NULL, MOE_E_SHAPE, MOE_E_UNSUPPORTED, MOE_E_ALIGN = 0, 1, 2, 3, 4
 MOE_E_WORKSPACE, MOE_E_DEVICE, MOE_E_LAUNCH, MOE_E_ALIAS = 5, 6, 7, 8
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_BACKWARD = range(5)
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_BACKWARD, MOE_OP_FORWARD_LORA = range(6)
 ABI_VERSION = 1
 
 
@@ -47,6 +47,11 @@ class MoeWeightsMx(ctypes.Structure):
                                    "ws13_s", "ws2_q", "ws2_s", "w_sgate")]
 
 
+class MoeLora(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("scale", ctypes.c_float)] + \
+        [(n, _VP) for n in ("a13", "b13", "a2", "b2")]
+
+
 class MoeRoutes(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("topk_idx", "topk_gate", "logits", "expert_offsets", "sorted_route",
                                    "route_pos")]
@@ -62,7 +67,8 @@ class MoeGrads(ctypes.Structure):
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
-           "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx")
+           "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
+           "moe_forward_lora")
 
 _lib = None
 
@@ -96,6 +102,9 @@ def load_library():
     lib.moe_forward_mx.restype = ctypes.c_int
     lib.moe_forward_mx.argtypes = [P(MoeDims), P(MoeWeightsMx), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP,
                                    *ws]
+    lib.moe_forward_lora.restype = ctypes.c_int
+    lib.moe_forward_lora.argtypes = [P(MoeDims), P(MoeWeights), P(MoeLora), _VP, P(MoeRoutes), P(MoeSaved),
+                                     _VP, _VP, *ws]
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                  P(MoeGrads), *ws]
@@ -181,6 +190,22 @@ class WeightsMx:
 
     def c(self) -> MoeWeightsMx:
         return MoeWeightsMx(*(_ptr(getattr(self, n)) for n, _ in MoeWeightsMx._fields_))
+
+
+@dataclasses.dataclass
+class Lora:
+    """LoRA adapters of the routed experts (bf16 tensors): a13 [E,rank,H],
+    b13 [E,2I,rank], a2 [E,rank,I], b2 [E,H,rank]; the update's scale."""
+    rank: int
+    scale: float
+    a13: object
+    b13: object
+    a2: object
+    b2: object
+
+    def c(self) -> MoeLora:
+        return MoeLora(int(self.rank), float(self.scale), _ptr(self.a13), _ptr(self.b13), _ptr(self.a2),
+                       _ptr(self.b2))
 
 
 @dataclasses.dataclass
@@ -279,6 +304,14 @@ def moe_forward_mx(dims, weights_mx, x, routes, saved, out_f32, out_bf16, ws, st
     return load_library().moe_forward_mx(ctypes.byref(dims.c()), ctypes.byref(weights_mx.c()), _ptr(x),
                                          ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(out_f32),
                                          _ptr(out_bf16), p, n, _stream(stream))
+
+
+def moe_forward_lora(dims, weights, lora, x, routes, saved, out_f32, out_bf16, ws, stream=None) -> int:
+    p, n = _ws(ws)
+    return load_library().moe_forward_lora(ctypes.byref(dims.c()), ctypes.byref(weights.c()),
+                                           ctypes.byref(lora.c()), _ptr(x), ctypes.byref(routes.c()),
+                                           ctypes.byref(saved.c()), _ptr(out_f32), _ptr(out_bf16), p, n,
+                                           _stream(stream))
 
 
 def moe_backward(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, ws, stream=None) -> int:

@@ -58,8 +58,12 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // ring of NSET register sets of loads (blocks kb + 1 .. kb + NSET - 1 are in
 // flight while kb is multiplied); NKB = 0 is the general loop with one block
 // in flight (NSET = 1).  All run the same MFMA sequence on every element.
+// LORA adds a routed expert's adapter update to gate and up before the
+// SwiGLU: g += scale * sum_j z[p][j] B13[col][j], u likewise with row I + col
+// of B13, each sum an fp32 fma chain over ascending j from +0 (z: the rows'
+// shrink results).
 // ---------------------------------------------------------------------------
-template <int NKB, int NSET, int MBT, bool MX>
+template <int NKB, int NSET, int MBT, bool MX, bool LORA>
 __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
     const uint16_t* __restrict__ ws13, const int32_t* __restrict__ offsets,
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     const int32_t* __restrict__ ntiles, uint16_t* __restrict__ act_hi,
     uint16_t* __restrict__ act_lo, uint16_t* __restrict__ sact_hi,
     uint16_t* __restrict__ sact_lo, float* __restrict__ gu, float* __restrict__ sgu, const MxWeights mx,
-    int64_t T, int H, int E, int K, int I, int Is, int ncol_tiles) {
+    const LoraExpand lx, int64_t T, int H, int E, int K, int I, int Is, int ncol_tiles) {
   constexpr int ROWS = 32 * MBT;  // rows of a work item
   const int item = xcd_item(blockIdx.x, ntiles[0] * ncol_tiles);
   if (item < 0) return;
@@ -86,10 +90,21 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[4][64 * 64];
   __shared__ int s_tok[ROWS];
+  __shared__ __attribute__((aligned(16))) float zs[LORA ? ROWS * kLoraMaxRank : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, half = lane >> 5;
   const int64_t R = T * K;
+  const bool lora = LORA && !shared;  // the shared expert has no adapter
+  if (lora) {
+    // the item's rows of shrink results, 16-byte pieces (ordered before the
+    // epilogue by the K loop's barriers)
+    for (int i = tid; i < ROWS * kLoraMaxRank / 4; i += 256) {
+      const int r = i / (kLoraMaxRank / 4);
+      if (r < rows)
+        st16(&zs[4 * i], ld16(lx.z + (static_cast<int64_t>(seg0) + row0) * kLoraMaxRank + 4 * i));
+    }
+  }
 
   // rows past the tile's end repeat its last row (loaded, never used)
   if (tid < ROWS) {
@@ -249,6 +264,17 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   uint16_t* olo = shared ? sact_lo : act_lo;
   float* ogu = shared ? sgu : gu;
   const int64_t p0 = shared ? row0 : static_cast<int64_t>(seg0) + row0;
+  // this lane's expand rows: B13[col][0..rank) (gate), B13[I + col][..] (up)
+  float lbg[kLoraMaxRank], lbu[kLoraMaxRank];
+  if constexpr (LORA) {
+    const uint16_t* bg = lx.b + (static_cast<int64_t>(grp) * 2 * I + col) * lx.rank;
+    const uint16_t* bu = bg + static_cast<int64_t>(I) * lx.rank;
+#pragma unroll
+    for (int jj = 0; jj < kLoraMaxRank; ++jj) {
+      lbg[jj] = lora && jj < lx.rank ? bf16_to_f32(bg[jj]) : 0.f;
+      lbu[jj] = lora && jj < lx.rank ? bf16_to_f32(bu[jj]) : 0.f;
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < MBT; ++mb) {
     if (mb < nmb) {
@@ -256,7 +282,22 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
       for (int v = 0; v < 16; ++v) {
         const int row = mb * 32 + acc_row(v, half);
         if (row < rows) {
-          const float g = accg[mb][v], u = accu[mb][v];
+          float g = accg[mb][v], u = accu[mb][v];
+          if constexpr (LORA) {
+            if (lora) {
+              float tg = 0.f, tu = 0.f;
+#pragma unroll
+              for (int jj = 0; jj < kLoraMaxRank; ++jj) {
+                if (jj < lx.rank) {
+                  const float zv = zs[row * kLoraMaxRank + jj];
+                  tg = fmaf(zv, lbg[jj], tg);
+                  tu = fmaf(zv, lbu[jj], tu);
+                }
+              }
+              g = fmaf(lx.scale, tg, g);
+              u = fmaf(lx.scale, tu, u);
+            }
+          }
           const float a = silu_f32(g) * u;
           uint16_t hi, lo;
           split_hi_lo(a, hi, lo);
@@ -286,15 +327,19 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 // ring of NSET register sets of loads (blocks kb + 1 .. kb + NSET - 1 in
 // flight while kb is multiplied); NKB = 0 is the general loop with one block
 // in flight (NSET = 1).  All run the same MFMA sequence on every element.
+// LORA adds a routed expert's adapter update to every element before it is
+// stored: y += scale * sum_j z[p][j] B2[col][j], an fp32 fma chain over
+// ascending j from +0 (z: the rows' shrink results).
 // ---------------------------------------------------------------------------
-template <int NKB, int NSET, int NBW, bool MX>
+template <int NKB, int NSET, int NBW, bool MX, bool LORA>
 __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     const uint16_t* __restrict__ act_hi, const uint16_t* __restrict__ act_lo,
     const uint16_t* __restrict__ sact_hi, const uint16_t* __restrict__ sact_lo,
     const uint16_t* __restrict__ w2, const uint16_t* __restrict__ ws2,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_route,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ meta, float* __restrict__ y,
-    float* __restrict__ sy, const MxWeights mx, int64_t T, int H, int E, int K, int I, int Is) {
+    float* __restrict__ sy, const MxWeights mx, const LoraExpand lx, int64_t T, int H, int E, int K,
+    int I, int Is) {
   constexpr int COLS = kDownCols * NBW;  // hidden columns of a work item
   constexpr int WROWS = 32 * NBW;        // W2 rows (hidden columns) of a wave
   const int ncol_tiles = H / COLS;
@@ -320,12 +365,22 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   static_assert((kAsElems + kBsElems) * 2 >= kRowsPerTile * COLS * 4, "the epilogue tile fits");
   __shared__ __attribute__((aligned(16))) uint16_t smem[kAsElems + kBsElems];
   __shared__ int s_dst[kRowsPerTile];
+  __shared__ __attribute__((aligned(16))) float zs[LORA ? kRowsPerTile * kLoraMaxRank : 4];
   auto As = [&](int buf, int plane) { return smem + (buf * 2 + plane) * kRowsPerTile * 64; };
   uint16_t* const Bw = smem + kAsElems + (threadIdx.x >> 6) * WROWS * 64;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, half = lane >> 5;
   const int64_t R = T * K;
+  const bool lora = LORA && !shared;  // the shared expert has no adapter
+  if (lora) {
+    // the item's rows of shrink results (ordered before the epilogue by the
+    // K loop's barriers)
+    for (int i = tid; i < kRowsPerTile * kLoraMaxRank / 4; i += 256) {
+      const int r = i / (kLoraMaxRank / 4);
+      if (r < rows) st16(&zs[4 * i], ld16(lx.z + p0 * kLoraMaxRank + 4 * i));
+    }
+  }
 
   if (tid < kRowsPerTile) {
     int dst = -1;
@@ -476,6 +531,32 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
 
   // Epilogue: the 64 x COLS fp32 tile is staged in LDS and each route row
   // goes out as 16-byte pieces, COLS * 4 contiguous bytes per row.
+  if constexpr (LORA) {
+    if (lora) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        // this lane's expand row B2[col][0..rank)
+        const uint16_t* b = lx.b + (static_cast<int64_t>(grp) * H + n0 + 32 * nb + j) * lx.rank;
+        float lb[kLoraMaxRank];
+#pragma unroll
+        for (int jj = 0; jj < kLoraMaxRank; ++jj) lb[jj] = jj < lx.rank ? bf16_to_f32(b[jj]) : 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if (mb < nmb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int row = mb * 32 + acc_row(v, half);
+              float t = 0.f;
+#pragma unroll
+              for (int jj = 0; jj < kLoraMaxRank; ++jj)
+                if (jj < lx.rank) t = fmaf(zs[row * kLoraMaxRank + jj], lb[jj], t);
+              acc[mb][nb][v] = fmaf(lx.scale, t, acc[mb][nb][v]);
+            }
+          }
+        }
+      }
+    }
+  }
   __syncthreads();  // every wave is done with the operand areas
   float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -589,25 +670,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 namespace moe {
 
 hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t* ws13,
-                         const MxWeights* mx, const int32_t* offsets, const int32_t* sorted_route,
-                         const int32_t* tiles, const int32_t* ntiles, int up_rows, uint16_t* act_hi,
-                         uint16_t* act_lo, uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu,
-                         int64_t T, int H, int E, int K, int I, int Is, int max_tiles,
-                         hipStream_t stream) {
+                         const MxWeights* mx, const LoraExpand* lora, const int32_t* offsets,
+                         const int32_t* sorted_route, const int32_t* tiles, const int32_t* ntiles,
+                         int up_rows, uint16_t* act_hi, uint16_t* act_lo, uint16_t* sact_hi,
+                         uint16_t* sact_lo, float* gu, float* sgu, int64_t T, int H, int E, int K,
+                         int I, int Is, int max_tiles, hipStream_t stream) {
   const int ncol = (I > Is ? I : Is) / kUpCols;
   const int64_t items = static_cast<int64_t>(max_tiles) * ncol;
   const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);
   const MxWeights m = mx ? *mx : MxWeights{nullptr, nullptr, nullptr, nullptr};
-#define MOE_UP(NKB, NSET, MBT)                                                                        \
-  do {                                                                                              \
-    if (mx)                                                                                         \
-      ffn_up_kernel<NKB, NSET, MBT, true><<<grid, 256, 0, stream>>>(                                \
-          x, w13, ws13, offsets, sorted_route, tiles, ntiles, act_hi, act_lo, sact_hi, sact_lo, gu, \
-          sgu, m, T, H, E, K, I, Is, ncol);                                                         \
-    else                                                                                            \
-      ffn_up_kernel<NKB, NSET, MBT, false><<<grid, 256, 0, stream>>>(                               \
-          x, w13, ws13, offsets, sorted_route, tiles, ntiles, act_hi, act_lo, sact_hi, sact_lo, gu, \
-          sgu, m, T, H, E, K, I, Is, ncol);                                                         \
+  const LoraExpand lx = lora ? *lora : LoraExpand{nullptr, nullptr, 0.f, 0};
+#define MOE_UP_ONE(NKB, NSET, MBT, MX, LORA)                                                          \
+  ffn_up_kernel<NKB, NSET, MBT, MX, LORA><<<grid, 256, 0, stream>>>(                                 \
+      x, w13, ws13, offsets, sorted_route, tiles, ntiles, act_hi, act_lo, sact_hi, sact_lo, gu, sgu, \
+      m, lx, T, H, E, K, I, Is, ncol)
+#define MOE_UP(NKB, NSET, MBT)                      \
+  do {                                              \
+    if (mx)                                         \
+      MOE_UP_ONE(NKB, NSET, MBT, true, false);      \
+    else if (lora)                                  \
+      MOE_UP_ONE(NKB, NSET, MBT, false, true);      \
+    else                                            \
+      MOE_UP_ONE(NKB, NSET, MBT, false, false);     \
   } while (0)
   // the unrolled instantiations cover hidden size 2048 (64- and 96-row items)
   if (H == 2048 && up_rows == kUpTallRows)
@@ -617,28 +701,33 @@ hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t*
   else
     MOE_UP(0, 1, kRowsPerTile / 32);
 #undef MOE_UP
+#undef MOE_UP_ONE
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
                            const uint16_t* sact_hi, const uint16_t* sact_lo, const uint16_t* w2,
-                           const uint16_t* ws2, const MxWeights* mx, const int32_t* offsets,
-                           const int32_t* sorted_route, const int32_t* tiles,
-                           const int32_t* meta, float* y, float* sy, int64_t T, int H, int E,
-                           int K, int I, int Is, int max_tiles, hipStream_t stream) {
+                           const uint16_t* ws2, const MxWeights* mx, const LoraExpand* lora,
+                           const int32_t* offsets, const int32_t* sorted_route,
+                           const int32_t* tiles, const int32_t* meta, float* y, float* sy,
+                           int64_t T, int H, int E, int K, int I, int Is, int max_tiles,
+                           hipStream_t stream) {
   const MxWeights m = mx ? *mx : MxWeights{nullptr, nullptr, nullptr, nullptr};
-#define MOE_DOWN(NKB, NSET, NBW, COLS)                                                                \
-  do {                                                                                              \
-    const int64_t items = static_cast<int64_t>(max_tiles) * (H / (COLS));                           \
-    const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);                             \
-    if (mx)                                                                                         \
-      ffn_down_kernel<NKB, NSET, NBW, true><<<grid, 256, 0, stream>>>(                              \
-          act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets, sorted_route, tiles, meta, y, sy, m,  \
-          T, H, E, K, I, Is);                                                                       \
-    else                                                                                            \
-      ffn_down_kernel<NKB, NSET, NBW, false><<<grid, 256, 0, stream>>>(                             \
-          act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets, sorted_route, tiles, meta, y, sy, m,  \
-          T, H, E, K, I, Is);                                                                       \
+  const LoraExpand lx = lora ? *lora : LoraExpand{nullptr, nullptr, 0.f, 0};
+#define MOE_DOWN_ONE(NKB, NSET, NBW, MX, LORA)                                                       \
+  ffn_down_kernel<NKB, NSET, NBW, MX, LORA><<<grid, 256, 0, stream>>>(                              \
+      act_hi, act_lo, sact_hi, sact_lo, w2, ws2, offsets, sorted_route, tiles, meta, y, sy, m, lx, \
+      T, H, E, K, I, Is)
+#define MOE_DOWN(NKB, NSET, NBW, COLS)                                                  \
+  do {                                                                                \
+    const int64_t items = static_cast<int64_t>(max_tiles) * (H / (COLS));             \
+    const unsigned grid = static_cast<unsigned>(((items + 7) / 8) * 8);               \
+    if (mx)                                                                           \
+      MOE_DOWN_ONE(NKB, NSET, NBW, true, false);                                      \
+    else if (lora)                                                                    \
+      MOE_DOWN_ONE(NKB, NSET, NBW, false, true);                                      \
+    else                                                                              \
+      MOE_DOWN_ONE(NKB, NSET, NBW, false, false);                                     \
   } while (0)
   // the unrolled instantiation covers expert and shared sizes of 512 (and
   // takes 256-column items when H allows); the general one 128 columns
@@ -647,6 +736,7 @@ hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
   else
     MOE_DOWN(0, 1, 1, kDownCols);
 #undef MOE_DOWN
+#undef MOE_DOWN_ONE
   return hipGetLastError();
 }
 

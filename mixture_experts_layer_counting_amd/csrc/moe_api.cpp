@@ -33,7 +33,10 @@ struct Layout {
   size_t act_hi = 0, act_lo = 0;    // [R][I] bf16
   size_t sact_hi = 0, sact_lo = 0;  // [T][Is] bf16
   size_t fwd_end = 0;
-  // backward regions (after fwd_end)
+  // LoRA shrink results (moe_forward_lora): [R][kLoraMaxRank] f32 each
+  size_t lora_z13 = 0, lora_z2 = 0;
+  size_t lora_end = 0;
+  // backward regions (after lora_end)
   size_t tiles_bwd = 0, meta_bwd = 0;  // work list of the backward's row tiles
   size_t dl = 0, dz = 0;             // [T][K], [T] f32
   size_t dgu[moe::kGradPlanes] = {};    // [R][2I] bf16 planes (hi, lo)
@@ -78,6 +81,9 @@ Layout make_layout(const moe_dims& d) {
   L.sact_hi = take(static_cast<size_t>(T) * Is * 2);
   L.sact_lo = take(static_cast<size_t>(T) * Is * 2);
   L.fwd_end = o;
+  L.lora_z13 = take(static_cast<size_t>(R) * moe::kLoraMaxRank * 4);
+  L.lora_z2 = take(static_cast<size_t>(R) * moe::kLoraMaxRank * 4);
+  L.lora_end = o;
   const int64_t H = d.hidden;
   L.max_tiles_bwd = static_cast<int>(moe::max_row_tiles(T, d.top_k, E, Is > 0, moe::kBwdRowsPerTile));
   L.tiles_bwd = take(static_cast<size_t>(L.max_tiles_bwd) * 2 * 4);
@@ -290,9 +296,12 @@ int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hip
 // the shared-expert gate by run_route.
 // mx13 / mx2: block-scaled FP8 expert weights of the two projections (then
 // w's expert matrices are not read), or null.
+// lora: the routed experts' adapters (shrink kernels before each grouped
+// GEMM, expand in its epilogue), or null.
 int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const moe_routes* r,
             moe_saved* sv, void* ws, const Layout& L, bool whole_forward, hipStream_t s,
-            const moe::MxWeights* mx13 = nullptr, const moe::MxWeights* mx2 = nullptr) {
+            const moe::MxWeights* mx13 = nullptr, const moe::MxWeights* mx2 = nullptr,
+            const moe_lora* lora = nullptr) {
   const int has_shared = d.shared_inter > 0;
   if (!whole_forward)
     MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles), tiles_up_of(ws, L),
@@ -301,7 +310,17 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
   if (has_shared && !whole_forward)
     MOE_LAUNCH(moe::launch_shared_gate(x, w->w_sgate, sv->shared_gate, d.tokens, d.hidden, s));
   const bool own_up = tiles_up_of(ws, L) != nullptr;
-  MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, mx13, r->expert_offsets, r->sorted_route,
+  moe::LoraExpand e13{}, e2{};
+  if (lora) {
+    e13 = {lora->b13, at<float>(ws, L.lora_z13), lora->scale, lora->rank};
+    e2 = {lora->b2, at<float>(ws, L.lora_z2), lora->scale, lora->rank};
+    MOE_LAUNCH(moe::launch_lora_shrink(x, nullptr, lora->a13, r->expert_offsets, r->sorted_route,
+                                       at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta),
+                                       at<float>(ws, L.lora_z13), d.tokens, d.hidden, d.experts,
+                                       d.top_k, lora->rank, L.max_tiles, s));
+  }
+  MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, mx13, lora ? &e13 : nullptr,
+                                r->expert_offsets, r->sorted_route,
                                 own_up ? tiles_up_of(ws, L) : at<int32_t>(ws, L.tiles),
                                 at<int32_t>(ws, L.meta) + (own_up ? 2 : 0), L.up_rows,
                                 at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
@@ -309,9 +328,16 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
                                 has_shared ? sv->shared_gu : nullptr, d.tokens, d.hidden,
                                 d.experts, d.top_k, d.inter, d.shared_inter,
                                 own_up ? L.max_tiles_up : L.max_tiles, s));
+  if (lora)
+    MOE_LAUNCH(moe::launch_lora_shrink(at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
+                                       lora->a2, r->expert_offsets, r->sorted_route,
+                                       at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta),
+                                       at<float>(ws, L.lora_z2), d.tokens, d.inter, d.experts,
+                                       d.top_k, lora->rank, L.max_tiles, s));
   MOE_LAUNCH(moe::launch_ffn_down(at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
                                   at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), w->w2,
-                                  w->ws2, mx2, r->expert_offsets, r->sorted_route,
+                                  w->ws2, mx2, lora ? &e2 : nullptr, r->expert_offsets,
+                                  r->sorted_route,
                                   at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta), sv->y,
                                   has_shared ? sv->shared_y : nullptr, d.tokens, d.hidden,
                                   d.experts, d.top_k, d.inter, d.shared_inter, L.max_tiles, s));
@@ -386,6 +412,7 @@ size_t moe_workspace_bytes(const moe_dims* dims, int op) {
     case MOE_OP_PERMUTE:
     case MOE_OP_FFN:
     case MOE_OP_FORWARD: return L.fwd_end;
+    case MOE_OP_FORWARD_LORA: return L.lora_end;
     case MOE_OP_BACKWARD: return L.bwd_end;
     default: return 0;
   }
@@ -493,6 +520,41 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, m
                     stream));
   MOE_TRY(run_permute(d, routes, ws, L, stream));
   MOE_TRY(run_ffn(d, x, w, routes, saved, ws, L, true, stream));
+  return run_combine(d, routes, saved, out_f32, out_bf16, stream);
+}
+
+int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,
+                     const uint16_t* x, moe_routes* routes, moe_saved* saved, float* out_f32,
+                     uint16_t* out_bf16, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (!lora) return MOE_E_NULL;
+  if (lora->rank < 1 || lora->rank > moe::kLoraMaxRank) return MOE_E_SHAPE;
+  if (dims->tokens == 0) return MOE_OK;
+  if (!w || !routes || !saved) return MOE_E_NULL;
+  if (!out_f32 && !out_bf16) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, H = d.hidden, E = d.experts, I = d.inter, rk = lora->rank;
+  Args a;
+  a.in(x, bytes_x(d));
+  add_weights(a, d, w, true, true);
+  a.in(lora->a13, E * rk * H * 2);
+  a.in(lora->b13, E * 2 * I * rk * 2);
+  a.in(lora->a2, E * rk * I * 2);
+  a.in(lora->b2, E * H * rk * 2);
+  add_routes_out(a, d, routes);
+  add_perm_out(a, d, routes);
+  add_saved(a, d, saved, true);
+  a.out(out_f32, T * H * 4, false);
+  a.out(out_bf16, T * H * 2, false);
+  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD_LORA));
+  MOE_TRY(check_device());
+  const Layout L = make_layout(d);
+  MOE_TRY(run_route(d, x, w, routes, ws, L, d.shared_inter > 0 ? saved->shared_gate : nullptr,
+                    stream));
+  MOE_TRY(run_permute(d, routes, ws, L, stream));
+  MOE_TRY(run_ffn(d, x, w, routes, saved, ws, L, true, stream, nullptr, nullptr, lora));
   return run_combine(d, routes, saved, out_f32, out_bf16, stream);
 }
 

@@ -98,6 +98,19 @@ struct MxWeights {
   const uint8_t* ss;
 };
 
+// LoRA adapters of the routed experts: largest rank, and the fp32 stride of
+// a row of shrink results z (one 64-byte row per sorted route position).
+constexpr int kLoraMaxRank = 16;
+// The expand half of one projection's adapters as the grouped-GEMM
+// epilogue applies it: B [E][out][rank] bf16, the rows' shrink results z
+// [sorted position][kLoraMaxRank] fp32, the update's scale and the rank.
+struct LoraExpand {
+  const uint16_t* b;
+  const float* z;
+  float scale;
+  int rank;
+};
+
 // E8M0 scale code -> 2^(code - 127) as a float (code 0 is the denormal 2^-127).
 __device__ __forceinline__ float e8m0_scale(uint32_t code) {
   return __uint_as_float(code ? (code << 23) : 0x00400000u);

@@ -58,17 +58,25 @@ inline int up_rows_per_tile(int64_t T, int H) {
 // mx: block-scaled FP8 expert weights (then w13 / ws13 resp. w2 / ws2 are
 // not read), or null for bf16 weights.
 hipError_t launch_ffn_up(const uint16_t* x, const uint16_t* w13, const uint16_t* ws13,
-                         const MxWeights* mx, const int32_t* offsets, const int32_t* sorted_route,
-                         const int32_t* tiles, const int32_t* ntiles, int up_rows, uint16_t* act_hi,
-                         uint16_t* act_lo, uint16_t* sact_hi, uint16_t* sact_lo, float* gu, float* sgu,
-                         int64_t T, int H, int E, int K, int I, int Is, int max_tiles,
-                         hipStream_t stream);
+                         const MxWeights* mx, const LoraExpand* lora, const int32_t* offsets,
+                         const int32_t* sorted_route, const int32_t* tiles, const int32_t* ntiles,
+                         int up_rows, uint16_t* act_hi, uint16_t* act_lo, uint16_t* sact_hi,
+                         uint16_t* sact_lo, float* gu, float* sgu, int64_t T, int H, int E, int K,
+                         int I, int Is, int max_tiles, hipStream_t stream);
 hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
                            const uint16_t* sact_hi, const uint16_t* sact_lo, const uint16_t* w2,
-                           const uint16_t* ws2, const MxWeights* mx, const int32_t* offsets,
-                           const int32_t* sorted_route, const int32_t* tiles,
-                           const int32_t* meta, float* y, float* sy, int64_t T, int H, int E,
-                           int K, int I, int Is, int max_tiles, hipStream_t stream);
+                           const uint16_t* ws2, const MxWeights* mx, const LoraExpand* lora,
+                           const int32_t* offsets, const int32_t* sorted_route,
+                           const int32_t* tiles, const int32_t* meta, float* y, float* sy,
+                           int64_t T, int H, int E, int K, int I, int Is, int max_tiles,
+                           hipStream_t stream);
+// LoRA shrink of the routed experts' rows (lora_kernels.hip): z[p][j] =
+// sum_k A_e[j][k] v_p[k] over the 64-row work list `tiles` (meta[0] items);
+// v_p = x[token of route sorted_route[p]] (v_lo null) or v_hi[p] + v_lo[p].
+hipError_t launch_lora_shrink(const uint16_t* v_hi, const uint16_t* v_lo, const uint16_t* a,
+                              const int32_t* offsets, const int32_t* sorted_route,
+                              const int32_t* tiles, const int32_t* meta, float* z, int64_t T,
+                              int Kd, int E, int K, int rank, int max_tiles, hipStream_t stream);
 hipError_t launch_combine(const float* y, const float* gate, const float* sy, const float* sg,
                           float* out32, uint16_t* out16, int64_t T, int H, int K,
                           hipStream_t stream);

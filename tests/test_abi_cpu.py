@@ -162,3 +162,30 @@ def test_mx_forward_validation_fails_closed(lib):
     import torch
     if not torch.cuda.is_available():
         assert mx(d, wm) == m.MOE_E_DEVICE
+
+
+def test_lora_forward_validation_fails_closed(lib):
+    """moe_forward_lora checks the rank, every adapter matrix (presence,
+    alignment, overlap with outputs) and its larger workspace on the host
+    before anything is launched."""
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    E, H, I, rk = d.experts, d.hidden, d.inter, 6
+    lo = m.Lora(rank=rk, scale=0.5, a13=f(E * rk * H * 2), b13=f(E * 2 * I * rk * 2), a2=f(E * rk * I * 2),
+                b2=f(E * H * rk * 2))
+    nws = m.moe_workspace_bytes(d, m.MOE_OP_FORWARD_LORA)
+    assert nws > m.moe_workspace_bytes(d, m.MOE_OP_FORWARD)
+    wsl = (f(nws), nws)
+    call = lambda ll, wss=wsl, dd=d, ss=s: m.moe_forward_lora(dd, w, ll, x, r, ss, o32, o16, wss, stream=0)
+    assert call(m.Lora(**{**lo.__dict__, "rank": 0})) == m.MOE_E_SHAPE
+    assert call(m.Lora(**{**lo.__dict__, "rank": 17})) == m.MOE_E_SHAPE
+    assert call(m.Lora(**{**lo.__dict__, "b2": None})) == m.MOE_E_NULL
+    assert call(m.Lora(**{**lo.__dict__, "a13": lo.a13 + 2})) == m.MOE_E_ALIGN
+    # an adapter matrix that overlaps an output
+    assert call(m.Lora(**{**lo.__dict__, "a2": s.y})) == m.MOE_E_ALIAS
+    # a workspace sized for the plain forward is too small
+    assert call(lo, wss=ws) == m.MOE_E_WORKSPACE
+    assert call(lo, dd=m.Dims(0, 512, 512, 10, 128, 128)) == m.MOE_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert call(lo) == m.MOE_E_DEVICE

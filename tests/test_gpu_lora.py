@@ -1,0 +1,131 @@
+"""GPU parity of the forward with LoRA adapters on the routed experts.
+
+The adapters are seeded (workloads/lora.py: rank 6 = 64 // 10, scale 0.5,
+N(0, 0.02) factors, B nonzero).  Checks, through the C ABI:
+  * routes, gates, the gate/up values (which carry the gate/up update), the
+    route rows Y before combine (which carry the down update), S and out
+    against the FP64 oracle with the same adapters, at the forward's
+    tolerance, on every token of the small layers and on sampled tokens of
+    the 8192-token layer (96-row up-projection items);
+  * each route row is a function of its own token: a sub-batch gives the
+    same bits;
+  * adapters whose expand matrices are zero give moe_forward's bits;
+  * ranks 1 and 16, a layer without shared expert, a single token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_counting_amd as m
+import oracle as O
+import workloads as W
+import workloads.lora as WL
+from tests.gpu_util import (DEV, GpuForward, assert_close, bf16_rne_bits, check_permutation, compare_routes,
+                            dev_bits, dev_weights, dims_of, gpu_forward, load_cfg, say)
+
+pytestmark = pytest.mark.gpu
+
+EDGE = {
+    # no shared expert, expert count not a multiple of 128, ragged tokens
+    "edge_noshared": dict(tokens=100, hidden=256, experts=192, top_k=6, inter=128, shared_inter=0),
+    # the unrolled kernels (H = 2048, I = 512) with a single token
+    "edge_t1": dict(tokens=1, hidden=2048, experts=64, top_k=10, inter=512, shared_inter=512),
+}
+
+
+def load_any(name):
+    if name in EDGE:
+        cfg = W.MoEConfig(name=name, **EDGE[name])
+        return cfg, W.make_layer(cfg), W.tokens(cfg)
+    return load_cfg(name)
+
+
+def dev_lora(ad) -> m.Lora:
+    return m.Lora(rank=ad["rank"], scale=ad["scale"], a13=dev_bits(ad["a13"]), b13=dev_bits(ad["b13"]),
+                  a2=dev_bits(ad["a2"]), b2=dev_bits(ad["b2"]))
+
+
+def gpu_forward_lora(cfg, w, lo, x_dev, with_gu=True) -> dict:
+    d = dims_of(cfg, int(x_dev.shape[0]))
+    routes = m.alloc_routes(d, DEV)
+    saved = m.alloc_saved(d, DEV, training=with_gu)
+    out32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD_LORA, DEV)
+    m.check(m.moe_forward_lora(d, w, lo, x_dev, routes, saved, out32, out16, ws), "moe_forward_lora")
+    torch.cuda.synchronize()
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+    return GpuForward(routes, saved, out32, out16).host()
+
+
+def check_lora_forward(cfg, layer, ad, x, g, tokens=None):
+    K = cfg.top_k
+    tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
+    ref = O.forward(layer, x, K, tokens=tok, lora=ad)
+    ties = compare_routes(g["idx"][tok], ref["idx"], ref["logits"])
+    say(f"  routes: {len(tok)} tokens compared, {len(ties)} with fp32 ties")
+    if ties:
+        ref = O.forward(layer, x, K, tokens=tok, forced_idx=g["idx"], lora=ad)
+    if tokens is None:
+        check_permutation(g, cfg.experts)
+    rows = (tok[:, None] * K + np.arange(K)[None, :]).reshape(-1)
+    assert_close(g["gates"][tok], ref["gates"], "gates", atol=1e-6, rtol=1e-5)
+    if g["gu"] is not None:
+        assert_close(g["gu"][g["route_pos"][rows]], ref["gu"], "gate/up values (sorted rows)")
+    assert_close(g["y"][rows], ref["y"], "route rows Y")
+    if cfg.shared_inter:
+        assert_close(g["s"][tok], ref["s"], "shared expert S")
+    assert_close(g["out32"][tok], ref["out"], "out_f32")
+    assert np.array_equal(g["out16"], bf16_rne_bits(g["out32"])), "out_bf16 is not the RNE of out_f32"
+    # the update is visible at this tolerance: the plain layer is far off
+    base = O.forward(layer, x, K, tokens=tok, forced_idx=g["idx"])
+    assert np.max(np.abs(base["y"] - ref["y"])) > 1e-3
+
+
+@pytest.mark.parametrize("name,rank", [("tiny", 6), ("tiny", 1), ("tiny", 16), ("moe1k", 6),
+                                       ("edge_noshared", 6), ("edge_t1", 6)])
+def test_lora_forward_matches_oracle(name, rank):
+    cfg, layer, x = load_any(name)
+    ad = WL.lora_adapters(cfg, rank)
+    say(f"case: {name}, rank {rank}, moe_forward_lora vs oracle")
+    g = gpu_forward_lora(cfg, dev_weights(layer), dev_lora(ad), dev_bits(x))
+    tokens = None if cfg.tokens <= 256 else np.unique(np.r_[0:24, cfg.tokens - 24:cfg.tokens,
+                                                              np.linspace(0, cfg.tokens - 1, 16).astype(int)])
+    check_lora_forward(cfg, layer, ad, x, g, tokens)
+
+
+def test_lora_forward_8k_sampled_tokens():
+    cfg, layer, x = load_cfg("moe8k")
+    ad = WL.lora_adapters(cfg)
+    say("case: moe8k, rank 6, sampled tokens vs oracle (96-row up items)")
+    g = gpu_forward_lora(cfg, dev_weights(layer), dev_lora(ad), dev_bits(x), with_gu=False)
+    tok = np.unique(np.r_[0:8, cfg.tokens - 8:cfg.tokens, np.linspace(0, cfg.tokens - 1, 24).astype(int)])
+    check_lora_forward(cfg, layer, ad, x, g, tok)
+
+
+@pytest.mark.parametrize("name", ["tiny", "moe1k"])
+def test_lora_rows_do_not_depend_on_the_batch(name):
+    cfg, layer, x = load_cfg(name)
+    ad = WL.lora_adapters(cfg)
+    w, lo = dev_weights(layer), dev_lora(ad)
+    say(f"case: {name}, full batch vs a 37-token sub-batch")
+    full = gpu_forward_lora(cfg, w, lo, dev_bits(x), with_gu=False)
+    a, n = 5, 37
+    sub = gpu_forward_lora(cfg, w, lo, dev_bits(x[a:a + n]), with_gu=False)
+    K = cfg.top_k
+    assert np.array_equal(sub["idx"], full["idx"][a:a + n])
+    assert np.array_equal(sub["y"].view(np.uint32), full["y"][a * K:(a + n) * K].view(np.uint32))
+    assert np.array_equal(sub["out32"].view(np.uint32), full["out32"][a:a + n].view(np.uint32))
+
+
+def test_lora_with_zero_expand_gives_the_plain_forward():
+    cfg, layer, x = load_cfg("moe1k")
+    ad = WL.lora_adapters(cfg)
+    ad["b13"][:] = 0
+    ad["b2"][:] = 0
+    w, xd = dev_weights(layer), dev_bits(x)
+    say("case: moe1k, zero expand matrices vs moe_forward")
+    g = gpu_forward_lora(cfg, w, dev_lora(ad), xd, with_gu=False)
+    p = gpu_forward(cfg, w, xd).host()
+    for k in ("idx", "sorted_route", "y", "out32"):
+        assert np.array_equal(g[k].view(np.uint32), p[k].view(np.uint32)), k
