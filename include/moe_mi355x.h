@@ -283,8 +283,10 @@ typedef struct {
  * deterministic, no atomics).  saved->gu, if given, receives the gate/up
  * values with the update; moe_backward does not take adapters.  Workspace:
  * moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA).  Errors as moe_forward,
- * plus MOE_E_NULL for a missing adapter matrix and MOE_E_SHAPE for a rank
- * outside 1..16. */
+ * plus MOE_E_NULL for a missing adapter matrix, MOE_E_SHAPE for a rank
+ * outside 1..16 and MOE_E_UNSUPPORTED unless max(H, I) <= 2048 and
+ * rank * max(H, I) <= 28672 (the shrink holds an expert's A in LDS; hidden
+ * 2048 allows rank 14). */
 int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,
                      const uint16_t* x, moe_routes* routes, moe_saved* saved, float* out_f32,
                      uint16_t* out_bf16, void* ws, size_t ws_bytes, hipStream_t stream);

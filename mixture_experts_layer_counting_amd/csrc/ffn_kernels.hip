@@ -90,23 +90,24 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[4][64 * 64];
   __shared__ int s_tok[ROWS];
-  __shared__ __attribute__((aligned(16))) float zs[LORA ? ROWS * kLoraMaxRank : 4];
+  // the item's rows of shrink results (bf16 hi | lo) and its expand rows
+  // (gate columns, then up columns), kLoraMaxRank bf16 each
+  __shared__ __attribute__((aligned(16))) uint16_t zs[LORA ? ROWS * 2 * kLoraMaxRank : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lbs[LORA ? 2 * kUpCols * kLoraMaxRank : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, half = lane >> 5;
   const int64_t R = T * K;
   const bool lora = LORA && !shared;  // the shared expert has no adapter
   if (lora) {
-    // the item's rows of shrink results, 16-byte pieces (ordered before the
-    // epilogue by the K loop's barriers)
-    for (int i = tid; i < ROWS * kLoraMaxRank / 4; i += 256) {
-      const int r = i / (kLoraMaxRank / 4);
-      if (r < rows)
-        st16(&zs[4 * i], ld16(lx.z + (static_cast<int64_t>(seg0) + row0) * kLoraMaxRank + 4 * i));
-    }
+    // ordered before the epilogue by the K loop's barriers
+    for (int i = tid; i < rows * 4; i += 256)
+      st16(&zs[8 * i], ld16(lx.zq + (static_cast<int64_t>(seg0) + row0) * 2 * kLoraMaxRank + 8 * i));
+    const int64_t b0 = (static_cast<int64_t>(grp) * 2 * I + nt * kUpCols) * lx.rank;
+    lora_stage_b(lbs, lx.b + (tid < kUpCols ? b0 : b0 + static_cast<int64_t>(I - kUpCols) * lx.rank),
+                 2 * kUpCols, lx.rank, tid);
   }
 
-  // rows past the tile's end repeat its last row (loaded, never used)
   if (tid < ROWS) {
     const int rr = min(tid, rows - 1);
     int64_t tok;
@@ -264,40 +265,30 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   uint16_t* olo = shared ? sact_lo : act_lo;
   float* ogu = shared ? sgu : gu;
   const int64_t p0 = shared ? row0 : static_cast<int64_t>(seg0) + row0;
-  // this lane's expand rows: B13[col][0..rank) (gate), B13[I + col][..] (up)
-  float lbg[kLoraMaxRank], lbu[kLoraMaxRank];
-  if constexpr (LORA) {
-    const uint16_t* bg = lx.b + (static_cast<int64_t>(grp) * 2 * I + col) * lx.rank;
-    const uint16_t* bu = bg + static_cast<int64_t>(I) * lx.rank;
-#pragma unroll
-    for (int jj = 0; jj < kLoraMaxRank; ++jj) {
-      lbg[jj] = lora && jj < lx.rank ? bf16_to_f32(bg[jj]) : 0.f;
-      lbu[jj] = lora && jj < lx.rank ? bf16_to_f32(bu[jj]) : 0.f;
-    }
-  }
 #pragma unroll
   for (int mb = 0; mb < MBT; ++mb) {
     if (mb < nmb) {
+      if constexpr (LORA) {
+        if (lora) {
+          // expand on the matrix cores: t = z_hi B^T + z_lo B^T over the 16
+          // (zero-padded) rank columns, then acc += scale * t
+          const u32x4_t zh = ld16(&zs[(mb * 32 + j) * 2 * kLoraMaxRank + 8 * half]);
+          const u32x4_t zl = ld16(&zs[(mb * 32 + j) * 2 * kLoraMaxRank + kLoraMaxRank + 8 * half]);
+          const u32x4_t bg = ld16(&lbs[(wave * 32 + j) * kLoraMaxRank + 8 * half]);
+          const u32x4_t bu = ld16(&lbs[(kUpCols + wave * 32 + j) * kLoraMaxRank + 8 * half]);
+          const f32x16_t tg = mfma32x32x16(zl, bg, mfma32x32x16(zh, bg, zero16()));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) accg[mb][v] = fmaf(lx.scale, tg[v], accg[mb][v]);
+          const f32x16_t tu = mfma32x32x16(zl, bu, mfma32x32x16(zh, bu, zero16()));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) accu[mb][v] = fmaf(lx.scale, tu[v], accu[mb][v]);
+        }
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = mb * 32 + acc_row(v, half);
         if (row < rows) {
-          float g = accg[mb][v], u = accu[mb][v];
-          if constexpr (LORA) {
-            if (lora) {
-              float tg = 0.f, tu = 0.f;
-#pragma unroll
-              for (int jj = 0; jj < kLoraMaxRank; ++jj) {
-                if (jj < lx.rank) {
-                  const float zv = zs[row * kLoraMaxRank + jj];
-                  tg = fmaf(zv, lbg[jj], tg);
-                  tu = fmaf(zv, lbu[jj], tu);
-                }
-              }
-              g = fmaf(lx.scale, tg, g);
-              u = fmaf(lx.scale, tu, u);
-            }
-          }
+          const float g = accg[mb][v], u = accu[mb][v];
           const float a = silu_f32(g) * u;
           uint16_t hi, lo;
           split_hi_lo(a, hi, lo);
@@ -365,7 +356,10 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   static_assert((kAsElems + kBsElems) * 2 >= kRowsPerTile * COLS * 4, "the epilogue tile fits");
   __shared__ __attribute__((aligned(16))) uint16_t smem[kAsElems + kBsElems];
   __shared__ int s_dst[kRowsPerTile];
-  __shared__ __attribute__((aligned(16))) float zs[LORA ? kRowsPerTile * kLoraMaxRank : 4];
+  // the item's rows of shrink results (bf16 hi | lo) and the expand rows of
+  // its hidden columns, kLoraMaxRank bf16 each
+  __shared__ __attribute__((aligned(16))) uint16_t zs[LORA ? kRowsPerTile * 2 * kLoraMaxRank : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lbs[LORA ? COLS * kLoraMaxRank : 8];
   auto As = [&](int buf, int plane) { return smem + (buf * 2 + plane) * kRowsPerTile * 64; };
   uint16_t* const Bw = smem + kAsElems + (threadIdx.x >> 6) * WROWS * 64;
 
@@ -374,12 +368,10 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   const int64_t R = T * K;
   const bool lora = LORA && !shared;  // the shared expert has no adapter
   if (lora) {
-    // the item's rows of shrink results (ordered before the epilogue by the
-    // K loop's barriers)
-    for (int i = tid; i < kRowsPerTile * kLoraMaxRank / 4; i += 256) {
-      const int r = i / (kLoraMaxRank / 4);
-      if (r < rows) st16(&zs[4 * i], ld16(lx.z + p0 * kLoraMaxRank + 4 * i));
-    }
+    // ordered before the epilogue by the K loop's barriers
+    for (int i = tid; i < rows * 4; i += 256)
+      st16(&zs[8 * i], ld16(lx.zq + p0 * 2 * kLoraMaxRank + 8 * i));
+    lora_stage_b(lbs, lx.b + (static_cast<int64_t>(grp) * H + nt * COLS) * lx.rank, COLS, lx.rank, tid);
   }
 
   if (tid < kRowsPerTile) {
@@ -533,25 +525,19 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   // goes out as 16-byte pieces, COLS * 4 contiguous bytes per row.
   if constexpr (LORA) {
     if (lora) {
+      // expand on the matrix cores: t = z_hi B2^T + z_lo B2^T over the 16
+      // (zero-padded) rank columns, then acc += scale * t
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        // this lane's expand row B2[col][0..rank)
-        const uint16_t* b = lx.b + (static_cast<int64_t>(grp) * H + n0 + 32 * nb + j) * lx.rank;
-        float lb[kLoraMaxRank];
+      for (int mb = 0; mb < 2; ++mb) {
+        if (mb < nmb) {
+          const u32x4_t zh = ld16(&zs[(mb * 32 + j) * 2 * kLoraMaxRank + 8 * half]);
+          const u32x4_t zl = ld16(&zs[(mb * 32 + j) * 2 * kLoraMaxRank + kLoraMaxRank + 8 * half]);
 #pragma unroll
-        for (int jj = 0; jj < kLoraMaxRank; ++jj) lb[jj] = jj < lx.rank ? bf16_to_f32(b[jj]) : 0.f;
+          for (int nb = 0; nb < NBW; ++nb) {
+            const u32x4_t b = ld16(&lbs[(wave * WROWS + 32 * nb + j) * kLoraMaxRank + 8 * half]);
+            const f32x16_t t = mfma32x32x16(zl, b, mfma32x32x16(zh, b, zero16()));
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          if (mb < nmb) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int row = mb * 32 + acc_row(v, half);
-              float t = 0.f;
-#pragma unroll
-              for (int jj = 0; jj < kLoraMaxRank; ++jj)
-                if (jj < lx.rank) t = fmaf(zs[row * kLoraMaxRank + jj], lb[jj], t);
-              acc[mb][nb][v] = fmaf(lx.scale, t, acc[mb][nb][v]);
-            }
+            for (int v = 0; v < 16; ++v) acc[mb][nb][v] = fmaf(lx.scale, t[v], acc[mb][nb][v]);
           }
         }
       }

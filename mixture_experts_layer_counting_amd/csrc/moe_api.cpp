@@ -3,6 +3,7 @@
 // layout and the launch sequence of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -33,7 +34,7 @@ struct Layout {
   size_t act_hi = 0, act_lo = 0;    // [R][I] bf16
   size_t sact_hi = 0, sact_lo = 0;  // [T][Is] bf16
   size_t fwd_end = 0;
-  // LoRA shrink results (moe_forward_lora): [R][kLoraMaxRank] f32 each
+  // LoRA shrink results (moe_forward_lora): [R][hi, lo][kLoraMaxRank] bf16 each
   size_t lora_z13 = 0, lora_z2 = 0;
   size_t lora_end = 0;
   // backward regions (after lora_end)
@@ -81,8 +82,8 @@ Layout make_layout(const moe_dims& d) {
   L.sact_hi = take(static_cast<size_t>(T) * Is * 2);
   L.sact_lo = take(static_cast<size_t>(T) * Is * 2);
   L.fwd_end = o;
-  L.lora_z13 = take(static_cast<size_t>(R) * moe::kLoraMaxRank * 4);
-  L.lora_z2 = take(static_cast<size_t>(R) * moe::kLoraMaxRank * 4);
+  L.lora_z13 = take(static_cast<size_t>(R) * 2 * moe::kLoraMaxRank * 2);
+  L.lora_z2 = take(static_cast<size_t>(R) * 2 * moe::kLoraMaxRank * 2);
   L.lora_end = o;
   const int64_t H = d.hidden;
   L.max_tiles_bwd = static_cast<int>(moe::max_row_tiles(T, d.top_k, E, Is > 0, moe::kBwdRowsPerTile));
@@ -312,11 +313,11 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
   const bool own_up = tiles_up_of(ws, L) != nullptr;
   moe::LoraExpand e13{}, e2{};
   if (lora) {
-    e13 = {lora->b13, at<float>(ws, L.lora_z13), lora->scale, lora->rank};
-    e2 = {lora->b2, at<float>(ws, L.lora_z2), lora->scale, lora->rank};
+    e13 = {lora->b13, at<uint16_t>(ws, L.lora_z13), lora->scale, lora->rank};
+    e2 = {lora->b2, at<uint16_t>(ws, L.lora_z2), lora->scale, lora->rank};
     MOE_LAUNCH(moe::launch_lora_shrink(x, nullptr, lora->a13, r->expert_offsets, r->sorted_route,
                                        at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta),
-                                       at<float>(ws, L.lora_z13), d.tokens, d.hidden, d.experts,
+                                       at<uint16_t>(ws, L.lora_z13), d.tokens, d.hidden, d.experts,
                                        d.top_k, lora->rank, L.max_tiles, s));
   }
   MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, mx13, lora ? &e13 : nullptr,
@@ -332,7 +333,7 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
     MOE_LAUNCH(moe::launch_lora_shrink(at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
                                        lora->a2, r->expert_offsets, r->sorted_route,
                                        at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta),
-                                       at<float>(ws, L.lora_z2), d.tokens, d.inter, d.experts,
+                                       at<uint16_t>(ws, L.lora_z2), d.tokens, d.inter, d.experts,
                                        d.top_k, lora->rank, L.max_tiles, s));
   MOE_LAUNCH(moe::launch_ffn_down(at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
                                   at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), w->w2,
@@ -529,6 +530,10 @@ int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora*
   MOE_TRY(check_dims(dims));
   if (!lora) return MOE_E_NULL;
   if (lora->rank < 1 || lora->rank > moe::kLoraMaxRank) return MOE_E_SHAPE;
+  // the shrink keeps an expert's whole A in LDS and a row in four pieces per lane
+  const int64_t kmax = std::max(dims->hidden, dims->inter);
+  if (kmax > 512 * moe::kLoraMaxPieces || lora->rank * kmax > moe::kLoraShrinkLds)
+    return MOE_E_UNSUPPORTED;
   if (dims->tokens == 0) return MOE_OK;
   if (!w || !routes || !saved) return MOE_E_NULL;
   if (!out_f32 && !out_bf16) return MOE_E_NULL;

@@ -101,15 +101,37 @@ struct MxWeights {
 // LoRA adapters of the routed experts: largest rank, and the fp32 stride of
 // a row of shrink results z (one 64-byte row per sorted route position).
 constexpr int kLoraMaxRank = 16;
+// The shrink holds an expert's whole A in LDS (rank * contraction bf16
+// elements at most this many, 56 KiB) and a row's contraction in at most
+// four 8-element pieces per lane (contraction <= 2048).
+constexpr int kLoraShrinkLds = 28672;
+constexpr int kLoraMaxPieces = 4;
 // The expand half of one projection's adapters as the grouped-GEMM
-// epilogue applies it: B [E][out][rank] bf16, the rows' shrink results z
-// [sorted position][kLoraMaxRank] fp32, the update's scale and the rank.
+// epilogue applies it: B [E][out][rank] bf16, the rows' shrink results as
+// bf16 pairs zq [sorted position][hi, lo][kLoraMaxRank], the update's scale
+// and the rank.
 struct LoraExpand {
   const uint16_t* b;
-  const float* z;
+  const uint16_t* zq;
   float scale;
   int rank;
 };
+
+// Stage the expand rows b[0 .. n) (rank bf16 each, packed) into LDS rows of
+// kLoraMaxRank bf16, zero past the rank: thread t < n fills row t.
+__device__ __forceinline__ void lora_stage_b(uint16_t* lds, const uint16_t* b, int n, int rank, int tid) {
+  if (tid < n) {
+    uint32_t w[kLoraMaxRank / 2];
+#pragma unroll
+    for (int i = 0; i < kLoraMaxRank / 2; ++i) {
+      const uint32_t e0 = 2 * i < rank ? b[static_cast<int64_t>(tid) * rank + 2 * i] : 0u;
+      const uint32_t e1 = 2 * i + 1 < rank ? b[static_cast<int64_t>(tid) * rank + 2 * i + 1] : 0u;
+      w[i] = e0 | (e1 << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(lds + tid * kLoraMaxRank) = u32x4_t{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4_t*>(lds + tid * kLoraMaxRank + 8) = u32x4_t{w[4], w[5], w[6], w[7]};
+  }
+}
 
 // E8M0 scale code -> 2^(code - 127) as a float (code 0 is the denormal 2^-127).
 __device__ __forceinline__ float e8m0_scale(uint32_t code) {

@@ -71,11 +71,12 @@ hipError_t launch_ffn_down(const uint16_t* act_hi, const uint16_t* act_lo,
                            int64_t T, int H, int E, int K, int I, int Is, int max_tiles,
                            hipStream_t stream);
 // LoRA shrink of the routed experts' rows (lora_kernels.hip): z[p][j] =
-// sum_k A_e[j][k] v_p[k] over the 64-row work list `tiles` (meta[0] items);
-// v_p = x[token of route sorted_route[p]] (v_lo null) or v_hi[p] + v_lo[p].
+// sum_k A_e[j][k] v_p[k] over the 64-row work list `tiles` (meta[0] items),
+// stored as bf16 pairs zq[p][0 hi | 1 lo][16]; v_p = x[token of route
+// sorted_route[p]] (v_lo null) or v_hi[p] + v_lo[p].
 hipError_t launch_lora_shrink(const uint16_t* v_hi, const uint16_t* v_lo, const uint16_t* a,
                               const int32_t* offsets, const int32_t* sorted_route,
-                              const int32_t* tiles, const int32_t* meta, float* z, int64_t T,
+                              const int32_t* tiles, const int32_t* meta, uint16_t* z, int64_t T,
                               int Kd, int E, int K, int rank, int max_tiles, hipStream_t stream);
 hipError_t launch_combine(const float* y, const float* gate, const float* sy, const float* sg,
                           float* out32, uint16_t* out16, int64_t T, int H, int K,
