@@ -276,9 +276,10 @@ typedef struct {
  *   z[p][j] = sum_k A_e[j][k] v_p[k] (fp32, one wave per row p, lane-strided
  *            ascending pieces, then a fixed 64-lane butterfly), v_p = x_t for
  *            the gate/up adapter, act_r (its exact bf16 hi + lo) for down;
- *   gate/up (and y) += scale * (fp32 fma chain over ascending j of z[p][j] *
- *            B[col][j]), one fma into the GEMM accumulator, before the
- *            SwiGLU (and before y is stored).
+ *            kept as a bf16 pair z_hi + z_lo;
+ *   t = z_hi B^T + z_lo B^T (two bf16 MFMAs, fp32 accumulation, over 16
+ *            zero-padded rank columns), then gate/up (and y) = fma(scale, t,
+ *            GEMM accumulator), before the SwiGLU (and before y is stored).
  * So every route row is a function of its own data only (batch invariant,
  * deterministic, no atomics).  saved->gu, if given, receives the gate/up
  * values with the update; moe_backward does not take adapters.  Workspace:

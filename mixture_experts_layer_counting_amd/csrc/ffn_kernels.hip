@@ -59,9 +59,10 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // flight while kb is multiplied); NKB = 0 is the general loop with one block
 // in flight (NSET = 1).  All run the same MFMA sequence on every element.
 // LORA adds a routed expert's adapter update to gate and up before the
-// SwiGLU: g += scale * sum_j z[p][j] B13[col][j], u likewise with row I + col
-// of B13, each sum an fp32 fma chain over ascending j from +0 (z: the rows'
-// shrink results).
+// SwiGLU: g = fma(scale, t, g) with t = sum_j z[p][j] B13[col][j] (u likewise
+// with row I + col of B13), t taken on the matrix cores as z_hi B^T + z_lo
+// B^T over 16 zero-padded rank columns (z: the rows' shrink results as bf16
+// pairs).
 // ---------------------------------------------------------------------------
 template <int NKB, int NSET, int MBT, bool MX, bool LORA>
 __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
@@ -319,8 +320,9 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 // flight while kb is multiplied); NKB = 0 is the general loop with one block
 // in flight (NSET = 1).  All run the same MFMA sequence on every element.
 // LORA adds a routed expert's adapter update to every element before it is
-// stored: y += scale * sum_j z[p][j] B2[col][j], an fp32 fma chain over
-// ascending j from +0 (z: the rows' shrink results).
+// stored: y = fma(scale, t, y) with t = sum_j z[p][j] B2[col][j] taken on the
+// matrix cores as z_hi B2^T + z_lo B2^T over 16 zero-padded rank columns (z:
+// the rows' shrink results as bf16 pairs).
 // ---------------------------------------------------------------------------
 template <int NKB, int NSET, int NBW, bool MX, bool LORA>
 __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
