@@ -273,10 +273,11 @@ typedef struct {
 /* Forward of the layer whose routed experts carry LoRA adapters.  Kernels
  * and per-element arithmetic of moe_forward, plus two shrink kernels and
  * the expand inside the grouped GEMMs' epilogues:
- *   z[p][j] = sum_k A_e[j][k] v_p[k] (fp32, one wave per row p, lane-strided
- *            ascending pieces, then a fixed 64-lane butterfly), v_p = x_t for
- *            the gate/up adapter, act_r (its exact bf16 hi + lo) for down;
- *            kept as a bf16 pair z_hi + z_lo;
+ *   z[p][j] = sum_k A_e[j][k] v_p[k] (16x16x32 bf16 MFMAs over ascending
+ *            32-wide K steps, fp32 accumulation, one wave per 16 rows and
+ *            the whole contraction), v_p = x_t for the gate/up adapter, act_r
+ *            (its bf16 hi + lo, two passes) for down; kept as a bf16 pair
+ *            z_hi + z_lo;
  *   t = z_hi B^T + z_lo B^T (two bf16 MFMAs, fp32 accumulation, over 16
  *            zero-padded rank columns), then gate/up (and y) = fma(scale, t,
  *            GEMM accumulator), before the SwiGLU (and before y is stored).
@@ -284,10 +285,8 @@ typedef struct {
  * deterministic, no atomics).  saved->gu, if given, receives the gate/up
  * values with the update; moe_backward does not take adapters.  Workspace:
  * moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA).  Errors as moe_forward,
- * plus MOE_E_NULL for a missing adapter matrix, MOE_E_SHAPE for a rank
- * outside 1..16 and MOE_E_UNSUPPORTED unless max(H, I) <= 2048 and
- * rank * max(H, I) <= 28672 (the shrink holds an expert's A in LDS; hidden
- * 2048 allows rank 14). */
+ * plus MOE_E_NULL for a missing adapter matrix and MOE_E_SHAPE for a rank
+ * outside 1..16. */
 int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,
                      const uint16_t* x, moe_routes* routes, moe_saved* saved, float* out_f32,
                      uint16_t* out_bf16, void* ws, size_t ws_bytes, hipStream_t stream);

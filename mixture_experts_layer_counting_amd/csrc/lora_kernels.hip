@@ -10,31 +10,37 @@
 //   z[p][j] = sum_k A_e[j][k] v_p[k]   for j < rank, z[p][rank .. 16) = 0,
 //
 // for every routed row p (sorted position) of expert e.  v_p is the gathered
-// token row x[t] (gate/up adapter, contraction H) or act_hi[p] + act_lo[p]
-// (down adapter, contraction I; the sum of the bf16 pair is exact in fp32).
-// Lane l of the row's wave takes the 8-element pieces l, l + 64, l + 128, ...
-// of the contraction in ascending order, one fp32 fma chain from +0 per j;
-// the 64 lane sums are then combined by a fixed xor butterfly (lane distance
-// 32, 16, ..., 1), which leaves the same bits in every lane.  A row's result
-// depends only on its own data, never on the batch or its position in it.
+// token row x[t] (gate/up adapter, contraction H) or act_r as its bf16 pair
+// act_hi + act_lo (down adapter, contraction I: two passes, hi first).
+// The contraction runs on the matrix cores: wave w of a 64-row work item
+// owns rows 16w .. 16w + 15 and multiplies them by A_e^T (16 columns, zero
+// past the rank) with 16x16x32 bf16 MFMAs over K in ascending 32-wide steps,
+// fp32 accumulation from zero.  A row's result depends only on its own data,
+// never on the batch or its position in it.
 //
 // The result leaves as a bf16 pair per element, hi = bf16(z), lo =
 // bf16(z - hi) (z = hi + lo to about 2^-17 relative), which the grouped
 // GEMMs' expand multiplies on the matrix cores: zq[p][0][j] = hi,
-// zq[p][1][j] = lo, j < 16.
-//
-// A workgroup of eight waves takes one 64-row work item of an expert and
-// stages all of A_e in LDS (rank * contraction <= kLoraShrinkLds elements,
-// checked by the host); wave w computes rows w, w + 8, ....  Each wave
-// issues its first row's loads before the staging barrier.
+// zq[p][1][j] = lo, j < 16.  Operands come straight from memory into
+// registers (16 bytes per lane and step), four steps per batch with the
+// next batch in flight.
 #include "moe_kernels.h"
 
 namespace moe {
 
-constexpr int kShrinkWaves = 8;
+constexpr int kShrinkSteps = 4;  // 32-wide K steps per batch of loads
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4m_t;
+
+// D = A(16x32) * B(32x16) + C, bf16 inputs, fp32 accumulate.  Lane l supplies
+// A[l%16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l%16]; it holds
+// D[4*(l/16) + i][l%16] in element i.
+__device__ __forceinline__ f32x4m_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4m_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
 
 template <bool ACT>
-__global__ __launch_bounds__(kShrinkWaves * 64) void lora_shrink_kernel(
+__global__ __launch_bounds__(256) void lora_shrink_kernel(
     const uint16_t* __restrict__ v_hi, const uint16_t* __restrict__ v_lo,
     const uint16_t* __restrict__ a, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_route, const int32_t* __restrict__ tiles,
@@ -45,86 +51,65 @@ __global__ __launch_bounds__(kShrinkWaves * 64) void lora_shrink_kernel(
   const GroupItem gi = group_item(item, 1, tiles, offsets, E, T, kRowsPerTile);
   if (gi.grp == E) return;  // the shared expert has no adapter
   const int rows = min(kRowsPerTile, gi.cnt - gi.row0);
-  if (rows <= 0) return;
-  extern __shared__ __attribute__((aligned(16))) uint16_t As[];  // A_e [rank][Kd]
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (16 * wave >= rows) return;  // no barriers below: waves are independent
+  const int r16 = lane & 15, kq = lane >> 4;
   const int64_t p0 = static_cast<int64_t>(gi.seg0) + gi.row0;
-  const int npieces = Kd >> 3;  // 8-element pieces of a row; lane pieces q = lane + 64 c
-  const int nc = (npieces + 63) >> 6;
-  auto src_of = [&](int r) -> int64_t {
-    if constexpr (ACT) {
-      return (p0 + r) * Kd;
-    } else {
-      const int64_t rr = sorted_route[p0 + r];
-      return ((rr >= 0 && rr < T * K) ? rr / K : 0) * Kd;
-    }
-  };
-  u32x4_t vh[kLoraMaxPieces], vl[kLoraMaxPieces];
-  auto load = [&](int r) {
-    const int64_t src = src_of(r);
-#pragma unroll
-    for (int c = 0; c < kLoraMaxPieces; ++c) {
-      const int q = lane + 64 * c;
-      if (c < nc && q < npieces) {
-        vh[c] = ld16(v_hi + src + 8 * q);
-        if constexpr (ACT) vl[c] = ld16(v_lo + src + 8 * q);
-      }
-    }
-  };
-  if (wave < rows) load(wave);
-  const uint16_t* ae = a + static_cast<int64_t>(gi.grp) * rank * Kd;
-  for (int i = tid; i < rank * Kd / 8; i += kShrinkWaves * 64) st16(&As[8 * i], ld16(ae + 8 * i));
-  __syncthreads();
+  // rows past the item's end repeat its last row (computed, not stored)
+  const int r = min(16 * wave + r16, rows - 1);
+  int64_t src;
+  if constexpr (ACT) {
+    src = (p0 + r) * Kd;
+  } else {
+    const int64_t rr = sorted_route[p0 + r];
+    src = ((rr >= 0 && rr < T * K) ? rr / K : 0) * Kd;
+  }
+  const uint16_t* xh = v_hi + src + 8 * kq;
+  const uint16_t* xl = ACT ? v_lo + src + 8 * kq : nullptr;
+  const bool jv = r16 < rank;  // this lane's B column is a rank row of A_e
+  const uint16_t* ar = a + (static_cast<int64_t>(gi.grp) * rank + (jv ? r16 : 0)) * Kd + 8 * kq;
 
-  for (int r = wave; r < rows; r += kShrinkWaves) {
-    if (r != wave) load(r);
-    float s[kLoraMaxRank];
+  u32x4_t h0[kShrinkSteps], l0[kShrinkSteps], b0[kShrinkSteps];
+  u32x4_t h1[kShrinkSteps], l1[kShrinkSteps], b1[kShrinkSteps];
+  auto fetch = [&](u32x4_t (&h)[kShrinkSteps], u32x4_t (&l)[kShrinkSteps], u32x4_t (&b)[kShrinkSteps],
+                   int k0) {
 #pragma unroll
-    for (int jj = 0; jj < kLoraMaxRank; ++jj) s[jj] = 0.f;
-#pragma unroll
-    for (int c = 0; c < kLoraMaxPieces; ++c) {
-      const int q = lane + 64 * c;
-      if (c < nc && q < npieces) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[2 * e] = __uint_as_float(vh[c][e] << 16);
-          v[2 * e + 1] = __uint_as_float(vh[c][e] & 0xffff0000u);
-          if constexpr (ACT) {
-            v[2 * e] += __uint_as_float(vl[c][e] << 16);
-            v[2 * e + 1] += __uint_as_float(vl[c][e] & 0xffff0000u);
-          }
-        }
-#pragma unroll
-        for (int jj = 0; jj < kLoraMaxRank; ++jj) {
-          if (jj < rank) {
-            const u32x4_t a4 = ld16(&As[jj * Kd + 8 * q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              s[jj] = fmaf(__uint_as_float(a4[e] << 16), v[2 * e], s[jj]);
-              s[jj] = fmaf(__uint_as_float(a4[e] & 0xffff0000u), v[2 * e + 1], s[jj]);
-            }
-          }
-        }
-      }
+    for (int st = 0; st < kShrinkSteps; ++st) {
+      const int k = k0 + 32 * st;
+      h[st] = ld16(xh + k);
+      if constexpr (ACT) l[st] = ld16(xl + k);
+      b[st] = jv ? ld16(ar + k) : u32x4_t{0u, 0u, 0u, 0u};
     }
+  };
+  f32x4m_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4_t (&h)[kShrinkSteps], const u32x4_t (&l)[kShrinkSteps],
+                     const u32x4_t (&b)[kShrinkSteps]) {
 #pragma unroll
-    for (int jj = 0; jj < kLoraMaxRank; ++jj) {
-      if (jj < rank) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) s[jj] += __shfl_xor(s[jj], off, 64);
-      }
+    for (int st = 0; st < kShrinkSteps; ++st) {
+      acc = mfma16x16x32(h[st], b[st], acc);
+      if constexpr (ACT) acc = mfma16x16x32(l[st], b[st], acc);
     }
-    // lanes 0..15 store hi of element j = lane, lanes 16..31 lo of j = lane - 16
-    const int jj_out = lane & 15;
-    float o = 0.f;
+  };
+  constexpr int KB = 32 * kShrinkSteps;  // contraction elements per batch
+  const int nb = Kd / KB;                // Kd % 128 == 0
+  fetch(h0, l0, b0, 0);
+  for (int bt = 0; bt < nb; bt += 2) {
+    if (bt + 1 < nb) fetch(h1, l1, b1, (bt + 1) * KB);
+    compute(h0, l0, b0);
+    if (bt + 2 < nb) fetch(h0, l0, b0, (bt + 2) * KB);
+    if (bt + 1 < nb) compute(h1, l1, b1);
+  }
+
 #pragma unroll
-    for (int jj = 0; jj < kLoraMaxRank; ++jj)
-      if (jj_out == jj) o = s[jj];
-    uint16_t hi, lo;
-    split_hi_lo(o, hi, lo);
-    if (lane < 2 * kLoraMaxRank) zq[(p0 + r) * 2 * kLoraMaxRank + lane] = lane < kLoraMaxRank ? hi : lo;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * wave + 4 * kq + i;
+    if (row < rows) {
+      uint16_t hi, lo;
+      split_hi_lo(acc[i], hi, lo);
+      uint16_t* o = zq + (p0 + row) * 2 * kLoraMaxRank;
+      o[r16] = hi;
+      o[kLoraMaxRank + r16] = lo;
+    }
   }
 }
 
@@ -132,17 +117,14 @@ hipError_t launch_lora_shrink(const uint16_t* v_hi, const uint16_t* v_lo, const 
                               const int32_t* offsets, const int32_t* sorted_route,
                               const int32_t* tiles, const int32_t* meta, uint16_t* z, int64_t T,
                               int Kd, int E, int K, int rank, int max_tiles, hipStream_t stream) {
-  if (rank < 1 || rank > kLoraMaxRank || static_cast<int64_t>(rank) * Kd > kLoraShrinkLds ||
-      Kd > 512 * kLoraMaxPieces || Kd % 8)
-    return hipErrorInvalidValue;
+  if (rank < 1 || rank > kLoraMaxRank || Kd % (32 * kShrinkSteps)) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>(((static_cast<int64_t>(max_tiles) + 7) / 8) * 8);
-  const size_t lds = static_cast<size_t>(rank) * Kd * 2;
   if (v_lo)
-    lora_shrink_kernel<true><<<grid, kShrinkWaves * 64, lds, stream>>>(v_hi, v_lo, a, offsets, sorted_route, tiles,
-                                                         meta, z, T, Kd, E, K, rank);
+    lora_shrink_kernel<true><<<grid, 256, 0, stream>>>(v_hi, v_lo, a, offsets, sorted_route, tiles,
+                                                       meta, z, T, Kd, E, K, rank);
   else
-    lora_shrink_kernel<false><<<grid, kShrinkWaves * 64, lds, stream>>>(v_hi, nullptr, a, offsets, sorted_route,
-                                                          tiles, meta, z, T, Kd, E, K, rank);
+    lora_shrink_kernel<false><<<grid, 256, 0, stream>>>(v_hi, nullptr, a, offsets, sorted_route,
+                                                        tiles, meta, z, T, Kd, E, K, rank);
   return hipGetLastError();
 }
 

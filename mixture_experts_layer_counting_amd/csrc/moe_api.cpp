@@ -3,7 +3,6 @@
 // layout and the launch sequence of each entry point.
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -530,10 +529,6 @@ int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora*
   MOE_TRY(check_dims(dims));
   if (!lora) return MOE_E_NULL;
   if (lora->rank < 1 || lora->rank > moe::kLoraMaxRank) return MOE_E_SHAPE;
-  // the shrink keeps an expert's whole A in LDS and a row in four pieces per lane
-  const int64_t kmax = std::max(dims->hidden, dims->inter);
-  if (kmax > 512 * moe::kLoraMaxPieces || lora->rank * kmax > moe::kLoraShrinkLds)
-    return MOE_E_UNSUPPORTED;
   if (dims->tokens == 0) return MOE_OK;
   if (!w || !routes || !saved) return MOE_E_NULL;
   if (!out_f32 && !out_bf16) return MOE_E_NULL;

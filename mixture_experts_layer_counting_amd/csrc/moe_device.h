@@ -101,11 +101,6 @@ struct MxWeights {
 // LoRA adapters of the routed experts: largest rank, and the fp32 stride of
 // a row of shrink results z (one 64-byte row per sorted route position).
 constexpr int kLoraMaxRank = 16;
-// The shrink holds an expert's whole A in LDS (rank * contraction bf16
-// elements at most this many, 56 KiB) and a row's contraction in at most
-// four 8-element pieces per lane (contraction <= 2048).
-constexpr int kLoraShrinkLds = 28672;
-constexpr int kLoraMaxPieces = 4;
 // The expand half of one projection's adapters as the grouped-GEMM
 // epilogue applies it: B [E][out][rank] bf16, the rows' shrink results as
 // bf16 pairs zq [sorted position][hi, lo][kLoraMaxRank], the update's scale
