@@ -129,3 +129,14 @@ def test_lora_with_zero_expand_gives_the_plain_forward():
     p = gpu_forward(cfg, w, xd).host()
     for k in ("idx", "sorted_route", "y", "out32"):
         assert np.array_equal(g[k].view(np.uint32), p[k].view(np.uint32)), k
+
+
+def test_lora_forward_is_deterministic():
+    cfg, layer, x = load_cfg("tiny")
+    ad = WL.lora_adapters(cfg)
+    w, lo, xd = dev_weights(layer), dev_lora(ad), dev_bits(x)
+    say("case: tiny, two LoRA forwards of the same batch")
+    a = gpu_forward_lora(cfg, w, lo, xd)
+    b = gpu_forward_lora(cfg, w, lo, xd)
+    for k in ("idx", "sorted_route", "gu", "y", "out32"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
