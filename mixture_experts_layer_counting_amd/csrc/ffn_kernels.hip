@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Bs[4][64 * 64];
   __shared__ int s_tok[ROWS];
   // the item's rows of shrink results (bf16 hi | lo) and its expand rows
-  // (gate columns, then up columns), kLoraMaxRank bf16 each
+  // (gate columns, then up columns; rank bf16 each, packed)
   __shared__ __attribute__((aligned(16))) uint16_t zs[LORA ? ROWS * 2 * kLoraMaxRank : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lbs[LORA ? 2 * kUpCols * kLoraMaxRank : 8];
 
@@ -104,9 +104,10 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     // ordered before the epilogue by the K loop's barriers
     for (int i = tid; i < rows * 4; i += 256)
       st16(&zs[8 * i], ld16(lx.zq + (static_cast<int64_t>(seg0) + row0) * 2 * kLoraMaxRank + 8 * i));
-    const int64_t b0 = (static_cast<int64_t>(grp) * 2 * I + nt * kUpCols) * lx.rank;
-    lora_stage_b(lbs, lx.b + (tid < kUpCols ? b0 : b0 + static_cast<int64_t>(I - kUpCols) * lx.rank),
-                 2 * kUpCols, lx.rank, tid);
+    // gate rows nt*128 .. +128, then up rows I + nt*128 .. +128
+    const uint16_t* b0 = lx.b + (static_cast<int64_t>(grp) * 2 * I + nt * kUpCols) * lx.rank;
+    lora_stage_b(lbs, b0, kUpCols, lx.rank, tid);
+    lora_stage_b(lbs + kUpCols * lx.rank, b0 + static_cast<int64_t>(I) * lx.rank, kUpCols, lx.rank, tid);
   }
 
   if (tid < ROWS) {
@@ -275,8 +276,8 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
           // (zero-padded) rank columns, then acc += scale * t
           const u32x4_t zh = ld16(&zs[(mb * 32 + j) * 2 * kLoraMaxRank + 8 * half]);
           const u32x4_t zl = ld16(&zs[(mb * 32 + j) * 2 * kLoraMaxRank + kLoraMaxRank + 8 * half]);
-          const u32x4_t bg = ld16(&lbs[(wave * 32 + j) * kLoraMaxRank + 8 * half]);
-          const u32x4_t bu = ld16(&lbs[(kUpCols + wave * 32 + j) * kLoraMaxRank + 8 * half]);
+          const u32x4_t bg = lora_b_operand(lbs, wave * 32 + j, half, lx.rank);
+          const u32x4_t bu = lora_b_operand(lbs, kUpCols + wave * 32 + j, half, lx.rank);
           const f32x16_t tg = mfma32x32x16(zl, bg, mfma32x32x16(zh, bg, zero16()));
 #pragma unroll
           for (int v = 0; v < 16; ++v) accg[mb][v] = fmaf(lx.scale, tg[v], accg[mb][v]);
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t smem[kAsElems + kBsElems];
   __shared__ int s_dst[kRowsPerTile];
   // the item's rows of shrink results (bf16 hi | lo) and the expand rows of
-  // its hidden columns, kLoraMaxRank bf16 each
+  // its hidden columns (rank bf16 each, packed)
   __shared__ __attribute__((aligned(16))) uint16_t zs[LORA ? kRowsPerTile * 2 * kLoraMaxRank : 8];
   __shared__ __attribute__((aligned(16))) uint16_t lbs[LORA ? COLS * kLoraMaxRank : 8];
   auto As = [&](int buf, int plane) { return smem + (buf * 2 + plane) * kRowsPerTile * 64; };
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
           const u32x4_t zl = ld16(&zs[(mb * 32 + j) * 2 * kLoraMaxRank + kLoraMaxRank + 8 * half]);
 #pragma unroll
           for (int nb = 0; nb < NBW; ++nb) {
-            const u32x4_t b = ld16(&lbs[(wave * WROWS + 32 * nb + j) * kLoraMaxRank + 8 * half]);
+            const u32x4_t b = lora_b_operand(lbs, wave * WROWS + 32 * nb + j, half, lx.rank);
             const f32x16_t t = mfma32x32x16(zl, b, mfma32x32x16(zh, b, zero16()));
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mb][nb][v] = fmaf(lx.scale, t[v], acc[mb][nb][v]);

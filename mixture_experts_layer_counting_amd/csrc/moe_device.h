@@ -112,20 +112,25 @@ struct LoraExpand {
   int rank;
 };
 
-// Stage the expand rows b[0 .. n) (rank bf16 each, packed) into LDS rows of
-// kLoraMaxRank bf16, zero past the rank: thread t < n fills row t.
+// Copy the expand rows b[0 .. n) (rank bf16 each, packed; n * rank a
+// multiple of 8 and b 16-byte aligned) into LDS as they are, 16 bytes per
+// thread and step.
 __device__ __forceinline__ void lora_stage_b(uint16_t* lds, const uint16_t* b, int n, int rank, int tid) {
-  if (tid < n) {
-    uint32_t w[kLoraMaxRank / 2];
+  for (int i = tid; i < n * rank / 8; i += 256) st16(lds + 8 * i, ld16(b + 8 * i));
+}
+
+// MFMA B operand of expand row `row` from the packed LDS copy: elements
+// j = 8 * half .. 8 * half + 7 of the row, zero past the rank.
+__device__ __forceinline__ u32x4_t lora_b_operand(const uint16_t* lds, int row, int half, int rank) {
+  uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < kLoraMaxRank / 2; ++i) {
-      const uint32_t e0 = 2 * i < rank ? b[static_cast<int64_t>(tid) * rank + 2 * i] : 0u;
-      const uint32_t e1 = 2 * i + 1 < rank ? b[static_cast<int64_t>(tid) * rank + 2 * i + 1] : 0u;
-      w[i] = e0 | (e1 << 16);
-    }
-    *reinterpret_cast<u32x4_t*>(lds + tid * kLoraMaxRank) = u32x4_t{w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<u32x4_t*>(lds + tid * kLoraMaxRank + 8) = u32x4_t{w[4], w[5], w[6], w[7]};
+  for (int i = 0; i < 4; ++i) {
+    const int j0 = 8 * half + 2 * i;
+    const uint32_t e0 = j0 < rank ? lds[row * rank + j0] : 0u;
+    const uint32_t e1 = j0 + 1 < rank ? lds[row * rank + j0 + 1] : 0u;
+    w[i] = e0 | (e1 << 16);
   }
+  return u32x4_t{w[0], w[1], w[2], w[3]};
 }
 
 // E8M0 scale code -> 2^(code - 127) as a float (code 0 is the denormal 2^-127).

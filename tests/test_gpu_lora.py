@@ -6,7 +6,8 @@ N(0, 0.02) factors, B nonzero).  Checks, through the C ABI:
     route rows Y before combine (which carry the down update), S and out
     against the FP64 oracle with the same adapters, at the forward's
     tolerance, on every token of the small layers and on sampled tokens of
-    the 8192-token layer (96-row up-projection items);
+    the 8192-token and skewed 16384-token layers (96-row up-projection
+    items; empty and very long expert segments);
   * each route row is a function of its own token: a sub-batch gives the
     same bits;
   * adapters whose expand matrices are zero give moe_forward's bits;
@@ -94,10 +95,12 @@ def test_lora_forward_matches_oracle(name, rank):
     check_lora_forward(cfg, layer, ad, x, g, tokens)
 
 
-def test_lora_forward_8k_sampled_tokens():
-    cfg, layer, x = load_cfg("moe8k")
+# skew16k: experts with > 2000 routes next to 100 experts with none
+@pytest.mark.parametrize("name", ["moe8k", "skew16k"])
+def test_lora_forward_large_batches_sampled_tokens(name):
+    cfg, layer, x = load_cfg(name)
     ad = WL.lora_adapters(cfg)
-    say("case: moe8k, rank 6, sampled tokens vs oracle (96-row up items)")
+    say(f"case: {name}, rank 6, sampled tokens vs oracle (96-row up items)")
     g = gpu_forward_lora(cfg, dev_weights(layer), dev_lora(ad), dev_bits(x), with_gu=False)
     tok = np.unique(np.r_[0:8, cfg.tokens - 8:cfg.tokens, np.linspace(0, cfg.tokens - 1, 24).astype(int)])
     check_lora_forward(cfg, layer, ad, x, g, tok)
