@@ -291,6 +291,15 @@ int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora*
                      const uint16_t* x, moe_routes* routes, moe_saved* saved, float* out_f32,
                      uint16_t* out_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Grouped FFN stage of moe_forward_lora on a caller-made permutation, as
+ * moe_grouped_ffn is to moe_forward (routing replay: moe_permute on
+ * replayed topk_idx, then this, then moe_combine give moe_forward_lora's
+ * bits for the same routes).  Workspace: moe_workspace_bytes(dims,
+ * MOE_OP_FORWARD_LORA).  Errors as moe_grouped_ffn and moe_forward_lora. */
+int moe_grouped_ffn_lora(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
+                         const moe_lora* lora, const moe_routes* routes, moe_saved* saved, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
 /* Profiling variant of moe_forward: the same kernels in the same order on
  * `stream`, with events[i] recorded just before kernel i and events[n] after
  * the last one, n = moe_forward_kernel_count(dims).  `events` are created by

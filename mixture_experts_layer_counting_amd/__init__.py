@@ -68,7 +68,7 @@ class MoeGrads(ctypes.Structure):
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
            "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
-           "moe_forward_lora")
+           "moe_forward_lora", "moe_grouped_ffn_lora")
 
 _lib = None
 
@@ -105,6 +105,9 @@ def load_library():
     lib.moe_forward_lora.restype = ctypes.c_int
     lib.moe_forward_lora.argtypes = [P(MoeDims), P(MoeWeights), P(MoeLora), _VP, P(MoeRoutes), P(MoeSaved),
                                      _VP, _VP, *ws]
+    lib.moe_grouped_ffn_lora.restype = ctypes.c_int
+    lib.moe_grouped_ffn_lora.argtypes = [P(MoeDims), _VP, P(MoeWeights), P(MoeLora), P(MoeRoutes), P(MoeSaved),
+                                         *ws]
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                  P(MoeGrads), *ws]
@@ -312,6 +315,13 @@ def moe_forward_lora(dims, weights, lora, x, routes, saved, out_f32, out_bf16, w
                                            ctypes.byref(lora.c()), _ptr(x), ctypes.byref(routes.c()),
                                            ctypes.byref(saved.c()), _ptr(out_f32), _ptr(out_bf16), p, n,
                                            _stream(stream))
+
+
+def moe_grouped_ffn_lora(dims, x, weights, lora, routes, saved, ws, stream=None) -> int:
+    p, n = _ws(ws)
+    return load_library().moe_grouped_ffn_lora(ctypes.byref(dims.c()), _ptr(x), ctypes.byref(weights.c()),
+                                               ctypes.byref(lora.c()), ctypes.byref(routes.c()),
+                                               ctypes.byref(saved.c()), p, n, _stream(stream))
 
 
 def moe_backward(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, ws, stream=None) -> int:

@@ -472,6 +472,33 @@ int moe_grouped_ffn(const moe_dims* dims, const uint16_t* x, const moe_weights* 
   return run_ffn(d, x, w, routes, saved, ws, make_layout(d), false, stream);
 }
 
+int moe_grouped_ffn_lora(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
+                         const moe_lora* lora, const moe_routes* routes, moe_saved* saved, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (!lora) return MOE_E_NULL;
+  if (lora->rank < 1 || lora->rank > moe::kLoraMaxRank) return MOE_E_SHAPE;
+  if (dims->tokens == 0) return MOE_OK;
+  if (!w || !routes || !saved) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, K = d.top_k, E = d.experts, H = d.hidden, I = d.inter, rk = lora->rank;
+  Args a;
+  a.in(x, bytes_x(d));
+  add_weights(a, d, w, false, true);
+  a.in(lora->a13, E * rk * H * 2);
+  a.in(lora->b13, E * 2 * I * rk * 2);
+  a.in(lora->a2, E * rk * I * 2);
+  a.in(lora->b2, E * H * rk * 2);
+  a.in(routes->expert_offsets, (E + 1) * 4);
+  a.in(routes->sorted_route, T * K * 4);
+  add_saved(a, d, saved, true);
+  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD_LORA));
+  MOE_TRY(check_device());
+  return run_ffn(d, x, w, routes, saved, ws, make_layout(d), false, stream, nullptr, nullptr, lora);
+}
+
 int moe_combine(const moe_dims* dims, const moe_routes* routes, const moe_saved* saved,
                 float* out_f32, uint16_t* out_bf16, hipStream_t stream) {
   MOE_TRY(check_dims(dims));

@@ -185,6 +185,11 @@ def test_lora_forward_validation_fails_closed(lib):
     assert call(m.Lora(**{**lo.__dict__, "a2": s.y})) == m.MOE_E_ALIAS
     # a workspace sized for the plain forward is too small
     assert call(lo, wss=ws) == m.MOE_E_WORKSPACE
+    # the grouped-FFN stage checks the same adapters and workspace
+    ffn = lambda ll, wss=wsl: m.moe_grouped_ffn_lora(d, x, w, ll, r, s, wss, stream=0)
+    assert ffn(m.Lora(**{**lo.__dict__, "rank": 0})) == m.MOE_E_SHAPE
+    assert ffn(m.Lora(**{**lo.__dict__, "a13": None})) == m.MOE_E_NULL
+    assert ffn(lo, wss=ws) == m.MOE_E_WORKSPACE
     assert call(lo, dd=m.Dims(0, 512, 512, 10, 128, 128)) == m.MOE_OK
     import torch
     if not torch.cuda.is_available():

@@ -143,3 +143,28 @@ def test_lora_forward_is_deterministic():
     b = gpu_forward_lora(cfg, w, lo, xd)
     for k in ("idx", "sorted_route", "gu", "y", "out32"):
         assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+
+def test_lora_stages_replay_the_routes_of_moe_forward_lora():
+    """Routing replay: moe_permute on the recorded topk_idx, then
+    moe_grouped_ffn_lora and moe_combine, reproduce moe_forward_lora."""
+    cfg, layer, x = load_cfg("moe1k")
+    ad = WL.lora_adapters(cfg)
+    w, lo, xd = dev_weights(layer), dev_lora(ad), dev_bits(x)
+    say("case: moe1k, LoRA forward vs replayed routes through the stage calls")
+    full = gpu_forward_lora(cfg, w, lo, xd, with_gu=False)
+    d = dims_of(cfg)
+    routes = m.alloc_routes(d, DEV, logits=False)
+    routes.topk_idx.copy_(torch.from_numpy(full["idx"]).to(DEV))
+    routes.topk_gate.copy_(torch.from_numpy(full["gates"]).to(DEV))
+    saved = m.alloc_saved(d, DEV)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD_LORA, DEV)
+    m.check(m.moe_permute(d, routes, ws), "moe_permute")
+    m.check(m.moe_grouped_ffn_lora(d, xd, w, lo, routes, saved, ws), "moe_grouped_ffn_lora")
+    out32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    m.check(m.moe_combine(d, routes, saved, out32, None), "moe_combine")
+    torch.cuda.synchronize()
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+    assert np.array_equal(routes.sorted_route.cpu().numpy(), full["sorted_route"])
+    assert np.array_equal(saved.y.cpu().numpy().view(np.uint32), full["y"].view(np.uint32))
+    assert np.array_equal(out32.cpu().numpy().view(np.uint32), full["out32"].view(np.uint32))
