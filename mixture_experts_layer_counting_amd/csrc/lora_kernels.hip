@@ -13,9 +13,9 @@
 // token row x[t] (gate/up adapter, contraction H) or act_r as its bf16 pair
 // act_hi + act_lo (down adapter, contraction I: two passes, hi first).
 // The contraction runs on the matrix cores: wave w of a 64-row work item
-// owns rows 16w .. 16w + 15 and multiplies them by A_e^T (16 columns, zero
-// past the rank) with 16x16x32 bf16 MFMAs over K in ascending 32-wide steps,
-// fp32 accumulation from zero.  A row's result depends only on its own data,
+// owns rows 32w .. 32w + 31 (two 16-row blocks sharing each A_e operand) and
+// multiplies them by A_e^T (16 columns, zero past the rank) with 16x16x32
+// bf16 MFMAs over K in ascending 32-wide steps, fp32 accumulation from zero.  A row's result depends only on its own data,
 // never on the batch or its position in it.
 //
 // The result leaves as a bf16 pair per element, hi = bf16(z), lo =
@@ -28,7 +28,8 @@
 
 namespace moe {
 
-constexpr int kShrinkSteps = 4;  // 32-wide K steps per batch of loads
+constexpr int kShrinkSteps = 4;   // 32-wide K steps per batch of loads
+constexpr int kShrinkBlocks = 2;  // 16-row blocks of a wave (sharing its A_e operands)
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4m_t;
 
@@ -40,7 +41,7 @@ __device__ __forceinline__ f32x4m_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4m_t 
 }
 
 template <bool ACT>
-__global__ __launch_bounds__(256) void lora_shrink_kernel(
+__global__ __launch_bounds__(128) void lora_shrink_kernel(
     const uint16_t* __restrict__ v_hi, const uint16_t* __restrict__ v_lo,
     const uint16_t* __restrict__ a, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_route, const int32_t* __restrict__ tiles,
@@ -52,42 +53,56 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(
   if (gi.grp == E) return;  // the shared expert has no adapter
   const int rows = min(kRowsPerTile, gi.cnt - gi.row0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (16 * wave >= rows) return;  // no barriers below: waves are independent
+  const int rb0 = kShrinkBlocks * wave;  // first 16-row block of this wave
+  if (16 * rb0 >= rows) return;         // no barriers below: waves are independent
   const int r16 = lane & 15, kq = lane >> 4;
   const int64_t p0 = static_cast<int64_t>(gi.seg0) + gi.row0;
   // rows past the item's end repeat its last row (computed, not stored)
-  const int r = min(16 * wave + r16, rows - 1);
-  int64_t src;
-  if constexpr (ACT) {
-    src = (p0 + r) * Kd;
-  } else {
-    const int64_t rr = sorted_route[p0 + r];
-    src = ((rr >= 0 && rr < T * K) ? rr / K : 0) * Kd;
+  const uint16_t* xh[kShrinkBlocks];
+  const uint16_t* xl[kShrinkBlocks];
+#pragma unroll
+  for (int q = 0; q < kShrinkBlocks; ++q) {
+    const int r = min(16 * (rb0 + q) + r16, rows - 1);
+    int64_t src;
+    if constexpr (ACT) {
+      src = (p0 + r) * Kd;
+    } else {
+      const int64_t rr = sorted_route[p0 + r];
+      src = ((rr >= 0 && rr < T * K) ? rr / K : 0) * Kd;
+    }
+    xh[q] = v_hi + src + 8 * kq;
+    xl[q] = ACT ? v_lo + src + 8 * kq : nullptr;
   }
-  const uint16_t* xh = v_hi + src + 8 * kq;
-  const uint16_t* xl = ACT ? v_lo + src + 8 * kq : nullptr;
   const bool jv = r16 < rank;  // this lane's B column is a rank row of A_e
   const uint16_t* ar = a + (static_cast<int64_t>(gi.grp) * rank + (jv ? r16 : 0)) * Kd + 8 * kq;
 
-  u32x4_t h0[kShrinkSteps], l0[kShrinkSteps], b0[kShrinkSteps];
-  u32x4_t h1[kShrinkSteps], l1[kShrinkSteps], b1[kShrinkSteps];
-  auto fetch = [&](u32x4_t (&h)[kShrinkSteps], u32x4_t (&l)[kShrinkSteps], u32x4_t (&b)[kShrinkSteps],
-                   int k0) {
+  u32x4_t h0[kShrinkBlocks][kShrinkSteps], l0[kShrinkBlocks][kShrinkSteps], b0[kShrinkSteps];
+  u32x4_t h1[kShrinkBlocks][kShrinkSteps], l1[kShrinkBlocks][kShrinkSteps], b1[kShrinkSteps];
+  auto fetch = [&](u32x4_t (&h)[kShrinkBlocks][kShrinkSteps], u32x4_t (&l)[kShrinkBlocks][kShrinkSteps],
+                   u32x4_t (&b)[kShrinkSteps], int k0) {
 #pragma unroll
     for (int st = 0; st < kShrinkSteps; ++st) {
       const int k = k0 + 32 * st;
-      h[st] = ld16(xh + k);
-      if constexpr (ACT) l[st] = ld16(xl + k);
       b[st] = jv ? ld16(ar + k) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < kShrinkBlocks; ++q) {
+        h[q][st] = ld16(xh[q] + k);
+        if constexpr (ACT) l[q][st] = ld16(xl[q] + k);
+      }
     }
   };
-  f32x4m_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const u32x4_t (&h)[kShrinkSteps], const u32x4_t (&l)[kShrinkSteps],
-                     const u32x4_t (&b)[kShrinkSteps]) {
+  f32x4m_t acc[kShrinkBlocks];
+#pragma unroll
+  for (int q = 0; q < kShrinkBlocks; ++q) acc[q] = f32x4m_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4_t (&h)[kShrinkBlocks][kShrinkSteps],
+                     const u32x4_t (&l)[kShrinkBlocks][kShrinkSteps], const u32x4_t (&b)[kShrinkSteps]) {
 #pragma unroll
     for (int st = 0; st < kShrinkSteps; ++st) {
-      acc = mfma16x16x32(h[st], b[st], acc);
-      if constexpr (ACT) acc = mfma16x16x32(l[st], b[st], acc);
+#pragma unroll
+      for (int q = 0; q < kShrinkBlocks; ++q) {
+        acc[q] = mfma16x16x32(h[q][st], b[st], acc[q]);
+        if constexpr (ACT) acc[q] = mfma16x16x32(l[q][st], b[st], acc[q]);
+      }
     }
   };
   constexpr int KB = 32 * kShrinkSteps;  // contraction elements per batch
@@ -101,14 +116,17 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * wave + 4 * kq + i;
-    if (row < rows) {
-      uint16_t hi, lo;
-      split_hi_lo(acc[i], hi, lo);
-      uint16_t* o = zq + (p0 + row) * 2 * kLoraMaxRank;
-      o[r16] = hi;
-      o[kLoraMaxRank + r16] = lo;
+  for (int q = 0; q < kShrinkBlocks; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * (rb0 + q) + 4 * kq + i;
+      if (row < rows) {
+        uint16_t hi, lo;
+        split_hi_lo(acc[q][i], hi, lo);
+        uint16_t* o = zq + (p0 + row) * 2 * kLoraMaxRank;
+        o[r16] = hi;
+        o[kLoraMaxRank + r16] = lo;
+      }
     }
   }
 }
@@ -120,10 +138,10 @@ hipError_t launch_lora_shrink(const uint16_t* v_hi, const uint16_t* v_lo, const 
   if (rank < 1 || rank > kLoraMaxRank || Kd % (32 * kShrinkSteps)) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>(((static_cast<int64_t>(max_tiles) + 7) / 8) * 8);
   if (v_lo)
-    lora_shrink_kernel<true><<<grid, 256, 0, stream>>>(v_hi, v_lo, a, offsets, sorted_route, tiles,
+    lora_shrink_kernel<true><<<grid, 64 * kRowsPerTile / (16 * kShrinkBlocks), 0, stream>>>(v_hi, v_lo, a, offsets, sorted_route, tiles,
                                                        meta, z, T, Kd, E, K, rank);
   else
-    lora_shrink_kernel<false><<<grid, 256, 0, stream>>>(v_hi, nullptr, a, offsets, sorted_route,
+    lora_shrink_kernel<false><<<grid, 64 * kRowsPerTile / (16 * kShrinkBlocks), 0, stream>>>(v_hi, nullptr, a, offsets, sorted_route,
                                                         tiles, meta, z, T, Kd, E, K, rank);
   return hipGetLastError();
 }
