@@ -482,3 +482,33 @@ def test_lora_one_hot_down_adapter_moves_one_hidden_column():
     d = lo["y"] - base["y"]
     assert np.max(np.abs(d[:, h1] - s * act[:, i0])) <= 1e-15
     assert not np.any(np.delete(d, h1, axis=1))
+
+
+def test_lora_merged_weights_at_production_shape():
+    """The merged-weight identity on four tokens of the 2048-hidden,
+    512-intermediate layer with rank-6 adapters (only the touched experts'
+    weights are generated)."""
+    import workloads.lora as WL
+    cfg = W.CONFIGS["moe1k"]
+    layer = W.make_layer(cfg, with_experts=False)
+    x = W.tokens(cfg)[:4]
+    idx = O.select_routes(O.router_logits(x, layer["w_router"]), cfg.top_k)
+    E, H, I, K = cfg.experts, cfg.hidden, cfg.inter, cfg.top_k
+    w13 = np.zeros((E, 2 * I, H), np.uint16)
+    w2 = np.zeros((E, H, I), np.uint16)
+    for e in np.unique(idx):
+        a, b = W.expert_weights(cfg, int(e), 1)
+        w13[e], w2[e] = a[0], b[0]
+    layer["w13"], layer["w2"] = w13, w2
+    ad = WL.lora_adapters(cfg)
+    s = ad["scale"]
+    fwd = O.forward(layer, x, K, lora=ad)
+    bf = O.bf16_to_f64
+    x64 = bf(x)
+    for t in range(4):
+        for k in range(K):
+            e = int(fwd["idx"][t, k])
+            gu = (bf(w13[e]) + s * bf(ad["b13"][e]) @ bf(ad["a13"][e])) @ x64[t]
+            act = gu[:I] / (1.0 + np.exp(-gu[:I])) * gu[I:]
+            y = (bf(w2[e]) + s * bf(ad["b2"][e]) @ bf(ad["a2"][e])) @ act
+            assert np.max(np.abs(y - fwd["y"][t * K + k])) <= 1e-12
