@@ -512,3 +512,18 @@ def test_lora_merged_weights_at_production_shape():
             act = gu[:I] / (1.0 + np.exp(-gu[:I])) * gu[I:]
             y = (bf(w2[e]) + s * bf(ad["b2"][e]) @ bf(ad["a2"][e])) @ act
             assert np.max(np.abs(y - fwd["y"][t * K + k])) <= 1e-12
+
+
+def test_lora_adapter_inputs_are_seeded_and_shaped():
+    """The adapter generator (input side only) is a pure function of the
+    seed: same bits on every call, one stream per matrix and expert."""
+    import workloads.lora as WL
+    cfg = small_cfg()
+    a, b = WL.lora_adapters(cfg, 3), WL.lora_adapters(cfg, 3)
+    E, H, I = cfg.experts, cfg.hidden, cfg.inter
+    shapes = {"a13": (E, 3, H), "b13": (E, 2 * I, 3), "a2": (E, 3, I), "b2": (E, H, 3)}
+    for k, shp in shapes.items():
+        assert a[k].shape == shp and a[k].dtype == np.uint16
+        assert np.array_equal(a[k], b[k])
+    assert not np.array_equal(a["a13"][0], a["a13"][1])
+    assert a["rank"] == 3 and a["scale"] == WL.DEFAULT_SCALE
