@@ -274,7 +274,7 @@ typedef struct {
  * and per-element arithmetic of moe_forward, plus two shrink kernels and
  * the expand inside the grouped GEMMs' epilogues:
  *   z[p][j] = sum_k A_e[j][k] v_p[k] (16x16x32 bf16 MFMAs over ascending
- *            32-wide K steps, fp32 accumulation, one wave per 16 rows and
+ *            32-wide K steps, fp32 accumulation, one wave per 32 rows and
  *            the whole contraction), v_p = x_t for the gate/up adapter, act_r
  *            (its bf16 hi + lo, two passes) for down; kept as a bf16 pair
  *            z_hi + z_lo;
