@@ -10,9 +10,9 @@
 // runs in a fixed order.
 //
 // Precision: products of bf16 values are exact on the matrix cores; an fp32
-// operand (activation gradients, gate-scaled activations) enters as a bf16
-// hi/lo pair (hi = bf16(v), lo = bf16(v - hi), 16 significant bits of v),
-// i.e. two MFMAs per K step.
+// operand (activation gradients, gate-scaled activations) enters the weight
+// gradients exactly, as three bf16 planes (hi + mid + lo == v), one MFMA per
+// plane, and the input gradient as the first two (16 significant bits of v).
 // The grouped GEMMs accumulate in fp32 on the matrix cores in a fixed K
 // order; the small reductions (route weights, shared gate, router weights)
 // accumulate in fp64.
@@ -21,75 +21,44 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Route-weight and shared-gate gradients, one workgroup per token.
-// dg[k] = <dOut[t], y[t*K+k]>, ds = <dOut[t], shared_y[t]>, accumulated in
-// fp64 (each thread over its columns in ascending order, then a fixed
-// butterfly inside each wave, then the four waves in a fixed order).
+// Route-weight and shared-gate gradients, one thread per token.
+// dg[k] = <dOut[t], y[t*K+k]> and ds = <dOut[t], shared_y[t]>.  Since
+// y = W2_e act, the same value is <W2_e^T dOut[t], act>, a sum over the
+// intermediate dimension: the dact GEMM's epilogue forms it from its fp32
+// product D = dOut W2_e and the fp32 activation recomputed from the saved
+// gate/up values, as fp64 partial sums per 128-column tile (part[r][nt],
+// nt < Ie / 128).  Here they are added in ascending tile order in fp64.
 // dl[k] = g_k (dg_k - sum_j g_j dg_j) (softmax backward over the selected
 // slots); dz = ds * sg * (1 - sg).
 // ---------------------------------------------------------------------------
-template <int KT>
-__global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restrict__ dout,
-                                                       const float* __restrict__ y,
-                                                       const float* __restrict__ sy,
+__global__ __launch_bounds__(256) void bwd_gate_kernel(const double* __restrict__ dgp,
+                                                       const double* __restrict__ dsp,
                                                        const float* __restrict__ gate,
                                                        const float* __restrict__ sg,
                                                        float* __restrict__ dl,
-                                                       float* __restrict__ dz, int H, int K) {
-  // rows k < K are the route rows y[t*K + k], row K the shared row; all KT+1
-  // row loads of a column chunk are issued before any is used (surplus
-  // slots re-read the last route row and are not used)
-  __shared__ double red[4][KT + 1];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint16_t* d = dout + t * H;
-  const float* rowp[KT + 1];
-#pragma unroll
-  for (int k = 0; k < KT; ++k) rowp[k] = y + (t * K + min(k, K - 1)) * H;
-  rowp[KT] = sy ? sy + t * H : rowp[KT - 1];
-  double part[KT + 1];
-#pragma unroll
-  for (int k = 0; k <= KT; ++k) part[k] = 0.0;
-  for (int c = tid * 4; c < H; c += 1024) {
-    const uint2 dv = *reinterpret_cast<const uint2*>(d + c);
-    f32x4v_t v[KT + 1];
-#pragma unroll
-    for (int k = 0; k <= KT; ++k) v[k] = *reinterpret_cast<const f32x4v_t*>(rowp[k] + c);
-    const double d0 = bf16_to_f32(static_cast<uint16_t>(dv.x & 0xffffu));
-    const double d1 = bf16_to_f32(static_cast<uint16_t>(dv.x >> 16));
-    const double d2 = bf16_to_f32(static_cast<uint16_t>(dv.y & 0xffffu));
-    const double d3 = bf16_to_f32(static_cast<uint16_t>(dv.y >> 16));
-#pragma unroll
-    for (int k = 0; k <= KT; ++k) {
-      part[k] += d0 * v[k][0];
-      part[k] += d1 * v[k][1];
-      part[k] += d2 * v[k][2];
-      part[k] += d3 * v[k][3];
-    }
+                                                       float* __restrict__ dz, int64_t T, int K,
+                                                       int nt_route, int nt_shared, int nt_stride) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= T) return;
+  double mean = 0.0;
+  for (int k = 0; k < K; ++k) {
+    const double* pr = dgp + (t * K + k) * nt_stride;
+    double dg = 0.0;
+    for (int n = 0; n < nt_route; ++n) dg += pr[n];
+    mean += static_cast<double>(gate[t * K + k]) * dg;
   }
-  // slot s of the reduction: route k = s for s < K, the shared row at s = K
-#pragma unroll
-  for (int k = 0; k <= KT; ++k) {
-    double v = part[k];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (lane == 0) red[wave][k] = v;
+  for (int k = 0; k < K; ++k) {
+    const double* pr = dgp + (t * K + k) * nt_stride;
+    double dg = 0.0;
+    for (int n = 0; n < nt_route; ++n) dg += pr[n];
+    const double g = gate[t * K + k];
+    dl[t * K + k] = static_cast<float>(g * (dg - mean));
   }
-  __syncthreads();
-  if (tid == 0) {
-    double dg[KT + 1];
-#pragma unroll
-    for (int k = 0; k <= KT; ++k) dg[k] = (red[0][k] + red[1][k]) + (red[2][k] + red[3][k]);
-    double mean = 0.0;
-    for (int k = 0; k < K; ++k) mean += static_cast<double>(gate[t * K + k]) * dg[k];
-    for (int k = 0; k < K; ++k) {
-      const double g = gate[t * K + k];
-      dl[t * K + k] = static_cast<float>(g * (dg[k] - mean));
-    }
-    if (sy) {
-      const double s = sg[t];
-      dz[t] = static_cast<float>(dg[KT] * s * (1.0 - s));
-    }
+  if (dsp) {
+    double ds = 0.0;
+    for (int n = 0; n < nt_shared; ++n) ds += dsp[t * nt_stride + n];
+    const double s = sg[t];
+    dz[t] = static_cast<float>(ds * s * (1.0 - s));
   }
 }
 
@@ -113,16 +82,19 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const uint16_t* __restric
 //     (ds_read_b64_tr_b16), two per fragment.  The 64 bytes of padding per
 //     row make those reads free of bank conflicts on MI355X (measured with
 //     the LDS bank-conflict counter: 256- and 288-byte rows conflict).
-// An fp32 operand (dGU, g*act) is given as kGradPlanes bf16 planes, a hi/lo
-// pair (hi = bf16(v), lo = bf16(v - hi)), and takes one MFMA per plane per K
-// step, hi first.
+// An fp32 operand (dGU, g*act) is given as kGradPlanes bf16 planes, its
+// exact split hi + mid + lo, and takes one MFMA per plane per K step in plane
+// order: all three in the weight gradients, hi and mid in kDx.
 //
 // Modes (group g: routed expert g < E, shared expert g == E; p = row of the
 // group's segment in sorted order, t(p) its token):
 //   kDact: m = p (128-row tile), n = i < Ie, k = h < H.  A = dOut[t(p)][h]
 //          ([row][k]); B = W2_g[h][i] ([k][col]).  Epilogue: dact = D * g_p,
 //          SwiGLU backward with the saved gate/up pre-activations -> dGU
-//          planes [p][2Ie] and g_p*act planes [p][Ie].
+//          planes [p][2Ie] and g_p*act planes [p][Ie]; and the partial
+//          route-weight gradient sum_i D[p][i] act[p][i] over the tile's
+//          columns, fp64, in dgp[r][nt] (routed, r = sorted_route[p]) or
+//          dsp[t][nt] (shared).
 //   kDx:   m = p, n = h < H, k = j < 2Ie.  A = dGU planes ([row][k]);
 //          B = W13_g[j][h] ([k][col]).  Epilogue: row of dx_route (route row
 //          sorted_route[p]) or of dx_shared (token row).
@@ -140,6 +112,7 @@ enum BwdMode { kDact = 0, kDx = 1, kDw2 = 2, kDw13 = 3 };
 
 constexpr int kBT = kBwdRowsPerTile;  // edge of every output tile (128)
 constexpr int kBwdTokLds = 256;       // weight-gradient segments up to this length keep their tokens in LDS
+constexpr int kDactChunk = 16;        // K blocks per chunk of the general dact loop's two-level sum
 constexpr int kBK = 32;
 // [row][k] layout: 64-byte rows (32 k), 16-byte piece c of a row stored at
 // c ^ ((row >> 2) & 3), which keeps both the loaders' stores (4 rows x 4
@@ -190,6 +163,9 @@ struct BwdArgs {
   uint16_t* sdgu[kGradPlanes];   // [T][2Is]
   uint16_t* gact[kGradPlanes];   // planes of g*act [R][I]
   uint16_t* sgact[kGradPlanes];  // [T][Is]
+  double* dgp;                   // [R][nt_stride] partial <D, act> per column tile (routed)
+  double* dsp;                   // [T][nt_stride] (shared)
+  int nt_stride;
   float* dx_route;
   float* dx_shared;
   float* dw13;
@@ -263,7 +239,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
   static_assert(NKB == 0 || !WGRAD, "the unrolled loop is for the dgrad modes");
   constexpr int NSET = NKB > 0 ? 4 : 1;
-  constexpr int NPA = (MODE == kDx || MODE == kDw13) ? kGradPlanes : 1;
+  constexpr int NPA = MODE == kDx ? kDxPlanes : (MODE == kDw13 ? kGradPlanes : 1);
   constexpr int NPB = MODE == kDw2 ? kGradPlanes : 1;
   constexpr int APLANE = WGRAD ? kRPlane : kKPlane;
   constexpr int STAGE = NPA * APLANE + NPB * kRPlane;
@@ -459,6 +435,18 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
       stash_set(0, 0);
       if (WGRAD && nkb > 1) wg_tokens(1, tok);
     }
+    // dact over a long hidden size: the matrix cores accumulate each chunk
+    // of kDactChunk K blocks from zero and the chunk sums are added in
+    // ascending order into a second fp32 sum, which keeps the rounding of
+    // the long contraction near that of a kDactChunk * 32-term one
+    constexpr bool CHUNKED = MODE == kDact;
+    f32x16_t tot[2][2];
+    if constexpr (CHUNKED) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) tot[mb][nb] = zero16();
+    }
     for (int it = 0; it < nkb; ++it) {
       __syncthreads();
       const int cur = NSTAGE == 2 ? (it & 1) : 0;
@@ -468,10 +456,28 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
         if (WGRAD && it + 2 < nkb) wg_tokens(it + 2, tok);
       }
       compute(cur);
+      if (CHUNKED && (it + 1) % kDactChunk == 0) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) tot[mb][nb][v] += acc[mb][nb][v];
+            acc[mb][nb] = zero16();
+          }
+      }
       if (more) {
         if (NSTAGE == 1) __syncthreads();  // every wave is done reading the stage
         stash_set(0, NSTAGE == 2 ? cur ^ 1 : 0);
       }
+    }
+    if constexpr (CHUNKED) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[mb][nb][v] = tot[mb][nb][v] + acc[mb][nb][v];
     }
   }
 
@@ -519,6 +525,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
         const f32x4v_t u0 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col);
         const f32x4v_t u1 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col + 4);
         uint32_t pg[kGradPlanes][4], pu[kGradPlanes][4], pa[kGradPlanes][4];
+        double dot = 0.0;  // this thread's 8 columns of <D, act>
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float dv = e < 4 ? d0[e] : d1[e - 4];
@@ -529,11 +536,13 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
           const float dgate = dact * uv * sgm * (1.0f + gv * (1.0f - sgm));
           const float silu = silu_f32(gv);
           const float dup = dact * silu;
-          const float gact = g * (silu * uv);
-          uint16_t sgp[kGradPlanes], sup[kGradPlanes], sap[kGradPlanes];
-          split_hi_lo(dgate, sgp[0], sgp[1]);
-          split_hi_lo(dup, sup[0], sup[1]);
-          split_hi_lo(gact, sap[0], sap[1]);
+          const float act = silu * uv;
+          const float gact = g * act;
+          dot = fma(static_cast<double>(dv), static_cast<double>(act), dot);
+          uint16_t sgp[3], sup[3], sap[3];
+          split3(dgate, sgp);
+          split3(dup, sup);
+          split3(gact, sap);
           const int sh = 16 * (e & 1);
 #pragma unroll
           for (int q = 0; q < kGradPlanes; ++q) {
@@ -546,6 +555,18 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
               pu[q][e >> 1] |= static_cast<uint32_t>(sup[q]) << sh;
               pa[q][e >> 1] |= static_cast<uint32_t>(sap[q]) << sh;
             }
+          }
+        }
+        // the 16 threads of this row (consecutive lanes) add their partial
+        // sums in a fixed butterfly; the first writes the tile's sum
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 16);
+        if ((tid & 15) == 0) {
+          if (w.shared) {
+            a.dsp[rowp * a.nt_stride + w.nt] = dot;
+          } else {
+            const int64_t r = a.sorted_route[rowp];
+            if (r >= 0 && r < a.T * a.K) a.dgp[r * a.nt_stride + w.nt] = dot;
           }
         }
 #pragma unroll
@@ -786,17 +807,17 @@ __global__ __launch_bounds__(256) void bwd_dx_sum_kernel(
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_bwd_gate(const uint16_t* dout, const float* y, const float* sy, const float* gate,
-                           const float* sg, float* dl, float* dz, int64_t T, int H, int K,
+hipError_t launch_bwd_gate(const double* dgp, const double* dsp, const float* gate, const float* sg,
+                           float* dl, float* dz, int64_t T, int K, int I, int Is,
                            hipStream_t stream) {
-  if (K <= 10)
-    bwd_gate_kernel<10><<<static_cast<unsigned>(T), 256, 0, stream>>>(dout, y, sy, gate, sg, dl, dz, H, K);
-  else
-    bwd_gate_kernel<16><<<static_cast<unsigned>(T), 256, 0, stream>>>(dout, y, sy, gate, sg, dl, dz, H, K);
+  const int stride = (I > Is ? I : Is) / kBT;
+  bwd_gate_kernel<<<static_cast<unsigned>((T + 255) / 256), 256, 0, stream>>>(
+      dgp, dsp, gate, sg, dl, dz, T, K, I / kBT, Is / kBT, stride);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
+namespace {
+BwdArgs bwd_args(const BwdLaunch& L) {
   BwdArgs a;
   a.T = L.T;
   a.H = L.H;
@@ -824,22 +845,38 @@ hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
     a.gact[q] = L.gact[q];
     a.sgact[q] = L.sgact[q];
   }
+  a.dgp = L.dgp;
+  a.dsp = L.dsp;
+  a.nt_stride = (L.I > L.Is ? L.I : L.Is) / kBT;
   a.dx_route = L.dx_route;
   a.dx_shared = L.dx_shared;
   a.dw13 = L.dw13;
   a.dw2 = L.dw2;
   a.dws13 = L.dws13;
   a.dws2 = L.dws2;
+  return a;
+}
+
+unsigned rounds(int64_t items) { return static_cast<unsigned>(((items + 7) / 8) * 8); }
+}  // namespace
+
+hipError_t launch_bwd_dact(const BwdLaunch& L, hipStream_t stream) {
+  const BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  auto rounds = [](int64_t items) { return static_cast<unsigned>(((items + 7) / 8) * 8); };
   const int64_t dgrad_tiles = L.max_tiles_bwd;
-  // the unrolled dgrad instantiations cover H = 2048 (dact) and expert and
-  // shared sizes of 512 (dx)
+  // the unrolled instantiation covers H = 2048
   if (L.H == 2048)
     bwd_gemm_kernel<kDact, 2048 / kBK><<<rounds(dgrad_tiles * (Imax / kBT)), 256, 0, stream>>>(a);
   else
     bwd_gemm_kernel<kDact><<<rounds(dgrad_tiles * (Imax / kBT)), 256, 0, stream>>>(a);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
+  const BwdArgs a = bwd_args(L);
+  const int Imax = L.I > L.Is ? L.I : L.Is;
+  const int64_t dgrad_tiles = L.max_tiles_bwd;
+  // the unrolled dx instantiation covers expert and shared sizes of 512
   if (L.I == 512 && (L.Is == 0 || L.Is == 512))
     bwd_gemm_kernel<kDx, 2 * 512 / kBK><<<rounds(dgrad_tiles * (L.H / kBT)), 256, 0, stream>>>(a);
   else

@@ -39,7 +39,8 @@ struct Layout {
   // backward regions (after lora_end)
   size_t tiles_bwd = 0, meta_bwd = 0;  // work list of the backward's row tiles
   size_t dl = 0, dz = 0;             // [T][K], [T] f32
-  size_t dgu[moe::kGradPlanes] = {};    // [R][2I] bf16 planes (hi, lo)
+  size_t dgp = 0, dsp = 0;           // [R][NT], [T][NT] f64 partial dot products, NT = max(I, Is) / 128
+  size_t dgu[moe::kGradPlanes] = {};    // [R][2I] bf16 planes (hi, mid, lo)
   size_t sdgu[moe::kGradPlanes] = {};   // [T][2Is]
   size_t gact[moe::kGradPlanes] = {};   // [R][I]
   size_t sgact[moe::kGradPlanes] = {};  // [T][Is]
@@ -90,6 +91,9 @@ Layout make_layout(const moe_dims& d) {
   L.meta_bwd = take(64 * 4);
   L.dl = take(static_cast<size_t>(R) * 4);
   L.dz = take(static_cast<size_t>(T) * 4);
+  const size_t nt = static_cast<size_t>(I > Is ? I : Is) / moe::kBwdRowsPerTile;
+  L.dgp = take(static_cast<size_t>(R) * nt * 8);
+  L.dsp = take(static_cast<size_t>(T) * nt * 8);
   for (int q = 0; q < moe::kGradPlanes; ++q) {
     L.dgu[q] = take(static_cast<size_t>(R) * 2 * I * 2);
     L.sdgu[q] = take(static_cast<size_t>(T) * 2 * Is * 2);
@@ -687,10 +691,10 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
   a.in(routes->topk_gate, T * K * 4);
   a.in(routes->expert_offsets, (E + 1) * 4);
   a.in(routes->sorted_route, T * K * 4);
-  a.in(saved->y, T * K * H * 4);
+  a.in(saved->y, T * K * H * 4, false);  // not read: dg is formed from D and act
   a.in(saved->gu, T * K * 2 * I * 4);
   if (Is) {
-    a.in(saved->shared_y, T * H * 4);
+    a.in(saved->shared_y, T * H * 4, false);  // not read: ds is formed from D and act
     a.in(saved->shared_gate, T * 4);
     a.in(saved->shared_gu, T * 2 * Is * 4);
   }
@@ -714,9 +718,6 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
   MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles_bwd), nullptr, 0,
                                    at<int32_t>(ws, L.meta_bwd), d.experts, d.tokens, sh,
                                    moe::kBwdRowsPerTile, s));
-  MOE_LAUNCH(moe::launch_bwd_gate(d_out, saved->y, sh ? saved->shared_y : nullptr, routes->topk_gate,
-                                  sh ? saved->shared_gate : nullptr, at<float>(ws, L.dl),
-                                  at<float>(ws, L.dz), d.tokens, d.hidden, d.top_k, s));
   moe::BwdLaunch b;
   b.T = d.tokens;
   b.H = d.hidden;
@@ -745,12 +746,18 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
     b.gact[q] = at<uint16_t>(ws, L.gact[q]);
     b.sgact[q] = at<uint16_t>(ws, L.sgact[q]);
   }
+  b.dgp = at<double>(ws, L.dgp);
+  b.dsp = sh ? at<double>(ws, L.dsp) : nullptr;
   b.dx_route = at<float>(ws, L.dx_route);
   b.dx_shared = sh ? at<float>(ws, L.dx_shared) : nullptr;
   b.dw13 = grads->d_w13;
   b.dw2 = grads->d_w2;
   b.dws13 = sh ? grads->d_ws13 : nullptr;
   b.dws2 = sh ? grads->d_ws2 : nullptr;
+  MOE_LAUNCH(moe::launch_bwd_dact(b, s));
+  MOE_LAUNCH(moe::launch_bwd_gate(b.dgp, b.dsp, routes->topk_gate, sh ? saved->shared_gate : nullptr,
+                                  at<float>(ws, L.dl), at<float>(ws, L.dz), d.tokens, d.top_k, d.inter,
+                                  d.shared_inter, s));
   MOE_LAUNCH(moe::launch_bwd_gemms(b, s));
   MOE_LAUNCH(moe::launch_bwd_router(x, at<float>(ws, L.dl), routes->expert_offsets,
                                     routes->sorted_route, grads->d_w_router, d.tokens, d.hidden,

@@ -31,9 +31,12 @@ constexpr int kSortSmallWords = 16384;
 // Rows per row tile of the backward's grouped GEMMs (and the edge of their
 // 128x128 output tiles).
 constexpr int kBwdRowsPerTile = 128;
-// bf16 planes carrying each fp32 backward GEMM operand (dGU, g*act): a hi/lo
-// pair, hi = bf16(v), lo = bf16(v - hi).
-constexpr int kGradPlanes = 2;
+// bf16 planes carrying each fp32 backward GEMM operand (dGU, g*act): the
+// exact three-way split of split3 (hi, mid, lo; hi + mid + lo == v).  The
+// weight gradients take all three planes; the input-gradient GEMM takes the
+// first kDxPlanes (hi + mid = v to 16 significant bits).
+constexpr int kGradPlanes = 3;
+constexpr int kDxPlanes = 2;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);

@@ -105,12 +105,18 @@ struct BwdLaunch {
   uint16_t* sdgu[kGradPlanes];
   uint16_t* gact[kGradPlanes];
   uint16_t* sgact[kGradPlanes];
+  double* dgp;  // [R][max(I, Is) / 128] partial route-weight gradients (kDact)
+  double* dsp;  // [T][max(I, Is) / 128] partial shared-gate gradients (kDact)
   float *dx_route, *dx_shared;
   float *dw13, *dw2, *dws13, *dws2;
 };
 
-hipError_t launch_bwd_gate(const uint16_t* dout, const float* y, const float* sy, const float* gate,
-                           const float* sg, float* dl, float* dz, int64_t T, int H, int K,
+// Backward order: launch_bwd_dact (dGU and g*act planes, partial dot
+// products), launch_bwd_gate (dl, dz from the partials), launch_bwd_gemms
+// (dx, dW2, dW13), then the router, shared-gate and dX kernels.
+hipError_t launch_bwd_dact(const BwdLaunch& L, hipStream_t stream);
+hipError_t launch_bwd_gate(const double* dgp, const double* dsp, const float* gate, const float* sg,
+                           float* dl, float* dz, int64_t T, int K, int I, int Is,
                            hipStream_t stream);
 hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream);
 hipError_t launch_bwd_router(const uint16_t* x, const float* dl, const int32_t* offsets,

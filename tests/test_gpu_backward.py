@@ -1,19 +1,24 @@
 """GPU parity of the backward against the FP64 oracle, through the C ABI,
 plus its determinism and the batch invariance of the input gradient.
 
-The input gradient dX, a per-token quantity, is compared with the per-token
-rule |gpu - ref| <= 5e-5 + 1e-3 |ref|.  A weight gradient sums n per-token
-terms over the batch; its absolute floor grows as sqrt(n)
-(tests/gpu_util.assert_close_sum), n = the routes summed into it (an
-expert's route count, or T for the shared expert and its gate).  The
-relative part is taken against the sum of the terms' absolute values (sum
-over routes of |dGU| |x| for dW13, |dy| |act| for dW2, |dl| |x| for the
-router, |dz| |x| for the shared gate): each term carries a small relative
-error (the bf16 hi/lo operands, fp32 forward outputs), and terms of both
-signs cancel in the sum while their errors do not.  The small
-layer is compared in full; the 4096-token layer on sampled tokens (dX rows),
-sampled experts (their dW13, dW2 and router rows, from those experts' own
-routes) and the shared expert's weight gradients in full.
+Every gradient -- dX, dW_router, dW13, dW2, dWs13, dWs2, dw_sgate -- is held
+to the layer's elementwise rule |gpu - ref| <= 5e-5 + 1e-3 |ref| against the
+plain FP64 oracle (RL-Kernel pull request 557 page, contract commit,
+Backward bullet; the prior-art table's "Max abs vs FP64" column).  The one
+exception is assert_grad_close's split, used only where the method's fp32
+forward values alone are outside the rule (the hidden-16384 edge shape).  Beside
+each check the test prints the same ratio for two splits of the error: the
+GPU against an oracle fed the GPU's own saved fp32 forward values -- gate/up
+pre-activations, route gates, shared gate -- (the backward kernels' own
+error) and that oracle against the plain one (what the forward's fp32
+rounding points alone cost).
+
+The small layers are compared in full; the 4096-token layer on sampled
+tokens (dX rows), sampled experts (their dW13, dW2 and router rows, from
+those experts' own routes) and the shared expert's gradients in full.
+Batch invariance of dX and bit-equality of repeated backwards are checked
+on the tiny layer and on the 4096-token layer's shape, whose kernels (the
+unrolled dgrad instantiations at hidden 2048 / intermediate 512) differ.
 """
 import numpy as np
 import pytest
@@ -22,11 +27,12 @@ import torch
 import mixture_experts_layer_counting_amd as m
 import oracle as O
 import workloads as W
-from tests.gpu_util import (DEV, assert_close, assert_close_sum, bf16_rne_bits, compare_routes, dev_bits,
-                            dev_weights, dims_of, expert_term_scales, gate_term_scale, gpu_forward, load_cfg,
-                            router_term_scale, say, shared_term_scales)
+from tests.gpu_util import (DEV, assert_close, bf16_rne_bits, compare_routes, dev_bits, dev_weights, dims_of,
+                            fed_forward, gpu_forward, load_cfg, say, strict_ratio)
 
 pytestmark = pytest.mark.gpu
+
+GRADS = ("d_w_router", "d_w13", "d_w2", "d_ws13", "d_ws2", "d_w_sgate")
 
 
 def gpu_backward(cfg, w, xd, g, dout_d, ws=None):
@@ -41,42 +47,51 @@ def gpu_backward(cfg, w, xd, g, dout_d, ws=None):
     return dx32, dx16, grads
 
 
+def split_report(what, got, ref, fed):
+    say(f"  {what}: kernels alone (vs the oracle fed the GPU's fp32 forward values) worst err/tol "
+        f"{strict_ratio(got, fed):.3f}; those fp32 values alone {strict_ratio(fed, ref):.3f}")
+
+
+def assert_grad_close(got, ref, fed, what):
+    """The layer's rule against the plain oracle.  Only where the method's own
+    fp32 forward values already move the exact gradient beyond it (the
+    oracle fed those values is itself outside the rule) does the check
+    split: the kernels' error must meet the rule against that fed oracle,
+    and each element's distance from the plain oracle may exceed the rule by
+    no more than the fed oracle's own distance from it."""
+    split_report(what, got, ref, fed)
+    got = np.asarray(got, np.float64)
+    if strict_ratio(got, ref) <= 1.0 or strict_ratio(fed, ref) <= 1.0:
+        assert_close(got, ref, what)
+        return
+    say(f"  {what}: the fp32 forward values alone exceed the rule; checking the split")
+    assert_close(got, fed, f"{what} vs the oracle fed the GPU's fp32 forward values")
+    tol = 5e-5 + 1e-3 * np.abs(ref)
+    bad = np.abs(got - ref) > tol + np.abs(fed - ref)
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond the rule plus the inherent distance"
+
+
 def full_backward_check(cfg, layer, x, dout):
     w = dev_weights(layer)
     xd = dev_bits(x)
     g = gpu_forward(cfg, w, xd, training=True)
-    idx = g.routes.topk_idx.cpu().numpy()
+    h = g.host()
+    idx = h["idx"]
     ref_f = O.forward(layer, x, cfg.top_k)
     ties = compare_routes(idx, ref_f["idx"], ref_f["logits"])
     if ties:
         say(f"  {len(ties)} tokens with router ties: oracle uses the GPU routes")
         ref_f = O.forward(layer, x, cfg.top_k, forced_idx=idx)
     ref = O.backward(layer, x, ref_f, dout)
+    fed = O.backward(layer, x, fed_forward(layer, x, idx, h["gates"], h["gu"], h["route_pos"], h["sgu"], h["sg"]),
+                     dout)
     dx32, dx16, gr = gpu_backward(cfg, w, xd, g, dev_bits(dout))
-    assert_close(dx32.cpu().numpy(), ref["dx"], "dX")
-    assert np.array_equal(dx16.cpu().numpy().view(np.uint16), bf16_rne_bits(dx32.cpu().numpy()))
-    load = np.bincount(idx.reshape(-1), minlength=cfg.experts)
-    scales = {"d_w_router": router_term_scale(x, ref_f["idx"], ref["dl"], cfg.experts),
-              "d_w13": np.zeros(layer["w13"].shape), "d_w2": np.zeros(layer["w2"].shape)}
-    for e in np.nonzero(load)[0]:
-        scales["d_w13"][e], scales["d_w2"][e] = expert_term_scales(layer, x, dout, ref_f["idx"], ref_f["gates"],
-                                                                  ref_f["gu"], int(e))
-    for name, key in (("dW_router", "d_w_router"), ("dW13", "d_w13"), ("dW2", "d_w2")):
-        got = getattr(gr, key).cpu().numpy().astype(np.float64)
-        err = np.abs(got - ref[key])
-        floor = 5e-5 * np.sqrt(np.maximum(1, load)).reshape(-1, *([1] * (got.ndim - 1)))
-        scale = np.maximum(np.abs(ref[key]), scales[key])
-        ratio = err / (floor + 1e-3 * scale)
-        strict = err / (5e-5 + 1e-3 * np.abs(ref[key]))
-        say(f"  {name}: max-abs {err.max():.3e}, worst err/tol {ratio.max():.3f} (sum rule), "
-            f"{strict.max():.3f} (per-token rule)")
-        assert ratio.max() <= 1.0, f"{name}: {(ratio > 1).sum()} elements outside tolerance"
-    if cfg.shared_inter:
-        s13, s2 = shared_term_scales(layer, x, dout, ref_f["sg"], ref_f["sgu"])
-        assert_close_sum(gr.d_ws13.cpu().numpy(), ref["d_ws13"], "dWs13", cfg.tokens, s13)
-        assert_close_sum(gr.d_ws2.cpu().numpy(), ref["d_ws2"], "dWs2", cfg.tokens, s2)
-        assert_close_sum(gr.d_w_sgate.cpu().numpy(), ref["d_w_sgate"], "dw_sgate", cfg.tokens,
-                         gate_term_scale(x, ref["dz"]))
+    dx = dx32.cpu().numpy()
+    assert_grad_close(dx, ref["dx"], fed["dx"], "dX")
+    assert np.array_equal(dx16.cpu().numpy().view(np.uint16), bf16_rne_bits(dx))
+    for key in GRADS:
+        if key in ref:
+            assert_grad_close(getattr(gr, key).cpu().numpy(), ref[key], fed[key], key)
 
 
 def test_tiny_backward_full():
@@ -107,18 +122,20 @@ def test_bwd4k_sampled():
     dout = W.grad_out(cfg)
     say("case: bwd4k forward + backward on GPU")
     g = gpu_forward(cfg, w, xd, training=True)
+    h = g.host()
     dx32, dx16, gr = gpu_backward(cfg, w, xd, g, dev_bits(dout))
-    idx = g.routes.topk_idx.cpu().numpy()
+    idx = h["idx"]
     rng = np.random.default_rng(11)
     # dX rows of sampled tokens: the oracle backward of the token subset
-    tok = np.unique(np.concatenate([[0, 1, 63, 64, 2047, cfg.tokens - 1], rng.choice(cfg.tokens, 26, replace=False)]))
+    tok = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 2047, cfg.tokens - 1],
+                                    rng.choice(cfg.tokens, 40, replace=False)]))
     say(f"  oracle backward on {len(tok)} sampled tokens")
     fs = O.forward(layer, x[tok], cfg.top_k, forced_idx=idx[tok])
     compare_routes(idx[tok], O.select_routes(fs["logits"], cfg.top_k), fs["logits"])
     bs = O.backward(layer, x[tok], fs, dout[tok])
     assert_close(dx32.cpu().numpy()[tok], bs["dx"], "dX (sampled tokens)")
     # sampled experts: their weight gradients from their own routes
-    experts = [0, 17, 255, 511] + list(rng.choice(cfg.experts, 4, replace=False))
+    experts = [0, 17, 255, 511] + list(rng.choice(cfg.experts, 6, replace=False))
     dw13 = gr.d_w13.cpu().numpy()
     dw2 = gr.d_w2.cpu().numpy()
     dwr = gr.d_w_router.cpu().numpy()
@@ -127,20 +144,39 @@ def test_bwd4k_sampled():
         fe = O.forward(layer, x[te], cfg.top_k, forced_idx=idx[te])
         rows = np.nonzero(fe["idx"].reshape(-1) == e)[0]
         r13, r2 = O.expert_weight_grads(layer, x[te], dout[te], fe["idx"], fe["gates"], fe["gu"][rows], int(e))
-        s13, s2 = expert_term_scales(layer, x[te], dout[te], fe["idx"], fe["gates"], fe["gu"], int(e))
-        assert_close_sum(dw13[e], r13, f"dW13[{e}]", len(te), s13)
-        assert_close_sum(dw2[e], r2, f"dW2[{e}]", len(te), s2)
+        assert_close(dw13[e], r13, f"dW13[{e}] ({len(te)} routes)")
+        assert_close(dw2[e], r2, f"dW2[{e}]")
         be = O.backward(layer, x[te], fe, dout[te])
-        assert_close_sum(dwr[e], be["d_w_router"][e], f"dW_router[{e}]", len(te),
-                         router_term_scale(x[te], fe["idx"], be["dl"], cfg.experts)[e])
+        assert_close(dwr[e], be["d_w_router"][e], f"dW_router[{e}]")
     say("  oracle shared-expert gradients over all tokens")
     sh = O.shared_expert_grads(layer, x, dout)
-    _, s_sg, s_sgu = O.shared_expert(x, layer["ws13"], layer["ws2"], layer["w_sgate"])
-    s13, s2 = shared_term_scales(layer, x, dout, s_sg, s_sgu)
-    assert_close_sum(gr.d_ws13.cpu().numpy(), sh["d_ws13"], "dWs13", cfg.tokens, s13)
-    assert_close_sum(gr.d_ws2.cpu().numpy(), sh["d_ws2"], "dWs2", cfg.tokens, s2)
-    assert_close_sum(gr.d_w_sgate.cpu().numpy(), sh["d_w_sgate"], "dw_sgate", cfg.tokens,
-                     gate_term_scale(x, sh["dz"]))
+    # the same with the GPU's saved fp32 shared gate/up values and gate
+    s_gu = h["sgu"].astype(np.float64)
+    i_s = s_gu.shape[1] // 2
+    s_sg = h["sg"].astype(np.float64)
+    act = O.silu(s_gu[:, :i_s]) * s_gu[:, i_s:]
+    s_fed = act @ O.bf16_to_f64(layer["ws2"]).T
+    d_o = O.bf16_to_f64(dout)
+    dz_fed = (d_o * s_fed).sum(axis=1) * s_sg * (1.0 - s_sg)
+    fed = {"d_w_sgate": dz_fed @ O.bf16_to_f64(x)}
+    _, fed["d_ws2"], fed["d_ws13"], _ = O.swiglu_backward(s_sg[:, None] * d_o, s_gu, O.bf16_to_f64(x),
+                                                           layer["ws13"], layer["ws2"])
+    for key, name in (("d_ws13", "dWs13"), ("d_ws2", "dWs2"), ("d_w_sgate", "dw_sgate")):
+        got = getattr(gr, key).cpu().numpy()
+        split_report(name, got, sh[key], fed[key])
+        assert_close(got, sh[key], name)
+
+
+def bits(t):
+    return t.contiguous().view(torch.int32)
+
+
+def assert_same_backward(a, b, what):
+    assert torch.equal(bits(a[0]), bits(b[0])), f"{what}: dX differs"
+    for k in GRADS:
+        ta, tb = getattr(a[2], k), getattr(b[2], k)
+        if ta is not None:
+            assert torch.equal(bits(ta), bits(tb)), f"{what}: {k} differs"
 
 
 def test_backward_deterministic_and_dx_batch_invariant():
@@ -152,11 +188,54 @@ def test_backward_deterministic_and_dx_batch_invariant():
     g = gpu_forward(cfg, w, xd, training=True)
     a = gpu_backward(cfg, w, xd, g, dout)
     b = gpu_backward(cfg, w, xd, g, dout)
-    for t1, t2 in [(a[0], b[0])] + [(getattr(a[2], k), getattr(b[2], k)) for k in
-                                     ("d_w_router", "d_w13", "d_w2", "d_ws13", "d_ws2", "d_w_sgate")]:
-        assert torch.equal(t1.view(torch.int32), t2.view(torch.int32))
+    assert_same_backward(a, b, "tiny, second backward")
     for start in (0, 100, 248):
         sl = slice(start, start + 8)
         gs = gpu_forward(cfg, w, xd[sl].clone(), training=True)
         p = gpu_backward(cfg, w, xd[sl].clone(), gs, dout[sl].clone())
-        assert torch.equal(p[0].view(torch.int32), a[0][sl].view(torch.int32)), f"dX rows at {start} differ"
+        assert torch.equal(bits(p[0]), bits(a[0][sl])), f"dX rows at {start} differ"
+
+
+@pytest.fixture(scope="module")
+def layer4k():
+    cfg, layer, x = load_cfg("bwd4k")
+    return cfg, dev_weights(layer), x
+
+
+def test_bwd4k_backward_twice_is_bitwise_identical(layer4k):
+    cfg, w, x = layer4k
+    xd = dev_bits(x)
+    dout = dev_bits(W.grad_out(cfg))
+    say("case: bwd4k, forward + backward twice, every gradient compared bit for bit")
+    g = gpu_forward(cfg, w, xd, training=True)
+    a = gpu_backward(cfg, w, xd, g, dout)
+    g2 = gpu_forward(cfg, w, xd, training=True)
+    b = gpu_backward(cfg, w, xd, g2, dout)
+    assert_same_backward(a, b, "bwd4k, second forward + backward")
+
+
+def test_bwd4k_dx_probe_alone_vs_in_batches(layer4k):
+    """dX of 4 probe tokens alone vs at the first, middle and last position of
+    batches of sizes around the layer's switch points (4096 tokens: the up
+    projection's 96-row items and the router's one-pass kernel; the 128-row
+    backward tiles) up to 8192, through the production-shape kernels."""
+    cfg, w, _ = layer4k
+    n = 4
+    probes = dev_bits(W.tokens(cfg, n, stream=W.S_COMPANION, index=11))
+    pd = dev_bits(W.normal_bf16(cfg.seed, W.S_COMPANION, 12, (n, cfg.hidden), 1.0))
+    filler = dev_bits(W.tokens(cfg, 8192, stream=W.S_COMPANION, index=13))
+    fd = dev_bits(W.normal_bf16(cfg.seed, W.S_COMPANION, 14, (8192, cfg.hidden), 1.0))
+    ref = gpu_backward(cfg, w, probes, gpu_forward(cfg, w, probes, training=True), pd)[0]
+    d = dims_of(cfg, 8192)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD, DEV)
+    for B in (8, 127, 128, 129, 1024, 4095, 4096, 4097, 8192):
+        for where in ("first", "middle", "last"):
+            start = {"first": 0, "middle": (B - n) // 2, "last": B - n}[where]
+            xb = filler[:B].clone()
+            db = fd[:B].clone()
+            xb[start:start + n] = probes
+            db[start:start + n] = pd
+            say(f"case: bwd4k dX, batch {B}, probes at {where} ({start})")
+            g = gpu_forward(cfg, w, xb, training=True, ws=ws)
+            dx = gpu_backward(cfg, w, xb, g, db, ws=ws)[0]
+            assert torch.equal(bits(dx[start:start + n]), bits(ref)), f"batch {B} {where}: dX differs"
