@@ -194,10 +194,16 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
 
 /* Backward (contract, Backward bullet).
  * Inputs: the forward's x, routes and saved tensors (saved->gu, and
- * saved->shared_gu when Is > 0, must have been written), d_out [T][H] bf16.
+ * saved->shared_gu and saved->shared_gate when Is > 0, must have been
+ * written; saved->y and saved->shared_y are not read and may be NULL),
+ * d_out [T][H] bf16.
  * Outputs: d_x_f32 [T][H] (and its bf16 rounding in d_x_bf16 if non-NULL)
  * and every weight gradient in `grads` (fp32, overwritten).
- *   dg[t][k] = <d_out[t], y[t*K+k]>   (fixed per-token reduction order)
+ *   dg[t][k] = <d_out[t], y[t*K+k]>, formed as the equal sum over the
+ *              intermediate size <W2_e^T d_out[t], act>, in fp64 from the
+ *              fp32 GEMM product and the fp32 activation recomputed from
+ *              saved->gu, in a fixed per-route order (the shared gate's
+ *              <d_out, shared_y> likewise)
  *   dl = g * (dg - sum_j g_j dg_j)     (softmax backward over selected slots)
  *   route r: dy = g * d_out[t]; dact = dy W2_e; SwiGLU backward -> dgu;
  *            dx_r = dgu W13_e; dW2_e = sum_r dy^T act; dW13_e = sum_r dgu^T x
@@ -206,8 +212,10 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
  *   router:  d_w_router[e] = sum_t dl[t][e] x[t];  dx_router = sum_k dl W_r
  *   d_x[t] = ((sum of dx_r over its routes in ascending expert id) +
  *            dx_shared) + dz * w_sgate + dx_router, in that order, fp32.
- * Weight-gradient sums run over routes (tokens) in ascending order; no
- * atomics anywhere. */
+ * Precision: the weight-gradient GEMMs take their fp32 operands (dgu,
+ * g * act) exactly as three bf16 planes; products of bf16 values are exact
+ * and accumulate in fp32.  Weight-gradient sums run over routes (tokens) in
+ * ascending order; no atomics anywhere. */
 int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                  const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
                  float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws,
