@@ -1,19 +1,33 @@
 #!/usr/bin/env python3
-"""Forward throughput of the routed 512-expert top-10 MoE layer on one MI355X.
+"""Forward (and backward) throughput of the routed 512-expert top-10 MoE
+layer on one MI355X.
 
 One step = one whole forward pass (router, top-k, permutation, grouped
 SwiGLU expert GEMMs with the shared expert, combine) over one batch of
 seeded synthetic tokens, through the C ABI, inputs already resident in HBM.
 The headline workload is the 1024-token layer (hidden 2048, 512 experts
-top-10, expert and shared intermediate 512); the 8192-token layer is reported
-alongside under "secondary".
+top-10, expert and shared intermediate 512).
 
-Prints ONE JSON line.  Besides the throughput it carries
-  roofline      the dominant kernel (ffn_up) against the HBM peak, timed live
-                with HIP events recorded by moe_forward_profiled on the
-                stream the kernels run on, over the timed steps;
-  layer_roofline the whole forward against max(FLOP/MFMA peak, bytes/HBM peak);
-  cpu_baseline  the FP64 oracle timed on this host on a bounded token sample.
+Timing protocol (the RL-Kernel pull request 557 page, "Latency" paragraph:
+warm-up, then the median of 20 forward calls and of 5 forward + backward
+calls), with the caches handled: W untimed warm-up calls, then K timed calls,
+each bracketed by HIP events on the kernels' stream, with a 1 GiB scratch
+write between calls so that no call finds the previous one's bytes in L2 or
+the 256 MB MALL (followed by a 1 GiB read, so that the write's dirty lines
+are written back before the call rather than during it).  ms_per_step is the median call; p10/p90 beside it; the
+wall clock of the whole timed loop (evictions included) and a back-to-back
+run without evictions are reported too.
+
+Prints ONE JSON line.  Besides the headline it carries
+  configs       every forward workload (tiny flushed and warm, 1K, 8K, the
+                skewed 16K) with its roofline fractions;
+  roofline      the dominant kernel (ffn_up at 1K) against the HBM peak,
+                timed live with HIP events recorded by moe_forward_profiled
+                on the stream the kernels run on;
+  backward      the 4096-token backward: 5 forward + backward calls and K
+                backward-only calls;
+  cpu_baseline  the FP64 oracle timed on this host on bounded token samples
+                of all five workloads.
 
 usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -26,6 +40,20 @@ import json
 import os
 import sys
 import time
+
+
+def _blas_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(n, int(cap))) if cap and cap.isdigit() else n
+
+
+# the oracle's BLAS threads are pinned before numpy is first imported
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = str(_blas_threads())
 
 import numpy as np
 
@@ -122,30 +150,68 @@ def device_layer(layer):
                      w_sgate=bits(layer["w_sgate"]))
 
 
-def run_config(cfg, w, steps, warmup, hip):
-    """Time `steps` profiled forwards; returns a dict of measurements."""
+class Evictor:
+    """Between timed calls: a 1 GiB fill (more than L2, 4 MB per XCD, and
+    the 256 MB MALL hold), then a 1 GiB read of another buffer, which pushes
+    the fill's dirty lines out before the timed call, so that the call
+    neither finds its own bytes in a cache nor pays for write-backs that
+    are not its own."""
+
+    def __init__(self, mib=1024):
+        import torch
+        n = mib * (1 << 20) // 4
+        self.wbuf = torch.empty(n, dtype=torch.float32, device="cuda:0")
+        self.rbuf = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda:0")
+        self.n = 0
+
+    def __call__(self):
+        import torch
+        self.n += 1
+        self.wbuf.fill_(float(self.n & 0xff))
+        torch.sum(self.rbuf, out=self.sink)
+
+
+def stats(ms):
+    a = np.asarray(ms, np.float64)
+    return {"median_ms": float(np.median(a)), "p10_ms": float(np.percentile(a, 10)),
+            "p90_ms": float(np.percentile(a, 90)), "mean_ms": float(a.mean()), "calls": int(a.size)}
+
+
+def forward_inputs(cfg, w):
     import torch
     import mixture_experts_layer_counting_amd as m
     import workloads as W
     dev = torch.device("cuda:0")
     x = torch.from_numpy(W.tokens(cfg).view(np.int16)).to(dev)
     d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
-    routes = m.alloc_routes(d, dev, logits=False)
-    saved = m.alloc_saved(d, dev)
-    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev)
-    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, dev)
+    return dict(d=d, x=x, routes=m.alloc_routes(d, dev, logits=False), saved=m.alloc_saved(d, dev),
+                out16=torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev),
+                ws=m.alloc_workspace(d, m.MOE_OP_FORWARD, dev))
+
+
+def run_config(cfg, w, steps, warmup, hip, evict, breakdown=True):
+    """Time `steps` forwards of `cfg`, each bracketed by HIP events on the
+    kernels' stream with an eviction write before it (the events around
+    ffn_up give the roofline kernel's duration in the same calls); then a
+    back-to-back run of `steps` forwards without evictions (wall clock), and,
+    untimed, one pass with an event before every kernel for the per-kernel
+    breakdown.  Returns the measurements."""
+    import torch
+    import mixture_experts_layer_counting_amd as m
+    f = forward_inputs(cfg, w)
+    d, x, routes, saved, out16, ws = f["d"], f["x"], f["routes"], f["saved"], f["out16"], f["ws"]
     names = m.forward_kernel_names(d)
     nk = len(names)
     assert nk == m.moe_forward_kernel_count(d)
     iu = names.index("ffn_up")
-    # timed region: events only around ffn_up (the roofline kernel), so the
-    # step time carries no per-kernel marker overhead
-    up_evs = []
+    stream = torch.cuda.current_stream()
+    evs = []
     for _ in range(steps):
         arr = (ctypes.c_void_p * (nk + 1))()
-        arr[iu], arr[iu + 1] = hip.event(), hip.event()
-        up_evs.append(arr)
-    stream = torch.cuda.current_stream()
+        for k in {0, iu, iu + 1, nk}:
+            arr[k] = hip.event()
+        evs.append(arr)
 
     def fwd():
         m.check(m.moe_forward(d, w, x, routes, saved, None, out16, ws, stream), "moe_forward")
@@ -153,53 +219,71 @@ def run_config(cfg, w, steps, warmup, hip):
     for _ in range(warmup):
         fwd()
     torch.cuda.synchronize()
-    # timed region: exactly `steps` forwards
+    # timed region: exactly `steps` forwards, an eviction write before each
     t0 = time.perf_counter()
     for i in range(steps):
-        m.check(m.moe_forward_profiled(d, w, x, routes, saved, None, out16, ws, up_evs[i], stream),
-                "moe_forward_profiled")
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    up_ms = [hip.elapsed_ms(up_evs[i][iu], up_evs[i][iu + 1]) for i in range(steps)]
-    # untimed: the same number of forwards with an event before every kernel,
-    # for the per-kernel breakdown (the markers add their own gaps)
-    evs = [(ctypes.c_void_p * (nk + 1))(*[hip.event() for _ in range(nk + 1)]) for _ in range(steps)]
-    for i in range(steps):
+        evict()
         m.check(m.moe_forward_profiled(d, w, x, routes, saved, None, out16, ws, evs[i], stream),
                 "moe_forward_profiled")
     torch.cuda.synchronize()
-    per_kernel = {n: [] for n in names}
-    for i in range(steps):
-        for k, n in enumerate(names):
-            per_kernel[n].append(hip.elapsed_ms(evs[i][k], evs[i][k + 1]))
+    wall = time.perf_counter() - t0
+    call_ms = [hip.elapsed_ms(evs[i][0], evs[i][nk]) for i in range(steps)]
+    up_ms = [hip.elapsed_ms(evs[i][iu], evs[i][iu + 1]) for i in range(steps)]
+    # back to back, no evictions, wall clock
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    b2b = (time.perf_counter() - t0) / steps * 1e3
+    per_kernel = {}
+    if breakdown:
+        # untimed: an event before every kernel (each marker adds its own gap)
+        mk = [(ctypes.c_void_p * (nk + 1))(*[hip.event() for _ in range(nk + 1)]) for _ in range(3)]
+        for i in range(3):
+            evict()
+            m.check(m.moe_forward_profiled(d, w, x, routes, saved, None, out16, ws, mk[i], stream),
+                    "moe_forward_profiled")
+        torch.cuda.synchronize()
+        per_kernel = {n: float(np.median([hip.elapsed_ms(mk[i][k], mk[i][k + 1]) for i in range(3)]))
+                      for k, n in enumerate(names)}
     assert m.moe_last_device_error(ws) == m.MOE_OK
     touched = int((np.diff(routes.expert_offsets.cpu().numpy()) > 0).sum())
-    return dict(wall=wall, up_ms=float(np.mean(up_ms)),
-                per_kernel={n: float(np.mean(v)) for n, v in per_kernel.items()}, touched=touched)
+    load = np.diff(routes.expert_offsets.cpu().numpy())
+    return dict(call=stats(call_ms), up=stats(up_ms), wall_ms=wall / steps * 1e3, b2b_ms=b2b,
+                per_kernel=per_kernel, touched=touched, max_load=int(load.max()),
+                empty=int((load == 0).sum()))
 
 
-def summarize(cfg, r, steps):
-    ms = r["wall"] / steps * 1e3
-    up_ms = r["up_ms"]
-    up_bytes = ffn_up_bytes(cfg, r["touched"])
-    dn_bytes = ffn_down_bytes(cfg, r["touched"])
+def summarize(cfg, r):
+    ms = r["call"]["median_ms"]
     flop, byts = layer_work(cfg, r["touched"])
-    t_roof = max(flop / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
-    return dict(
+    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = byts / (PEAK_HBM_GBS * 1e9)
+    t_roof = max(t_mfma, t_hbm)
+    out = dict(
+        workload=f"{cfg.name}: {cfg.tokens} tokens, hidden {cfg.hidden}, {cfg.experts} experts top-{cfg.top_k}, "
+                 f"expert inter {cfg.inter}, shared inter {cfg.shared_inter}"
+                 + (f", router bias Zipf s={cfg.zipf_s} (tau {cfg.zipf_tau}, {cfg.zipf_off} experts off)"
+                    if cfg.zipf_s else ""),
         tokens_per_s=cfg.tokens / (ms / 1e3),
-        ms_per_step=ms,
-        ffn_up_ms=up_ms,
-        kernel_ms=r["per_kernel"],
-        touched_experts=r["touched"],
-        ffn_up_gbs=up_bytes / (up_ms / 1e3) / 1e9,
-        ffn_down_gbs=dn_bytes / (r["per_kernel"]["ffn_down"] / 1e3) / 1e9,
+        ms_per_step=ms, p10_ms=r["call"]["p10_ms"], p90_ms=r["call"]["p90_ms"],
+        wall_ms_per_step_incl_eviction=r["wall_ms"], back_to_back_ms_per_step=r["b2b_ms"],
+        ffn_up_ms=r["up"]["median_ms"],
+        kernel_ms_marked=r["per_kernel"],
+        touched_experts=r["touched"], max_expert_routes=r["max_load"], empty_experts=r["empty"],
         layer_roofline=dict(
-            flop=flop, bytes=byts, t_roof_ms=t_roof * 1e3,
-            bound="mfma" if flop / (PEAK_BF16_TFLOPS * 1e12) > byts / (PEAK_HBM_GBS * 1e9) else "hbm",
+            flop=flop, bytes=byts, t_roof_ms=t_roof * 1e3, t_mfma_ms=t_mfma * 1e3, t_hbm_ms=t_hbm * 1e3,
+            bound="mfma" if t_mfma > t_hbm else "hbm",
             frac=t_roof / (ms / 1e3),
             hbm_frac=byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9),
-            mfma_frac=flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)),
+            mfma_frac=flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
+            mfma_frac_cap=t_mfma / t_roof),
     )
+    if r["per_kernel"]:
+        out["ffn_up_gbs"] = ffn_up_bytes(cfg, r["touched"]) / (r["up"]["median_ms"] / 1e3) / 1e9
+        out["ffn_down_gbs"] = ffn_down_bytes(cfg, r["touched"]) / (r["per_kernel"]["ffn_down"] / 1e3) / 1e9
+    return out
 
 
 def expert_share(m, cfg, w, x, share):
@@ -361,14 +445,14 @@ def run_lora(cfg, w, steps, warmup):
             "plain_forward_ms": ms_plain, "adapter_bytes": sum(int(ad[k].nbytes) for k in ("a13", "b13", "a2", "b2"))}
 
 
-def run_backward(cfg, steps, warmup):
-    """Forward (training mode) once, then `steps` timed backward passes of
-    the same batch (HIP-event timed on the kernels' stream)."""
+def run_backward(cfg, w, steps, warmup, evict, fb_calls=5):
+    """`fb_calls` forward (training mode) + backward calls, then `steps`
+    backward-only calls of the same batch, each HIP-event timed on the
+    kernels' stream with an eviction write before it."""
     import torch
     import mixture_experts_layer_counting_amd as m
     import workloads as W
     dev = torch.device("cuda:0")
-    w = device_layer(W.make_layer(cfg))
     x = torch.from_numpy(W.tokens(cfg).view(np.int16)).to(dev)
     dout = torch.from_numpy(W.grad_out(cfg).view(np.int16)).to(dev)
     d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
@@ -376,59 +460,112 @@ def run_backward(cfg, steps, warmup):
     routes = m.alloc_routes(d, dev, logits=False)
     saved = m.alloc_saved(d, dev, training=True)
     out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev)
-    m.check(m.moe_forward(d, w, x, routes, saved, None, out16, ws), "moe_forward")
     grads = m.alloc_grads(d, dev)
     dx32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    def fwd():
+        m.check(m.moe_forward(d, w, x, routes, saved, None, out16, ws, stream), "moe_forward")
+
     def bwd():
         m.check(m.moe_backward(d, w, x, routes, saved, dout, dx32, None, grads, ws, stream), "moe_backward")
 
-    for _ in range(warmup):
-        bwd()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        bwd()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    def timed(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            evict()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return stats([e0.elapsed_time(e1) for e0, e1 in ev])
+
+    fb = timed(lambda: (fwd(), bwd()), fb_calls)
+    bo = timed(bwd, steps)
+    assert m.moe_last_device_error(ws) == m.MOE_OK
     touched = int((np.diff(routes.expert_offsets.cpu().numpy()) > 0).sum())
     H, I, Is, T, R, E = cfg.hidden, cfg.inter, cfg.shared_inter, cfg.tokens, cfg.routes, cfg.experts
     # algorithmic bytes: weights read, fp32 weight gradients written, per-route
-    # and per-token activations read once (Y, gate/up, x, dOut), dx route rows
+    # and per-token activations read once (gate/up, x, dOut), dx route rows
     # written and read once, dX written
     byts = (touched * 3 * I * H * 2 + 3 * Is * H * 2 + E * H * 4 + touched * 3 * I * H * 4 + 3 * Is * H * 4
-            + E * H * 4 + R * H * 4 + R * 2 * I * 4 + T * 2 * Is * 4 + T * H * 4 + 2 * T * H * 2
+            + E * H * 4 + R * 2 * I * 4 + T * 2 * Is * 4 + T * H * 4 + 2 * T * H * 2
             + R * H * 4 * 2 + T * H * 4)
     flop = 2 * 2 * (R * 3 * I * H + T * 3 * Is * H)
+    ms = bo["median_ms"]
     t_roof = max(flop / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
-    return {"workload": f"{cfg.name}: {T} tokens backward", "ms": ms, "tokens_per_s": T / (ms / 1e3),
+    return {"workload": f"{cfg.name}: {T} tokens backward (hidden {H}, {E} experts top-{cfg.top_k}, "
+                        f"inter {I}, shared {Is})",
+            "ms": ms, "p10_ms": bo["p10_ms"], "p90_ms": bo["p90_ms"], "calls": bo["calls"],
+            "tokens_per_s": T / (ms / 1e3),
+            "fwd_bwd_ms": fb["median_ms"], "fwd_bwd_p10_ms": fb["p10_ms"], "fwd_bwd_p90_ms": fb["p90_ms"],
+            "fwd_bwd_calls": fb["calls"], "fwd_bwd_tokens_per_s": T / (fb["median_ms"] / 1e3),
             "bytes": byts, "flop": flop, "t_roof_ms": t_roof * 1e3, "roofline_frac": t_roof / (ms / 1e3),
-            "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9)}
+            "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9),
+            "mfma_frac": flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)}
 
 
-def cpu_baseline(cfg, layer, budget_s=12.0):
-    """The FP64 oracle as it stands, on the first tokens of the same workload,
-    64 at a time until `budget_s` seconds have passed."""
-    import oracle as O
-    import workloads as W
+def host_info():
+    """CPU model, BLAS library and thread count of this host."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    blas, threads = "unknown", 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = int(info[0].get("num_threads", 1))
     except Exception:  # pragma: no cover
-        threads = 1
-    x = W.tokens(cfg)
-    done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and done < cfg.tokens:
-        tok = np.arange(done, min(done + 64, cfg.tokens))
-        O.forward(layer, x, cfg.top_k, tokens=tok)
-        done += len(tok)
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle forward (numpy float64) on tokens 0..{done - 1} of the {cfg.name} workload, "
-                      f"{el:.1f} s"}
+        pass
+    return model, blas, threads
+
+
+def cpu_baseline(layers, sample=32, bwd_sample=16, tiny_calls=20):
+    """The FP64 oracle as it stands, timed on this host: for each workload one
+    warm-up call and the median of 3 calls (the tiny one: `tiny_calls`),
+    excluding data generation, on the workload's first `sample` tokens (the
+    whole batch for the tiny one; `bwd_sample` for the backward workload,
+    whose oracle allocates the dense fp64 weight gradients of every expert);
+    forward for the forward workloads,
+    forward + backward for the backward one.  Reported as tokens/s."""
+    import oracle as O
+    import workloads as W
+    model, blas, threads = host_info()
+    per = {}
+    for name, layer in layers.items():
+        cfg = W.CONFIGS[name]
+        n = cfg.tokens if name == "tiny" else min(bwd_sample if cfg.backward else sample, cfg.tokens)
+        x = W.tokens(cfg)[:n]
+        if cfg.backward:
+            dout = W.grad_out(cfg)[:n]
+            fn = lambda: O.backward(layer, x, O.forward(layer, x, cfg.top_k), dout)
+        else:
+            fn = lambda: O.forward(layer, x, cfg.top_k)
+        fn()
+        times = []
+        for _ in range(tiny_calls if name == "tiny" else 3):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        med = float(np.median(times))
+        per[name] = {"tokens_per_s": n / med, "median_s": med, "tokens": n, "calls": len(times),
+                     "what": "forward + backward" if cfg.backward else "forward"}
+        log(f"bench: cpu oracle {name}: {n / med:.1f} tokens/s")
+    head = per["moe1k"]
+    return {"value": head["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle (numpy float64) on the first {head['tokens']} tokens of the moe1k workload, "
+                      f"median of {head['calls']} calls after one warm-up; every workload in per_config",
+            "cpu_model": model, "blas": blas, "per_config": per}
 
 
 def main():
@@ -437,7 +574,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="moe1k")
-    ap.add_argument("--secondary", default="moe8k", help="second workload to report, or 'none'")
+    ap.add_argument("--configs", default="tiny,moe8k,skew16k",
+                    help="further forward workloads to report (comma separated), or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", default="bwd4k", help="workload of the backward timing, or 'none'")
     ap.add_argument("--ep-share", type=int, default=8,
@@ -446,6 +584,7 @@ def main():
                     help="also time the forward with block-scaled FP8 expert weights (0: off)")
     ap.add_argument("--lora", type=int, default=1,
                     help="also time the forward with LoRA adapters on the routed experts (0: off)")
+    ap.add_argument("--no-evict", action="store_true", help="time without the eviction writes (profiling runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -460,9 +599,34 @@ def main():
     m.load_library()
     hip = Hip()
     cfg = W.CONFIGS[args.config]
-    log(f"bench: generating {cfg.name} weights")
-    layer = W.make_layer(cfg)
-    w = device_layer(layer)
+    extra = [] if args.configs == "none" else [c for c in args.configs.split(",") if c and c != cfg.name]
+    # host layers: the 2048-hidden workloads share one set of weights (the
+    # skewed one adds its router bias)
+    host = {}
+
+    def host_layer(c):
+        key = (c.hidden, c.inter, c.shared_inter, c.experts, c.seed)
+        if key not in host:
+            log(f"bench: generating the weights of {c.name}")
+            host[key] = W.make_layer(c)
+        base = host[key]
+        return base if c.zipf_s == 0.0 else dict(base, router_bias=W.zipf_bias(c))
+
+    dev_cache = {}
+
+    def dev_layer(c):
+        key = (c.hidden, c.inter, c.shared_inter, c.experts, c.seed)
+        if key not in dev_cache:
+            dev_cache[key] = device_layer(host_layer(c))
+        w = dev_cache[key]
+        if c.zipf_s == 0.0:
+            return w
+        b = torch.from_numpy(np.ascontiguousarray(W.zipf_bias(c), np.float32)).to("cuda:0")
+        return m.Weights(w_router=w.w_router, w13=w.w13, w2=w.w2, router_bias=b, ws13=w.ws13, ws2=w.ws2,
+                         w_sgate=w.w_sgate)
+
+    w = dev_layer(cfg)
+    evict = (lambda: None) if args.no_evict else Evictor()
     torch.cuda.synchronize()
 
     if args.copy_probe_mib:
@@ -474,20 +638,23 @@ def main():
         del a, b
 
     log(f"bench: {cfg.name} warmup {args.warmup}, steps {args.steps}")
-    main_r = run_config(cfg, w, args.steps, args.warmup, hip)
-    main_s = summarize(cfg, main_r, args.steps)
-    log(f"bench: {cfg.name} {main_s['ms_per_step']:.3f} ms/step, kernels {main_s['kernel_ms']}")
+    main_r = run_config(cfg, w, args.steps, args.warmup, hip, evict)
+    main_s = summarize(cfg, main_r)
+    log(f"bench: {cfg.name} median {main_s['ms_per_step']:.3f} ms (p10 {main_s['p10_ms']:.3f}, "
+        f"p90 {main_s['p90_ms']:.3f}), back to back {main_s['back_to_back_ms_per_step']:.3f} ms, "
+        f"kernels {main_s['kernel_ms_marked']}")
 
-    secondary = {}
-    if args.secondary != "none":
-        c2 = W.CONFIGS[args.secondary]
-        same_weights = (c2.hidden, c2.inter, c2.shared_inter, c2.experts, c2.seed, c2.zipf_s) == \
-                       (cfg.hidden, cfg.inter, cfg.shared_inter, cfg.experts, cfg.seed, cfg.zipf_s)
-        w2 = w if same_weights else device_layer(W.make_layer(c2))
+    configs = {cfg.name: main_s}
+    for name in extra:
+        c2 = W.CONFIGS[name]
         log(f"bench: {c2.name} warmup {args.warmup}, steps {args.steps}")
-        r2 = run_config(c2, w2, args.steps, args.warmup, hip)
-        secondary[c2.name] = summarize(c2, r2, args.steps)
-        log(f"bench: {c2.name} {secondary[c2.name]['ms_per_step']:.3f} ms/step")
+        r2 = run_config(c2, dev_layer(c2), args.steps, args.warmup, hip, evict)
+        configs[c2.name] = summarize(c2, r2)
+        if name == "tiny":
+            # the tiny layer's weights fit in the MALL: its warm number beside the flushed one
+            configs[c2.name]["warm_ms_per_step"] = configs[c2.name]["back_to_back_ms_per_step"]
+        log(f"bench: {c2.name} median {configs[c2.name]['ms_per_step']:.3f} ms, "
+            f"roofline {configs[c2.name]['layer_roofline']['frac']:.3f}")
 
     ep_share = None
     if args.ep_share > 1:
@@ -498,7 +665,7 @@ def main():
     mx = None
     if args.mx:
         log(f"bench: {cfg.name} with block-scaled FP8 expert weights")
-        mx = run_mx(cfg, layer, args.steps, args.warmup)
+        mx = run_mx(cfg, host_layer(cfg), args.steps, args.warmup)
         log(f"bench: {cfg.name} mx {mx['ms']:.3f} ms/step")
 
     lora = None
@@ -509,14 +676,18 @@ def main():
 
     backward = None
     if args.backward != "none":
-        log(f"bench: backward {args.backward}")
-        backward = run_backward(W.CONFIGS[args.backward], max(3, args.steps // 4), 1)
-        log(f"bench: backward {backward['ms']:.3f} ms")
+        cb = W.CONFIGS[args.backward]
+        log(f"bench: backward {cb.name}")
+        backward = run_backward(cb, dev_layer(cb), args.steps, 1, evict)
+        log(f"bench: backward {backward['ms']:.3f} ms, forward + backward {backward['fwd_bwd_ms']:.3f} ms")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        cpu = cpu_baseline(cfg, layer)
+        names = [cfg.name] + extra + ([args.backward] if args.backward != "none" else [])
+        if "moe1k" not in names:
+            names.append("moe1k")
+        cpu = cpu_baseline({n: host_layer(W.CONFIGS[n]) for n in dict.fromkeys(names)})
 
     up_ms = main_s["ffn_up_ms"]
     up_bytes = ffn_up_bytes(cfg, main_r["touched"])
@@ -535,18 +706,21 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights; no checkpoint)",
-        "config": {"workload": f"{cfg.name}: {cfg.tokens} tokens, hidden {cfg.hidden}, {cfg.experts} experts "
-                               f"top-{cfg.top_k}, expert inter {cfg.inter}, shared inter {cfg.shared_inter}",
-                   "tokens": cfg.tokens, "hidden": cfg.hidden, "experts": cfg.experts, "top_k": cfg.top_k,
-                   "inter": cfg.inter, "shared_inter": cfg.shared_inter},
+        "config": {"workload": main_s["workload"], "tokens": cfg.tokens, "hidden": cfg.hidden,
+                   "experts": cfg.experts, "top_k": cfg.top_k, "inter": cfg.inter,
+                   "shared_inter": cfg.shared_inter},
+        "timing": {"protocol": ("median of the timed calls, each bracketed by HIP events on the kernels' "
+                                "stream after a 1 GiB eviction write and a 1 GiB read" if not args.no_evict else
+                                "median of the timed calls, HIP events, no eviction writes"),
+                   "p10_ms": main_s["p10_ms"], "p90_ms": main_s["p90_ms"],
+                   "wall_ms_per_step_incl_eviction": main_s["wall_ms_per_step_incl_eviction"],
+                   "back_to_back_ms_per_step": main_s["back_to_back_ms_per_step"]},
         "roofline": {"kernel": "ffn_up", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes": up_bytes, "avg_ms": up_ms},
         "layer_roofline": main_s["layer_roofline"],
-        "kernel_ms_marked": main_s["kernel_ms"],
-        "ffn_down_gbs": main_s["ffn_down_gbs"],
         "cpu_baseline": cpu,
-        "secondary": secondary,
+        "configs": configs,
         "ep_share": ep_share,
         "mx_weights": mx,
         "lora": lora,
