@@ -331,6 +331,27 @@ int moe_forward_kernel_count(const moe_dims* dims);
  * static string; NULL if the dims are invalid or i is out of range. */
 const char* moe_forward_kernel_name(const moe_dims* dims, int i);
 
+/* Size of the device array that moe_forward_noalloc uses as its workspace
+ * (one array per GPU, held by the library until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward
+ * with its workspace in a library-owned device array of
+ * MOE_NOALLOC_SCRATCH_BYTES instead of a caller buffer; the caller still
+ * passes every input and output.  Same kernels, arguments, results (bit for
+ * bit) and errors as moe_forward, plus MOE_E_WORKSPACE when these dims need
+ * a larger workspace than the array (moe_workspace_bytes(dims,
+ * MOE_OP_FORWARD) > MOE_NOALLOC_SCRATCH_BYTES: at hidden 2048, 512 experts
+ * top-10, intermediate 512, up to about 1550 tokens).  Allocates nothing and
+ * calls no allocating routine; the first call on a device looks the array's
+ * address up once.  All calls on one GPU share its array: calls that overlap
+ * on one GPU (other streams or threads) race.  moe_last_device_error cannot
+ * read this workspace; a bad caller route shows only through the outputs. */
+int moe_forward_noalloc(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                        moe_routes* routes, moe_saved* saved, float* out_f32, uint16_t* out_bf16,
+                        hipStream_t stream);
+
 /* Synchronises `stream`, then returns the device error word of workspace
  * `ws` (MOE_OK or MOE_E_DEVICE) as left by the last moe_permute or
  * moe_forward on that workspace (each such call overwrites it).

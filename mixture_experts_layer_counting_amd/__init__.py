@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 MOE_OK, MOE_E_NULL, MOE_E_SHAPE, MOE_E_UNSUPPORTED, MOE_E_ALIGN = 0, 1, 2, 3, 4
 MOE_E_WORKSPACE, MOE_E_DEVICE, MOE_E_LAUNCH, MOE_E_ALIAS = 5, 6, 7, 8
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_BACKWARD, MOE_OP_FORWARD_LORA = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 ABI_VERSION = 1
 
 
@@ -68,7 +69,7 @@ class MoeGrads(ctypes.Structure):
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
            "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
-           "moe_forward_lora", "moe_grouped_ffn_lora")
+           "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc")
 
 _lib = None
 
@@ -120,6 +121,8 @@ def load_library():
     lib.moe_forward_kernel_name.argtypes = [P(MoeDims), ctypes.c_int]
     lib.moe_last_device_error.restype = ctypes.c_int
     lib.moe_last_device_error.argtypes = [_VP, _VP]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP]
     if lib.moe_abi_version() != ABI_VERSION:
         raise MoEError(f"ABI version mismatch: library {lib.moe_abi_version()}, binding {ABI_VERSION}")
     _lib = lib
@@ -300,6 +303,12 @@ def moe_forward(dims, weights, x, routes, saved, out_f32, out_bf16, ws, stream=N
     return load_library().moe_forward(ctypes.byref(dims.c()), ctypes.byref(weights.c()), _ptr(x),
                                       ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(out_f32),
                                       _ptr(out_bf16), p, n, _stream(stream))
+
+
+def moe_forward_noalloc(dims, weights, x, routes, saved, out_f32, out_bf16, stream=None) -> int:
+    return load_library().moe_forward_noalloc(ctypes.byref(dims.c()), ctypes.byref(weights.c()), _ptr(x),
+                                              ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(out_f32),
+                                              _ptr(out_bf16), _stream(stream))
 
 
 def moe_forward_mx(dims, weights_mx, x, routes, saved, out_f32, out_bf16, ws, stream=None) -> int:
