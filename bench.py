@@ -169,7 +169,7 @@ class Evictor:
         import torch
         self.n += 1
         self.wbuf.fill_(float(self.n & 0xff))
-        torch.sum(self.rbuf, out=self.sink)
+        torch.sum(self.rbuf, dim=0, out=self.sink)
 
 
 def stats(ms):
