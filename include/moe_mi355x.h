@@ -38,7 +38,10 @@
  *    enqueued nothing (fail closed).  Bad data found on the device (a
  *    caller-supplied expert id out of range or repeated within a token) sets
  *    an error word in the workspace, which each moe_permute / moe_forward
- *    overwrites; moe_last_device_error() reads it.
+ *    overwrites; caller-supplied expert_offsets that are not a partition of
+ *    [0, T*K) (moe_grouped_ffn, moe_grouped_ffn_lora, moe_backward) set it
+ *    too and the call then computes nothing; moe_last_device_error() reads
+ *    it.
  *  - Supported sizes: E % 64 == 0 and 64 <= E <= 1024; 1 <= K <= 16 and
  *    K <= E; H % 256 == 0, 256 <= H <= 16384; I % 128 == 0, 128 <= I <= 4096;
  *    Is == 0 or the same rule as I; 0 <= T and T*K < 2^31.  T == 0 returns
@@ -343,7 +346,9 @@ const char* moe_forward_kernel_name(const moe_dims* dims, int i);
  * bit) and errors as moe_forward, plus MOE_E_WORKSPACE when these dims need
  * a larger workspace than the array (moe_workspace_bytes(dims,
  * MOE_OP_FORWARD) > MOE_NOALLOC_SCRATCH_BYTES: at hidden 2048, 512 experts
- * top-10, intermediate 512, up to about 1550 tokens).  Allocates nothing and
+ * top-10, intermediate 512, up to about 1550 tokens); the device's array is
+ * looked up before the other arguments are checked, so without a current
+ * gfx950 device it returns MOE_E_DEVICE first.  Allocates nothing and
  * calls no allocating routine; the first call on a device looks the array's
  * address up once.  All calls on one GPU share its array: calls that overlap
  * on one GPU (other streams or threads) race.  moe_last_device_error cannot

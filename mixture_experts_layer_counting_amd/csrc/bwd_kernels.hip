@@ -203,6 +203,10 @@ __device__ __forceinline__ bool bwd_decode(const BwdArgs& a, int g, BwdTile& w) 
     w.rows = min(kBT, cnt - w.m0);
     return w.rows > 0;
   }
+  // an empty work list means the caller's offsets failed the check of
+  // ffn_tiles_kernel (with T > 0 there is always a routed tile): no group
+  // segment is trusted then
+  if (a.meta[0] == 0) return false;
   const int groups = a.E + (a.Is > 0 ? 1 : 0);
   const int mt = MODE == kDw2 ? a.H / kBT : 2 * Imax / kBT;
   const int nt = MODE == kDw2 ? Imax / kBT : a.H / kBT;
@@ -640,12 +644,15 @@ __global__ __launch_bounds__(256) void bwd_router_w_kernel(const uint16_t* __res
   const int e = blockIdx.x;
   const int c = blockIdx.y * 2048 + threadIdx.x * 8;
   if (c >= H) return;
-  const int p0 = offsets[e], p1 = offsets[e + 1];
+  const int64_t R = T * K;
+  // segment bounds clamped to [0, R] (caller offsets are checked elsewhere;
+  // this only keeps the reads in bounds)
+  const int64_t p0 = min(max(static_cast<int64_t>(offsets[e]), int64_t{0}), R);
+  const int64_t p1 = max(min(static_cast<int64_t>(offsets[e + 1]), R), p0);
   double acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-  const int64_t R = T * K;
-  for (int p = p0; p < p1; ++p) {
+  for (int64_t p = p0; p < p1; ++p) {
     const int64_t r = sorted_route[p];
     if (r < 0 || r >= R) continue;
     const double s = dl[r];

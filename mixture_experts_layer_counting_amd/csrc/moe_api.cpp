@@ -3,6 +3,7 @@
 // layout and the launch sequence of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -309,8 +310,8 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
   const int has_shared = d.shared_inter > 0;
   if (!whole_forward)
     MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles), tiles_up_of(ws, L),
-                                     L.up_rows, at<int32_t>(ws, L.meta), d.experts, d.tokens,
-                                     has_shared, moe::kRowsPerTile, s));
+                                     L.up_rows, at<int32_t>(ws, L.meta), at<int>(ws, L.err), d.experts,
+                                     d.tokens, d.top_k, has_shared, moe::kRowsPerTile, s));
   if (has_shared && !whole_forward)
     MOE_LAUNCH(moe::launch_shared_gate(x, w->w_sgate, sv->shared_gate, d.tokens, d.hidden, s));
   const bool own_up = tiles_up_of(ws, L) != nullptr;
@@ -432,7 +433,7 @@ int moe_route(const moe_dims* dims, const uint16_t* x, const moe_weights* w, moe
   a.in(x, bytes_x(d));
   add_weights(a, d, w, true, false);
   add_routes_out(a, d, routes);
-  a.in(ws, moe_workspace_bytes(dims, MOE_OP_ROUTE), false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_ROUTE)), false);
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_ROUTE));
   MOE_TRY(check_device());
@@ -448,7 +449,7 @@ int moe_permute(const moe_dims* dims, moe_routes* routes, void* ws, size_t ws_by
   Args a;
   a.in(routes->topk_idx, static_cast<size_t>(d.tokens) * d.top_k * 4);
   add_perm_out(a, d, routes);
-  a.in(ws, moe_workspace_bytes(dims, MOE_OP_PERMUTE), false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_PERMUTE)), false);
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_PERMUTE));
   MOE_TRY(check_device());
@@ -469,7 +470,7 @@ int moe_grouped_ffn(const moe_dims* dims, const uint16_t* x, const moe_weights* 
   a.in(routes->expert_offsets, (E + 1) * 4);
   a.in(routes->sorted_route, T * K * 4);
   add_saved(a, d, saved, true);
-  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FFN), false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_FFN)), false);
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FFN));
   MOE_TRY(check_device());
@@ -496,7 +497,7 @@ int moe_grouped_ffn_lora(const moe_dims* dims, const uint16_t* x, const moe_weig
   a.in(routes->expert_offsets, (E + 1) * 4);
   a.in(routes->sorted_route, T * K * 4);
   add_saved(a, d, saved, true);
-  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA), false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA)), false);
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD_LORA));
   MOE_TRY(check_device());
@@ -542,7 +543,7 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, m
   add_saved(a, d, saved, true);
   a.out(out_f32, T * H * 4, false);
   a.out(out_bf16, T * H * 2, false);
-  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FORWARD), false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_FORWARD)), false);
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD));
   MOE_TRY(check_device());
@@ -577,7 +578,7 @@ int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora*
   add_saved(a, d, saved, true);
   a.out(out_f32, T * H * 4, false);
   a.out(out_bf16, T * H * 2, false);
-  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA), false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA)), false);
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD_LORA));
   MOE_TRY(check_device());
@@ -618,7 +619,7 @@ int moe_forward_mx(const moe_dims* dims, const moe_weights_mx* w, const uint16_t
   add_saved(a, d, saved, true);
   a.out(out_f32, T * H * 4, false);
   a.out(out_bf16, T * H * 2, false);
-  a.in(ws, moe_workspace_bytes(dims, MOE_OP_FORWARD), false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_FORWARD)), false);
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD));
   MOE_TRY(check_device());
@@ -708,7 +709,7 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
     a.out(grads->d_ws2, H * Is * 4);
     a.out(grads->d_w_sgate, H * 4);
   }
-  a.in(ws, moe_workspace_bytes(dims, MOE_OP_BACKWARD), false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_BACKWARD)), false);
   MOE_TRY(a.status());
   MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_BACKWARD));
   MOE_TRY(check_device());
@@ -716,8 +717,8 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
   const bool sh = Is > 0;
   hipStream_t s = stream;
   MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles_bwd), nullptr, 0,
-                                   at<int32_t>(ws, L.meta_bwd), d.experts, d.tokens, sh,
-                                   moe::kBwdRowsPerTile, s));
+                                   at<int32_t>(ws, L.meta_bwd), at<int>(ws, L.err), d.experts, d.tokens,
+                                   d.top_k, sh, moe::kBwdRowsPerTile, s));
   moe::BwdLaunch b;
   b.T = d.tokens;
   b.H = d.hidden;

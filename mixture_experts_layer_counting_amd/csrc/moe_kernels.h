@@ -40,9 +40,11 @@ hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* 
                              int32_t* tiles, int32_t* tiles_up, int up_rows, int32_t* meta,
                              int nblocks, int E, int64_t T, int has_shared, int* err_word,
                              hipStream_t stream);
+// Work list from caller-supplied offsets; offsets that are not a partition
+// of [0, T*K) set *err_word and give an empty list.
 hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* tiles_up, int up_rows,
-                            int32_t* meta, int E, int64_t T, int has_shared, int rows_per_tile,
-                            hipStream_t stream);
+                            int32_t* meta, int* err_word, int E, int64_t T, int K, int has_shared,
+                            int rows_per_tile, hipStream_t stream);
 hipError_t launch_route_scatter(const int32_t* topk_idx, const int32_t* block_base,
                                 const int32_t* offsets, int32_t* route_pos, int32_t* sorted_route,
                                 int64_t T, int E, int K, hipStream_t stream);

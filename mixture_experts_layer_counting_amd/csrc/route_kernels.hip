@@ -629,19 +629,34 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 
 // Work list alone, from caller-supplied expert offsets (grouped FFN run on
 // its own, with the up projection's list when tiles_up is given, or the
-// backward's list).
+// backward's list).  The offsets are checked first: offsets[0] == 0, never
+// decreasing, offsets[E] == T*K.  Offsets that fail set the device-error
+// word (it is never cleared here, so a permutation's error survives) and
+// give an empty work list, so no kernel reads past the route arrays.
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ tiles_up, int up_rows,
-                                                         int32_t* __restrict__ meta, int E,
-                                                         int64_t T, int has_shared,
+                                                         int32_t* __restrict__ meta, int* __restrict__ err_word,
+                                                         int E, int64_t T, int K, int has_shared,
                                                          int rows_per_tile) {
   __shared__ int buf[1024];
+  __shared__ int bad;
   const int e = threadIdx.x;
+  if (e == 0) bad = 0;
+  __syncthreads();
   int count = 0;
   if (e < E) {
     count = offsets[e + 1] - offsets[e];
-    if (count < 0) count = 0;
+    if (count < 0 || (e == 0 && offsets[0] != 0) || (e == E - 1 && offsets[E] != T * K)) bad = 1;
+  }
+  __syncthreads();
+  if (bad) {
+    if (e == 0) {
+      meta[0] = 0;
+      if (tiles_up) meta[2] = 0;
+      *err_word = 1;
+    }
+    return;
   }
   emit_tiles(count, E, T, has_shared, tiles, &meta[0], buf, rows_per_tile);
   if (tiles_up) emit_tiles(count, E, T, has_shared, tiles_up, &meta[2], buf, up_rows);
@@ -910,10 +925,10 @@ hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* 
 }
 
 hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* tiles_up, int up_rows,
-                            int32_t* meta, int E, int64_t T, int has_shared, int rows_per_tile,
-                            hipStream_t stream) {
-  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, tiles_up, up_rows, meta, E, T, has_shared,
-                                           rows_per_tile);
+                            int32_t* meta, int* err_word, int E, int64_t T, int K, int has_shared,
+                            int rows_per_tile, hipStream_t stream) {
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, tiles_up, up_rows, meta, err_word, E, T, K,
+                                           has_shared, rows_per_tile);
   return hipGetLastError();
 }
 

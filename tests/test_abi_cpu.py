@@ -194,3 +194,66 @@ def test_lora_forward_validation_fails_closed(lib):
     import torch
     if not torch.cuda.is_available():
         assert call(lo) == m.MOE_E_DEVICE
+
+
+def backward_args(d: m.Dims):
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    T, H, E, K, I, Is = d.tokens, d.hidden, d.experts, d.top_k, d.inter, d.shared_inter
+    s.gu = f(T * K * 2 * I * 4)
+    s.shared_gu = f(T * 2 * Is * 4)
+    g = m.Grads(d_w_router=f(E * H * 4), d_w13=f(E * 2 * I * H * 4), d_w2=f(E * H * I * 4),
+                d_ws13=f(2 * Is * H * 4), d_ws2=f(H * Is * 4), d_w_sgate=f(H * 4))
+    dout, dx32, dx16 = f(T * H * 2), f(T * H * 4), f(T * H * 2)
+    nws = m.moe_workspace_bytes(d, m.MOE_OP_BACKWARD)
+    return w, r, s, x, g, dout, dx32, dx16, (f(nws), nws), ws
+
+
+def test_backward_validation_fails_closed(lib):
+    """moe_backward checks dims, the saved forward tensors it needs (gate/up
+    values, the shared gate), every gradient buffer (presence, alignment,
+    overlap) and its own larger workspace on the host before anything is
+    launched; the saved route rows are not read and may be NULL."""
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, g, dout, dx32, dx16, wsb, wsf = backward_args(d)
+    bwd = lambda dd=d, ss=s, gg=g, dd32=dx32, ww=wsb, do=dout: m.moe_backward(dd, w, x, r, ss, do, dd32, dx16, gg,
+                                                                            ww, stream=0)
+    assert bwd(dd=m.Dims(64, 500, 512, 10, 128, 128)) == m.MOE_E_SHAPE
+    assert bwd(dd=m.Dims(64, 512, 512, 10, 100, 128)) == m.MOE_E_SHAPE
+    assert bwd(do=None) == m.MOE_E_NULL
+    assert bwd(dd32=None) == m.MOE_E_NULL
+    assert bwd(ss=m.Saved(**{**s.__dict__, "gu": None})) == m.MOE_E_NULL
+    assert bwd(ss=m.Saved(**{**s.__dict__, "shared_gu": None})) == m.MOE_E_NULL
+    assert bwd(ss=m.Saved(**{**s.__dict__, "shared_gate": None})) == m.MOE_E_NULL
+    assert bwd(gg=m.Grads(**{**g.__dict__, "d_w13": None})) == m.MOE_E_NULL
+    assert bwd(gg=m.Grads(**{**g.__dict__, "d_w_sgate": None})) == m.MOE_E_NULL
+    assert bwd(gg=m.Grads(**{**g.__dict__, "d_w2": g.d_w2 + 8})) == m.MOE_E_ALIGN
+    # a gradient aliasing an input, or another gradient
+    assert bwd(gg=m.Grads(**{**g.__dict__, "d_w_router": x})) == m.MOE_E_ALIAS
+    assert bwd(gg=m.Grads(**{**g.__dict__, "d_ws2": g.d_ws13})) == m.MOE_E_ALIAS
+    assert bwd(dd32=s.gu) == m.MOE_E_ALIAS
+    # the forward's workspace is too small for the backward
+    assert bwd(ww=wsf) == m.MOE_E_WORKSPACE
+    assert bwd(ww=None) == m.MOE_E_WORKSPACE
+    # T == 0 is a no-op
+    assert bwd(dd=m.Dims(0, 512, 512, 10, 128, 128)) == m.MOE_OK
+    import torch
+    if not torch.cuda.is_available():
+        # the route rows are not needed: valid otherwise, it stops at the device check
+        assert bwd(ss=m.Saved(**{**s.__dict__, "y": None, "shared_y": None})) == m.MOE_E_DEVICE
+        assert bwd() == m.MOE_E_DEVICE
+
+
+def test_noalloc_forward_refuses_what_its_array_cannot_hold(lib):
+    """moe_forward_noalloc needs no workspace argument; dims whose forward
+    workspace exceeds its array are refused on the host, invalid dims too."""
+    big = m.Dims(4096, 2048, 512, 10, 512, 512)
+    assert m.moe_workspace_bytes(big, m.MOE_OP_FORWARD) > m.NOALLOC_SCRATCH_BYTES
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    assert m.moe_forward_noalloc(big, w, x, r, s, o32, o16, stream=0) == m.MOE_E_WORKSPACE
+    assert m.moe_forward_noalloc(m.Dims(64, 500, 512, 10, 128, 128), w, x, r, s, o32, o16, stream=0) == m.MOE_E_SHAPE
+    assert m.moe_forward_noalloc(m.Dims(0, 512, 512, 10, 128, 128), w, None, r, s, None, None, stream=0) == m.MOE_OK
+    import torch
+    if not torch.cuda.is_available():
+        # dims it can hold: the device's array is looked up first, so without a GPU it stops there
+        assert m.moe_forward_noalloc(d, w, None, r, s, o32, o16, stream=0) == m.MOE_E_DEVICE

@@ -228,3 +228,35 @@ def test_shape_edge_cases(shape):
     say(f"case: edge shape {shape}")
     g = gpu_forward(cfg, dev_weights(layer), dev_bits(x)).host()
     check_forward(cfg, layer, x, g)
+
+
+def test_bad_offsets_set_device_error(tiny):
+    """Caller-supplied expert offsets that are not a partition of [0, T*K)
+    (not starting at 0, decreasing, not ending at T*K) set the device error
+    word in the grouped FFN and the backward and run no GEMM work; nothing
+    reads past the route arrays."""
+    cfg, layer, x, w = tiny
+    say("case: tiny, invalid caller offsets -> device error")
+    T = 64
+    d = dims_of(cfg, T)
+    xd = dev_bits(x[:T])
+    g = gpu_forward(cfg, w, xd, training=True)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD, DEV)
+    good = g.routes.expert_offsets.clone()
+    bads = []
+    b = good.clone(); b[0] = 3; bads.append(("first", b))
+    b = good.clone(); b[7] = b[8] + 5; bads.append(("decreasing", b))
+    b = good.clone(); b[-1] = T * cfg.top_k + 40; bads.append(("total", b))
+    dout = dev_bits(W.grad_out(cfg, T))
+    for what, off in bads:
+        r = m.Routes(**{**g.routes.__dict__, "expert_offsets": off})
+        m.check(m.moe_permute(d, g.routes, ws), "moe_permute")  # clears the word
+        assert m.moe_last_device_error(ws) == m.MOE_OK
+        saved = m.alloc_saved(d, DEV)
+        m.check(m.moe_grouped_ffn(d, xd, w, r, saved, ws), "moe_grouped_ffn")
+        assert m.moe_last_device_error(ws) == m.MOE_E_DEVICE, what
+        m.check(m.moe_permute(d, g.routes, ws), "moe_permute")
+        grads = m.alloc_grads(d, DEV)
+        dx = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+        m.check(m.moe_backward(d, w, xd, r, g.saved, dout, dx, None, grads, ws), "moe_backward")
+        assert m.moe_last_device_error(ws) == m.MOE_E_DEVICE, what
