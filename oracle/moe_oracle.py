@@ -307,7 +307,44 @@ def _swiglu_backward(dy, gu, x_rows, w13_bits, w2_bits):
     return dgu @ w13, dy.T @ act, dgu.T @ x_rows, dgu
 
 
-def backward(layer: dict, x_bits, fwd: dict, d_out_bits) -> dict:
+def _swiglu_backward_lora(dy, gu, x_rows, w13_bits, w2_bits, ad):
+    """Backward of one SwiGLU expert whose projections carry the LoRA
+    update of swiglu_expert (ad = (a13, b13, a2, b2, scale)).
+
+    With z13 = x A13^T and z2 = act A2^T the forward is gu = x W13^T + s
+    z13 B13^T and y = act W2^T + s z2 B2^T, so by the chain rule (every
+    product a plain matrix product):
+      v    = dy B2                      (route x rank)
+      dact = dy W2 + s v A2
+      dgu  = SwiGLU backward of dact, as in _swiglu_backward
+      u    = dgu B13                    (route x rank)
+      dx   = dgu W13 + s u A13
+      dW2  = dy^T act,  dW13 = dgu^T x
+      dA13 = s u^T x,   dB13 = s dgu^T z13
+      dA2  = s v^T act, dB2  = s dy^T z2.
+    Returns (dx, dW2, dW13, dA13, dB13, dA2, dB2)."""
+    w13 = bf16_to_f64(w13_bits)
+    w2 = bf16_to_f64(w2_bits)
+    a13, b13, a2, b2 = (bf16_to_f64(m) for m in ad[:4])
+    scale = float(ad[4])
+    inter = w13.shape[0] // 2
+    gate, up = gu[:, :inter], gu[:, inter:]
+    s = sigmoid(gate)
+    act = gate * s * up
+    z13 = x_rows @ a13.T
+    z2 = act @ a2.T
+    v = dy @ b2
+    dact = dy @ w2 + scale * (v @ a2)
+    dgate = dact * up * s * (1.0 + gate * (1.0 - s))
+    dup = dact * gate * s
+    dgu = np.concatenate([dgate, dup], axis=1)
+    u = dgu @ b13
+    dx = dgu @ w13 + scale * (u @ a13)
+    return (dx, dy.T @ act, dgu.T @ x_rows, scale * (u.T @ x_rows), scale * (dgu.T @ z13),
+            scale * (v.T @ act), scale * (dy.T @ z2))
+
+
+def backward(layer: dict, x_bits, fwd: dict, d_out_bits, lora=None) -> dict:
     """Gradients of every input of the layer for upstream gradient dOut.
 
     Contract "Backward" bullet: per-expert weight gradients into one dense
@@ -315,7 +352,10 @@ def backward(layer: dict, x_bits, fwd: dict, d_out_bits) -> dict:
     immaterial in exact arithmetic; the GPU's order is its own contract).
     The route-weight gradient dg = <dOut, Y> and its softmax backward
     through the renormalised gates follow from the combine definition.
-    Needs the full batch (fwd from forward(..., tokens=None))."""
+    Needs the full batch (fwd from forward(..., tokens=None)).  `lora`
+    (the dict of forward(); fwd must come from the same adapters) adds the
+    routed experts' adapter terms and returns their gradients d_a13, d_b13,
+    d_a2, d_b2 too."""
     x64 = bf16_to_f64(x_bits)
     dO = bf16_to_f64(d_out_bits)
     idx, g = fwd["idx"], fwd["gates"]
@@ -333,17 +373,28 @@ def backward(layer: dict, x_bits, fwd: dict, d_out_bits) -> dict:
     # routed experts
     d_w13 = np.zeros(layer["w13"].shape, F64)
     d_w2 = np.zeros(layer["w2"].shape, F64)
+    if lora is not None:
+        lg = {k: np.zeros(np.shape(lora[k[2:]]), F64) for k in ("d_a13", "d_b13", "d_a2", "d_b2")}
     flat = idx.reshape(-1)
     gflat = g.reshape(-1)
     for e in np.unique(flat):
         rows = np.nonzero(flat == e)[0]
         t = rows // K
         dy = gflat[rows, None] * dO[t]
-        dxr, dw2, dw13, _ = _swiglu_backward(dy, fwd["gu"][rows], x64[t], layer["w13"][e], layer["w2"][e])
+        if lora is None:
+            dxr, dw2, dw13, _ = _swiglu_backward(dy, fwd["gu"][rows], x64[t], layer["w13"][e], layer["w2"][e])
+        else:
+            ad = (lora["a13"][e], lora["b13"][e], lora["a2"][e], lora["b2"][e], float(lora["scale"]))
+            dxr, dw2, dw13, *dad = _swiglu_backward_lora(dy, fwd["gu"][rows], x64[t], layer["w13"][e],
+                                                          layer["w2"][e], ad)
+            for key, val in zip(("d_a13", "d_b13", "d_a2", "d_b2"), dad):
+                lg[key][e] = val
         np.add.at(dx, t, dxr)
         d_w2[e] = dw2
         d_w13[e] = dw13
     res = {"dg": dg, "dl": dl_sel, "d_w_router": d_w_router, "d_w13": d_w13, "d_w2": d_w2}
+    if lora is not None:
+        res.update(lg)
     if layer.get("ws13") is not None:
         s, sg = fwd["s"], fwd["sg"]
         dz = (dO * s).sum(axis=1) * sg * (1.0 - sg)

@@ -553,3 +553,124 @@ def test_selection_boundary_spacing_matches_the_closed_form(name, gaps):
         observed = int((gap < d).sum())
         assert abs(observed - expected) <= 5.0 * np.sqrt(expected) + 0.15 * expected, (d, observed, expected)
     assert {"tiny": 0.014, "moe8k": 0.23}[name] == pytest.approx(cfg.tokens * rho * 1e-6, rel=0.03)
+
+
+# ---------------------------------------------------------------- LoRA backward
+def _tiny_lora_float(cfg, rank=3, scale=0.75):
+    rng = np.random.default_rng(5)
+    E, H, I = cfg.experts, cfg.hidden, cfg.inter
+    return {"a13": rng.normal(0, 0.3, (E, rank, H)), "b13": rng.normal(0, 0.3, (E, 2 * I, rank)),
+            "a2": rng.normal(0, 0.3, (E, rank, I)), "b2": rng.normal(0, 0.3, (E, H, rank)), "rank": rank,
+            "scale": scale}
+
+
+def _lora_loss(layer, x, d_out, idx, top_k, lora):
+    fwd = O.forward(layer, x, top_k, forced_idx=idx, lora=lora)
+    return float(np.sum(O.bf16_to_f64(d_out) * fwd["out"]))
+
+
+@pytest.mark.parametrize("name", ["a13", "b13", "a2", "b2", "w13", "w2", "w_router", "x"])
+def test_lora_backward_matches_central_differences(name):
+    """Every adapter matrix, the base expert weights, the router and the
+    input: the oracle's LoRA backward against central differences of the
+    LoRA forward (routing frozen)."""
+    cfg, layer, x, d_out = _tiny_float_layer()
+    ad = _tiny_lora_float(cfg)
+    fwd = O.forward(layer, x, cfg.top_k, lora=ad)
+    idx = fwd["idx"]
+    grads = O.backward(layer, x, fwd, d_out, lora=ad)
+    key = {"x": "dx", "w_router": "d_w_router"}.get(name, "d_" + name)
+    g = grads[key]
+    if name in ("a13", "b13", "a2", "b2"):
+        base = ad[name]
+    else:
+        base = x if name == "x" else layer[name]
+    rng = np.random.default_rng(2)
+    h = 1e-6
+    for fi in rng.choice(base.size, size=min(24, base.size), replace=False):
+        pert = base.copy().reshape(-1)
+        orig = pert[fi]
+        vals = []
+        for s in (+1, -1):
+            pert[fi] = orig + s * h
+            arr = pert.reshape(base.shape)
+            lay, xx, aa = layer, x, ad
+            if name in ("a13", "b13", "a2", "b2"):
+                aa = dict(ad)
+                aa[name] = arr
+            elif name == "x":
+                xx = arr
+            else:
+                lay = dict(layer)
+                lay[name] = arr
+            vals.append(_lora_loss(lay, xx, d_out, idx, cfg.top_k, aa))
+        fd = (vals[0] - vals[1]) / (2 * h)
+        an = g.reshape(-1)[fi]
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fi, fd, an)
+
+
+def test_lora_backward_matches_torch_float64_autograd():
+    """An independently written LoRA forward in torch float64 (per token,
+    per route, the update scale * B (A v) on both projections), its autograd
+    gradients against the oracle's."""
+    torch = pytest.importorskip("torch")
+    cfg, layer, x, d_out = _tiny_float_layer()
+    ad = _tiny_lora_float(cfg)
+    fwd = O.forward(layer, x, cfg.top_k, lora=ad)
+    idx = fwd["idx"]
+    grads = O.backward(layer, x, fwd, d_out, lora=ad)
+    T = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    tx, twr, tw13, tw2 = T(x), T(layer["w_router"]), T(layer["w13"]), T(layer["w2"])
+    tws13, tws2, twsg = T(layer["ws13"]), T(layer["ws2"]), T(layer["w_sgate"])
+    ta13, tb13, ta2, tb2 = T(ad["a13"]), T(ad["b13"]), T(ad["a2"]), T(ad["b2"])
+    sc = ad["scale"]
+    I = cfg.inter
+    logits = tx @ twr.T
+    gates = torch.softmax(torch.gather(logits, 1, torch.tensor(idx, dtype=torch.int64)), dim=1)
+    out = torch.zeros(cfg.tokens, cfg.hidden, dtype=torch.float64)
+    for t in range(cfg.tokens):
+        for k in range(cfg.top_k):
+            e = int(idx[t, k])
+            h = tw13[e] @ tx[t] + sc * (tb13[e] @ (ta13[e] @ tx[t]))
+            act = torch.nn.functional.silu(h[:I]) * h[I:]
+            y = tw2[e] @ act + sc * (tb2[e] @ (ta2[e] @ act))
+            out[t] = out[t] + gates[t, k] * y
+    hs = tx @ tws13.T
+    s = (torch.nn.functional.silu(hs[:, :I]) * hs[:, I:]) @ tws2.T
+    out = out + torch.sigmoid(tx @ twsg)[:, None] * s
+    (out * torch.tensor(O.bf16_to_f64(d_out))).sum().backward()
+    assert np.max(np.abs(fwd["out"] - out.detach().numpy())) <= 1e-12
+    pairs = [("dx", tx), ("d_w_router", twr), ("d_w13", tw13), ("d_w2", tw2), ("d_ws13", tws13),
+             ("d_ws2", tws2), ("d_w_sgate", twsg), ("d_a13", ta13), ("d_b13", tb13), ("d_a2", ta2),
+             ("d_b2", tb2)]
+    for key, tt in pairs:
+        assert np.max(np.abs(grads[key] - tt.grad.numpy())) <= 1e-12, key
+
+
+def test_lora_backward_with_zero_expand():
+    """B13 = B2 = 0: the adapters change nothing, so every base gradient is
+    the plain backward's, the shrink matrices get no gradient, and the
+    expand matrices' gradients are s * dgu^T (x A13^T) and s * dy^T (act
+    A2^T) route by route."""
+    cfg, layer, x, d_out = _tiny_float_layer()
+    ad = _tiny_lora_float(cfg)
+    ad["b13"][:] = 0.0
+    ad["b2"][:] = 0.0
+    fwd = O.forward(layer, x, cfg.top_k, lora=ad)
+    plain = O.backward(layer, x, O.forward(layer, x, cfg.top_k), d_out)
+    lo = O.backward(layer, x, fwd, d_out, lora=ad)
+    for key in ("dx", "d_w_router", "d_w13", "d_w2", "d_ws13", "d_ws2", "d_w_sgate"):
+        assert np.max(np.abs(lo[key] - plain[key])) <= 1e-13, key
+    assert not lo["d_a13"].any() and not lo["d_a2"].any()
+    K, I = cfg.top_k, cfg.inter
+    dO = O.bf16_to_f64(d_out)
+    flat = fwd["idx"].reshape(-1)
+    for e in np.unique(flat):
+        rows = np.nonzero(flat == e)[0]
+        t = rows // K
+        dy = fwd["gates"].reshape(-1)[rows, None] * dO[t]
+        gu = fwd["gu"][rows]
+        act = O.silu(gu[:, :I]) * gu[:, I:]
+        dgu = O.swiglu_backward(dy, gu, x[t], layer["w13"][e], layer["w2"][e])[3]
+        assert np.max(np.abs(lo["d_b13"][e] - ad["scale"] * dgu.T @ (x[t] @ ad["a13"][e].T))) <= 1e-13
+        assert np.max(np.abs(lo["d_b2"][e] - ad["scale"] * dy.T @ (act @ ad["a2"][e].T))) <= 1e-13
