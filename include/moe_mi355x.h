@@ -37,11 +37,11 @@
  *    enqueues anything; on failure it returns a non-zero status and has
  *    enqueued nothing (fail closed).  Bad data found on the device (a
  *    caller-supplied expert id out of range or repeated within a token) sets
- *    an error word in the workspace, which each moe_permute / moe_forward
- *    overwrites; caller-supplied expert_offsets that are not a partition of
- *    [0, T*K) (moe_grouped_ffn, moe_grouped_ffn_lora, moe_backward) set it
- *    too and the call then computes nothing; moe_last_device_error() reads
- *    it.
+ *    an error word in the workspace, which each moe_permute, moe_forward,
+ *    moe_backward and moe_backward_lora overwrites; caller-supplied
+ *    expert_offsets that are not a partition of [0, T*K) (moe_grouped_ffn,
+ *    moe_grouped_ffn_lora, moe_backward, moe_backward_lora) set it too and
+ *    the call then computes nothing; moe_last_device_error() reads it.
  *  - Supported sizes: E % 64 == 0 and 64 <= E <= 1024; 1 <= K <= 16 and
  *    K <= E; H % 256 == 0, 256 <= H <= 16384; I % 128 == 0, 128 <= I <= 4096;
  *    Is == 0 or the same rule as I; 0 <= T and T*K < 2^31.  T == 0 returns
@@ -84,7 +84,8 @@ enum moe_op {
   MOE_OP_FFN = 2,
   MOE_OP_FORWARD = 3,
   MOE_OP_BACKWARD = 4,
-  MOE_OP_FORWARD_LORA = 5
+  MOE_OP_FORWARD_LORA = 5,
+  MOE_OP_BACKWARD_LORA = 6
 };
 
 typedef struct moe_dims {
@@ -294,7 +295,7 @@ typedef struct {
  *            GEMM accumulator), before the SwiGLU (and before y is stored).
  * So every route row is a function of its own data only (batch invariant,
  * deterministic, no atomics).  saved->gu, if given, receives the gate/up
- * values with the update; moe_backward does not take adapters.  Workspace:
+ * values with the update (moe_backward_lora needs them).  Workspace:
  * moe_workspace_bytes(dims, MOE_OP_FORWARD_LORA).  Errors as moe_forward,
  * plus MOE_E_NULL for a missing adapter matrix and MOE_E_SHAPE for a rank
  * outside 1..16. */
@@ -310,6 +311,47 @@ int moe_forward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora*
 int moe_grouped_ffn_lora(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
                          const moe_lora* lora, const moe_routes* routes, moe_saved* saved, void* ws,
                          size_t ws_bytes, hipStream_t stream);
+
+/* Gradients of the routed experts' adapters, fp32, caller-owned, 16-byte
+ * aligned, overwritten, in the adapters' layouts:
+ *   d_a13 [E][rank][H], d_b13 [E][2I][rank], d_a2 [E][rank][I], d_b2 [E][H][rank].
+ * An expert with no routes gets zeros. */
+typedef struct {
+  float* d_a13;
+  float* d_b13;
+  float* d_a2;
+  float* d_b2;
+} moe_lora_grads;
+
+/* Backward of moe_forward_lora: the adapters are trained (ROLL pull request
+ * 502 page, opening summary: LoRA SFT, RL and OPD over the grouped expert
+ * adapters of the "What this changes" rank bullet).  Inputs and outputs of
+ * moe_backward, with saved->gu from moe_forward_lora (gate/up values with
+ * the update), plus the adapters and their gradients.  With s = scale and
+ * route r of expert e (token t, gate g, dy = g d_out[t]), by the chain rule
+ * through gu += s B13 (A13 x) and y += s B2 (A2 act):
+ *   v2   = B2^T dy / g = B2^T d_out[t]      (shrink, before the dact GEMM)
+ *   dact = dy W2_e + s g A2^T v2            (LoRA term added to the GEMM
+ *          product before the SwiGLU backward; dg[t][k] likewise uses
+ *          <W2_e^T d_out[t] + s A2^T v2, act>, the route's y with the update)
+ *   u13  = B13^T dgu;   dx_r = dgu W13_e + s A13^T u13
+ *   dA13_e = s sum_r u13 x^T      dB13_e = s sum_r dgu (A13 x)^T
+ *   dA2_e  = s sum_r g v2 act^T   dB2_e  = s sum_r d_out[t] (A2 g act)^T
+ * the base weight gradients and everything else as in moe_backward.  The
+ * shrinks (v2, u13, A13 x, A2 (g act)) are those of moe_forward_lora's
+ * shrink kernel (fp32 on the matrix cores, kept as bf16 hi + lo pairs; dgu
+ * and g act enter them as their first two bf16 planes, 16 significant
+ * bits); the expand terms run on the matrix cores in the grouped GEMMs'
+ * epilogues as in the forward; the adapter-gradient sums run over each
+ * expert's routes in ascending sorted position in fp64, with dgu and g act
+ * exact (three planes).  No atomics; results are deterministic.  Workspace:
+ * moe_workspace_bytes(dims, MOE_OP_BACKWARD_LORA).  Errors as moe_backward,
+ * plus MOE_E_NULL for a missing adapter, gradient struct or adapter
+ * gradient and MOE_E_SHAPE for a rank outside 1..16. */
+int moe_backward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,
+                      const uint16_t* x, const moe_routes* routes, const moe_saved* saved,
+                      const uint16_t* d_out, float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads,
+                      moe_lora_grads* lora_grads, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Profiling variant of moe_forward: the same kernels in the same order on
  * `stream`, with events[i] recorded just before kernel i and events[n] after
@@ -358,8 +400,9 @@ int moe_forward_noalloc(const moe_dims* dims, const moe_weights* w, const uint16
                         hipStream_t stream);
 
 /* Synchronises `stream`, then returns the device error word of workspace
- * `ws` (MOE_OK or MOE_E_DEVICE) as left by the last moe_permute or
- * moe_forward on that workspace (each such call overwrites it).
+ * `ws` (MOE_OK or MOE_E_DEVICE) as left by the calls on that workspace
+ * since the last one that overwrites it (moe_permute, moe_forward,
+ * moe_backward, moe_backward_lora).
  * Debug/validation use. */
 int moe_last_device_error(void* ws, hipStream_t stream);
 

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 
 MOE_OK, MOE_E_NULL, MOE_E_SHAPE, MOE_E_UNSUPPORTED, MOE_E_ALIGN = 0, 1, 2, 3, 4
 MOE_E_WORKSPACE, MOE_E_DEVICE, MOE_E_LAUNCH, MOE_E_ALIAS = 5, 6, 7, 8
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_BACKWARD, MOE_OP_FORWARD_LORA = range(6)
+(MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_BACKWARD, MOE_OP_FORWARD_LORA,
+ MOE_OP_BACKWARD_LORA) = range(7)
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 ABI_VERSION = 1
 
@@ -66,10 +67,14 @@ class MoeGrads(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("d_w_router", "d_w13", "d_w2", "d_ws13", "d_ws2", "d_w_sgate")]
 
 
+class MoeLoraGrads(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in ("d_a13", "d_b13", "d_a2", "d_b2")]
+
+
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
            "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
-           "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc")
+           "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc", "moe_backward_lora")
 
 _lib = None
 
@@ -112,6 +117,9 @@ def load_library():
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                  P(MoeGrads), *ws]
+    lib.moe_backward_lora.restype = ctypes.c_int
+    lib.moe_backward_lora.argtypes = [P(MoeDims), P(MoeWeights), P(MoeLora), _VP, P(MoeRoutes), P(MoeSaved),
+                                      _VP, _VP, _VP, P(MoeGrads), P(MoeLoraGrads), *ws]
     lib.moe_forward_profiled.restype = ctypes.c_int
     lib.moe_forward_profiled.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP,
                                          _VP, ctypes.c_size_t, _VP, ctypes.c_int, _VP]
@@ -252,6 +260,19 @@ class Grads:
         return MoeGrads(*(_ptr(getattr(self, n)) for n, _ in MoeGrads._fields_))
 
 
+@dataclasses.dataclass
+class LoraGrads:
+    """Adapter gradients (fp32): d_a13 [E,rank,H], d_b13 [E,2I,rank],
+    d_a2 [E,rank,I], d_b2 [E,H,rank]."""
+    d_a13: object = None
+    d_b13: object = None
+    d_a2: object = None
+    d_b2: object = None
+
+    def c(self) -> MoeLoraGrads:
+        return MoeLoraGrads(*(_ptr(getattr(self, n)) for n, _ in MoeLoraGrads._fields_))
+
+
 def _ws(ws):
     if ws is None:
         return None, 0
@@ -341,6 +362,17 @@ def moe_backward(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grad
                                        _stream(stream))
 
 
+def moe_backward_lora(dims, weights, lora, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, lora_grads, ws,
+                      stream=None) -> int:
+    p, n = _ws(ws)
+    lg = ctypes.byref(lora_grads.c()) if lora_grads is not None else None
+    lc = ctypes.byref(lora.c()) if lora is not None else None
+    return load_library().moe_backward_lora(ctypes.byref(dims.c()), ctypes.byref(weights.c()), lc, _ptr(x),
+                                            ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(d_out),
+                                            _ptr(d_x_f32), _ptr(d_x_bf16), ctypes.byref(grads.c()), lg, p, n,
+                                            _stream(stream))
+
+
 def moe_forward_profiled(dims, weights, x, routes, saved, out_f32, out_bf16, ws, events, stream=None) -> int:
     """events: a ctypes array of hipEvent_t handles (see forward_kernel_names)."""
     p, n = _ws(ws)
@@ -398,6 +430,13 @@ def alloc_grads(dims: Dims, device) -> Grads:
     return Grads(d_w_router=f(E, H), d_w13=f(E, 2 * I, H), d_w2=f(E, H, I),
                  d_ws13=f(2 * Is, H) if Is else None, d_ws2=f(H, Is) if Is else None,
                  d_w_sgate=f(H) if Is else None)
+
+
+def alloc_lora_grads(dims: Dims, rank: int, device) -> LoraGrads:
+    import torch
+    E, H, I = dims.experts, dims.hidden, dims.inter
+    f = lambda *s: torch.empty(*s, dtype=torch.float32, device=device)
+    return LoraGrads(d_a13=f(E, rank, H), d_b13=f(E, 2 * I, rank), d_a2=f(E, rank, I), d_b2=f(E, H, rank))
 
 
 def alloc_workspace(dims: Dims, op: int, device):

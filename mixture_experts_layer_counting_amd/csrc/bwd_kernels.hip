@@ -172,6 +172,14 @@ struct BwdArgs {
   float* dw2;
   float* dws13;
   float* dws2;
+  // LoRA term of the dgrad epilogues (LORA instantiations): the rows' shrink
+  // results as bf16 pairs lzq [p][hi, lo][kLoraMaxRank] and the matrix
+  // lbx [E][rank][out] they multiply (the adapter's A, row-major, out = the
+  // GEMM's output columns)
+  const uint16_t* lzq;
+  const uint16_t* lbx;
+  float lscale;
+  int lrank;
 };
 
 // Work item of a grouped-GEMM launch.
@@ -238,7 +246,15 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
 // blocks' loads are in flight while one is multiplied; NKB = 0 is the
 // general loop with one block in flight.  Both run the same MFMA sequence on
 // every element.
-template <int MODE, int NKB = 0>
+// LORA (dgrad modes, routed groups): before the epilogue the routed rows'
+// LoRA term is added on the matrix cores, acc = fma(scale, z A, acc) with z
+// the rows' shrink results (bf16 hi + lo, two MFMAs) and A the adapter's
+// rank x 128 slice of the tile's columns (zero past the rank).  kDact takes
+// z = B2^T dOut and A2, so D + s A2^T B2^T dOut is the gradient of act and
+// dact = g (D + s A2^T B2^T dOut) and the route-weight gradient
+// <D + s A2^T B2^T dOut, act> include the adapter; kDx takes z = B13^T dGU
+// and A13.
+template <int MODE, int NKB = 0, bool LORA = false>
 __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void bwd_gemm_kernel(const BwdArgs a) {
   constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
   static_assert(NKB == 0 || !WGRAD, "the unrolled loop is for the dgrad modes");
@@ -254,6 +270,9 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   // the same area
   constexpr int EPI = 64 * (kBT + 4) * 2;
   __shared__ __attribute__((aligned(16))) uint16_t smem[NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI];
+  // LoRA: the tile's rows' shrink results and its columns' expand rows
+  __shared__ __attribute__((aligned(16))) uint16_t zs[LORA ? kBT * 2 * kLoraMaxRank : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lbs[LORA ? kLoraMaxRank * kBT : 8];
 
   BwdTile w;
   if (!bwd_decode<MODE>(a, blockIdx.x, w)) return;
@@ -262,6 +281,20 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   const int i = lane & 31, half = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
   const int Ie = w.Ie;
+  const bool lora = LORA && !w.shared;  // the shared expert has no adapter
+  if (lora) {
+    // rows past the tile's end get zeros; ordered before the epilogue by the
+    // K loop's barriers
+    const uint16_t* z0 = a.lzq + (static_cast<int64_t>(w.seg0) + w.m0) * 2 * kLoraMaxRank;
+    for (int q = tid; q < kBT * 4; q += 256)
+      st16(&zs[8 * q], q < w.rows * 4 ? ld16(z0 + 8 * q) : u32x4_t{0u, 0u, 0u, 0u});
+    const int64_t nout = MODE == kDact ? a.I : a.H;
+    const uint16_t* b0 = a.lbx + static_cast<int64_t>(w.grp) * a.lrank * nout + w.n0;
+    for (int q = tid; q < a.lrank * (kBT / 8); q += 256) {
+      const int j = q / (kBT / 8), c = q - j * (kBT / 8);
+      st16(&lbs[j * kBT + 8 * c], ld16(b0 + j * nout + 8 * c));
+    }
+  }
 
   int kdim;
   if (MODE == kDact) kdim = a.H;
@@ -482,6 +515,34 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[mb][nb][v] = tot[mb][nb][v] + acc[mb][nb][v];
+    }
+  }
+
+  if constexpr (LORA) {
+    if (lora) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int zr = wm * 64 + mb * 32 + i;
+        const u32x4_t zh = ld16(&zs[zr * 2 * kLoraMaxRank + 8 * half]);
+        const u32x4_t zl = ld16(&zs[zr * 2 * kLoraMaxRank + kLoraMaxRank + 8 * half]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          // B[k][n] = A[k][n0 + col] for k < rank, else 0
+          const int col = wn * 64 + nb * 32 + i;
+          uint32_t bw[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j0 = 8 * half + 2 * q;
+            const uint32_t e0 = j0 < a.lrank ? lbs[j0 * kBT + col] : 0u;
+            const uint32_t e1 = j0 + 1 < a.lrank ? lbs[(j0 + 1) * kBT + col] : 0u;
+            bw[q] = e0 | (e1 << 16);
+          }
+          const u32x4_t b{bw[0], bw[1], bw[2], bw[3]};
+          const f32x16_t t = mfma32x32x16(zl, b, mfma32x32x16(zh, b, zero16()));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[mb][nb][v] = fmaf(a.lscale, t[v], acc[mb][nb][v]);
+        }
+      }
     }
   }
 
@@ -812,6 +873,88 @@ __global__ __launch_bounds__(256) void bwd_dx_sum_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// LoRA adapter gradients of the routed experts.  Each is a sum over the
+// expert's routes p (ascending sorted position) of a rank vector r[p] (a
+// shrink result, its bf16 hi + lo) times a feature row f[p], in fp64, times
+// the scale s:
+//   kind 0  dA13[e][j][h] = s sum_p u13[p][j] x[t(p)][h]      u13 = B13^T dGU
+//   kind 1  dB13[e][c][j] = s sum_p dGU[p][c] z13[p][j]        z13 = A13 x
+//   kind 2  dA2[e][j][i]  = s sum_p v2[p][j] (g act)[p][i]     v2 = B2^T dOut
+//   kind 3  dB2[e][h][j]  = s sum_p dOut[t(p)][h] gz2[p][j]    gz2 = A2 (g act)
+// The gradient reaching the down adapter's output is g dOut, so kinds 2 and
+// 3 carry the route's gate g in the feature (g act, exact as three planes)
+// or in the shrink (gz2 = g z2).  dGU also enters exactly, as three planes.
+// Workgroup = (expert, 256 features), one feature per thread.  No atomics.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_lora_grad_kernel(const BwdArgs a, int kind,
+                                                            const uint16_t* __restrict__ rq,
+                                                            float* __restrict__ out) {
+  // offsets that failed ffn_tiles_kernel's check left an empty work list
+  if (a.meta[0] == 0) return;
+  const int e = blockIdx.x;
+  const int nf = (kind == 0 || kind == 3) ? a.H : (kind == 1 ? 2 * a.I : a.I);
+  const int f = blockIdx.y * 256 + threadIdx.x;
+  __shared__ float rs[64][kLoraMaxRank];
+  const int64_t R = a.T * a.K;
+  // segment bounds clamped to [0, R] (only keeps the reads in bounds)
+  const int64_t p0 = min(max(static_cast<int64_t>(a.offsets[e]), int64_t{0}), R);
+  const int64_t p1 = max(min(static_cast<int64_t>(a.offsets[e + 1]), R), p0);
+  const uint16_t* tok_src = kind == 0 ? a.x : a.dout;
+  const uint16_t* pl0 = kind == 1 ? a.dgu[0] : a.gact[0];
+  const uint16_t* pl1 = kind == 1 ? a.dgu[1] : a.gact[1];
+  const uint16_t* pl2 = kind == 1 ? a.dgu[2] : a.gact[2];
+  const bool gathered = kind == 0 || kind == 3;
+  double acc[kLoraMaxRank];
+#pragma unroll
+  for (int j = 0; j < kLoraMaxRank; ++j) acc[j] = 0.0;
+  for (int64_t pb = p0; pb < p1; pb += 64) {
+    const int n = static_cast<int>(min(static_cast<int64_t>(64), p1 - pb));
+    __syncthreads();
+    for (int q = threadIdx.x; q < n * kLoraMaxRank; q += 256) {
+      const int r = q / kLoraMaxRank, j = q - r * kLoraMaxRank;
+      const uint16_t* z = rq + (pb + r) * 2 * kLoraMaxRank;
+      rs[r][j] = bf16_to_f32(z[j]) + bf16_to_f32(z[kLoraMaxRank + j]);
+    }
+    __syncthreads();
+    if (f < nf) {
+      for (int r = 0; r < n; ++r) {
+        const int64_t p = pb + r;
+        double fv;
+        if (gathered) {
+          const int64_t rt = a.sorted_route[p];
+          const int64_t t = (rt >= 0 && rt < R) ? rt / a.K : 0;
+          fv = bf16_to_f32(tok_src[t * a.H + f]);
+        } else {
+          const int64_t o = p * nf + f;
+          fv = static_cast<double>(bf16_to_f32(pl0[o])) + bf16_to_f32(pl1[o]) + bf16_to_f32(pl2[o]);
+        }
+#pragma unroll
+        for (int j = 0; j < kLoraMaxRank; ++j) acc[j] = fma(static_cast<double>(rs[r][j]), fv, acc[j]);
+      }
+    }
+  }
+  if (f >= nf) return;
+  const double sc = a.lscale;
+  for (int j = 0; j < a.lrank; ++j) {
+    const float v = static_cast<float>(sc * acc[j]);
+    if (kind == 0 || kind == 2) out[(static_cast<int64_t>(e) * a.lrank + j) * nf + f] = v;
+    else out[(static_cast<int64_t>(e) * nf + f) * a.lrank + j] = v;
+  }
+}
+
+// dst[e][n][m] = src[e][m][n] (bf16), for the adapters' transposed copies.
+__global__ __launch_bounds__(256) void lora_transpose_kernel(const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst, int64_t total,
+                                                             int M, int N) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (q >= total) return;
+  const int64_t mn = static_cast<int64_t>(M) * N;
+  const int64_t e = q / mn, rem = q - e * mn;
+  const int n = static_cast<int>(rem / M), m = static_cast<int>(rem - static_cast<int64_t>(n) * M);
+  dst[q] = src[e * mn + static_cast<int64_t>(m) * N + n];
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_bwd_gate(const double* dgp, const double* dsp, const float* gate, const float* sg,
@@ -861,6 +1004,10 @@ BwdArgs bwd_args(const BwdLaunch& L) {
   a.dw2 = L.dw2;
   a.dws13 = L.dws13;
   a.dws2 = L.dws2;
+  a.lzq = nullptr;
+  a.lbx = nullptr;
+  a.lscale = L.lscale;
+  a.lrank = L.lrank;
   return a;
 }
 
@@ -868,31 +1015,67 @@ unsigned rounds(int64_t items) { return static_cast<unsigned>(((items + 7) / 8) 
 }  // namespace
 
 hipError_t launch_bwd_dact(const BwdLaunch& L, hipStream_t stream) {
-  const BwdArgs a = bwd_args(L);
+  BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  const int64_t dgrad_tiles = L.max_tiles_bwd;
-  // the unrolled instantiation covers H = 2048
-  if (L.H == 2048)
-    bwd_gemm_kernel<kDact, 2048 / kBK><<<rounds(dgrad_tiles * (Imax / kBT)), 256, 0, stream>>>(a);
-  else
-    bwd_gemm_kernel<kDact><<<rounds(dgrad_tiles * (Imax / kBT)), 256, 0, stream>>>(a);
+  const unsigned grid = rounds(static_cast<int64_t>(L.max_tiles_bwd) * (Imax / kBT));
+  // the unrolled instantiations cover H = 2048
+  if (L.la2) {
+    a.lzq = L.lv2;
+    a.lbx = L.la2;
+    if (L.H == 2048) bwd_gemm_kernel<kDact, 2048 / kBK, true><<<grid, 256, 0, stream>>>(a);
+    else bwd_gemm_kernel<kDact, 0, true><<<grid, 256, 0, stream>>>(a);
+  } else if (L.H == 2048) {
+    bwd_gemm_kernel<kDact, 2048 / kBK><<<grid, 256, 0, stream>>>(a);
+  } else {
+    bwd_gemm_kernel<kDact><<<grid, 256, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
-  const BwdArgs a = bwd_args(L);
+  BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  const int64_t dgrad_tiles = L.max_tiles_bwd;
-  // the unrolled dx instantiation covers expert and shared sizes of 512
-  if (L.I == 512 && (L.Is == 0 || L.Is == 512))
-    bwd_gemm_kernel<kDx, 2 * 512 / kBK><<<rounds(dgrad_tiles * (L.H / kBT)), 256, 0, stream>>>(a);
-  else
-    bwd_gemm_kernel<kDx><<<rounds(dgrad_tiles * (L.H / kBT)), 256, 0, stream>>>(a);
+  const unsigned dx_grid = rounds(static_cast<int64_t>(L.max_tiles_bwd) * (L.H / kBT));
+  // the unrolled dx instantiations cover expert and shared sizes of 512
+  const bool unrolled = L.I == 512 && (L.Is == 0 || L.Is == 512);
+  if (L.la13) {
+    a.lzq = L.lu13;
+    a.lbx = L.la13;
+    if (unrolled) bwd_gemm_kernel<kDx, 2 * 512 / kBK, true><<<dx_grid, 256, 0, stream>>>(a);
+    else bwd_gemm_kernel<kDx, 0, true><<<dx_grid, 256, 0, stream>>>(a);
+    a.lzq = nullptr;
+    a.lbx = nullptr;
+  } else if (unrolled) {
+    bwd_gemm_kernel<kDx, 2 * 512 / kBK><<<dx_grid, 256, 0, stream>>>(a);
+  } else {
+    bwd_gemm_kernel<kDx><<<dx_grid, 256, 0, stream>>>(a);
+  }
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
   bwd_gemm_kernel<kDw2><<<rounds(groups * (L.H / kBT) * (Imax / kBT)), 256, 0, stream>>>(a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   bwd_gemm_kernel<kDw13><<<rounds(groups * (2 * Imax / kBT) * (L.H / kBT)), 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_lora_grads(const BwdLaunch& L, const uint16_t* z13, const uint16_t* gz2, float* da13,
+                                 float* db13, float* da2, float* db2, hipStream_t stream) {
+  const BwdArgs a = bwd_args(L);
+  const uint16_t* rq[4] = {L.lu13, z13, L.lv2, gz2};
+  float* out[4] = {da13, db13, da2, db2};
+  const int nf[4] = {L.H, 2 * L.I, L.I, L.H};
+  for (int k = 0; k < 4; ++k) {
+    const dim3 grid(static_cast<unsigned>(L.E), static_cast<unsigned>((nf[k] + 255) / 256));
+    bwd_lora_grad_kernel<<<grid, 256, 0, stream>>>(a, k, rq[k], out[k]);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_lora_transpose(const uint16_t* src, uint16_t* dst, int E, int M, int N, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(E) * M * N;
+  if (total == 0) return hipSuccess;
+  lora_transpose_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(src, dst, total, M, N);
   return hipGetLastError();
 }
 

@@ -49,6 +49,13 @@ struct Layout {
   size_t dx_shared = 0;              // [T][H] f32
   size_t wsg_partial = 0;            // [ceil(T/64)][H] f64
   size_t bwd_end = 0;
+  // LoRA backward (after bwd_end): shrink results v2 = B2^T dOut and u13 =
+  // B13^T dGU ([R][hi, lo][kLoraMaxRank] bf16), and the transposed expand
+  // matrices B2^T [E][rank][H] and B13^T [E][rank][2I] the shrinks read
+  // (A13 x and A2 (g act) reuse lora_z13 and lora_z2, the 64-row work list
+  // reuses tiles and meta)
+  size_t lora_v2 = 0, lora_u13 = 0, lora_b2t = 0, lora_b13t = 0;
+  size_t lora_bwd_end = 0;
   int nblocks = 0;
   int max_tiles = 0;
   int up_rows = 0;       // rows per up-projection item (moe::up_rows_per_tile)
@@ -105,6 +112,11 @@ Layout make_layout(const moe_dims& d) {
   L.dx_shared = take(static_cast<size_t>(T) * H * 4);
   L.wsg_partial = take(static_cast<size_t>((T + 63) / 64) * H * 8);
   L.bwd_end = o;
+  L.lora_v2 = take(static_cast<size_t>(R) * 2 * moe::kLoraMaxRank * 2);
+  L.lora_u13 = take(static_cast<size_t>(R) * 2 * moe::kLoraMaxRank * 2);
+  L.lora_b2t = take(static_cast<size_t>(E) * moe::kLoraMaxRank * H * 2);
+  L.lora_b13t = take(static_cast<size_t>(E) * moe::kLoraMaxRank * 2 * I * 2);
+  L.lora_bwd_end = o;
   return L;
 }
 
@@ -310,8 +322,8 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
   const int has_shared = d.shared_inter > 0;
   if (!whole_forward)
     MOE_LAUNCH(moe::launch_ffn_tiles(r->expert_offsets, at<int32_t>(ws, L.tiles), tiles_up_of(ws, L),
-                                     L.up_rows, at<int32_t>(ws, L.meta), at<int>(ws, L.err), d.experts,
-                                     d.tokens, d.top_k, has_shared, moe::kRowsPerTile, s));
+                                     L.up_rows, at<int32_t>(ws, L.meta), at<int>(ws, L.err), 0,
+                                     d.experts, d.tokens, d.top_k, has_shared, moe::kRowsPerTile, s));
   if (has_shared && !whole_forward)
     MOE_LAUNCH(moe::launch_shared_gate(x, w->w_sgate, sv->shared_gate, d.tokens, d.hidden, s));
   const bool own_up = tiles_up_of(ws, L) != nullptr;
@@ -385,6 +397,149 @@ void add_saved(Args& a, const moe_dims& d, const moe_saved* sv, bool out) {
   }
 }
 
+// moe_backward (lora null) and moe_backward_lora (rank already checked).
+int run_backward(const moe_dims* dims, const moe_weights* w, const moe_lora* lora, const uint16_t* x,
+                 const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
+                 float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, moe_lora_grads* lg, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!w || !routes || !saved || !grads) return MOE_E_NULL;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, K = d.top_k, E = d.experts, H = d.hidden, I = d.inter,
+               Is = d.shared_inter;
+  Args a;
+  a.in(x, bytes_x(d));
+  a.in(d_out, bytes_x(d));
+  add_weights(a, d, w, true, true);
+  a.in(routes->topk_idx, T * K * 4);
+  a.in(routes->topk_gate, T * K * 4);
+  a.in(routes->expert_offsets, (E + 1) * 4);
+  a.in(routes->sorted_route, T * K * 4);
+  a.in(saved->y, T * K * H * 4, false);  // not read: dg is formed from D and act
+  a.in(saved->gu, T * K * 2 * I * 4);
+  if (Is) {
+    a.in(saved->shared_y, T * H * 4, false);  // not read: ds is formed from D and act
+    a.in(saved->shared_gate, T * 4);
+    a.in(saved->shared_gu, T * 2 * Is * 4);
+  }
+  a.out(d_x_f32, T * H * 4);
+  a.out(d_x_bf16, T * H * 2, false);
+  a.out(grads->d_w_router, E * H * 4);
+  a.out(grads->d_w13, E * 2 * I * H * 4);
+  a.out(grads->d_w2, E * H * I * 4);
+  if (Is) {
+    a.out(grads->d_ws13, 2 * Is * H * 4);
+    a.out(grads->d_ws2, H * Is * 4);
+    a.out(grads->d_w_sgate, H * 4);
+  }
+  const size_t rk = lora ? lora->rank : 0;
+  if (lora) {
+    a.in(lora->a13, E * rk * H * 2);
+    a.in(lora->b13, E * 2 * I * rk * 2);
+    a.in(lora->a2, E * rk * I * 2);
+    a.in(lora->b2, E * H * rk * 2);
+    a.out(lg->d_a13, E * rk * H * 4);
+    a.out(lg->d_b13, E * 2 * I * rk * 4);
+    a.out(lg->d_a2, E * rk * I * 4);
+    a.out(lg->d_b2, E * H * rk * 4);
+  }
+  const int op = lora ? MOE_OP_BACKWARD_LORA : MOE_OP_BACKWARD;
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, op)), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, op));
+  MOE_TRY(check_device());
+  const Layout L = make_layout(d);
+  const bool sh = Is > 0;
+  hipStream_t s = stream;
+  // the backward's first kernel also overwrites the workspace's error word
+  MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles_bwd), nullptr, 0,
+                                   at<int32_t>(ws, L.meta_bwd), at<int>(ws, L.err), 1, d.experts, d.tokens,
+                                   d.top_k, sh, moe::kBwdRowsPerTile, s));
+  moe::BwdLaunch b;
+  b.T = d.tokens;
+  b.H = d.hidden;
+  b.E = d.experts;
+  b.K = d.top_k;
+  b.I = d.inter;
+  b.Is = d.shared_inter;
+  b.max_tiles_bwd = L.max_tiles_bwd;
+  b.offsets = routes->expert_offsets;
+  b.sorted_route = routes->sorted_route;
+  b.gate = routes->topk_gate;
+  b.sg = sh ? saved->shared_gate : nullptr;
+  b.tiles = at<int32_t>(ws, L.tiles_bwd);
+  b.meta = at<int32_t>(ws, L.meta_bwd);
+  b.x = x;
+  b.dout = d_out;
+  b.w13 = w->w13;
+  b.w2 = w->w2;
+  b.ws13 = sh ? w->ws13 : nullptr;
+  b.ws2 = sh ? w->ws2 : nullptr;
+  b.gu = saved->gu;
+  b.sgu = sh ? saved->shared_gu : nullptr;
+  for (int q = 0; q < moe::kGradPlanes; ++q) {
+    b.dgu[q] = at<uint16_t>(ws, L.dgu[q]);
+    b.sdgu[q] = at<uint16_t>(ws, L.sdgu[q]);
+    b.gact[q] = at<uint16_t>(ws, L.gact[q]);
+    b.sgact[q] = at<uint16_t>(ws, L.sgact[q]);
+  }
+  b.dgp = at<double>(ws, L.dgp);
+  b.dsp = sh ? at<double>(ws, L.dsp) : nullptr;
+  b.dx_route = at<float>(ws, L.dx_route);
+  b.dx_shared = sh ? at<float>(ws, L.dx_shared) : nullptr;
+  b.dw13 = grads->d_w13;
+  b.dw2 = grads->d_w2;
+  b.dws13 = sh ? grads->d_ws13 : nullptr;
+  b.dws2 = sh ? grads->d_ws2 : nullptr;
+  // the adapters' shrinks run over the 64-row work list of the forward
+  auto shrink = [&](const uint16_t* vh, const uint16_t* vl, const uint16_t* am, size_t z, int kd) {
+    return moe::launch_lora_shrink(vh, vl, am, routes->expert_offsets, routes->sorted_route,
+                                   at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta), at<uint16_t>(ws, z),
+                                   d.tokens, kd, d.experts, d.top_k, lora->rank, L.max_tiles, s);
+  };
+  if (lora) {
+    b.la13 = lora->a13;
+    b.la2 = lora->a2;
+    b.lv2 = at<uint16_t>(ws, L.lora_v2);
+    b.lu13 = at<uint16_t>(ws, L.lora_u13);
+    b.lscale = lora->scale;
+    b.lrank = lora->rank;
+    MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles), nullptr, 0,
+                                     at<int32_t>(ws, L.meta), at<int>(ws, L.err), 0, d.experts, d.tokens,
+                                     d.top_k, sh, moe::kRowsPerTile, s));
+    MOE_LAUNCH(moe::launch_lora_transpose(lora->b2, at<uint16_t>(ws, L.lora_b2t), d.experts, d.hidden,
+                                          lora->rank, s));
+    MOE_LAUNCH(moe::launch_lora_transpose(lora->b13, at<uint16_t>(ws, L.lora_b13t), d.experts,
+                                          2 * d.inter, lora->rank, s));
+    MOE_LAUNCH(shrink(d_out, nullptr, at<uint16_t>(ws, L.lora_b2t), L.lora_v2, d.hidden));
+  }
+  MOE_LAUNCH(moe::launch_bwd_dact(b, s));
+  MOE_LAUNCH(moe::launch_bwd_gate(b.dgp, b.dsp, routes->topk_gate, sh ? saved->shared_gate : nullptr,
+                                  at<float>(ws, L.dl), at<float>(ws, L.dz), d.tokens, d.top_k, d.inter,
+                                  d.shared_inter, s));
+  if (lora) {
+    MOE_LAUNCH(shrink(b.dgu[0], b.dgu[1], at<uint16_t>(ws, L.lora_b13t), L.lora_u13, 2 * d.inter));
+    MOE_LAUNCH(shrink(x, nullptr, lora->a13, L.lora_z13, d.hidden));
+    MOE_LAUNCH(shrink(b.gact[0], b.gact[1], lora->a2, L.lora_z2, d.inter));
+  }
+  MOE_LAUNCH(moe::launch_bwd_gemms(b, s));
+  if (lora)
+    MOE_LAUNCH(moe::launch_bwd_lora_grads(b, at<uint16_t>(ws, L.lora_z13), at<uint16_t>(ws, L.lora_z2),
+                                          lg->d_a13, lg->d_b13, lg->d_a2, lg->d_b2, s));
+  MOE_LAUNCH(moe::launch_bwd_router(x, at<float>(ws, L.dl), routes->expert_offsets,
+                                    routes->sorted_route, grads->d_w_router, d.tokens, d.hidden,
+                                    d.experts, d.top_k, s));
+  if (sh)
+    MOE_LAUNCH(moe::launch_bwd_wsg(x, at<float>(ws, L.dz), at<double>(ws, L.wsg_partial),
+                                   grads->d_w_sgate, d.tokens, d.hidden, s));
+  MOE_LAUNCH(moe::launch_bwd_dx_sum(routes->topk_idx, at<float>(ws, L.dl), at<float>(ws, L.dx_route),
+                                    sh ? at<float>(ws, L.dx_shared) : nullptr, at<float>(ws, L.dz),
+                                    sh ? w->w_sgate : nullptr, w->w_router, d_x_f32, d_x_bf16,
+                                    d.tokens, d.hidden, d.experts, d.top_k, s));
+  return MOE_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -418,6 +573,7 @@ size_t moe_workspace_bytes(const moe_dims* dims, int op) {
     case MOE_OP_FFN:
     case MOE_OP_FORWARD: return L.fwd_end;
     case MOE_OP_FORWARD_LORA: return L.lora_end;
+    case MOE_OP_BACKWARD_LORA: return L.lora_bwd_end;
     case MOE_OP_BACKWARD: return L.bwd_end;
     default: return 0;
   }
@@ -678,99 +834,20 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                  const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
                  float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws, size_t ws_bytes,
                  hipStream_t stream) {
+  return run_backward(dims, w, nullptr, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+int moe_backward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,
+                      const uint16_t* x, const moe_routes* routes, const moe_saved* saved,
+                      const uint16_t* d_out, float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads,
+                      moe_lora_grads* lora_grads, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_dims(dims));
   if (dims->tokens == 0) return MOE_OK;
-  if (!w || !routes || !saved || !grads) return MOE_E_NULL;
-  const moe_dims& d = *dims;
-  const size_t T = d.tokens, K = d.top_k, E = d.experts, H = d.hidden, I = d.inter,
-               Is = d.shared_inter;
-  Args a;
-  a.in(x, bytes_x(d));
-  a.in(d_out, bytes_x(d));
-  add_weights(a, d, w, true, true);
-  a.in(routes->topk_idx, T * K * 4);
-  a.in(routes->topk_gate, T * K * 4);
-  a.in(routes->expert_offsets, (E + 1) * 4);
-  a.in(routes->sorted_route, T * K * 4);
-  a.in(saved->y, T * K * H * 4, false);  // not read: dg is formed from D and act
-  a.in(saved->gu, T * K * 2 * I * 4);
-  if (Is) {
-    a.in(saved->shared_y, T * H * 4, false);  // not read: ds is formed from D and act
-    a.in(saved->shared_gate, T * 4);
-    a.in(saved->shared_gu, T * 2 * Is * 4);
-  }
-  a.out(d_x_f32, T * H * 4);
-  a.out(d_x_bf16, T * H * 2, false);
-  a.out(grads->d_w_router, E * H * 4);
-  a.out(grads->d_w13, E * 2 * I * H * 4);
-  a.out(grads->d_w2, E * H * I * 4);
-  if (Is) {
-    a.out(grads->d_ws13, 2 * Is * H * 4);
-    a.out(grads->d_ws2, H * Is * 4);
-    a.out(grads->d_w_sgate, H * 4);
-  }
-  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_BACKWARD)), false);
-  MOE_TRY(a.status());
-  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_BACKWARD));
-  MOE_TRY(check_device());
-  const Layout L = make_layout(d);
-  const bool sh = Is > 0;
-  hipStream_t s = stream;
-  MOE_LAUNCH(moe::launch_ffn_tiles(routes->expert_offsets, at<int32_t>(ws, L.tiles_bwd), nullptr, 0,
-                                   at<int32_t>(ws, L.meta_bwd), at<int>(ws, L.err), d.experts, d.tokens,
-                                   d.top_k, sh, moe::kBwdRowsPerTile, s));
-  moe::BwdLaunch b;
-  b.T = d.tokens;
-  b.H = d.hidden;
-  b.E = d.experts;
-  b.K = d.top_k;
-  b.I = d.inter;
-  b.Is = d.shared_inter;
-  b.max_tiles_bwd = L.max_tiles_bwd;
-  b.offsets = routes->expert_offsets;
-  b.sorted_route = routes->sorted_route;
-  b.gate = routes->topk_gate;
-  b.sg = sh ? saved->shared_gate : nullptr;
-  b.tiles = at<int32_t>(ws, L.tiles_bwd);
-  b.meta = at<int32_t>(ws, L.meta_bwd);
-  b.x = x;
-  b.dout = d_out;
-  b.w13 = w->w13;
-  b.w2 = w->w2;
-  b.ws13 = sh ? w->ws13 : nullptr;
-  b.ws2 = sh ? w->ws2 : nullptr;
-  b.gu = saved->gu;
-  b.sgu = sh ? saved->shared_gu : nullptr;
-  for (int q = 0; q < moe::kGradPlanes; ++q) {
-    b.dgu[q] = at<uint16_t>(ws, L.dgu[q]);
-    b.sdgu[q] = at<uint16_t>(ws, L.sdgu[q]);
-    b.gact[q] = at<uint16_t>(ws, L.gact[q]);
-    b.sgact[q] = at<uint16_t>(ws, L.sgact[q]);
-  }
-  b.dgp = at<double>(ws, L.dgp);
-  b.dsp = sh ? at<double>(ws, L.dsp) : nullptr;
-  b.dx_route = at<float>(ws, L.dx_route);
-  b.dx_shared = sh ? at<float>(ws, L.dx_shared) : nullptr;
-  b.dw13 = grads->d_w13;
-  b.dw2 = grads->d_w2;
-  b.dws13 = sh ? grads->d_ws13 : nullptr;
-  b.dws2 = sh ? grads->d_ws2 : nullptr;
-  MOE_LAUNCH(moe::launch_bwd_dact(b, s));
-  MOE_LAUNCH(moe::launch_bwd_gate(b.dgp, b.dsp, routes->topk_gate, sh ? saved->shared_gate : nullptr,
-                                  at<float>(ws, L.dl), at<float>(ws, L.dz), d.tokens, d.top_k, d.inter,
-                                  d.shared_inter, s));
-  MOE_LAUNCH(moe::launch_bwd_gemms(b, s));
-  MOE_LAUNCH(moe::launch_bwd_router(x, at<float>(ws, L.dl), routes->expert_offsets,
-                                    routes->sorted_route, grads->d_w_router, d.tokens, d.hidden,
-                                    d.experts, d.top_k, s));
-  if (sh)
-    MOE_LAUNCH(moe::launch_bwd_wsg(x, at<float>(ws, L.dz), at<double>(ws, L.wsg_partial),
-                                   grads->d_w_sgate, d.tokens, d.hidden, s));
-  MOE_LAUNCH(moe::launch_bwd_dx_sum(routes->topk_idx, at<float>(ws, L.dl), at<float>(ws, L.dx_route),
-                                    sh ? at<float>(ws, L.dx_shared) : nullptr, at<float>(ws, L.dz),
-                                    sh ? w->w_sgate : nullptr, w->w_router, d_x_f32, d_x_bf16,
-                                    d.tokens, d.hidden, d.experts, d.top_k, s));
-  return MOE_OK;
+  if (!lora || !lora_grads) return MOE_E_NULL;
+  if (lora->rank < 1 || lora->rank > moe::kLoraMaxRank) return MOE_E_SHAPE;
+  return run_backward(dims, w, lora, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, lora_grads, ws,
+                      ws_bytes, stream);
 }
 
 int moe_last_device_error(void* ws, hipStream_t stream) {

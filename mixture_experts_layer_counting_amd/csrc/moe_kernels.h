@@ -42,9 +42,11 @@ hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* 
                              hipStream_t stream);
 // Work list from caller-supplied offsets; offsets that are not a partition
 // of [0, T*K) set *err_word and give an empty list.
+// Offsets that are not a partition of [0, T*K) set *err_word = 1 and leave
+// an empty list; with err_overwrite valid offsets clear it (0).
 hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* tiles_up, int up_rows,
-                            int32_t* meta, int* err_word, int E, int64_t T, int K, int has_shared,
-                            int rows_per_tile, hipStream_t stream);
+                            int32_t* meta, int* err_word, int err_overwrite, int E, int64_t T, int K,
+                            int has_shared, int rows_per_tile, hipStream_t stream);
 hipError_t launch_route_scatter(const int32_t* topk_idx, const int32_t* block_base,
                                 const int32_t* offsets, int32_t* route_pos, int32_t* sorted_route,
                                 int64_t T, int E, int K, hipStream_t stream);
@@ -111,6 +113,16 @@ struct BwdLaunch {
   double* dsp;  // [T][max(I, Is) / 128] partial shared-gate gradients (kDact)
   float *dx_route, *dx_shared;
   float *dw13, *dw2, *dws13, *dws2;
+  // LoRA adapters of the routed experts (la13 = la2 = null: none): A13
+  // [E][rank][H] and A2 [E][rank][I], and the shrink results (bf16 pairs
+  // [R][hi, lo][kLoraMaxRank]) v2 = B2^T dOut, read by launch_bwd_dact, and
+  // u13 = B13^T dGU, read by launch_bwd_gemms and launch_bwd_lora_grads
+  const uint16_t* la13 = nullptr;
+  const uint16_t* la2 = nullptr;
+  const uint16_t* lv2 = nullptr;
+  const uint16_t* lu13 = nullptr;
+  float lscale = 0.f;
+  int lrank = 0;
 };
 
 // Backward order: launch_bwd_dact (dGU and g*act planes, partial dot
@@ -121,6 +133,14 @@ hipError_t launch_bwd_gate(const double* dgp, const double* dsp, const float* ga
                            float* dl, float* dz, int64_t T, int K, int I, int Is,
                            hipStream_t stream);
 hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream);
+// With adapters: the shrinks of v2 (before launch_bwd_dact) and of u13, z13
+// = A13 x and gz2 = A2 (g act) (after it) by launch_lora_shrink, then
+// launch_bwd_lora_grads writes dA13 [E][rank][H], dB13 [E][2I][rank], dA2
+// [E][rank][I] and dB2 [E][H][rank].
+hipError_t launch_bwd_lora_grads(const BwdLaunch& L, const uint16_t* z13, const uint16_t* gz2, float* da13,
+                                 float* db13, float* da2, float* db2, hipStream_t stream);
+// dst[e][n][m] = src[e][m][n] for bf16 [E][M][N] matrices.
+hipError_t launch_lora_transpose(const uint16_t* src, uint16_t* dst, int E, int M, int N, hipStream_t stream);
 hipError_t launch_bwd_router(const uint16_t* x, const float* dl, const int32_t* offsets,
                              const int32_t* sorted_route, float* dwr, int64_t T, int H, int E,
                              int K, hipStream_t stream);

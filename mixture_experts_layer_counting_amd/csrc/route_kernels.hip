@@ -637,8 +637,8 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ tiles_up, int up_rows,
                                                          int32_t* __restrict__ meta, int* __restrict__ err_word,
-                                                         int E, int64_t T, int K, int has_shared,
-                                                         int rows_per_tile) {
+                                                         int err_overwrite, int E, int64_t T, int K,
+                                                         int has_shared, int rows_per_tile) {
   __shared__ int buf[1024];
   __shared__ int bad;
   const int e = threadIdx.x;
@@ -658,6 +658,7 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
     }
     return;
   }
+  if (err_overwrite && e == 0) *err_word = 0;
   emit_tiles(count, E, T, has_shared, tiles, &meta[0], buf, rows_per_tile);
   if (tiles_up) emit_tiles(count, E, T, has_shared, tiles_up, &meta[2], buf, up_rows);
 }
@@ -925,10 +926,10 @@ hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* 
 }
 
 hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* tiles_up, int up_rows,
-                            int32_t* meta, int* err_word, int E, int64_t T, int K, int has_shared,
-                            int rows_per_tile, hipStream_t stream) {
-  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, tiles_up, up_rows, meta, err_word, E, T, K,
-                                           has_shared, rows_per_tile);
+                            int32_t* meta, int* err_word, int err_overwrite, int E, int64_t T, int K,
+                            int has_shared, int rows_per_tile, hipStream_t stream) {
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, tiles, tiles_up, up_rows, meta, err_word, err_overwrite,
+                                           E, T, K, has_shared, rows_per_tile);
   return hipGetLastError();
 }
 

@@ -97,7 +97,7 @@ def assert_close(got, ref, what, atol=ATOL, rtol=RTOL):
     return err.max()
 
 
-def fed_forward(layer, x_bits, idx, gates, gu_sorted, route_pos, sgu=None, sg=None):
+def fed_forward(layer, x_bits, idx, gates, gu_sorted, route_pos, sgu=None, sg=None, lora=None):
     """An oracle forward dict holding the GPU's saved fp32 forward values --
     gate/up pre-activations, route gates, shared gate -- (exact in float64),
     with Y and S recomputed from them in float64.
@@ -107,7 +107,8 @@ def fed_forward(layer, x_bits, idx, gates, gu_sorted, route_pos, sgu=None, sg=No
     them).  Feeding them to the oracle's backward isolates what these
     rounding points alone cost: the distance of this oracle from the plain
     one is inherent to the method, the distance of the GPU from this oracle
-    is the backward kernels' own error."""
+    is the backward kernels' own error.  With `lora` (the adapters of the
+    forward) Y carries the down adapter's update."""
     K = idx.shape[1]
     x64 = O.bf16_to_f64(x_bits)
     gu = np.asarray(gu_sorted, np.float64)[np.asarray(route_pos)]
@@ -118,6 +119,9 @@ def fed_forward(layer, x_bits, idx, gates, gu_sorted, route_pos, sgu=None, sg=No
         rows = np.nonzero(flat == e)[0]
         act = O.silu(gu[rows, :inter]) * gu[rows, inter:]
         y[rows] = act @ O.bf16_to_f64(layer["w2"][e]).T
+        if lora is not None:
+            z2 = act @ O.bf16_to_f64(lora["a2"][e]).T
+            y[rows] += float(lora["scale"]) * (z2 @ O.bf16_to_f64(lora["b2"][e]).T)
     f = dict(idx=idx, gates=np.asarray(gates, np.float64), gu=gu, y=y)
     if sgu is not None:
         s_gu = np.asarray(sgu, np.float64)

@@ -243,6 +243,47 @@ def test_backward_validation_fails_closed(lib):
         assert bwd() == m.MOE_E_DEVICE
 
 
+def test_lora_backward_validation_fails_closed(lib):
+    """moe_backward_lora checks everything moe_backward checks, plus the
+    rank, the adapters, the adapter-gradient buffers (presence, alignment,
+    overlap) and its own larger workspace, before anything is launched."""
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, g, dout, dx32, dx16, wsb, wsf = backward_args(d)
+    f = Fake()
+    f.next = 1 << 44  # clear of the addresses backward_args handed out
+    E, H, I, rk = d.experts, d.hidden, d.inter, 6
+    lo = m.Lora(rank=rk, scale=0.5, a13=f(E * rk * H * 2), b13=f(E * 2 * I * rk * 2), a2=f(E * rk * I * 2),
+                b2=f(E * H * rk * 2))
+    lg = m.LoraGrads(d_a13=f(E * rk * H * 4), d_b13=f(E * 2 * I * rk * 4), d_a2=f(E * rk * I * 4),
+                     d_b2=f(E * H * rk * 4))
+    nws = m.moe_workspace_bytes(d, m.MOE_OP_BACKWARD_LORA)
+    assert nws > m.moe_workspace_bytes(d, m.MOE_OP_BACKWARD)
+    wsl = (f(nws), nws)
+
+    def call(ll=lo, lgg=lg, wss=wsl, dd=d, gg=g, ss=s):
+        return m.moe_backward_lora(dd, w, ll, x, r, ss, dout, dx32, dx16, gg, lgg, wss, stream=0)
+
+    assert call(dd=m.Dims(64, 500, 512, 10, 128, 128)) == m.MOE_E_SHAPE
+    assert call(ll=None) == m.MOE_E_NULL
+    assert call(lgg=None) == m.MOE_E_NULL
+    assert call(ll=m.Lora(**{**lo.__dict__, "rank": 0})) == m.MOE_E_SHAPE
+    assert call(ll=m.Lora(**{**lo.__dict__, "rank": 17})) == m.MOE_E_SHAPE
+    assert call(ll=m.Lora(**{**lo.__dict__, "b13": None})) == m.MOE_E_NULL
+    assert call(lgg=m.LoraGrads(**{**lg.__dict__, "d_b2": None})) == m.MOE_E_NULL
+    assert call(lgg=m.LoraGrads(**{**lg.__dict__, "d_a2": lg.d_a2 + 4})) == m.MOE_E_ALIGN
+    # an adapter gradient overlapping an adapter, a base gradient or another adapter gradient
+    assert call(lgg=m.LoraGrads(**{**lg.__dict__, "d_a13": lo.a13})) == m.MOE_E_ALIAS
+    assert call(lgg=m.LoraGrads(**{**lg.__dict__, "d_b13": g.d_w13})) == m.MOE_E_ALIAS
+    assert call(lgg=m.LoraGrads(**{**lg.__dict__, "d_b2": lg.d_a2})) == m.MOE_E_ALIAS
+    # the plain backward's workspace is too small
+    assert call(wss=wsb) == m.MOE_E_WORKSPACE
+    assert call(ss=m.Saved(**{**s.__dict__, "gu": None})) == m.MOE_E_NULL
+    assert call(dd=m.Dims(0, 512, 512, 10, 128, 128)) == m.MOE_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == m.MOE_E_DEVICE
+
+
 def test_noalloc_forward_refuses_what_its_array_cannot_hold(lib):
     """moe_forward_noalloc needs no workspace argument; dims whose forward
     workspace exceeds its array are refused on the host, invalid dims too."""

@@ -44,6 +44,7 @@ def gpu_backward(cfg, w, xd, g, dout_d, ws=None):
         ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD, DEV)
     m.check(m.moe_backward(d, w, xd, g.routes, g.saved, dout_d, dx32, dx16, grads, ws), "moe_backward")
     torch.cuda.synchronize()
+    assert m.moe_last_device_error(ws) == m.MOE_OK
     return dx32, dx16, grads
 
 

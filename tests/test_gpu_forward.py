@@ -233,15 +233,20 @@ def test_shape_edge_cases(shape):
 def test_bad_offsets_set_device_error(tiny):
     """Caller-supplied expert offsets that are not a partition of [0, T*K)
     (not starting at 0, decreasing, not ending at T*K) set the device error
-    word in the grouped FFN and the backward and run no GEMM work; nothing
-    reads past the route arrays."""
+    word in the grouped FFN and both backwards and run no GEMM work; nothing
+    reads past the route arrays.  A backward with valid offsets clears the
+    word again."""
     cfg, layer, x, w = tiny
     say("case: tiny, invalid caller offsets -> device error")
     T = 64
     d = dims_of(cfg, T)
     xd = dev_bits(x[:T])
     g = gpu_forward(cfg, w, xd, training=True)
-    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD, DEV)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD_LORA, DEV)
+    import workloads.lora as WL
+    ad = WL.lora_adapters(cfg)
+    lo = m.Lora(rank=ad["rank"], scale=ad["scale"], a13=dev_bits(ad["a13"]), b13=dev_bits(ad["b13"]),
+                a2=dev_bits(ad["a2"]), b2=dev_bits(ad["b2"]))
     good = g.routes.expert_offsets.clone()
     bads = []
     b = good.clone(); b[0] = 3; bads.append(("first", b))
@@ -259,4 +264,10 @@ def test_bad_offsets_set_device_error(tiny):
         grads = m.alloc_grads(d, DEV)
         dx = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
         m.check(m.moe_backward(d, w, xd, r, g.saved, dout, dx, None, grads, ws), "moe_backward")
+        assert m.moe_last_device_error(ws) == m.MOE_E_DEVICE, what
+        # the backward overwrites the word: valid offsets clear it
+        m.check(m.moe_backward(d, w, xd, g.routes, g.saved, dout, dx, None, grads, ws), "moe_backward")
+        assert m.moe_last_device_error(ws) == m.MOE_OK, what
+        lg = m.alloc_lora_grads(d, lo.rank, DEV)
+        m.check(m.moe_backward_lora(d, w, lo, xd, r, g.saved, dout, dx, None, grads, lg, ws), "moe_backward_lora")
         assert m.moe_last_device_error(ws) == m.MOE_E_DEVICE, what
