@@ -445,10 +445,13 @@ def run_lora(cfg, w, steps, warmup):
             "plain_forward_ms": ms_plain, "adapter_bytes": sum(int(ad[k].nbytes) for k in ("a13", "b13", "a2", "b2"))}
 
 
-def run_backward(cfg, w, steps, warmup, evict, fb_calls=5):
+def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True):
     """`fb_calls` forward (training mode) + backward calls, then `steps`
     backward-only calls of the same batch, each HIP-event timed on the
-    kernels' stream with an eviction write before it."""
+    kernels' stream with an eviction write before it.  With `lora`, also
+    `steps` backward calls of the layer with seeded LoRA adapters on every
+    routed expert (after one training-mode LoRA forward), timed the same
+    way."""
     import torch
     import mixture_experts_layer_counting_amd as m
     import workloads as W
@@ -456,7 +459,7 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5):
     x = torch.from_numpy(W.tokens(cfg).view(np.int16)).to(dev)
     dout = torch.from_numpy(W.grad_out(cfg).view(np.int16)).to(dev)
     d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
-    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD, dev)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD_LORA if lora else m.MOE_OP_BACKWARD, dev)
     routes = m.alloc_routes(d, dev, logits=False)
     saved = m.alloc_saved(d, dev, training=True)
     out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev)
@@ -486,6 +489,23 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5):
     fb = timed(lambda: (fwd(), bwd()), fb_calls)
     bo = timed(bwd, steps)
     assert m.moe_last_device_error(ws) == m.MOE_OK
+    lb = None
+    if lora:
+        import workloads.lora as WL
+        ad = WL.lora_adapters(cfg)
+        bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        lo = m.Lora(rank=ad["rank"], scale=ad["scale"], a13=bits(ad["a13"]), b13=bits(ad["b13"]),
+                    a2=bits(ad["a2"]), b2=bits(ad["b2"]))
+        lg = m.alloc_lora_grads(d, lo.rank, dev)
+        m.check(m.moe_forward_lora(d, w, lo, x, routes, saved, None, out16, ws, stream), "moe_forward_lora")
+        lbs = timed(lambda: m.check(m.moe_backward_lora(d, w, lo, x, routes, saved, dout, dx32, None, grads, lg,
+                                                        ws, stream), "moe_backward_lora"), steps)
+        assert m.moe_last_device_error(ws) == m.MOE_OK
+        lb = {"workload": f"{cfg.name}: backward with LoRA adapters of rank {ad['rank']} on all {cfg.experts} "
+                          f"routed experts (adapter gradients included)",
+              "ms": lbs["median_ms"], "p10_ms": lbs["p10_ms"], "p90_ms": lbs["p90_ms"], "calls": lbs["calls"],
+              "tokens_per_s": cfg.tokens / (lbs["median_ms"] / 1e3),
+              "over_plain_ms": lbs["median_ms"] - bo["median_ms"]}
     touched = int((np.diff(routes.expert_offsets.cpu().numpy()) > 0).sum())
     H, I, Is, T, R, E = cfg.hidden, cfg.inter, cfg.shared_inter, cfg.tokens, cfg.routes, cfg.experts
     # algorithmic bytes: weights read, fp32 weight gradients written, per-route
@@ -505,7 +525,7 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5):
             "fwd_bwd_calls": fb["calls"], "fwd_bwd_tokens_per_s": T / (fb["median_ms"] / 1e3),
             "bytes": byts, "flop": flop, "t_roof_ms": t_roof * 1e3, "roofline_frac": t_roof / (ms / 1e3),
             "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9),
-            "mfma_frac": flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12)}
+            "mfma_frac": flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12), "lora": lb}
 
 
 def host_info():
@@ -678,8 +698,9 @@ def main():
     if args.backward != "none":
         cb = W.CONFIGS[args.backward]
         log(f"bench: backward {cb.name}")
-        backward = run_backward(cb, dev_layer(cb), args.steps, 1, evict)
-        log(f"bench: backward {backward['ms']:.3f} ms, forward + backward {backward['fwd_bwd_ms']:.3f} ms")
+        backward = run_backward(cb, dev_layer(cb), args.steps, 1, evict, lora=bool(args.lora))
+        log(f"bench: backward {backward['ms']:.3f} ms, forward + backward {backward['fwd_bwd_ms']:.3f} ms"
+            + (f", LoRA backward {backward['lora']['ms']:.3f} ms" if backward["lora"] else ""))
 
     cpu = None
     if not args.no_cpu_baseline:

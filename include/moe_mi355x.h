@@ -342,9 +342,10 @@ typedef struct {
  * shrink kernel (fp32 on the matrix cores, kept as bf16 hi + lo pairs; dgu
  * and g act enter them as their first two bf16 planes, 16 significant
  * bits); the expand terms run on the matrix cores in the grouped GEMMs'
- * epilogues as in the forward; the adapter-gradient sums run over each
- * expert's routes in ascending sorted position in fp64, with dgu and g act
- * exact (three planes).  No atomics; results are deterministic.  Workspace:
+ * epilogues as in the forward; each adapter-gradient sum runs over the
+ * expert's routes in sorted order in fp32 (four contiguous quarters of the
+ * routes summed separately, then added in quarter order), with dgu and
+ * g act exact (three planes).  No atomics; results are deterministic.  Workspace:
  * moe_workspace_bytes(dims, MOE_OP_BACKWARD_LORA).  Errors as moe_backward,
  * plus MOE_E_NULL for a missing adapter, gradient struct or adapter
  * gradient and MOE_E_SHAPE for a rank outside 1..16. */

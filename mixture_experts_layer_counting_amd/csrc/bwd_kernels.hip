@@ -874,71 +874,139 @@ __global__ __launch_bounds__(256) void bwd_dx_sum_kernel(
 
 // ---------------------------------------------------------------------------
 // LoRA adapter gradients of the routed experts.  Each is a sum over the
-// expert's routes p (ascending sorted position) of a rank vector r[p] (a
-// shrink result, its bf16 hi + lo) times a feature row f[p], in fp64, times
-// the scale s:
+// expert's routes p of a rank vector r[p] (a shrink result, its bf16 hi +
+// lo) times a feature row f[p], times the scale s:
 //   kind 0  dA13[e][j][h] = s sum_p u13[p][j] x[t(p)][h]      u13 = B13^T dGU
 //   kind 1  dB13[e][c][j] = s sum_p dGU[p][c] z13[p][j]        z13 = A13 x
 //   kind 2  dA2[e][j][i]  = s sum_p v2[p][j] (g act)[p][i]     v2 = B2^T dOut
 //   kind 3  dB2[e][h][j]  = s sum_p dOut[t(p)][h] gz2[p][j]    gz2 = A2 (g act)
 // The gradient reaching the down adapter's output is g dOut, so kinds 2 and
-// 3 carry the route's gate g in the feature (g act, exact as three planes)
-// or in the shrink (gz2 = g z2).  dGU also enters exactly, as three planes.
-// Workgroup = (expert, 256 features), one feature per thread.  No atomics.
+// 3 carry the route's gate g in the feature (g act) or in the shrink (gz2 =
+// g z2).  The fp32 features (dGU, g act) enter exactly: hi + mid + lo of
+// their three bf16 planes is the fp32 value, and so is each partial sum.
+//
+// One launch covers the four kinds: blockIdx.y runs over each kind's
+// feature tiles in turn.  Workgroup = (expert, 64 * FPT features): lane l of
+// every wave owns
+// features FPT l .. FPT l + FPT - 1 (one 16- or 8-byte load per plane and
+// route), and wave w sums the w-th quarter of the expert's routes (in
+// ascending sorted position, fp32 fma, rank vector from a wave-uniform
+// load); the four partial sums are then added in wave order through LDS,
+// ((q0 + q1) + q2) + q3.  RK = the rank rounded up to 4, 8 or 16 (the shrink
+// results are zero past the rank).  No atomics; the result depends only on
+// the expert's routes.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_lora_grad_kernel(const BwdArgs a, int kind,
-                                                            const uint16_t* __restrict__ rq,
-                                                            float* __restrict__ out) {
+struct LoraGradOut {
+  const uint16_t* rq[4];  // rank vectors of kinds 0..3 (u13, z13, v2, gz2)
+  float* out[4];          // dA13, dB13, dA2, dB2
+  int tiles[5];           // first feature tile of each kind; tiles[4] = total
+};
+
+template <int RK>
+__global__ __launch_bounds__(256) void bwd_lora_grad_kernel(const BwdArgs a, const LoraGradOut o) {
+  constexpr int FPT = RK == 16 ? 4 : 8;  // features per lane (registers)
+  constexpr int NW = FPT / 2;            // 32-bit words per plane load
   // offsets that failed ffn_tiles_kernel's check left an empty work list
   if (a.meta[0] == 0) return;
   const int e = blockIdx.x;
+  int kind = 0;
+  while (kind < 3 && static_cast<int>(blockIdx.y) >= o.tiles[kind + 1]) ++kind;
+  const int tile = blockIdx.y - o.tiles[kind];
+  const uint16_t* __restrict__ rq = o.rq[kind];
+  float* __restrict__ out = o.out[kind];
   const int nf = (kind == 0 || kind == 3) ? a.H : (kind == 1 ? 2 * a.I : a.I);
-  const int f = blockIdx.y * 256 + threadIdx.x;
-  __shared__ float rs[64][kLoraMaxRank];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int f = (tile * 64 + lane) * FPT;
+  const bool live = f < nf;  // nf is a multiple of 128
+  const int fo = live ? f : 0;
   const int64_t R = a.T * a.K;
   // segment bounds clamped to [0, R] (only keeps the reads in bounds)
   const int64_t p0 = min(max(static_cast<int64_t>(a.offsets[e]), int64_t{0}), R);
   const int64_t p1 = max(min(static_cast<int64_t>(a.offsets[e + 1]), R), p0);
-  const uint16_t* tok_src = kind == 0 ? a.x : a.dout;
-  const uint16_t* pl0 = kind == 1 ? a.dgu[0] : a.gact[0];
-  const uint16_t* pl1 = kind == 1 ? a.dgu[1] : a.gact[1];
-  const uint16_t* pl2 = kind == 1 ? a.dgu[2] : a.gact[2];
+  const int64_t per = (p1 - p0 + 3) >> 2;
+  const int64_t q0 = min(p0 + wave * per, p1), q1 = min(q0 + per, p1);
   const bool gathered = kind == 0 || kind == 3;
-  double acc[kLoraMaxRank];
+  const uint16_t* src0 = gathered ? (kind == 0 ? a.x : a.dout) : (kind == 1 ? a.dgu[0] : a.gact[0]);
+  const uint16_t* src1 = kind == 1 ? a.dgu[1] : a.gact[1];
+  const uint16_t* src2 = kind == 1 ? a.dgu[2] : a.gact[2];
+
+  float acc[FPT][RK];
 #pragma unroll
-  for (int j = 0; j < kLoraMaxRank; ++j) acc[j] = 0.0;
-  for (int64_t pb = p0; pb < p1; pb += 64) {
-    const int n = static_cast<int>(min(static_cast<int64_t>(64), p1 - pb));
-    __syncthreads();
-    for (int q = threadIdx.x; q < n * kLoraMaxRank; q += 256) {
-      const int r = q / kLoraMaxRank, j = q - r * kLoraMaxRank;
-      const uint16_t* z = rq + (pb + r) * 2 * kLoraMaxRank;
-      rs[r][j] = bf16_to_f32(z[j]) + bf16_to_f32(z[kLoraMaxRank + j]);
+  for (int c = 0; c < FPT; ++c)
+#pragma unroll
+    for (int j = 0; j < RK; ++j) acc[c][j] = 0.f;
+
+  typedef uint32_t words_t __attribute__((ext_vector_type(NW)));
+  auto ldw = [&](const uint16_t* p) { return *reinterpret_cast<const words_t*>(p); };
+  // element offset of route p's feature row
+  auto row_of = [&](int64_t p) -> int64_t {
+    if (!gathered) return p * nf;
+    const int64_t rt = a.sorted_route[p];
+    return ((rt >= 0 && rt < R) ? rt / a.K : 0) * a.H;
+  };
+  auto feat = [&](int64_t o, float (&v)[FPT]) {
+    const words_t w0 = ldw(src0 + o + fo);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      v[2 * i] = bf16_to_f32(static_cast<uint16_t>(w0[i] & 0xffffu));
+      v[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w0[i] >> 16));
     }
-    __syncthreads();
-    if (f < nf) {
-      for (int r = 0; r < n; ++r) {
-        const int64_t p = pb + r;
-        double fv;
-        if (gathered) {
-          const int64_t rt = a.sorted_route[p];
-          const int64_t t = (rt >= 0 && rt < R) ? rt / a.K : 0;
-          fv = bf16_to_f32(tok_src[t * a.H + f]);
-        } else {
-          const int64_t o = p * nf + f;
-          fv = static_cast<double>(bf16_to_f32(pl0[o])) + bf16_to_f32(pl1[o]) + bf16_to_f32(pl2[o]);
-        }
+    if (!gathered) {
+      const words_t w1 = ldw(src1 + o + fo);
+      const words_t w2 = ldw(src2 + o + fo);
 #pragma unroll
-        for (int j = 0; j < kLoraMaxRank; ++j) acc[j] = fma(static_cast<double>(rs[r][j]), fv, acc[j]);
+      for (int i = 0; i < NW; ++i) {
+        v[2 * i] = (v[2 * i] + bf16_to_f32(static_cast<uint16_t>(w1[i] & 0xffffu))) +
+                   bf16_to_f32(static_cast<uint16_t>(w2[i] & 0xffffu));
+        v[2 * i + 1] = (v[2 * i + 1] + bf16_to_f32(static_cast<uint16_t>(w1[i] >> 16))) +
+                       bf16_to_f32(static_cast<uint16_t>(w2[i] >> 16));
       }
     }
+  };
+  auto accumulate = [&](int64_t p, const float (&v)[FPT]) {
+    const uint16_t* z = rq + p * 2 * kLoraMaxRank;
+#pragma unroll
+    for (int j = 0; j < RK; ++j) {
+      const float r = bf16_to_f32(z[j]) + bf16_to_f32(z[kLoraMaxRank + j]);
+#pragma unroll
+      for (int c = 0; c < FPT; ++c) acc[c][j] = fmaf(r, v[c], acc[c][j]);
+    }
+  };
+  constexpr int U = 4;  // routes per step: their feature loads in flight together
+  int64_t p = q0;
+  for (; p + U <= q1; p += U) {
+    float v[U][FPT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) feat(row_of(p + u), v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) accumulate(p + u, v[u]);
   }
-  if (f >= nf) return;
-  const double sc = a.lscale;
-  for (int j = 0; j < a.lrank; ++j) {
-    const float v = static_cast<float>(sc * acc[j]);
-    if (kind == 0 || kind == 2) out[(static_cast<int64_t>(e) * a.lrank + j) * nf + f] = v;
-    else out[(static_cast<int64_t>(e) * nf + f) * a.lrank + j] = v;
+  for (; p < q1; ++p) {
+    float v[FPT];
+    feat(row_of(p), v);
+    accumulate(p, v);
+  }
+
+  // the four waves' partial sums, added in wave order, one rank column at a
+  // time
+  __shared__ float part[4][64 * FPT];
+  const float sc = a.lscale;
+#pragma unroll
+  for (int j = 0; j < RK; ++j) {
+    if (j < a.lrank) {  // uniform
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < FPT; ++c) part[wave][lane * FPT + c] = acc[c][j];
+      __syncthreads();
+      for (int t = threadIdx.x; t < 64 * FPT; t += 256) {
+        const int ff = tile * 64 * FPT + t;
+        if (ff < nf) {
+          const float v = sc * (((part[0][t] + part[1][t]) + part[2][t]) + part[3][t]);
+          if (kind == 0 || kind == 2) out[(static_cast<int64_t>(e) * a.lrank + j) * nf + ff] = v;
+          else out[(static_cast<int64_t>(e) * nf + ff) * a.lrank + j] = v;
+        }
+      }
+    }
   }
 }
 
@@ -1061,15 +1129,17 @@ hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
 hipError_t launch_bwd_lora_grads(const BwdLaunch& L, const uint16_t* z13, const uint16_t* gz2, float* da13,
                                  float* db13, float* da2, float* db2, hipStream_t stream) {
   const BwdArgs a = bwd_args(L);
-  const uint16_t* rq[4] = {L.lu13, z13, L.lv2, gz2};
-  float* out[4] = {da13, db13, da2, db2};
+  LoraGradOut o{{L.lu13, z13, L.lv2, gz2}, {da13, db13, da2, db2}, {}};
   const int nf[4] = {L.H, 2 * L.I, L.I, L.H};
-  for (int k = 0; k < 4; ++k) {
-    const dim3 grid(static_cast<unsigned>(L.E), static_cast<unsigned>((nf[k] + 255) / 256));
-    bwd_lora_grad_kernel<<<grid, 256, 0, stream>>>(a, k, rq[k], out[k]);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  }
-  return hipSuccess;
+  // 64 lanes x 8 features per workgroup (x 4 at rank 16)
+  const int per_wg = L.lrank <= 8 ? 512 : 256;
+  o.tiles[0] = 0;
+  for (int k = 0; k < 4; ++k) o.tiles[k + 1] = o.tiles[k] + (nf[k] + per_wg - 1) / per_wg;
+  const dim3 grid(static_cast<unsigned>(L.E), static_cast<unsigned>(o.tiles[4]));
+  if (L.lrank <= 4) bwd_lora_grad_kernel<4><<<grid, 256, 0, stream>>>(a, o);
+  else if (L.lrank <= 8) bwd_lora_grad_kernel<8><<<grid, 256, 0, stream>>>(a, o);
+  else bwd_lora_grad_kernel<16><<<grid, 256, 0, stream>>>(a, o);
+  return hipGetLastError();
 }
 
 hipError_t launch_lora_transpose(const uint16_t* src, uint16_t* dst, int E, int M, int N, hipStream_t stream) {
