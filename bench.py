@@ -139,15 +139,22 @@ def traffic_from_profile():
 
 
 # ---------------------------------------------------------------------------
-def device_layer(layer):
+def device_layer(layer, cfg=None):
+    """The layer's weights in device memory; with `cfg`, also the router
+    weight's three bf16 planes, split once here (moe_split_router) as a
+    deployment splits its constant router weight at load time."""
     import torch
     dev = torch.device("cuda:0")
     bits = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
     f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
     import mixture_experts_layer_counting_amd as m
-    return m.Weights(w_router=f32(layer["w_router"]), w13=bits(layer["w13"]), w2=bits(layer["w2"]),
-                     router_bias=f32(layer["router_bias"]), ws13=bits(layer["ws13"]), ws2=bits(layer["ws2"]),
-                     w_sgate=bits(layer["w_sgate"]))
+    w = m.Weights(w_router=f32(layer["w_router"]), w13=bits(layer["w13"]), w2=bits(layer["w2"]),
+                  router_bias=f32(layer["router_bias"]), ws13=bits(layer["ws13"]), ws2=bits(layer["ws2"]),
+                  w_sgate=bits(layer["w_sgate"]))
+    if cfg is not None:
+        d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
+        w.w_router_planes = m.split_router(d, w.w_router)
+    return w
 
 
 class Evictor:
@@ -369,6 +376,7 @@ def run_mx(cfg, layer, steps, warmup):
     del mxl
     x = torch.from_numpy(W.tokens(cfg).view(np.int16)).to(dev)
     d = m.Dims(cfg.tokens, cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
+    wm.w_router_planes = m.split_router(d, wm.w_router)  # once, as at weight load
     routes = m.alloc_routes(d, dev, logits=False)
     saved = m.alloc_saved(d, dev)
     out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=dev)
@@ -637,13 +645,13 @@ def main():
     def dev_layer(c):
         key = (c.hidden, c.inter, c.shared_inter, c.experts, c.seed)
         if key not in dev_cache:
-            dev_cache[key] = device_layer(host_layer(c))
+            dev_cache[key] = device_layer(host_layer(c), c)
         w = dev_cache[key]
         if c.zipf_s == 0.0:
             return w
         b = torch.from_numpy(np.ascontiguousarray(W.zipf_bias(c), np.float32)).to("cuda:0")
         return m.Weights(w_router=w.w_router, w13=w.w13, w2=w.w2, router_bias=b, ws13=w.ws13, ws2=w.ws2,
-                         w_sgate=w.w_sgate)
+                         w_sgate=w.w_sgate, w_router_planes=w.w_router_planes)
 
     w = dev_layer(cfg)
     evict = (lambda: None) if args.no_evict else Evictor()
@@ -729,7 +737,8 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights; no checkpoint)",
         "config": {"workload": main_s["workload"], "tokens": cfg.tokens, "hidden": cfg.hidden,
                    "experts": cfg.experts, "top_k": cfg.top_k, "inter": cfg.inter,
-                   "shared_inter": cfg.shared_inter},
+                   "shared_inter": cfg.shared_inter,
+                   "router_weight": "fp32, split once into its exact bf16 planes at weight load (moe_split_router)"},
         "timing": {"protocol": ("median of the timed calls, each bracketed by HIP events on the kernels' "
                                 "stream after a 1 GiB eviction write and a 1 GiB read" if not args.no_evict else
                                 "median of the timed calls, HIP events, no eviction writes"),

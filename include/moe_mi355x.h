@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum moe_status {
   MOE_OK = 0,
@@ -105,6 +105,11 @@ typedef struct moe_weights {
   const uint16_t* ws13;     /* [2Is][H] bf16 shared gate/up (NULL iff Is==0)  */
   const uint16_t* ws2;      /* [H][Is] bf16 shared down (NULL iff Is==0)      */
   const uint16_t* w_sgate;  /* [H] bf16 shared-expert gate (NULL iff Is==0)   */
+  const uint16_t* w_router_planes; /* [3][E][H] bf16: w_router's exact split
+                         (moe_split_router), made once and reused by every
+                         call, or NULL: each call splits w_router itself.  If
+                         given it must be moe_split_router's result for this
+                         w_router (it is what the router multiplies). */
 } moe_weights;
 
 typedef struct moe_routes {
@@ -158,6 +163,18 @@ size_t moe_workspace_bytes(const moe_dims* dims, int op);
  * the selected slots, in fp32. */
 int moe_route(const moe_dims* dims, const uint16_t* x, const moe_weights* w,
               moe_routes* routes, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The router weight's exact split (Routing bullet: the FP32 router on bf16
+ * matrix cores): planes[q][e][h], q = 0, 1, 2, with hi = bf16(w), mid =
+ * bf16(w - hi), lo = bf16(w - hi - mid), round to nearest even, so that
+ * hi + mid + lo == w exactly for every finite fp32 w.  The router is constant
+ * across calls, so a caller splits it once and passes the planes as
+ * moe_weights.w_router_planes; without them every routing call makes this
+ * split in its workspace first (one more kernel).  Uses dims' E and H only;
+ * no workspace.  Errors: MOE_E_NULL, MOE_E_SHAPE, MOE_E_ALIGN, MOE_E_ALIAS
+ * (planes overlapping w_router), MOE_E_DEVICE. */
+int moe_split_router(const moe_dims* dims, const float* w_router, uint16_t* planes,
+                     hipStream_t stream);
 
 /* Permute (page "What": local selection of each expert's routes).
  * Reads routes->topk_idx (from moe_route, or supplied by the caller, e.g.
@@ -247,6 +264,7 @@ typedef struct {
   const uint8_t* ws2_q;     /* [H][Is] */
   const uint8_t* ws2_s;     /* [H][Is/32] */
   const uint16_t* w_sgate;  /* [H] bf16 (NULL iff Is == 0) */
+  const uint16_t* w_router_planes; /* [3][E][H] bf16 or NULL, as in moe_weights */
 } moe_weights_mx;
 
 /* Forward with block-scaled FP8 expert weights (the MXFP8 item of the

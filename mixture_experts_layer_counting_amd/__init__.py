@@ -6,10 +6,8 @@ stream; nothing here computes any part of the layer, and there is no CPU
 fallback -- importing works without a GPU, but every compute call needs the
 built library and a gfx950 device.
 
-The entry points mirror include/moe_mi355x.h one to one (moe_route,
-moe_permute, moe_grouped_ffn, moe_combine, moe_forward, moe_backward,
-moe_workspace_bytes, moe_status_str, moe_abi_version, moe_last_device_error)
-and return the library's status code.  `Layer` is a convenience holder that
+The entry points mirror include/moe_mi355x.h one to one (EXPORTS lists
+them) and return the library's status code.  `Layer` is a convenience holder that
 allocates outputs and raises MoEError on a non-zero status.
 """
 from __future__ import annotations
@@ -25,7 +23,7 @@ MOE_E_WORKSPACE, MOE_E_DEVICE, MOE_E_LAUNCH, MOE_E_ALIAS = 5, 6, 7, 8
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_BACKWARD, MOE_OP_FORWARD_LORA,
  MOE_OP_BACKWARD_LORA) = range(7)
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class MoEError(RuntimeError):
@@ -41,12 +39,13 @@ _VP = ctypes.c_void_p
 
 
 class MoeWeights(ctypes.Structure):
-    _fields_ = [(n, _VP) for n in ("w_router", "router_bias", "w13", "w2", "ws13", "ws2", "w_sgate")]
+    _fields_ = [(n, _VP) for n in ("w_router", "router_bias", "w13", "w2", "ws13", "ws2", "w_sgate",
+                                   "w_router_planes")]
 
 
 class MoeWeightsMx(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("w_router", "router_bias", "w13_q", "w13_s", "w2_q", "w2_s", "ws13_q",
-                                   "ws13_s", "ws2_q", "ws2_s", "w_sgate")]
+                                   "ws13_s", "ws2_q", "ws2_s", "w_sgate", "w_router_planes")]
 
 
 class MoeLora(ctypes.Structure):
@@ -74,7 +73,8 @@ class MoeLoraGrads(ctypes.Structure):
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
            "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
-           "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc", "moe_backward_lora")
+           "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc", "moe_backward_lora",
+           "moe_split_router")
 
 _lib = None
 
@@ -117,6 +117,8 @@ def load_library():
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                  P(MoeGrads), *ws]
+    lib.moe_split_router.restype = ctypes.c_int
+    lib.moe_split_router.argtypes = [P(MoeDims), _VP, _VP, _VP]
     lib.moe_backward_lora.restype = ctypes.c_int
     lib.moe_backward_lora.argtypes = [P(MoeDims), P(MoeWeights), P(MoeLora), _VP, P(MoeRoutes), P(MoeSaved),
                                       _VP, _VP, _VP, P(MoeGrads), P(MoeLoraGrads), *ws]
@@ -181,6 +183,7 @@ class Weights:
     ws13: object = None
     ws2: object = None
     w_sgate: object = None
+    w_router_planes: object = None  # [3, E, H] bf16 from moe_split_router, or None
 
     def c(self) -> MoeWeights:
         return MoeWeights(*(_ptr(getattr(self, n)) for n, _ in MoeWeights._fields_))
@@ -201,6 +204,7 @@ class WeightsMx:
     ws2_q: object = None
     ws2_s: object = None
     w_sgate: object = None
+    w_router_planes: object = None
 
     def c(self) -> MoeWeightsMx:
         return MoeWeightsMx(*(_ptr(getattr(self, n)) for n, _ in MoeWeightsMx._fields_))
@@ -360,6 +364,20 @@ def moe_backward(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grad
                                        ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(d_out),
                                        _ptr(d_x_f32), _ptr(d_x_bf16), ctypes.byref(grads.c()), p, n,
                                        _stream(stream))
+
+
+def moe_split_router(dims, w_router, planes, stream=None) -> int:
+    return load_library().moe_split_router(ctypes.byref(dims.c()), _ptr(w_router), _ptr(planes), _stream(stream))
+
+
+def split_router(dims, w_router, device=None):
+    """The router weight's three bf16 planes [3, E, H] (moe_split_router), to
+    pass as Weights.w_router_planes."""
+    import torch
+    planes = torch.empty(3, dims.experts, dims.hidden, dtype=torch.int16,
+                         device=device if device is not None else w_router.device)
+    check(moe_split_router(dims, w_router, planes), "moe_split_router")
+    return planes
 
 
 def moe_backward_lora(dims, weights, lora, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, lora_grads, ws,

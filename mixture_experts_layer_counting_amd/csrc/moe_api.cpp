@@ -245,6 +245,7 @@ void add_weights(Args& a, const moe_dims& d, const moe_weights* w, bool router, 
   if (router) {
     a.in(w->w_router, E * H * 4);
     a.in(w->router_bias, E * 4, false);
+    a.in(w->w_router_planes, 3 * E * H * 2, false);
   }
   if (experts) {
     a.in(w->w13, E * 2 * I * H * 2);
@@ -263,11 +264,17 @@ void add_weights(Args& a, const moe_dims& d, const moe_weights* w, bool router, 
 // sg: when non-null, the top-k kernel also writes the shared-expert gate.
 int run_route(const moe_dims& d, const uint16_t* x, const moe_weights* w, moe_routes* r, void* ws,
               const Layout& L, float* sg, hipStream_t s) {
-  uint16_t* planes = at<uint16_t>(ws, L.wsplit);
+  const uint16_t* planes = w->w_router_planes;
   float* rbuf = at<float>(ws, L.rlogits);
   const uint16_t* xs = sg ? x : nullptr;
   const uint16_t* wsg = sg ? w->w_sgate : nullptr;
-  MOE_LAUNCH(moe::launch_router_split(w->w_router, planes, d.hidden, d.experts, s));
+  if (planes) {
+    MOE_LAUNCH(hipSuccess);  // the caller's split: the profiling marker only
+  } else {
+    uint16_t* own = at<uint16_t>(ws, L.wsplit);
+    MOE_LAUNCH(moe::launch_router_split(w->w_router, own, d.hidden, d.experts, s));
+    planes = own;
+  }
   if (moe::router_full(d.tokens)) {
     float* logits = r->logits ? r->logits : rbuf;
     MOE_LAUNCH(moe::launch_router_full(x, planes, w->router_bias, logits, d.tokens, d.hidden,
@@ -759,6 +766,7 @@ int moe_forward_mx(const moe_dims* dims, const moe_weights_mx* w, const uint16_t
   a.in(x, bytes_x(d));
   a.in(w->w_router, E * H * 4);
   a.in(w->router_bias, E * 4, false);
+  a.in(w->w_router_planes, 3 * E * H * 2, false);
   a.in(w->w13_q, E * 2 * I * H);
   a.in(w->w13_s, E * 2 * I * (H / 32));
   a.in(w->w2_q, E * H * I);
@@ -783,6 +791,7 @@ int moe_forward_mx(const moe_dims* dims, const moe_weights_mx* w, const uint16_t
   wr.w_router = w->w_router;
   wr.router_bias = w->router_bias;
   wr.w_sgate = w->w_sgate;
+  wr.w_router_planes = w->w_router_planes;
   const moe::MxWeights mx13{w->w13_q, w->w13_s, w->ws13_q, w->ws13_s};
   const moe::MxWeights mx2{w->w2_q, w->w2_s, w->ws2_q, w->ws2_s};
   const Layout L = make_layout(d);
@@ -848,6 +857,19 @@ int moe_backward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora
   if (lora->rank < 1 || lora->rank > moe::kLoraMaxRank) return MOE_E_SHAPE;
   return run_backward(dims, w, lora, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, lora_grads, ws,
                       ws_bytes, stream);
+}
+
+int moe_split_router(const moe_dims* dims, const float* w_router, uint16_t* planes,
+                     hipStream_t stream) {
+  MOE_TRY(check_dims(dims));
+  const size_t E = dims->experts, H = dims->hidden;
+  Args a;
+  a.in(w_router, E * H * 4);
+  a.out(planes, 3 * E * H * 2);
+  MOE_TRY(a.status());
+  MOE_TRY(check_device());
+  MOE_LAUNCH(moe::launch_router_split(w_router, planes, dims->hidden, dims->experts, stream));
+  return MOE_OK;
 }
 
 int moe_last_device_error(void* ws, hipStream_t stream) {

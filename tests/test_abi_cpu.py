@@ -284,6 +284,29 @@ def test_lora_backward_validation_fails_closed(lib):
         assert call() == m.MOE_E_DEVICE
 
 
+def test_split_router_and_caller_planes_validation(lib):
+    """moe_split_router checks dims, both buffers (presence, alignment,
+    overlap) and the device; a forward given pre-split router planes checks
+    them like any other input (alignment, overlap with an output)."""
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    E, H = d.experts, d.hidden
+    planes = f(3 * E * H * 2)
+    split = lambda dd=d, wr=w.w_router, pl=planes: m.moe_split_router(dd, wr, pl, stream=0)
+    assert split(dd=m.Dims(64, 500, 512, 10, 128, 128)) == m.MOE_E_SHAPE
+    assert split(wr=None) == m.MOE_E_NULL
+    assert split(pl=None) == m.MOE_E_NULL
+    assert split(pl=planes + 8) == m.MOE_E_ALIGN
+    assert split(pl=w.w_router + 4096) == m.MOE_E_ALIAS
+    wp = m.Weights(**{**w.__dict__, "w_router_planes": planes})
+    assert fwd(d, m.Weights(**{**wp.__dict__, "w_router_planes": planes + 2}), r, s, x, o32, o16, ws) == m.MOE_E_ALIGN
+    assert fwd(d, m.Weights(**{**wp.__dict__, "w_router_planes": o32}), r, s, x, o32, o16, ws) == m.MOE_E_ALIAS
+    import torch
+    if not torch.cuda.is_available():
+        assert split() == m.MOE_E_DEVICE
+        assert fwd(d, wp, r, s, x, o32, o16, ws) == m.MOE_E_DEVICE
+
+
 def test_noalloc_forward_refuses_what_its_array_cannot_hold(lib):
     """moe_forward_noalloc needs no workspace argument; dims whose forward
     workspace exceeds its array are refused on the host, invalid dims too."""

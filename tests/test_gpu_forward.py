@@ -15,7 +15,8 @@ import mixture_experts_layer_counting_amd as m
 import oracle as O
 import workloads as W
 from tests.gpu_util import (DEV, assert_close, check_forward, check_permutation, compare_routes, dev_bits,
-                            dev_weights, dims_of, gpu_forward, load_cfg, p8_expected_ties, say, tie_census)
+                            bf16_rne_bits, dev_weights, dims_of, gpu_forward, load_cfg, p8_expected_ties, say,
+                            tie_census)
 
 pytestmark = pytest.mark.gpu
 
@@ -271,3 +272,33 @@ def test_bad_offsets_set_device_error(tiny):
         lg = m.alloc_lora_grads(d, lo.rank, DEV)
         m.check(m.moe_backward_lora(d, w, lo, xd, r, g.saved, dout, dx, None, grads, lg, ws), "moe_backward_lora")
         assert m.moe_last_device_error(ws) == m.MOE_E_DEVICE, what
+
+
+@pytest.mark.parametrize("name", ["tiny", "moe1k", "moe8k"])
+def test_caller_router_planes(name):
+    """moe_split_router gives the exact three-part split of the fp32 router
+    weight (each part the round-to-nearest-even bf16 of what the previous
+    parts leave; their sum is the weight), and a forward given those planes
+    is bit for bit the forward that splits the weight itself, through both
+    router kernels (per-chunk sums below 4096 tokens, one pass from 4096)."""
+    cfg, layer, x = load_cfg(name)
+    w = dev_weights(layer)
+    d = dims_of(cfg)
+    say(f"case: {name}, router planes from moe_split_router")
+    planes = m.split_router(d, w.w_router)
+    torch.cuda.synchronize()
+    pl = planes.cpu().numpy().view(np.uint16)
+    f32 = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    wr = np.ascontiguousarray(layer["w_router"], np.float32)
+    hi, mid, lo = f32(pl[0]), f32(pl[1]), f32(pl[2])
+    assert np.array_equal(pl[0], bf16_rne_bits(wr))
+    assert np.array_equal(pl[1], bf16_rne_bits(wr - hi))
+    assert np.array_equal(pl[2], bf16_rne_bits((wr - hi) - mid))
+    assert np.array_equal(hi.astype(np.float64) + mid + lo, wr.astype(np.float64))
+    xd = dev_bits(x)
+    wp = m.Weights(**{**w.__dict__, "w_router_planes": planes})
+    a = gpu_forward(cfg, w, xd).host()
+    b = gpu_forward(cfg, wp, xd).host()
+    for k in ("idx", "gates", "logits", "sorted_route", "y", "s", "out32", "out16"):
+        if a[k] is not None:
+            assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k

@@ -109,3 +109,19 @@ def test_mx_forward_equals_bf16_forward_on_represented_weights(name):
     if name in ("tiny", "edge_noshared", "edge_t1"):
         say("  oracle on the represented weights, all tokens")
         check_forward(cfg, rep, x, g_mx)
+
+
+def test_mx_forward_with_caller_router_planes():
+    """moe_forward_mx given moe_split_router's planes gives the bits it gives
+    when it splits the router weight itself."""
+    cfg, layer, x = load_any("tiny")
+    mxl = MX.mx_layer(layer)
+    wm = mx_weights(layer, mxl)
+    say("case: tiny, moe_forward_mx with and without caller router planes")
+    planes = m.split_router(dims_of(cfg), wm.w_router)
+    wp = m.WeightsMx(**{**wm.__dict__, "w_router_planes": planes})
+    xd = dev_bits(x)
+    a = gpu_forward_mx(cfg, wm, xd)
+    b = gpu_forward_mx(cfg, wp, xd)
+    for k in ("idx", "gates", "logits", "y", "s", "out32", "out16"):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
