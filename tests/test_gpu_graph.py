@@ -1,8 +1,9 @@
-"""The forward under HIP graph capture: captured once, replayed several
-times with other eager work and synchronisations between the replays, every
-replay bit-identical to an eager forward (the library enqueues only kernel
-launches on the caller's stream: no memset, no allocation, no host sync).
-Also for moe_forward_noalloc, whose callers are the ones that capture."""
+"""The forward and the backward under HIP graph capture: captured once,
+replayed several times with other eager work and synchronisations between
+the replays, every replay bit-identical to an eager call (the library
+enqueues only kernel launches on the caller's stream: no memset, no
+allocation, no host sync).  Also for moe_forward_noalloc, whose callers are
+the ones that capture, and for the LoRA backward."""
 import pytest
 import torch
 
@@ -59,3 +60,78 @@ def test_forward_graph_replays_match_eager(name, noalloc):
         assert torch.equal(out16, want.out16), f"replay {i}: out_bf16"
         # eager work between replays
         gpu_forward(cfg, w, other if i % 2 else xd)
+
+
+GRADS = ("d_w_router", "d_w13", "d_w2", "d_ws13", "d_ws2", "d_w_sgate")
+
+
+@pytest.mark.parametrize("lora", [False, True])
+def test_backward_graph_replays_match_eager(lora):
+    """moe_backward (and moe_backward_lora) captured once on the tiny layer
+    and replayed four times with a different upstream gradient on every
+    other replay and eager backwards between the replays: every replay's dX
+    and weight (and adapter) gradients equal an eager backward's bits."""
+    import workloads.lora as WL
+    cfg, layer, x = load_cfg("tiny")
+    w = dev_weights(layer)
+    xd = dev_bits(x)
+    d = dims_of(cfg)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD_LORA, DEV)
+    lo = None
+    if lora:
+        ad = WL.lora_adapters(cfg)
+        lo = m.Lora(rank=ad["rank"], scale=ad["scale"], a13=dev_bits(ad["a13"]), b13=dev_bits(ad["b13"]),
+                    a2=dev_bits(ad["a2"]), b2=dev_bits(ad["b2"]))
+    routes = m.alloc_routes(d, DEV)
+    saved = m.alloc_saved(d, DEV, training=True)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV)
+    if lora:
+        m.check(m.moe_forward_lora(d, w, lo, xd, routes, saved, None, out16, ws), "moe_forward_lora")
+    else:
+        m.check(m.moe_forward(d, w, xd, routes, saved, None, out16, ws), "moe_forward")
+    dout_a = dev_bits(W.grad_out(cfg))
+    dout_b = dev_bits(W.normal_bf16(cfg.seed, W.S_COMPANION, 22, (cfg.tokens, cfg.hidden), 1.0))
+    din = dout_a.clone()
+
+    def alloc():
+        g = m.alloc_grads(d, DEV)
+        lg = m.alloc_lora_grads(d, lo.rank, DEV) if lora else None
+        return torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV), g, lg
+
+    def bwd(dout, dx, g, lg, stream):
+        if lora:
+            return m.moe_backward_lora(d, w, lo, xd, routes, saved, dout, dx, None, g, lg, ws, stream)
+        return m.moe_backward(d, w, xd, routes, saved, dout, dx, None, g, ws, stream)
+
+    def eager(dout):
+        dx, g, lg = alloc()
+        m.check(bwd(dout, dx, g, lg, None), "eager backward")
+        torch.cuda.synchronize()
+        return dx, g, lg
+
+    ref = {0: eager(dout_a), 1: eager(dout_b)}
+    dx, g, lg = alloc()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.check(bwd(din, dx, g, lg, s), "warm-up")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say(f"case: tiny, capture {'moe_backward_lora' if lora else 'moe_backward'}")
+    with torch.cuda.graph(graph, stream=s):
+        m.check(bwd(din, dx, g, lg, torch.cuda.current_stream()), "captured backward")
+    for i in range(4):
+        din.copy_(dout_b if i % 2 else dout_a)
+        dx.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        rdx, rg, rlg = ref[i % 2]
+        assert torch.equal(bits(dx), bits(rdx)), f"replay {i}: dX"
+        for k in GRADS:
+            if getattr(g, k) is not None:
+                assert torch.equal(bits(getattr(g, k)), bits(getattr(rg, k))), f"replay {i}: {k}"
+        if lora:
+            for k in ("d_a13", "d_b13", "d_a2", "d_b2"):
+                assert torch.equal(bits(getattr(lg, k)), bits(getattr(rlg, k))), f"replay {i}: {k}"
+        eager(dout_a if i % 2 else dout_b)
+    assert m.moe_last_device_error(ws) == m.MOE_OK
