@@ -347,10 +347,6 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   // load.
   __shared__ int s_tok[WGRAD ? kBwdTokLds : 1];
   const bool tok_lds = WGRAD && w.rows <= kBwdTokLds;
-  if (tok_lds) {
-    if (tid < w.rows) s_tok[tid] = static_cast<int>(bwd_token(a, w, static_cast<int64_t>(w.seg0) + tid));
-    __syncthreads();
-  }
   int64_t tok[2] = {-1, -1};
   auto wg_tokens = [&](int kb, int64_t (&t)[2]) {
 #pragma unroll
@@ -363,6 +359,39 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   };
 
   u32x4_t ra_set[NSET][NPA][2], rb_set[NSET][NPB][2];
+  // wgrad operands of K block kb: the one stored in route order (dGU or
+  // g*act planes, rows p) and the one gathered by token (dOut or x rows)
+  auto fetch_plain = [&](int set, int kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int kk = kb * kBK + kr + 16 * c;
+      const bool in = kk < w.rows;
+      const int64_t rowp = w.shared ? kk : static_cast<int64_t>(w.seg0) + kk;
+      if (MODE == kDw2) {
+        // B = g*act planes [p][n0 + tc]
+#pragma unroll
+        for (int q = 0; q < NPB; ++q)
+          rb_set[set][q][c] = in ? ld16((w.shared ? a.sgact[q] : a.gact[q]) + rowp * Ie + w.n0 + tc)
+                                 : u32x4_t{0u, 0u, 0u, 0u};
+      } else if (MODE == kDw13) {
+        // A = dGU planes [p][m0 + tc]
+#pragma unroll
+        for (int q = 0; q < NPA; ++q)
+          ra_set[set][q][c] = in ? ld16((w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie + w.m0 + tc)
+                                 : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto fetch_gathered = [&](int set, int kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool in = kb * kBK + kr + 16 * c < w.rows;
+      if (MODE == kDw2)  // A = dOut[t(p)][m0 + tc]
+        ra_set[set][0][c] = in ? ld16(a.dout + tok[c] * a.H + w.m0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
+      else if (MODE == kDw13)  // B = x[t(p)][n0 + tc]
+        rb_set[set][0][c] = in ? ld16(a.x + tok[c] * a.H + w.n0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
   auto fetch_set = [&](int set, int kb) {
     const int k0 = kb * kBK;
     if (!WGRAD) {
@@ -375,29 +404,8 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
         rb_set[set][0][c] = ld16(wbase + static_cast<int64_t>(k0 + kr + 16 * c) * wcols + w.n0 + tc);
       return;
     }
-    auto& ra = ra_set[set];
-    auto& rb = rb_set[set];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int kk = k0 + kr + 16 * c;
-      const bool in = kk < w.rows;
-      const int64_t rowp = w.shared ? kk : static_cast<int64_t>(w.seg0) + kk;
-      if (MODE == kDw2) {
-        // A = dOut[t(p)][m0 + tc], B = g*act planes [p][n0 + tc]
-        ra[0][c] = in ? ld16(a.dout + tok[c] * a.H + w.m0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int q = 0; q < NPB; ++q)
-          rb[q][c] = in ? ld16((w.shared ? a.sgact[q] : a.gact[q]) + rowp * Ie + w.n0 + tc)
-                        : u32x4_t{0u, 0u, 0u, 0u};
-      } else {
-        // A = dGU planes [p][m0 + tc], B = x[t(p)][n0 + tc]
-#pragma unroll
-        for (int q = 0; q < NPA; ++q)
-          ra[q][c] = in ? ld16((w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie + w.m0 + tc)
-                        : u32x4_t{0u, 0u, 0u, 0u};
-        rb[0][c] = in ? ld16(a.x + tok[c] * a.H + w.n0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
+    fetch_plain(set, kb);
+    fetch_gathered(set, kb);
   };
   auto stash_set = [&](int set, int stage) {
     const auto& ra = ra_set[set];
@@ -467,8 +475,19 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
     }
   } else {
     if (nkb > 0) {
-      if (WGRAD) wg_tokens(0, tok);
-      fetch_set(0, 0);
+      if constexpr (WGRAD) {
+        // the route-ordered operand of block 0 is in flight while the
+        // segment's tokens are read
+        fetch_plain(0, 0);
+        if (tok_lds) {
+          if (tid < w.rows) s_tok[tid] = static_cast<int>(bwd_token(a, w, static_cast<int64_t>(w.seg0) + tid));
+          __syncthreads();
+        }
+        wg_tokens(0, tok);
+        fetch_gathered(0, 0);
+      } else {
+        fetch_set(0, 0);
+      }
       stash_set(0, 0);
       if (WGRAD && nkb > 1) wg_tokens(1, tok);
     }
