@@ -536,6 +536,53 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True):
             "mfma_frac": flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12), "lora": lb}
 
 
+def gpu_info():
+    """Identity of the timed GPU (torch's view of the HIP device)."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", "unknown"),
+            "compute_units": p.multi_processor_count, "memory_gib": round(p.total_memory / 2**30, 1)}
+
+
+def achieved_peaks():
+    """What this machine reaches, beside the vendor peaks, with the library's
+    measurement probes (include/moe_probes.h): a 4 GiB streaming read, a
+    2 GiB streaming copy (read + write bytes) and back-to-back bf16 MFMAs on
+    independent accumulators; each the median of 5 HIP-event-timed runs
+    after a warm-up."""
+    import torch
+    import mixture_experts_layer_counting_amd as m
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n=5):
+        fn()
+        ms = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    sink = torch.zeros(64, dtype=torch.float32, device=dev)
+    a = torch.ones((1 << 30,), dtype=torch.float32, device=dev)
+    read_ms = timed(lambda: m.check(m.moe_probe_read(a, 1 << 32, sink, stream), "moe_probe_read"))
+    b = torch.empty((1 << 29,), dtype=torch.float32, device=dev)
+    copy_ms = timed(lambda: m.check(m.moe_probe_copy(b, a, 1 << 31, stream), "moe_probe_copy"))
+    del a, b
+    iters = 8192
+    mfma_ms = timed(lambda: m.check(m.moe_probe_mfma(sink, iters, stream), "moe_probe_mfma"))
+    torch.cuda.empty_cache()
+    flop = iters * 1024 * 4 * 8 * 32768
+    return {"read_gbs": (1 << 32) / (read_ms / 1e3) / 1e9, "copy_gbs": (1 << 32) / (copy_ms / 1e3) / 1e9,
+            "bf16_mfma_tflops": flop / (mfma_ms / 1e3) / 1e12,
+            "how": "moe_probe_read (4 GiB), moe_probe_copy (2 GiB, read + write bytes), moe_probe_mfma "
+                   "(32x32x16 bf16, 8 independent accumulators per wave); median of 5 after a warm-up"}
+
+
 def host_info():
     """CPU model, BLAS library and thread count of this host."""
     model = "unknown"
@@ -613,6 +660,7 @@ def main():
     ap.add_argument("--lora", type=int, default=1,
                     help="also time the forward with LoRA adapters on the routed experts (0: off)")
     ap.add_argument("--no-evict", action="store_true", help="time without the eviction writes (profiling runs)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the achieved-peak probes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -718,6 +766,13 @@ def main():
             names.append("moe1k")
         cpu = cpu_baseline({n: host_layer(W.CONFIGS[n]) for n in dict.fromkeys(names)})
 
+    peaks = None
+    if not args.no_peaks:
+        log("bench: achieved peaks (read stream, copy, bf16 MFMA)")
+        peaks = achieved_peaks()
+        log(f"bench: achieved read {peaks['read_gbs']:.0f} GB/s, copy {peaks['copy_gbs']:.0f} GB/s, "
+            f"bf16 MFMA {peaks['bf16_mfma_tflops']:.0f} TFLOP/s")
+
     up_ms = main_s["ffn_up_ms"]
     up_bytes = ffn_up_bytes(cfg, main_r["touched"])
     achieved = up_bytes / (up_ms / 1e3) / 1e9
@@ -747,7 +802,10 @@ def main():
                    "back_to_back_ms_per_step": main_s["back_to_back_ms_per_step"]},
         "roofline": {"kernel": "ffn_up", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "algorithmic_bytes": up_bytes, "avg_ms": up_ms},
+                     "algorithmic_bytes": up_bytes, "avg_ms": up_ms,
+                     "frac_of_achieved_read": achieved / peaks["read_gbs"] if peaks else None},
+        "gpu": gpu_info(),
+        "achieved_peaks": peaks,
         "layer_roofline": main_s["layer_roofline"],
         "cpu_baseline": cpu,
         "configs": configs,

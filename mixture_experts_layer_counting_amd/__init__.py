@@ -74,7 +74,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
            "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
            "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc", "moe_backward_lora",
-           "moe_split_router")
+           "moe_split_router", "moe_probe_read", "moe_probe_copy", "moe_probe_mfma")
 
 _lib = None
 
@@ -117,6 +117,11 @@ def load_library():
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                  P(MoeGrads), *ws]
+    for name, args in (("moe_probe_read", [_VP, ctypes.c_size_t, _VP, _VP]),
+                       ("moe_probe_copy", [_VP, _VP, ctypes.c_size_t, _VP]),
+                       ("moe_probe_mfma", [_VP, ctypes.c_int, _VP])):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = args
     lib.moe_split_router.restype = ctypes.c_int
     lib.moe_split_router.argtypes = [P(MoeDims), _VP, _VP, _VP]
     lib.moe_backward_lora.restype = ctypes.c_int
@@ -368,6 +373,19 @@ def moe_backward(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grad
 
 def moe_split_router(dims, w_router, planes, stream=None) -> int:
     return load_library().moe_split_router(ctypes.byref(dims.c()), _ptr(w_router), _ptr(planes), _stream(stream))
+
+
+def moe_probe_read(buf, nbytes, sink, stream=None) -> int:
+    """Measurement probe (include/moe_probes.h): stream `nbytes` of `buf`."""
+    return load_library().moe_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
+
+
+def moe_probe_copy(dst, src, nbytes, stream=None) -> int:
+    return load_library().moe_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream))
+
+
+def moe_probe_mfma(sink, iters, stream=None) -> int:
+    return load_library().moe_probe_mfma(_ptr(sink), iters, _stream(stream))
 
 
 def split_router(dims, w_router, device=None):

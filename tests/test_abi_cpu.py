@@ -1,11 +1,12 @@
 """Host-side checks of the C ABI (no GPU needed, nothing is launched).
 
-The library must load, export every entry point include/moe_mi355x.h
-declares, size its workspace, and reject bad arguments with the documented
+The library must load, export every entry point the headers in include/
+declare (the layer's boundary and the measurement probes), size its workspace, and reject bad arguments with the documented
 status before anything is enqueued (fail closed).  Validation runs before
 the device check, so these calls return without touching a GPU; fake but
 aligned addresses are fine because nothing dereferences them.
 """
+import glob
 import os
 import re
 
@@ -25,22 +26,27 @@ def lib():
     return m.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^[a-z][\w ]*?\**\s*\**(moe_\w+)\(", text, flags=re.M)))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        names |= set(re.findall(r"^[a-z][\w ]*?\**\s*\**(moe_\w+)\(", open(h).read(), flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for n in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward",
               "moe_workspace_bytes", "moe_status_str", "moe_abi_version", "moe_last_device_error"):
         assert n in names, n
 
 
 def test_library_exports_every_declared_symbol(lib):
-    for n in declared_functions():
-        assert hasattr(lib, n), f"{n} declared in the header but not exported"
-    assert set(declared_functions()) <= set(m.EXPORTS) | set(declared_functions())
+    declared = declared_functions()
+    assert "moe_probe_read" in declared and "moe_backward_lora" in declared
+    for n in declared:
+        assert hasattr(lib, n), f"{n} declared in a header but not exported"
+    # the binding lists every declared entry point, and nothing else
+    assert set(declared) == set(m.EXPORTS), set(declared) ^ set(m.EXPORTS)
     assert m.moe_abi_version() == m.ABI_VERSION
 
 
@@ -321,3 +327,20 @@ def test_noalloc_forward_refuses_what_its_array_cannot_hold(lib):
     if not torch.cuda.is_available():
         # dims it can hold: the device's array is looked up first, so without a GPU it stops there
         assert m.moe_forward_noalloc(d, w, None, r, s, o32, o16, stream=0) == m.MOE_E_DEVICE
+
+
+def test_probe_validation(lib):
+    """The measurement probes check their arguments before launching."""
+    f = Fake()
+    buf, sink = f(1 << 20), f(256)
+    assert m.moe_probe_read(None, 1 << 20, sink, stream=0) == m.MOE_E_NULL
+    assert m.moe_probe_read(buf, 0, sink, stream=0) == m.MOE_E_SHAPE
+    assert m.moe_probe_read(buf, 1000, sink, stream=0) == m.MOE_E_SHAPE
+    assert m.moe_probe_read(buf + 8, 1 << 20, sink, stream=0) == m.MOE_E_ALIGN
+    assert m.moe_probe_copy(buf + 4096, buf, 1 << 16, stream=0) == m.MOE_E_ALIAS
+    assert m.moe_probe_mfma(sink, 0, stream=0) == m.MOE_E_SHAPE
+    assert m.moe_probe_mfma(None, 10, stream=0) == m.MOE_E_NULL
+    import torch
+    if not torch.cuda.is_available():
+        assert m.moe_probe_read(buf, 1 << 20, sink, stream=0) == m.MOE_E_DEVICE
+        assert m.moe_probe_mfma(sink, 10, stream=0) == m.MOE_E_DEVICE
