@@ -108,6 +108,7 @@ def test_tiny_backward_full():
     dict(tokens=24, hidden=16384, experts=64, top_k=2, inter=128, shared_inter=128),
     dict(tokens=40, hidden=256, experts=64, top_k=4, inter=4096, shared_inter=0),
     dict(tokens=1, hidden=512, experts=512, top_k=10, inter=512, shared_inter=512),
+    dict(tokens=130, hidden=256, experts=1024, top_k=16, inter=128, shared_inter=128),
 ])
 def test_backward_shape_edge_cases(shape):
     cfg = W.MoEConfig(name="edge", **shape)
