@@ -497,6 +497,10 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True):
     fb = timed(lambda: (fwd(), bwd()), fb_calls)
     bo = timed(bwd, steps)
     assert m.moe_last_device_error(ws) == m.MOE_OK
+    side = m.SideStreams(dev)
+    bs = timed(lambda: m.check(m.moe_backward_side(d, w, x, routes, saved, dout, dx32, None, grads, ws, side,
+                                                   stream), "moe_backward_side"), steps)
+    assert m.moe_last_device_error(ws) == m.MOE_OK
     lb = None
     if lora:
         import workloads.lora as WL
@@ -533,7 +537,10 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True):
             "fwd_bwd_calls": fb["calls"], "fwd_bwd_tokens_per_s": T / (fb["median_ms"] / 1e3),
             "bytes": byts, "flop": flop, "t_roof_ms": t_roof * 1e3, "roofline_frac": t_roof / (ms / 1e3),
             "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9),
-            "mfma_frac": flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12), "lora": lb}
+            "mfma_frac": flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12), "lora": lb,
+            "side_streams": {"what": "moe_backward_side: dW13 and dW2 on two caller-owned streams beside dx",
+                             "ms": bs["median_ms"], "p10_ms": bs["p10_ms"], "p90_ms": bs["p90_ms"],
+                             "calls": bs["calls"], "tokens_per_s": T / (bs["median_ms"] / 1e3)}}
 
 
 def gpu_info():
@@ -755,7 +762,8 @@ def main():
         cb = W.CONFIGS[args.backward]
         log(f"bench: backward {cb.name}")
         backward = run_backward(cb, dev_layer(cb), args.steps, 1, evict, lora=bool(args.lora))
-        log(f"bench: backward {backward['ms']:.3f} ms, forward + backward {backward['fwd_bwd_ms']:.3f} ms"
+        log(f"bench: backward {backward['ms']:.3f} ms (side streams {backward['side_streams']['ms']:.3f} ms), "
+            f"forward + backward {backward['fwd_bwd_ms']:.3f} ms"
             + (f", LoRA backward {backward['lora']['ms']:.3f} ms" if backward["lora"] else ""))
 
     cpu = None

@@ -242,6 +242,31 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                  float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws,
                  size_t ws_bytes, hipStream_t stream);
 
+/* Streams and events of the caller that let moe_backward_side run its
+ * independent weight-gradient GEMMs beside the input-gradient GEMM.  The
+ * caller creates and owns all of them (streams of default priority, events
+ * preferably with hipEventDisableTiming); the library only records and
+ * waits on them, so concurrent calls must not share them. */
+typedef struct {
+  hipStream_t side[2]; /* two streams other than the call's and each other */
+  hipEvent_t fork;     /* recorded on the call's stream, waited for by both */
+  hipEvent_t join[2];  /* recorded on side[i], waited for by the call's stream */
+} moe_side_streams;
+
+/* moe_backward with its three independent grouped GEMMs on three streams:
+ * dW13 on side[0] and dW2 on side[1], from the point where the activation
+ * gradients exist (`fork`), dx and the kernels after it on `stream`, which
+ * then waits for both side streams (`join`), so work enqueued on `stream`
+ * after this call sees every output.  The store-bound weight gradients then
+ * share the CUs with the load-bound dx GEMM.  Results are bit for bit those
+ * of moe_backward (the same kernels on the same data).  Errors as
+ * moe_backward, plus MOE_E_NULL for a missing stream or event and
+ * MOE_E_ALIAS for streams or events that are not distinct. */
+int moe_backward_side(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                      const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
+                      float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws, size_t ws_bytes,
+                      hipStream_t stream, const moe_side_streams* side);
+
 /* Block-scaled FP8 expert weights (OCP MX format, the E4M3 element type).
  * Every 32 consecutive elements of a weight row along its contraction axis
  * (H for W13 / Ws13, I for W2 / Ws2) share one E8M0 scale code s, value

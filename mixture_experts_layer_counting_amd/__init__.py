@@ -66,6 +66,10 @@ class MoeGrads(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("d_w_router", "d_w13", "d_w2", "d_ws13", "d_ws2", "d_w_sgate")]
 
 
+class MoeSideStreams(ctypes.Structure):
+    _fields_ = [("side", _VP * 2), ("fork", _VP), ("join", _VP * 2)]
+
+
 class MoeLoraGrads(ctypes.Structure):
     _fields_ = [(n, _VP) for n in ("d_a13", "d_b13", "d_a2", "d_b2")]
 
@@ -74,7 +78,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
            "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
            "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc", "moe_backward_lora",
-           "moe_split_router", "moe_probe_read", "moe_probe_copy", "moe_probe_mfma")
+           "moe_split_router", "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_backward_side")
 
 _lib = None
 
@@ -122,6 +126,9 @@ def load_library():
                        ("moe_probe_mfma", [_VP, ctypes.c_int, _VP])):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = args
+    lib.moe_backward_side.restype = ctypes.c_int
+    lib.moe_backward_side.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
+                                      P(MoeGrads), *ws, P(MoeSideStreams)]
     lib.moe_split_router.restype = ctypes.c_int
     lib.moe_split_router.argtypes = [P(MoeDims), _VP, _VP, _VP]
     lib.moe_backward_lora.restype = ctypes.c_int
@@ -369,6 +376,43 @@ def moe_backward(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grad
                                        ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(d_out),
                                        _ptr(d_x_f32), _ptr(d_x_bf16), ctypes.byref(grads.c()), p, n,
                                        _stream(stream))
+
+
+class SideStreams:
+    """Two side streams (torch, default priority) and three HIP events (no
+    timing) owned by the caller, for moe_backward_side."""
+
+    def __init__(self, device=None):
+        import torch
+        self.streams = [torch.cuda.Stream(device=device) for _ in range(2)]
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_VP), ctypes.c_uint]
+        self._hip.hipEventCreateWithFlags.restype = ctypes.c_int
+        self._hip.hipEventDestroy.argtypes = [_VP]
+        self.events = []
+        for _ in range(3):
+            e = _VP()
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(e), 0x2) != 0:  # hipEventDisableTiming
+                raise MoEError("hipEventCreateWithFlags failed")
+            self.events.append(e)
+
+    def c(self) -> MoeSideStreams:
+        s = [_VP(st.cuda_stream) for st in self.streams]
+        return MoeSideStreams((_VP * 2)(s[0], s[1]), self.events[0], (_VP * 2)(self.events[1], self.events[2]))
+
+    def __del__(self):
+        for e in getattr(self, "events", []):
+            self._hip.hipEventDestroy(e)
+
+
+def moe_backward_side(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, ws, side,
+                      stream=None) -> int:
+    p, n = _ws(ws)
+    sc = ctypes.byref(side.c()) if side is not None else None
+    return load_library().moe_backward_side(ctypes.byref(dims.c()), ctypes.byref(weights.c()), _ptr(x),
+                                            ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(d_out),
+                                            _ptr(d_x_f32), _ptr(d_x_bf16), ctypes.byref(grads.c()), p, n,
+                                            _stream(stream), sc)
 
 
 def moe_split_router(dims, w_router, planes, stream=None) -> int:

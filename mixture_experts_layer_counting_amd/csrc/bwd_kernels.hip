@@ -1119,9 +1119,8 @@ hipError_t launch_bwd_dact(const BwdLaunch& L, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
+hipError_t launch_bwd_dx(const BwdLaunch& L, hipStream_t stream) {
   BwdArgs a = bwd_args(L);
-  const int Imax = L.I > L.Is ? L.I : L.Is;
   const unsigned dx_grid = rounds(static_cast<int64_t>(L.max_tiles_bwd) * (L.H / kBT));
   // the unrolled dx instantiations cover expert and shared sizes of 512
   const bool unrolled = L.I == 512 && (L.Is == 0 || L.Is == 512);
@@ -1137,12 +1136,29 @@ hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
   } else {
     bwd_gemm_kernel<kDx><<<dx_grid, 256, 0, stream>>>(a);
   }
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dw2(const BwdLaunch& L, hipStream_t stream) {
+  const BwdArgs a = bwd_args(L);
+  const int Imax = L.I > L.Is ? L.I : L.Is;
   const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
   bwd_gemm_kernel<kDw2><<<rounds(groups * (L.H / kBT) * (Imax / kBT)), 256, 0, stream>>>(a);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dw13(const BwdLaunch& L, hipStream_t stream) {
+  const BwdArgs a = bwd_args(L);
+  const int Imax = L.I > L.Is ? L.I : L.Is;
+  const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
   bwd_gemm_kernel<kDw13><<<rounds(groups * (2 * Imax / kBT) * (L.H / kBT)), 256, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream) {
+  if (launch_bwd_dx(L, stream) != hipSuccess) return hipErrorLaunchFailure;
+  if (launch_bwd_dw2(L, stream) != hipSuccess) return hipErrorLaunchFailure;
+  return launch_bwd_dw13(L, stream);
 }
 
 hipError_t launch_bwd_lora_grads(const BwdLaunch& L, const uint16_t* z13, const uint16_t* gz2, float* da13,

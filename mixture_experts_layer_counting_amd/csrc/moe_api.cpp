@@ -404,11 +404,13 @@ void add_saved(Args& a, const moe_dims& d, const moe_saved* sv, bool out) {
   }
 }
 
-// moe_backward (lora null) and moe_backward_lora (rank already checked).
+// moe_backward (lora null), moe_backward_lora (rank already checked) and
+// moe_backward_side (ss: the caller's side streams and events; null: one
+// stream).
 int run_backward(const moe_dims* dims, const moe_weights* w, const moe_lora* lora, const uint16_t* x,
                  const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
                  float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, moe_lora_grads* lg, void* ws,
-                 size_t ws_bytes, hipStream_t stream) {
+                 size_t ws_bytes, hipStream_t stream, const moe_side_streams* ss = nullptr) {
   MOE_TRY(check_dims(dims));
   if (dims->tokens == 0) return MOE_OK;
   if (!w || !routes || !saved || !grads) return MOE_E_NULL;
@@ -530,7 +532,20 @@ int run_backward(const moe_dims* dims, const moe_weights* w, const moe_lora* lor
     MOE_LAUNCH(shrink(x, nullptr, lora->a13, L.lora_z13, d.hidden));
     MOE_LAUNCH(shrink(b.gact[0], b.gact[1], lora->a2, L.lora_z2, d.inter));
   }
-  MOE_LAUNCH(moe::launch_bwd_gemms(b, s));
+  if (ss) {
+    // the weight gradients on the side streams, from the point where dGU and
+    // g*act exist; dx and everything after it stay on `stream`
+    if (hipEventRecord(ss->fork, s) != hipSuccess) return MOE_E_LAUNCH;
+    for (int i = 0; i < 2; ++i)
+      if (hipStreamWaitEvent(ss->side[i], ss->fork, 0) != hipSuccess) return MOE_E_LAUNCH;
+    MOE_LAUNCH(moe::launch_bwd_dw13(b, ss->side[0]));
+    MOE_LAUNCH(moe::launch_bwd_dw2(b, ss->side[1]));
+    for (int i = 0; i < 2; ++i)
+      if (hipEventRecord(ss->join[i], ss->side[i]) != hipSuccess) return MOE_E_LAUNCH;
+    MOE_LAUNCH(moe::launch_bwd_dx(b, s));
+  } else {
+    MOE_LAUNCH(moe::launch_bwd_gemms(b, s));
+  }
   if (lora)
     MOE_LAUNCH(moe::launch_bwd_lora_grads(b, at<uint16_t>(ws, L.lora_z13), at<uint16_t>(ws, L.lora_z2),
                                           lg->d_a13, lg->d_b13, lg->d_a2, lg->d_b2, s));
@@ -544,6 +559,9 @@ int run_backward(const moe_dims* dims, const moe_weights* w, const moe_lora* lor
                                     sh ? at<float>(ws, L.dx_shared) : nullptr, at<float>(ws, L.dz),
                                     sh ? w->w_sgate : nullptr, w->w_router, d_x_f32, d_x_bf16,
                                     d.tokens, d.hidden, d.experts, d.top_k, s));
+  if (ss)
+    for (int i = 0; i < 2; ++i)
+      if (hipStreamWaitEvent(s, ss->join[i], 0) != hipSuccess) return MOE_E_LAUNCH;
   return MOE_OK;
 }
 
@@ -845,6 +863,22 @@ int moe_backward(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
                  hipStream_t stream) {
   return run_backward(dims, w, nullptr, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, nullptr, ws,
                       ws_bytes, stream);
+}
+
+int moe_backward_side(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                      const moe_routes* routes, const moe_saved* saved, const uint16_t* d_out,
+                      float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws, size_t ws_bytes,
+                      hipStream_t stream, const moe_side_streams* side) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!side || !side->side[0] || !side->side[1] || !side->fork || !side->join[0] || !side->join[1])
+    return MOE_E_NULL;
+  if (side->side[0] == side->side[1] || side->side[0] == stream || side->side[1] == stream)
+    return MOE_E_ALIAS;
+  if (side->fork == side->join[0] || side->fork == side->join[1] || side->join[0] == side->join[1])
+    return MOE_E_ALIAS;
+  return run_backward(dims, w, nullptr, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, nullptr, ws,
+                      ws_bytes, stream, side);
 }
 
 int moe_backward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,

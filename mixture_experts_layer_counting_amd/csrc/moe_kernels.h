@@ -133,6 +133,10 @@ hipError_t launch_bwd_gate(const double* dgp, const double* dsp, const float* ga
                            float* dl, float* dz, int64_t T, int K, int I, int Is,
                            hipStream_t stream);
 hipError_t launch_bwd_gemms(const BwdLaunch& L, hipStream_t stream);
+// its three GEMMs one by one (independent of each other): dx, dW2, dW13
+hipError_t launch_bwd_dx(const BwdLaunch& L, hipStream_t stream);
+hipError_t launch_bwd_dw2(const BwdLaunch& L, hipStream_t stream);
+hipError_t launch_bwd_dw13(const BwdLaunch& L, hipStream_t stream);
 // With adapters: the shrinks of v2 (before launch_bwd_dact) and of u13, z13
 // = A13 x and gz2 = A2 (g act) (after it) by launch_lora_shrink, then
 // launch_bwd_lora_grads writes dA13 [E][rank][H], dB13 [E][2I][rank], dA2

@@ -344,3 +344,34 @@ def test_probe_validation(lib):
     if not torch.cuda.is_available():
         assert m.moe_probe_read(buf, 1 << 20, sink, stream=0) == m.MOE_E_DEVICE
         assert m.moe_probe_mfma(sink, 10, stream=0) == m.MOE_E_DEVICE
+
+
+def test_backward_side_validation(lib):
+    """moe_backward_side checks everything moe_backward checks, plus its side
+    streams and events (present, distinct from each other and from the
+    call's stream), before anything is enqueued."""
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, g, dout, dx32, dx16, wsb, wsf = backward_args(d)
+
+    class Side:
+        def __init__(self, side=(0x1000, 0x2000), fork=0x3000, join=(0x4000, 0x5000)):
+            self.v = (side, fork, join)
+
+        def c(self):
+            (a, b), f, (j0, j1) = self.v
+            return m.MoeSideStreams((m._VP * 2)(a, b), f, (m._VP * 2)(j0, j1))
+
+    call = lambda side, stream=0x9000, dd=d: m.moe_backward_side(dd, w, x, r, s, dout, dx32, dx16, g, wsb, side,
+                                                                 stream=stream)
+    assert call(None) == m.MOE_E_NULL
+    assert call(Side(side=(0x1000, 0))) == m.MOE_E_NULL
+    assert call(Side(join=(0x4000, 0))) == m.MOE_E_NULL
+    assert call(Side(side=(0x1000, 0x1000))) == m.MOE_E_ALIAS
+    assert call(Side(), stream=0x2000) == m.MOE_E_ALIAS
+    assert call(Side(fork=0x4000)) == m.MOE_E_ALIAS
+    assert call(Side(), dd=m.Dims(64, 500, 512, 10, 128, 128)) == m.MOE_E_SHAPE
+    assert call(Side(), dd=m.Dims(0, 512, 512, 10, 128, 128)) == m.MOE_OK
+    assert m.moe_backward_side(d, w, x, r, s, dout, dx32, dx16, g, wsf, Side(), stream=0x9000) == m.MOE_E_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert call(Side()) == m.MOE_E_DEVICE

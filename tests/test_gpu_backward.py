@@ -241,3 +241,29 @@ def test_bwd4k_dx_probe_alone_vs_in_batches(layer4k):
             g = gpu_forward(cfg, w, xb, training=True, ws=ws)
             dx = gpu_backward(cfg, w, xb, g, db, ws=ws)[0]
             assert torch.equal(bits(dx[start:start + n]), bits(ref)), f"batch {B} {where}: dX differs"
+
+
+@pytest.mark.parametrize("name", ["tiny", "bwd4k"])
+def test_backward_side_streams_equal_moe_backward(name):
+    """moe_backward_side (weight gradients on two caller-owned side streams)
+    gives moe_backward's bits for every gradient, twice in a row on the same
+    streams and events."""
+    cfg, layer, x = load_cfg(name)
+    w = dev_weights(layer)
+    xd = dev_bits(x)
+    dout = dev_bits(W.grad_out(cfg))
+    say(f"case: {name}, moe_backward_side vs moe_backward")
+    g = gpu_forward(cfg, w, xd, training=True)
+    ref = gpu_backward(cfg, w, xd, g, dout)
+    d = dims_of(cfg)
+    side = m.SideStreams(DEV)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD, DEV)
+    for rep in range(2):
+        grads = m.alloc_grads(d, DEV)
+        dx32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+        dx16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV)
+        m.check(m.moe_backward_side(d, w, xd, g.routes, g.saved, dout, dx32, dx16, grads, ws, side),
+                "moe_backward_side")
+        torch.cuda.synchronize()
+        assert m.moe_last_device_error(ws) == m.MOE_OK
+        assert_same_backward((dx32, dx16, grads), ref, f"{name}, side streams, call {rep}")

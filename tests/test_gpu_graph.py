@@ -135,3 +135,54 @@ def test_backward_graph_replays_match_eager(lora):
                 assert torch.equal(bits(getattr(lg, k)), bits(getattr(rlg, k))), f"replay {i}: {k}"
         eager(dout_a if i % 2 else dout_b)
     assert m.moe_last_device_error(ws) == m.MOE_OK
+
+
+def test_backward_side_streams_graph_replays_match_eager():
+    """moe_backward_side captured on a stream: its fork and join events pull
+    the two side streams into the capture; four replays with alternating
+    upstream gradients equal eager moe_backward bit for bit."""
+    cfg, layer, x = load_cfg("tiny")
+    w = dev_weights(layer)
+    xd = dev_bits(x)
+    d = dims_of(cfg)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD, DEV)
+    routes = m.alloc_routes(d, DEV)
+    saved = m.alloc_saved(d, DEV, training=True)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV)
+    m.check(m.moe_forward(d, w, xd, routes, saved, None, out16, ws), "moe_forward")
+    dout_a = dev_bits(W.grad_out(cfg))
+    dout_b = dev_bits(W.normal_bf16(cfg.seed, W.S_COMPANION, 23, (cfg.tokens, cfg.hidden), 1.0))
+    din = dout_a.clone()
+
+    def eager(dout):
+        g = m.alloc_grads(d, DEV)
+        dx = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+        m.check(m.moe_backward(d, w, xd, routes, saved, dout, dx, None, g, ws), "eager backward")
+        torch.cuda.synchronize()
+        return dx, g
+
+    ref = {0: eager(dout_a), 1: eager(dout_b)}
+    side = m.SideStreams(DEV)
+    g = m.alloc_grads(d, DEV)
+    dx = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.check(m.moe_backward_side(d, w, xd, routes, saved, din, dx, None, g, ws, side, s), "warm-up")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("case: tiny, capture moe_backward_side")
+    with torch.cuda.graph(graph, stream=s):
+        m.check(m.moe_backward_side(d, w, xd, routes, saved, din, dx, None, g, ws, side,
+                                    torch.cuda.current_stream()), "captured backward")
+    for i in range(4):
+        din.copy_(dout_b if i % 2 else dout_a)
+        dx.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        rdx, rg = ref[i % 2]
+        assert torch.equal(bits(dx), bits(rdx)), f"replay {i}: dX"
+        for k in GRADS:
+            if getattr(g, k) is not None:
+                assert torch.equal(bits(getattr(g, k)), bits(getattr(rg, k))), f"replay {i}: {k}"
+        eager(dout_a if i % 2 else dout_b)
