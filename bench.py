@@ -255,11 +255,30 @@ def run_config(cfg, w, steps, warmup, hip, evict, breakdown=True):
         per_kernel = {n: float(np.median([hip.elapsed_ms(mk[i][k], mk[i][k + 1]) for i in range(3)]))
                       for k, n in enumerate(names)}
     assert m.moe_last_device_error(ws) == m.MOE_OK
+    # the same forwards with the shared expert on a side stream (moe_forward_side)
+    side = m.SideStreams(torch.device("cuda:0"))
+
+    def fwd_side():
+        m.check(m.moe_forward_side(d, w, x, routes, saved, None, out16, ws, side, stream), "moe_forward_side")
+
+    for _ in range(warmup):
+        fwd_side()
+    torch.cuda.synchronize()
+    side_ms = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        evict()
+        e0.record(stream)
+        fwd_side()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        side_ms.append(e0.elapsed_time(e1))
+    assert m.moe_last_device_error(ws) == m.MOE_OK
     touched = int((np.diff(routes.expert_offsets.cpu().numpy()) > 0).sum())
     load = np.diff(routes.expert_offsets.cpu().numpy())
     return dict(call=stats(call_ms), up=stats(up_ms), wall_ms=wall / steps * 1e3, b2b_ms=b2b,
                 per_kernel=per_kernel, touched=touched, max_load=int(load.max()),
-                empty=int((load == 0).sum()))
+                empty=int((load == 0).sum()), side=stats(side_ms))
 
 
 def summarize(cfg, r):
@@ -287,6 +306,11 @@ def summarize(cfg, r):
             mfma_frac=flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
             mfma_frac_cap=t_mfma / t_roof),
     )
+    sm = r["side"]["median_ms"]
+    out["side_streams"] = dict(what="moe_forward_side: the shared expert's GEMMs on a side stream beside "
+                                    "the routing and the routed GEMMs (same protocol, bit-identical output)",
+                               ms_per_step=sm, p10_ms=r["side"]["p10_ms"], p90_ms=r["side"]["p90_ms"],
+                               tokens_per_s=cfg.tokens / (sm / 1e3), layer_roofline_frac=t_roof / (sm / 1e3))
     if r["per_kernel"]:
         out["ffn_up_gbs"] = ffn_up_bytes(cfg, r["touched"]) / (r["up"]["median_ms"] / 1e3) / 1e9
         out["ffn_down_gbs"] = ffn_down_bytes(cfg, r["touched"]) / (r["per_kernel"]["ffn_down"] / 1e3) / 1e9
@@ -724,7 +748,7 @@ def main():
     main_r = run_config(cfg, w, args.steps, args.warmup, hip, evict)
     main_s = summarize(cfg, main_r)
     log(f"bench: {cfg.name} median {main_s['ms_per_step']:.3f} ms (p10 {main_s['p10_ms']:.3f}, "
-        f"p90 {main_s['p90_ms']:.3f}), back to back {main_s['back_to_back_ms_per_step']:.3f} ms, "
+        f"p90 {main_s['p90_ms']:.3f}), back to back {main_s['back_to_back_ms_per_step']:.3f} ms, side streams {main_s['side_streams']['ms_per_step']:.3f} ms, "
         f"kernels {main_s['kernel_ms_marked']}")
 
     configs = {cfg.name: main_s}
@@ -736,7 +760,8 @@ def main():
         if name == "tiny":
             # the tiny layer's weights fit in the MALL: its warm number beside the flushed one
             configs[c2.name]["warm_ms_per_step"] = configs[c2.name]["back_to_back_ms_per_step"]
-        log(f"bench: {c2.name} median {configs[c2.name]['ms_per_step']:.3f} ms, "
+        log(f"bench: {c2.name} median {configs[c2.name]['ms_per_step']:.3f} ms "
+            f"(side streams {configs[c2.name]['side_streams']['ms_per_step']:.3f}), "
             f"roofline {configs[c2.name]['layer_roofline']['frac']:.3f}")
 
     ep_share = None

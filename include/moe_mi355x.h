@@ -267,6 +267,18 @@ int moe_backward_side(const moe_dims* dims, const moe_weights* w, const uint16_t
                       float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws, size_t ws_bytes,
                       hipStream_t stream, const moe_side_streams* side);
 
+/* moe_forward with the shared expert on side[0]: its two GEMMs, which do
+ * not depend on the routing, run from the call's start (`fork`) on lists of
+ * their own, beside the router, top-k, permutation and routed GEMMs on
+ * `stream`; `stream` waits for them (`join[0]`) before the combine.  The
+ * routed GEMMs' lists then hold routed tiles only.  Results are bit for bit
+ * those of moe_forward.  side[1] and join[1] are not used (validated as in
+ * moe_backward_side).  Without a shared expert it is moe_forward.  Errors as
+ * moe_forward and moe_backward_side. */
+int moe_forward_side(const moe_dims* dims, const moe_weights* w, const uint16_t* x,
+                     moe_routes* routes, moe_saved* saved, float* out_f32, uint16_t* out_bf16,
+                     void* ws, size_t ws_bytes, hipStream_t stream, const moe_side_streams* side);
+
 /* Block-scaled FP8 expert weights (OCP MX format, the E4M3 element type).
  * Every 32 consecutive elements of a weight row along its contraction axis
  * (H for W13 / Ws13, I for W2 / Ws2) share one E8M0 scale code s, value

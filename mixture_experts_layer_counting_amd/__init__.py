@@ -78,7 +78,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward", "moe_last_device_error",
            "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
            "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc", "moe_backward_lora",
-           "moe_split_router", "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_backward_side")
+           "moe_split_router", "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_backward_side",
+           "moe_forward_side")
 
 _lib = None
 
@@ -126,6 +127,9 @@ def load_library():
                        ("moe_probe_mfma", [_VP, ctypes.c_int, _VP])):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = args
+    lib.moe_forward_side.restype = ctypes.c_int
+    lib.moe_forward_side.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, *ws,
+                                     P(MoeSideStreams)]
     lib.moe_backward_side.restype = ctypes.c_int
     lib.moe_backward_side.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                       P(MoeGrads), *ws, P(MoeSideStreams)]
@@ -403,6 +407,14 @@ class SideStreams:
     def __del__(self):
         for e in getattr(self, "events", []):
             self._hip.hipEventDestroy(e)
+
+
+def moe_forward_side(dims, weights, x, routes, saved, out_f32, out_bf16, ws, side, stream=None) -> int:
+    p, n = _ws(ws)
+    sc = ctypes.byref(side.c()) if side is not None else None
+    return load_library().moe_forward_side(ctypes.byref(dims.c()), ctypes.byref(weights.c()), _ptr(x),
+                                           ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(out_f32),
+                                           _ptr(out_bf16), p, n, _stream(stream), sc)
 
 
 def moe_backward_side(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, ws, side,

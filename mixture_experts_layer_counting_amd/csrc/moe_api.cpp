@@ -31,6 +31,9 @@ struct Layout {
   size_t tiles = 0;       // [2*max_tiles] i32
   size_t tiles_up = 0;    // [2*max_tiles_up] i32: the up projection's list when its rows differ
   size_t meta = 0;        // [64] i32
+  // the shared expert's own work lists (moe_forward_side): 64-row tiles,
+  // up_rows-row tiles when those differ, and their lengths (meta_sh[0], [2])
+  size_t tiles_sh = 0, tiles_sh_up = 0, meta_sh = 0;
   size_t act_hi = 0, act_lo = 0;    // [R][I] bf16
   size_t sact_hi = 0, sact_lo = 0;  // [T][Is] bf16
   size_t fwd_end = 0;
@@ -85,6 +88,9 @@ Layout make_layout(const moe_dims& d) {
   L.tiles = take(static_cast<size_t>(L.max_tiles) * 2 * 4);
   L.tiles_up = take(L.up_rows != moe::kRowsPerTile ? static_cast<size_t>(L.max_tiles_up) * 2 * 4 : 0);
   L.meta = take(64 * 4);
+  L.tiles_sh = take(static_cast<size_t>((T + moe::kRowsPerTile - 1) / moe::kRowsPerTile) * 2 * 4);
+  L.tiles_sh_up = take(L.up_rows != moe::kRowsPerTile ? static_cast<size_t>((T + L.up_rows - 1) / L.up_rows) * 2 * 4 : 0);
+  L.meta_sh = take(64 * 4);
   L.act_hi = take(static_cast<size_t>(R) * I * 2);
   L.act_lo = take(static_cast<size_t>(R) * I * 2);
   L.sact_hi = take(static_cast<size_t>(T) * Is * 2);
@@ -295,13 +301,17 @@ int32_t* tiles_up_of(void* ws, const Layout& L) {
   return L.up_rows != moe::kRowsPerTile ? at<int32_t>(ws, L.tiles_up) : nullptr;
 }
 
-int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hipStream_t s) {
+// with_shared: the work lists also take the shared expert's tiles (false
+// when it runs on a side stream with lists of its own)
+int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hipStream_t s,
+                bool with_shared = true) {
+  const int has_shared = with_shared && d.shared_inter > 0;
   if (moe::sort_small_fits(d.tokens, d.experts)) {
     MOE_LAUNCH(moe::launch_route_sort_small(r->topk_idx, r->expert_offsets, r->route_pos,
                                             r->sorted_route, at<int32_t>(ws, L.tiles),
                                             tiles_up_of(ws, L), L.up_rows, at<int32_t>(ws, L.meta),
                                             at<int>(ws, L.err), d.tokens, d.experts, d.top_k,
-                                            d.shared_inter > 0, s));
+                                            has_shared, s));
     return MOE_OK;
   }
   MOE_LAUNCH(moe::launch_route_hist(r->topk_idx, at<int32_t>(ws, L.hist), r->route_pos, d.tokens,
@@ -309,7 +319,7 @@ int run_permute(const moe_dims& d, moe_routes* r, void* ws, const Layout& L, hip
   MOE_LAUNCH(moe::launch_route_scan(at<int32_t>(ws, L.hist), at<int32_t>(ws, L.block_base),
                                     r->expert_offsets, at<int32_t>(ws, L.tiles), tiles_up_of(ws, L),
                                     L.up_rows, at<int32_t>(ws, L.meta), L.nblocks, d.experts,
-                                    d.tokens, d.shared_inter > 0, at<int>(ws, L.err), s));
+                                    d.tokens, has_shared, at<int>(ws, L.err), s));
   MOE_LAUNCH(moe::launch_route_scatter(r->topk_idx, at<int32_t>(ws, L.block_base),
                                        r->expert_offsets, r->route_pos, r->sorted_route, d.tokens,
                                        d.experts, d.top_k, s));
@@ -365,6 +375,33 @@ int run_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const mo
                                   at<int32_t>(ws, L.tiles), at<int32_t>(ws, L.meta), sv->y,
                                   has_shared ? sv->shared_y : nullptr, d.tokens, d.hidden,
                                   d.experts, d.top_k, d.inter, d.shared_inter, L.max_tiles, s));
+  return MOE_OK;
+}
+
+// The shared expert's two GEMMs alone, on their own work lists (it does not
+// depend on the routing): the side-stream half of moe_forward_side.
+int run_shared_ffn(const moe_dims& d, const uint16_t* x, const moe_weights* w, const moe_routes* r,
+                   moe_saved* sv, void* ws, const Layout& L, hipStream_t s) {
+  const bool own_up = L.up_rows != moe::kRowsPerTile;
+  int32_t* meta = at<int32_t>(ws, L.meta_sh);
+  const int n64 = static_cast<int>((d.tokens + moe::kRowsPerTile - 1) / moe::kRowsPerTile);
+  const int nup = static_cast<int>((d.tokens + L.up_rows - 1) / L.up_rows);
+  MOE_LAUNCH(moe::launch_shared_tiles(at<int32_t>(ws, L.tiles_sh), meta, d.tokens, d.experts,
+                                      moe::kRowsPerTile, s));
+  if (own_up)
+    MOE_LAUNCH(moe::launch_shared_tiles(at<int32_t>(ws, L.tiles_sh_up), meta + 2, d.tokens, d.experts,
+                                        L.up_rows, s));
+  MOE_LAUNCH(moe::launch_ffn_up(x, w->w13, w->ws13, nullptr, nullptr, r->expert_offsets, r->sorted_route,
+                                at<int32_t>(ws, own_up ? L.tiles_sh_up : L.tiles_sh), meta + (own_up ? 2 : 0),
+                                L.up_rows, at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
+                                at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), sv->gu,
+                                sv->shared_gu, d.tokens, d.hidden, d.experts, d.top_k, d.inter,
+                                d.shared_inter, own_up ? nup : n64, s));
+  MOE_LAUNCH(moe::launch_ffn_down(at<uint16_t>(ws, L.act_hi), at<uint16_t>(ws, L.act_lo),
+                                  at<uint16_t>(ws, L.sact_hi), at<uint16_t>(ws, L.sact_lo), w->w2, w->ws2,
+                                  nullptr, nullptr, r->expert_offsets, r->sorted_route,
+                                  at<int32_t>(ws, L.tiles_sh), meta, sv->y, sv->shared_y, d.tokens, d.hidden,
+                                  d.experts, d.top_k, d.inter, d.shared_inter, n64, s));
   return MOE_OK;
 }
 
@@ -733,6 +770,49 @@ int moe_forward(const moe_dims* dims, const moe_weights* w, const uint16_t* x, m
                     stream));
   MOE_TRY(run_permute(d, routes, ws, L, stream));
   MOE_TRY(run_ffn(d, x, w, routes, saved, ws, L, true, stream));
+  return run_combine(d, routes, saved, out_f32, out_bf16, stream);
+}
+
+int moe_forward_side(const moe_dims* dims, const moe_weights* w, const uint16_t* x, moe_routes* routes,
+                     moe_saved* saved, float* out_f32, uint16_t* out_bf16, void* ws, size_t ws_bytes,
+                     hipStream_t stream, const moe_side_streams* side) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!w || !routes || !saved) return MOE_E_NULL;
+  if (!out_f32 && !out_bf16) return MOE_E_NULL;
+  if (!side || !side->side[0] || !side->side[1] || !side->fork || !side->join[0] || !side->join[1])
+    return MOE_E_NULL;
+  if (side->side[0] == side->side[1] || side->side[0] == stream || side->side[1] == stream)
+    return MOE_E_ALIAS;
+  if (side->fork == side->join[0] || side->fork == side->join[1] || side->join[0] == side->join[1])
+    return MOE_E_ALIAS;
+  const moe_dims& d = *dims;
+  const size_t T = d.tokens, H = d.hidden;
+  Args a;
+  a.in(x, bytes_x(d));
+  add_weights(a, d, w, true, true);
+  add_routes_out(a, d, routes);
+  add_perm_out(a, d, routes);
+  add_saved(a, d, saved, true);
+  a.out(out_f32, T * H * 4, false);
+  a.out(out_bf16, T * H * 2, false);
+  a.in(ws, std::min(ws_bytes, moe_workspace_bytes(dims, MOE_OP_FORWARD)), false);
+  MOE_TRY(a.status());
+  MOE_TRY(check_ws(d, ws, ws_bytes, MOE_OP_FORWARD));
+  MOE_TRY(check_device());
+  const Layout L = make_layout(d);
+  const bool sh = d.shared_inter > 0;
+  if (sh) {
+    // the shared expert on side[0], from this point of the call's stream
+    if (hipEventRecord(side->fork, stream) != hipSuccess) return MOE_E_LAUNCH;
+    if (hipStreamWaitEvent(side->side[0], side->fork, 0) != hipSuccess) return MOE_E_LAUNCH;
+    MOE_TRY(run_shared_ffn(d, x, w, routes, saved, ws, L, side->side[0]));
+    if (hipEventRecord(side->join[0], side->side[0]) != hipSuccess) return MOE_E_LAUNCH;
+  }
+  MOE_TRY(run_route(d, x, w, routes, ws, L, sh ? saved->shared_gate : nullptr, stream));
+  MOE_TRY(run_permute(d, routes, ws, L, stream, false));
+  MOE_TRY(run_ffn(d, x, w, routes, saved, ws, L, true, stream));
+  if (sh && hipStreamWaitEvent(stream, side->join[0], 0) != hipSuccess) return MOE_E_LAUNCH;
   return run_combine(d, routes, saved, out_f32, out_bf16, stream);
 }
 

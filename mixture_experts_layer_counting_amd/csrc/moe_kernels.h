@@ -42,6 +42,8 @@ hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* 
                              hipStream_t stream);
 // Work list from caller-supplied offsets; offsets that are not a partition
 // of [0, T*K) set *err_word and give an empty list.
+// The shared expert's work list alone (rows-row tiles), length in *ntiles.
+hipError_t launch_shared_tiles(int32_t* tiles, int32_t* ntiles, int64_t T, int E, int rows, hipStream_t stream);
 // Offsets that are not a partition of [0, T*K) set *err_word = 1 and leave
 // an empty list; with err_overwrite valid offsets clear it (0).
 hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* tiles_up, int up_rows,

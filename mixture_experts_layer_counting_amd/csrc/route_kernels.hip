@@ -925,6 +925,26 @@ hipError_t launch_route_scan(const int32_t* hist, int32_t* block_base, int32_t* 
   return hipGetLastError();
 }
 
+// The shared expert's work list alone: tiles (E, c * rows) for c < ceil(T /
+// rows), and its length in *ntiles.
+__global__ __launch_bounds__(256) void shared_tiles_kernel(int32_t* __restrict__ tiles,
+                                                           int32_t* __restrict__ ntiles, int64_t T, int E,
+                                                           int rows) {
+  const int64_t n = (T + rows - 1) / rows;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (c < n) {
+    tiles[2 * c] = E;
+    tiles[2 * c + 1] = static_cast<int32_t>(c * rows);
+  }
+  if (c == 0) *ntiles = static_cast<int32_t>(n);
+}
+
+hipError_t launch_shared_tiles(int32_t* tiles, int32_t* ntiles, int64_t T, int E, int rows, hipStream_t stream) {
+  const int64_t n = (T + rows - 1) / rows;
+  shared_tiles_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(tiles, ntiles, T, E, rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_tiles(const int32_t* offsets, int32_t* tiles, int32_t* tiles_up, int up_rows,
                             int32_t* meta, int* err_word, int err_overwrite, int E, int64_t T, int K,
                             int has_shared, int rows_per_tile, hipStream_t stream) {

@@ -375,3 +375,24 @@ def test_backward_side_validation(lib):
     import torch
     if not torch.cuda.is_available():
         assert call(Side()) == m.MOE_E_DEVICE
+
+
+def test_forward_side_validation(lib):
+    """moe_forward_side checks moe_forward's arguments and the side streams
+    and events before anything is enqueued."""
+    d = m.Dims(64, 512, 512, 10, 128, 128)
+    w, r, s, x, o32, o16, ws, f = full_args(d)
+    mk = lambda side=(0x1000, 0x2000), fork=0x3000, join=(0x4000, 0x5000): type(
+        "S", (), {"c": lambda self: m.MoeSideStreams((m._VP * 2)(*side), fork, (m._VP * 2)(*join))})()
+    call = lambda side, stream=0x9000, dd=d: m.moe_forward_side(dd, w, x, r, s, o32, o16, ws, side, stream=stream)
+    assert call(None) == m.MOE_E_NULL
+    assert call(mk(side=(0, 0x2000))) == m.MOE_E_NULL
+    assert call(mk(side=(0x1000, 0x1000))) == m.MOE_E_ALIAS
+    assert call(mk(), stream=0x1000) == m.MOE_E_ALIAS
+    assert call(mk(join=(0x4000, 0x4000))) == m.MOE_E_ALIAS
+    assert call(mk(), dd=m.Dims(64, 500, 512, 10, 128, 128)) == m.MOE_E_SHAPE
+    assert call(mk(), dd=m.Dims(0, 512, 512, 10, 128, 128)) == m.MOE_OK
+    assert m.moe_forward_side(d, w, x, r, s, None, None, ws, mk(), stream=0x9000) == m.MOE_E_NULL
+    import torch
+    if not torch.cuda.is_available():
+        assert call(mk()) == m.MOE_E_DEVICE

@@ -186,3 +186,44 @@ def test_backward_side_streams_graph_replays_match_eager():
             if getattr(g, k) is not None:
                 assert torch.equal(bits(getattr(g, k)), bits(getattr(rg, k))), f"replay {i}: {k}"
         eager(dout_a if i % 2 else dout_b)
+
+
+def test_forward_side_streams_graph_replays_match_eager():
+    """moe_forward_side captured: the fork event pulls the shared expert's
+    side stream into the capture and the join brings it back before the
+    combine; four replays on alternating inputs equal eager forwards."""
+    cfg, layer, x = load_cfg("moe1k")
+    w = dev_weights(layer)
+    xd = dev_bits(x)
+    other = dev_bits(W.tokens(cfg, stream=W.S_COMPANION, index=24))
+    d = dims_of(cfg)
+    routes = m.alloc_routes(d, DEV)
+    saved = m.alloc_saved(d, DEV)
+    out32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, DEV)
+    side = m.SideStreams(DEV)
+    xin = xd.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.check(m.moe_forward_side(d, w, xin, routes, saved, out32, out16, ws, side, s), "warm-up")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("case: moe1k, capture moe_forward_side")
+    with torch.cuda.graph(graph, stream=s):
+        m.check(m.moe_forward_side(d, w, xin, routes, saved, out32, out16, ws, side,
+                                   torch.cuda.current_stream()), "captured forward")
+    ref = gpu_forward(cfg, w, xd)
+    ref_other = gpu_forward(cfg, w, other)
+    for i in range(4):
+        xin.copy_(other if i % 2 else xd)
+        out32.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = ref_other if i % 2 else ref
+        assert torch.equal(routes.topk_idx, want.routes.topk_idx), f"replay {i}: routes"
+        assert torch.equal(bits(saved.shared_y), bits(want.saved.shared_y)), f"replay {i}: shared rows"
+        assert torch.equal(bits(out32), bits(want.out32)), f"replay {i}: out_f32"
+        assert torch.equal(out16, want.out16), f"replay {i}: out_bf16"
+        gpu_forward(cfg, w, other if i % 2 else xd)
