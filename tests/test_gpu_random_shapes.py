@@ -36,3 +36,34 @@ def test_random_shape_forward_and_backward(shape):
     g = gpu_forward(cfg, dev_weights(layer), dev_bits(x)).host()
     check_forward(cfg, layer, x, g)
     full_backward_check(cfg, layer, x, W.grad_out(cfg))
+
+
+@pytest.mark.parametrize("shape", random_shapes()[:5], ids=lambda s: "T{tokens}-H{hidden}-E{experts}-K{top_k}-I{inter}-S{shared_inter}".format(**s))
+def test_random_shape_mx_and_lora(shape):
+    """The same random shapes with block-scaled FP8 expert weights (bit for
+    bit the bf16 forward on the represented weights) and with LoRA adapters
+    of a random rank (forward and every gradient against the oracle)."""
+    import workloads.lora as WL
+    import workloads.mx as MX
+    from tests.test_gpu_lora_backward import full_check
+    from tests.test_gpu_mx import gpu_forward_mx, mx_weights, represented_bits
+    cfg = W.MoEConfig(name="random", **shape)
+    layer = W.make_layer(cfg)
+    x = W.tokens(cfg)
+    xd = dev_bits(x)
+    say(f"case: random shape {shape}, MX weights")
+    mxl = MX.mx_layer(layer)
+    rep = dict(layer)
+    for k in ("w13", "w2", "ws13", "ws2"):
+        if mxl[k] is not None:
+            rep[k] = represented_bits(*mxl[k])
+    g_mx = gpu_forward_mx(cfg, mx_weights(layer, mxl), xd)
+    g_bf = gpu_forward(cfg, dev_weights(rep), xd).host()
+    for k in ("idx", "sorted_route", "gates", "y", "s", "out32", "out16"):
+        if g_bf[k] is None:
+            assert g_mx[k] is None, k
+            continue
+        assert np.array_equal(np.asarray(g_mx[k]).view(np.uint8), np.asarray(g_bf[k]).view(np.uint8)), k
+    rank = int(np.random.default_rng(shape["tokens"]).integers(1, 17))
+    say(f"case: random shape {shape}, LoRA rank {rank}")
+    full_check(cfg, layer, WL.lora_adapters(cfg, rank), x, W.grad_out(cfg))
