@@ -197,7 +197,7 @@ def forward_inputs(cfg, w):
                 ws=m.alloc_workspace(d, m.MOE_OP_FORWARD, dev))
 
 
-def run_config(cfg, w, steps, warmup, hip, evict, breakdown=True):
+def run_config(cfg, w, steps, warmup, hip, evict, breakdown=True, side=True):
     """Time `steps` forwards of `cfg`, each bracketed by HIP events on the
     kernels' stream with an eviction write before it (the events around
     ffn_up give the roofline kernel's duration in the same calls); then a
@@ -256,16 +256,16 @@ def run_config(cfg, w, steps, warmup, hip, evict, breakdown=True):
                       for k, n in enumerate(names)}
     assert m.moe_last_device_error(ws) == m.MOE_OK
     # the same forwards with the shared expert on a side stream (moe_forward_side)
-    side = m.SideStreams(torch.device("cuda:0"))
+    streams = m.SideStreams(torch.device("cuda:0")) if side else None
 
     def fwd_side():
-        m.check(m.moe_forward_side(d, w, x, routes, saved, None, out16, ws, side, stream), "moe_forward_side")
+        m.check(m.moe_forward_side(d, w, x, routes, saved, None, out16, ws, streams, stream), "moe_forward_side")
 
-    for _ in range(warmup):
+    for _ in range(warmup if side else 0):
         fwd_side()
     torch.cuda.synchronize()
     side_ms = []
-    for _ in range(steps):
+    for _ in range(steps if side else 0):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         evict()
         e0.record(stream)
@@ -278,7 +278,7 @@ def run_config(cfg, w, steps, warmup, hip, evict, breakdown=True):
     load = np.diff(routes.expert_offsets.cpu().numpy())
     return dict(call=stats(call_ms), up=stats(up_ms), wall_ms=wall / steps * 1e3, b2b_ms=b2b,
                 per_kernel=per_kernel, touched=touched, max_load=int(load.max()),
-                empty=int((load == 0).sum()), side=stats(side_ms))
+                empty=int((load == 0).sum()), side=stats(side_ms) if side_ms else None)
 
 
 def summarize(cfg, r):
@@ -306,8 +306,8 @@ def summarize(cfg, r):
             mfma_frac=flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
             mfma_frac_cap=t_mfma / t_roof),
     )
-    sm = r["side"]["median_ms"]
-    out["side_streams"] = dict(what="moe_forward_side: the shared expert's GEMMs on a side stream beside "
+    sm = r["side"]["median_ms"] if r["side"] else None
+    out["side_streams"] = None if sm is None else dict(what="moe_forward_side: the shared expert's GEMMs on a side stream beside "
                                     "the routing and the routed GEMMs (same protocol, bit-identical output)",
                                ms_per_step=sm, p10_ms=r["side"]["p10_ms"], p90_ms=r["side"]["p90_ms"],
                                tokens_per_s=cfg.tokens / (sm / 1e3), layer_roofline_frac=t_roof / (sm / 1e3))
@@ -477,7 +477,7 @@ def run_lora(cfg, w, steps, warmup):
             "plain_forward_ms": ms_plain, "adapter_bytes": sum(int(ad[k].nbytes) for k in ("a13", "b13", "a2", "b2"))}
 
 
-def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True):
+def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True, side=True):
     """`fb_calls` forward (training mode) + backward calls, then `steps`
     backward-only calls of the same batch, each HIP-event timed on the
     kernels' stream with an eviction write before it.  With `lora`, also
@@ -521,10 +521,12 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True):
     fb = timed(lambda: (fwd(), bwd()), fb_calls)
     bo = timed(bwd, steps)
     assert m.moe_last_device_error(ws) == m.MOE_OK
-    side = m.SideStreams(dev)
-    bs = timed(lambda: m.check(m.moe_backward_side(d, w, x, routes, saved, dout, dx32, None, grads, ws, side,
-                                                   stream), "moe_backward_side"), steps)
-    assert m.moe_last_device_error(ws) == m.MOE_OK
+    bs = None
+    if side:
+        streams = m.SideStreams(dev)
+        bs = timed(lambda: m.check(m.moe_backward_side(d, w, x, routes, saved, dout, dx32, None, grads, ws,
+                                                       streams, stream), "moe_backward_side"), steps)
+        assert m.moe_last_device_error(ws) == m.MOE_OK
     lb = None
     if lora:
         import workloads.lora as WL
@@ -562,9 +564,10 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True):
             "bytes": byts, "flop": flop, "t_roof_ms": t_roof * 1e3, "roofline_frac": t_roof / (ms / 1e3),
             "hbm_frac": byts / (ms / 1e3) / (PEAK_HBM_GBS * 1e9),
             "mfma_frac": flop / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12), "lora": lb,
-            "side_streams": {"what": "moe_backward_side: dW13 and dW2 on two caller-owned streams beside dx",
-                             "ms": bs["median_ms"], "p10_ms": bs["p10_ms"], "p90_ms": bs["p90_ms"],
-                             "calls": bs["calls"], "tokens_per_s": T / (bs["median_ms"] / 1e3)}}
+            "side_streams": None if bs is None else {
+                "what": "moe_backward_side: dW13 and dW2 on two caller-owned streams beside dx",
+                "ms": bs["median_ms"], "p10_ms": bs["p10_ms"], "p90_ms": bs["p90_ms"],
+                "calls": bs["calls"], "tokens_per_s": T / (bs["median_ms"] / 1e3)}}
 
 
 def gpu_info():
@@ -692,6 +695,8 @@ def main():
                     help="also time the forward with LoRA adapters on the routed experts (0: off)")
     ap.add_argument("--no-evict", action="store_true", help="time without the eviction writes (profiling runs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achieved-peak probes")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the side-stream variants (profiling runs: their shared-only launches share kernel names)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -745,24 +750,26 @@ def main():
         del a, b
 
     log(f"bench: {cfg.name} warmup {args.warmup}, steps {args.steps}")
-    main_r = run_config(cfg, w, args.steps, args.warmup, hip, evict)
+    main_r = run_config(cfg, w, args.steps, args.warmup, hip, evict, side=not args.no_side)
     main_s = summarize(cfg, main_r)
     log(f"bench: {cfg.name} median {main_s['ms_per_step']:.3f} ms (p10 {main_s['p10_ms']:.3f}, "
-        f"p90 {main_s['p90_ms']:.3f}), back to back {main_s['back_to_back_ms_per_step']:.3f} ms, side streams {main_s['side_streams']['ms_per_step']:.3f} ms, "
+        f"p90 {main_s['p90_ms']:.3f}), back to back {main_s['back_to_back_ms_per_step']:.3f} ms, "
+        + (f"side streams {main_s['side_streams']['ms_per_step']:.3f} ms, " if main_s["side_streams"] else "") +
         f"kernels {main_s['kernel_ms_marked']}")
 
     configs = {cfg.name: main_s}
     for name in extra:
         c2 = W.CONFIGS[name]
         log(f"bench: {c2.name} warmup {args.warmup}, steps {args.steps}")
-        r2 = run_config(c2, dev_layer(c2), args.steps, args.warmup, hip, evict)
+        r2 = run_config(c2, dev_layer(c2), args.steps, args.warmup, hip, evict, side=not args.no_side)
         configs[c2.name] = summarize(c2, r2)
         if name == "tiny":
             # the tiny layer's weights fit in the MALL: its warm number beside the flushed one
             configs[c2.name]["warm_ms_per_step"] = configs[c2.name]["back_to_back_ms_per_step"]
-        log(f"bench: {c2.name} median {configs[c2.name]['ms_per_step']:.3f} ms "
-            f"(side streams {configs[c2.name]['side_streams']['ms_per_step']:.3f}), "
-            f"roofline {configs[c2.name]['layer_roofline']['frac']:.3f}")
+        ss = configs[c2.name]["side_streams"]
+        log(f"bench: {c2.name} median {configs[c2.name]['ms_per_step']:.3f} ms"
+            + (f" (side streams {ss['ms_per_step']:.3f})" if ss else "")
+            + f", roofline {configs[c2.name]['layer_roofline']['frac']:.3f}")
 
     ep_share = None
     if args.ep_share > 1:
@@ -786,9 +793,10 @@ def main():
     if args.backward != "none":
         cb = W.CONFIGS[args.backward]
         log(f"bench: backward {cb.name}")
-        backward = run_backward(cb, dev_layer(cb), args.steps, 1, evict, lora=bool(args.lora))
-        log(f"bench: backward {backward['ms']:.3f} ms (side streams {backward['side_streams']['ms']:.3f} ms), "
-            f"forward + backward {backward['fwd_bwd_ms']:.3f} ms"
+        backward = run_backward(cb, dev_layer(cb), args.steps, 1, evict, lora=bool(args.lora), side=not args.no_side)
+        log(f"bench: backward {backward['ms']:.3f} ms"
+            + (f" (side streams {backward['side_streams']['ms']:.3f} ms)" if backward["side_streams"] else "")
+            + f", forward + backward {backward['fwd_bwd_ms']:.3f} ms"
             + (f", LoRA backward {backward['lora']['ms']:.3f} ms" if backward["lora"] else ""))
 
     cpu = None
