@@ -539,11 +539,19 @@ def run_backward(cfg, w, steps, warmup, evict, fb_calls=5, lora=True, side=True)
         lbs = timed(lambda: m.check(m.moe_backward_lora(d, w, lo, x, routes, saved, dout, dx32, None, grads, lg,
                                                         ws, stream), "moe_backward_lora"), steps)
         assert m.moe_last_device_error(ws) == m.MOE_OK
+        lss = None
+        if side:
+            streams_l = m.SideStreams(dev)
+            lss = timed(lambda: m.check(m.moe_backward_lora_side(d, w, lo, x, routes, saved, dout, dx32, None, grads,
+                                                                 lg, ws, streams_l, stream),
+                                        "moe_backward_lora_side"), steps)
+            assert m.moe_last_device_error(ws) == m.MOE_OK
         lb = {"workload": f"{cfg.name}: backward with LoRA adapters of rank {ad['rank']} on all {cfg.experts} "
                           f"routed experts (adapter gradients included)",
               "ms": lbs["median_ms"], "p10_ms": lbs["p10_ms"], "p90_ms": lbs["p90_ms"], "calls": lbs["calls"],
               "tokens_per_s": cfg.tokens / (lbs["median_ms"] / 1e3),
-              "over_plain_ms": lbs["median_ms"] - bo["median_ms"]}
+              "over_plain_ms": lbs["median_ms"] - bo["median_ms"],
+              "side_streams_ms": lss["median_ms"] if lss else None}
     touched = int((np.diff(routes.expert_offsets.cpu().numpy()) > 0).sum())
     H, I, Is, T, R, E = cfg.hidden, cfg.inter, cfg.shared_inter, cfg.tokens, cfg.routes, cfg.experts
     # algorithmic bytes: weights read, fp32 weight gradients written, per-route

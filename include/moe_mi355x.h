@@ -409,6 +409,16 @@ int moe_backward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora
                       const uint16_t* d_out, float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads,
                       moe_lora_grads* lora_grads, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_backward_lora with the base weight gradients on the side streams as in
+ * moe_backward_side (the adapter gradients stay on `stream`, after dx).
+ * Bit for bit moe_backward_lora.  Errors as moe_backward_lora and
+ * moe_backward_side. */
+int moe_backward_lora_side(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,
+                           const uint16_t* x, const moe_routes* routes, const moe_saved* saved,
+                           const uint16_t* d_out, float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads,
+                           moe_lora_grads* lora_grads, void* ws, size_t ws_bytes, hipStream_t stream,
+                           const moe_side_streams* side);
+
 /* Profiling variant of moe_forward: the same kernels in the same order on
  * `stream`, with events[i] recorded just before kernel i and events[n] after
  * the last one, n = moe_forward_kernel_count(dims).  `events` are created by

@@ -79,7 +79,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_forward_profiled", "moe_forward_kernel_count", "moe_forward_kernel_name", "moe_forward_mx",
            "moe_forward_lora", "moe_grouped_ffn_lora", "moe_forward_noalloc", "moe_backward_lora",
            "moe_split_router", "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_backward_side",
-           "moe_forward_side")
+           "moe_forward_side", "moe_backward_lora_side")
 
 _lib = None
 
@@ -130,6 +130,9 @@ def load_library():
     lib.moe_forward_side.restype = ctypes.c_int
     lib.moe_forward_side.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, *ws,
                                      P(MoeSideStreams)]
+    lib.moe_backward_lora_side.restype = ctypes.c_int
+    lib.moe_backward_lora_side.argtypes = [P(MoeDims), P(MoeWeights), P(MoeLora), _VP, P(MoeRoutes), P(MoeSaved),
+                                           _VP, _VP, _VP, P(MoeGrads), P(MoeLoraGrads), *ws, P(MoeSideStreams)]
     lib.moe_backward_side.restype = ctypes.c_int
     lib.moe_backward_side.argtypes = [P(MoeDims), P(MoeWeights), _VP, P(MoeRoutes), P(MoeSaved), _VP, _VP, _VP,
                                       P(MoeGrads), *ws, P(MoeSideStreams)]
@@ -415,6 +418,18 @@ def moe_forward_side(dims, weights, x, routes, saved, out_f32, out_bf16, ws, sid
     return load_library().moe_forward_side(ctypes.byref(dims.c()), ctypes.byref(weights.c()), _ptr(x),
                                            ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(out_f32),
                                            _ptr(out_bf16), p, n, _stream(stream), sc)
+
+
+def moe_backward_lora_side(dims, weights, lora, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, lora_grads, ws,
+                           side, stream=None) -> int:
+    p, n = _ws(ws)
+    lg = ctypes.byref(lora_grads.c()) if lora_grads is not None else None
+    lc = ctypes.byref(lora.c()) if lora is not None else None
+    sc = ctypes.byref(side.c()) if side is not None else None
+    return load_library().moe_backward_lora_side(ctypes.byref(dims.c()), ctypes.byref(weights.c()), lc, _ptr(x),
+                                                 ctypes.byref(routes.c()), ctypes.byref(saved.c()), _ptr(d_out),
+                                                 _ptr(d_x_f32), _ptr(d_x_bf16), ctypes.byref(grads.c()), lg, p, n,
+                                                 _stream(stream), sc)
 
 
 def moe_backward_side(dims, weights, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, ws, side,

@@ -441,6 +441,17 @@ void add_saved(Args& a, const moe_dims& d, const moe_saved* sv, bool out) {
   }
 }
 
+// side streams and events: all present, all distinct, none the call's stream
+int check_side(const moe_side_streams* side, hipStream_t stream) {
+  if (!side || !side->side[0] || !side->side[1] || !side->fork || !side->join[0] || !side->join[1])
+    return MOE_E_NULL;
+  if (side->side[0] == side->side[1] || side->side[0] == stream || side->side[1] == stream)
+    return MOE_E_ALIAS;
+  if (side->fork == side->join[0] || side->fork == side->join[1] || side->join[0] == side->join[1])
+    return MOE_E_ALIAS;
+  return MOE_OK;
+}
+
 // moe_backward (lora null), moe_backward_lora (rank already checked) and
 // moe_backward_side (ss: the caller's side streams and events; null: one
 // stream).
@@ -780,12 +791,7 @@ int moe_forward_side(const moe_dims* dims, const moe_weights* w, const uint16_t*
   if (dims->tokens == 0) return MOE_OK;
   if (!w || !routes || !saved) return MOE_E_NULL;
   if (!out_f32 && !out_bf16) return MOE_E_NULL;
-  if (!side || !side->side[0] || !side->side[1] || !side->fork || !side->join[0] || !side->join[1])
-    return MOE_E_NULL;
-  if (side->side[0] == side->side[1] || side->side[0] == stream || side->side[1] == stream)
-    return MOE_E_ALIAS;
-  if (side->fork == side->join[0] || side->fork == side->join[1] || side->join[0] == side->join[1])
-    return MOE_E_ALIAS;
+  MOE_TRY(check_side(side, stream));
   const moe_dims& d = *dims;
   const size_t T = d.tokens, H = d.hidden;
   Args a;
@@ -951,13 +957,22 @@ int moe_backward_side(const moe_dims* dims, const moe_weights* w, const uint16_t
                       hipStream_t stream, const moe_side_streams* side) {
   MOE_TRY(check_dims(dims));
   if (dims->tokens == 0) return MOE_OK;
-  if (!side || !side->side[0] || !side->side[1] || !side->fork || !side->join[0] || !side->join[1])
-    return MOE_E_NULL;
-  if (side->side[0] == side->side[1] || side->side[0] == stream || side->side[1] == stream)
-    return MOE_E_ALIAS;
-  if (side->fork == side->join[0] || side->fork == side->join[1] || side->join[0] == side->join[1])
-    return MOE_E_ALIAS;
+  MOE_TRY(check_side(side, stream));
   return run_backward(dims, w, nullptr, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, nullptr, ws,
+                      ws_bytes, stream, side);
+}
+
+int moe_backward_lora_side(const moe_dims* dims, const moe_weights* w, const moe_lora* lora,
+                           const uint16_t* x, const moe_routes* routes, const moe_saved* saved,
+                           const uint16_t* d_out, float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads,
+                           moe_lora_grads* lora_grads, void* ws, size_t ws_bytes, hipStream_t stream,
+                           const moe_side_streams* side) {
+  MOE_TRY(check_dims(dims));
+  if (dims->tokens == 0) return MOE_OK;
+  if (!lora || !lora_grads) return MOE_E_NULL;
+  if (lora->rank < 1 || lora->rank > moe::kLoraMaxRank) return MOE_E_SHAPE;
+  MOE_TRY(check_side(side, stream));
+  return run_backward(dims, w, lora, x, routes, saved, d_out, d_x_f32, d_x_bf16, grads, lora_grads, ws,
                       ws_bytes, stream, side);
 }
 

@@ -207,3 +207,32 @@ def test_lora_backward_deterministic_and_dx_batch_invariant():
         gs = forward_lora_training(cfg, w, lo, xd[sl].clone())
         p = backward_lora(cfg, w, lo, xd[sl].clone(), gs, dd[sl].clone())
         assert torch.equal(bits(p[0]), bits(a[0][sl])), f"dX rows at {start} differ"
+
+
+@pytest.mark.parametrize("name", ["tiny", "bwd4k"])
+def test_lora_backward_side_streams_equal(name):
+    """moe_backward_lora_side gives moe_backward_lora's bits for every
+    gradient, adapter gradients included."""
+    cfg, layer, x = load_any(name)
+    ad = WL.lora_adapters(cfg)
+    w, lo, xd = dev_weights(layer), dev_lora(ad), dev_bits(x)
+    dd = dev_bits(W.grad_out(cfg))
+    say(f"case: {name}, moe_backward_lora_side vs moe_backward_lora")
+    g = forward_lora_training(cfg, w, lo, xd)
+    ref = backward_lora(cfg, w, lo, xd, g, dd)
+    d = dims_of(cfg)
+    side = m.SideStreams(DEV)
+    ws = m.alloc_workspace(d, m.MOE_OP_BACKWARD_LORA, DEV)
+    grads = m.alloc_grads(d, DEV)
+    lg = m.alloc_lora_grads(d, lo.rank, DEV)
+    dx32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    m.check(m.moe_backward_lora_side(d, w, lo, xd, g.routes, g.saved, dd, dx32, None, grads, lg, ws, side),
+            "moe_backward_lora_side")
+    torch.cuda.synchronize()
+    assert m.moe_last_device_error(ws) == m.MOE_OK
+    assert torch.equal(bits(dx32), bits(ref[0])), "dX"
+    for k in GRADS:
+        if getattr(grads, k) is not None:
+            assert torch.equal(bits(getattr(grads, k)), bits(getattr(ref[2], k))), k
+    for k in LGRADS:
+        assert torch.equal(bits(getattr(lg, k)), bits(getattr(ref[3], k))), k
