@@ -709,7 +709,7 @@ def main():
                     help="also launch one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the whole layer on a single MI355X "
+        print("bench.py measures one GPU only: the library runs the whole layer on a single MI355X "
               "with all experts resident and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 

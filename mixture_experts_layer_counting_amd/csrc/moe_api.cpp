@@ -198,23 +198,23 @@ int check_ws(const moe_dims& d, const void* ws, size_t ws_bytes, int op) {
 // gfx950 check of the current device, cached per device id.
 int check_device() {
   static std::mutex mu;
-  static std::vector<int> verdict;  // 0 unknown, 1 ok, 2 bad
+  static std::vector<int> arch_ok;  // 0 unknown, 1 ok, 2 bad
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
     return MOE_E_DEVICE;
   }
   std::lock_guard<std::mutex> lock(mu);
-  if (static_cast<size_t>(dev) >= verdict.size()) verdict.resize(dev + 1, 0);
-  if (verdict[dev] == 0) {
+  if (static_cast<size_t>(dev) >= arch_ok.size()) arch_ok.resize(dev + 1, 0);
+  if (arch_ok[dev] == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
       (void)hipGetLastError();
       return MOE_E_DEVICE;
     }
-    verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
   }
-  return verdict[dev] == 1 ? MOE_OK : MOE_E_DEVICE;
+  return arch_ok[dev] == 1 ? MOE_OK : MOE_E_DEVICE;
 }
 
 #define MOE_TRY(expr)                       \
