@@ -253,7 +253,8 @@ typedef struct {
   hipEvent_t join[2];  /* recorded on side[i], waited for by the call's stream */
 } moe_side_streams;
 
-/* moe_backward with its three independent grouped GEMMs on three streams:
+/* Backward (contract, Backward bullet: the operation of moe_backward) with
+ * its three independent grouped GEMMs on three streams:
  * dW13 on side[0] and dW2 on side[1], from the point where the activation
  * gradients exist (`fork`), dx and the kernels after it on `stream`, which
  * then waits for both side streams (`join`), so work enqueued on `stream`
@@ -267,7 +268,9 @@ int moe_backward_side(const moe_dims* dims, const moe_weights* w, const uint16_t
                       float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads, void* ws, size_t ws_bytes,
                       hipStream_t stream, const moe_side_streams* side);
 
-/* moe_forward with the shared expert on side[0]: its two GEMMs, which do
+/* Whole forward (contract, Routing, Experts and Combine bullets; the shared
+ * expert of the SkyRL pull request 2513 page's What section: the operation
+ * of moe_forward) with the shared expert on side[0]: its two GEMMs, which do
  * not depend on the routing, run from the call's start (`fork`) on lists of
  * their own, beside the router, top-k, permutation and routed GEMMs on
  * `stream`; `stream` waits for them (`join[0]`) before the combine.  The
@@ -409,7 +412,8 @@ int moe_backward_lora(const moe_dims* dims, const moe_weights* w, const moe_lora
                       const uint16_t* d_out, float* d_x_f32, uint16_t* d_x_bf16, moe_grads* grads,
                       moe_lora_grads* lora_grads, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* moe_backward_lora with the base weight gradients on the side streams as in
+/* LoRA backward (ROLL pull request 502 page, opening summary: the operation
+ * of moe_backward_lora) with the base weight gradients on the side streams as in
  * moe_backward_side (the adapter gradients stay on `stream`, after dx).
  * Bit for bit moe_backward_lora.  Errors as moe_backward_lora and
  * moe_backward_side. */
