@@ -295,7 +295,7 @@ def summarize(cfg, r):
         tokens_per_s=cfg.tokens / (ms / 1e3),
         ms_per_step=ms, p10_ms=r["call"]["p10_ms"], p90_ms=r["call"]["p90_ms"],
         wall_ms_per_step_incl_eviction=r["wall_ms"], back_to_back_ms_per_step=r["b2b_ms"],
-        ffn_up_ms=r["up"]["median_ms"],
+        ffn_up_ms=r["up"]["mean_ms"], ffn_up_median_ms=r["up"]["median_ms"],
         kernel_ms_marked=r["per_kernel"],
         touched_experts=r["touched"], max_expert_routes=r["max_load"], empty_experts=r["empty"],
         layer_roofline=dict(
@@ -312,7 +312,7 @@ def summarize(cfg, r):
                                ms_per_step=sm, p10_ms=r["side"]["p10_ms"], p90_ms=r["side"]["p90_ms"],
                                tokens_per_s=cfg.tokens / (sm / 1e3), layer_roofline_frac=t_roof / (sm / 1e3))
     if r["per_kernel"]:
-        out["ffn_up_gbs"] = ffn_up_bytes(cfg, r["touched"]) / (r["up"]["median_ms"] / 1e3) / 1e9
+        out["ffn_up_gbs"] = ffn_up_bytes(cfg, r["touched"]) / (r["up"]["mean_ms"] / 1e3) / 1e9
         out["ffn_down_gbs"] = ffn_down_bytes(cfg, r["touched"]) / (r["per_kernel"]["ffn_down"] / 1e3) / 1e9
     return out
 
@@ -852,6 +852,7 @@ def main():
         "roofline": {"kernel": "ffn_up", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "algorithmic_bytes": up_bytes, "avg_ms": up_ms,
+                     "median_ms": main_s["ffn_up_median_ms"],
                      "frac_of_achieved_read": achieved / peaks["read_gbs"] if peaks else None},
         "gpu": gpu_info(),
         "achieved_peaks": peaks,
