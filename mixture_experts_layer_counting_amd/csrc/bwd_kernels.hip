@@ -74,14 +74,12 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const double* __restrict_
 //   * [row][k] (64-byte rows, XOR-swizzled 16-byte pieces: rk_off) for
 //     sources stored k-contiguous (the routed or token rows of a dgrad);
 //     fragments are 16-byte LDS loads;
-//   * [k][col] (320-byte rows) for sources whose rows are indexed by k (the
-//     expert weights read along their output dimension, and both operands
-//     of a weight gradient, whose contraction runs over the routes of an
-//     expert).  Rows are stored as the 16-byte pieces they are loaded in and
-//     fragments are read with the gfx950 LDS transpose read
-//     (ds_read_b64_tr_b16), two per fragment.  The 64 bytes of padding per
-//     row make those reads free of bank conflicts on MI355X (measured with
-//     the LDS bank-conflict counter: 256- and 288-byte rows conflict).
+//   * [k][col] (256-byte rows, XOR-swizzled 64-byte quarters: rc_off) for
+//     sources whose rows are indexed by k (the expert weights read along
+//     their output dimension, and both operands of a weight gradient, whose
+//     contraction runs over the routes of an expert).  Rows are stored as
+//     the 16-byte pieces they are loaded in and fragments are read with the
+//     gfx950 LDS transpose read (ds_read_b64_tr_b16), two per fragment.
 // An fp32 operand (dGU, g*act) is given as kGradPlanes bf16 planes, its
 // exact split hi + mid + lo, and takes one MFMA per plane per K step in plane
 // order: all three in the weight gradients, hi and mid in kDx.
@@ -118,7 +116,15 @@ constexpr int kBK = 32;
 // c ^ ((row >> 2) & 3), which keeps both the loaders' stores (4 rows x 4
 // pieces per 16 lanes) and the 32-row fragment reads free of bank conflicts.
 __device__ __forceinline__ int rk_off(int row, int c) { return row * kBK + ((c ^ ((row >> 2) & 3)) << 3); }
-constexpr int kRStride = 160;  // [k][col] layout: 128 columns + 32 padding
+// [k][col] layout: 128 columns per row; the 64-byte quarter of row `row`
+// that holds column `col` is stored at quarter (col / 32) ^ (row % 4).  A
+// transpose read's 32 lanes of a half-wave take 64 bytes of each of four
+// consecutive rows (4-aligned), which the swizzle spreads over the four
+// quarters, i.e. all 64 banks once; unswizzled 256-byte rows put them on
+// the same 16 banks (measured with the LDS bank-conflict counter).  The
+// loaders write whole 256-byte rows per 16 lanes, conflict-free either way.
+constexpr int kRStride = 128;
+__device__ __forceinline__ int rc_off(int row, int col) { return row * kRStride + (col ^ ((row & 3) << 5)); }
 constexpr int kKPlane = kBT * kBK;
 constexpr int kRPlane = kBK * kRStride;
 
@@ -135,7 +141,8 @@ __device__ __forceinline__ u32x4_t frag_tr(const uint16_t* plane, int k0, int co
   const int L = lane & 15;
   const int row = k0 + 8 * (lane >> 5) + (L >> 2);
   const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
-  const uint16_t* p = plane + row * kRStride + col;
+  // rows row and row + 4 share the swizzle
+  const uint16_t* p = plane + rc_off(row, col);
   const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
   const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p + 4 * kRStride));
   const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -188,6 +195,7 @@ struct BwdTile {
   int rows;  // valid rows (dgrad) / contraction length (wgrad)
   int seg0;  // first sorted position of the group (0 for the shared group)
   bool shared;
+  bool wstream;  // dgrad: the group's only row tile, which reads each weight once
   int Ie;
 };
 
@@ -209,6 +217,7 @@ __device__ __forceinline__ bool bwd_decode(const BwdArgs& a, int g, BwdTile& w) 
     w.seg0 = w.shared ? 0 : a.offsets[w.grp];
     const int cnt = w.shared ? static_cast<int>(a.T) : a.offsets[w.grp + 1] - w.seg0;
     w.rows = min(kBT, cnt - w.m0);
+    w.wstream = cnt <= kBT;
     return w.rows > 0;
   }
   // an empty work list means the caller's offsets failed the check of
@@ -231,6 +240,7 @@ __device__ __forceinline__ bool bwd_decode(const BwdArgs& a, int g, BwdTile& w) 
   if (MODE == kDw13 && w.m0 >= 2 * w.Ie) return false;
   w.seg0 = w.shared ? 0 : a.offsets[w.grp];
   w.rows = w.shared ? static_cast<int>(a.T) : a.offsets[w.grp + 1] - w.seg0;
+  w.wstream = false;
   return true;
 }
 
@@ -255,7 +265,7 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
 // <D + s A2^T B2^T dOut, act> include the adapter; kDx takes z = B13^T dGU
 // and A13.
 template <int MODE, int NKB = 0, bool LORA = false>
-__global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void bwd_gemm_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void bwd_gemm_kernel(const BwdArgs a) {
   constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
   static_assert(NKB == 0 || !WGRAD, "the unrolled loop is for the dgrad modes");
   constexpr int NSET = NKB > 0 ? 4 : 1;
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
   constexpr int APLANE = WGRAD ? kRPlane : kKPlane;
   constexpr int STAGE = NPA * APLANE + NPB * kRPlane;
   // weight gradients (short contractions): one LDS stage and two barriers
-  // per K block, which leaves room for three workgroups per CU
+  // per K block, which leaves room for four workgroups per CU
   constexpr int NSTAGE = WGRAD ? 1 : 2;
   // the epilogue stages a 64-row half of the fp32 tile (stride kBT + 4) in
   // the same area
@@ -400,8 +410,10 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
 #pragma unroll
         for (int c = 0; c < 2; ++c) ra_set[set][q][c] = ld16(a_base[q] + a_off[c] + k0 + lc);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        rb_set[set][0][c] = ld16(wbase + static_cast<int64_t>(k0 + kr + 16 * c) * wcols + w.n0 + tc);
+      for (int c = 0; c < 2; ++c) {
+        const uint16_t* wp = wbase + static_cast<int64_t>(k0 + kr + 16 * c) * wcols + w.n0 + tc;
+        rb_set[set][0][c] = w.wstream ? ld16_nt(wp) : ld16(wp);
+      }
       return;
     }
     fetch_plain(set, kb);
@@ -416,12 +428,12 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         if (!WGRAD) st16(s + q * APLANE + rk_off(lr + 64 * c, lc >> 3), ra[q][c]);
-        else st16(s + q * APLANE + (kr + 16 * c) * kRStride + tc, ra[q][c]);
+        else st16(s + q * APLANE + rc_off(kr + 16 * c, tc), ra[q][c]);
       }
 #pragma unroll
     for (int q = 0; q < NPB; ++q)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) st16(s + NPA * APLANE + q * kRPlane + (kr + 16 * c) * kRStride + tc, rb[q][c]);
+      for (int c = 0; c < 2; ++c) st16(s + NPA * APLANE + q * kRPlane + rc_off(kr + 16 * c, tc), rb[q][c]);
   };
 
   f32x16_t acc[2][2];
@@ -507,11 +519,16 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
       __syncthreads();
       const int cur = NSTAGE == 2 ? (it & 1) : 0;
       const bool more = it + 1 < nkb;
-      if (more) {
-        fetch_set(0, it + 1);
-        if (WGRAD && it + 2 < nkb) wg_tokens(it + 2, tok);
-      }
+      // dgrad: the next block's loads are in flight during this block's
+      // MFMAs.  Weight gradients issue them after the MFMAs, so that their
+      // registers and the fragments' are never live together (this fits
+      // four workgroups per CU; their contractions are a few blocks long)
+      if (more && !WGRAD) fetch_set(0, it + 1);
       compute(cur);
+      if (more && WGRAD) {
+        fetch_set(0, it + 1);
+        if (it + 2 < nkb) wg_tokens(it + 2, tok);
+      }
       if (CHUNKED && (it + 1) % kDactChunk == 0) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -694,17 +711,17 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 3 : 2) void 
       if (MODE == kDx) {
         if (lrow >= w.rows) continue;
         if (w.shared) {
-          st16(a.dx_shared + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
+          st16_nt(a.dx_shared + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
         } else {
           const int64_t rt = a.sorted_route[static_cast<int64_t>(w.seg0) + w.m0 + lrow];
-          if (rt >= 0 && rt < a.T * a.K) st16(a.dx_route + rt * a.H + col, val);
+          if (rt >= 0 && rt < a.T * a.K) st16_nt(a.dx_route + rt * a.H + col, val);
         }
       } else if (MODE == kDw2) {
         float* o = w.shared ? a.dws2 : a.dw2 + static_cast<int64_t>(w.grp) * a.H * a.I;
-        st16(o + static_cast<int64_t>(w.m0 + lrow) * Ie + col, val);
+        st16_nt(o + static_cast<int64_t>(w.m0 + lrow) * Ie + col, val);
       } else {
         float* o = w.shared ? a.dws13 : a.dw13 + static_cast<int64_t>(w.grp) * 2 * a.I * a.H;
-        st16(o + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
+        st16_nt(o + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
       }
     }
   }

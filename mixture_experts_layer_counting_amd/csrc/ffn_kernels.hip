@@ -84,6 +84,8 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   const int seg0 = gi.seg0;
   const int cnt = gi.cnt;
   const int rows = min(ROWS, cnt - row0);
+  // the group's only row tile reads each of its weights once: stream them
+  const bool wstream = cnt <= ROWS;
   if (rows <= 0) return;
   const int nmb = (rows + 31) >> 5;
   const uint16_t* W = shared ? ws13 : w13 + static_cast<int64_t>(grp) * 2 * I * H;
@@ -190,8 +192,13 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        rb[set][q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp);
-        rb[set][4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp);
+        if (wstream) {
+          rb[set][q] = ld16_nt(wgp + static_cast<int64_t>(8 * q) * H + kp);
+          rb[set][4 + q] = ld16_nt(wup + static_cast<int64_t>(8 * q) * H + kp);
+        } else {
+          rb[set][q] = ld16(wgp + static_cast<int64_t>(8 * q) * H + kp);
+          rb[set][4 + q] = ld16(wup + static_cast<int64_t>(8 * q) * H + kp);
+        }
       }
     }
   };
@@ -346,6 +353,8 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   const int seg0 = gi.seg0;
   const int cnt = gi.cnt;
   const int rows = min(kRowsPerTile, cnt - row0);
+  // the group's only row tile reads each of its weights once: stream them
+  const bool wstream = cnt <= kRowsPerTile;
   if (rows <= 0) return;
   const int nmb = (rows + 31) >> 5;
   const uint16_t* W = shared ? ws2 : w2 + static_cast<int64_t>(grp) * H * I;
@@ -452,7 +461,9 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4 * NBW; ++q) rb[set][q] = ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp);
+      for (int q = 0; q < 4 * NBW; ++q)
+        rb[set][q] = wstream ? ld16_nt(wb + static_cast<int64_t>(8 * q) * Ie + kp)
+                             : ld16(wb + static_cast<int64_t>(8 * q) * Ie + kp);
     }
   };
   // blk: the K block being staged (compile-time in the unrolled loop)
@@ -567,7 +578,7 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     const int r = tid / kPieces + kRowsPerPass * i;
     if (r < rows) {
       const int dst = s_dst[r];
-      if (dst >= 0) st16(out + static_cast<int64_t>(dst) * H + nt * COLS + piece * 4, ld16(Cs + r * COLS + piece * 4));
+      if (dst >= 0) st16_nt(out + static_cast<int64_t>(dst) * H + nt * COLS + piece * 4, ld16(Cs + r * COLS + piece * 4));
     }
   }
 }
@@ -606,8 +617,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const int c = min(c0 + 1024 * b, H - 4);
 #pragma unroll
       for (int k = 0; k < KT; ++k)
-        v[b][k] = *reinterpret_cast<const f32x4v_t*>(yt + static_cast<int64_t>(min(k, K - 1)) * H + c);
-      vs[b] = *reinterpret_cast<const f32x4v_t*>(st + c);
+        v[b][k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(yt + static_cast<int64_t>(min(k, K - 1)) * H + c));
+      vs[b] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(st + c));
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -635,15 +646,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         o[1] = a1;
         o[2] = a2;
         o[3] = a3;
-        *reinterpret_cast<f32x4v_t*>(out32 + t * H + c) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4v_t*>(out32 + t * H + c));
       }
       if (out16) {
         const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(a0)) | (static_cast<uint32_t>(f32_to_bf16(a1)) << 16);
         const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(a2)) | (static_cast<uint32_t>(f32_to_bf16(a3)) << 16);
-        uint2 pk;
-        pk.x = lo;
-        pk.y = hi;
-        *reinterpret_cast<uint2*>(out16 + t * H + c) = pk;
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(out16 + t * H + c));
       }
     }
   }

@@ -56,6 +56,16 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cas
 
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
+// Non-temporal 16-byte vector load and store, for data that is streamed
+// (read or written once): it then does not push the operands that other
+// work items re-read out of the caches.
+__device__ __forceinline__ u32x4_t ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 // D = A(32x16) * B(16x32) + C on the matrix cores, bf16 inputs, fp32 accumulate.
 // Lane l supplies A[l%32][8*(l/32) .. +8] and B[8*(l/32) .. +8][l%32]; it holds
 // D[8*(v/4) + 4*(l/32) + v%4][l%32] in element v.
