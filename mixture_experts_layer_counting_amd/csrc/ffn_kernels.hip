@@ -181,8 +181,10 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
 
   auto issue = [&](int set, int kb) {
     const int kp = kb << 6;
+    // row blocks past the item's last row are neither loaded nor multiplied
 #pragma unroll
-    for (int q = 0; q < MBT; ++q) ra[set][q] = ld16(xa[q] + kp);
+    for (int q = 0; q < MBT; ++q)
+      if (q < nmb) ra[set][q] = ld16(xa[q] + kp);
     if constexpr (MX) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -205,7 +207,8 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   // blk: the K block being staged (compile-time in the unrolled loop)
   auto stash = [&](int set, int buf, int blk) {
 #pragma unroll
-    for (int q = 0; q < MBT; ++q) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[set][q]);
+    for (int q = 0; q < MBT; ++q)
+      if (q < nmb) st16(&As[buf][lds_off(ar0 + 32 * q, ac)], ra[set][q]);
     if constexpr (MX) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -448,10 +451,13 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   // activation rows past the tile's end repeat its last row (unused)
   auto issue = [&](int set, int kb) {
     const int kp = kb << 6;
+    // row blocks past the item's last row are neither loaded nor multiplied
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      rh[set][q] = ld16(ahi + aoff[q] + kp);
-      rl[set][q] = ld16(alo + aoff[q] + kp);
+      if (q < nmb) {
+        rh[set][q] = ld16(ahi + aoff[q] + kp);
+        rl[set][q] = ld16(alo + aoff[q] + kp);
+      }
     }
     if constexpr (MX) {
 #pragma unroll
@@ -470,8 +476,10 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
   auto stash = [&](int set, int buf, int blk) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      st16(As(buf, 0) + lds_off(ar0 + 32 * q, ac), rh[set][q]);
-      st16(As(buf, 1) + lds_off(ar0 + 32 * q, ac), rl[set][q]);
+      if (q < nmb) {
+        st16(As(buf, 0) + lds_off(ar0 + 32 * q, ac), rh[set][q]);
+        st16(As(buf, 1) + lds_off(ar0 + 32 * q, ac), rl[set][q]);
+      }
     }
     if constexpr (MX) {
 #pragma unroll
