@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
     if constexpr (MX) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        rq[set][q] = ld16(mq[q] + kp);
+        rq[set][q] = wstream ? ld16_nt(mq[q] + kp) : ld16(mq[q] + kp);
         if constexpr (NKB == 0) rs[set][q] = ms[q][2 * kb];
       }
     } else {
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256, 2) void ffn_down_kernel(
     if constexpr (MX) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        rq[set][q] = ld16(mq[q] + kp);
+        rq[set][q] = wstream ? ld16_nt(mq[q] + kp) : ld16(mq[q] + kp);
         if constexpr (NKB == 0) rs[set][q] = ms[q][2 * kb];
       }
     } else {
