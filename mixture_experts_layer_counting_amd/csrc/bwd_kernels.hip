@@ -268,7 +268,12 @@ template <int MODE, int NKB = 0, bool LORA = false>
 __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void bwd_gemm_kernel(const BwdArgs a) {
   constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
   static_assert(NKB == 0 || !WGRAD, "the unrolled loop is for the dgrad modes");
-  constexpr int NSET = NKB > 0 ? 4 : 1;
+  // unrolled dgrad: register rings of NSA K blocks for the routed or token
+  // rows (A: mostly cache hits) and NSB for the expert weight (B: streamed
+  // from HBM).  dx keeps more weight blocks in flight (3 + 5 sets measured
+  // 676 us at 4096 tokens against 694 for 4 + 4); dact is fastest at 4 + 4
+  constexpr int NSA = NKB > 0 ? (MODE == kDx ? 3 : 4) : 1;
+  constexpr int NSB = NKB > 0 ? (MODE == kDx ? 5 : 4) : 1;
   constexpr int NPA = MODE == kDx ? kDxPlanes : (MODE == kDw13 ? kGradPlanes : 1);
   constexpr int NPB = MODE == kDw2 ? kGradPlanes : 1;
   constexpr int APLANE = WGRAD ? kRPlane : kKPlane;
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
     }
   };
 
-  u32x4_t ra_set[NSET][NPA][2], rb_set[NSET][NPB][2];
+  u32x4_t ra_set[NSA][NPA][2], rb_set[NSB][NPB][2];
   // wgrad operands of K block kb: the one stored in route order (dGU or
   // g*act planes, rows p) and the one gathered by token (dOut or x rows)
   auto fetch_plain = [&](int set, int kb) {
@@ -402,38 +407,49 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
         rb_set[set][0][c] = in ? ld16(a.x + tok[c] * a.H + w.n0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
+  // dgrad operands of K block kb: A (routed or token rows) and B (weight)
+  auto fetch_a = [&](int set, int kb) {
+#pragma unroll
+    for (int q = 0; q < NPA; ++q)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) ra_set[set][q][c] = ld16(a_base[q] + a_off[c] + kb * kBK + lc);
+  };
+  auto fetch_b = [&](int set, int kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint16_t* wp = wbase + static_cast<int64_t>(kb * kBK + kr + 16 * c) * wcols + w.n0 + tc;
+      rb_set[set][0][c] = w.wstream ? ld16_nt(wp) : ld16(wp);
+    }
+  };
   auto fetch_set = [&](int set, int kb) {
-    const int k0 = kb * kBK;
     if (!WGRAD) {
-#pragma unroll
-      for (int q = 0; q < NPA; ++q)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) ra_set[set][q][c] = ld16(a_base[q] + a_off[c] + k0 + lc);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint16_t* wp = wbase + static_cast<int64_t>(k0 + kr + 16 * c) * wcols + w.n0 + tc;
-        rb_set[set][0][c] = w.wstream ? ld16_nt(wp) : ld16(wp);
-      }
+      fetch_a(set, kb);
+      fetch_b(set, kb);
       return;
     }
     fetch_plain(set, kb);
     fetch_gathered(set, kb);
   };
-  auto stash_set = [&](int set, int stage) {
-    const auto& ra = ra_set[set];
-    const auto& rb = rb_set[set];
+  auto stash_a = [&](int set, int stage) {
     uint16_t* s = smem + stage * STAGE;
 #pragma unroll
     for (int q = 0; q < NPA; ++q)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        if (!WGRAD) st16(s + q * APLANE + rk_off(lr + 64 * c, lc >> 3), ra[q][c]);
-        else st16(s + q * APLANE + rc_off(kr + 16 * c, tc), ra[q][c]);
+        if (!WGRAD) st16(s + q * APLANE + rk_off(lr + 64 * c, lc >> 3), ra_set[set][q][c]);
+        else st16(s + q * APLANE + rc_off(kr + 16 * c, tc), ra_set[set][q][c]);
       }
+  };
+  auto stash_b = [&](int set, int stage) {
+    uint16_t* s = smem + stage * STAGE;
 #pragma unroll
     for (int q = 0; q < NPB; ++q)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) st16(s + NPA * APLANE + q * kRPlane + rc_off(kr + 16 * c, tc), rb[q][c]);
+      for (int c = 0; c < 2; ++c) st16(s + NPA * APLANE + q * kRPlane + rc_off(kr + 16 * c, tc), rb_set[set][q][c]);
+  };
+  auto stash_set = [&](int set, int stage) {
+    stash_a(set, stage);
+    stash_b(set, stage);
   };
 
   f32x16_t acc[2][2];
@@ -474,16 +490,25 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
   };
 
   if constexpr (NKB > 0) {
-    // dgrad, unrolled: blocks it + 1 .. it + 3 in flight while it is multiplied
+    // dgrad, unrolled: A blocks it + 1 .. it + NSA - 1 and B blocks it + 1
+    // .. it + NSB - 1 in flight while block it is multiplied; the prologue
+    // issues them in K order, A before B within a block
 #pragma unroll
-    for (int q = 0; q < NSET && q < NKB; ++q) fetch_set(q, q);
+    for (int q = 0; q < (NSA > NSB ? NSA : NSB) && q < NKB; ++q) {
+      if (q < NSA) fetch_a(q, q);
+      if (q < NSB) fetch_b(q, q);
+    }
     stash_set(0, 0);
 #pragma unroll
     for (int it = 0; it < NKB; ++it) {
       __syncthreads();
-      if (it + NSET < NKB) fetch_set(it % NSET, it + NSET);
+      if (it + NSA < NKB) fetch_a(it % NSA, it + NSA);
+      if (it + NSB < NKB) fetch_b(it % NSB, it + NSB);
       compute(it & 1);
-      if (it + 1 < NKB) stash_set((it + 1) % NSET, (it + 1) & 1);
+      if (it + 1 < NKB) {
+        stash_a((it + 1) % NSA, (it + 1) & 1);
+        stash_b((it + 1) % NSB, (it + 1) & 1);
+      }
     }
   } else {
     if (nkb > 0) {
