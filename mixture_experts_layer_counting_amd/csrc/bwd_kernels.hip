@@ -21,15 +21,18 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Route-weight and shared-gate gradients, one thread per token.
+// Route-weight and shared-gate gradients.
 // dg[k] = <dOut[t], y[t*K+k]> and ds = <dOut[t], shared_y[t]>.  Since
 // y = W2_e act, the same value is <W2_e^T dOut[t], act>, a sum over the
 // intermediate dimension: the dact GEMM's epilogue forms it from its fp32
 // product D = dOut W2_e and the fp32 activation recomputed from the saved
 // gate/up values, as fp64 partial sums per 128-column tile (part[r][nt],
 // nt < Ie / 128).  Here they are added in ascending tile order in fp64.
-// dl[k] = g_k (dg_k - sum_j g_j dg_j) (softmax backward over the selected
-// slots); dz = ds * sg * (1 - sg).
+// One thread per route (a workgroup takes 256 / K whole tokens): it forms
+// its dg[k] and leaves it and its gate in LDS; every thread of a token then
+// forms mean = sum_k' g_k' dg_k' as an fma chain in ascending k' (the same
+// chain in every one of them) and dl = g (dg - mean); the token's first
+// thread forms dz from ds.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const double* __restrict__ dgp,
                                                        const double* __restrict__ dsp,
@@ -38,23 +41,25 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const double* __restrict_
                                                        float* __restrict__ dl,
                                                        float* __restrict__ dz, int64_t T, int K,
                                                        int nt_route, int nt_shared, int nt_stride) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= T) return;
+  __shared__ double s_g[256], s_dg[256];
+  const int per = 256 / K;  // tokens per workgroup
+  const int lt = threadIdx.x / K, k = threadIdx.x - lt * K;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * per + lt;
+  const bool live = lt < per && t < T;
+  double dg = 0.0, g = 0.0;
+  if (live) {
+    const double* pr = dgp + (t * K + k) * nt_stride;
+    for (int n = 0; n < nt_route; ++n) dg += pr[n];
+    g = gate[t * K + k];
+    s_g[threadIdx.x] = g;
+    s_dg[threadIdx.x] = dg;
+  }
+  __syncthreads();
+  if (!live) return;
   double mean = 0.0;
-  for (int k = 0; k < K; ++k) {
-    const double* pr = dgp + (t * K + k) * nt_stride;
-    double dg = 0.0;
-    for (int n = 0; n < nt_route; ++n) dg += pr[n];
-    mean += static_cast<double>(gate[t * K + k]) * dg;
-  }
-  for (int k = 0; k < K; ++k) {
-    const double* pr = dgp + (t * K + k) * nt_stride;
-    double dg = 0.0;
-    for (int n = 0; n < nt_route; ++n) dg += pr[n];
-    const double g = gate[t * K + k];
-    dl[t * K + k] = static_cast<float>(g * (dg - mean));
-  }
-  if (dsp) {
+  for (int q = 0; q < K; ++q) mean = fma(s_g[lt * K + q], s_dg[lt * K + q], mean);
+  dl[t * K + k] = static_cast<float>(g * (dg - mean));
+  if (dsp && k == 0) {
     double ds = 0.0;
     for (int n = 0; n < nt_shared; ++n) ds += dsp[t * nt_stride + n];
     const double s = sg[t];
@@ -774,15 +779,29 @@ __global__ __launch_bounds__(256) void bwd_router_w_kernel(const uint16_t* __res
   double acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-  for (int64_t p = p0; p < p1; ++p) {
-    const int64_t r = sorted_route[p];
-    if (r < 0 || r >= R) continue;
-    const double s = dl[r];
-    const u32x4_t xv = ld16(x + (r / K) * H + c);
+  // eight routes' loads are issued ahead of their additions, which keep the
+  // ascending route order
+  for (int64_t pb = p0; pb < p1; pb += 8) {
+    int64_t rr[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += s * bf16_to_f32(static_cast<uint16_t>(xv[q] & 0xffffu));
-      acc[2 * q + 1] += s * bf16_to_f32(static_cast<uint16_t>(xv[q] >> 16));
+    for (int u = 0; u < 8; ++u) rr[u] = sorted_route[min(pb + u, p1 - 1)];
+    float sv[8];
+    u32x4_t xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = rr[u] >= 0 && rr[u] < R;
+      sv[u] = ok ? dl[rr[u]] : 0.f;
+      xv[u] = ld16(x + (ok ? rr[u] / K : 0) * H + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (pb + u >= p1 || rr[u] < 0 || rr[u] >= R) continue;
+      const double s = sv[u];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += s * bf16_to_f32(static_cast<uint16_t>(xv[u][q] & 0xffffu));
+        acc[2 * q + 1] += s * bf16_to_f32(static_cast<uint16_t>(xv[u][q] >> 16));
+      }
     }
   }
   float* o = dwr + static_cast<int64_t>(e) * H + c;
@@ -791,40 +810,58 @@ __global__ __launch_bounds__(256) void bwd_router_w_kernel(const uint16_t* __res
 }
 
 // Shared-gate weight gradient, pass 1: partial[b][h] = sum over tokens
-// 64b .. 64b+63 (ascending) of dz[t] * x[t][h], fp64.
+// 64b .. 64b+63 (ascending) of dz[t] * x[t][h], fp64.  A thread owns two
+// columns; its tokens' loads are issued eight at a time, ahead of their
+// additions, which keep the ascending token order.
 __global__ __launch_bounds__(256) void bwd_wsg_partial_kernel(const uint16_t* __restrict__ x,
                                                               const float* __restrict__ dz,
                                                               double* __restrict__ partial,
                                                               int64_t T, int H) {
   const int b = blockIdx.x;
-  const int c = blockIdx.y * 2048 + threadIdx.x * 8;
+  const int c = blockIdx.y * 512 + threadIdx.x * 2;
   if (c >= H) return;
-  double acc[8];
+  double a0 = 0.0, a1 = 0.0;
+  const int64_t t0 = static_cast<int64_t>(b) * 64;
+  const int64_t t1 = min(t0 + 64, T);
+  for (int64_t tb = t0; tb < t1; tb += 8) {
+    uint32_t xv[8];
+    float sv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-  const int64_t t1 = min(static_cast<int64_t>(b + 1) * 64, T);
-  for (int64_t t = static_cast<int64_t>(b) * 64; t < t1; ++t) {
-    const double s = dz[t];
-    const u32x4_t xv = ld16(x + t * H + c);
+    for (int u = 0; u < 8; ++u) {
+      const int64_t t = min(tb + u, t1 - 1);
+      xv[u] = *reinterpret_cast<const uint32_t*>(x + t * H + c);
+      sv[u] = dz[t];
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += s * bf16_to_f32(static_cast<uint16_t>(xv[q] & 0xffffu));
-      acc[2 * q + 1] += s * bf16_to_f32(static_cast<uint16_t>(xv[q] >> 16));
+    for (int u = 0; u < 8; ++u) {
+      if (tb + u < t1) {
+        const double sd = sv[u];
+        a0 += sd * bf16_to_f32(static_cast<uint16_t>(xv[u] & 0xffffu));
+        a1 += sd * bf16_to_f32(static_cast<uint16_t>(xv[u] >> 16));
+      }
     }
   }
   double* o = partial + static_cast<int64_t>(b) * H + c;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = acc[j];
+  o[0] = a0;
+  o[1] = a1;
 }
 
-// pass 2: d_w_sgate[h] = sum over blocks b (ascending) of partial[b][h].
+// pass 2: d_w_sgate[h] = sum over blocks b (ascending) of partial[b][h];
+// the partials are loaded sixteen at a time ahead of their additions.
 __global__ __launch_bounds__(256) void bwd_wsg_final_kernel(const double* __restrict__ partial,
                                                             float* __restrict__ dwsg, int nb,
                                                             int H) {
   const int h = blockIdx.x * 256 + threadIdx.x;
   if (h >= H) return;
   double s = 0.0;
-  for (int b = 0; b < nb; ++b) s += partial[static_cast<int64_t>(b) * H + h];
+  for (int b0 = 0; b0 < nb; b0 += 16) {
+    double v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = partial[static_cast<int64_t>(min(b0 + u, nb - 1)) * H + h];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (b0 + u < nb) s += v[u];
+  }
   dwsg[h] = static_cast<float>(s);
 }
 
@@ -1090,7 +1127,8 @@ hipError_t launch_bwd_gate(const double* dgp, const double* dsp, const float* ga
                            float* dl, float* dz, int64_t T, int K, int I, int Is,
                            hipStream_t stream) {
   const int stride = (I > Is ? I : Is) / kBT;
-  bwd_gate_kernel<<<static_cast<unsigned>((T + 255) / 256), 256, 0, stream>>>(
+  const int per = 256 / K;  // tokens per workgroup (K <= 16)
+  bwd_gate_kernel<<<static_cast<unsigned>((T + per - 1) / per), 256, 0, stream>>>(
       dgp, dsp, gate, sg, dl, dz, T, K, I / kBT, Is / kBT, stride);
   return hipGetLastError();
 }
@@ -1237,7 +1275,7 @@ hipError_t launch_bwd_router(const uint16_t* x, const float* dl, const int32_t* 
 hipError_t launch_bwd_wsg(const uint16_t* x, const float* dz, double* partial, float* dwsg, int64_t T,
                           int H, hipStream_t stream) {
   const int nb = static_cast<int>((T + 63) / 64);
-  dim3 grid(static_cast<unsigned>(nb), static_cast<unsigned>((H + 2047) / 2048));
+  dim3 grid(static_cast<unsigned>(nb), static_cast<unsigned>((H + 511) / 512));
   bwd_wsg_partial_kernel<<<grid, 256, 0, stream>>>(x, dz, partial, T, H);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   bwd_wsg_final_kernel<<<static_cast<unsigned>((H + 255) / 256), 256, 0, stream>>>(partial, dwsg, nb, H);
