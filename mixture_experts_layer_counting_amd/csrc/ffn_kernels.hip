@@ -77,13 +77,24 @@ __global__ __launch_bounds__(256, 2) void ffn_up_kernel(
   const int item = xcd_item(blockIdx.x, ntiles[0] * ncol_tiles);
   if (item < 0) return;
   const GroupItem gi = group_item(item, ncol_tiles, tiles, offsets, E, T, ROWS);
-  const int nt = gi.nt, grp = gi.grp, row0 = gi.row0;
+  const int nt = gi.nt, grp = gi.grp;
   const bool shared = grp == E;
   const int Ie = shared ? Is : I;
   if (nt * kUpCols >= Ie) return;
   const int seg0 = gi.seg0;
   const int cnt = gi.cnt;
-  const int rows = min(ROWS, cnt - row0);
+  // 96-row work lists: a group's routes are cut into its ceil(cnt / 96) row
+  // tiles of (almost) equal length, so that the tiles that stream the same
+  // weight slice do the same work per K block and stay close enough for the
+  // later ones to find it in L2 (a row's arithmetic does not depend on its
+  // tile)
+  int row0 = gi.row0, span = ROWS;
+  if constexpr (MBT == kUpTallRows / 32) {
+    const int nrt = max(1, (cnt + ROWS - 1) / ROWS);
+    span = (cnt + nrt - 1) / nrt;  // <= ROWS
+    row0 = (gi.row0 / ROWS) * span;
+  }
+  const int rows = min(span, cnt - row0);
   // the group's only row tile reads each of its weights once: stream them
   const bool wstream = cnt <= ROWS;
   if (rows <= 0) return;
