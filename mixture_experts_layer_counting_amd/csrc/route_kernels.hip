@@ -363,11 +363,11 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // largest untaken logit (a wave maximum of order-preserving keys), ties going
 // to the lower expert id; that gives the stable descending order with ties
 // to the lower id.  Gates: w_k = exp(l_k - l_0), summed in slot order from
-// zero, g_k = w_k / sum.  With w_sgate given, the same wave also computes
-// the token's shared-expert gate.
+// zero, g_k = w_k / sum.  With w_sgate given, waves 4..7 of the workgroup
+// compute the shared-expert gates of its four tokens, beside the selection.
 // ---------------------------------------------------------------------------
 template <int NQ>
-__global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict__ src, int nchunk,
+__global__ __launch_bounds__(512) void topk_gate_kernel(const float* __restrict__ src, int nchunk,
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ logits_out,
                                                         int32_t* __restrict__ topk_idx,
@@ -377,8 +377,13 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
                                                         float* __restrict__ sg, int64_t T, int H,
                                                         int E, int K) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + ((threadIdx.x >> 6) & 3);
   if (t >= T) return;
+  if (threadIdx.x >= 256) {  // a shared-gate wave (launched only with w_sgate)
+    const float g = shared_gate_of_row(x + t * H, w_sgate, H, lane);
+    if (lane == 0) sg[t] = g;
+    return;
+  }
   const int nq = E >> 6;  // logits per lane, <= NQ
   // loads are issued in batches, unconditionally (indices clamped into
   // range, surplus values unused), so that their latencies overlap
@@ -455,10 +460,6 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
   if (lane < K) {
     topk_idx[t * K + lane] = my_id;
     topk_gate[t * K + lane] = w / sum;
-  }
-  if (w_sgate) {
-    const float g = shared_gate_of_row(x + t * H, w_sgate, H, lane);
-    if (lane == 0) sg[t] = g;
   }
 }
 
@@ -876,8 +877,8 @@ hipError_t launch_topk_gate(const float* src, int nchunk, const float* bias, flo
   const unsigned grid = static_cast<unsigned>((T + 3) / 4);
   const int nq = E / 64;
 #define MOE_TOPK(NQ)                                                                           \
-  topk_gate_kernel<NQ><<<grid, 256, 0, stream>>>(src, nchunk, bias, logits_out, topk_idx, topk_gate, \
-                                                 x, w_sgate, sg, T, H, E, K)
+  topk_gate_kernel<NQ><<<grid, w_sgate ? 512 : 256, 0, stream>>>(src, nchunk, bias, logits_out, topk_idx, \
+                                                                 topk_gate, x, w_sgate, sg, T, H, E, K)
   if (nq <= 2)
     MOE_TOPK(2);
   else if (nq <= 4)
