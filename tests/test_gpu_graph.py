@@ -3,7 +3,8 @@ replayed several times with other eager work and synchronisations between
 the replays, every replay bit-identical to an eager call (the library
 enqueues only kernel launches on the caller's stream: no memset, no
 allocation, no host sync).  Also for moe_forward_noalloc, whose callers are
-the ones that capture, and for the LoRA backward."""
+the ones that capture, for the LoRA backward and for the forwards with FP8
+expert weights and with LoRA adapters."""
 import pytest
 import torch
 
@@ -227,3 +228,68 @@ def test_forward_side_streams_graph_replays_match_eager():
         assert torch.equal(bits(out32), bits(want.out32)), f"replay {i}: out_f32"
         assert torch.equal(out16, want.out16), f"replay {i}: out_bf16"
         gpu_forward(cfg, w, other if i % 2 else xd)
+
+
+@pytest.mark.parametrize("variant", ["mx", "lora"])
+def test_mx_and_lora_forward_graph_replays_match_eager(variant):
+    """moe_forward_mx (block-scaled FP8 expert weights) and moe_forward_lora
+    captured once on the 256-token layer and replayed four times on
+    alternating inputs, with eager forwards between the replays: every
+    replay equals an eager call bit for bit."""
+    import workloads.lora as WL
+    import workloads.mx as MX
+    from tests.test_gpu_mx import mx_weights
+    cfg, layer, x = load_cfg("tiny")
+    xd = dev_bits(x)
+    other = dev_bits(W.tokens(cfg, stream=W.S_COMPANION, index=25))
+    d = dims_of(cfg)
+    if variant == "mx":
+        wm = mx_weights(layer, MX.mx_layer(layer))
+        ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, DEV)
+
+        def fwd(xin, routes, saved, out32, out16, stream):
+            return m.moe_forward_mx(d, wm, xin, routes, saved, out32, out16, ws, stream)
+    else:
+        w = dev_weights(layer)
+        ad = WL.lora_adapters(cfg)
+        lo = m.Lora(rank=ad["rank"], scale=ad["scale"], a13=dev_bits(ad["a13"]), b13=dev_bits(ad["b13"]),
+                    a2=dev_bits(ad["a2"]), b2=dev_bits(ad["b2"]))
+        ws = m.alloc_workspace(d, m.MOE_OP_FORWARD_LORA, DEV)
+
+        def fwd(xin, routes, saved, out32, out16, stream):
+            return m.moe_forward_lora(d, w, lo, xin, routes, saved, out32, out16, ws, stream)
+
+    def alloc():
+        return (m.alloc_routes(d, DEV), m.alloc_saved(d, DEV),
+                torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV),
+                torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV))
+
+    def eager(xin):
+        r, sv, o32, o16 = alloc()
+        m.check(fwd(xin, r, sv, o32, o16, None), "eager forward")
+        torch.cuda.synchronize()
+        return r, sv, o32, o16
+
+    ref = {0: eager(xd), 1: eager(other)}
+    xin = xd.clone()
+    routes, saved, out32, out16 = alloc()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.check(fwd(xin, routes, saved, out32, out16, s), "warm-up")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say(f"case: tiny, capture moe_forward_{variant}")
+    with torch.cuda.graph(graph, stream=s):
+        m.check(fwd(xin, routes, saved, out32, out16, torch.cuda.current_stream()), "captured forward")
+    for i in range(4):
+        xin.copy_(other if i % 2 else xd)
+        out32.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        wr, wsv, w32, w16 = ref[i % 2]
+        assert torch.equal(routes.topk_idx, wr.topk_idx), f"replay {i}: routes"
+        assert torch.equal(bits(saved.y), bits(wsv.y)), f"replay {i}: route rows"
+        assert torch.equal(bits(out32), bits(w32)), f"replay {i}: out_f32"
+        assert torch.equal(out16, w16), f"replay {i}: out_bf16"
+        eager(xd if i % 2 else other)
