@@ -3,8 +3,9 @@ replayed several times with other eager work and synchronisations between
 the replays, every replay bit-identical to an eager call (the library
 enqueues only kernel launches on the caller's stream: no memset, no
 allocation, no host sync).  Also for moe_forward_noalloc, whose callers are
-the ones that capture, for the LoRA backward and for the forwards with FP8
-expert weights and with LoRA adapters."""
+the ones that capture, for the LoRA backward, for the forwards with FP8
+expert weights and with LoRA adapters, and for the four stage calls
+captured as one graph."""
 import pytest
 import torch
 
@@ -293,3 +294,49 @@ def test_mx_and_lora_forward_graph_replays_match_eager(variant):
         assert torch.equal(bits(out32), bits(w32)), f"replay {i}: out_f32"
         assert torch.equal(out16, w16), f"replay {i}: out_bf16"
         eager(xd if i % 2 else other)
+
+
+def test_staged_calls_graph_replays_match_forward():
+    """The four stage calls (moe_route, moe_permute, moe_grouped_ffn,
+    moe_combine) captured as one graph on the 1024-token layer: four replays
+    on alternating inputs equal moe_forward's bits."""
+    cfg, layer, x = load_cfg("moe1k")
+    w = dev_weights(layer)
+    xd = dev_bits(x)
+    other = dev_bits(W.tokens(cfg, stream=W.S_COMPANION, index=26))
+    d = dims_of(cfg)
+    ws = m.alloc_workspace(d, m.MOE_OP_FORWARD, DEV)
+    routes = m.alloc_routes(d, DEV)
+    saved = m.alloc_saved(d, DEV)
+    out32 = torch.empty(d.tokens, d.hidden, dtype=torch.float32, device=DEV)
+    out16 = torch.empty(d.tokens, d.hidden, dtype=torch.int16, device=DEV)
+    xin = xd.clone()
+
+    def staged(stream):
+        m.check(m.moe_route(d, xin, w, routes, ws, stream), "moe_route")
+        m.check(m.moe_permute(d, routes, ws, stream), "moe_permute")
+        m.check(m.moe_grouped_ffn(d, xin, w, routes, saved, ws, stream), "moe_grouped_ffn")
+        m.check(m.moe_combine(d, routes, saved, out32, out16, stream), "moe_combine")
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        staged(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say("case: moe1k, capture moe_route + moe_permute + moe_grouped_ffn + moe_combine")
+    with torch.cuda.graph(graph, stream=s):
+        staged(torch.cuda.current_stream())
+    ref = gpu_forward(cfg, w, xd)
+    ref_other = gpu_forward(cfg, w, other)
+    for i in range(4):
+        xin.copy_(other if i % 2 else xd)
+        out32.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = ref_other if i % 2 else ref
+        assert torch.equal(routes.topk_idx, want.routes.topk_idx), f"replay {i}: routes"
+        assert torch.equal(bits(out32), bits(want.out32)), f"replay {i}: out_f32"
+        assert torch.equal(out16, want.out16), f"replay {i}: out_bf16"
+        gpu_forward(cfg, w, other if i % 2 else xd)
+    assert m.moe_last_device_error(ws) == m.MOE_OK
