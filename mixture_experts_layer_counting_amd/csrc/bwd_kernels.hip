@@ -28,11 +28,12 @@ namespace moe {
 // product D = dOut W2_e and the fp32 activation recomputed from the saved
 // gate/up values, as fp64 partial sums per 128-column tile (part[r][nt],
 // nt < Ie / 128).  Here they are added in ascending tile order in fp64.
+// dl[k] = g_k (dg_k - sum_j g_j dg_j) (softmax backward over the selected
+// slots); dz = ds * sg * (1 - sg).
 // One thread per route (a workgroup takes 256 / K whole tokens): it forms
 // its dg[k] and leaves it and its gate in LDS; every thread of a token then
-// forms mean = sum_k' g_k' dg_k' as an fma chain in ascending k' (the same
-// chain in every one of them) and dl = g (dg - mean); the token's first
-// thread forms dz from ds.
+// forms sum_j g_j dg_j as an fma chain in ascending j (the same chain in
+// every one of them) and its dl[k]; the token's first thread forms dz.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const double* __restrict__ dgp,
                                                        const double* __restrict__ dsp,
