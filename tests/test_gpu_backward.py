@@ -6,7 +6,8 @@ to the layer's elementwise rule |gpu - ref| <= 5e-5 + 1e-3 |ref| against the
 plain FP64 oracle (RL-Kernel pull request 557 page, contract commit,
 Backward bullet; the prior-art table's "Max abs vs FP64" column).  The one
 exception is assert_grad_close's split, used only where the method's fp32
-forward values alone are outside the rule (the hidden-16384 edge shape).  Beside
+forward values alone are outside the rule (the hidden-16384 edge shape,
+and the router gradient when every token routes to the same experts).  Beside
 each check the test prints the same ratio for two splits of the error: the
 GPU against an oracle fed the GPU's own saved fp32 forward values -- gate/up
 pre-activations, route gates, shared gate -- (the backward kernels' own
