@@ -70,13 +70,16 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const double* __restrict_
 
 // ---------------------------------------------------------------------------
 // Grouped GEMMs of the expert backward: D[m][n] = sum_k A[m][k] B[k][n] over
-// 128x128 output tiles and 32-wide K blocks; four waves in a 2x2 grid, each
-// owning a 64x64 block (2x2 MFMA 32x32x16 blocks) accumulated in fp32 on the
-// matrix cores.
+// 32-wide K blocks, accumulated in fp32 on the matrix cores (MFMA 32x32x16).
+// The input-gradient GEMMs (kDact, kDx: bwd_gemm_kernel) take 128x128
+// output tiles, four waves in a 2x2 grid each owning a 64x64 block; the
+// weight gradients (kDw2, kDw13: bwd_wgrad_kernel) take 256x128 / 128x256
+// tiles, described with that kernel.
 //
-// Operands are staged in LDS, two stages: the next K block's global loads are
-// issued before the current block's MFMAs and stored to the other stage after
-// them, so one barrier per block separates the stages.  Two LDS layouts:
+// bwd_gemm_kernel stages its operands in LDS, two stages: the next K block's
+// global loads are issued before the current block's MFMAs and stored to the
+// other stage after them, so one barrier per block separates the stages.
+// Two LDS layouts:
 //   * [row][k] (64-byte rows, XOR-swizzled 16-byte pieces: rk_off) for
 //     sources stored k-contiguous (the routed or token rows of a dgrad);
 //     fragments are 16-byte LDS loads;
@@ -108,13 +111,13 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const double* __restrict_
 //   kDw13: m = j < 2Ie, n = h < H, k = p.  A = dGU planes [p][j] ([k][col]);
 //          B = x[t(p)][h] ([k][col], gathered rows).  Epilogue: dW13_g[j][h].
 // The K order of every output element is fixed: K blocks in ascending order,
-// in each block K step 0 then 1, and in each step the planes hi, lo.  A
+// in each block K step 0 then 1, and in each step the planes in order.  A
 // dgrad row's result therefore depends only on its own row and its expert,
 // never on the batch.
 // ---------------------------------------------------------------------------
 enum BwdMode { kDact = 0, kDx = 1, kDw2 = 2, kDw13 = 3 };
 
-constexpr int kBT = kBwdRowsPerTile;  // edge of every output tile (128)
+constexpr int kBT = kBwdRowsPerTile;  // edge of a dgrad tile and of the weight gradients' narrow side (128)
 constexpr int kBwdTokLds = 256;       // weight-gradient segments up to this length keep their tokens in LDS
 constexpr int kDactChunk = 16;        // K blocks per chunk of the general dact loop's two-level sum
 constexpr int kBK = 32;
@@ -198,7 +201,7 @@ struct BwdArgs {
 // Work item of a grouped-GEMM launch.
 struct BwdTile {
   int grp, m0, n0, nt;
-  int rows;  // valid rows (dgrad) / contraction length (wgrad)
+  int rows;  // valid rows (dgrad) / contraction length (weight gradients)
   int seg0;  // first sorted position of the group (0 for the shared group)
   bool shared;
   bool wstream;  // dgrad: the group's only row tile, which reads each weight once
@@ -207,47 +210,24 @@ struct BwdTile {
 
 template <int MODE>
 __device__ __forceinline__ bool bwd_decode(const BwdArgs& a, int g, BwdTile& w) {
+  static_assert(MODE == kDact || MODE == kDx, "dgrad modes");
   const int Imax = a.I > a.Is ? a.I : a.Is;
-  if (MODE == kDact || MODE == kDx) {
-    const int ncol = MODE == kDact ? Imax / kBT : a.H / kBT;
-    const int item = xcd_item(g, a.meta[0] * ncol);
-    if (item < 0) return false;
-    const int tile = item / ncol;
-    w.nt = item - tile * ncol;
-    w.grp = a.tiles[2 * tile];
-    w.m0 = a.tiles[2 * tile + 1];
-    w.n0 = w.nt * kBT;
-    w.shared = w.grp == a.E;
-    w.Ie = w.shared ? a.Is : a.I;
-    if (MODE == kDact && w.n0 >= w.Ie) return false;
-    w.seg0 = w.shared ? 0 : a.offsets[w.grp];
-    const int cnt = w.shared ? static_cast<int>(a.T) : a.offsets[w.grp + 1] - w.seg0;
-    w.rows = min(kBT, cnt - w.m0);
-    w.wstream = cnt <= kBT;
-    return w.rows > 0;
-  }
-  // an empty work list means the caller's offsets failed the check of
-  // ffn_tiles_kernel (with T > 0 there is always a routed tile): no group
-  // segment is trusted then
-  if (a.meta[0] == 0) return false;
-  const int groups = a.E + (a.Is > 0 ? 1 : 0);
-  const int mt = MODE == kDw2 ? a.H / kBT : 2 * Imax / kBT;
-  const int nt = MODE == kDw2 ? Imax / kBT : a.H / kBT;
-  const int item = xcd_item(g, groups * mt * nt);
+  const int ncol = MODE == kDact ? Imax / kBT : a.H / kBT;
+  const int item = xcd_item(g, a.meta[0] * ncol);
   if (item < 0) return false;
-  w.grp = item / (mt * nt);
-  const int rem = item - w.grp * (mt * nt);
-  w.nt = rem % nt;
-  w.m0 = (rem / nt) * kBT;
+  const int tile = item / ncol;
+  w.nt = item - tile * ncol;
+  w.grp = a.tiles[2 * tile];
+  w.m0 = a.tiles[2 * tile + 1];
   w.n0 = w.nt * kBT;
   w.shared = w.grp == a.E;
   w.Ie = w.shared ? a.Is : a.I;
-  if (MODE == kDw2 && w.n0 >= w.Ie) return false;
-  if (MODE == kDw13 && w.m0 >= 2 * w.Ie) return false;
+  if (MODE == kDact && w.n0 >= w.Ie) return false;
   w.seg0 = w.shared ? 0 : a.offsets[w.grp];
-  w.rows = w.shared ? static_cast<int>(a.T) : a.offsets[w.grp + 1] - w.seg0;
-  w.wstream = false;
-  return true;
+  const int cnt = w.shared ? static_cast<int>(a.T) : a.offsets[w.grp + 1] - w.seg0;
+  w.rows = min(kBT, cnt - w.m0);
+  w.wstream = cnt <= kBT;
+  return w.rows > 0;
 }
 
 // token of sorted row p of a group (route ids outside [0, T*K) map to token 0)
@@ -257,12 +237,12 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
   return (r >= 0 && r < a.T * a.K) ? r / a.K : 0;
 }
 
-// NKB > 0 (dgrad modes only) instantiates the K loop fully unrolled for a
-// contraction of NKB blocks with a ring of four register sets, so three K
-// blocks' loads are in flight while one is multiplied; NKB = 0 is the
-// general loop with one block in flight.  Both run the same MFMA sequence on
-// every element.
-// LORA (dgrad modes, routed groups): before the epilogue the routed rows'
+// The input-gradient GEMMs kDact and kDx.  NKB > 0 instantiates the K loop
+// fully unrolled for a contraction of NKB blocks with register rings (below),
+// so several K blocks' loads are in flight while one is multiplied; NKB = 0
+// is the general loop with one block in flight.  Both run the same MFMA
+// sequence on every element.
+// LORA (routed groups): before the epilogue the routed rows'
 // LoRA term is added on the matrix cores, acc = fma(scale, z A, acc) with z
 // the rows' shrink results (bf16 hi + lo, two MFMAs) and A the adapter's
 // rank x 128 slice of the tile's columns (zero past the rank).  kDact takes
@@ -271,22 +251,19 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
 // <D + s A2^T B2^T dOut, act> include the adapter; kDx takes z = B13^T dGU
 // and A13.
 template <int MODE, int NKB = 0, bool LORA = false>
-__global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void bwd_gemm_kernel(const BwdArgs a) {
-  constexpr bool WGRAD = MODE == kDw2 || MODE == kDw13;
-  static_assert(NKB == 0 || !WGRAD, "the unrolled loop is for the dgrad modes");
+__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
+  static_assert(MODE == kDact || MODE == kDx, "dgrad modes");
   // unrolled dgrad: register rings of NSA K blocks for the routed or token
   // rows (A: mostly cache hits) and NSB for the expert weight (B: streamed
   // from HBM).  dx keeps more weight blocks in flight (3 + 5 sets measured
   // 676 us at 4096 tokens against 694 for 4 + 4); dact is fastest at 4 + 4
   constexpr int NSA = NKB > 0 ? (MODE == kDx ? 3 : 4) : 1;
   constexpr int NSB = NKB > 0 ? (MODE == kDx ? 5 : 4) : 1;
-  constexpr int NPA = MODE == kDx ? kDxPlanes : (MODE == kDw13 ? kGradPlanes : 1);
-  constexpr int NPB = MODE == kDw2 ? kGradPlanes : 1;
-  constexpr int APLANE = WGRAD ? kRPlane : kKPlane;
+  constexpr int NPA = MODE == kDx ? kDxPlanes : 1;
+  constexpr int NPB = 1;
+  constexpr int APLANE = kKPlane;
   constexpr int STAGE = NPA * APLANE + NPB * kRPlane;
-  // weight gradients (short contractions): one LDS stage and two barriers
-  // per K block, which leaves room for four workgroups per CU
-  constexpr int NSTAGE = WGRAD ? 1 : 2;
+  constexpr int NSTAGE = 2;
   // the epilogue stages a 64-row half of the fp32 tile (stride kBT + 4) in
   // the same area
   constexpr int EPI = 64 * (kBT + 4) * 2;
@@ -317,37 +294,32 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
     }
   }
 
-  int kdim;
-  if (MODE == kDact) kdim = a.H;
-  else if (MODE == kDx) kdim = 2 * Ie;
-  else kdim = w.rows;
+  const int kdim = MODE == kDact ? a.H : 2 * Ie;
   const int nkb = NKB > 0 ? NKB : (kdim + kBK - 1) / kBK;
 
-  // ---- load roles.  [row][k] operand: rows lr + 64c, 8 k at lc.
-  // [k][col] operands: k rows kr + 16c, 8 columns at tc.
+  // ---- load roles.  [row][k] operand (A): rows lr + 64c, 8 k at lc.
+  // [k][col] operand (B): k rows kr + 16c, 8 columns at tc.
   const int lr = tid >> 2, lc = (tid & 3) * 8;
   const int kr = tid >> 4, tc = (tid & 15) * 8;
 
   // dgrad A: element offsets of this thread's two rows in the source
   int64_t a_off[2] = {0, 0};
   const uint16_t* a_base[NPA];
-  if (!WGRAD) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int rr = min(lr + 64 * c, w.rows - 1);
-      if (MODE == kDact) {
-        a_off[c] = bwd_token(a, w, static_cast<int64_t>(w.seg0) + w.m0 + rr) * a.H;
-      } else {
-        const int64_t rowp = w.shared ? (w.m0 + rr) : (static_cast<int64_t>(w.seg0) + w.m0 + rr);
-        a_off[c] = rowp * 2 * Ie;
-      }
-    }
+  for (int c = 0; c < 2; ++c) {
+    const int rr = min(lr + 64 * c, w.rows - 1);
     if (MODE == kDact) {
-      a_base[0] = a.dout;
+      a_off[c] = bwd_token(a, w, static_cast<int64_t>(w.seg0) + w.m0 + rr) * a.H;
     } else {
-#pragma unroll
-      for (int q = 0; q < NPA; ++q) a_base[q] = w.shared ? a.sdgu[q] : a.dgu[q];
+      const int64_t rowp = w.shared ? (w.m0 + rr) : (static_cast<int64_t>(w.seg0) + w.m0 + rr);
+      a_off[c] = rowp * 2 * Ie;
     }
+  }
+  if (MODE == kDact) {
+    a_base[0] = a.dout;
+  } else {
+#pragma unroll
+    for (int q = 0; q < NPA; ++q) a_base[q] = w.shared ? a.sdgu[q] : a.dgu[q];
   }
   // dgrad B: the expert's weight, rows indexed by k
   const uint16_t* wbase = nullptr;
@@ -361,58 +333,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
     wcols = a.H;
   }
 
-  // wgrad: token of each of this thread's two k rows in the block being
-  // fetched next (-1: beyond the segment); the gathered operand's rows.  A
-  // segment of at most kBwdTokLds rows has all its tokens read into LDS
-  // once, so later blocks' gathers wait on one LDS read instead of a global
-  // load.
-  __shared__ int s_tok[WGRAD ? kBwdTokLds : 1];
-  const bool tok_lds = WGRAD && w.rows <= kBwdTokLds;
-  int64_t tok[2] = {-1, -1};
-  auto wg_tokens = [&](int kb, int64_t (&t)[2]) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int kk = kb * kBK + kr + 16 * c;
-      t[c] = kk < w.rows ? (tok_lds ? static_cast<int64_t>(s_tok[kk])
-                                    : bwd_token(a, w, static_cast<int64_t>(w.seg0) + kk))
-                         : -1;
-    }
-  };
-
   u32x4_t ra_set[NSA][NPA][2], rb_set[NSB][NPB][2];
-  // wgrad operands of K block kb: the one stored in route order (dGU or
-  // g*act planes, rows p) and the one gathered by token (dOut or x rows)
-  auto fetch_plain = [&](int set, int kb) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int kk = kb * kBK + kr + 16 * c;
-      const bool in = kk < w.rows;
-      const int64_t rowp = w.shared ? kk : static_cast<int64_t>(w.seg0) + kk;
-      if (MODE == kDw2) {
-        // B = g*act planes [p][n0 + tc]
-#pragma unroll
-        for (int q = 0; q < NPB; ++q)
-          rb_set[set][q][c] = in ? ld16((w.shared ? a.sgact[q] : a.gact[q]) + rowp * Ie + w.n0 + tc)
-                                 : u32x4_t{0u, 0u, 0u, 0u};
-      } else if (MODE == kDw13) {
-        // A = dGU planes [p][m0 + tc]
-#pragma unroll
-        for (int q = 0; q < NPA; ++q)
-          ra_set[set][q][c] = in ? ld16((w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie + w.m0 + tc)
-                                 : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto fetch_gathered = [&](int set, int kb) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bool in = kb * kBK + kr + 16 * c < w.rows;
-      if (MODE == kDw2)  // A = dOut[t(p)][m0 + tc]
-        ra_set[set][0][c] = in ? ld16(a.dout + tok[c] * a.H + w.m0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
-      else if (MODE == kDw13)  // B = x[t(p)][n0 + tc]
-        rb_set[set][0][c] = in ? ld16(a.x + tok[c] * a.H + w.n0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
   // dgrad operands of K block kb: A (routed or token rows) and B (weight)
   auto fetch_a = [&](int set, int kb) {
 #pragma unroll
@@ -428,23 +349,15 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
     }
   };
   auto fetch_set = [&](int set, int kb) {
-    if (!WGRAD) {
-      fetch_a(set, kb);
-      fetch_b(set, kb);
-      return;
-    }
-    fetch_plain(set, kb);
-    fetch_gathered(set, kb);
+    fetch_a(set, kb);
+    fetch_b(set, kb);
   };
   auto stash_a = [&](int set, int stage) {
     uint16_t* s = smem + stage * STAGE;
 #pragma unroll
     for (int q = 0; q < NPA; ++q)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        if (!WGRAD) st16(s + q * APLANE + rk_off(lr + 64 * c, lc >> 3), ra_set[set][q][c]);
-        else st16(s + q * APLANE + rc_off(kr + 16 * c, tc), ra_set[set][q][c]);
-      }
+      for (int c = 0; c < 2; ++c) st16(s + q * APLANE + rk_off(lr + 64 * c, lc >> 3), ra_set[set][q][c]);
   };
   auto stash_b = [&](int set, int stage) {
     uint16_t* s = smem + stage * STAGE;
@@ -472,12 +385,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int q = 0; q < NPA; ++q) {
-          if (!WGRAD)
-            fa[mb][q] = ld16(s + q * APLANE + rk_off(wm * 64 + mb * 32 + i, 2 * st + half));
-          else
-            fa[mb][q] = frag_tr(s + q * APLANE, 16 * st, wm * 64 + mb * 32, lane);
-        }
+        for (int q = 0; q < NPA; ++q) fa[mb][q] = ld16(s + q * APLANE + rk_off(wm * 64 + mb * 32 + i, 2 * st + half));
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -486,11 +394,8 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          // at most one operand has several planes
 #pragma unroll
           for (int q = 0; q < NPA; ++q) acc[mb][nb] = mfma32x32x16(fa[mb][q], fb[nb][0], acc[mb][nb]);
-#pragma unroll
-          for (int q = 1; q < NPB; ++q) acc[mb][nb] = mfma32x32x16(fa[mb][0], fb[nb][q], acc[mb][nb]);
         }
     }
   };
@@ -518,21 +423,8 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
     }
   } else {
     if (nkb > 0) {
-      if constexpr (WGRAD) {
-        // the route-ordered operand of block 0 is in flight while the
-        // segment's tokens are read
-        fetch_plain(0, 0);
-        if (tok_lds) {
-          if (tid < w.rows) s_tok[tid] = static_cast<int>(bwd_token(a, w, static_cast<int64_t>(w.seg0) + tid));
-          __syncthreads();
-        }
-        wg_tokens(0, tok);
-        fetch_gathered(0, 0);
-      } else {
-        fetch_set(0, 0);
-      }
+      fetch_set(0, 0);
       stash_set(0, 0);
-      if (WGRAD && nkb > 1) wg_tokens(1, tok);
     }
     // dact over a long hidden size: the matrix cores accumulate each chunk
     // of kDactChunk K blocks from zero and the chunk sums are added in
@@ -548,18 +440,11 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
     }
     for (int it = 0; it < nkb; ++it) {
       __syncthreads();
-      const int cur = NSTAGE == 2 ? (it & 1) : 0;
+      const int cur = it & 1;
       const bool more = it + 1 < nkb;
-      // dgrad: the next block's loads are in flight during this block's
-      // MFMAs.  Weight gradients issue them after the MFMAs, so that their
-      // registers and the fragments' are never live together (this fits
-      // four workgroups per CU; their contractions are a few blocks long)
-      if (more && !WGRAD) fetch_set(0, it + 1);
+      // the next block's loads are in flight during this block's MFMAs
+      if (more) fetch_set(0, it + 1);
       compute(cur);
-      if (more && WGRAD) {
-        fetch_set(0, it + 1);
-        if (it + 2 < nkb) wg_tokens(it + 2, tok);
-      }
       if (CHUNKED && (it + 1) % kDactChunk == 0) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -570,10 +455,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
             acc[mb][nb] = zero16();
           }
       }
-      if (more) {
-        if (NSTAGE == 1) __syncthreads();  // every wave is done reading the stage
-        stash_set(0, NSTAGE == 2 ? cur ^ 1 : 0);
-      }
+      if (more) stash_set(0, cur ^ 1);
     }
     if constexpr (CHUNKED) {
 #pragma unroll
@@ -714,7 +596,7 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
     return;
   }
 
-  // ---- epilogue: the 128x128 fp32 tile goes through LDS one 64-row half at
+  // ---- dx epilogue: the 128x128 fp32 tile goes through LDS one 64-row half at
   // a time (waves with wm == half write their accumulators), then each row
   // leaves as 16-byte pieces, 512 contiguous bytes per row per 32 lanes.
   constexpr int ES = kBT + 4;  // fp32 row stride of a staged half
@@ -739,21 +621,232 @@ __global__ __launch_bounds__(256, (MODE == kDw2 || MODE == kDw13) ? 4 : 2) void 
       const int lrow = hh * 64 + r;
       const u32x4_t val = ld16(ep + r * ES + piece * 4);
       const int col = w.n0 + piece * 4;
-      if (MODE == kDx) {
-        if (lrow >= w.rows) continue;
-        if (w.shared) {
-          st16_nt(a.dx_shared + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
-        } else {
-          const int64_t rt = a.sorted_route[static_cast<int64_t>(w.seg0) + w.m0 + lrow];
-          if (rt >= 0 && rt < a.T * a.K) st16_nt(a.dx_route + rt * a.H + col, val);
-        }
-      } else if (MODE == kDw2) {
-        float* o = w.shared ? a.dws2 : a.dw2 + static_cast<int64_t>(w.grp) * a.H * a.I;
-        st16_nt(o + static_cast<int64_t>(w.m0 + lrow) * Ie + col, val);
+      if (lrow >= w.rows) continue;
+      if (w.shared) {
+        st16_nt(a.dx_shared + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
       } else {
-        float* o = w.shared ? a.dws13 : a.dw13 + static_cast<int64_t>(w.grp) * 2 * a.I * a.H;
-        st16_nt(o + static_cast<int64_t>(w.m0 + lrow) * a.H + col, val);
+        const int64_t rt = a.sorted_route[static_cast<int64_t>(w.seg0) + w.m0 + lrow];
+        if (rt >= 0 && rt < a.T * a.K) st16_nt(a.dx_route + rt * a.H + col, val);
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Expert weight gradients on wide tiles.  One workgroup of four waves per
+// output tile: kDw13 128 x 256 (gate/up rows j x hidden columns h), kDw2
+// 256 x 128 (hidden rows h x intermediate columns i).  Of the two operands
+// of each K block, the one stored in route order as kGradPlanes bf16 planes
+// (dGU for kDw13, g*act for kDw2; 24 KB per block) spans 128 of the tile's
+// edge and the gathered single-plane one (x rows for kDw13, dOut rows for
+// kDw2; 16 KB) spans the 256-wide edge, so the three-plane operand is read
+// once for twice the output of a 128 x 128 tile.  Waves: 2 x 2, each owning
+// 64 x 128 (kDw13) or 128 x 64 (kDw2), i.e. eight 32x32 accumulators.  The
+// next K block's loads are in flight in registers while a block is
+// multiplied (one LDS stage, two workgroups per CU).  The MFMA sequence of
+// every output element is that of the 128 x 128 kernel: K blocks ascending,
+// K steps 0 then 1, planes hi, mid, lo.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
+  static_assert(MODE == kDw2 || MODE == kDw13, "weight-gradient modes only");
+  constexpr bool W13 = MODE == kDw13;
+  constexpr int TM = W13 ? kBT : 2 * kBT;  // tile rows
+  constexpr int TN = W13 ? 2 * kBT : kBT;  // tile columns
+  constexpr int MB = W13 ? 2 : 4;          // 32-row blocks per wave
+  constexpr int NB = W13 ? 4 : 2;          // 32-column blocks per wave
+  // LDS: planes of the route-ordered operand, then the two 128-column halves
+  // of the gathered one, each [32 k][128 columns] (rc_off layout)
+  constexpr int PREG = kGradPlanes * kRPlane;
+  constexpr int STAGE = PREG + 2 * kRPlane;
+  // epilogue: one 64 x 256 (kDw13) or 128 x 128 (kDw2) fp32 half of the tile
+  constexpr int ES = TN + 4;
+  constexpr int EROWS = TM / 2;
+  constexpr int EPI = EROWS * ES * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[STAGE > EPI ? STAGE : EPI];
+  __shared__ int s_tok[kBwdTokLds];
+
+  // ---- work item (group, tile rows m0, tile columns n0)
+  if (a.meta[0] == 0) return;  // caller offsets failed the work-list check
+  const int Imax = a.I > a.Is ? a.I : a.Is;
+  const int groups = a.E + (a.Is > 0 ? 1 : 0);
+  const int mt = W13 ? 2 * Imax / TM : a.H / TM;
+  const int ntl = W13 ? a.H / TN : Imax / TN;
+  const int item = xcd_item(blockIdx.x, groups * mt * ntl);
+  if (item < 0) return;
+  const int grp = item / (mt * ntl);
+  const int rem = item - grp * (mt * ntl);
+  const int m0 = (rem / ntl) * TM, n0 = (rem % ntl) * TN;
+  const bool shared = grp == a.E;
+  const int Ie = shared ? a.Is : a.I;
+  if (!W13 && n0 >= Ie) return;
+  if (W13 && m0 >= 2 * Ie) return;
+  const int seg0 = shared ? 0 : a.offsets[grp];
+  const int rows = shared ? static_cast<int>(a.T) : a.offsets[grp + 1] - seg0;
+  const int nkb = (rows + kBK - 1) / kBK;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;
+  // loader role: k rows kr and kr + 16 of a block, 8 columns at tc
+  const int kr = tid >> 4, tc = (tid & 15) * 8;
+
+  // route-ordered operand: plane q, row p, columns c0 + tc
+  const uint16_t* pbase[kGradPlanes];
+  int64_t pstride;
+  int pc0;
+#pragma unroll
+  for (int q = 0; q < kGradPlanes; ++q)
+    pbase[q] = W13 ? (shared ? a.sdgu[q] : a.dgu[q]) : (shared ? a.sgact[q] : a.gact[q]);
+  pstride = W13 ? 2 * Ie : Ie;
+  pc0 = W13 ? m0 : n0;
+  // gathered operand: token row, columns g0 + 128 h + tc
+  const uint16_t* gsrc = W13 ? a.x : a.dout;
+  const int g0 = W13 ? n0 : m0;
+
+  const bool tok_lds = rows <= kBwdTokLds;
+  auto token_of = [&](int kk) -> int64_t {
+    return tok_lds ? static_cast<int64_t>(s_tok[kk]) : bwd_token(a, BwdTile{grp, 0, 0, 0, rows, seg0, shared, false, Ie},
+                                                              static_cast<int64_t>(seg0) + kk);
+  };
+
+  u32x4_t rp[kGradPlanes][2], rg[2][2];
+  auto fetch_plain = [&](int kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int kk = kb * kBK + kr + 16 * c;
+      const int64_t rowp = static_cast<int64_t>(seg0) + kk;
+#pragma unroll
+      for (int q = 0; q < kGradPlanes; ++q)
+        rp[q][c] = kk < rows ? ld16(pbase[q] + rowp * pstride + pc0 + tc) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  int64_t tok[2] = {0, 0};
+  auto fetch_gathered = [&](int kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool in = kb * kBK + kr + 16 * c < rows;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        rg[h][c] = in ? ld16(gsrc + tok[c] * a.H + g0 + 128 * h + tc) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto next_tokens = [&](int kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int kk = kb * kBK + kr + 16 * c;
+      tok[c] = kk < rows ? token_of(kk) : 0;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int q = 0; q < kGradPlanes; ++q) st16(smem + q * kRPlane + rc_off(kr + 16 * c, tc), rp[q][c]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) st16(smem + PREG + h * kRPlane + rc_off(kr + 16 * c, tc), rg[h][c]);
+    }
+  };
+
+  f32x16_t acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero16();
+
+  auto compute = [&]() {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if constexpr (W13) {
+        // A = dGU planes (rows m), B = x half wn (columns n)
+        u32x4_t fa[MB][kGradPlanes];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int q = 0; q < kGradPlanes; ++q) fa[mb][q] = frag_tr(smem + q * kRPlane, 16 * st, wm * 64 + mb * 32, lane);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const u32x4_t fb = frag_tr(smem + PREG + wn * kRPlane, 16 * st, nb * 32, lane);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int q = 0; q < kGradPlanes; ++q) acc[mb][nb] = mfma32x32x16(fa[mb][q], fb, acc[mb][nb]);
+        }
+      } else {
+        // A = dOut half wm (rows m), B = g*act planes (columns n)
+        u32x4_t fb[NB][kGradPlanes];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int q = 0; q < kGradPlanes; ++q) fb[nb][q] = frag_tr(smem + q * kRPlane, 16 * st, wn * 64 + nb * 32, lane);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4_t fa = frag_tr(smem + PREG + wm * kRPlane, 16 * st, mb * 32, lane);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int q = 0; q < kGradPlanes; ++q) acc[mb][nb] = mfma32x32x16(fa, fb[nb][q], acc[mb][nb]);
+        }
+      }
+    }
+  };
+
+  if (nkb > 0) {
+    // the route-ordered operand of block 0 is in flight while the segment's
+    // tokens are read
+    fetch_plain(0);
+    if (tok_lds) {
+      if (tid < rows) s_tok[tid] = static_cast<int>(bwd_token(a, BwdTile{grp, 0, 0, 0, rows, seg0, shared, false, Ie},
+                                                              static_cast<int64_t>(seg0) + tid));
+      __syncthreads();
+    }
+    next_tokens(0);
+    fetch_gathered(0);
+    stash();
+    if (nkb > 1) next_tokens(1);
+  }
+  for (int it = 0; it < nkb; ++it) {
+    __syncthreads();
+    const bool more = it + 1 < nkb;
+    if (more) {
+      fetch_plain(it + 1);
+      fetch_gathered(it + 1);
+      if (it + 2 < nkb) next_tokens(it + 2);
+    }
+    compute();
+    if (more) {
+      __syncthreads();  // every wave is done reading the stage
+      stash();
+    }
+  }
+
+  // ---- epilogue: the tile leaves through LDS one half at a time (the two
+  // waves with wm == hh stage theirs), then each row as 16-byte pieces
+  float* ep = reinterpret_cast<float*>(smem);
+  const int half = lane >> 5;
+  float* out = W13 ? (shared ? a.dws13 : a.dw13 + static_cast<int64_t>(grp) * 2 * a.I * a.H)
+                   : (shared ? a.dws2 : a.dw2 + static_cast<int64_t>(grp) * a.H * a.I);
+  const int64_t ostride = W13 ? a.H : Ie;
+  constexpr int PIECES = TN / 4;         // 16-byte pieces per tile row
+  constexpr int RPP = 256 / PIECES;      // rows per pass of the workgroup
+  for (int hh = 0; hh < 2; ++hh) {
+    __syncthreads();
+    if (wm == hh) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            ep[(mb * 32 + acc_row(v, half)) * ES + wn * (NB * 32) + nb * 32 + i] = acc[mb][nb][v];
+    }
+    __syncthreads();
+    const int piece = tid % PIECES;
+#pragma unroll
+    for (int j = 0; j < EROWS / RPP; ++j) {
+      const int r = tid / PIECES + RPP * j;
+      st16_nt(out + static_cast<int64_t>(m0 + hh * EROWS + r) * ostride + n0 + piece * 4,
+              ld16(ep + r * ES + piece * 4));
     }
   }
 }
@@ -1224,7 +1317,7 @@ hipError_t launch_bwd_dw2(const BwdLaunch& L, hipStream_t stream) {
   const BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
   const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
-  bwd_gemm_kernel<kDw2><<<rounds(groups * (L.H / kBT) * (Imax / kBT)), 256, 0, stream>>>(a);
+  bwd_wgrad_kernel<kDw2><<<rounds(groups * (L.H / (2 * kBT)) * (Imax / kBT)), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1232,7 +1325,7 @@ hipError_t launch_bwd_dw13(const BwdLaunch& L, hipStream_t stream) {
   const BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
   const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
-  bwd_gemm_kernel<kDw13><<<rounds(groups * (2 * Imax / kBT) * (L.H / kBT)), 256, 0, stream>>>(a);
+  bwd_wgrad_kernel<kDw13><<<rounds(groups * (2 * Imax / kBT) * (L.H / (2 * kBT))), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
