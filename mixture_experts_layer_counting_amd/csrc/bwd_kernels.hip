@@ -633,6 +633,157 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Input gradient per route (kDx) on 128 x 256 tiles, for a contraction of NKB
+// 32-wide blocks (2Ie = 32 NKB for the routed and the shared expert alike).
+// A = dGU planes hi, mid ([row][k] layout, 16 KB per block for 128 rows) is
+// read once for 256 columns of dX; B = W13_g rows k, as two 128-column
+// halves ([k][col] layout, 16 KB per block).  Waves 2 x 2, each owning
+// 64 rows x 128 columns (eight 32x32 accumulators).  Register ring of two
+// K blocks: blocks it + 1 and it + 2 are in flight while block it is
+// multiplied, two LDS stages.  Every element's MFMA sequence is that of
+// bwd_gemm_kernel<kDx>: K blocks ascending, K steps 0 then 1, planes hi, mid.
+// ---------------------------------------------------------------------------
+template <int NKB>
+__global__ __launch_bounds__(256, 2) void bwd_dx_wide_kernel(const BwdArgs a) {
+  constexpr int NP = kDxPlanes;
+  constexpr int TN = 2 * kBT;
+  constexpr int STAGE = NP * kKPlane + 2 * kRPlane;
+  constexpr int ES = TN + 4;  // fp32 row stride of a staged 64-row half
+  constexpr int EPI = 64 * ES * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE > EPI ? 2 * STAGE : EPI];
+
+  // ---- work item: (row tile of the work list, 256-column tile)
+  const int ncol = a.H / TN;
+  const int item = xcd_item(blockIdx.x, a.meta[0] * ncol);
+  if (item < 0) return;
+  const int tile = item / ncol;
+  const int n0 = (item - tile * ncol) * TN;
+  const int grp = a.tiles[2 * tile];
+  const int m0 = a.tiles[2 * tile + 1];
+  const bool shared = grp == a.E;
+  const int Ie = shared ? a.Is : a.I;
+  const int seg0 = shared ? 0 : a.offsets[grp];
+  const int cnt = shared ? static_cast<int>(a.T) : a.offsets[grp + 1] - seg0;
+  const int rows = min(kBT, cnt - m0);
+  if (rows <= 0) return;
+  const bool wstream = cnt <= kBT;  // the group's only row tile reads each weight once
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 31, half = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  // load roles: A rows lr + 64c, 8 k at lc; B k rows kr + 16c, 8 columns at tc
+  const int lr = tid >> 2, lc = (tid & 3) * 8;
+  const int kr = tid >> 4, tc = (tid & 15) * 8;
+
+  int64_t a_off[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int rr = min(lr + 64 * c, rows - 1);  // rows past the tile repeat its last row, unused
+    const int64_t rowp = shared ? (m0 + rr) : (static_cast<int64_t>(seg0) + m0 + rr);
+    a_off[c] = rowp * 2 * Ie;
+  }
+  const uint16_t* a_base[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) a_base[q] = shared ? a.sdgu[q] : a.dgu[q];
+  const uint16_t* wbase = (shared ? a.ws13 : a.w13 + static_cast<int64_t>(grp) * 2 * a.I * a.H) + n0 + tc;
+
+  u32x4_t ra[2][NP][2], rb[2][2][2];
+  auto fetch = [&](int set, int kb) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) ra[set][q][c] = ld16(a_base[q] + a_off[c] + kb * kBK + lc);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint16_t* wp = wbase + static_cast<int64_t>(kb * kBK + kr + 16 * c) * a.H + 128 * h;
+        rb[set][h][c] = wstream ? ld16_nt(wp) : ld16(wp);
+      }
+  };
+  auto stash = [&](int set, int stage) {
+    uint16_t* s = smem + stage * STAGE;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) st16(s + q * kKPlane + rk_off(lr + 64 * c, lc >> 3), ra[set][q][c]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) st16(s + NP * kKPlane + h * kRPlane + rc_off(kr + 16 * c, tc), rb[set][h][c]);
+    }
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero16();
+
+  auto compute = [&](int stage) {
+    const uint16_t* s = smem + stage * STAGE;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      u32x4_t fa[2][NP];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int q = 0; q < NP; ++q) fa[mb][q] = ld16(s + q * kKPlane + rk_off(wm * 64 + mb * 32 + i, 2 * st + half));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x4_t fb = frag_tr(s + NP * kKPlane + wn * kRPlane, 16 * st, nb * 32, lane);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int q = 0; q < NP; ++q) acc[mb][nb] = mfma32x32x16(fa[mb][q], fb, acc[mb][nb]);
+      }
+    }
+  };
+
+  fetch(0, 0);
+  if (NKB > 1) fetch(1, 1);
+  stash(0, 0);
+#pragma unroll
+  for (int it = 0; it < NKB; ++it) {
+    __syncthreads();
+    if (it + 2 < NKB) fetch(it & 1, it + 2);
+    compute(it & 1);
+    if (it + 1 < NKB) stash((it + 1) & 1, (it + 1) & 1);
+  }
+
+  // ---- epilogue: each 64-row half of the tile goes through LDS (the waves
+  // with wm == hh stage theirs); each row leaves as 16-byte pieces, 1 KB
+  // contiguous per row
+  float* ep = reinterpret_cast<float*>(smem);
+  const int piece = tid & 63;
+  for (int hh = 0; hh < 2; ++hh) {
+    __syncthreads();
+    if (wm == hh) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            ep[(mb * 32 + acc_row(v, half)) * ES + wn * 128 + nb * 32 + i] = acc[mb][nb][v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = (tid >> 6) + 4 * j;
+      const int lrow = hh * 64 + r;
+      if (lrow >= rows) continue;
+      const u32x4_t val = ld16(ep + r * ES + piece * 4);
+      const int col = n0 + piece * 4;
+      if (shared) {
+        st16_nt(a.dx_shared + static_cast<int64_t>(m0 + lrow) * a.H + col, val);
+      } else {
+        const int64_t rt = a.sorted_route[static_cast<int64_t>(seg0) + m0 + lrow];
+        if (rt >= 0 && rt < a.T * a.K) st16_nt(a.dx_route + rt * a.H + col, val);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Expert weight gradients on wide tiles.  One workgroup of four waves per
 // output tile: kDw13 128 x 256 (gate/up rows j x hidden columns h), kDw2
 // 256 x 128 (hidden rows h x intermediate columns i).  Of the two operands
@@ -1306,7 +1457,8 @@ hipError_t launch_bwd_dx(const BwdLaunch& L, hipStream_t stream) {
     a.lzq = nullptr;
     a.lbx = nullptr;
   } else if (unrolled) {
-    bwd_gemm_kernel<kDx, 2 * 512 / kBK><<<dx_grid, 256, 0, stream>>>(a);
+    const unsigned wide_grid = rounds(static_cast<int64_t>(L.max_tiles_bwd) * (L.H / (2 * kBT)));
+    bwd_dx_wide_kernel<2 * 512 / kBK><<<wide_grid, 256, 0, stream>>>(a);
   } else {
     bwd_gemm_kernel<kDx><<<dx_grid, 256, 0, stream>>>(a);
   }
