@@ -121,11 +121,12 @@ def layer_work(cfg, touched):
     return flop, byts
 
 
-def traffic_from_profile():
+def traffic_from_profile(workload: str):
     """Measured HBM bytes per ffn_up launch from the committed counter
-    summary, or None if the summary is missing or the kernel source changed
-    since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    summary, or None if the summary is missing, the kernel source changed
+    since the counters were taken, or the timed workload is not the one the
+    counters were taken on (moe1k)."""
+    if workload != "moe1k" or not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
@@ -825,7 +826,7 @@ def main():
     up_ms = main_s["ffn_up_ms"]
     up_bytes = ffn_up_bytes(cfg, main_r["touched"])
     achieved = up_bytes / (up_ms / 1e3) / 1e9
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile(cfg.name)
     line = {
         "metric": METRIC,
         "value": main_s["tokens_per_s"],

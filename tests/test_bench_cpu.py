@@ -1,6 +1,7 @@
 """Host-side checks of bench.py (no GPU): the HIP event wrapper declares full
 signatures (an undeclared 64-bit handle would be truncated to a C int), the
-multi-GPU request is refused with a message, and the byte/flop model."""
+multi-GPU request is refused with a message, the byte/flop model, and that
+measured traffic is reported only for the workload it was measured on."""
 import subprocess
 import sys
 
@@ -28,3 +29,11 @@ def test_algorithmic_work_model():
     assert 3.2e9 < byts < 3.5e9
     up = bench.ffn_up_bytes(cfg, 512)
     assert up > 512 * 4 * 2**20
+
+
+def test_measured_traffic_is_reported_only_for_its_workload():
+    # the committed counter summary covers the 1024-token up projection only
+    for name in ("tiny", "moe8k", "skew16k", "bwd4k"):
+        assert bench.traffic_from_profile(name) is None
+    t = bench.traffic_from_profile("moe1k")
+    assert t is None or 2.0e9 < t < 3.0e9
