@@ -817,16 +817,34 @@ __global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[STAGE > EPI ? STAGE : EPI];
   __shared__ int s_tok[kBwdTokLds];
 
-  // ---- work item (group, tile rows m0, tile columns n0)
+  // ---- work item (group, tile rows m0, tile columns n0).  The shared
+  // expert's tiles contract over all T tokens, the routed ones over a few
+  // blocks of routes: the shared tiles are dealt round-robin to the eight
+  // XCDs and come first in each XCD's order (so they are not all left to the
+  // end of one XCD's range), then each XCD takes a contiguous range of the
+  // routed tiles (so an expert's tiles share its operands in one L2).
   if (a.meta[0] == 0) return;  // caller offsets failed the work-list check
   const int Imax = a.I > a.Is ? a.I : a.Is;
-  const int groups = a.E + (a.Is > 0 ? 1 : 0);
   const int mt = W13 ? 2 * Imax / TM : a.H / TM;
   const int ntl = W13 ? a.H / TN : Imax / TN;
-  const int item = xcd_item(blockIdx.x, groups * mt * ntl);
-  if (item < 0) return;
-  const int grp = item / (mt * ntl);
-  const int rem = item - grp * (mt * ntl);
+  int grp, rem;
+  {
+    const int per_grp = mt * ntl;
+    const int nsh = a.Is > 0 ? per_grp : 0;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int sx = (nsh - xcd + 7) >> 3;  // shared tiles xcd, xcd + 8, ... below nsh
+    if (slot < sx) {
+      grp = a.E;
+      rem = xcd + 8 * slot;
+    } else {
+      const int nr = a.E * per_grp;
+      const int per = (nr + 7) >> 3;
+      const int it = xcd * per + (slot - sx);
+      if (slot - sx >= per || it >= nr) return;
+      grp = it / per_grp;
+      rem = it - grp * per_grp;
+    }
+  }
   const int m0 = (rem / ntl) * TM, n0 = (rem % ntl) * TN;
   const bool shared = grp == a.E;
   const int Ie = shared ? a.Is : a.I;
@@ -1424,6 +1442,13 @@ BwdArgs bwd_args(const BwdLaunch& L) {
 }
 
 unsigned rounds(int64_t items) { return static_cast<unsigned>(((items + 7) / 8) * 8); }
+
+// weight-gradient grid: per XCD, its share of the shared expert's tiles plus
+// its contiguous range of the routed tiles (per_grp tiles per group)
+unsigned wgrad_grid(const BwdLaunch& L, int64_t per_grp) {
+  const int64_t nsh = L.Is > 0 ? per_grp : 0;
+  return static_cast<unsigned>(8 * ((nsh + 7) / 8 + (L.E * per_grp + 7) / 8));
+}
 }  // namespace
 
 hipError_t launch_bwd_dact(const BwdLaunch& L, hipStream_t stream) {
@@ -1468,16 +1493,14 @@ hipError_t launch_bwd_dx(const BwdLaunch& L, hipStream_t stream) {
 hipError_t launch_bwd_dw2(const BwdLaunch& L, hipStream_t stream) {
   const BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
-  bwd_wgrad_kernel<kDw2><<<rounds(groups * (L.H / (2 * kBT)) * (Imax / kBT)), 256, 0, stream>>>(a);
+  bwd_wgrad_kernel<kDw2><<<wgrad_grid(L, (L.H / (2 * kBT)) * (Imax / kBT)), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dw13(const BwdLaunch& L, hipStream_t stream) {
   const BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  const int64_t groups = L.E + (L.Is > 0 ? 1 : 0);
-  bwd_wgrad_kernel<kDw13><<<rounds(groups * (2 * Imax / kBT) * (L.H / (2 * kBT))), 256, 0, stream>>>(a);
+  bwd_wgrad_kernel<kDw13><<<wgrad_grid(L, (2 * Imax / kBT) * (L.H / (2 * kBT))), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
