@@ -794,11 +794,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_wide_kernel(const BwdArgs a) {
 // once for twice the output of a 128 x 128 tile.  Waves: 2 x 2, each owning
 // 64 x 128 (kDw13) or 128 x 64 (kDw2), i.e. eight 32x32 accumulators.  The
 // next K block's loads are in flight in registers while a block is
-// multiplied (one LDS stage, two workgroups per CU).  The MFMA sequence of
+// multiplied (one LDS stage, two workgroups per CU).  A work item is NT
+// tiles of one group, computed one after the other.  The MFMA sequence of
 // every output element is that of the 128 x 128 kernel: K blocks ascending,
 // K steps 0 then 1, planes hi, mid, lo.
 // ---------------------------------------------------------------------------
-template <int MODE>
+template <int MODE, int NT>
 __global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
   static_assert(MODE == kDw2 || MODE == kDw13, "weight-gradient modes only");
   constexpr bool W13 = MODE == kDw13;
@@ -827,29 +828,50 @@ __global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
   const int Imax = a.I > a.Is ? a.I : a.Is;
   const int mt = W13 ? 2 * Imax / TM : a.H / TM;
   const int ntl = W13 ? a.H / TN : Imax / TN;
-  int grp, rem;
+  // A work item is NT consecutive tiles of one group (same rows m0 while
+  // the group's column tiles last), run one after the other: the next
+  // tile's first K block is loaded during the current tile's epilogue, and
+  // the group's tokens are read once.
+  const int per_grp = mt * ntl;
+  const int ppg = (per_grp + NT - 1) / NT;  // items per group
+  int grp, rem0;
   {
-    const int per_grp = mt * ntl;
-    const int nsh = a.Is > 0 ? per_grp : 0;
+    const int nsh = a.Is > 0 ? ppg : 0;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int sx = (nsh - xcd + 7) >> 3;  // shared tiles xcd, xcd + 8, ... below nsh
+    const int sx = (nsh - xcd + 7) >> 3;  // shared items xcd, xcd + 8, ... below nsh
     if (slot < sx) {
       grp = a.E;
-      rem = xcd + 8 * slot;
+      rem0 = xcd + 8 * slot;
     } else {
-      const int nr = a.E * per_grp;
+      const int nr = a.E * ppg;
       const int per = (nr + 7) >> 3;
       const int it = xcd * per + (slot - sx);
       if (slot - sx >= per || it >= nr) return;
-      grp = it / per_grp;
-      rem = it - grp * per_grp;
+      grp = it / ppg;
+      rem0 = it - grp * ppg;
     }
   }
-  const int m0 = (rem / ntl) * TM, n0 = (rem % ntl) * TN;
   const bool shared = grp == a.E;
   const int Ie = shared ? a.Is : a.I;
-  if (!W13 && n0 >= Ie) return;
-  if (W13 && m0 >= 2 * Ie) return;
+  // the item's tiles that exist for this group (a smaller shared expert has
+  // fewer intermediate tiles)
+  int tm0[NT] = {}, tn0[NT] = {};
+  int ntiles = 0;
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int t = rem0 * NT + u;
+    const int mm = (t / ntl) * TM, nn = (t % ntl) * TN;
+    if (t < per_grp && (W13 ? mm < 2 * Ie : nn < Ie)) {
+#pragma unroll
+      for (int w = 0; w < NT; ++w)  // register arrays take constant indices only
+        if (w == ntiles) {
+          tm0[w] = mm;
+          tn0[w] = nn;
+        }
+      ++ntiles;
+    }
+  }
+  if (ntiles == 0) return;
   const int seg0 = shared ? 0 : a.offsets[grp];
   const int rows = shared ? static_cast<int>(a.T) : a.offsets[grp + 1] - seg0;
   const int nkb = (rows + kBK - 1) / kBK;
@@ -860,18 +882,21 @@ __global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
   // loader role: k rows kr and kr + 16 of a block, 8 columns at tc
   const int kr = tid >> 4, tc = (tid & 15) * 8;
 
-  // route-ordered operand: plane q, row p, columns c0 + tc
+  // route-ordered operand: plane q, row p, columns pc0 + tc; gathered
+  // operand: token row, columns g0 + 128 h + tc (pc0, g0: the tile being
+  // fetched)
   const uint16_t* pbase[kGradPlanes];
-  int64_t pstride;
-  int pc0;
 #pragma unroll
   for (int q = 0; q < kGradPlanes; ++q)
     pbase[q] = W13 ? (shared ? a.sdgu[q] : a.dgu[q]) : (shared ? a.sgact[q] : a.gact[q]);
-  pstride = W13 ? 2 * Ie : Ie;
-  pc0 = W13 ? m0 : n0;
-  // gathered operand: token row, columns g0 + 128 h + tc
+  const int64_t pstride = W13 ? 2 * Ie : Ie;
   const uint16_t* gsrc = W13 ? a.x : a.dout;
-  const int g0 = W13 ? n0 : m0;
+  int pc0 = 0, g0 = 0;
+  auto aim = [&](int u) {
+    pc0 = W13 ? tm0[u] : tn0[u];
+    g0 = W13 ? tn0[u] : tm0[u];
+  };
+  aim(0);
 
   const bool tok_lds = rows <= kBwdTokLds;
   auto token_of = [&](int kk) -> int64_t {
@@ -918,10 +943,6 @@ __global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
   };
 
   f32x16_t acc[MB][NB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero16();
 
   auto compute = [&]() {
 #pragma unroll
@@ -974,23 +995,7 @@ __global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
     stash();
     if (nkb > 1) next_tokens(1);
   }
-  for (int it = 0; it < nkb; ++it) {
-    __syncthreads();
-    const bool more = it + 1 < nkb;
-    if (more) {
-      fetch_plain(it + 1);
-      fetch_gathered(it + 1);
-      if (it + 2 < nkb) next_tokens(it + 2);
-    }
-    compute();
-    if (more) {
-      __syncthreads();  // every wave is done reading the stage
-      stash();
-    }
-  }
 
-  // ---- epilogue: the tile leaves through LDS one half at a time (the two
-  // waves with wm == hh stage theirs), then each row as 16-byte pieces
   float* ep = reinterpret_cast<float*>(smem);
   const int half = lane >> 5;
   float* out = W13 ? (shared ? a.dws13 : a.dw13 + static_cast<int64_t>(grp) * 2 * a.I * a.H)
@@ -998,24 +1003,64 @@ __global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
   const int64_t ostride = W13 ? a.H : Ie;
   constexpr int PIECES = TN / 4;         // 16-byte pieces per tile row
   constexpr int RPP = 256 / PIECES;      // rows per pass of the workgroup
-  for (int hh = 0; hh < 2; ++hh) {
-    __syncthreads();
-    if (wm == hh) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+  for (int u = 0; u < NT; ++u) {
+    if (u >= ntiles) break;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            ep[(mb * 32 + acc_row(v, half)) * ES + wn * (NB * 32) + nb * 32 + i] = acc[mb][nb][v];
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero16();
+    for (int it = 0; it < nkb; ++it) {
+      __syncthreads();
+      const bool more = it + 1 < nkb;
+      if (more) {
+        fetch_plain(it + 1);
+        fetch_gathered(it + 1);
+        if (it + 2 < nkb) next_tokens(it + 2);
+      }
+      compute();
+      if (more) {
+        __syncthreads();  // every wave is done reading the stage
+        stash();
+      }
     }
-    __syncthreads();
-    const int piece = tid % PIECES;
+    // the next tile's first K block (the same routes) is in flight during
+    // this tile's epilogue
+    const bool next = u + 1 < ntiles && nkb > 0;
+    if (next) {
+      aim(u + 1);
+      next_tokens(0);
+      fetch_plain(0);
+      fetch_gathered(0);
+    }
+
+    // ---- epilogue: the tile leaves through LDS one half at a time (the two
+    // waves with wm == hh stage theirs), then each row as 16-byte pieces
+    const int m0 = tm0[u], n0 = tn0[u];
+    for (int hh = 0; hh < 2; ++hh) {
+      __syncthreads();
+      if (wm == hh) {
 #pragma unroll
-    for (int j = 0; j < EROWS / RPP; ++j) {
-      const int r = tid / PIECES + RPP * j;
-      st16_nt(out + static_cast<int64_t>(m0 + hh * EROWS + r) * ostride + n0 + piece * 4,
-              ld16(ep + r * ES + piece * 4));
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              ep[(mb * 32 + acc_row(v, half)) * ES + wn * (NB * 32) + nb * 32 + i] = acc[mb][nb][v];
+      }
+      __syncthreads();
+      const int piece = tid % PIECES;
+#pragma unroll
+      for (int j = 0; j < EROWS / RPP; ++j) {
+        const int r = tid / PIECES + RPP * j;
+        st16_nt(out + static_cast<int64_t>(m0 + hh * EROWS + r) * ostride + n0 + piece * 4,
+                ld16(ep + r * ES + piece * 4));
+      }
+    }
+    if (next) {
+      __syncthreads();  // every wave is done reading the staged tile
+      stash();
+      if (nkb > 1) next_tokens(1);
     }
   }
 }
@@ -1443,11 +1488,18 @@ BwdArgs bwd_args(const BwdLaunch& L) {
 
 unsigned rounds(int64_t items) { return static_cast<unsigned>(((items + 7) / 8) * 8); }
 
-// weight-gradient grid: per XCD, its share of the shared expert's tiles plus
-// its contiguous range of the routed tiles (per_grp tiles per group)
-unsigned wgrad_grid(const BwdLaunch& L, int64_t per_grp) {
-  const int64_t nsh = L.Is > 0 ? per_grp : 0;
-  return static_cast<unsigned>(8 * ((nsh + 7) / 8 + (L.E * per_grp + 7) / 8));
+// tiles per weight-gradient work item: dW13 takes two (measured at 4096
+// tokens: 1175 -> 1126 us), dW2 one (two measured 596 -> 722 us)
+template <int MODE>
+constexpr int wgrad_tiles() { return MODE == kDw13 ? 2 : 1; }
+
+// weight-gradient grid: per XCD, its share of the shared expert's items plus
+// its contiguous range of the routed items (per_grp tiles per group, nt tiles
+// per item)
+unsigned wgrad_grid(const BwdLaunch& L, int64_t per_grp, int nt) {
+  const int64_t ppg = (per_grp + nt - 1) / nt;
+  const int64_t nsh = L.Is > 0 ? ppg : 0;
+  return static_cast<unsigned>(8 * ((nsh + 7) / 8 + (L.E * ppg + 7) / 8));
 }
 }  // namespace
 
@@ -1493,14 +1545,16 @@ hipError_t launch_bwd_dx(const BwdLaunch& L, hipStream_t stream) {
 hipError_t launch_bwd_dw2(const BwdLaunch& L, hipStream_t stream) {
   const BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  bwd_wgrad_kernel<kDw2><<<wgrad_grid(L, (L.H / (2 * kBT)) * (Imax / kBT)), 256, 0, stream>>>(a);
+  constexpr int nt = wgrad_tiles<kDw2>();
+  bwd_wgrad_kernel<kDw2, nt><<<wgrad_grid(L, (L.H / (2 * kBT)) * (Imax / kBT), nt), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dw13(const BwdLaunch& L, hipStream_t stream) {
   const BwdArgs a = bwd_args(L);
   const int Imax = L.I > L.Is ? L.I : L.Is;
-  bwd_wgrad_kernel<kDw13><<<wgrad_grid(L, (2 * Imax / kBT) * (L.H / (2 * kBT))), 256, 0, stream>>>(a);
+  constexpr int nt = wgrad_tiles<kDw13>();
+  bwd_wgrad_kernel<kDw13, nt><<<wgrad_grid(L, (2 * Imax / kBT) * (L.H / (2 * kBT)), nt), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
