@@ -19,7 +19,8 @@ tokens (dX rows), sampled experts (their dW13, dW2 and router rows, from
 those experts' own routes) and the shared expert's gradients in full.
 Batch invariance of dX and bit-equality of repeated backwards are checked
 on the tiny layer and on the 4096-token layer's shape, whose kernels (the
-unrolled dgrad instantiations at hidden 2048 / intermediate 512) differ.
+unrolled dact at hidden 2048, the 128 x 256 dx tiles at intermediate 512)
+differ.
 """
 import numpy as np
 import pytest
