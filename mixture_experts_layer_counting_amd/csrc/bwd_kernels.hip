@@ -642,8 +642,12 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
 // K blocks: blocks it + 1 and it + 2 are in flight while block it is
 // multiplied, two LDS stages.  Every element's MFMA sequence is that of
 // bwd_gemm_kernel<kDx>: K blocks ascending, K steps 0 then 1, planes hi, mid.
+// LORA (routed groups): after the K loop the rows' shrink results z = B13^T
+// dGU and the adapter's A13 rows for the tile's 256 columns are staged in
+// the freed LDS, and acc = fma(scale, z A13, acc) with the product taken as
+// z_hi A13 then z_lo A13 on the matrix cores, as in bwd_gemm_kernel.
 // ---------------------------------------------------------------------------
-template <int NKB>
+template <int NKB, bool LORA>
 __global__ __launch_bounds__(256, 2) void bwd_dx_wide_kernel(const BwdArgs a) {
   constexpr int NP = kDxPlanes;
   constexpr int TN = 2 * kBT;
@@ -747,6 +751,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_wide_kernel(const BwdArgs a) {
     if (it + 2 < NKB) fetch(it & 1, it + 2);
     compute(it & 1);
     if (it + 1 < NKB) stash((it + 1) & 1, (it + 1) & 1);
+  }
+
+  if constexpr (LORA) {
+    if (!shared) {
+      // zs [row][hi | lo][kLoraMaxRank] (rows past the tile: zeros), then
+      // lbs [rank][256 columns]
+      uint16_t* zs = smem;
+      uint16_t* lbs = smem + kBT * 2 * kLoraMaxRank;
+      __syncthreads();  // every wave is done with the K loop's stages
+      const uint16_t* z0 = a.lzq + (static_cast<int64_t>(seg0) + m0) * 2 * kLoraMaxRank;
+      for (int q = tid; q < kBT * 4; q += 256)
+        st16(&zs[8 * q], q < rows * 4 ? ld16(z0 + 8 * q) : u32x4_t{0u, 0u, 0u, 0u});
+      const uint16_t* b0 = a.lbx + static_cast<int64_t>(grp) * a.lrank * a.H + n0;
+      for (int q = tid; q < a.lrank * (TN / 8); q += 256) {
+        const int j = q / (TN / 8), c = q - j * (TN / 8);
+        st16(&lbs[j * TN + 8 * c], ld16(b0 + static_cast<int64_t>(j) * a.H + 8 * c));
+      }
+      __syncthreads();
+      u32x4_t zh[2], zl[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int zr = wm * 64 + mb * 32 + i;
+        zh[mb] = ld16(&zs[zr * 2 * kLoraMaxRank + 8 * half]);
+        zl[mb] = ld16(&zs[zr * 2 * kLoraMaxRank + kLoraMaxRank + 8 * half]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        // B[k][n] = A13[k][n0 + col] for k < rank, else 0
+        const int col = wn * 128 + nb * 32 + i;
+        uint32_t bw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j0 = 8 * half + 2 * q;
+          const uint32_t e0 = j0 < a.lrank ? lbs[j0 * TN + col] : 0u;
+          const uint32_t e1 = j0 + 1 < a.lrank ? lbs[(j0 + 1) * TN + col] : 0u;
+          bw[q] = e0 | (e1 << 16);
+        }
+        const u32x4_t b{bw[0], bw[1], bw[2], bw[3]};
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const f32x16_t t = mfma32x32x16(zl[mb], b, mfma32x32x16(zh[mb], b, zero16()));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[mb][nb][v] = fmaf(a.lscale, t[v], acc[mb][nb][v]);
+        }
+      }
+    }
   }
 
   // ---- epilogue: each 64-row half of the tile goes through LDS (the waves
@@ -1529,13 +1579,17 @@ hipError_t launch_bwd_dx(const BwdLaunch& L, hipStream_t stream) {
   if (L.la13) {
     a.lzq = L.lu13;
     a.lbx = L.la13;
-    if (unrolled) bwd_gemm_kernel<kDx, 2 * 512 / kBK, true><<<dx_grid, 256, 0, stream>>>(a);
-    else bwd_gemm_kernel<kDx, 0, true><<<dx_grid, 256, 0, stream>>>(a);
+    if (unrolled) {
+      const unsigned wide_grid = rounds(static_cast<int64_t>(L.max_tiles_bwd) * (L.H / (2 * kBT)));
+      bwd_dx_wide_kernel<2 * 512 / kBK, true><<<wide_grid, 256, 0, stream>>>(a);
+    } else {
+      bwd_gemm_kernel<kDx, 0, true><<<dx_grid, 256, 0, stream>>>(a);
+    }
     a.lzq = nullptr;
     a.lbx = nullptr;
   } else if (unrolled) {
     const unsigned wide_grid = rounds(static_cast<int64_t>(L.max_tiles_bwd) * (L.H / (2 * kBT)));
-    bwd_dx_wide_kernel<2 * 512 / kBK><<<wide_grid, 256, 0, stream>>>(a);
+    bwd_dx_wide_kernel<2 * 512 / kBK, false><<<wide_grid, 256, 0, stream>>>(a);
   } else {
     bwd_gemm_kernel<kDx><<<dx_grid, 256, 0, stream>>>(a);
   }
