@@ -253,12 +253,13 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
 template <int MODE, int NKB = 0, bool LORA = false>
 __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
   static_assert(MODE == kDact || MODE == kDx, "dgrad modes");
-  // unrolled dgrad: register rings of NSA K blocks for the routed or token
+  // the unrolled loop serves dact at hidden 2048 (dx at intermediate 512
+  // runs bwd_dx_wide_kernel): register rings of NSA K blocks for the token
   // rows (A: mostly cache hits) and NSB for the expert weight (B: streamed
-  // from HBM).  dx keeps more weight blocks in flight (3 + 5 sets measured
-  // 676 us at 4096 tokens against 694 for 4 + 4); dact is fastest at 4 + 4
-  constexpr int NSA = NKB > 0 ? (MODE == kDx ? 3 : 4) : 1;
-  constexpr int NSB = NKB > 0 ? (MODE == kDx ? 5 : 4) : 1;
+  // from HBM); dact was fastest at 4 + 4
+  static_assert(NKB == 0 || MODE == kDact, "the unrolled loop is dact's");
+  constexpr int NSA = NKB > 0 ? 4 : 1;
+  constexpr int NSB = NKB > 0 ? 4 : 1;
   constexpr int NPA = MODE == kDx ? kDxPlanes : 1;
   constexpr int NPB = 1;
   constexpr int APLANE = kKPlane;
