@@ -17,6 +17,9 @@ rounding points alone cost).
 The small layers are compared in full; the 4096-token layer on sampled
 tokens (dX rows), sampled experts (their dW13, dW2 and router rows, from
 those experts' own routes) and the shared expert's gradients in full.
+A skewed routing (the skewed workload's router bias at 4096 tokens: busiest
+expert ~600 routes, 100 experts without any) is checked on sampled tokens
+and on its busiest and some random experts.
 Batch invariance of dX and bit-equality of repeated backwards are checked
 on the tiny layer and on the 4096-token layer's shape, whose kernels (the
 unrolled dact at hidden 2048, the 128 x 256 dx tiles at intermediate 512)
@@ -169,6 +172,54 @@ def test_bwd4k_sampled():
         got = getattr(gr, key).cpu().numpy()
         split_report(name, got, sh[key], fed[key])
         assert_close(got, sh[key], name)
+
+
+def test_skewed_backward_sampled():
+    """The skewed workload's router bias (Zipf 1.2, 100 experts switched off)
+    at 4096 tokens: the busiest experts hold several hundred routes (long
+    weight-gradient contractions whose tokens do not fit on chip), the
+    switched-off ones none.  dX on sampled tokens, the three busiest and
+    three random experts' dW13 / dW2 / router rows from their own routes,
+    and zero weight gradients for every expert without routes."""
+    base = W.CONFIGS["skew16k"]
+    cfg = W.MoEConfig(name="skew4k", tokens=4096, hidden=2048, zipf_s=base.zipf_s, zipf_tau=base.zipf_tau,
+                      zipf_off=base.zipf_off, backward=True)
+    layer = W.make_layer(cfg)
+    x = W.tokens(cfg)
+    w = dev_weights(layer)
+    xd = dev_bits(x)
+    dout = W.grad_out(cfg)
+    say("case: skewed routing at 4096 tokens, forward + backward on GPU")
+    g = gpu_forward(cfg, w, xd, training=True)
+    h = g.host()
+    dx32, _, gr = gpu_backward(cfg, w, xd, g, dev_bits(dout))
+    idx = h["idx"]
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.experts)
+    say(f"  busiest expert {counts.max()} routes, {int((counts == 0).sum())} experts without routes")
+    assert counts.max() > 256
+    rng = np.random.default_rng(21)
+    tok = np.unique(np.concatenate([[0, cfg.tokens - 1], rng.choice(cfg.tokens, 30, replace=False)]))
+    fs = O.forward(layer, x[tok], cfg.top_k, forced_idx=idx[tok])
+    compare_routes(idx[tok], O.select_routes(fs["logits"], cfg.top_k), fs["logits"])
+    bs = O.backward(layer, x[tok], fs, dout[tok])
+    assert_close(dx32.cpu().numpy()[tok], bs["dx"], "dX (sampled tokens)")
+    dw13 = gr.d_w13.cpu().numpy()
+    dw2 = gr.d_w2.cpu().numpy()
+    dwr = gr.d_w_router.cpu().numpy()
+    busy = np.argsort(-counts, kind="stable")[:3]
+    used = np.nonzero(counts)[0]
+    experts = list(busy) + list(rng.choice(used, 3, replace=False))
+    for e in experts:
+        te = np.unique(np.nonzero((idx == e).any(axis=1))[0])
+        fe = O.forward(layer, x[te], cfg.top_k, forced_idx=idx[te])
+        rows = np.nonzero(fe["idx"].reshape(-1) == e)[0]
+        r13, r2 = O.expert_weight_grads(layer, x[te], dout[te], fe["idx"], fe["gates"], fe["gu"][rows], int(e))
+        assert_close(dw13[e], r13, f"dW13[{e}] ({len(te)} routes)")
+        assert_close(dw2[e], r2, f"dW2[{e}]")
+        be = O.backward(layer, x[te], fe, dout[te])
+        assert_close(dwr[e], be["d_w_router"][e], f"dW_router[{e}]")
+    empty = np.nonzero(counts == 0)[0]
+    assert not dw13[empty].any() and not dw2[empty].any() and not dwr[empty].any()
 
 
 def bits(t):
