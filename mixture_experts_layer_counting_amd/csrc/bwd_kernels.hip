@@ -847,8 +847,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dx_wide_kernel(const BwdArgs a) {
 // next K block's loads are in flight in registers while a block is
 // multiplied (one LDS stage, two workgroups per CU).  A work item is NT
 // tiles of one group, computed one after the other.  The MFMA sequence of
-// every output element is that of the 128 x 128 kernel: K blocks ascending,
-// K steps 0 then 1, planes hi, mid, lo.
+// every output element is fixed: 32-route K blocks in ascending sorted
+// position, K steps 0 then 1, planes hi, mid, lo; it does not depend on
+// the tile shape or on which workgroup computes the tile.
 // ---------------------------------------------------------------------------
 template <int MODE, int NT>
 __global__ __launch_bounds__(256, 2) void bwd_wgrad_kernel(const BwdArgs a) {
