@@ -237,11 +237,145 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
   return (r >= 0 && r < a.T * a.K) ? r / a.K : 0;
 }
 
-// The input-gradient GEMMs kDact and kDx.  NKB > 0 instantiates the K loop
-// fully unrolled for a contraction of NKB blocks with register rings (below),
-// so several K blocks' loads are in flight while one is multiplied; NKB = 0
-// is the general loop with one block in flight.  Both run the same MFMA
-// sequence on every element.
+// LoRA term of a dgrad tile (routed groups; kDact: z = B2^T dOut with the
+// adapter's A2, kDx: z = B13^T dGU with A13): the tile's rows' shrink
+// results, bf16 hi | lo, into zs [128 rows][2][kLoraMaxRank] (zeros past
+// the tile's rows), and the adapter matrix's rank rows for the tile's 128
+// columns into lbs [rank][128].  nout: the adapter matrix's row length.
+__device__ __forceinline__ void lora_stage_tile(const BwdArgs& a, const BwdTile& w, uint16_t* zs, uint16_t* lbs,
+                                                int64_t nout, int tid) {
+  const uint16_t* z0 = a.lzq + (static_cast<int64_t>(w.seg0) + w.m0) * 2 * kLoraMaxRank;
+  for (int q = tid; q < kBT * 4; q += 256)
+    st16(&zs[8 * q], q < w.rows * 4 ? ld16(z0 + 8 * q) : u32x4_t{0u, 0u, 0u, 0u});
+  const uint16_t* b0 = a.lbx + static_cast<int64_t>(w.grp) * a.lrank * nout + w.n0;
+  for (int q = tid; q < a.lrank * (kBT / 8); q += 256) {
+    const int j = q / (kBT / 8), c = q - j * (kBT / 8);
+    st16(&lbs[j * kBT + 8 * c], ld16(b0 + j * nout + 8 * c));
+  }
+}
+// acc = fma(scale, z A, acc) on a wave's 64 x 64 block (2 x 2 MFMA blocks),
+// the product as z_hi A then z_lo A over the 16 zero-padded rank columns.
+__device__ __forceinline__ void lora_add_tile(const BwdArgs& a, const uint16_t* zs, const uint16_t* lbs,
+                                              f32x16_t (&acc)[2][2], int wm, int wn, int lane) {
+  const int i = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int zr = wm * 64 + mb * 32 + i;
+    const u32x4_t zh = ld16(&zs[zr * 2 * kLoraMaxRank + 8 * half]);
+    const u32x4_t zl = ld16(&zs[zr * 2 * kLoraMaxRank + kLoraMaxRank + 8 * half]);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      // B[k][n] = A[k][n0 + col] for k < rank, else 0
+      const int col = wn * 64 + nb * 32 + i;
+      uint32_t bw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j0 = 8 * half + 2 * q;
+        const uint32_t e0 = j0 < a.lrank ? lbs[j0 * kBT + col] : 0u;
+        const uint32_t e1 = j0 + 1 < a.lrank ? lbs[(j0 + 1) * kBT + col] : 0u;
+        bw[q] = e0 | (e1 << 16);
+      }
+      const u32x4_t b{bw[0], bw[1], bw[2], bw[3]};
+      const f32x16_t t = mfma32x32x16(zl, b, mfma32x32x16(zh, b, zero16()));
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = fmaf(a.lscale, t[v], acc[mb][nb][v]);
+    }
+  }
+}
+
+// dact epilogue of one 64-row half (hh) of a tile and one 128-column group
+// (columns n0 .. n0 + 127, column tile nt of the partial route-weight
+// gradients), from the fp32 GEMM result staged at ep (row stride ES floats):
+// each thread takes 8 consecutive columns of four rows for the SwiGLU
+// backward, so the saved pre-activations are read and the gradient planes
+// written 16 bytes at a time.
+__device__ __forceinline__ void dact_epilogue(const BwdArgs& a, const BwdTile& w, const float* ep, int ES, int n0,
+                                              int nt, int hh, int tid) {
+  const int Ie = w.Ie;
+  const int er = tid >> 4, ec = (tid & 15) * 8;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int lrow = hh * 64 + er + 16 * c;
+    if (lrow >= w.rows) continue;
+    float g;
+    int64_t rowp;
+    if (w.shared) {
+      rowp = w.m0 + lrow;
+      g = a.sg[rowp];
+    } else {
+      rowp = static_cast<int64_t>(w.seg0) + w.m0 + lrow;
+      const int64_t r = a.sorted_route[rowp];
+      g = (r >= 0 && r < a.T * a.K) ? a.gate[r] : 0.f;
+    }
+    const int col = n0 + ec;
+    const float* gur = (w.shared ? a.sgu : a.gu) + rowp * 2 * Ie;
+    const f32x4v_t* dsrc = reinterpret_cast<const f32x4v_t*>(ep + (er + 16 * c) * ES + ec);
+    const f32x4v_t d0 = dsrc[0], d1 = dsrc[1];
+    const f32x4v_t g0 = *reinterpret_cast<const f32x4v_t*>(gur + col);
+    const f32x4v_t g1 = *reinterpret_cast<const f32x4v_t*>(gur + col + 4);
+    const f32x4v_t u0 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col);
+    const f32x4v_t u1 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col + 4);
+    uint32_t pg[kGradPlanes][4], pu[kGradPlanes][4], pa[kGradPlanes][4];
+    double dot = 0.0;  // this thread's 8 columns of <D, act>
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float dv = e < 4 ? d0[e] : d1[e - 4];
+      const float gv = e < 4 ? g0[e] : g1[e - 4];
+      const float uv = e < 4 ? u0[e] : u1[e - 4];
+      const float dact = dv * g;
+      const float sgm = 1.0f / (1.0f + expf(-gv));
+      const float dgate = dact * uv * sgm * (1.0f + gv * (1.0f - sgm));
+      const float silu = silu_f32(gv);
+      const float dup = dact * silu;
+      const float act = silu * uv;
+      const float gact = g * act;
+      dot = fma(static_cast<double>(dv), static_cast<double>(act), dot);
+      uint16_t sgp[3], sup[3], sap[3];
+      split3(dgate, sgp);
+      split3(dup, sup);
+      split3(gact, sap);
+      const int sh = 16 * (e & 1);
+#pragma unroll
+      for (int q = 0; q < kGradPlanes; ++q) {
+        if ((e & 1) == 0) {
+          pg[q][e >> 1] = sgp[q];
+          pu[q][e >> 1] = sup[q];
+          pa[q][e >> 1] = sap[q];
+        } else {
+          pg[q][e >> 1] |= static_cast<uint32_t>(sgp[q]) << sh;
+          pu[q][e >> 1] |= static_cast<uint32_t>(sup[q]) << sh;
+          pa[q][e >> 1] |= static_cast<uint32_t>(sap[q]) << sh;
+        }
+      }
+    }
+    // the 16 threads of this row (consecutive lanes) add their partial
+    // sums in a fixed butterfly; the first writes the tile's sum
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 16);
+    if ((tid & 15) == 0) {
+      if (w.shared) {
+        a.dsp[rowp * a.nt_stride + nt] = dot;
+      } else {
+        const int64_t r = a.sorted_route[rowp];
+        if (r >= 0 && r < a.T * a.K) a.dgp[r * a.nt_stride + nt] = dot;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kGradPlanes; ++q) {
+      uint16_t* dq = (w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie;
+      st16(dq + col, u32x4_t{pg[q][0], pg[q][1], pg[q][2], pg[q][3]});
+      st16(dq + Ie + col, u32x4_t{pu[q][0], pu[q][1], pu[q][2], pu[q][3]});
+      st16((w.shared ? a.sgact[q] : a.gact[q]) + rowp * Ie + col,
+           u32x4_t{pa[q][0], pa[q][1], pa[q][2], pa[q][3]});
+    }
+  }
+}
+
+// The input-gradient GEMMs kDact and kDx for the shapes without a
+// specialised kernel (bwd_dact_k64_kernel takes dact at hidden 2048,
+// bwd_dx_wide_kernel dx at intermediate 512): a general K loop with the next
+// block's loads in flight.  dact sums its long contraction in chunks of
+// kDactChunk K blocks (below).
 // LORA (routed groups): before the epilogue the routed rows'
 // LoRA term is added on the matrix cores, acc = fma(scale, z A, acc) with z
 // the rows' shrink results (bf16 hi + lo, two MFMAs) and A the adapter's
@@ -250,16 +384,9 @@ __device__ __forceinline__ int64_t bwd_token(const BwdArgs& a, const BwdTile& w,
 // dact = g (D + s A2^T B2^T dOut) and the route-weight gradient
 // <D + s A2^T B2^T dOut, act> include the adapter; kDx takes z = B13^T dGU
 // and A13.
-template <int MODE, int NKB = 0, bool LORA = false>
+template <int MODE, bool LORA = false>
 __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
   static_assert(MODE == kDact || MODE == kDx, "dgrad modes");
-  // the unrolled loop serves dact at hidden 2048 (dx at intermediate 512
-  // runs bwd_dx_wide_kernel): register rings of NSA K blocks for the token
-  // rows (A: mostly cache hits) and NSB for the expert weight (B: streamed
-  // from HBM); dact was fastest at 4 + 4
-  static_assert(NKB == 0 || MODE == kDact, "the unrolled loop is dact's");
-  constexpr int NSA = NKB > 0 ? 4 : 1;
-  constexpr int NSB = NKB > 0 ? 4 : 1;
   constexpr int NPA = MODE == kDx ? kDxPlanes : 1;
   constexpr int NPB = 1;
   constexpr int APLANE = kKPlane;
@@ -281,22 +408,11 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
   const int wm = wave & 1, wn = wave >> 1;
   const int Ie = w.Ie;
   const bool lora = LORA && !w.shared;  // the shared expert has no adapter
-  if (lora) {
-    // rows past the tile's end get zeros; ordered before the epilogue by the
-    // K loop's barriers
-    const uint16_t* z0 = a.lzq + (static_cast<int64_t>(w.seg0) + w.m0) * 2 * kLoraMaxRank;
-    for (int q = tid; q < kBT * 4; q += 256)
-      st16(&zs[8 * q], q < w.rows * 4 ? ld16(z0 + 8 * q) : u32x4_t{0u, 0u, 0u, 0u});
-    const int64_t nout = MODE == kDact ? a.I : a.H;
-    const uint16_t* b0 = a.lbx + static_cast<int64_t>(w.grp) * a.lrank * nout + w.n0;
-    for (int q = tid; q < a.lrank * (kBT / 8); q += 256) {
-      const int j = q / (kBT / 8), c = q - j * (kBT / 8);
-      st16(&lbs[j * kBT + 8 * c], ld16(b0 + j * nout + 8 * c));
-    }
-  }
+  // ordered before the epilogue by the K loop's barriers
+  if (lora) lora_stage_tile(a, w, zs, lbs, MODE == kDact ? a.I : a.H, tid);
 
   const int kdim = MODE == kDact ? a.H : 2 * Ie;
-  const int nkb = NKB > 0 ? NKB : (kdim + kBK - 1) / kBK;
+  const int nkb = (kdim + kBK - 1) / kBK;
 
   // ---- load roles.  [row][k] operand (A): rows lr + 64c, 8 k at lc.
   // [k][col] operand (B): k rows kr + 16c, 8 columns at tc.
@@ -334,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
     wcols = a.H;
   }
 
-  u32x4_t ra_set[NSA][NPA][2], rb_set[NSB][NPB][2];
+  u32x4_t ra_set[1][NPA][2], rb_set[1][NPB][2];
   // dgrad operands of K block kb: A (routed or token rows) and B (weight)
   auto fetch_a = [&](int set, int kb) {
 #pragma unroll
@@ -401,110 +517,59 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
     }
   };
 
-  if constexpr (NKB > 0) {
-    // dgrad, unrolled: A blocks it + 1 .. it + NSA - 1 and B blocks it + 1
-    // .. it + NSB - 1 in flight while block it is multiplied; the prologue
-    // issues them in K order, A before B within a block
-#pragma unroll
-    for (int q = 0; q < (NSA > NSB ? NSA : NSB) && q < NKB; ++q) {
-      if (q < NSA) fetch_a(q, q);
-      if (q < NSB) fetch_b(q, q);
-    }
+  if (nkb > 0) {
+    fetch_set(0, 0);
     stash_set(0, 0);
+  }
+  // dact over a long hidden size: the matrix cores accumulate each chunk
+  // of kDactChunk K blocks from zero and the chunk sums are added in
+  // ascending order into a second fp32 sum, which keeps the rounding of
+  // the long contraction near that of a kDactChunk * 32-term one
+  constexpr bool CHUNKED = MODE == kDact;
+  f32x16_t tot[2][2];
+  if constexpr (CHUNKED) {
 #pragma unroll
-    for (int it = 0; it < NKB; ++it) {
-      __syncthreads();
-      if (it + NSA < NKB) fetch_a(it % NSA, it + NSA);
-      if (it + NSB < NKB) fetch_b(it % NSB, it + NSB);
-      compute(it & 1);
-      if (it + 1 < NKB) {
-        stash_a((it + 1) % NSA, (it + 1) & 1);
-        stash_b((it + 1) % NSB, (it + 1) & 1);
-      }
-    }
-  } else {
-    if (nkb > 0) {
-      fetch_set(0, 0);
-      stash_set(0, 0);
-    }
-    // dact over a long hidden size: the matrix cores accumulate each chunk
-    // of kDactChunk K blocks from zero and the chunk sums are added in
-    // ascending order into a second fp32 sum, which keeps the rounding of
-    // the long contraction near that of a kDactChunk * 32-term one
-    constexpr bool CHUNKED = MODE == kDact;
-    f32x16_t tot[2][2];
-    if constexpr (CHUNKED) {
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) tot[mb][nb] = zero16();
+  }
+  for (int it = 0; it < nkb; ++it) {
+    __syncthreads();
+    const int cur = it & 1;
+    const bool more = it + 1 < nkb;
+    // the next block's loads are in flight during this block's MFMAs
+    if (more) fetch_set(0, it + 1);
+    compute(cur);
+    if (CHUNKED && (it + 1) % kDactChunk == 0) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) tot[mb][nb] = zero16();
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) tot[mb][nb][v] += acc[mb][nb][v];
+          acc[mb][nb] = zero16();
+        }
     }
-    for (int it = 0; it < nkb; ++it) {
-      __syncthreads();
-      const int cur = it & 1;
-      const bool more = it + 1 < nkb;
-      // the next block's loads are in flight during this block's MFMAs
-      if (more) fetch_set(0, it + 1);
-      compute(cur);
-      if (CHUNKED && (it + 1) % kDactChunk == 0) {
+    if (more) stash_set(0, cur ^ 1);
+  }
+  if constexpr (CHUNKED) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) tot[mb][nb][v] += acc[mb][nb][v];
-            acc[mb][nb] = zero16();
-          }
-      }
-      if (more) stash_set(0, cur ^ 1);
-    }
-    if constexpr (CHUNKED) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[mb][nb][v] = tot[mb][nb][v] + acc[mb][nb][v];
-    }
+        for (int v = 0; v < 16; ++v) acc[mb][nb][v] = tot[mb][nb][v] + acc[mb][nb][v];
   }
 
   if constexpr (LORA) {
-    if (lora) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int zr = wm * 64 + mb * 32 + i;
-        const u32x4_t zh = ld16(&zs[zr * 2 * kLoraMaxRank + 8 * half]);
-        const u32x4_t zl = ld16(&zs[zr * 2 * kLoraMaxRank + kLoraMaxRank + 8 * half]);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          // B[k][n] = A[k][n0 + col] for k < rank, else 0
-          const int col = wn * 64 + nb * 32 + i;
-          uint32_t bw[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int j0 = 8 * half + 2 * q;
-            const uint32_t e0 = j0 < a.lrank ? lbs[j0 * kBT + col] : 0u;
-            const uint32_t e1 = j0 + 1 < a.lrank ? lbs[(j0 + 1) * kBT + col] : 0u;
-            bw[q] = e0 | (e1 << 16);
-          }
-          const u32x4_t b{bw[0], bw[1], bw[2], bw[3]};
-          const f32x16_t t = mfma32x32x16(zl, b, mfma32x32x16(zh, b, zero16()));
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[mb][nb][v] = fmaf(a.lscale, t[v], acc[mb][nb][v]);
-        }
-      }
-    }
+    if (lora) lora_add_tile(a, zs, lbs, acc, wm, wn, lane);
   }
 
   if (MODE == kDact) {
-    // D goes through LDS one 64-row half at a time; then each thread takes
-    // 8 consecutive columns of a row for the SwiGLU backward, so the saved
-    // pre-activations are read and the gradient planes written 16 bytes at a
-    // time.
+    // D goes through LDS one 64-row half at a time (dact_epilogue)
     constexpr int ES = kBT + 4;  // fp32 row stride of a staged half
     static_assert(64 * ES * 2 <= EPI, "a staged half fits in the shared area");
     float* ep = reinterpret_cast<float*>(smem);
-    const int er = tid >> 4, ec = (tid & 15) * 8;
     for (int hh = 0; hh < 2; ++hh) {
       __syncthreads();
       if (wm == hh) {
@@ -517,82 +582,7 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
               ep[(mb * 32 + acc_row(v, half)) * ES + wn * 64 + nb * 32 + i] = acc[mb][nb][v];
       }
       __syncthreads();
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int lrow = hh * 64 + er + 16 * c;
-        if (lrow >= w.rows) continue;
-        float g;
-        int64_t rowp;
-        if (w.shared) {
-          rowp = w.m0 + lrow;
-          g = a.sg[rowp];
-        } else {
-          rowp = static_cast<int64_t>(w.seg0) + w.m0 + lrow;
-          const int64_t r = a.sorted_route[rowp];
-          g = (r >= 0 && r < a.T * a.K) ? a.gate[r] : 0.f;
-        }
-        const int col = w.n0 + ec;
-        const float* gur = (w.shared ? a.sgu : a.gu) + rowp * 2 * Ie;
-        const f32x4v_t* dsrc = reinterpret_cast<const f32x4v_t*>(ep + (er + 16 * c) * ES + ec);
-        const f32x4v_t d0 = dsrc[0], d1 = dsrc[1];
-        const f32x4v_t g0 = *reinterpret_cast<const f32x4v_t*>(gur + col);
-        const f32x4v_t g1 = *reinterpret_cast<const f32x4v_t*>(gur + col + 4);
-        const f32x4v_t u0 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col);
-        const f32x4v_t u1 = *reinterpret_cast<const f32x4v_t*>(gur + Ie + col + 4);
-        uint32_t pg[kGradPlanes][4], pu[kGradPlanes][4], pa[kGradPlanes][4];
-        double dot = 0.0;  // this thread's 8 columns of <D, act>
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float dv = e < 4 ? d0[e] : d1[e - 4];
-          const float gv = e < 4 ? g0[e] : g1[e - 4];
-          const float uv = e < 4 ? u0[e] : u1[e - 4];
-          const float dact = dv * g;
-          const float sgm = 1.0f / (1.0f + expf(-gv));
-          const float dgate = dact * uv * sgm * (1.0f + gv * (1.0f - sgm));
-          const float silu = silu_f32(gv);
-          const float dup = dact * silu;
-          const float act = silu * uv;
-          const float gact = g * act;
-          dot = fma(static_cast<double>(dv), static_cast<double>(act), dot);
-          uint16_t sgp[3], sup[3], sap[3];
-          split3(dgate, sgp);
-          split3(dup, sup);
-          split3(gact, sap);
-          const int sh = 16 * (e & 1);
-#pragma unroll
-          for (int q = 0; q < kGradPlanes; ++q) {
-            if ((e & 1) == 0) {
-              pg[q][e >> 1] = sgp[q];
-              pu[q][e >> 1] = sup[q];
-              pa[q][e >> 1] = sap[q];
-            } else {
-              pg[q][e >> 1] |= static_cast<uint32_t>(sgp[q]) << sh;
-              pu[q][e >> 1] |= static_cast<uint32_t>(sup[q]) << sh;
-              pa[q][e >> 1] |= static_cast<uint32_t>(sap[q]) << sh;
-            }
-          }
-        }
-        // the 16 threads of this row (consecutive lanes) add their partial
-        // sums in a fixed butterfly; the first writes the tile's sum
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 16);
-        if ((tid & 15) == 0) {
-          if (w.shared) {
-            a.dsp[rowp * a.nt_stride + w.nt] = dot;
-          } else {
-            const int64_t r = a.sorted_route[rowp];
-            if (r >= 0 && r < a.T * a.K) a.dgp[r * a.nt_stride + w.nt] = dot;
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < kGradPlanes; ++q) {
-          uint16_t* dq = (w.shared ? a.sdgu[q] : a.dgu[q]) + rowp * 2 * Ie;
-          st16(dq + col, u32x4_t{pg[q][0], pg[q][1], pg[q][2], pg[q][3]});
-          st16(dq + Ie + col, u32x4_t{pu[q][0], pu[q][1], pu[q][2], pu[q][3]});
-          st16((w.shared ? a.sgact[q] : a.gact[q]) + rowp * Ie + col,
-               u32x4_t{pa[q][0], pa[q][1], pa[q][2], pa[q][3]});
-        }
-      }
+      dact_epilogue(a, w, ep, ES, w.n0, w.nt, hh, tid);
     }
     return;
   }
@@ -630,6 +620,121 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
         if (rt >= 0 && rt < a.T * a.K) st16_nt(a.dx_route + rt * a.H + col, val);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dact at hidden 64 * NKB with 64-wide K blocks (half the K blocks, and so
+// half the barriers and LDS round trips, of the 32-wide loop; each gathered
+// dOut row contributes a whole 128-byte line per block).  Tiles, waves,
+// epilogue and the MFMA sequence of every element (16-wide K steps in
+// ascending order) are those of bwd_gemm_kernel<kDact>.  A (dOut rows) is
+// staged [row][64 k] with 128-byte rows whose 16-byte pieces are swizzled
+// by row (rk64_off), B (W2 rows h) [k][col] as in the other kernels.
+// Register ring of three K blocks (two in flight while one is multiplied),
+// two LDS stages.  LORA adds the routed rows' adapter term before the
+// epilogue as bwd_gemm_kernel does.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int rk64_off(int row, int c) { return row * 64 + ((c ^ ((row >> 1) & 7)) << 3); }
+
+template <int NKB, bool LORA>
+__global__ __launch_bounds__(256, 2) void bwd_dact_k64_kernel(const BwdArgs a) {
+  constexpr int NS = 3;
+  constexpr int APL = kBT * 64;  // A stage: 128 rows x 64 k
+  constexpr int BPL = 64 * kRStride;  // B stage: 64 k rows x 128 columns
+  constexpr int STAGE = APL + BPL;
+  constexpr int ES = kBT + 4;  // fp32 row stride of a staged epilogue half
+  constexpr int EPI = 64 * ES * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE > EPI ? 2 * STAGE : EPI];
+  // LoRA: the tile's rows' shrink results and its columns' A2 rows
+  __shared__ __attribute__((aligned(16))) uint16_t zs[LORA ? kBT * 2 * kLoraMaxRank : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t lbs[LORA ? kLoraMaxRank * kBT : 8];
+
+  BwdTile w;
+  if (!bwd_decode<kDact>(a, blockIdx.x, w)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 31, half = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int Ie = w.Ie;
+  const bool lora = LORA && !w.shared;  // the shared expert has no adapter
+  // ordered before the epilogue by the K loop's barriers
+  if (lora) lora_stage_tile(a, w, zs, lbs, a.I, tid);
+  // A loader: row ar, 16-byte pieces ap .. ap + 3 (32 k); B loader: k rows
+  // kr + 16c, 8 columns at tc
+  const int ar = tid >> 1, ap = (tid & 1) * 4;
+  const int kr = tid >> 4, tc = (tid & 15) * 8;
+  const int rr = min(ar, w.rows - 1);  // rows past the tile repeat its last row, unused
+  const uint16_t* arow = a.dout + bwd_token(a, w, static_cast<int64_t>(w.seg0) + w.m0 + rr) * a.H + ap * 8;
+  const uint16_t* wbase = (w.shared ? a.ws2 : a.w2 + static_cast<int64_t>(w.grp) * a.H * a.I) + w.n0 + tc;
+
+  u32x4_t ra[NS][4], rb[NS][4];
+  auto fetch = [&](int set, int kb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ra[set][q] = ld16(arow + kb * 64 + 8 * q);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint16_t* wp = wbase + static_cast<int64_t>(kb * 64 + kr + 16 * c) * Ie;
+      rb[set][c] = w.wstream ? ld16_nt(wp) : ld16(wp);
+    }
+  };
+  auto stash = [&](int set, int stage) {
+    uint16_t* s = smem + stage * STAGE;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st16(s + rk64_off(ar, ap + q), ra[set][q]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) st16(s + APL + rc_off(kr + 16 * c, tc), rb[set][c]);
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = zero16();
+  auto compute = [&](int stage) {
+    const uint16_t* s = smem + stage * STAGE;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      u32x4_t fa[2], fb[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) fa[mb] = ld16(s + rk64_off(wm * 64 + mb * 32 + i, 2 * st + half));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) fb[nb] = frag_tr(s + APL, 16 * st, wn * 64 + nb * 32, lane);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32x32x16(fa[mb], fb[nb], acc[mb][nb]);
+    }
+  };
+
+#pragma unroll
+  for (int q = 0; q < NS - 1 && q < NKB; ++q) fetch(q, q);
+  stash(0, 0);
+#pragma unroll
+  for (int it = 0; it < NKB; ++it) {
+    __syncthreads();
+    if (it + NS - 1 < NKB) fetch((it + NS - 1) % NS, it + NS - 1);
+    compute(it & 1);
+    if (it + 1 < NKB) stash((it + 1) % NS, (it + 1) & 1);
+  }
+  if constexpr (LORA) {
+    if (lora) lora_add_tile(a, zs, lbs, acc, wm, wn, lane);
+  }
+
+  // epilogue: D through LDS one 64-row half at a time, then dact_epilogue
+  float* ep = reinterpret_cast<float*>(smem);
+  for (int hh = 0; hh < 2; ++hh) {
+    __syncthreads();
+    if (wm == hh) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            ep[(mb * 32 + acc_row(v, half)) * ES + wn * 64 + nb * 32 + i] = acc[mb][nb][v];
+    }
+    __syncthreads();
+    dact_epilogue(a, w, ep, ES, w.n0, w.nt, hh, tid);
   }
 }
 
@@ -1563,10 +1668,10 @@ hipError_t launch_bwd_dact(const BwdLaunch& L, hipStream_t stream) {
   if (L.la2) {
     a.lzq = L.lv2;
     a.lbx = L.la2;
-    if (L.H == 2048) bwd_gemm_kernel<kDact, 2048 / kBK, true><<<grid, 256, 0, stream>>>(a);
-    else bwd_gemm_kernel<kDact, 0, true><<<grid, 256, 0, stream>>>(a);
+    if (L.H == 2048) bwd_dact_k64_kernel<2048 / 64, true><<<grid, 256, 0, stream>>>(a);
+    else bwd_gemm_kernel<kDact, true><<<grid, 256, 0, stream>>>(a);
   } else if (L.H == 2048) {
-    bwd_gemm_kernel<kDact, 2048 / kBK><<<grid, 256, 0, stream>>>(a);
+    bwd_dact_k64_kernel<2048 / 64, false><<<grid, 256, 0, stream>>>(a);
   } else {
     bwd_gemm_kernel<kDact><<<grid, 256, 0, stream>>>(a);
   }
@@ -1585,7 +1690,7 @@ hipError_t launch_bwd_dx(const BwdLaunch& L, hipStream_t stream) {
       const unsigned wide_grid = rounds(static_cast<int64_t>(L.max_tiles_bwd) * (L.H / (2 * kBT)));
       bwd_dx_wide_kernel<2 * 512 / kBK, true><<<wide_grid, 256, 0, stream>>>(a);
     } else {
-      bwd_gemm_kernel<kDx, 0, true><<<dx_grid, 256, 0, stream>>>(a);
+      bwd_gemm_kernel<kDx, true><<<dx_grid, 256, 0, stream>>>(a);
     }
     a.lzq = nullptr;
     a.lbx = nullptr;
