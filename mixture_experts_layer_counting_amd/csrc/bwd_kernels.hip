@@ -630,7 +630,9 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(const BwdArgs a) {
 // epilogue and the MFMA sequence of every element (16-wide K steps in
 // ascending order) are those of bwd_gemm_kernel<kDact>.  A (dOut rows) is
 // staged [row][64 k] with 128-byte rows whose 16-byte pieces are swizzled
-// by row (rk64_off), B (W2 rows h) [k][col] as in the other kernels.
+// by row (rk64_off; each wave instruction writes 8 whole rows, and the
+// 32-row fragment reads are conflict-free), B (W2 rows h) [k][col] as in
+// the other kernels.
 // Register ring of three K blocks (two in flight while one is multiplied),
 // two LDS stages.  LORA adds the routed rows' adapter term before the
 // epilogue as bwd_gemm_kernel does.
@@ -659,18 +661,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dact_k64_kernel(const BwdArgs a) {
   const bool lora = LORA && !w.shared;  // the shared expert has no adapter
   // ordered before the epilogue by the K loop's barriers
   if (lora) lora_stage_tile(a, w, zs, lbs, a.I, tid);
-  // A loader: row ar, 16-byte pieces ap .. ap + 3 (32 k); B loader: k rows
-  // kr + 16c, 8 columns at tc
-  const int ar = tid >> 1, ap = (tid & 1) * 4;
+  // A loader: rows wave * 32 + 8q + lane / 8, 16-byte piece ap = lane % 8,
+  // so that each wave instruction writes 8 whole 128-byte rows; B loader: k
+  // rows kr + 16c, 8 columns at tc
+  const int ap = lane & 7;
   const int kr = tid >> 4, tc = (tid & 15) * 8;
-  const int rr = min(ar, w.rows - 1);  // rows past the tile repeat its last row, unused
-  const uint16_t* arow = a.dout + bwd_token(a, w, static_cast<int64_t>(w.seg0) + w.m0 + rr) * a.H + ap * 8;
+  const uint16_t* arow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // rows past the tile repeat its last row, unused
+    const int rr = min(wave * 32 + 8 * q + (lane >> 3), w.rows - 1);
+    arow[q] = a.dout + bwd_token(a, w, static_cast<int64_t>(w.seg0) + w.m0 + rr) * a.H + ap * 8;
+  }
   const uint16_t* wbase = (w.shared ? a.ws2 : a.w2 + static_cast<int64_t>(w.grp) * a.H * a.I) + w.n0 + tc;
 
   u32x4_t ra[NS][4], rb[NS][4];
   auto fetch = [&](int set, int kb) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ra[set][q] = ld16(arow + kb * 64 + 8 * q);
+    for (int q = 0; q < 4; ++q) ra[set][q] = ld16(arow[q] + kb * 64);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint16_t* wp = wbase + static_cast<int64_t>(kb * 64 + kr + 16 * c) * Ie;
@@ -680,7 +688,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dact_k64_kernel(const BwdArgs a) {
   auto stash = [&](int set, int stage) {
     uint16_t* s = smem + stage * STAGE;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st16(s + rk64_off(ar, ap + q), ra[set][q]);
+    for (int q = 0; q < 4; ++q) st16(s + rk64_off(wave * 32 + 8 * q + (lane >> 3), ap), ra[set][q]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) st16(s + APL + rc_off(kr + 16 * c, tc), rb[set][c]);
   };
